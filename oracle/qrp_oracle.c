@@ -1,0 +1,428 @@
+/*
+ * qrp_oracle.c -- CPU oracle (TEST INFRASTRUCTURE ONLY; see qrp_oracle.h).
+ *
+ * Each function writes out the plain definition of the operation, in the
+ * order the documentation pages describe it, with no blocking or fusion:
+ *
+ *   seq(t)   the sequence b whose ragged row range [off[b], off[b+1])
+ *            holds token t (rope_split_store_paged_ragged page, Args:
+ *            input_row_offsets; generic_kv_cache_radd_dispatch page, Args:
+ *            input_row_offsets "start of each sequence");
+ *   pos(t)   cache_lengths[seq(t) + batch_offset] + t - off[seq(t)]
+ *            (generic_kv_cache_radd_dispatch page, Description: batch
+ *            offset and per-batch cache lengths locate the target rows);
+ *   slot     page = lookup_table[seq][pos / page_size], row pos % page_size
+ *            of that page, at layer layer_idx (rope_split_store_paged_ragged
+ *            page, Args: kv_collection, layer_idx);
+ *   rope     pairs rotated by the (cos, sin) freqs_cis entry of their
+ *            frequency at pos (rope_split_store_paged_ragged page,
+ *            Parameters: interleaved; Args: freqs_cis);
+ *   norm     per-head RMSNorm with gamma + weight_offset, epsilon added to
+ *            the mean square before the reciprocal square root
+ *            (fused_dual_qk_rms_norm_rope_ragged_paged page, signature and
+ *            Description; MatmulFusedPartialRMSNorm page, Args: epsilon);
+ *   radd     cache += a, K half then V half of a's last dimension
+ *            (generic_kv_cache_radd_dispatch page, Summary, Description).
+ *
+ * Built with -ffp-contract=off and no fast-math, so double and float
+ * expressions round exactly as written.
+ */
+#include "qrp_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* element access                                                      */
+/* ------------------------------------------------------------------ */
+
+static size_t elem_bytes(int32_t dt) { return dt == ORC_F32 ? 4u : 2u; }
+
+double orc_bf16_to_double(uint16_t b) {
+  /* a bf16 value is the upper half of an IEEE binary32 word */
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+uint16_t orc_round_bf16(double x) {
+  float f;
+  uint32_t u;
+  if (isnan(x)) {
+    f = (float)x;
+    memcpy(&u, &f, 4);
+    return (uint16_t)((u >> 16) | 0x0040u); /* quiet NaN, sign and top payload kept */
+  }
+  if (x == 0.0 || isinf(x)) {
+    f = (float)x; /* exact */
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+  }
+  /* bf16 keeps 8 significant bits; its exponent range is binary32's, so
+   * below 2^-126 the spacing stays 2^-133 (subnormals). */
+  int e = ilogb(x);
+  if (e < -126) e = -126;
+  double quantum = ldexp(1.0, e - 7);
+  double r = nearbyint(x / quantum) * quantum; /* ties to even (default rounding mode) */
+  if (fabs(r) >= ldexp(1.0, 128)) return (uint16_t)(x < 0 ? 0xFF80u : 0x7F80u);
+  f = (float)r; /* exact: r has at most 8 significant bits */
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+static double get(const void* base, int32_t dt, int64_t i) {
+  if (dt == ORC_F32) return (double)((const float*)base)[i];
+  return orc_bf16_to_double(((const uint16_t*)base)[i]);
+}
+
+/* value rounded to dtype, returned as double */
+static double round_to(int32_t dt, double v) {
+  if (dt == ORC_F32) return (double)(float)v;
+  return orc_bf16_to_double(orc_round_bf16(v));
+}
+
+static void put(void* base, int32_t dt, int64_t i, double v) {
+  if (dt == ORC_F32)
+    ((float*)base)[i] = (float)v;
+  else
+    ((uint16_t*)base)[i] = orc_round_bf16(v);
+}
+
+static void copy_bits(void* dst, int64_t di, const void* src, int64_t si, int32_t dt) {
+  size_t n = elem_bytes(dt);
+  memcpy((char*)dst + (size_t)di * n, (const char*)src + (size_t)si * n, n);
+}
+
+/* ------------------------------------------------------------------ */
+/* ragged batch and paged placement                                    */
+/* ------------------------------------------------------------------ */
+
+static int32_t check_offsets(const uint32_t* off, uint32_t B, uint32_t T) {
+  if (off[0] != 0 || off[B] != T) return ORC_EDATA;
+  for (uint32_t b = 0; b < B; ++b)
+    if (off[b + 1] < off[b]) return ORC_EDATA;
+  return ORC_OK;
+}
+
+/* the unique b with off[b] <= t < off[b+1], by linear scan */
+static int64_t seq_of(const uint32_t* off, uint32_t B, uint32_t t) {
+  for (uint32_t b = 0; b < B; ++b)
+    if (off[b] <= t && t < off[b + 1]) return (int64_t)b;
+  return -1;
+}
+
+/* page and in-page row of position `pos` of cache sequence `cseq` */
+static int32_t locate(const orc_cache* c, uint32_t cseq, uint32_t pos, uint64_t* page,
+                      uint32_t* slot) {
+  if (cseq >= c->cache_batch) return ORC_EDATA;
+  uint32_t idx = pos / c->page_size;
+  if (idx >= c->max_pages_per_seq) return ORC_EDATA;
+  uint64_t pg = c->lookup_table[(uint64_t)cseq * c->max_pages_per_seq + idx];
+  if (pg >= c->num_pages) return ORC_EDATA;
+  *page = pg;
+  *slot = pos % c->page_size;
+  return ORC_OK;
+}
+
+/* element offset of head `h` of row `slot` in plane `plane`, layer `layer` */
+static int64_t row_offset(const orc_cache* c, uint64_t page, uint32_t plane, uint32_t layer,
+                          uint32_t slot, uint32_t h) {
+  return (int64_t)page * c->page_stride + (int64_t)plane * c->plane_stride +
+         (int64_t)layer * c->layer_stride + (int64_t)slot * c->slot_stride +
+         (int64_t)h * c->head_stride;
+}
+
+/* Token t -> (cache sequence, position, page, slot), with every bound checked. */
+typedef struct {
+  uint32_t cseq, pos, slot;
+  uint64_t page;
+} where_t;
+
+static int32_t where_is(const orc_cache* c, const uint32_t* off, uint32_t B, uint32_t batch_offset,
+                        uint32_t t, uint32_t max_seq_len, where_t* w) {
+  int64_t b = seq_of(off, B, t);
+  if (b < 0) return ORC_EDATA;
+  uint32_t cseq = (uint32_t)b + batch_offset;
+  if (cseq >= c->cache_batch) return ORC_EDATA;
+  uint64_t pos = (uint64_t)c->cache_lengths[cseq] + (t - off[b]);
+  if (max_seq_len && pos >= max_seq_len) return ORC_EDATA;
+  if (pos > 0xFFFFFFFFull) return ORC_EDATA;
+  w->cseq = cseq;
+  w->pos = (uint32_t)pos;
+  return locate(c, cseq, w->pos, &w->page, &w->slot);
+}
+
+/* ------------------------------------------------------------------ */
+/* per-head arithmetic                                                 */
+/* ------------------------------------------------------------------ */
+
+/* RoPE of one head x[D] at position pos; y gets the rotated values and
+ * mag[j] the length of the pair j belongs to (|x_j| for dims >= R). */
+static void rope_head(const double* x, double* y, double* mag, uint32_t D, const float* freqs,
+                      uint32_t pos, uint32_t R, int32_t interleaved) {
+  for (uint32_t j = 0; j < D; ++j) {
+    y[j] = x[j];
+    mag[j] = fabs(x[j]);
+  }
+  const float* row = freqs + (uint64_t)pos * R;
+  for (uint32_t i = 0; i < R / 2; ++i) {
+    double c = (double)row[2 * i];     /* cos(pos * theta_i) */
+    double s = (double)row[2 * i + 1]; /* sin(pos * theta_i) */
+    uint32_t j0 = interleaved ? 2 * i : i;
+    uint32_t j1 = interleaved ? 2 * i + 1 : i + R / 2;
+    double re = x[j0], im = x[j1];
+    /* (re + i im) * (c + i s) */
+    y[j0] = re * c - im * s;
+    y[j1] = re * s + im * c;
+    double m = hypot(y[j0], y[j1]);
+    mag[j0] = m;
+    mag[j1] = m;
+  }
+}
+
+/* per-head RMSNorm: y_j = x_j / sqrt(mean(x^2) + eps) * (gamma_j + w) */
+static void rmsnorm_head(const double* x, double* y, uint32_t D, const void* gamma, int32_t dt,
+                         double w, double eps, int32_t multiply_before_cast) {
+  double ss = 0.0;
+  for (uint32_t j = 0; j < D; ++j) ss += x[j] * x[j];
+  double r = 1.0 / sqrt(ss / (double)D + eps);
+  for (uint32_t j = 0; j < D; ++j) {
+    double g = get(gamma, dt, j);
+    if (multiply_before_cast) {
+      y[j] = x[j] * r * (g + w);
+    } else {
+      double n = round_to(dt, x[j] * r);
+      double gw = round_to(dt, g + w);
+      y[j] = round_to(dt, n * gw);
+    }
+  }
+}
+
+/* Scratch for one head. */
+typedef struct {
+  double *x, *xn, *y, *mag;
+} head_buf;
+
+static int head_buf_alloc(head_buf* hb, uint32_t D) {
+  hb->x = (double*)malloc(sizeof(double) * D * 4);
+  if (!hb->x) return 0;
+  hb->xn = hb->x + D;
+  hb->y = hb->x + 2 * D;
+  hb->mag = hb->x + 3 * D;
+  return 1;
+}
+
+/* Process one head: read x, optional norm, rope, write with the rule
+ * "roped or normed elements are rounded; the rest move as raw bits". */
+static void do_head(const void* src, int64_t src_off, void* dst, int64_t dst_off, int32_t dt,
+                    uint32_t D, const void* gamma, double w, double eps, int32_t mbc,
+                    const float* freqs, uint32_t pos, uint32_t R, int32_t interleaved, head_buf* hb,
+                    double* exact, double* mag) {
+  for (uint32_t j = 0; j < D; ++j) hb->x[j] = get(src, dt, src_off + j);
+  const double* in = hb->x;
+  if (gamma) {
+    rmsnorm_head(hb->x, hb->xn, D, gamma, dt, w, eps, mbc);
+    in = hb->xn;
+  }
+  rope_head(in, hb->y, hb->mag, D, freqs, pos, R, interleaved);
+  for (uint32_t j = 0; j < D; ++j) {
+    if (gamma || j < R)
+      put(dst, dt, dst_off + j, hb->y[j]);
+    else
+      copy_bits(dst, dst_off + j, src, src_off + j, dt);
+    if (exact) exact[j] = hb->y[j];
+    if (mag) mag[j] = hb->mag[j];
+  }
+}
+
+static int32_t check_common(int32_t dtype, const orc_cache* c, uint32_t rope_dim,
+                            uint32_t layer_idx, uint32_t max_seq_len) {
+  if (!c || !c->pool || !c->cache_lengths || !c->lookup_table) return ORC_EINVAL;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_EINVAL;
+  if (c->dtype != dtype) return ORC_EINVAL;
+  if (c->head_dim == 0 || c->page_size == 0) return ORC_EINVAL;
+  if (rope_dim == 0 || rope_dim % 2 || rope_dim > c->head_dim) return ORC_EINVAL;
+  if (layer_idx >= c->num_layers) return ORC_EINVAL;
+  if (max_seq_len == 0) return ORC_EINVAL;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* operations                                                          */
+/* ------------------------------------------------------------------ */
+
+int32_t orc_rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t T,
+                                   uint64_t qkv_row_stride, uint32_t n_q_heads,
+                                   const uint32_t* off, uint32_t B, const float* freqs,
+                                   uint32_t max_seq_len, uint32_t R, int32_t interleaved,
+                                   orc_cache* c, uint32_t layer_idx, void* q_out,
+                                   uint64_t q_out_row_stride, orc_trace* tr) {
+  int32_t st = check_common(dtype, c, R, layer_idx, max_seq_len);
+  if (st) return st;
+  if (c->kv_planes != 2) return ORC_EINVAL;
+  if (T == 0) return ORC_OK;
+  if (!qkv || !off || !freqs || !q_out) return ORC_EINVAL;
+  if (B > c->cache_batch) return ORC_EINVAL;
+  const uint32_t D = c->head_dim, Hq = n_q_heads, Hk = c->num_kv_heads;
+  if (qkv_row_stride < (uint64_t)(Hq + 2 * Hk) * D || q_out_row_stride < (uint64_t)Hq * D)
+    return ORC_EINVAL;
+  if ((st = check_offsets(off, B, T))) return st;
+  where_t w;
+  for (uint32_t t = 0; t < T; ++t)
+    if ((st = where_is(c, off, B, 0, t, max_seq_len, &w))) return st;
+
+  head_buf hb;
+  if (!head_buf_alloc(&hb, D)) return ORC_EINVAL;
+  for (uint32_t t = 0; t < T; ++t) {
+    where_is(c, off, B, 0, t, max_seq_len, &w);
+    const int64_t in_row = (int64_t)t * (int64_t)qkv_row_stride;
+    /* Q heads -> dense q_output */
+    for (uint32_t h = 0; h < Hq; ++h) {
+      double* ex = tr && tr->q_exact ? tr->q_exact + ((uint64_t)t * Hq + h) * D : NULL;
+      double* mg = tr && tr->q_mag ? tr->q_mag + ((uint64_t)t * Hq + h) * D : NULL;
+      do_head(qkv, in_row + (int64_t)h * D, q_out, (int64_t)t * (int64_t)q_out_row_stride + (int64_t)h * D,
+              dtype, D, NULL, 0.0, 0.0, 1, freqs, w.pos, R, interleaved, &hb, ex, mg);
+    }
+    /* K heads -> plane 0 of the cache, roped */
+    for (uint32_t h = 0; h < Hk; ++h) {
+      int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);
+      double* ex = tr && tr->k_exact ? tr->k_exact + ((uint64_t)t * Hk + h) * D : NULL;
+      double* mg = tr && tr->k_mag ? tr->k_mag + ((uint64_t)t * Hk + h) * D : NULL;
+      do_head(qkv, in_row + (int64_t)(Hq + h) * D, c->pool, dst, dtype, D, NULL, 0.0, 0.0, 1, freqs,
+              w.pos, R, interleaved, &hb, ex, mg);
+      if (tr && tr->k_row_off) tr->k_row_off[(uint64_t)t * Hk + h] = dst;
+    }
+    /* V heads -> plane 1 of the cache, bit copy */
+    for (uint32_t h = 0; h < Hk; ++h) {
+      int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);
+      int64_t src = in_row + (int64_t)(Hq + Hk + h) * D;
+      for (uint32_t j = 0; j < D; ++j) copy_bits(c->pool, dst + j, qkv, src + j, dtype);
+      if (tr && tr->v_row_off) tr->v_row_off[(uint64_t)t * Hk + h] = dst;
+    }
+  }
+  free(hb.x);
+  return ORC_OK;
+}
+
+int32_t orc_qk_rmsnorm_rope_paged(const void* buf, int32_t dtype, uint32_t T,
+                                  uint64_t buf_row_stride, const orc_band* band,
+                                  float weight_offset, int32_t multiply_before_cast,
+                                  const uint32_t* off, uint32_t B, const float* freqs,
+                                  uint32_t max_seq_len, uint32_t R, int32_t interleaved,
+                                  uint32_t layer_idx, orc_trace* tr) {
+  if (!band) return ORC_EINVAL;
+  orc_cache* c = band->cache;
+  int32_t st = check_common(dtype, c, R, layer_idx, max_seq_len);
+  if (st) return st;
+  if (band->v_col >= 0 && (band->k_col < 0 || c->kv_planes != 2)) return ORC_EINVAL;
+  if (T == 0) return ORC_OK;
+  if (!buf || !off || !freqs || (band->n_q_heads && !band->q_output)) return ORC_EINVAL;
+  if (B > c->cache_batch) return ORC_EINVAL;
+  const uint32_t D = c->head_dim, Hq = band->n_q_heads, Hk = c->num_kv_heads;
+  if ((st = check_offsets(off, B, T))) return st;
+  where_t w;
+  for (uint32_t t = 0; t < T; ++t)
+    if ((st = where_is(c, off, B, 0, t, max_seq_len, &w))) return st;
+
+  /* weight_offset is a Scalar[dtype] (fused_dual_qk_rms_norm_rope_ragged_paged
+   * page, signature): take its dtype value. */
+  const double wv = round_to(dtype, (double)weight_offset);
+  const double eps = (double)band->epsilon;
+  head_buf hb;
+  if (!head_buf_alloc(&hb, D)) return ORC_EINVAL;
+  for (uint32_t t = 0; t < T; ++t) {
+    where_is(c, off, B, 0, t, max_seq_len, &w);
+    const int64_t in_row = (int64_t)t * (int64_t)buf_row_stride;
+    for (uint32_t h = 0; h < Hq; ++h) {
+      double* ex = tr && tr->q_exact ? tr->q_exact + ((uint64_t)t * Hq + h) * D : NULL;
+      double* mg = tr && tr->q_mag ? tr->q_mag + ((uint64_t)t * Hq + h) * D : NULL;
+      do_head(buf, in_row + (int64_t)band->q_col + (int64_t)h * D, band->q_output,
+              (int64_t)t * (int64_t)band->q_out_row_stride + (int64_t)h * D, dtype, D,
+              band->q_gamma, wv, eps, multiply_before_cast, freqs, w.pos, R, interleaved, &hb, ex,
+              mg);
+    }
+    for (uint32_t h = 0; h < Hk; ++h) {
+      int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);
+      double* ex = tr && tr->k_exact ? tr->k_exact + ((uint64_t)t * Hk + h) * D : NULL;
+      double* mg = tr && tr->k_mag ? tr->k_mag + ((uint64_t)t * Hk + h) * D : NULL;
+      if (band->k_col >= 0) /* K from the buffer */
+        do_head(buf, in_row + band->k_col + (int64_t)h * D, c->pool, dst, dtype, D, band->k_gamma,
+                wv, eps, multiply_before_cast, freqs, w.pos, R, interleaved, &hb, ex, mg);
+      else /* K already in the cache: updated in place (the row is read whole first) */
+        do_head(c->pool, dst, c->pool, dst, dtype, D, band->k_gamma, wv, eps,
+                multiply_before_cast, freqs, w.pos, R, interleaved, &hb, ex, mg);
+      if (tr && tr->k_row_off) tr->k_row_off[(uint64_t)t * Hk + h] = dst;
+    }
+    if (band->v_col >= 0) {
+      for (uint32_t h = 0; h < Hk; ++h) {
+        int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);
+        int64_t src = in_row + band->v_col + (int64_t)h * D;
+        for (uint32_t j = 0; j < D; ++j) copy_bits(c->pool, dst + j, buf, src + j, dtype);
+        if (tr && tr->v_row_off) tr->v_row_off[(uint64_t)t * Hk + h] = dst;
+      }
+    }
+  }
+  free(hb.x);
+  return ORC_OK;
+}
+
+int32_t orc_dual_band(const void* buf, int32_t dtype, uint32_t T, uint64_t buf_row_stride,
+                      const orc_band* main_band, const orc_band* index_band, float weight_offset,
+                      int32_t multiply_before_cast, const uint32_t* off, uint32_t B,
+                      const float* freqs, uint32_t max_seq_len, uint32_t R, int32_t interleaved,
+                      uint32_t layer_idx, orc_trace* main_trace, orc_trace* index_trace) {
+  if (!main_band || !index_band || !main_band->cache || !index_band->cache) return ORC_EINVAL;
+  /* the two bands must agree on dtype and head size (fused_dual_qk_rms_norm_rope_ragged_paged
+   * page, Description: identical RoPE geometry across both bands) */
+  if (main_band->cache->dtype != index_band->cache->dtype ||
+      main_band->cache->head_dim != index_band->cache->head_dim)
+    return ORC_EINVAL;
+  /* one launch fusing two single-band launches: the same result as the two in turn */
+  int32_t st = orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, main_band, weight_offset,
+                                         multiply_before_cast, off, B, freqs, max_seq_len, R,
+                                         interleaved, layer_idx, main_trace);
+  if (st) return st;
+  return orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, index_band, weight_offset,
+                                   multiply_before_cast, off, B, freqs, max_seq_len, R,
+                                   interleaved, layer_idx, index_trace);
+}
+
+int32_t orc_kv_cache_radd(const void* a, int32_t dtype, uint32_t T, uint64_t a_row_stride,
+                          const uint32_t* off, uint32_t B, uint32_t batch_offset, orc_cache* c,
+                          uint32_t layer_idx, int64_t* k_row_off, int64_t* v_row_off) {
+  if (!c || !c->pool || !c->cache_lengths || !c->lookup_table) return ORC_EINVAL;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_EINVAL;
+  if (c->dtype != dtype || c->kv_planes != 2 || layer_idx >= c->num_layers) return ORC_EINVAL;
+  if ((uint64_t)batch_offset + B > c->cache_batch) return ORC_EINVAL;
+  if (T == 0) return ORC_OK;
+  if (!a || !off) return ORC_EINVAL;
+  const uint32_t D = c->head_dim, Hk = c->num_kv_heads;
+  const uint64_t hidden = (uint64_t)Hk * D; /* a is (rows, 2 * hidden) */
+  if (a_row_stride < 2 * hidden) return ORC_EINVAL;
+  int32_t st = check_offsets(off, B, T);
+  if (st) return st;
+  where_t w;
+  for (uint32_t t = 0; t < T; ++t)
+    if ((st = where_is(c, off, B, batch_offset, t, 0, &w))) return st;
+
+  for (uint32_t t = 0; t < T; ++t) {
+    where_is(c, off, B, batch_offset, t, 0, &w);
+    for (uint32_t plane = 0; plane < 2; ++plane) { /* first half of a -> K, second -> V */
+      for (uint32_t h = 0; h < Hk; ++h) {
+        int64_t dst = row_offset(c, w.page, plane, layer_idx, w.slot, h);
+        int64_t src = (int64_t)t * (int64_t)a_row_stride + (int64_t)(plane * hidden) + (int64_t)h * D;
+        for (uint32_t j = 0; j < D; ++j) {
+          float cur = (float)get(c->pool, dtype, dst + j);
+          float add = (float)get(a, dtype, src + j);
+          float sum = cur + add; /* one IEEE binary32 add */
+          put(c->pool, dtype, dst + j, (double)sum);
+        }
+        int64_t* rec = plane == 0 ? k_row_off : v_row_off;
+        if (rec) rec[(uint64_t)t * Hk + h] = dst;
+      }
+    }
+  }
+  return ORC_OK;
+}

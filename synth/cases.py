@@ -1,0 +1,472 @@
+"""Seeded synthetic workloads for the ragged RoPE / split / paged-store pass.
+
+A :class:`Case` holds host numpy arrays only: the flat input buffer (raw bits
+of its dtype), ragged row offsets, the freqs_cis table, one or two paged
+caches and the scalar arguments.  Tests, the benchmark and the smoke check
+turn a case into arguments for the HIP library and, separately, for the CPU
+oracle.  Nothing here computes any part of the method itself.
+
+Workload shapes follow the configurations the pass is measured on:
+
+* ``c1``  tiny fp32 interleaved store (batch 2, lengths {3, 5}, cache lengths
+  {0, 4}, 4 Q / 2 KV heads, head_dim 64, page 16, 8 pages);
+* ``c2``  Llama-3-8B-shaped bf16 prefill store, half-split RoPE (batch 8,
+  lengths U[128, 2048], 32 Q / 8 KV heads, head_dim 128, theta 5e5, page 128,
+  32 layers, layer 17);
+* ``c3``  the matching decode (256 sequences x 1 token, cache lengths
+  U[0, 8191], interleaved, 20000-page pool);
+* ``c4``  dual-band RMSNorm + RoPE (main 64 Q / 8 KV heads, index 16 Q heads
+  + single-head K-only cache, head_dim 128, rope_dim 64, page 64);
+* ``c5``  K/V radd (8 KV heads, head_dim 128, batch 32 of a 64-sequence
+  cache at batch_offset 4, page 128, layer 3).
+
+``small=True`` gives a reduced variant of each that the oracle finishes in
+well under a second while still spanning several work tiles and a ragged tail.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+from . import prng
+
+F32, BF16 = "f32", "bf16"
+SENTINEL = {F32: np.uint32(0x7FBADBAD), BF16: np.uint16(0x7FBA)}  # signalling-NaN patterns
+BITS_DTYPE = {F32: np.uint32, BF16: np.uint16}
+ELEM_BYTES = {F32: 4, BF16: 2}
+NO_PAGE = np.uint32(0xFFFFFFFF)
+
+# stream numbers (one per generated array)
+S_LENS, S_CLEN, S_PERM, S_BUF, S_GAMMA, S_A, S_PREFILL, S_SPECIAL = 1, 2, 3, 4, 5, 6, 7, 8
+
+
+def to_bits(values: np.ndarray, dtype: str) -> np.ndarray:
+    """Doubles -> raw bits of ``dtype`` (binary32 RNE, then bf16 RNE)."""
+    f = np.asarray(values, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32)
+    if dtype == F32:
+        return u.copy()
+    rounded = (u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == F32:
+        return bits.view(np.float32).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def freqs_table(max_seq_len: int, rope_dim: int, base: float) -> np.ndarray:
+    """freqs_cis[p, 2i] = cos(p * base^(-2i/R)), [p, 2i+1] = sin(...), fp64 -> fp32."""
+    i = np.arange(rope_dim // 2, dtype=np.float64)
+    inv = base ** (-2.0 * i / rope_dim)
+    ang = np.arange(max_seq_len, dtype=np.float64)[:, None] * inv[None, :]
+    tab = np.empty((max_seq_len, rope_dim), dtype=np.float64)
+    tab[:, 0::2] = np.cos(ang)
+    tab[:, 1::2] = np.sin(ang)
+    return tab.astype(np.float32)
+
+
+@dataclass
+class PagedCache:
+    """Paged pool, page-major: [num_pages][kv_planes][num_layers][page_size][Hk][D].
+
+    The pool is held lazily: every element is the sentinel except the rows
+    listed in ``prefill`` (page, plane, layer, slot, values[Hk, D]), so a
+    20000-page pool costs nothing until someone materialises it."""
+    dtype: str
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    num_layers: int
+    kv_planes: int
+    num_pages: int
+    cache_lengths: np.ndarray          # uint32 [cache_batch]
+    lookup_table: np.ndarray           # uint32 [cache_batch, max_pages_per_seq]
+    prefill: list = field(default_factory=list)
+
+    @property
+    def cache_batch(self) -> int:
+        return int(self.lookup_table.shape[0])
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return int(self.lookup_table.shape[1])
+
+    @property
+    def shape(self) -> tuple:
+        return (self.num_pages, self.kv_planes, self.num_layers, self.page_size,
+                self.num_kv_heads, self.head_dim)
+
+    @property
+    def strides(self) -> dict:
+        """Element strides of the page-major layout (C order of ``shape``)."""
+        st = np.empty(6, dtype=np.int64)
+        acc = 1
+        for i in range(5, -1, -1):
+            st[i] = acc
+            acc *= self.shape[i]
+        return dict(page_stride=int(st[0]), plane_stride=int(st[1]), layer_stride=int(st[2]),
+                    slot_stride=int(st[3]), head_stride=int(st[4]))
+
+    @property
+    def page_elems(self) -> int:
+        return int(np.prod(self.shape[1:]))
+
+    @property
+    def nbytes(self) -> int:
+        return self.num_pages * self.page_elems * ELEM_BYTES[self.dtype]
+
+    def prefill_arrays(self):
+        """(pages, planes, layers, slots) int64 arrays and values [n, Hk, D] bits."""
+        if not self.prefill:
+            z = np.zeros(0, dtype=np.int64)
+            return z, z, z, z, np.zeros((0, self.num_kv_heads, self.head_dim),
+                                        dtype=BITS_DTYPE[self.dtype])
+        cols = [np.concatenate([np.asarray(p[i], dtype=np.int64) for p in self.prefill])
+                for i in range(4)]
+        vals = np.concatenate([p[4] for p in self.prefill])
+        return cols[0], cols[1], cols[2], cols[3], vals
+
+    def materialize(self, pages: Optional[np.ndarray] = None) -> np.ndarray:
+        """The pool as a numpy array; with ``pages`` only those pages, in that order."""
+        n = self.num_pages if pages is None else len(pages)
+        pool = np.full((n,) + self.shape[1:], SENTINEL[self.dtype], dtype=BITS_DTYPE[self.dtype])
+        pg, pl, ly, sl, vals = self.prefill_arrays()
+        if len(pg):
+            if pages is not None:
+                remap = np.full(self.num_pages, -1, dtype=np.int64)
+                remap[np.asarray(pages, dtype=np.int64)] = np.arange(len(pages))
+                pg = remap[pg]
+                keep = pg >= 0
+                pg, pl, ly, sl, vals = pg[keep], pl[keep], ly[keep], sl[keep], vals[keep]
+            pool[pg, pl, ly, sl] = vals
+        return pool
+
+
+@dataclass
+class Band:
+    q_col: int
+    n_q_heads: int
+    k_col: int                          # < 0: K already in the cache (in place)
+    v_col: int                          # < 0: no V
+    q_gamma: Optional[np.ndarray]       # raw bits [D] or None
+    k_gamma: Optional[np.ndarray]
+    epsilon: float
+    cache: int                          # index into Case.caches
+    q_out_row_stride: int
+
+
+@dataclass
+class Case:
+    name: str
+    op: str                             # 'store' | 'norm' | 'dual' | 'radd'
+    dtype: str
+    seed: int
+    lengths: np.ndarray                 # int64 [B]
+    offsets: np.ndarray                 # uint32 [B + 1]
+    buf: np.ndarray                     # raw bits [T, row_stride]
+    freqs: Optional[np.ndarray]         # float32 [max_seq_len, rope_dim]
+    rope_dim: int
+    interleaved: bool
+    caches: List[PagedCache]
+    layer_idx: int = 0
+    batch_offset: int = 0
+    n_q_heads: int = 0                  # store op
+    q_out_row_stride: int = 0           # store op
+    bands: List[Band] = field(default_factory=list)
+    weight_offset: float = 0.0
+    multiply_before_cast: bool = True
+
+    @property
+    def T(self) -> int:
+        return int(self.offsets[-1])
+
+    @property
+    def batch(self) -> int:
+        return int(self.lengths.shape[0])
+
+    @property
+    def row_stride(self) -> int:
+        return int(self.buf.shape[1])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.freqs.shape[0]) if self.freqs is not None else 0
+
+
+# ---------------------------------------------------------------------------
+# builders
+# ---------------------------------------------------------------------------
+
+def _offsets(lengths: np.ndarray) -> np.ndarray:
+    off = np.zeros(len(lengths) + 1, dtype=np.uint64)
+    off[1:] = np.cumsum(lengths)
+    return off.astype(np.uint32)
+
+
+def _paged_cache(seed: int, stream: int, dtype: str, Hk: int, D: int, P: int, L: int, planes: int,
+                 cache_lengths: np.ndarray, rows_needed: np.ndarray, max_pages: int,
+                 num_pages: Optional[int], slack: float) -> PagedCache:
+    """Pool + page table: sequence b takes the next ceil(rows_needed[b] / P) ids
+    of a seeded permutation of the pool; left-over table entries take the
+    remaining ids while any remain, then NO_PAGE."""
+    need = [(int(r) + P - 1) // P for r in rows_needed]
+    if max(need, default=0) > max_pages:
+        raise ValueError("max_pages_per_seq too small for the lengths drawn")
+    total = sum(need)
+    if num_pages is None:
+        num_pages = max(1, int(np.ceil(total * (1.0 + slack))))
+    if total > num_pages:
+        raise ValueError("pool too small")
+    perm = prng.permutation(seed, stream, num_pages).astype(np.uint32)
+    cb = len(rows_needed)
+    table = np.full((cb, max_pages), NO_PAGE, dtype=np.uint32)
+    k = 0
+    for b in range(cb):
+        table[b, :need[b]] = perm[k:k + need[b]]
+        k += need[b]
+    for b in range(cb):
+        for j in range(need[b], max_pages):
+            if k >= num_pages:
+                break
+            table[b, j] = perm[k]
+            k += 1
+    return PagedCache(dtype=dtype, num_kv_heads=Hk, head_dim=D, page_size=P, num_layers=L,
+                      kv_planes=planes, num_pages=num_pages,
+                      cache_lengths=np.asarray(cache_lengths, dtype=np.uint32), lookup_table=table)
+
+
+def _prefill_rows(cache: PagedCache, seed: int, stream: int, layer: int, planes, seqs,
+                  starts, counts, std: float = 1.0) -> None:
+    """N(0, std^2) into rows [start, start + count) of the given sequences."""
+    P, H, D = cache.page_size, cache.num_kv_heads, cache.head_dim
+    pos_list, seq_list = [], []
+    for s, st, cnt in zip(seqs, starts, counts):
+        pos_list.append(np.arange(int(st), int(st) + int(cnt), dtype=np.int64))
+        seq_list.append(np.full(int(cnt), int(s), dtype=np.int64))
+    pos = np.concatenate(pos_list) if pos_list else np.zeros(0, np.int64)
+    seq = np.concatenate(seq_list) if seq_list else np.zeros(0, np.int64)
+    n_rows = len(pos) * len(planes)
+    vals = to_bits(prng.normal(seed, stream, n_rows * H * D, std=std), cache.dtype)
+    vals = vals.reshape(len(planes), len(pos), H, D)
+    pages = cache.lookup_table[seq, pos // P].astype(np.int64)
+    for k, plane in enumerate(planes):
+        cache.prefill.append((pages, np.full(len(pos), plane, np.int64),
+                              np.full(len(pos), layer, np.int64), pos % P, vals[k]))
+
+
+def make_store_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq: int, Hk: int,
+                    D: int, rope_dim: int, interleaved: bool, theta: float, max_seq_len: int,
+                    P: int, L: int, layer: int, num_pages: Optional[int] = None,
+                    max_pages: Optional[int] = None, slack: float = 0.25,
+                    q_out_pad: int = 0, row_pad: int = 0, specials: bool = False) -> Case:
+    """rope_split_store_paged workload: qkv [T, (Hq + 2Hk) D (+row_pad)] N(0, 1)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cache_lengths = np.asarray(cache_lengths, dtype=np.int64)
+    rows = cache_lengths + lengths
+    if max_pages is None:
+        max_pages = max(1, (max_seq_len + P - 1) // P)
+    cache = _paged_cache(seed, S_PERM, dtype, Hk, D, P, L, 2, cache_lengths, rows, max_pages,
+                         num_pages, slack)
+    off = _offsets(lengths)
+    T = int(off[-1])
+    width = (Hq + 2 * Hk) * D
+    stride = width + row_pad
+    buf = np.zeros((T, stride), dtype=BITS_DTYPE[dtype])
+    buf[:, :width] = to_bits(prng.normal(seed, S_BUF, T * width), dtype).reshape(T, width)
+    if row_pad:
+        buf[:, width:] = SENTINEL[dtype]
+    if specials and T:
+        _inject_specials(buf, seed, dtype, Hq, Hk, D, rope_dim)
+    return Case(name=name, op="store", dtype=dtype, seed=seed, lengths=lengths, offsets=off,
+                buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta), rope_dim=rope_dim,
+                interleaved=interleaved, caches=[cache], layer_idx=layer, n_q_heads=Hq,
+                q_out_row_stride=Hq * D + q_out_pad)
+
+
+def _special_values(dtype: str) -> np.ndarray:
+    """+-0, +-inf, quiet/signalling NaNs with payloads, subnormals, extremes."""
+    if dtype == F32:
+        return np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00001, 0x7F800001,
+                         0xFFBADBAD, 0x00000001, 0x807FFFFF, 0x7F7FFFFF, 0x00800000],
+                        dtype=np.uint32)
+    return np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC1, 0x7F81, 0xFFBA, 0x0001, 0x807F,
+                     0x7F7F, 0x0080], dtype=np.uint16)
+
+
+def _inject_specials(buf, seed, dtype, Hq, Hk, D, rope_dim):
+    """Put special bit patterns into V columns and un-roped Q/K dims only."""
+    T = buf.shape[0]
+    sv = _special_values(dtype)
+    cols = [(Hq + Hk) * D + j for j in range(Hk * D)]                 # all V columns
+    for h in range(Hq + Hk):
+        cols += [h * D + j for j in range(rope_dim, D)]               # un-roped dims
+    cols = np.asarray(cols, dtype=np.int64)
+    n = max(1, (T * len(cols)) // 16)
+    pick_t = prng.integers(seed, S_SPECIAL, n, 0, T - 1)
+    pick_c = cols[prng.integers(seed, S_SPECIAL + 100, n, 0, len(cols) - 1)]
+    pick_v = sv[prng.integers(seed, S_SPECIAL + 200, n, 0, len(sv) - 1)]
+    buf[pick_t, pick_c] = pick_v
+
+
+def make_norm_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq: int, Hk: int,
+                   D: int, rope_dim: int, interleaved: bool, theta: float, max_seq_len: int,
+                   P: int, L: int, layer: int, k_in_cache: bool, q_norm: bool = True,
+                   k_norm: bool = True, eps: float = 1e-6, weight_offset: float = 0.0,
+                   multiply_before_cast: bool = True, slack: float = 0.25,
+                   gamma_std: float = 0.1) -> Case:
+    """Single-band qk_rmsnorm_rope_paged workload.  Buffer [T, (Hq+2Hk) D] =
+    Q | K | V; with ``k_in_cache`` K is prefilled in the cache and updated in
+    place (the buffer's K and V columns are then unread)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cache_lengths = np.asarray(cache_lengths, dtype=np.int64)
+    rows = cache_lengths + lengths
+    max_pages = max(1, (max_seq_len + P - 1) // P)
+    cache = _paged_cache(seed, S_PERM, dtype, Hk, D, P, L, 2, cache_lengths, rows, max_pages,
+                         None, slack)
+    off = _offsets(lengths)
+    T = int(off[-1])
+    width = (Hq + 2 * Hk) * D
+    buf = to_bits(prng.normal(seed, S_BUF, T * width), dtype).reshape(T, width)
+    if k_in_cache:
+        _prefill_rows(cache, seed, S_PREFILL, layer, [0], range(len(lengths)), cache_lengths,
+                      lengths)
+    g = to_bits(prng.normal(seed, S_GAMMA, 2 * D, mean=1.0, std=gamma_std), dtype).reshape(2, D)
+    band = Band(q_col=0, n_q_heads=Hq, k_col=-1 if k_in_cache else Hq * D,
+                v_col=-1 if k_in_cache else (Hq + Hk) * D,
+                q_gamma=g[0] if q_norm else None, k_gamma=g[1] if k_norm else None,
+                epsilon=eps, cache=0, q_out_row_stride=Hq * D)
+    return Case(name=name, op="norm", dtype=dtype, seed=seed, lengths=lengths, offsets=off,
+                buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta), rope_dim=rope_dim,
+                interleaved=interleaved, caches=[cache], layer_idx=layer, bands=[band],
+                weight_offset=weight_offset, multiply_before_cast=multiply_before_cast)
+
+
+def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_main: int,
+                   Hq_index: int, D: int, rope_dim: int, interleaved: bool, theta: float,
+                   max_seq_len: int, P_main: int, P_index: int, eps_main: float = 1e-6,
+                   eps_index: float = 1e-6, weight_offset: float = 0.0,
+                   multiply_before_cast: bool = True, slack: float = 0.25,
+                   cache_lengths=None) -> Case:
+    """Dual-band workload: buffer [T, (Hq_main + 2 Hk_main + Hq_index) D] =
+    Q-main | K-main | V-main | Q-index; both bands' K caches updated in place."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    B = len(lengths)
+    cl = np.zeros(B, dtype=np.int64) if cache_lengths is None else np.asarray(cache_lengths,
+                                                                             dtype=np.int64)
+    rows = cl + lengths
+    mp_main = max(1, (max_seq_len + P_main - 1) // P_main)
+    mp_index = max(1, (max_seq_len + P_index - 1) // P_index)
+    main = _paged_cache(seed, S_PERM, dtype, Hk_main, D, P_main, 1, 2, cl, rows, mp_main, None,
+                        slack)
+    index = _paged_cache(seed, S_PERM + 1000, dtype, 1, D, P_index, 1, 1, cl, rows, mp_index, None,
+                         slack)
+    off = _offsets(lengths)
+    T = int(off[-1])
+    width = (Hq_main + 2 * Hk_main + Hq_index) * D
+    buf = to_bits(prng.normal(seed, S_BUF, T * width), dtype).reshape(T, width)
+    _prefill_rows(main, seed, S_PREFILL, 0, [0], range(B), cl, lengths)
+    _prefill_rows(index, seed, S_PREFILL + 1000, 0, [0], range(B), cl, lengths)
+    g = to_bits(prng.normal(seed, S_GAMMA, 4 * D, mean=1.0, std=0.1), dtype).reshape(4, D)
+    main_band = Band(q_col=0, n_q_heads=Hq_main, k_col=-1, v_col=-1, q_gamma=g[0], k_gamma=g[1],
+                     epsilon=eps_main, cache=0, q_out_row_stride=Hq_main * D)
+    index_band = Band(q_col=(Hq_main + 2 * Hk_main) * D, n_q_heads=Hq_index, k_col=-1, v_col=-1,
+                      q_gamma=g[2], k_gamma=g[3], epsilon=eps_index, cache=1,
+                      q_out_row_stride=Hq_index * D)
+    return Case(name=name, op="dual", dtype=dtype, seed=seed, lengths=lengths, offsets=off,
+                buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta), rope_dim=rope_dim,
+                interleaved=interleaved, caches=[main, index], layer_idx=0,
+                bands=[main_band, index_band], weight_offset=weight_offset,
+                multiply_before_cast=multiply_before_cast)
+
+
+def make_radd_case(name: str, seed: int, dtype: str, lengths, cache_lengths, batch_offset: int,
+                   Hk: int, D: int, P: int, L: int, layer: int, a_std: float = 0.02,
+                   slack: float = 0.25, a_values: Optional[np.ndarray] = None) -> Case:
+    """kv_cache_radd workload: a [T, 2 Hk D] N(0, a_std^2) added into rows
+    [cache_len, cache_len + len) of cache sequences batch_offset + b, which
+    hold N(0, 1) before the call."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cache_lengths = np.asarray(cache_lengths, dtype=np.int64)
+    B = len(lengths)
+    cb = len(cache_lengths)
+    if batch_offset + B > cb:
+        raise ValueError("batch_offset + batch exceeds the cache batch")
+    rows = np.zeros(cb, dtype=np.int64)
+    active = np.arange(batch_offset, batch_offset + B)
+    rows[active] = cache_lengths[active] + lengths
+    max_pages = max(1, int((rows.max() + P - 1) // P))
+    cache = _paged_cache(seed, S_PERM, dtype, Hk, D, P, L, 2, cache_lengths, rows, max_pages,
+                         None, slack)
+    off = _offsets(lengths)
+    T = int(off[-1])
+    width = 2 * Hk * D
+    if a_values is None:
+        buf = to_bits(prng.normal(seed, S_A, T * width, std=a_std), dtype).reshape(T, width)
+    else:
+        buf = np.asarray(a_values).reshape(T, width)
+    _prefill_rows(cache, seed, S_PREFILL, layer, [0, 1], active, cache_lengths[active], lengths)
+    return Case(name=name, op="radd", dtype=dtype, seed=seed, lengths=lengths, offsets=off,
+                buf=buf, freqs=None, rope_dim=0, interleaved=True, caches=[cache],
+                layer_idx=layer, batch_offset=batch_offset)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+def c1(seed: int = 1) -> Case:
+    return make_store_case("c1_tiny_fp32", seed, F32, [3, 5], [0, 4], Hq=4, Hk=2, D=64,
+                           rope_dim=64, interleaved=True, theta=1e4, max_seq_len=64, P=16, L=1,
+                           layer=0, num_pages=8, max_pages=4)
+
+
+def c2(seed: int = 2, small: bool = False) -> Case:
+    if small:
+        B = 4
+        lens = prng.integers(seed, S_LENS, B, 1, 300)
+        return make_store_case("c2_prefill_small", seed, BF16, lens, np.zeros(B, np.int64), Hq=32,
+                               Hk=8, D=128, rope_dim=128, interleaved=False, theta=5e5,
+                               max_seq_len=8192, P=128, L=4, layer=2)
+    B = 8
+    lens = prng.integers(seed, S_LENS, B, 128, 2048)
+    return make_store_case("c2_prefill", seed, BF16, lens, np.zeros(B, np.int64), Hq=32, Hk=8,
+                           D=128, rope_dim=128, interleaved=False, theta=5e5, max_seq_len=8192,
+                           P=128, L=32, layer=17)
+
+
+def c3(seed: int = 3, small: bool = False) -> Case:
+    B = 32 if small else 256
+    lens = np.ones(B, dtype=np.int64)
+    clen = prng.integers(seed, S_CLEN, B, 0, 8191)
+    return make_store_case("c3_decode_small" if small else "c3_decode", seed, BF16, lens, clen,
+                           Hq=32, Hk=8, D=128, rope_dim=128, interleaved=True, theta=5e5,
+                           max_seq_len=8192, P=128, L=1, layer=0,
+                           num_pages=1400 if small else 20000, max_pages=64)
+
+
+def c4(seed: int = 4, small: bool = False) -> Case:
+    B = 4 if small else 16
+    lens = prng.integers(seed, S_LENS, B, 1, 150 if small else 1024)
+    return make_dual_case("c4_dual_small" if small else "c4_dual", seed, BF16, lens, Hq_main=64,
+                          Hk_main=8, Hq_index=16, D=128, rope_dim=64, interleaved=True,
+                          theta=1e4, max_seq_len=8192, P_main=64, P_index=64)
+
+
+def c5(seed: int = 5, small: bool = False) -> Case:
+    if small:
+        B, cb, boff = 6, 12, 4
+        lens = prng.integers(seed, S_LENS, B, 1, 64)
+        clen = prng.integers(seed, S_CLEN, cb, 0, 600)
+    else:
+        B, cb, boff = 32, 64, 4
+        lens = prng.integers(seed, S_LENS, B, 16, 512)
+        clen = prng.integers(seed, S_CLEN, cb, 0, 4096)
+    return make_radd_case("c5_radd_small" if small else "c5_radd", seed, BF16, lens, clen, boff,
+                          Hk=8, D=128, P=128, L=4, layer=3)
+
+
+CONFIGS = {"c1": c1, "c2": c2, "c3": c3, "c4": c4, "c5": c5}

@@ -1,0 +1,100 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each mutation plants one mistake in a temporary copy of the oracle's C
+source (a flipped sign, a wrong pair index, epsilon outside the root, a
+dropped cache length, a transposed page/slot, ...), builds it on the CPU,
+points the oracle adapter at it and runs the pin tests: at least one pin
+must fail for every mutant.  Nothing here touches a GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTATIONS = {
+    "rotation_sign": ("y[j0] = re * c - im * s;", "y[j0] = re * c + im * s;"),
+    "rotation_imag": ("y[j1] = re * s + im * c;", "y[j1] = im * c - re * s;"),
+    "cos_sin_swapped": ("double c = (double)row[2 * i];", "double c = (double)row[2 * i + 1];"),
+    "half_split_partner": ("uint32_t j1 = interleaved ? 2 * i + 1 : i + R / 2;",
+                           "uint32_t j1 = interleaved ? 2 * i + 1 : i + D / 2;"),
+    "interleaved_freq_index": ("const float* row = freqs + (uint64_t)pos * R;",
+                               "const float* row = freqs + (uint64_t)pos * D;"),
+    "position_ignores_cache_len": ("uint64_t pos = (uint64_t)c->cache_lengths[cseq] + (t - off[b]);",
+                                   "uint64_t pos = (uint64_t)(t - off[b]);"),
+    "position_off_by_one": ("uint64_t pos = (uint64_t)c->cache_lengths[cseq] + (t - off[b]);",
+                            "uint64_t pos = (uint64_t)c->cache_lengths[cseq] + (t - off[b]) + (t > 0);"),
+    "slot_from_page_index": ("*slot = pos % c->page_size;", "*slot = (pos / c->page_size) % c->page_size;"),
+    "v_into_k_plane": ("int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);\n      int64_t src = in_row + (int64_t)(Hq + Hk + h) * D;",
+                       "int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h) + 1;\n      int64_t src = in_row + (int64_t)(Hq + Hk + h) * D;"),
+    "layer_ignored": ("(int64_t)layer * c->layer_stride +", ""),
+    "eps_outside_root": ("double r = 1.0 / sqrt(ss / (double)D + eps);",
+                         "double r = 1.0 / (sqrt(ss / (double)D) + eps);"),
+    "norm_sum_not_mean": ("double r = 1.0 / sqrt(ss / (double)D + eps);",
+                          "double r = 1.0 / sqrt(ss + eps);"),
+    "weight_offset_dropped": ("y[j] = x[j] * r * (g + w);", "y[j] = x[j] * r * g;"),
+    "bf16_ties_away": ("double r = nearbyint(x / quantum) * quantum;",
+                       "double r = round(x / quantum) * quantum;"),
+    "bf16_truncate": ("double r = nearbyint(x / quantum) * quantum;",
+                      "double r = trunc(x / quantum) * quantum;"),
+    "bf16_no_subnormals": ("if (e < -126) e = -126;", ""),
+    "batch_offset_ignored": ("uint32_t cseq = (uint32_t)b + batch_offset;",
+                             "uint32_t cseq = (uint32_t)b;"),
+    "radd_adds_twice": ("float sum = cur + add; /* one IEEE binary32 add */",
+                        "float sum = cur + add + add;"),
+    "radd_halves_swapped": ("(int64_t)(plane * hidden)", "(int64_t)((1 - plane) * hidden)"),
+    "unroped_dims_rounded": ("if (gamma || j < R)", "if (1)"),
+}
+
+PIN_TESTS = [
+    (pins.test_bf16_rounding_golden_cases, {}),
+    (pins.test_bf16_rounding_matches_exhaustive_search, {}),
+    (pins.test_tiny_store_matches_complex_brute_force, {"interleaved": True}),
+    (pins.test_tiny_store_matches_complex_brute_force, {"interleaved": False}),
+    (pins.test_partial_rope_and_ragged_batch_brute_force, {"interleaved": True, "dtype": "bf16"}),
+    (pins.test_partial_rope_and_ragged_batch_brute_force, {"interleaved": False, "dtype": "f32"}),
+    (pins.test_unit_vectors_give_cos_sin_closed_form, {"interleaved": True}),
+    (pins.test_unit_vectors_give_cos_sin_closed_form, {"interleaved": False}),
+    (pins.test_roped_dot_product_depends_only_on_position_difference, {}),
+    (pins.test_copies_keep_every_bit_including_specials, {}),
+    (pins.test_rmsnorm_constant_vector_closed_form, {}),
+    (pins.test_rmsnorm_invariants, {}),
+    (pins.test_rmsnorm_epsilon_sits_inside_the_root, {}),
+    (pins.test_radd_is_one_binary32_add_per_element, {"dtype": "bf16"}),
+    (pins.test_radd_is_one_binary32_add_per_element, {"dtype": "f32"}),
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(oracle.SRC).read()
+    assert src.count(old) >= 1, f"mutation {name}: pattern not found"
+    mutated = src.replace(old, new)
+    c_path = tmp_path / f"{name}.c"
+    c_path.write_text(mutated)
+    (tmp_path / "qrp_oracle.h").write_text(open(os.path.join(oracle.HERE, "qrp_oracle.h")).read())
+    so = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-w",
+                    str(c_path), "-o", str(so), "-lm"], check=True)
+    return str(so)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_fails_on_mutant(name, tmp_path, monkeypatch):
+    old, new = MUTATIONS[name]
+    so = _build_mutant(tmp_path, name, old, new)
+    monkeypatch.setattr(oracle, "LIB_PATH", so)
+    monkeypatch.setattr(oracle, "_lib", None)
+    caught = []
+    for fn, kwargs in PIN_TESTS:
+        try:
+            fn(**kwargs)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(fn.__name__)
+            break
+    monkeypatch.setattr(oracle, "_lib", None)
+    assert caught, f"no pin catches mutation {name}"
