@@ -1,0 +1,248 @@
+/*
+ * qk_rope_paged.h -- C ABI of the MI355X (gfx950) ragged RoPE / split /
+ * paged-KV-store library.
+ *
+ * The operations are the ones the Modular MAX kernel documentation describes
+ * for a ragged batch right after an attention block's QKV projection:
+ *
+ *   rope_split_store_paged   "rope_split_store_paged_ragged" page
+ *   qk_rmsnorm_rope_paged    the single-band op named in the Summary of the
+ *                            "fused_dual_qk_rms_norm_rope_ragged_paged" page
+ *   dual_band                "fused_dual_qk_rms_norm_rope_ragged_paged" page
+ *   kv_cache_radd            "generic_kv_cache_radd_dispatch" page
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership    The caller allocates and owns every buffer.  The library
+ *              allocates no device memory, keeps no pointer after a call
+ *              returns and holds no global state apart from a thread-local
+ *              error string.
+ * Asynchrony   Each call checks its host-visible arguments, enqueues ONE
+ *              kernel on `stream` (a hipStream_t passed as void*; NULL is the
+ *              null stream) and returns without synchronising.
+ * Metadata     input_row_offsets, cache_lengths and lookup_table are device
+ *              arrays the library does not read on the host.  The caller
+ *              guarantees them; qrp_validate() checks them on demand.  A
+ *              token whose metadata is out of range (position >= max_seq_len,
+ *              page index >= max_pages_per_seq, page id >= num_pages,
+ *              offsets not covering it) is skipped by the kernel: nothing is
+ *              read out of bounds and nothing is written for that token.
+ * Layout       Row-major.  A head row is head_dim contiguous elements.  All
+ *              strides are in ELEMENTS.  Buffers and row/cache strides must
+ *              be 16-byte aligned (QRP_EALIGN otherwise).
+ * Rounding     Arithmetic is binary32; results are rounded to the storage
+ *              dtype with round-to-nearest-even.  Values that are only moved
+ *              (V rows, un-roped dimensions of the rope-only op) keep every
+ *              bit.  Denormals are kept.
+ * Errors       Every call returns a qrp_status; qrp_last_error() gives text
+ *              for the last failure on the calling thread.
+ * Degenerate   total_seq_len == 0 returns QRP_OK without a launch.
+ * Aliasing     Outputs must not overlap inputs or each other, except the
+ *              in-place cache updates the operation defines.  Two written
+ *              rows must not share a cache slot.
+ */
+#ifndef QK_ROPE_PAGED_H
+#define QK_ROPE_PAGED_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QRP_ABI_VERSION 1
+
+typedef enum qrp_status {
+  QRP_OK = 0,
+  QRP_EINVAL = -1,       /* null pointer, bad size or index */
+  QRP_EALIGN = -2,       /* pointer or stride not 16-byte aligned */
+  QRP_EUNSUPPORTED = -3, /* dtype / head_dim / rope_dim combination not built */
+  QRP_EGEOMETRY = -4,    /* dual band: the two bands' RoPE geometry differs */
+  QRP_EHIP = -5,         /* the HIP runtime reported an error */
+  QRP_EDATA = -6         /* qrp_validate: metadata inconsistent */
+} qrp_status;
+
+typedef enum qrp_dtype {
+  QRP_F32 = 0,
+  QRP_BF16 = 1
+} qrp_dtype;
+
+/*
+ * A paged K/V cache collection (rope_split_store_paged_ragged page, Args:
+ * kv_collection; fused_dual_qk_rms_norm_rope_ragged_paged page, signature:
+ * per-collection static params, page size and cache dtype).
+ *
+ * Element (page, plane, layer, slot, head, d) lives at
+ *   blocks + page*page_stride + plane*plane_stride + layer*layer_stride
+ *          + slot*slot_stride + head*head_stride + d
+ * Plane 0 holds K, plane 1 holds V (kv_planes == 1: a K-only cache).
+ * Sequence s (s < cache_batch) stores its position p in row p % page_size of
+ * page lookup_table[s * max_pages_per_seq + p / page_size].
+ * blocks is device memory; cache_lengths [cache_batch] and lookup_table
+ * [cache_batch * max_pages_per_seq] are device arrays of uint32.
+ */
+typedef struct qrp_paged_cache {
+  void* blocks;
+  int32_t dtype;               /* qrp_dtype; must equal the op's dtype */
+  uint32_t num_kv_heads;
+  uint32_t head_dim;           /* 64, 128 or 256 */
+  uint32_t page_size;          /* > 0 */
+  uint32_t num_layers;
+  uint32_t kv_planes;          /* 2: K and V; 1: K only */
+  uint64_t num_pages;
+  int64_t page_stride, plane_stride, layer_stride, slot_stride, head_stride;
+  const uint32_t* cache_lengths;
+  const uint32_t* lookup_table;
+  uint32_t cache_batch;
+  uint32_t max_pages_per_seq;
+} qrp_paged_cache;
+
+/*
+ * The RoPE table (rope_split_store_paged_ragged page, Args: freqs_cis;
+ * Parameters: freq_dtype, interleaved).  freqs_cis is a device array
+ * [max_seq_len][rope_dim] whose entries (2i, 2i+1) hold cos and sin of
+ * frequency i at that position.  rope_dim <= head_dim; the first rope_dim
+ * dimensions of a head are rotated and the rest pass through (the width of
+ * the table fixes rope_dim: fused_dual_qk_rms_norm_rope_ragged_paged page,
+ * Description).  interleaved != 0 pairs dims (2i, 2i+1); interleaved == 0
+ * (half-split) pairs dims (i, i + rope_dim/2).  A pair (x, y) becomes
+ * (x cos - y sin, x sin + y cos).  rope_dim must be a multiple of
+ * 16 bytes / sizeof(dtype) * 2 (16 for bf16, 8 for f32).
+ */
+typedef struct qrp_rope {
+  const void* freqs_cis;
+  int32_t freq_dtype;          /* QRP_F32 */
+  uint32_t max_seq_len;
+  uint32_t rope_dim;
+  int32_t interleaved;
+} qrp_rope;
+
+/*
+ * One band of the fused per-head RMSNorm + RoPE op
+ * (fused_dual_qk_rms_norm_rope_ragged_paged page, signature and
+ * Description: per band a cache, a gamma per role, an epsilon, a DPS output
+ * and a Q reader).  The Q reader is affine: head h of token t starts at
+ * column q_col + h*head_dim of row t of the input buffer.
+ *   k_col >= 0 : K heads are read from columns k_col.. of the buffer and
+ *                stored into the cache (V heads from v_col.. copied when
+ *                v_col >= 0);
+ *   k_col <  0 : K is already in the cache and is normalised and rotated in
+ *                place ("the respective key caches are updated in place").
+ * A NULL gamma skips the norm for that role.  The norm of a head x is
+ *   x_j / sqrt(mean(x^2) + epsilon) * (gamma_j + weight_offset)
+ * and it is applied before the rotation.
+ */
+typedef struct qrp_band {
+  uint64_t q_col;
+  uint32_t n_q_heads;
+  int64_t k_col;
+  int64_t v_col;
+  const void* q_gamma;         /* [head_dim] of dtype, device, or NULL */
+  const void* k_gamma;         /* [head_dim] of dtype, device, or NULL */
+  float epsilon;
+  const qrp_paged_cache* cache;
+  void* q_output;              /* [total_seq_len][q_out_row_stride] of dtype, device */
+  uint64_t q_out_row_stride;
+} qrp_band;
+
+/*
+ * rope_split_store_paged_ragged page (signature, Summary, Parameters, Args).
+ *
+ * qkv               device [total_seq_len][qkv_row_stride] of dtype, columns
+ *                   Q heads | K heads | V heads (n_q_heads, then
+ *                   cache->num_kv_heads twice, head_dim each).
+ * input_row_offsets device uint32 [batch_size + 1]: sequence b's new tokens
+ *                   are rows [offsets[b], offsets[b+1]); offsets[0] == 0 and
+ *                   offsets[batch_size] == total_seq_len.
+ * Token t of sequence b sits at position p = cache_lengths[b] + t - offsets[b].
+ * Q head h of token t, rotated at p, goes to q_output[t][h*head_dim ..];
+ * K heads, rotated, and V heads, copied bit for bit, go to row p of sequence
+ * b's pages at layer layer_idx.  cache_lengths are not updated.
+ * q_out_dtype must equal dtype (other output dtypes are not built).
+ */
+int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_seq_len,
+                               uint64_t qkv_row_stride, uint32_t n_q_heads,
+                               const uint32_t* input_row_offsets, uint32_t batch_size,
+                               const qrp_rope* rope, const qrp_paged_cache* cache,
+                               uint32_t layer_idx, void* q_output, int32_t q_out_dtype,
+                               uint64_t q_out_row_stride, void* stream);
+
+/*
+ * Single-band fused per-head RMSNorm + RoPE (named in the Summary of the
+ * fused_dual_qk_rms_norm_rope_ragged_paged page; semantics from its
+ * Description).  Same ragged addressing as rope_split_store_paged, through
+ * band->cache.  weight_offset is a Scalar[dtype]: it is rounded to dtype
+ * first.  multiply_before_cast != 0: y = x * r * (gamma + w) in binary32,
+ * rounded once after the rotation; == 0: n = dtype(x * r),
+ * g = dtype(gamma + w), y = dtype(n * g), then the rotation and a final
+ * rounding.
+ */
+int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq_len,
+                              uint64_t qkv_row_stride, const qrp_band* band, float weight_offset,
+                              int32_t multiply_before_cast, const uint32_t* input_row_offsets,
+                              uint32_t batch_size, const qrp_rope* rope, uint32_t layer_idx,
+                              void* stream);
+
+/*
+ * fused_dual_qk_rms_norm_rope_ragged_paged page: the main band and the index
+ * band in ONE launch over the four row groups
+ * [q_main | k_main | q_index | k_index] of each token.  Both bands read the
+ * same buffer, offsets and freqs table; each row takes its own band's cache,
+ * gamma, epsilon, output and Q columns.  The two caches must have the same
+ * dtype and head_dim (QRP_EGEOMETRY otherwise: the page requires identical
+ * RoPE geometry across the bands).  The result equals main_band's
+ * qk_rmsnorm_rope_paged call followed by index_band's.
+ */
+int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64_t buf_row_stride,
+                  const qrp_band* main_band, const qrp_band* index_band, float weight_offset,
+                  int32_t multiply_before_cast, const uint32_t* input_row_offsets,
+                  uint32_t batch_size, const qrp_rope* rope, uint32_t layer_idx, void* stream);
+
+/*
+ * generic_kv_cache_radd_dispatch page (signature, Summary, Description,
+ * Args).  a is device [total_rows][a_row_stride] of dtype; its first
+ * num_kv_heads*head_dim columns are added into the K rows and the next
+ * num_kv_heads*head_dim into the V rows of cache sequence b + batch_offset,
+ * at positions cache_lengths[b + batch_offset] + t - offsets[b], layer
+ * layer_idx.  Each element becomes dtype(float(cache) + float(a)), one
+ * binary32 add.  Requires batch_offset + batch_size <= cache_batch and
+ * kv_planes == 2.
+ */
+int32_t kv_cache_radd(const void* a, int32_t dtype, uint32_t total_rows, uint64_t a_row_stride,
+                      const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t batch_offset,
+                      const qrp_paged_cache* cache, uint32_t layer_idx, void* stream);
+
+/*
+ * Debug check of the device metadata one of the calls above would use:
+ * copies offsets, cache_lengths and lookup_table to the host (synchronising
+ * `stream`) and runs qrp_validate_host.  Returns QRP_EDATA with a message
+ * on the first inconsistency.
+ */
+int32_t qrp_validate(const uint32_t* input_row_offsets, uint32_t batch_size,
+                     uint32_t total_seq_len, uint32_t batch_offset, const qrp_paged_cache* cache,
+                     uint32_t max_seq_len, void* stream);
+
+/*
+ * The same checks on host arrays: offsets start at 0, never decrease and end
+ * at total_seq_len; batch_offset + batch_size <= cache_batch; every token's
+ * position is below max_seq_len (when max_seq_len > 0), its page index below
+ * max_pages_per_seq and its page id below num_pages; no two tokens land on
+ * the same (page, row).
+ */
+int32_t qrp_validate_host(const uint32_t* input_row_offsets, uint32_t batch_size,
+                          uint32_t total_seq_len, uint32_t batch_offset,
+                          const uint32_t* cache_lengths, const uint32_t* lookup_table,
+                          uint32_t cache_batch, uint32_t max_pages_per_seq, uint32_t page_size,
+                          uint64_t num_pages, uint32_t max_seq_len);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* qrp_last_error(void);
+
+/* QRP_ABI_VERSION of the loaded library. */
+int32_t qrp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QK_ROPE_PAGED_H */

@@ -1,0 +1,264 @@
+"""Python binding of the qk_rope_paged C ABI (include/qk_rope_paged.h).
+
+Argument marshalling only: every step of the pass runs in the HIP library
+``libqk_rope_paged.so`` that sits next to this file.  Importing the package
+fails loudly when that library is missing; there is no fallback path.
+
+Tensors are torch tensors on the GPU (any dtype whose storage holds the
+right bits: bfloat16 / int16 / uint16 for bf16 data, float32 / int32 for
+fp32).  Streams default to torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqk_rope_paged.so")
+
+QRP_OK, QRP_EINVAL, QRP_EALIGN, QRP_EUNSUPPORTED, QRP_EGEOMETRY, QRP_EHIP, QRP_EDATA = (
+    0, -1, -2, -3, -4, -5, -6)
+QRP_F32, QRP_BF16 = 0, 1
+STATUS_NAMES = {0: "QRP_OK", -1: "QRP_EINVAL", -2: "QRP_EALIGN", -3: "QRP_EUNSUPPORTED",
+                -4: "QRP_EGEOMETRY", -5: "QRP_EHIP", -6: "QRP_EDATA"}
+
+# entry points declared in include/qk_rope_paged.h
+EXPORTS = ("rope_split_store_paged", "qk_rmsnorm_rope_paged", "dual_band", "kv_cache_radd",
+           "qrp_validate", "qrp_validate_host", "qrp_last_error", "qrp_abi_version")
+
+
+class QrpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class QrpPagedCache(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_uint32), ("head_dim", ctypes.c_uint32),
+                ("page_size", ctypes.c_uint32), ("num_layers", ctypes.c_uint32),
+                ("kv_planes", ctypes.c_uint32), ("num_pages", ctypes.c_uint64),
+                ("page_stride", ctypes.c_int64), ("plane_stride", ctypes.c_int64),
+                ("layer_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64),
+                ("cache_lengths", ctypes.c_void_p), ("lookup_table", ctypes.c_void_p),
+                ("cache_batch", ctypes.c_uint32), ("max_pages_per_seq", ctypes.c_uint32)]
+
+
+class QrpRope(ctypes.Structure):
+    _fields_ = [("freqs_cis", ctypes.c_void_p), ("freq_dtype", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_uint32), ("rope_dim", ctypes.c_uint32),
+                ("interleaved", ctypes.c_int32)]
+
+
+class QrpBand(ctypes.Structure):
+    _fields_ = [("q_col", ctypes.c_uint64), ("n_q_heads", ctypes.c_uint32),
+                ("k_col", ctypes.c_int64), ("v_col", ctypes.c_int64),
+                ("q_gamma", ctypes.c_void_p), ("k_gamma", ctypes.c_void_p),
+                ("epsilon", ctypes.c_float), ("cache", ctypes.POINTER(QrpPagedCache)),
+                ("q_output", ctypes.c_void_p), ("q_out_row_stride", ctypes.c_uint64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m qk_rope_paged_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, U32, U64, I32, F = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32, ctypes.c_float
+    PC, PR, PB = ctypes.POINTER(QrpPagedCache), ctypes.POINTER(QrpRope), ctypes.POINTER(QrpBand)
+    sig = {
+        "rope_split_store_paged": [P, I32, U32, U64, U32, P, U32, PR, PC, U32, P, I32, U64, P],
+        "qk_rmsnorm_rope_paged": [P, I32, U32, U64, PB, F, I32, P, U32, PR, U32, P],
+        "dual_band": [P, I32, U32, U64, PB, PB, F, I32, P, U32, PR, U32, P],
+        "kv_cache_radd": [P, I32, U32, U64, P, U32, U32, PC, U32, P],
+        "qrp_validate": [P, U32, U32, U32, PC, U32, P],
+        "qrp_validate_host": [P, U32, U32, U32, P, P, U32, U32, U32, U64, U32],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = I32
+    lib.qrp_last_error.argtypes = []
+    lib.qrp_last_error.restype = ctypes.c_char_p
+    lib.qrp_abi_version.argtypes = []
+    lib.qrp_abi_version.restype = I32
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.qrp_last_error().decode()
+
+
+def _check(status: int, raise_on_error: bool) -> int:
+    if status != QRP_OK and raise_on_error:
+        raise QrpError(status, last_error())
+    return status
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+@dataclass
+class PagedCache:
+    """A paged K/V cache: device pool + metadata, with element strides.
+
+    ``blocks`` is the pool tensor; ``cache_lengths`` ([cache_batch]) and
+    ``lookup_table`` ([cache_batch, max_pages_per_seq]) are uint32 data held
+    in int32 tensors.  ``to_c()`` gives the C struct."""
+    blocks: object
+    dtype: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    num_layers: int
+    kv_planes: int
+    num_pages: int
+    page_stride: int
+    plane_stride: int
+    layer_stride: int
+    slot_stride: int
+    head_stride: int
+    cache_lengths: object
+    lookup_table: object
+    cache_batch: int
+    max_pages_per_seq: int
+
+    def to_c(self) -> QrpPagedCache:
+        return QrpPagedCache(
+            blocks=_ptr(self.blocks), dtype=self.dtype, num_kv_heads=self.num_kv_heads,
+            head_dim=self.head_dim, page_size=self.page_size, num_layers=self.num_layers,
+            kv_planes=self.kv_planes, num_pages=self.num_pages, page_stride=self.page_stride,
+            plane_stride=self.plane_stride, layer_stride=self.layer_stride,
+            slot_stride=self.slot_stride, head_stride=self.head_stride,
+            cache_lengths=_ptr(self.cache_lengths), lookup_table=_ptr(self.lookup_table),
+            cache_batch=self.cache_batch, max_pages_per_seq=self.max_pages_per_seq)
+
+
+@dataclass
+class Rope:
+    freqs_cis: object        # float32 [max_seq_len, rope_dim]
+    max_seq_len: int
+    rope_dim: int
+    interleaved: bool
+
+    def to_c(self) -> QrpRope:
+        return QrpRope(freqs_cis=_ptr(self.freqs_cis), freq_dtype=QRP_F32,
+                       max_seq_len=self.max_seq_len, rope_dim=self.rope_dim,
+                       interleaved=int(bool(self.interleaved)))
+
+
+@dataclass
+class Band:
+    q_col: int
+    n_q_heads: int
+    k_col: int
+    v_col: int
+    q_gamma: object
+    k_gamma: object
+    epsilon: float
+    cache: PagedCache
+    q_output: object
+    q_out_row_stride: int
+
+    def to_c(self, keep: list) -> QrpBand:
+        cc = self.cache.to_c()
+        keep.append(cc)
+        return QrpBand(q_col=self.q_col, n_q_heads=self.n_q_heads, k_col=self.k_col,
+                       v_col=self.v_col, q_gamma=_ptr(self.q_gamma), k_gamma=_ptr(self.k_gamma),
+                       epsilon=self.epsilon, cache=ctypes.pointer(cc), q_output=_ptr(self.q_output),
+                       q_out_row_stride=self.q_out_row_stride)
+
+
+def rope_split_store_paged(qkv, dtype: int, total_seq_len: int, qkv_row_stride: int,
+                           n_q_heads: int, input_row_offsets, batch_size: int, rope: Rope,
+                           cache: PagedCache, layer_idx: int, q_output, q_out_dtype: int,
+                           q_out_row_stride: int, stream=None, raise_on_error: bool = True) -> int:
+    cr, cc = rope.to_c(), cache.to_c()
+    st = lib.rope_split_store_paged(_ptr(qkv), dtype, total_seq_len, qkv_row_stride, n_q_heads,
+                                    _ptr(input_row_offsets), batch_size, ctypes.byref(cr),
+                                    ctypes.byref(cc), layer_idx, _ptr(q_output), q_out_dtype,
+                                    q_out_row_stride, _stream(stream))
+    return _check(st, raise_on_error)
+
+
+def qk_rmsnorm_rope_paged(qkv, dtype: int, total_seq_len: int, qkv_row_stride: int, band: Band,
+                          weight_offset: float, multiply_before_cast: bool, input_row_offsets,
+                          batch_size: int, rope: Rope, layer_idx: int, stream=None,
+                          raise_on_error: bool = True) -> int:
+    keep: list = []
+    cb, cr = band.to_c(keep), rope.to_c()
+    st = lib.qk_rmsnorm_rope_paged(_ptr(qkv), dtype, total_seq_len, qkv_row_stride,
+                                   ctypes.byref(cb), weight_offset, int(bool(multiply_before_cast)),
+                                   _ptr(input_row_offsets), batch_size, ctypes.byref(cr), layer_idx,
+                                   _stream(stream))
+    return _check(st, raise_on_error)
+
+
+def dual_band(buf, dtype: int, total_seq_len: int, buf_row_stride: int, main_band: Band,
+              index_band: Band, weight_offset: float, multiply_before_cast: bool,
+              input_row_offsets, batch_size: int, rope: Rope, layer_idx: int, stream=None,
+              raise_on_error: bool = True) -> int:
+    keep: list = []
+    cm, ci, cr = main_band.to_c(keep), index_band.to_c(keep), rope.to_c()
+    st = lib.dual_band(_ptr(buf), dtype, total_seq_len, buf_row_stride, ctypes.byref(cm),
+                       ctypes.byref(ci), weight_offset, int(bool(multiply_before_cast)),
+                       _ptr(input_row_offsets), batch_size, ctypes.byref(cr), layer_idx,
+                       _stream(stream))
+    return _check(st, raise_on_error)
+
+
+def kv_cache_radd(a, dtype: int, total_rows: int, a_row_stride: int, input_row_offsets,
+                  batch_size: int, batch_offset: int, cache: PagedCache, layer_idx: int,
+                  stream=None, raise_on_error: bool = True) -> int:
+    cc = cache.to_c()
+    st = lib.kv_cache_radd(_ptr(a), dtype, total_rows, a_row_stride, _ptr(input_row_offsets),
+                           batch_size, batch_offset, ctypes.byref(cc), layer_idx, _stream(stream))
+    return _check(st, raise_on_error)
+
+
+def qrp_validate(input_row_offsets, batch_size: int, total_seq_len: int, batch_offset: int,
+                 cache: PagedCache, max_seq_len: int, stream=None,
+                 raise_on_error: bool = False) -> int:
+    cc = cache.to_c()
+    st = lib.qrp_validate(_ptr(input_row_offsets), batch_size, total_seq_len, batch_offset,
+                          ctypes.byref(cc), max_seq_len, _stream(stream))
+    return _check(st, raise_on_error)
+
+
+def qrp_validate_host(offsets, batch_size: int, total_seq_len: int, batch_offset: int,
+                      cache_lengths, lookup_table, cache_batch: int, max_pages_per_seq: int,
+                      page_size: int, num_pages: int, max_seq_len: int) -> int:
+    """Host-array form; numpy uint32 arrays."""
+    import numpy as np
+
+    off = np.ascontiguousarray(offsets, dtype=np.uint32)
+    lens = np.ascontiguousarray(cache_lengths, dtype=np.uint32)
+    tab = np.ascontiguousarray(lookup_table, dtype=np.uint32)
+    return lib.qrp_validate_host(off.ctypes.data, batch_size, total_seq_len, batch_offset,
+                                 lens.ctypes.data, tab.ctypes.data, cache_batch,
+                                 max_pages_per_seq, page_size, num_pages, max_seq_len)
+
+
+def abi_version() -> int:
+    return lib.qrp_abi_version()

@@ -1,0 +1,472 @@
+// abi.cpp -- the library's extern "C" entry points: argument checks, the
+// launch descriptor of the band engine, and the metadata validator.
+//
+// Each entry point checks what it can see on the host (pointers, sizes,
+// alignment, dtype and geometry), turns the call into at most four row
+// segments per token and enqueues one kernel on the caller's stream.  Device
+// metadata (offsets, cache lengths, page tables) is never read here; the
+// kernel skips tokens whose metadata is out of range and qrp_validate()
+// reports it.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "engine.hpp"
+#include "qk_rope_paged.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+uint32_t elem_bytes(int32_t dt) { return dt == QRP_F32 ? 4u : 2u; }
+uint32_t chunk_elems(int32_t dt) { return 16u / elem_bytes(dt); }
+bool dtype_ok(int32_t dt) { return dt == QRP_F32 || dt == QRP_BF16; }
+
+// binary32 -> nearest-even bf16 -> binary32 (weight_offset is a Scalar[dtype])
+float to_dtype(int32_t dt, float v) {
+  if (dt == QRP_F32) return v;
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
+    u = (u | 0x00400000u) & 0xFFFF0000u;
+  } else {
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+  }
+  std::memcpy(&v, &u, 4);
+  return v;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+int32_t check_cache(const qrp_paged_cache* c, int32_t dtype, uint32_t layer_idx, const char* what) {
+  const std::string w(what);
+  if (!c) return fail(QRP_EINVAL, w + ": cache is NULL");
+  if (!c->blocks || !c->cache_lengths || !c->lookup_table)
+    return fail(QRP_EINVAL, w + ": blocks, cache_lengths and lookup_table must be non-NULL");
+  if (c->dtype != dtype) return fail(QRP_EUNSUPPORTED, w + ": cache dtype differs from the op dtype");
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+    return fail(QRP_EUNSUPPORTED, w + ": head_dim must be 64, 128 or 256");
+  if (c->num_kv_heads == 0 || c->page_size == 0 || c->num_pages == 0 || c->cache_batch == 0 ||
+      c->max_pages_per_seq == 0)
+    return fail(QRP_EINVAL, w + ": num_kv_heads, page_size, num_pages, cache_batch and "
+                                "max_pages_per_seq must be positive");
+  if (c->kv_planes != 1 && c->kv_planes != 2) return fail(QRP_EINVAL, w + ": kv_planes must be 1 or 2");
+  if (layer_idx >= c->num_layers) return fail(QRP_EINVAL, w + ": layer_idx >= num_layers");
+  if (!aligned16(c->blocks)) return fail(QRP_EALIGN, w + ": blocks not 16-byte aligned");
+  const int64_t ce = chunk_elems(dtype);
+  const int64_t st[5] = {c->page_stride, c->plane_stride, c->layer_stride, c->slot_stride,
+                         c->head_stride};
+  for (int64_t s : st) {
+    if (s < 0) return fail(QRP_EINVAL, w + ": negative cache stride");
+    if (s % ce) return fail(QRP_EALIGN, w + ": cache strides must be multiples of 16 bytes");
+  }
+  if ((reinterpret_cast<uintptr_t>(c->cache_lengths) | reinterpret_cast<uintptr_t>(c->lookup_table)) & 3u)
+    return fail(QRP_EALIGN, w + ": cache_lengths / lookup_table not 4-byte aligned");
+  return QRP_OK;
+}
+
+int32_t check_rope(const qrp_rope* r, int32_t dtype, uint32_t head_dim) {
+  if (!r || !r->freqs_cis) return fail(QRP_EINVAL, "rope / freqs_cis is NULL");
+  if (r->freq_dtype != QRP_F32) return fail(QRP_EUNSUPPORTED, "freqs_cis must be float32");
+  if (!aligned16(r->freqs_cis)) return fail(QRP_EALIGN, "freqs_cis not 16-byte aligned");
+  if (r->max_seq_len == 0) return fail(QRP_EINVAL, "max_seq_len must be positive");
+  if (r->rope_dim == 0 || r->rope_dim > head_dim || r->rope_dim % 2)
+    return fail(QRP_EINVAL, "rope_dim must be even, positive and <= head_dim");
+  if (r->rope_dim % (2 * chunk_elems(dtype)))
+    return fail(QRP_EUNSUPPORTED, "rope_dim must be a multiple of 32 bytes of dtype");
+  return QRP_OK;
+}
+
+qrp::CacheDesc make_cache(const qrp_paged_cache* c, uint32_t layer_idx) {
+  qrp::CacheDesc d{};
+  d.blocks = c->blocks;
+  d.page_stride = c->page_stride;
+  d.plane_stride = c->plane_stride;
+  d.slot_stride = c->slot_stride;
+  d.head_stride = c->head_stride;
+  d.layer_off = (int64_t)layer_idx * c->layer_stride;
+  d.cache_lengths = c->cache_lengths;
+  d.table = c->lookup_table;
+  d.num_pages = c->num_pages;
+  d.max_pages = c->max_pages_per_seq;
+  d.page_size = c->page_size;
+  d.page_shift = 0xFFFFFFFFu;
+  if ((c->page_size & (c->page_size - 1)) == 0) {
+    uint32_t s = 0;
+    while ((1u << s) < c->page_size) ++s;
+    d.page_shift = s;
+  }
+  d.cache_batch = c->cache_batch;
+  return d;
+}
+
+struct Builder {
+  qrp::BandArgs a{};
+  int32_t dtype = QRP_BF16;
+  uint32_t head_dim = 0;
+  uint32_t rpp = 0;
+
+  void add_seg(qrp::SegKind kind, const void* src, int64_t src_stride, void* dst, int64_t dst_stride,
+               const void* gamma, float eps, uint32_t n_heads, uint32_t cache, uint32_t plane) {
+    if (n_heads == 0) return;
+    qrp::SegDesc& s = a.seg[a.nseg];
+    s.src = src;
+    s.dst = dst;
+    s.gamma = gamma;
+    s.src_row_stride = src_stride;
+    s.dst_row_stride = dst_stride;
+    s.eps = eps;
+    s.n_heads = n_heads;
+    s.kind = kind;
+    s.cache = cache;
+    s.plane = plane;
+    s.pass_begin = a.passes_per_token;
+    s.n_passes = (n_heads + rpp - 1) / rpp;
+    a.passes_per_token += s.n_passes;
+    ++a.nseg;
+  }
+
+  // split tokens x passes into waves and blocks
+  int32_t finish(uint32_t total_tokens, bool radd) {
+    const uint32_t npmax = radd ? 4u : 6u;
+    const uint32_t ppt = a.passes_per_token;
+    uint32_t ppg = std::min<uint32_t>(npmax, ppt);
+    const int forced = env_int("QRP_PASSES_PER_WAVE", 0);
+    if (forced > 0) {
+      ppg = std::min<uint32_t>((uint32_t)forced, std::min(npmax, ppt));
+    } else {
+      // enough waves to cover every SIMD a few times over: shrink the group
+      const uint64_t want = 4096;
+      while (ppg > 1 && (uint64_t)total_tokens * ((ppt + ppg - 1) / ppg) < want) --ppg;
+    }
+    a.passes_per_group = ppg;
+    a.groups_per_token = (ppt + ppg - 1) / ppg;
+    const uint64_t items = (uint64_t)total_tokens * a.groups_per_token;
+    if (items >= (1ull << 31)) return fail(QRP_EINVAL, "batch too large for one launch");
+    a.n_items = (uint32_t)items;
+    a.n_blocks = (uint32_t)((items + qrp::kWavesPerBlock - 1) / qrp::kWavesPerBlock);
+    a.per_xcd = env_int("QRP_XCD_REMAP", 1) ? (a.n_blocks + qrp::kXcds - 1) / qrp::kXcds : 0;
+    a.total_tokens = total_tokens;
+    a.guess_mul = (((uint64_t)a.batch) << 32) / total_tokens;
+    return QRP_OK;
+  }
+};
+
+int32_t launch(const Builder& b, bool interleaved, bool radd, void* stream) {
+  const int e = qrp::launch_band(b.a, b.dtype, b.head_dim, interleaved, radd, stream);
+  if (e != 0)
+    return fail(QRP_EHIP, std::string("kernel launch failed: ") +
+                               hipGetErrorString(static_cast<hipError_t>(e)));
+  return QRP_OK;
+}
+
+const char* elem_ptr(const void* base, uint64_t elems, int32_t dt) {
+  return static_cast<const char*>(base) + elems * elem_bytes(dt);
+}
+
+int32_t check_batch(const uint32_t* offsets, uint32_t T, uint32_t B) {
+  if (!offsets) return fail(QRP_EINVAL, "input_row_offsets is NULL");
+  if (B == 0) return fail(QRP_EINVAL, "batch_size is 0 with total_seq_len > 0");
+  if (reinterpret_cast<uintptr_t>(offsets) & 3u) return fail(QRP_EALIGN, "input_row_offsets not 4-byte aligned");
+  (void)T;
+  return QRP_OK;
+}
+
+int32_t check_band(const qrp_band* band, int32_t dtype, uint64_t row_stride, uint32_t layer_idx,
+                   const char* what) {
+  const std::string w(what);
+  if (!band) return fail(QRP_EINVAL, w + " is NULL");
+  int32_t st = check_cache(band->cache, dtype, layer_idx, what);
+  if (st) return st;
+  const uint64_t D = band->cache->head_dim, Hk = band->cache->num_kv_heads;
+  const uint32_t ce = chunk_elems(dtype);
+  if (band->n_q_heads) {
+    if (!band->q_output) return fail(QRP_EINVAL, w + ": q_output is NULL");
+    if (!aligned16(band->q_output)) return fail(QRP_EALIGN, w + ": q_output not 16-byte aligned");
+    if (band->q_out_row_stride % ce) return fail(QRP_EALIGN, w + ": q_out_row_stride not a multiple of 16 bytes");
+    if (band->q_out_row_stride < band->n_q_heads * D) return fail(QRP_EINVAL, w + ": q_out_row_stride < n_q_heads * head_dim");
+    if (band->q_col % ce) return fail(QRP_EALIGN, w + ": q_col not a multiple of 16 bytes");
+    if (band->q_col + band->n_q_heads * D > row_stride) return fail(QRP_EINVAL, w + ": Q columns exceed the row");
+  }
+  if (band->k_col >= 0) {
+    if ((uint64_t)band->k_col % ce) return fail(QRP_EALIGN, w + ": k_col not a multiple of 16 bytes");
+    if ((uint64_t)band->k_col + Hk * D > row_stride) return fail(QRP_EINVAL, w + ": K columns exceed the row");
+  }
+  if (band->v_col >= 0) {
+    if (band->k_col < 0) return fail(QRP_EINVAL, w + ": v_col needs k_col >= 0");
+    if (band->cache->kv_planes != 2) return fail(QRP_EINVAL, w + ": v_col needs a cache with a V plane");
+    if ((uint64_t)band->v_col % ce) return fail(QRP_EALIGN, w + ": v_col not a multiple of 16 bytes");
+    if ((uint64_t)band->v_col + Hk * D > row_stride) return fail(QRP_EINVAL, w + ": V columns exceed the row");
+  }
+  if ((band->q_gamma && !aligned16(band->q_gamma)) || (band->k_gamma && !aligned16(band->k_gamma)))
+    return fail(QRP_EALIGN, w + ": gamma not 16-byte aligned");
+  return QRP_OK;
+}
+
+void add_band(Builder& b, const qrp_band* band, const void* buf, uint64_t row_stride, int32_t dtype,
+              uint32_t cache_slot) {
+  const uint64_t D = band->cache->head_dim;
+  const uint32_t Hk = band->cache->num_kv_heads;
+  b.add_seg(qrp::SEG_Q, elem_ptr(buf, band->q_col, dtype), (int64_t)row_stride, band->q_output,
+            (int64_t)band->q_out_row_stride, band->q_gamma, band->epsilon, band->n_q_heads, cache_slot, 0);
+  if (band->k_col >= 0)
+    b.add_seg(qrp::SEG_K_BUF, elem_ptr(buf, (uint64_t)band->k_col, dtype), (int64_t)row_stride,
+              nullptr, 0, band->k_gamma, band->epsilon, Hk, cache_slot, 0);
+  else
+    b.add_seg(qrp::SEG_K_INPLACE, nullptr, 0, nullptr, 0, band->k_gamma, band->epsilon, Hk,
+              cache_slot, 0);
+  if (band->v_col >= 0)
+    b.add_seg(qrp::SEG_V_COPY, elem_ptr(buf, (uint64_t)band->v_col, dtype), (int64_t)row_stride,
+              nullptr, 0, nullptr, 0.f, Hk, cache_slot, 1);
+  (void)D;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qrp_last_error(void) { return g_err.c_str(); }
+
+int32_t qrp_abi_version(void) { return QRP_ABI_VERSION; }
+
+int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_seq_len,
+                               uint64_t qkv_row_stride, uint32_t n_q_heads,
+                               const uint32_t* input_row_offsets, uint32_t batch_size,
+                               const qrp_rope* rope, const qrp_paged_cache* cache,
+                               uint32_t layer_idx, void* q_output, int32_t q_out_dtype,
+                               uint64_t q_out_row_stride, void* stream) {
+  g_err.clear();
+  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32 or QRP_BF16");
+  if (q_out_dtype != dtype) return fail(QRP_EUNSUPPORTED, "q_out_dtype must equal dtype");
+  if (total_seq_len == 0) return QRP_OK;
+  int32_t st;
+  if ((st = check_batch(input_row_offsets, total_seq_len, batch_size))) return st;
+  if ((st = check_cache(cache, dtype, layer_idx, "cache"))) return st;
+  if (cache->kv_planes != 2) return fail(QRP_EINVAL, "cache needs K and V planes");
+  if ((st = check_rope(rope, dtype, cache->head_dim))) return st;
+  if (!qkv || !q_output) return fail(QRP_EINVAL, "qkv / q_output is NULL");
+  if (n_q_heads == 0) return fail(QRP_EINVAL, "n_q_heads is 0");
+  if (!aligned16(qkv) || !aligned16(q_output)) return fail(QRP_EALIGN, "qkv / q_output not 16-byte aligned");
+  const uint32_t ce = chunk_elems(dtype);
+  if (qkv_row_stride % ce || q_out_row_stride % ce)
+    return fail(QRP_EALIGN, "row strides must be multiples of 16 bytes");
+  const uint64_t D = cache->head_dim, Hk = cache->num_kv_heads;
+  if (qkv_row_stride < (n_q_heads + 2 * Hk) * D) return fail(QRP_EINVAL, "qkv_row_stride < q_dim + k_dim + v_dim");
+  if (q_out_row_stride < n_q_heads * D) return fail(QRP_EINVAL, "q_out_row_stride < q_dim");
+  if (batch_size > cache->cache_batch) return fail(QRP_EINVAL, "batch_size > cache_batch");
+
+  Builder b;
+  b.dtype = dtype;
+  b.head_dim = cache->head_dim;
+  b.rpp = qrp::rows_per_pass(dtype, cache->head_dim);
+  b.a.cache[0] = make_cache(cache, layer_idx);
+  b.a.ncache = 1;
+  b.a.offsets = input_row_offsets;
+  b.a.batch = batch_size;
+  b.a.batch_offset = 0;
+  b.a.freqs = static_cast<const float*>(rope->freqs_cis);
+  b.a.rope_dim = rope->rope_dim;
+  b.a.max_seq_len = rope->max_seq_len;
+  b.a.multiply_before_cast = 1;
+  b.add_seg(qrp::SEG_Q, qkv, (int64_t)qkv_row_stride, q_output, (int64_t)q_out_row_stride, nullptr,
+            0.f, n_q_heads, 0, 0);
+  b.add_seg(qrp::SEG_K_BUF, elem_ptr(qkv, n_q_heads * D, dtype), (int64_t)qkv_row_stride, nullptr,
+            0, nullptr, 0.f, (uint32_t)Hk, 0, 0);
+  b.add_seg(qrp::SEG_V_COPY, elem_ptr(qkv, (n_q_heads + Hk) * D, dtype), (int64_t)qkv_row_stride,
+            nullptr, 0, nullptr, 0.f, (uint32_t)Hk, 0, 1);
+  if ((st = b.finish(total_seq_len, false))) return st;
+  return launch(b, rope->interleaved != 0, false, stream);
+}
+
+int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq_len,
+                              uint64_t qkv_row_stride, const qrp_band* band, float weight_offset,
+                              int32_t multiply_before_cast, const uint32_t* input_row_offsets,
+                              uint32_t batch_size, const qrp_rope* rope, uint32_t layer_idx,
+                              void* stream) {
+  g_err.clear();
+  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32 or QRP_BF16");
+  if (total_seq_len == 0) return QRP_OK;
+  int32_t st;
+  if ((st = check_batch(input_row_offsets, total_seq_len, batch_size))) return st;
+  if (!qkv) return fail(QRP_EINVAL, "qkv is NULL");
+  if (!aligned16(qkv)) return fail(QRP_EALIGN, "qkv not 16-byte aligned");
+  if (qkv_row_stride % chunk_elems(dtype)) return fail(QRP_EALIGN, "qkv_row_stride not a multiple of 16 bytes");
+  if ((st = check_band(band, dtype, qkv_row_stride, layer_idx, "band"))) return st;
+  if ((st = check_rope(rope, dtype, band->cache->head_dim))) return st;
+  if (batch_size > band->cache->cache_batch) return fail(QRP_EINVAL, "batch_size > cache_batch");
+
+  Builder b;
+  b.dtype = dtype;
+  b.head_dim = band->cache->head_dim;
+  b.rpp = qrp::rows_per_pass(dtype, b.head_dim);
+  b.a.cache[0] = make_cache(band->cache, layer_idx);
+  b.a.ncache = 1;
+  b.a.offsets = input_row_offsets;
+  b.a.batch = batch_size;
+  b.a.freqs = static_cast<const float*>(rope->freqs_cis);
+  b.a.rope_dim = rope->rope_dim;
+  b.a.max_seq_len = rope->max_seq_len;
+  b.a.weight_offset = to_dtype(dtype, weight_offset);
+  b.a.multiply_before_cast = multiply_before_cast != 0;
+  add_band(b, band, qkv, qkv_row_stride, dtype, 0);
+  if ((st = b.finish(total_seq_len, false))) return st;
+  return launch(b, rope->interleaved != 0, false, stream);
+}
+
+int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64_t buf_row_stride,
+                  const qrp_band* main_band, const qrp_band* index_band, float weight_offset,
+                  int32_t multiply_before_cast, const uint32_t* input_row_offsets,
+                  uint32_t batch_size, const qrp_rope* rope, uint32_t layer_idx, void* stream) {
+  g_err.clear();
+  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32 or QRP_BF16");
+  if (!main_band || !index_band || !main_band->cache || !index_band->cache)
+    return fail(QRP_EINVAL, "bands and their caches must be non-NULL");
+  if (main_band->cache->dtype != index_band->cache->dtype ||
+      main_band->cache->head_dim != index_band->cache->head_dim)
+    return fail(QRP_EGEOMETRY, "main and index bands differ in cache dtype or head_dim");
+  if (total_seq_len == 0) return QRP_OK;
+  int32_t st;
+  if ((st = check_batch(input_row_offsets, total_seq_len, batch_size))) return st;
+  if (!buf) return fail(QRP_EINVAL, "buffer is NULL");
+  if (!aligned16(buf)) return fail(QRP_EALIGN, "buffer not 16-byte aligned");
+  if (buf_row_stride % chunk_elems(dtype)) return fail(QRP_EALIGN, "buf_row_stride not a multiple of 16 bytes");
+  if ((st = check_band(main_band, dtype, buf_row_stride, layer_idx, "main_band"))) return st;
+  if ((st = check_band(index_band, dtype, buf_row_stride, layer_idx, "index_band"))) return st;
+  if (main_band->v_col >= 0 || index_band->v_col >= 0)
+    return fail(QRP_EUNSUPPORTED, "dual_band carries no V rows (v_col must be < 0)");
+  if ((st = check_rope(rope, dtype, main_band->cache->head_dim))) return st;
+  if (batch_size > main_band->cache->cache_batch || batch_size > index_band->cache->cache_batch)
+    return fail(QRP_EINVAL, "batch_size > cache_batch");
+
+  Builder b;
+  b.dtype = dtype;
+  b.head_dim = main_band->cache->head_dim;
+  b.rpp = qrp::rows_per_pass(dtype, b.head_dim);
+  b.a.cache[0] = make_cache(main_band->cache, layer_idx);
+  b.a.cache[1] = make_cache(index_band->cache, layer_idx);
+  b.a.ncache = 2;
+  b.a.offsets = input_row_offsets;
+  b.a.batch = batch_size;
+  b.a.freqs = static_cast<const float*>(rope->freqs_cis);
+  b.a.rope_dim = rope->rope_dim;
+  b.a.max_seq_len = rope->max_seq_len;
+  b.a.weight_offset = to_dtype(dtype, weight_offset);
+  b.a.multiply_before_cast = multiply_before_cast != 0;
+  // rows [q_main | k_main | q_index | k_index]
+  add_band(b, main_band, buf, buf_row_stride, dtype, 0);
+  add_band(b, index_band, buf, buf_row_stride, dtype, 1);
+  if ((st = b.finish(total_seq_len, false))) return st;
+  return launch(b, rope->interleaved != 0, false, stream);
+}
+
+int32_t kv_cache_radd(const void* a, int32_t dtype, uint32_t total_rows, uint64_t a_row_stride,
+                      const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t batch_offset,
+                      const qrp_paged_cache* cache, uint32_t layer_idx, void* stream) {
+  g_err.clear();
+  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32 or QRP_BF16");
+  if (total_rows == 0) return QRP_OK;
+  int32_t st;
+  if ((st = check_batch(input_row_offsets, total_rows, batch_size))) return st;
+  if ((st = check_cache(cache, dtype, layer_idx, "cache"))) return st;
+  if (cache->kv_planes != 2) return fail(QRP_EINVAL, "cache needs K and V planes");
+  if (!a) return fail(QRP_EINVAL, "a is NULL");
+  if (!aligned16(a)) return fail(QRP_EALIGN, "a not 16-byte aligned");
+  if (a_row_stride % chunk_elems(dtype)) return fail(QRP_EALIGN, "a_row_stride not a multiple of 16 bytes");
+  const uint64_t D = cache->head_dim, Hk = cache->num_kv_heads;
+  if (a_row_stride < 2 * Hk * D) return fail(QRP_EINVAL, "a_row_stride < 2 * num_kv_heads * head_dim");
+  if ((uint64_t)batch_offset + batch_size > cache->cache_batch)
+    return fail(QRP_EINVAL, "batch_offset + batch_size > cache_batch");
+
+  Builder b;
+  b.dtype = dtype;
+  b.head_dim = cache->head_dim;
+  b.rpp = qrp::rows_per_pass(dtype, b.head_dim);
+  b.a.cache[0] = make_cache(cache, layer_idx);
+  b.a.ncache = 1;
+  b.a.offsets = input_row_offsets;
+  b.a.batch = batch_size;
+  b.a.batch_offset = batch_offset;
+  b.a.max_seq_len = 0;
+  b.add_seg(qrp::SEG_RADD, a, (int64_t)a_row_stride, nullptr, 0, nullptr, 0.f, (uint32_t)Hk, 0, 0);
+  b.add_seg(qrp::SEG_RADD, elem_ptr(a, Hk * D, dtype), (int64_t)a_row_stride, nullptr, 0, nullptr,
+            0.f, (uint32_t)Hk, 0, 1);
+  if ((st = b.finish(total_rows, true))) return st;
+  return launch(b, true, true, stream);
+}
+
+int32_t qrp_validate_host(const uint32_t* off, uint32_t B, uint32_t T, uint32_t batch_offset,
+                          const uint32_t* cache_lengths, const uint32_t* table, uint32_t cache_batch,
+                          uint32_t max_pages, uint32_t page_size, uint64_t num_pages,
+                          uint32_t max_seq_len) {
+  g_err.clear();
+  if (!off) return fail(QRP_EINVAL, "offsets is NULL");
+  if (T > 0 && (!cache_lengths || !table)) return fail(QRP_EINVAL, "cache metadata is NULL");
+  if (page_size == 0) return fail(QRP_EINVAL, "page_size is 0");
+  if (off[0] != 0) return fail(QRP_EDATA, "input_row_offsets[0] != 0");
+  for (uint32_t b = 0; b < B; ++b)
+    if (off[b + 1] < off[b])
+      return fail(QRP_EDATA, "input_row_offsets decrease at " + std::to_string(b + 1));
+  if (off[B] != T) return fail(QRP_EDATA, "input_row_offsets[batch_size] != total_seq_len");
+  if ((uint64_t)batch_offset + B > cache_batch) return fail(QRP_EDATA, "batch_offset + batch_size > cache_batch");
+  std::vector<uint64_t> rows;
+  rows.reserve(T);
+  for (uint32_t b = 0; b < B; ++b) {
+    const uint32_t s = b + batch_offset;
+    for (uint32_t t = off[b]; t < off[b + 1]; ++t) {
+      const uint64_t pos = (uint64_t)cache_lengths[s] + (t - off[b]);
+      if (max_seq_len && pos >= max_seq_len)
+        return fail(QRP_EDATA, "token " + std::to_string(t) + ": position " + std::to_string(pos) +
+                                   " >= max_seq_len");
+      const uint64_t pidx = pos / page_size;
+      if (pidx >= max_pages)
+        return fail(QRP_EDATA, "token " + std::to_string(t) + ": page index beyond max_pages_per_seq");
+      const uint64_t page = table[(uint64_t)s * max_pages + pidx];
+      if (page >= num_pages)
+        return fail(QRP_EDATA, "token " + std::to_string(t) + ": page id " + std::to_string(page) +
+                                   " >= num_pages");
+      rows.push_back(page * page_size + pos % page_size);
+    }
+  }
+  std::sort(rows.begin(), rows.end());
+  if (std::adjacent_find(rows.begin(), rows.end()) != rows.end())
+    return fail(QRP_EDATA, "two tokens write the same cache row (shared page)");
+  return QRP_OK;
+}
+
+int32_t qrp_validate(const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t total_seq_len,
+                     uint32_t batch_offset, const qrp_paged_cache* cache, uint32_t max_seq_len,
+                     void* stream) {
+  g_err.clear();
+  if (!input_row_offsets || !cache || !cache->cache_lengths || !cache->lookup_table)
+    return fail(QRP_EINVAL, "NULL metadata");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::vector<uint32_t> off(batch_size + 1ull), lens(cache->cache_batch),
+      table((uint64_t)cache->cache_batch * cache->max_pages_per_seq);
+  hipError_t e = hipMemcpyAsync(off.data(), input_row_offsets, off.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(lens.data(), cache->cache_lengths, lens.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(table.data(), cache->lookup_table, table.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(QRP_EHIP, std::string("metadata copy failed: ") + hipGetErrorString(e));
+  return qrp_validate_host(off.data(), batch_size, total_seq_len, batch_offset, lens.data(),
+                           table.data(), cache->cache_batch, cache->max_pages_per_seq,
+                           cache->page_size, cache->num_pages, max_seq_len);
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// engine.hpp -- launch descriptor of the band engine (internal to the library).
+//
+// Every operation of the library is one launch of the same kernel family.
+// A token's head rows are grouped into at most four SEGMENTS, each a run of
+// heads with one role:
+//
+//   SEG_Q        read from the input buffer, optionally normalised, rotated,
+//                written to a dense output row            (Q of every op)
+//   SEG_K_BUF    read from the buffer, optionally normalised, rotated,
+//                written to the K plane of a paged cache   (store ops)
+//   SEG_K_INPLACE read from the K plane of a paged cache, normalised,
+//                rotated, written back to the same row     (norm ops, K in cache)
+//   SEG_V_COPY   read from the buffer, written bit for bit to the V plane
+//   SEG_RADD     read from the buffer, added to a cache row in binary32
+//
+// A wave processes one token's rows in PASSES of RPP rows (64 lanes, D/16
+// lanes per row when rows are bf16 x 128).  Segment s covers passes
+// [pass_begin, pass_begin + n_passes) of the token.
+#pragma once
+
+#include <stdint.h>
+
+namespace qrp {
+
+enum SegKind : uint32_t {
+  SEG_Q = 0,
+  SEG_K_BUF = 1,
+  SEG_K_INPLACE = 2,
+  SEG_V_COPY = 3,
+  SEG_RADD = 4,
+};
+
+constexpr int kMaxSegs = 4;
+constexpr int kMaxCaches = 2;
+constexpr int kWavesPerBlock = 4;
+constexpr int kThreads = 64 * kWavesPerBlock;
+constexpr int kXcds = 8;
+
+struct SegDesc {
+  const void* src;          // buffer elements, already offset to the segment's first column
+  void* dst;                // dense output (SEG_Q)
+  const void* gamma;        // [D] of dtype, or nullptr: no norm
+  int64_t src_row_stride;   // elements between tokens in src
+  int64_t dst_row_stride;   // elements between tokens in dst
+  float eps;
+  uint32_t n_heads;
+  uint32_t kind;            // SegKind
+  uint32_t cache;           // cache slot (0 / 1) for the row address and position
+  uint32_t plane;           // cache plane written / read
+  uint32_t pass_begin;
+  uint32_t n_passes;
+  uint32_t pad_;
+};
+
+struct CacheDesc {
+  void* blocks;             // element base
+  int64_t page_stride, plane_stride, slot_stride, head_stride;
+  int64_t layer_off;        // layer_idx * layer_stride
+  const uint32_t* cache_lengths;
+  const uint32_t* table;
+  uint64_t num_pages;
+  uint32_t max_pages;
+  uint32_t page_size;
+  uint32_t page_shift;      // log2(page_size) when a power of two, else 0xFFFFFFFF
+  uint32_t cache_batch;
+};
+
+struct BandArgs {
+  SegDesc seg[kMaxSegs];
+  CacheDesc cache[kMaxCaches];
+  const uint32_t* offsets;  // [batch + 1]
+  const float* freqs;       // [max_seq_len][rope_dim]
+  uint32_t nseg;
+  uint32_t ncache;
+  uint32_t batch;
+  uint32_t total_tokens;
+  uint32_t batch_offset;
+  uint32_t rope_dim;
+  uint32_t max_seq_len;     // 0: positions unchecked (no rotation)
+  float weight_offset;      // already rounded to the dtype
+  uint32_t multiply_before_cast;
+  uint32_t passes_per_token;
+  uint32_t passes_per_group;
+  uint32_t groups_per_token;
+  uint32_t n_items;         // total_tokens * groups_per_token waves of work
+  uint32_t n_blocks;        // blocks holding work
+  uint32_t per_xcd;         // blocks per XCD after the XCD-contiguous remap (0: no remap)
+  uint64_t guess_mul;       // floor(batch * 2^32 / total_tokens): token -> first sequence guess
+};
+
+enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+
+// Launch the band engine; returns 0 or a hipError_t value.
+int launch_band(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interleaved, bool radd,
+                void* stream);
+
+// Rows handled per 64-lane pass for a dtype / head_dim.
+inline uint32_t rows_per_pass(int32_t dtype, uint32_t head_dim) {
+  const uint32_t elems_per_chunk = dtype == DT_F32 ? 4u : 8u;
+  const uint32_t lanes_per_row = head_dim / elems_per_chunk / 2u;
+  return 64u / lanes_per_row;
+}
+
+}  // namespace qrp

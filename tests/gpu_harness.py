@@ -1,0 +1,194 @@
+"""Device side of the tests and the benchmark: put a synthetic case on the GPU
+and run it through the C ABI (via the thin Python binding).
+
+Buffers hold raw bits (int16 for bf16, int32 for fp32).  Output buffers and
+cache pools start as the signalling-NaN sentinel so that any stray write,
+or any float round trip of a copied value, shows up in a bit comparison.
+``q_output`` buffers carry GUARD sentinel rows before and after the rows
+the call may write.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List
+
+import numpy as np
+import torch
+
+import qk_rope_paged_amd as qrp
+from synth import cases as sc
+
+GUARD = 2
+TORCH_BITS = {sc.F32: torch.int32, sc.BF16: torch.int16}
+QRP_DT = {sc.F32: qrp.QRP_F32, sc.BF16: qrp.QRP_BF16}
+
+
+def bits_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    signed = a.view(np.int16 if a.dtype == np.uint16 else np.int32)
+    return torch.from_numpy(signed).to(device)
+
+
+def sentinel_int(dtype: str) -> int:
+    s = int(sc.SENTINEL[dtype])
+    bits = 16 if dtype == sc.BF16 else 32
+    return s - (1 << bits) if s >= 1 << (bits - 1) else s
+
+
+def to_numpy_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
+    a = t.cpu().numpy()
+    return a.view(np.uint16 if dtype == sc.BF16 else np.uint32)
+
+
+@dataclass
+class DeviceCache:
+    host: sc.PagedCache
+    pool: torch.Tensor                 # flat raw bits
+    cache_lengths: torch.Tensor
+    lookup_table: torch.Tensor
+    desc: qrp.PagedCache = None
+
+    def pages(self, page_ids: np.ndarray) -> np.ndarray:
+        """Copy the given pages back, shaped like the host pool."""
+        view = self.pool.view(self.host.num_pages, self.host.page_elems)
+        idx = torch.from_numpy(np.asarray(page_ids, dtype=np.int64)).to(self.pool.device)
+        sel = view.index_select(0, idx)
+        return to_numpy_bits(sel, self.host.dtype).reshape((len(page_ids),) + self.host.shape[1:])
+
+
+def upload_cache(c: sc.PagedCache, device="cuda") -> DeviceCache:
+    n = c.num_pages * c.page_elems
+    pool = torch.full((n,), sentinel_int(c.dtype), dtype=TORCH_BITS[c.dtype], device=device)
+    pg, pl, ly, sl, vals = c.prefill_arrays()
+    if len(pg):
+        row0 = np.ravel_multi_index((pg, pl, ly, sl, np.zeros_like(pg), np.zeros_like(pg)), c.shape)
+        idx = row0[:, None] + np.arange(c.num_kv_heads * c.head_dim)[None, :]
+        pool[torch.from_numpy(idx.reshape(-1)).to(device)] = bits_tensor(vals.reshape(-1), device)
+    lens = torch.from_numpy(c.cache_lengths.astype(np.uint32).view(np.int32)).to(device)
+    tab = torch.from_numpy(np.ascontiguousarray(c.lookup_table, dtype=np.uint32).view(np.int32)).to(device)
+    st = c.strides
+    desc = qrp.PagedCache(blocks=pool, dtype=QRP_DT[c.dtype], num_kv_heads=c.num_kv_heads,
+                          head_dim=c.head_dim, page_size=c.page_size, num_layers=c.num_layers,
+                          kv_planes=c.kv_planes, num_pages=c.num_pages,
+                          page_stride=st["page_stride"], plane_stride=st["plane_stride"],
+                          layer_stride=st["layer_stride"], slot_stride=st["slot_stride"],
+                          head_stride=st["head_stride"], cache_lengths=lens, lookup_table=tab,
+                          cache_batch=c.cache_batch, max_pages_per_seq=c.max_pages_per_seq)
+    return DeviceCache(host=c, pool=pool, cache_lengths=lens, lookup_table=tab, desc=desc)
+
+
+@dataclass
+class DeviceCase:
+    case: sc.Case
+    buf: torch.Tensor
+    offsets: torch.Tensor
+    freqs: torch.Tensor
+    caches: List[DeviceCache]
+    q_out: List[torch.Tensor] = field(default_factory=list)      # with guard rows
+    gammas: list = field(default_factory=list)
+
+    def q_out_rows(self, i: int) -> torch.Tensor:
+        return self.q_out[i][GUARD:GUARD + self.case.T]
+
+
+def upload(case: sc.Case, device="cuda") -> DeviceCase:
+    buf = bits_tensor(case.buf, device) if case.buf.size else torch.zeros(
+        (0, case.row_stride), dtype=TORCH_BITS[case.dtype], device=device)
+    off = torch.from_numpy(case.offsets.astype(np.uint32).view(np.int32)).to(device)
+    freqs = (torch.from_numpy(np.ascontiguousarray(case.freqs)).to(device)
+             if case.freqs is not None else torch.zeros(4, dtype=torch.float32, device=device))
+    dc = DeviceCase(case=case, buf=buf, offsets=off, freqs=freqs,
+                    caches=[upload_cache(c, device) for c in case.caches])
+    strides = ([case.q_out_row_stride] if case.op == "store"
+               else [b.q_out_row_stride for b in case.bands])
+    for s in strides:
+        dc.q_out.append(torch.full((case.T + 2 * GUARD, max(s, 1)), sentinel_int(case.dtype),
+                                   dtype=TORCH_BITS[case.dtype], device=device))
+    for b in case.bands:
+        dc.gammas.append((None if b.q_gamma is None else bits_tensor(b.q_gamma, device),
+                          None if b.k_gamma is None else bits_tensor(b.k_gamma, device)))
+    return dc
+
+
+def rope_of(dc: DeviceCase) -> qrp.Rope:
+    c = dc.case
+    return qrp.Rope(freqs_cis=dc.freqs, max_seq_len=c.max_seq_len, rope_dim=c.rope_dim,
+                    interleaved=c.interleaved)
+
+
+def band_of(dc: DeviceCase, i: int) -> qrp.Band:
+    b = dc.case.bands[i]
+    qg, kg = dc.gammas[i]
+    return qrp.Band(q_col=b.q_col, n_q_heads=b.n_q_heads, k_col=b.k_col, v_col=b.v_col,
+                    q_gamma=qg, k_gamma=kg, epsilon=b.epsilon, cache=dc.caches[b.cache].desc,
+                    q_output=dc.q_out_rows(i), q_out_row_stride=b.q_out_row_stride)
+
+
+def run(dc: DeviceCase, stream=None, raise_on_error=True, op=None) -> int:
+    """One call of the case's operation through the C ABI."""
+    c = dc.case
+    op = op or c.op
+    dt = QRP_DT[c.dtype]
+    if op == "store":
+        return qrp.rope_split_store_paged(
+            dc.buf, dt, c.T, c.row_stride, c.n_q_heads, dc.offsets, c.batch, rope_of(dc),
+            dc.caches[0].desc, c.layer_idx, dc.q_out_rows(0), dt, c.q_out_row_stride,
+            stream=stream, raise_on_error=raise_on_error)
+    if op == "norm":
+        return qrp.qk_rmsnorm_rope_paged(
+            dc.buf, dt, c.T, c.row_stride, band_of(dc, 0), c.weight_offset,
+            c.multiply_before_cast, dc.offsets, c.batch, rope_of(dc), c.layer_idx,
+            stream=stream, raise_on_error=raise_on_error)
+    if op == "dual":
+        return qrp.dual_band(
+            dc.buf, dt, c.T, c.row_stride, band_of(dc, 0), band_of(dc, 1), c.weight_offset,
+            c.multiply_before_cast, dc.offsets, c.batch, rope_of(dc), c.layer_idx,
+            stream=stream, raise_on_error=raise_on_error)
+    if op == "radd":
+        return qrp.kv_cache_radd(
+            dc.buf, dt, c.T, c.row_stride, dc.offsets, c.batch, c.batch_offset,
+            dc.caches[0].desc, c.layer_idx, stream=stream, raise_on_error=raise_on_error)
+    raise ValueError(op)
+
+
+def algorithmic_bytes(case: sc.Case) -> int:
+    """Bytes the operation must move: inputs read, outputs written, cache rows
+    read for in-place updates, distinct freqs rows, metadata and gammas."""
+    eb = sc.ELEM_BYTES[case.dtype]
+    T = case.T
+    total = 0
+    if case.op == "store":
+        c = case.caches[0]
+        D, Hk, Hq = c.head_dim, c.num_kv_heads, case.n_q_heads
+        total += T * (Hq + 2 * Hk) * D * eb          # qkv read
+        total += T * (Hq + 2 * Hk) * D * eb          # q_out + K + V written
+    elif case.op in ("norm", "dual"):
+        for b in case.bands:
+            c = case.caches[b.cache]
+            D, Hk = c.head_dim, c.num_kv_heads
+            total += 2 * T * b.n_q_heads * D * eb    # Q read + written
+            total += 2 * T * Hk * D * eb             # K read (buffer or cache) + written
+            if b.v_col >= 0:
+                total += 2 * T * Hk * D * eb         # V read + written
+            total += (int(b.q_gamma is not None) + int(b.k_gamma is not None)) * D * eb
+    elif case.op == "radd":
+        c = case.caches[0]
+        total += 3 * T * 2 * c.num_kv_heads * c.head_dim * eb   # read a, read cache, write cache
+    if case.freqs is not None and T:
+        pos = token_positions(case)
+        total += len(np.unique(pos)) * case.rope_dim * 4
+    total += (case.batch + 1) * 4                                 # offsets
+    for c in case.caches:
+        total += min(c.cache_batch, case.batch) * 4                # cache lengths
+        total += T * 4                                             # page-table entries (upper bound: one per token)
+    return int(total)
+
+
+def token_positions(case: sc.Case) -> np.ndarray:
+    off = case.offsets.astype(np.int64)
+    out = []
+    for b in range(case.batch):
+        n = int(off[b + 1] - off[b])
+        cl = int(case.caches[0].cache_lengths[b + case.batch_offset])
+        out.append(np.arange(cl, cl + n))
+    return np.concatenate(out) if out else np.zeros(0, np.int64)

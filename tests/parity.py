@@ -1,0 +1,133 @@
+"""Element-by-element comparison of the HIP path with the CPU oracle.
+
+The bar:
+* bit-exact: every cache element outside the rows written, every V element,
+  the un-roped dims of the rope-only op, every radd result, q_output guard
+  rows and padding columns, and the input buffer (unchanged);
+* computed values (rotated and/or normalised):
+    fp32:  |gpu - v| <= 1e-5 * max(|v|, m)
+    bf16:  |gpu - v| <= ulps * ulp_bf16(max(|v|, 2^-8 * m))
+  with v the oracle's unrounded value and m the length of v's RoPE pair
+  (|v| for unrotated elements).  The pair-length floor is there because
+  x*cos - y*sin can cancel: a bound relative to |v| alone would demand more
+  than binary32 arithmetic can give.  ulps = 1 ("one bf16 ulp on a value
+  computed in binary32"); 2 for multiply_before_cast = false, whose
+  intermediate roundings can flip.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from synth import cases as sc
+from tests import brute
+from tests import gpu_harness as gh
+
+
+class Report(dict):
+    pass
+
+
+def tol_ok(gpu_bits: np.ndarray, exact: np.ndarray, mag: np.ndarray, dtype: str, ulps: int):
+    g = sc.bits_to_f64(gpu_bits, dtype)
+    if dtype == sc.F32:
+        tol = 1e-5 * np.maximum(np.abs(exact), mag)
+    else:
+        tol = ulps * brute.ulp_bf16(np.maximum(np.abs(exact), 2.0 ** -8 * mag))
+    return np.abs(g - exact) <= tol
+
+
+def check_rows(gpu: np.ndarray, ora: np.ndarray, exact: np.ndarray, mag: np.ndarray,
+               copy_cols: np.ndarray, dtype: str, ulps: int, what: str, rep: Report):
+    """Rows [N, D]: copy columns bit-exact, the others within tolerance."""
+    if gpu.size == 0:
+        return
+    assert np.array_equal(gpu[:, copy_cols], ora[:, copy_cols]), f"{what}: copied dims differ"
+    comp = ~copy_cols
+    g, o = gpu[:, comp], ora[:, comp]
+    ok = tol_ok(g, exact[:, comp], mag[:, comp], dtype, ulps)
+    if not ok.all():
+        bad = np.argwhere(~ok)[:5]
+        det = [(int(r), int(c), float(sc.bits_to_f64(g[r, c], dtype)), float(exact[:, comp][r, c]),
+                float(mag[:, comp][r, c])) for r, c in bad]
+        raise AssertionError(f"{what}: {int((~ok).sum())} values out of tolerance, e.g. {det}")
+    rep[what + "_exact_rate"] = float((g == o).mean()) if g.size else 1.0
+    rep[what + "_n"] = int(g.size)
+
+
+def _copy_cols(D: int, R: int, normed: bool) -> np.ndarray:
+    cols = np.zeros(D, dtype=bool)
+    if not normed:
+        cols[R:] = True
+    return cols
+
+
+def bands_of(case):
+    """(q_out index, cache index, n_q_heads, q normed, k normed, has V) per band."""
+    if case.op == "store":
+        return [(0, 0, case.n_q_heads, False, False, True)]
+    if case.op in ("norm", "dual"):
+        return [(i, b.cache, b.n_q_heads, b.q_gamma is not None, b.k_gamma is not None,
+                 b.v_col >= 0) for i, b in enumerate(case.bands)]
+    return []
+
+
+def compare(case, dc: gh.DeviceCase, res, ulps: int = 1) -> Report:
+    """Full comparison of one GPU call (already run) against the oracle result."""
+    assert res.status == 0, f"oracle status {res.status}"
+    rep = Report()
+    dt = case.dtype
+    T = case.T
+    sent = sc.SENTINEL[dt]
+    # the input buffer is unchanged
+    if case.buf.size:
+        assert np.array_equal(gh.to_numpy_bits(dc.buf, dt), case.buf), "input buffer modified"
+    # ---- Q outputs ----
+    for qi, ci, Hq, qn, kn, hv in bands_of(case):
+        D = case.caches[ci].head_dim
+        full = gh.to_numpy_bits(dc.q_out[qi], dt)
+        g = gh.GUARD
+        assert np.all(full[:g] == sent) and np.all(full[g + T:] == sent), "q_output guard rows written"
+        rows = full[g:g + T]
+        ora = res.q_out[qi]
+        stride = ora.shape[1]
+        assert np.array_equal(rows[:, Hq * D:stride], ora[:, Hq * D:]), "q_output padding written"
+        if Hq and T:
+            tr = res.traces[qi]
+            check_rows(rows[:, :Hq * D].reshape(-1, D), ora[:, :Hq * D].reshape(-1, D),
+                       tr["q_exact"].reshape(-1, D), tr["q_mag"].reshape(-1, D),
+                       _copy_cols(D, case.rope_dim, qn), dt, ulps, f"q{qi}", rep)
+    # ---- caches ----
+    for ci, dcache in enumerate(dc.caches):
+        host = dcache.host
+        ora_pool = res.pools[ci]
+        pages = res.page_maps[ci]
+        if pages is None:
+            pages = np.arange(host.num_pages)
+        gpu_pool = dcache.pages(pages)
+        D = host.head_dim
+        g_flat = gpu_pool.reshape(-1).copy()
+        o_flat = ora_pool.reshape(-1).copy()
+        for qi, cj, Hq, qn, kn, hv in bands_of(case):
+            if cj != ci or T == 0:
+                continue
+            tr = res.traces[qi]
+            koff = tr["k_row_off"].reshape(-1)
+            idx = koff[:, None] + np.arange(D)[None, :]
+            check_rows(g_flat[idx], o_flat[idx], tr["k_exact"].reshape(-1, D),
+                       tr["k_mag"].reshape(-1, D), _copy_cols(D, case.rope_dim, kn), dt, ulps,
+                       f"k{qi}", rep)
+            # written K rows are checked: blank them before the bitwise comparison
+            g_flat[idx] = 0
+            o_flat[idx] = 0
+        if not np.array_equal(g_flat, o_flat):
+            bad = np.flatnonzero(g_flat != o_flat)
+            raise AssertionError(f"cache {ci}: {len(bad)} elements differ outside the checked K "
+                                 f"rows, first at flat {bad[:5]} "
+                                 f"gpu={g_flat[bad[:5]]} oracle={o_flat[bad[:5]]}")
+        if res.page_maps[ci] is not None:
+            # pages the batch does not touch must hold nothing but the sentinel
+            n_dev = int((dcache.pool != gh.sentinel_int(dt)).sum().item())
+            n_touched = int((gpu_pool != sent).sum())
+            assert n_dev == n_touched, "a page outside the batch was written"
+    return rep
