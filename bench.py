@@ -1,0 +1,446 @@
+#!/usr/bin/env python3
+"""Throughput of the fused ragged RoPE + split + paged-KV store on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill|decode|dual|radd]
+
+A step is one call of the pass over one batch of seeded synthetic input that
+is already resident in HBM.  The default workload is the Llama-3-8B-shaped
+prefill (32 Q / 8 KV heads, head_dim 128, bf16, half-split RoPE, theta 5e5,
+batch 8 with lengths U[128, 2048], page 128, 32 layers, layer 17).  Other
+workloads (decode, dual band, radd) are for measuring the other kernels.
+
+Each step runs on its own set of buffers, cycling through enough sets that
+the data touched between two uses of a set exceeds the 256 MB Infinity
+Cache: every step reads its inputs from HBM, not from a warm cache.  Each
+set is its own seeded batch (seeds s, s+100, s+200, ...), so the steps sample
+the workload's length distribution instead of repeating one draw.
+
+Also measured in the same run: a plain streaming copy moving the same bytes
+(half read, half written) -- the practical bandwidth ceiling at this size.
+
+Printed: one JSON line.  `value` is effective GB/s (algorithmic bytes per
+step / wall time per step), `roofline.achieved` the same bytes over the
+kernel's own average duration (HIP events around each launch on the launch
+stream), `cpu_baseline` the CPU oracle on the host, single-threaded.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective HBM GB/s & tokens/s of fused RoPE+paged-store; % of HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 << 20         # Infinity Cache
+KERNEL_NAME = "band_kernel"
+KERNEL_SOURCES = ("qk_rope_paged_amd/csrc/kernels.hip", "qk_rope_paged_amd/csrc/engine.hpp",
+                  "qk_rope_paged_amd/csrc/abi.cpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, seeds):
+    """Measured HBM bytes per launch, averaged like the timed steps, from the
+    committed counter summary (per-batch read and write bytes, already scaled
+    by the copy calibration), or None when the summary is missing, lacks a
+    batch, or was taken from a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    total = 0.0
+    try:
+        for sd in seeds:
+            rd, wr = kv[f"seed_{sd}_bytes"].split()[:2]
+            total += float(rd) + float(wr)
+    except (KeyError, ValueError):
+        return None
+    return int(total / len(seeds))
+
+
+def algorithmic_bytes(case) -> int:
+    """Bytes the operation must move: inputs read, outputs written, cache rows
+    read for in-place updates, distinct freqs rows, metadata and gammas."""
+    import numpy as np
+    from synth import cases as sc
+
+    eb = sc.ELEM_BYTES[case.dtype]
+    T = case.T
+    total = 0
+    if case.op == "store":
+        c = case.caches[0]
+        D, Hk, Hq = c.head_dim, c.num_kv_heads, case.n_q_heads
+        total += T * (Hq + 2 * Hk) * D * eb          # qkv read
+        total += T * (Hq + 2 * Hk) * D * eb          # q_out + K + V written
+    elif case.op in ("norm", "dual"):
+        for b in case.bands:
+            c = case.caches[b.cache]
+            D, Hk = c.head_dim, c.num_kv_heads
+            total += 2 * T * b.n_q_heads * D * eb    # Q read + written
+            total += 2 * T * Hk * D * eb             # K read (buffer or cache) + written
+            if b.v_col >= 0:
+                total += 2 * T * Hk * D * eb         # V read + written
+            total += (int(b.q_gamma is not None) + int(b.k_gamma is not None)) * D * eb
+    elif case.op == "radd":
+        c = case.caches[0]
+        total += 3 * T * 2 * c.num_kv_heads * c.head_dim * eb   # read a, read cache, write cache
+    if case.freqs is not None and T:
+        pos = token_positions(case)
+        total += len(np.unique(pos)) * case.rope_dim * 4
+    total += (case.batch + 1) * 4                                 # offsets
+    pos = token_positions(case)
+    seq = np.repeat(np.arange(case.batch), np.diff(case.offsets.astype(np.int64)))
+    for c in case.caches:
+        total += case.batch * 4                                    # cache lengths
+        if T:                                                      # distinct page-table entries
+            total += len(np.unique(seq * (c.max_pages_per_seq + 1) + pos // c.page_size)) * 4
+    return int(total)
+
+
+def token_positions(case):
+    """Cache position of every token: its sequence's cache length plus its
+    index within the sequence."""
+    import numpy as np
+
+    off = case.offsets.astype(np.int64)
+    out = []
+    for b in range(case.batch):
+        n = int(off[b + 1] - off[b])
+        cl = int(case.caches[0].cache_lengths[b + case.batch_offset])
+        out.append(np.arange(cl, cl + n))
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5}
+
+
+def make_case(workload: str, seed: int = None):
+    from synth import cases as sc
+    fn = sc.WORKLOADS[workload]
+    return fn(seed=DEFAULT_SEED[workload] if seed is None else seed)
+
+
+def workload_config(case, cases) -> dict:
+    c = case.caches[0]
+    cfg = {"workload": {"store": "rope_split_store_paged", "norm": "qk_rmsnorm_rope_paged",
+                        "dual": "dual_band", "radd": "kv_cache_radd"}[case.op] + ":" + case.name,
+           "batch": case.batch, "head_dim": c.head_dim, "kv_heads": c.num_kv_heads,
+           "page_size": c.page_size, "num_layers": c.num_layers, "layer_idx": case.layer_idx,
+           "seeds": [x.seed for x in cases], "tokens_per_batch": [x.T for x in cases],
+           "tokens_mean": round(sum(x.T for x in cases) / len(cases), 1)}
+    if case.op == "store":
+        cfg["q_heads"] = case.n_q_heads
+    if case.op in ("store", "norm", "dual"):
+        cfg["rope"] = "interleaved" if case.interleaved else "half-split"
+        cfg["rope_dim"] = case.rope_dim
+    if case.op == "dual":
+        cfg["q_heads"] = [b.n_q_heads for b in case.bands]
+    if case.op == "radd":
+        cfg["batch_offset"] = case.batch_offset
+    return cfg
+
+
+def build_sets(cases):
+    """One device copy per case.  Store-op pools larger than 2 GiB are shared:
+    every set after the first gets a page table whose referenced entries
+    point at fresh pages, disjoint from the pages any other set touches, so
+    no set overwrites another's rows."""
+    import numpy as np
+    import torch
+    from tests import gpu_harness as gh
+
+    def referenced(case):
+        c = case.caches[0]
+        seq = np.repeat(np.arange(case.batch), np.diff(case.offsets.astype(np.int64)))
+        pidx = token_positions(case) // c.page_size
+        return np.unique(seq * c.max_pages_per_seq + pidx)
+
+    first = cases[0]
+    sets = [gh.upload(first)]
+    shared = first.op == "store" and first.caches[0].nbytes > (2 << 30)
+    if shared:
+        c0 = first.caches[0]
+        used = np.unique(c0.lookup_table.reshape(-1)[referenced(first)].astype(np.int64))
+        free = np.setdiff1d(np.arange(c0.num_pages), used)
+        cursor = 0
+    for case in cases[1:]:
+        if not shared:
+            sets.append(gh.upload(case))
+            continue
+        host = case.caches[0]
+        entries = referenced(case)
+        if cursor + len(entries) > len(free):
+            raise RuntimeError("pool too small for disjoint buffer sets")
+        tab = np.full(host.lookup_table.size, 0xFFFFFFFF, dtype=np.uint32)
+        tab[entries] = free[cursor:cursor + len(entries)]
+        cursor += len(entries)
+        saved = case.caches
+        case.caches = []
+        dc = gh.upload(case)
+        case.caches = saved
+        base = sets[0].caches[0]
+        ttab = torch.from_numpy(tab.view(np.int32)).cuda()
+        lens = torch.from_numpy(host.cache_lengths.astype(np.uint32).view(np.int32)).cuda()
+        desc = gh.qrp.PagedCache(**{**base.desc.__dict__, "lookup_table": ttab,
+                                    "cache_lengths": lens})
+        dc.caches = [gh.DeviceCache(host=host, pool=base.pool, cache_lengths=lens,
+                                    lookup_table=ttab, desc=desc)]
+        sets.append(dc)
+    return sets, shared
+
+
+def time_launches(calls, steps: int, warmup: int):
+    """Warm up, then time `steps` launches cycling through `calls`: wall time
+    between two synchronisations, and each launch's duration from events
+    recorded around it on the launch stream."""
+    import torch
+
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev_s[k].record()
+        calls[k % len(calls)]()
+        ev_e[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) / 1e3 for s, e in zip(ev_s, ev_e)]
+
+
+def time_region(calls, steps: int, warmup: int):
+    """Warm up, then run `steps` launches back to back (cycling `calls`)
+    between one pair of HIP events on the launch stream and two
+    synchronisations: (wall seconds, GPU seconds)."""
+    import torch
+
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for k in range(steps):
+        calls[k % len(calls)]()
+    ev1.record()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, ev0.elapsed_time(ev1) / 1e3
+
+
+def copy_ceiling(nbytes: int, n_bufs: int, steps: int) -> dict:
+    """A plain streaming copy of nbytes/2 (read) into nbytes/2 (written),
+    cycling through n_bufs buffer pairs: the best of 1 and 4 chunks/thread."""
+    import ctypes
+    import torch
+    from qk_rope_paged_amd import build as hip_build
+
+    lib = ctypes.CDLL(hip_build.COPY_LIB_PATH)
+    lib.qrp_bench_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                          ctypes.c_int32, ctypes.c_void_p]
+    lib.qrp_bench_stream_copy.restype = ctypes.c_int32
+    half = (nbytes // 2) // 16 * 16
+    bufs = [(torch.ones(half // 8, dtype=torch.int64, device="cuda"),
+             torch.empty(half // 8, dtype=torch.int64, device="cuda")) for _ in range(n_bufs)]
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for u in (1, 4):
+        def mk(a, b, u=u):
+            def f():
+                if lib.qrp_bench_stream_copy(b.data_ptr(), a.data_ptr(), half, u, stream) != 0:
+                    raise RuntimeError("copy launch failed")
+            return f
+        _, gpu = time_region([mk(a, b) for a, b in bufs], steps, 10)
+        avg = gpu / steps
+        if best is None or avg < best[1]:
+            best = (u, avg)
+    ok = all(torch.equal(a, b) for a, b in bufs[:2])
+    del bufs
+    torch.cuda.empty_cache()
+    return {"value": round(2 * half / best[1] / 1e9, 2), "unit": "GB/s",
+            "kernel_us": round(best[1] * 1e6, 3), "bytes": 2 * half,
+            "chunks_per_thread": best[0], "verified": ok,
+            "kind": "nontemporal streaming copy, same bytes as one step (half read, half written)"}
+
+
+def cpu_baseline(cases, seconds: float, max_passes: int) -> dict:
+    """The CPU oracle as it stands, single-threaded, on the same batches
+    (cycled), repeated until about `seconds` of oracle time."""
+    import oracle
+    from tests import gpu_harness as gh
+
+    total, passes, nbytes, ntok = 0.0, 0, 0, 0
+    while passes < max_passes and (passes == 0 or total < seconds):
+        case = cases[passes % len(cases)]
+        res = oracle.run_case(case, trace=False)
+        if res.status != 0:
+            raise RuntimeError(f"oracle failed with status {res.status}")
+        total += res.seconds
+        nbytes += algorithmic_bytes(case)
+        ntok += case.T
+        passes += 1
+    return {"value": round(nbytes / total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full passes over the first {min(passes, len(cases))} seeded "
+                      f"batches ({ntok} tokens), {total:.1f} s of oracle time (C call only)",
+            "tokens_per_s": round(ntok / total, 1)}
+
+
+def check_parity(case, dc, shared_pool: bool) -> str:
+    """Compare the first device set against the oracle (store ops repeat to
+    the same result; in-place ops accumulate, so they are not checked here).
+    With a shared pool the other sets' pages are not expected to hold the
+    sentinel."""
+    if case.op != "store":
+        return "not checked (in-place op applied repeatedly)"
+    import oracle
+    from tests import parity
+    res = oracle.run_case(case)
+    parity.compare(case, dc, res, untouched_pages=not shared_pool)
+    return "ok"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "dual", "radd"])
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-max-passes", type=int, default=30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--seed", type=int, default=None, help="seed of the first batch")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run a plain device copy of this size first (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the pass shards by sequence or by head with "
+              "no exchange between GPUs, and this library has no multi-GPU code. "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    from qk_rope_paged_amd import build as hip_build
+    if not os.path.exists(hip_build.LIB_PATH):
+        hip_build.build()
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    from tests import gpu_harness as gh
+
+    t_gen = time.perf_counter()
+    base_seed = args.seed if args.seed is not None else DEFAULT_SEED[args.workload]
+    first = make_case(args.workload, base_seed)
+    per_step = max(algorithmic_bytes(first), 1)
+    n_sets = args.sets or min(16, max(2, -(-3 * MALL_BYTES // per_step) + 1))
+    cases = [first] + [make_case(args.workload, base_seed + 100 * k) for k in range(1, n_sets)]
+    set_bytes = [algorithmic_bytes(c) for c in cases]
+    log(f"[bench] {first.name}: {n_sets} seeded batches, tokens {[c.T for c in cases]}, "
+        f"mean bytes/step {sum(set_bytes) / n_sets:.0f} (generated in "
+        f"{time.perf_counter() - t_gen:.1f}s)")
+    sets, shared_pool = build_sets(cases)
+    calls = [gh.run(dc, prepare=True) for dc in sets]
+    torch.cuda.synchronize()
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 copies of {n} bytes")
+        del src, dst
+
+    K = args.steps
+    # Timed region: K steps back to back on the launch stream, bracketed by
+    # one pair of HIP events (GPU time) and two synchronisations (wall time).
+    wall, gpu_time = time_region(calls, K, args.warmup)
+    # spread of single launches: the same K launches again, each between its
+    # own two events (an event pair adds about 2 us to what it measures)
+    _, durs = time_launches(calls, K, 0)
+    step_bytes = [set_bytes[k % n_sets] for k in range(K)]
+    step_tokens = [cases[k % n_sets].T for k in range(K)]
+    kern = sorted(durs)
+    log(f"[bench] timed {K} steps: wall {wall * 1e3:.2f} ms, events {gpu_time * 1e3:.2f} ms "
+        f"({gpu_time / K * 1e6:.2f} us per launch); single launches p10 {kern[K // 10] * 1e6:.2f} "
+        f"us, p90 {kern[(9 * K) // 10] * 1e6:.2f} us")
+
+    parity_status = "skipped" if args.no_parity else check_parity(first, sets[0], shared_pool)
+    log(f"[bench] parity: {parity_status}")
+
+    mean_bytes = sum(step_bytes) / K
+    value = sum(step_bytes) / wall / 1e9
+    achieved = sum(step_bytes) / gpu_time / 1e9
+    traffic = traffic_from_profiles(args.workload, [cases[k % n_sets].seed for k in range(K)])
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": first.dtype,
+        "data": "synthetic (seeded batches with the workload's shapes and length distribution)",
+        "config": workload_config(first, cases),
+        "tokens_per_s": round(sum(step_tokens) / wall, 1),
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": round(mean_bytes),
+        "kernel_us": {"avg": round(gpu_time / K * 1e6, 3),
+                      "single_launch_p10": round(kern[K // 10] * 1e6, 3),
+                      "single_launch_p90": round(kern[(9 * K) // 10] * 1e6, 3)},
+        "parity": parity_status,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": KERNEL_NAME},
+    }
+    if not args.no_copy_ceiling:
+        del sets, calls
+        torch.cuda.empty_cache()
+        log("[bench] timing the copy ceiling ...")
+        cc = copy_ceiling(int(mean_bytes), n_sets, max(20, K // 2))
+        out["copy_ceiling"] = cc
+        out["roofline"]["frac_of_copy_ceiling"] = round(achieved / cc["value"], 4)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds, args.cpu_max_passes)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

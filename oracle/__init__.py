@@ -17,6 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+import time
 from dataclasses import dataclass, field
 from typing import List, Optional
 
@@ -117,6 +118,7 @@ def bf16_to_double(b: int) -> float:
 @dataclass
 class OracleResult:
     status: int
+    seconds: float = 0.0                                       # wall time of the C call
     q_out: List[np.ndarray] = field(default_factory=list)     # per band, raw bits
     pools: List[np.ndarray] = field(default_factory=list)     # per cache, after the op
     page_maps: List[Optional[np.ndarray]] = field(default_factory=list)
@@ -199,6 +201,7 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
         D, Hk, Hq = cache.head_dim, cache.num_kv_heads, case.n_q_heads
         q_out = np.full((T, case.q_out_row_stride), _SENT[case.dtype], dtype=_BITS[case.dtype])
         tr, otr = _trace(T, Hq, Hk, D, keep) if trace else (None, None)
+        t0 = time.perf_counter()
         st = lib.orc_rope_split_store_paged(
             _ptr(buf), dt, T, case.row_stride, Hq, _ptr(off), case.batch, _ptr(freqs),
             case.max_seq_len, case.rope_dim, int(case.interleaved), ctypes.byref(ocaches[0]),
@@ -225,6 +228,7 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
             trs.append(tr)
             otrs.append(otr)
         keep.append(obands)
+        t0 = time.perf_counter()
         if case.op == "norm":
             st = lib.orc_qk_rmsnorm_rope_paged(
                 _ptr(buf), dt, T, case.row_stride, ctypes.byref(obands[0]),
@@ -246,11 +250,13 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
         Hk = cache.num_kv_heads
         krow = np.full((T, Hk), -1, dtype=np.int64)
         vrow = np.full((T, Hk), -1, dtype=np.int64)
+        t0 = time.perf_counter()
         st = lib.orc_kv_cache_radd(_ptr(buf), dt, T, case.row_stride, _ptr(off), case.batch,
                                    case.batch_offset, ctypes.byref(ocaches[0]), case.layer_idx,
                                    _ptr(krow), _ptr(vrow))
         res.traces.append(dict(k_row_off=krow, v_row_off=vrow))
     else:
         raise ValueError(case.op)
+    res.seconds = time.perf_counter() - t0
     res.status = int(st)
     return res

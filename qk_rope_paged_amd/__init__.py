@@ -61,12 +61,20 @@ class QrpBand(ctypes.Structure):
                 ("q_output", ctypes.c_void_p), ("q_out_row_stride", ctypes.c_uint64)]
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    # One HIP runtime per process: PyTorch-ROCm ships its own libamdhip64
+    # (same soname as the system one it was not linked by name against), so
+    # torch is loaded first and the library then binds to that runtime.
+    # Loading the library first would leave two runtimes in the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m qk_rope_paged_amd.build` "
+            f"{path} is missing: build it with `python -m qk_rope_paged_amd.build` "
             "(or __graft_entry__.build()); there is no non-HIP fallback")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, U32, U64, I32, F = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32, ctypes.c_float
     PC, PR, PB = ctypes.POINTER(QrpPagedCache), ctypes.POINTER(QrpRope), ctypes.POINTER(QrpBand)
     sig = {
@@ -99,6 +107,23 @@ def _check(status: int, raise_on_error: bool) -> int:
     if status != QRP_OK and raise_on_error:
         raise QrpError(status, last_error())
     return status
+
+
+class PreparedCall:
+    """A library call with its arguments marshalled once (``prepare=True``):
+    calling it costs one ctypes call, for tight launch loops."""
+
+    def __init__(self, fn, args, keep, raise_on_error):
+        self._fn, self._args, self._keep, self._raise = fn, args, keep, raise_on_error
+
+    def __call__(self) -> int:
+        return _check(self._fn(*self._args), self._raise)
+
+
+def _call(fn, args, keep, raise_on_error, prepare):
+    if prepare:
+        return PreparedCall(fn, args, keep, raise_on_error)
+    return _check(fn(*args), raise_on_error)
 
 
 def _ptr(t) -> Optional[int]:
@@ -193,48 +218,46 @@ class Band:
 def rope_split_store_paged(qkv, dtype: int, total_seq_len: int, qkv_row_stride: int,
                            n_q_heads: int, input_row_offsets, batch_size: int, rope: Rope,
                            cache: PagedCache, layer_idx: int, q_output, q_out_dtype: int,
-                           q_out_row_stride: int, stream=None, raise_on_error: bool = True) -> int:
+                           q_out_row_stride: int, stream=None, raise_on_error: bool = True,
+                           prepare: bool = False):
     cr, cc = rope.to_c(), cache.to_c()
-    st = lib.rope_split_store_paged(_ptr(qkv), dtype, total_seq_len, qkv_row_stride, n_q_heads,
-                                    _ptr(input_row_offsets), batch_size, ctypes.byref(cr),
-                                    ctypes.byref(cc), layer_idx, _ptr(q_output), q_out_dtype,
-                                    q_out_row_stride, _stream(stream))
-    return _check(st, raise_on_error)
+    args = (_ptr(qkv), dtype, total_seq_len, qkv_row_stride, n_q_heads, _ptr(input_row_offsets),
+            batch_size, ctypes.byref(cr), ctypes.byref(cc), layer_idx, _ptr(q_output),
+            q_out_dtype, q_out_row_stride, _stream(stream))
+    return _call(lib.rope_split_store_paged, args, [cr, cc], raise_on_error, prepare)
 
 
 def qk_rmsnorm_rope_paged(qkv, dtype: int, total_seq_len: int, qkv_row_stride: int, band: Band,
                           weight_offset: float, multiply_before_cast: bool, input_row_offsets,
                           batch_size: int, rope: Rope, layer_idx: int, stream=None,
-                          raise_on_error: bool = True) -> int:
+                          raise_on_error: bool = True, prepare: bool = False):
     keep: list = []
     cb, cr = band.to_c(keep), rope.to_c()
-    st = lib.qk_rmsnorm_rope_paged(_ptr(qkv), dtype, total_seq_len, qkv_row_stride,
-                                   ctypes.byref(cb), weight_offset, int(bool(multiply_before_cast)),
-                                   _ptr(input_row_offsets), batch_size, ctypes.byref(cr), layer_idx,
-                                   _stream(stream))
-    return _check(st, raise_on_error)
+    args = (_ptr(qkv), dtype, total_seq_len, qkv_row_stride, ctypes.byref(cb), weight_offset,
+            int(bool(multiply_before_cast)), _ptr(input_row_offsets), batch_size,
+            ctypes.byref(cr), layer_idx, _stream(stream))
+    return _call(lib.qk_rmsnorm_rope_paged, args, keep + [cb, cr], raise_on_error, prepare)
 
 
 def dual_band(buf, dtype: int, total_seq_len: int, buf_row_stride: int, main_band: Band,
               index_band: Band, weight_offset: float, multiply_before_cast: bool,
               input_row_offsets, batch_size: int, rope: Rope, layer_idx: int, stream=None,
-              raise_on_error: bool = True) -> int:
+              raise_on_error: bool = True, prepare: bool = False):
     keep: list = []
     cm, ci, cr = main_band.to_c(keep), index_band.to_c(keep), rope.to_c()
-    st = lib.dual_band(_ptr(buf), dtype, total_seq_len, buf_row_stride, ctypes.byref(cm),
-                       ctypes.byref(ci), weight_offset, int(bool(multiply_before_cast)),
-                       _ptr(input_row_offsets), batch_size, ctypes.byref(cr), layer_idx,
-                       _stream(stream))
-    return _check(st, raise_on_error)
+    args = (_ptr(buf), dtype, total_seq_len, buf_row_stride, ctypes.byref(cm), ctypes.byref(ci),
+            weight_offset, int(bool(multiply_before_cast)), _ptr(input_row_offsets), batch_size,
+            ctypes.byref(cr), layer_idx, _stream(stream))
+    return _call(lib.dual_band, args, keep + [cm, ci, cr], raise_on_error, prepare)
 
 
 def kv_cache_radd(a, dtype: int, total_rows: int, a_row_stride: int, input_row_offsets,
                   batch_size: int, batch_offset: int, cache: PagedCache, layer_idx: int,
-                  stream=None, raise_on_error: bool = True) -> int:
+                  stream=None, raise_on_error: bool = True, prepare: bool = False):
     cc = cache.to_c()
-    st = lib.kv_cache_radd(_ptr(a), dtype, total_rows, a_row_stride, _ptr(input_row_offsets),
-                           batch_size, batch_offset, ctypes.byref(cc), layer_idx, _stream(stream))
-    return _check(st, raise_on_error)
+    args = (_ptr(a), dtype, total_rows, a_row_stride, _ptr(input_row_offsets), batch_size,
+            batch_offset, ctypes.byref(cc), layer_idx, _stream(stream))
+    return _call(lib.kv_cache_radd, args, [cc], raise_on_error, prepare)
 
 
 def qrp_validate(input_row_offsets, batch_size: int, total_seq_len: int, batch_offset: int,

@@ -18,6 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libqk_rope_paged.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["kernels.hip", "abi.cpp"]
+# measurement helper for the benchmark (not part of the C ABI)
+COPY_LIB_PATH = os.path.join(HERE, "libqrp_bench_copy.so")
+COPY_SOURCES = ["bench_copy.hip"]
 ARCH = "gfx950"
 
 
@@ -27,24 +30,28 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def command(out: str = LIB_PATH, extra=()) -> list:
+def command(out: str = LIB_PATH, extra=(), sources=SOURCES) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-command-line-argument",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            *[os.path.join(CSRC, s) for s in SOURCES], *extra, "-o", out]
+            *[os.path.join(CSRC, s) for s in sources], *extra, "-o", out]
+
+
+def _compile(out: str, sources, verbose: bool) -> None:
+    tmp = out + ".tmp"
+    res = subprocess.run(command(tmp, sources=sources), capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building " + os.path.basename(out))
+    if verbose:
+        sys.stderr.write(res.stderr)
+    os.replace(tmp, out)
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = command(tmp)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building " + LIB_NAME)
-    if verbose:
-        sys.stderr.write(res.stderr)
-    os.replace(tmp, LIB_PATH)
+    _compile(LIB_PATH, SOURCES, verbose)
+    _compile(COPY_LIB_PATH, COPY_SOURCES, verbose)
     return LIB_PATH
 
 

@@ -143,12 +143,18 @@ struct Builder {
 
   // split tokens x passes into waves and blocks
   int32_t finish(uint32_t total_tokens, bool radd) {
-    const uint32_t npmax = radd ? 4u : 6u;
+    bool norm = false;
+    for (uint32_t s = 0; s < a.nseg; ++s) norm = norm || a.seg[s].gamma != nullptr;
+    const uint32_t npmax = qrp::max_passes(radd, norm);
     const uint32_t ppt = a.passes_per_token;
     uint32_t ppg = std::min<uint32_t>(npmax, ppt);
     const int forced = env_int("QRP_PASSES_PER_WAVE", 0);
     if (forced > 0) {
       ppg = std::min<uint32_t>((uint32_t)forced, std::min(npmax, ppt));
+    } else if (radd) {
+      // a radd pass already carries two loads per chunk (a and the cache
+      // row): one pass per wave measured fastest
+      ppg = 1;
     } else {
       // enough waves to cover every SIMD a few times over: shrink the group
       const uint64_t want = 4096;
@@ -160,7 +166,7 @@ struct Builder {
     if (items >= (1ull << 31)) return fail(QRP_EINVAL, "batch too large for one launch");
     a.n_items = (uint32_t)items;
     a.n_blocks = (uint32_t)((items + qrp::kWavesPerBlock - 1) / qrp::kWavesPerBlock);
-    a.per_xcd = env_int("QRP_XCD_REMAP", 1) ? (a.n_blocks + qrp::kXcds - 1) / qrp::kXcds : 0;
+    a.per_xcd = env_int("QRP_XCD_REMAP", 0) ? (a.n_blocks + qrp::kXcds - 1) / qrp::kXcds : 0;
     a.total_tokens = total_tokens;
     a.guess_mul = (((uint64_t)a.batch) << 32) / total_tokens;
     return QRP_OK;

@@ -36,6 +36,20 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = 64 * kWavesPerBlock;
 constexpr int kXcds = 8;
 
+// Passes (rows of 64 lanes) one wave may hold in registers at once.
+#ifndef QRP_MAX_PASSES_STORE
+#define QRP_MAX_PASSES_STORE 6
+#endif
+#ifndef QRP_MAX_PASSES_NORM
+#define QRP_MAX_PASSES_NORM 4
+#endif
+#ifndef QRP_MAX_PASSES_RADD
+#define QRP_MAX_PASSES_RADD 4
+#endif
+constexpr int kMaxPassesStore = QRP_MAX_PASSES_STORE;
+constexpr int kMaxPassesNorm = QRP_MAX_PASSES_NORM;
+constexpr int kMaxPassesRadd = QRP_MAX_PASSES_RADD;
+
 struct SegDesc {
   const void* src;          // buffer elements, already offset to the segment's first column
   void* dst;                // dense output (SEG_Q)
@@ -89,6 +103,11 @@ struct BandArgs {
 };
 
 enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+
+// Largest passes-per-wave the kernel for this op holds in registers.
+inline uint32_t max_passes(bool radd, bool norm) {
+  return radd ? kMaxPassesRadd : (norm ? kMaxPassesNorm : kMaxPassesStore);
+}
 
 // Launch the band engine; returns 0 or a hipError_t value.
 int launch_band(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interleaved, bool radd,

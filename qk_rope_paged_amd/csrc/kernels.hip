@@ -54,8 +54,38 @@ struct Fmt<uint16_t> {  // bf16 stored as raw 16-bit words
   static constexpr int E = 8;
 };
 
+// Streamed rows (read once / written once) may bypass cache retention with
+// nontemporal accesses; the switches exist to measure both forms.
+#ifndef QRP_NT_LOADS
+#define QRP_NT_LOADS 1
+#endif
+#ifndef QRP_NT_STORES
+#define QRP_NT_STORES 1
+#endif
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void st16(void* p, const uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// a head-row chunk that is read exactly once
+__device__ __forceinline__ uint4 ld16s(const void* p) {
+#if QRP_NT_LOADS
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return ld16(p);
+#endif
+}
+
+// a head-row chunk that is written exactly once
+__device__ __forceinline__ void st16s(void* p, const uint4 v) {
+#if QRP_NT_STORES
+  const v4u w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<v4u*>(p));
+#else
+  *reinterpret_cast<uint4*>(p) = v;
+#endif
+}
 
 template <typename T>
 __device__ __forceinline__ void unpack(const uint4 v, float* f) {
@@ -165,7 +195,54 @@ __device__ __forceinline__ uint32_t seg_of(const BandArgs& a, uint32_t kp) {
   return s;
 }
 
-template <typename T, int D, bool IL, int NPMAX, bool RADD>
+// This lane's (cos, sin) entries of freqs row `pos`: the 2E table floats of
+// the frequencies its chunks rotate (zero where a chunk is not rotated).
+template <typename T, bool IL>
+__device__ __forceinline__ void load_freqs(const float* __restrict__ freqs, uint32_t rope_dim,
+                                           uint32_t pos, uint32_t c0, uint32_t c1, uint32_t j,
+                                           bool rot0, bool rot1, float* fl) {
+  constexpr int E = Fmt<T>::E;
+#pragma unroll
+  for (int e = 0; e < 2 * E; ++e) fl[e] = 0.f;
+  const float* fr = freqs + (int64_t)pos * rope_dim;
+  if constexpr (IL) {
+    // chunk c holds pairs c*E/2 .. c*E/2 + E/2 - 1: table columns c*E .. c*E + E - 1
+    if (rot0) {
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) {
+        const uint4 v = ld16(fr + c0 * E + 4 * q);
+        fl[4 * q] = __uint_as_float(v.x);
+        fl[4 * q + 1] = __uint_as_float(v.y);
+        fl[4 * q + 2] = __uint_as_float(v.z);
+        fl[4 * q + 3] = __uint_as_float(v.w);
+      }
+    }
+    if (rot1) {
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) {
+        const uint4 v = ld16(fr + c1 * E + 4 * q);
+        fl[E + 4 * q] = __uint_as_float(v.x);
+        fl[E + 4 * q + 1] = __uint_as_float(v.y);
+        fl[E + 4 * q + 2] = __uint_as_float(v.z);
+        fl[E + 4 * q + 3] = __uint_as_float(v.w);
+      }
+    }
+  } else {
+    // a half-split lane j < rope_dim/(2E) rotates frequencies j*E .. j*E + E - 1
+    if (rot0) {
+#pragma unroll
+      for (int q = 0; q < E / 2; ++q) {
+        const uint4 v = ld16(fr + 2 * j * E + 4 * q);
+        fl[4 * q] = __uint_as_float(v.x);
+        fl[4 * q + 1] = __uint_as_float(v.y);
+        fl[4 * q + 2] = __uint_as_float(v.z);
+        fl[4 * q + 3] = __uint_as_float(v.w);
+      }
+    }
+  }
+}
+
+template <typename T, int D, bool IL, int NPMAX, bool RADD, bool NORM>
 __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   constexpr int E = Fmt<T>::E;
   constexpr int CH = D / E;      // 16-byte chunks per head row
@@ -177,7 +254,23 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t blk = blockIdx.x;
   if (a.per_xcd) blk = (blk % kXcds) * a.per_xcd + blk / kXcds;
-  if (blk >= a.n_blocks) return;
+  if (blk >= a.n_blocks) return;  // the whole block leaves together
+
+  // Gammas of every segment, once per block, in LDS.  Reading them there
+  // keeps the store loop free of vector-memory loads (vmcnt counts stores as
+  // well as loads, so a load issued after a store would wait for it).
+  __shared__ uint4 lds_gamma[NORM ? kMaxSegs : 1][NORM ? CH : 1];
+  if constexpr (NORM) {
+    for (uint32_t i = threadIdx.x; i < kMaxSegs * CH; i += kThreads) {
+      const uint32_t si = i / CH, c = i % CH;
+      uint4 g = make_uint4(0, 0, 0, 0);
+      if (si < a.nseg && a.seg[si].gamma != nullptr)
+        g = ld16(reinterpret_cast<const T*>(a.seg[si].gamma) + c * E);
+      lds_gamma[si][c] = g;
+    }
+    __syncthreads();
+  }
+
   const uint32_t item = blk * kWavesPerBlock + wave;
   if (item >= a.n_items) return;
 
@@ -209,8 +302,8 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
         const uint32_t h = min((kp - sd.pass_begin) * RPP + row, sd.n_heads - 1);
         const T* src = reinterpret_cast<const T*>(sd.src) + (int64_t)t * sd.src_row_stride +
                        (int64_t)h * D;
-        x[p][0] = ld16(src + c0 * E);
-        x[p][1] = ld16(src + c1 * E);
+        x[p][0] = ld16s(src + c0 * E);
+        x[p][1] = ld16s(src + c1 * E);
       }
     }
   }
@@ -264,76 +357,28 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
         const T* src = reinterpret_cast<const T*>(cd.blocks) + base[sd.cache] +
                        (int64_t)sd.plane * cd.plane_stride + (int64_t)h * cd.head_stride;
         if constexpr (RADD) {
-          y[p][0] = ld16(src + c0 * E);
-          y[p][1] = ld16(src + c1 * E);
+          y[p][0] = ld16s(src + c0 * E);
+          y[p][1] = ld16s(src + c1 * E);
         } else {
-          x[p][0] = ld16(src + c0 * E);
-          x[p][1] = ld16(src + c1 * E);
+          x[p][0] = ld16s(src + c0 * E);
+          x[p][1] = ld16s(src + c1 * E);
         }
       }
     }
   }
 
   // ---- D: this lane's (cos, sin) entries of the token's freqs row ----
-  float fl[kMaxCaches][2 * E];
-  if constexpr (!RADD) {
-#pragma unroll
-    for (int ci = 0; ci < kMaxCaches; ++ci) {
-#pragma unroll
-      for (int e = 0; e < 2 * E; ++e) fl[ci][e] = 0.f;
-    }
-#pragma unroll
-    for (int ci = 0; ci < kMaxCaches; ++ci) {
-      if ((uint32_t)ci < a.ncache && (ci == 0 || pos[ci] != pos[0])) {
-        const float* fr = a.freqs + (int64_t)pos[ci] * a.rope_dim;
-        if constexpr (IL) {
-          // chunk c holds pairs c*E/2 .. c*E/2 + E/2 - 1: table columns c*E .. c*E + E - 1
-          if (rot0) {
-#pragma unroll
-            for (int q = 0; q < E / 4; ++q) {
-              const uint4 v = ld16(fr + c0 * E + 4 * q);
-              fl[ci][4 * q] = __uint_as_float(v.x);
-              fl[ci][4 * q + 1] = __uint_as_float(v.y);
-              fl[ci][4 * q + 2] = __uint_as_float(v.z);
-              fl[ci][4 * q + 3] = __uint_as_float(v.w);
-            }
-          }
-          if (rot1) {
-#pragma unroll
-            for (int q = 0; q < E / 4; ++q) {
-              const uint4 v = ld16(fr + c1 * E + 4 * q);
-              fl[ci][E + 4 * q] = __uint_as_float(v.x);
-              fl[ci][E + 4 * q + 1] = __uint_as_float(v.y);
-              fl[ci][E + 4 * q + 2] = __uint_as_float(v.z);
-              fl[ci][E + 4 * q + 3] = __uint_as_float(v.w);
-            }
-          }
-        } else {
-          // half-split lane j < hh rotates frequencies j*E .. j*E + E - 1
-          if (rot0) {
-#pragma unroll
-            for (int q = 0; q < E / 2; ++q) {
-              const uint4 v = ld16(fr + 2 * j * E + 4 * q);
-              fl[ci][4 * q] = __uint_as_float(v.x);
-              fl[ci][4 * q + 1] = __uint_as_float(v.y);
-              fl[ci][4 * q + 2] = __uint_as_float(v.z);
-              fl[ci][4 * q + 3] = __uint_as_float(v.w);
-            }
-          }
-        }
-      } else if ((uint32_t)ci < a.ncache) {
-#pragma unroll
-        for (int e = 0; e < 2 * E; ++e) fl[ci][e] = fl[0][e];
-      }
-    }
-  }
+  float fl[RADD ? 1 : 2 * E];
+  uint32_t fl_pos = pos[0];
+  if constexpr (!RADD) load_freqs<T, IL>(a.freqs, a.rope_dim, fl_pos, c0, c1, j, rot0, rot1, fl);
 
   // ---- E: arithmetic and stores ----
 #pragma unroll
   for (int p = 0; p < NPMAX; ++p) {
     if ((uint32_t)p < np) {
       const uint32_t kp = p0 + p;
-      const SegDesc& sd = a.seg[seg_of(a, kp)];
+      const uint32_t si = seg_of(a, kp);
+      const SegDesc& sd = a.seg[si];
       const uint32_t kind = sd.kind;
       const uint32_t h = (kp - sd.pass_begin) * RPP + row;
       const bool active = h < sd.n_heads;
@@ -366,101 +411,111 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
           float v0[E], v1[E];
           unpack<T>(x[p][0], v0);
           unpack<T>(x[p][1], v1);
-          const bool norm = sd.gamma != nullptr;
-          if (norm) {
-            float ss = 0.f;
+          const bool norm = NORM && sd.gamma != nullptr;
+          if constexpr (NORM) {
+            if (norm) {
+              float ss = 0.f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) ss += v0[e] * v0[e] + v1[e] * v1[e];
-            ss = row_sum<LPR>(ss);
-            const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + sd.eps);
-            const T* gp = reinterpret_cast<const T*>(sd.gamma);
-            float g0[E], g1[E];
-            unpack<T>(ld16(gp + c0 * E), g0);
-            unpack<T>(ld16(gp + c1 * E), g1);
-            const float w = a.weight_offset;
-            if (a.multiply_before_cast) {
+              for (int e = 0; e < E; ++e) ss += v0[e] * v0[e] + v1[e] * v1[e];
+              ss = row_sum<LPR>(ss);
+              const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + sd.eps);
+              float g0[E], g1[E];
+              unpack<T>(lds_gamma[si][c0], g0);
+              unpack<T>(lds_gamma[si][c1], g1);
+              const float w = a.weight_offset;
+              if (a.multiply_before_cast) {
 #pragma unroll
-              for (int e = 0; e < E; ++e) {
-                v0[e] = v0[e] * r * (g0[e] + w);
-                v1[e] = v1[e] * r * (g1[e] + w);
-              }
-            } else {
+                for (int e = 0; e < E; ++e) {
+                  v0[e] = v0[e] * r * (g0[e] + w);
+                  v1[e] = v1[e] * r * (g1[e] + w);
+                }
+              } else {
 #pragma unroll
-              for (int e = 0; e < E; ++e) {
-                v0[e] = to_dtype<T>(to_dtype<T>(v0[e] * r) * to_dtype<T>(g0[e] + w));
-                v1[e] = to_dtype<T>(to_dtype<T>(v1[e] * r) * to_dtype<T>(g1[e] + w));
+                for (int e = 0; e < E; ++e) {
+                  v0[e] = to_dtype<T>(to_dtype<T>(v0[e] * r) * to_dtype<T>(g0[e] + w));
+                  v1[e] = to_dtype<T>(to_dtype<T>(v1[e] * r) * to_dtype<T>(g1[e] + w));
+                }
               }
             }
           }
-          const float* f = fl[sd.cache ? 1 : 0];
-          float r0[E], r1[E];
+          // Segments run cache 0 first, then cache 1; a second cache whose
+          // cache length differs for this sequence needs the freqs row of its
+          // own position (uniform, taken at most once per wave).
+          if (pos[sd.cache] != fl_pos) {
+            fl_pos = pos[sd.cache];
+            load_freqs<T, IL>(a.freqs, a.rope_dim, fl_pos, c0, c1, j, rot0, rot1, fl);
+          }
           if constexpr (IL) {
 #pragma unroll
             for (int m = 0; m < E / 2; ++m) {
-              const float cs = f[2 * m], sn = f[2 * m + 1];
-              r0[2 * m] = v0[2 * m] * cs - v0[2 * m + 1] * sn;
-              r0[2 * m + 1] = v0[2 * m] * sn + v0[2 * m + 1] * cs;
-              const float cs1 = f[E + 2 * m], sn1 = f[E + 2 * m + 1];
-              r1[2 * m] = v1[2 * m] * cs1 - v1[2 * m + 1] * sn1;
-              r1[2 * m + 1] = v1[2 * m] * sn1 + v1[2 * m + 1] * cs1;
+              const float a0 = v0[2 * m], b0 = v0[2 * m + 1];
+              const float cs = fl[2 * m], sn = fl[2 * m + 1];
+              v0[2 * m] = rot0 ? a0 * cs - b0 * sn : a0;
+              v0[2 * m + 1] = rot0 ? a0 * sn + b0 * cs : b0;
+              const float a1 = v1[2 * m], b1 = v1[2 * m + 1];
+              const float cs1 = fl[E + 2 * m], sn1 = fl[E + 2 * m + 1];
+              v1[2 * m] = rot1 ? a1 * cs1 - b1 * sn1 : a1;
+              v1[2 * m + 1] = rot1 ? a1 * sn1 + b1 * cs1 : b1;
             }
           } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-              const float cs = f[2 * e], sn = f[2 * e + 1];
-              r0[e] = v0[e] * cs - v1[e] * sn;
-              r1[e] = v0[e] * sn + v1[e] * cs;
+              const float re = v0[e], im = v1[e];
+              const float cs = fl[2 * e], sn = fl[2 * e + 1];
+              v0[e] = rot0 ? re * cs - im * sn : re;
+              v1[e] = rot0 ? re * sn + im * cs : im;
             }
           }
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            r0[e] = rot0 ? r0[e] : v0[e];
-            r1[e] = rot1 ? r1[e] : v1[e];
-          }
-          o0 = (norm || rot0) ? pack<T>(r0) : x[p][0];
-          o1 = (norm || rot1) ? pack<T>(r1) : x[p][1];
+          o0 = (norm || rot0) ? pack<T>(v0) : x[p][0];
+          o1 = (norm || rot1) ? pack<T>(v1) : x[p][1];
         }
       }
       if (active) {
-        st16(dst + c0 * E, o0);
-        st16(dst + c1 * E, o1);
+        st16s(dst + c0 * E, o0);
+        st16s(dst + c1 * E, o1);
       }
     }
   }
 }
 
-template <typename T, int D, bool IL, bool RADD>
+template <typename T, int D, bool IL, bool RADD, bool NORM>
 int launch_t(const BandArgs& a, void* stream) {
-  constexpr int NPMAX = RADD ? 4 : 6;
+  constexpr int NPMAX = RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : kMaxPassesStore);
   const uint32_t grid = a.per_xcd ? a.per_xcd * kXcds : a.n_blocks;
-  hipLaunchKernelGGL((band_kernel<T, D, IL, NPMAX, RADD>), dim3(grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((band_kernel<T, D, IL, NPMAX, RADD, NORM>), dim3(grid), dim3(kThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
-template <typename T, bool IL, bool RADD>
+template <typename T, bool IL, bool RADD, bool NORM>
 int launch_d(const BandArgs& a, uint32_t head_dim, void* stream) {
   switch (head_dim) {
-    case 64: return launch_t<T, 64, IL, RADD>(a, stream);
-    case 128: return launch_t<T, 128, IL, RADD>(a, stream);
-    case 256: return launch_t<T, 256, IL, RADD>(a, stream);
+    case 64: return launch_t<T, 64, IL, RADD, NORM>(a, stream);
+    case 128: return launch_t<T, 128, IL, RADD, NORM>(a, stream);
+    case 256: return launch_t<T, 256, IL, RADD, NORM>(a, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }
 
 template <typename T>
-int launch_dt(const BandArgs& a, uint32_t head_dim, bool interleaved, bool radd, void* stream) {
-  if (radd) return launch_d<T, true, true>(a, head_dim, stream);
-  return interleaved ? launch_d<T, true, false>(a, head_dim, stream)
-                     : launch_d<T, false, false>(a, head_dim, stream);
+int launch_dt(const BandArgs& a, uint32_t head_dim, bool interleaved, bool radd, bool norm,
+              void* stream) {
+  if (radd) return launch_d<T, true, true, false>(a, head_dim, stream);
+  if (norm)
+    return interleaved ? launch_d<T, true, false, true>(a, head_dim, stream)
+                       : launch_d<T, false, false, true>(a, head_dim, stream);
+  return interleaved ? launch_d<T, true, false, false>(a, head_dim, stream)
+                     : launch_d<T, false, false, false>(a, head_dim, stream);
 }
 
 }  // namespace
 
 int launch_band(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interleaved, bool radd,
                 void* stream) {
-  if (dtype == DT_F32) return launch_dt<float>(a, head_dim, interleaved, radd, stream);
-  return launch_dt<uint16_t>(a, head_dim, interleaved, radd, stream);
+  bool norm = false;
+  for (uint32_t s = 0; s < a.nseg; ++s) norm = norm || a.seg[s].gamma != nullptr;
+  if (dtype == DT_F32) return launch_dt<float>(a, head_dim, interleaved, radd, norm, stream);
+  return launch_dt<uint16_t>(a, head_dim, interleaved, radd, norm, stream);
 }
 
 }  // namespace qrp

@@ -8,16 +8,16 @@ oracle.  Nothing here computes any part of the method itself.
 
 Workload shapes follow the configurations the pass is measured on:
 
-* ``c1``  tiny fp32 interleaved store (batch 2, lengths {3, 5}, cache lengths
+* ``tiny_fp32``  tiny fp32 interleaved store (batch 2, lengths {3, 5}, cache lengths
   {0, 4}, 4 Q / 2 KV heads, head_dim 64, page 16, 8 pages);
-* ``c2``  Llama-3-8B-shaped bf16 prefill store, half-split RoPE (batch 8,
+* ``prefill``    Llama-3-8B-shaped bf16 prefill store, half-split RoPE (batch 8,
   lengths U[128, 2048], 32 Q / 8 KV heads, head_dim 128, theta 5e5, page 128,
   32 layers, layer 17);
-* ``c3``  the matching decode (256 sequences x 1 token, cache lengths
+* ``decode``     the matching decode (256 sequences x 1 token, cache lengths
   U[0, 8191], interleaved, 20000-page pool);
-* ``c4``  dual-band RMSNorm + RoPE (main 64 Q / 8 KV heads, index 16 Q heads
+* ``dual``       dual-band RMSNorm + RoPE (main 64 Q / 8 KV heads, index 16 Q heads
   + single-head K-only cache, head_dim 128, rope_dim 64, page 64);
-* ``c5``  K/V radd (8 KV heads, head_dim 128, batch 32 of a 64-sequence
+* ``radd``       K/V radd (8 KV heads, head_dim 128, batch 32 of a 64-sequence
   cache at batch_offset 4, page 128, layer 3).
 
 ``small=True`` gives a reduced variant of each that the oracle finishes in
@@ -418,45 +418,45 @@ def make_radd_case(name: str, seed: int, dtype: str, lengths, cache_lengths, bat
 # the five workloads
 # ---------------------------------------------------------------------------
 
-def c1(seed: int = 1) -> Case:
-    return make_store_case("c1_tiny_fp32", seed, F32, [3, 5], [0, 4], Hq=4, Hk=2, D=64,
+def tiny_fp32(seed: int = 1) -> Case:
+    return make_store_case("tiny_fp32", seed, F32, [3, 5], [0, 4], Hq=4, Hk=2, D=64,
                            rope_dim=64, interleaved=True, theta=1e4, max_seq_len=64, P=16, L=1,
                            layer=0, num_pages=8, max_pages=4)
 
 
-def c2(seed: int = 2, small: bool = False) -> Case:
+def prefill(seed: int = 2, small: bool = False) -> Case:
     if small:
         B = 4
         lens = prng.integers(seed, S_LENS, B, 1, 300)
-        return make_store_case("c2_prefill_small", seed, BF16, lens, np.zeros(B, np.int64), Hq=32,
+        return make_store_case("prefill_small", seed, BF16, lens, np.zeros(B, np.int64), Hq=32,
                                Hk=8, D=128, rope_dim=128, interleaved=False, theta=5e5,
                                max_seq_len=8192, P=128, L=4, layer=2)
     B = 8
     lens = prng.integers(seed, S_LENS, B, 128, 2048)
-    return make_store_case("c2_prefill", seed, BF16, lens, np.zeros(B, np.int64), Hq=32, Hk=8,
+    return make_store_case("prefill", seed, BF16, lens, np.zeros(B, np.int64), Hq=32, Hk=8,
                            D=128, rope_dim=128, interleaved=False, theta=5e5, max_seq_len=8192,
                            P=128, L=32, layer=17)
 
 
-def c3(seed: int = 3, small: bool = False) -> Case:
+def decode(seed: int = 3, small: bool = False) -> Case:
     B = 32 if small else 256
     lens = np.ones(B, dtype=np.int64)
     clen = prng.integers(seed, S_CLEN, B, 0, 8191)
-    return make_store_case("c3_decode_small" if small else "c3_decode", seed, BF16, lens, clen,
+    return make_store_case("decode_small" if small else "decode", seed, BF16, lens, clen,
                            Hq=32, Hk=8, D=128, rope_dim=128, interleaved=True, theta=5e5,
                            max_seq_len=8192, P=128, L=1, layer=0,
                            num_pages=1400 if small else 20000, max_pages=64)
 
 
-def c4(seed: int = 4, small: bool = False) -> Case:
+def dual(seed: int = 4, small: bool = False) -> Case:
     B = 4 if small else 16
     lens = prng.integers(seed, S_LENS, B, 1, 150 if small else 1024)
-    return make_dual_case("c4_dual_small" if small else "c4_dual", seed, BF16, lens, Hq_main=64,
+    return make_dual_case("dual_small" if small else "dual", seed, BF16, lens, Hq_main=64,
                           Hk_main=8, Hq_index=16, D=128, rope_dim=64, interleaved=True,
                           theta=1e4, max_seq_len=8192, P_main=64, P_index=64)
 
 
-def c5(seed: int = 5, small: bool = False) -> Case:
+def radd(seed: int = 5, small: bool = False) -> Case:
     if small:
         B, cb, boff = 6, 12, 4
         lens = prng.integers(seed, S_LENS, B, 1, 64)
@@ -465,8 +465,9 @@ def c5(seed: int = 5, small: bool = False) -> Case:
         B, cb, boff = 32, 64, 4
         lens = prng.integers(seed, S_LENS, B, 16, 512)
         clen = prng.integers(seed, S_CLEN, cb, 0, 4096)
-    return make_radd_case("c5_radd_small" if small else "c5_radd", seed, BF16, lens, clen, boff,
+    return make_radd_case("radd_small" if small else "radd", seed, BF16, lens, clen, boff,
                           Hk=8, D=128, P=128, L=4, layer=3)
 
 
-CONFIGS = {"c1": c1, "c2": c2, "c3": c3, "c4": c4, "c5": c5}
+WORKLOADS = {"tiny_fp32": tiny_fp32, "prefill": prefill, "decode": decode, "dual": dual,
+             "radd": radd}

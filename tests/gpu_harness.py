@@ -124,71 +124,27 @@ def band_of(dc: DeviceCase, i: int) -> qrp.Band:
                     q_output=dc.q_out_rows(i), q_out_row_stride=b.q_out_row_stride)
 
 
-def run(dc: DeviceCase, stream=None, raise_on_error=True, op=None) -> int:
-    """One call of the case's operation through the C ABI."""
+def run(dc: DeviceCase, stream=None, raise_on_error=True, op=None, prepare=False):
+    """One call of the case's operation through the C ABI (or, with
+    ``prepare``, the call bound to its marshalled arguments)."""
     c = dc.case
     op = op or c.op
     dt = QRP_DT[c.dtype]
+    kw = dict(stream=stream, raise_on_error=raise_on_error, prepare=prepare)
     if op == "store":
         return qrp.rope_split_store_paged(
             dc.buf, dt, c.T, c.row_stride, c.n_q_heads, dc.offsets, c.batch, rope_of(dc),
-            dc.caches[0].desc, c.layer_idx, dc.q_out_rows(0), dt, c.q_out_row_stride,
-            stream=stream, raise_on_error=raise_on_error)
+            dc.caches[0].desc, c.layer_idx, dc.q_out_rows(0), dt, c.q_out_row_stride, **kw)
     if op == "norm":
         return qrp.qk_rmsnorm_rope_paged(
             dc.buf, dt, c.T, c.row_stride, band_of(dc, 0), c.weight_offset,
-            c.multiply_before_cast, dc.offsets, c.batch, rope_of(dc), c.layer_idx,
-            stream=stream, raise_on_error=raise_on_error)
+            c.multiply_before_cast, dc.offsets, c.batch, rope_of(dc), c.layer_idx, **kw)
     if op == "dual":
         return qrp.dual_band(
             dc.buf, dt, c.T, c.row_stride, band_of(dc, 0), band_of(dc, 1), c.weight_offset,
-            c.multiply_before_cast, dc.offsets, c.batch, rope_of(dc), c.layer_idx,
-            stream=stream, raise_on_error=raise_on_error)
+            c.multiply_before_cast, dc.offsets, c.batch, rope_of(dc), c.layer_idx, **kw)
     if op == "radd":
         return qrp.kv_cache_radd(
             dc.buf, dt, c.T, c.row_stride, dc.offsets, c.batch, c.batch_offset,
-            dc.caches[0].desc, c.layer_idx, stream=stream, raise_on_error=raise_on_error)
+            dc.caches[0].desc, c.layer_idx, **kw)
     raise ValueError(op)
-
-
-def algorithmic_bytes(case: sc.Case) -> int:
-    """Bytes the operation must move: inputs read, outputs written, cache rows
-    read for in-place updates, distinct freqs rows, metadata and gammas."""
-    eb = sc.ELEM_BYTES[case.dtype]
-    T = case.T
-    total = 0
-    if case.op == "store":
-        c = case.caches[0]
-        D, Hk, Hq = c.head_dim, c.num_kv_heads, case.n_q_heads
-        total += T * (Hq + 2 * Hk) * D * eb          # qkv read
-        total += T * (Hq + 2 * Hk) * D * eb          # q_out + K + V written
-    elif case.op in ("norm", "dual"):
-        for b in case.bands:
-            c = case.caches[b.cache]
-            D, Hk = c.head_dim, c.num_kv_heads
-            total += 2 * T * b.n_q_heads * D * eb    # Q read + written
-            total += 2 * T * Hk * D * eb             # K read (buffer or cache) + written
-            if b.v_col >= 0:
-                total += 2 * T * Hk * D * eb         # V read + written
-            total += (int(b.q_gamma is not None) + int(b.k_gamma is not None)) * D * eb
-    elif case.op == "radd":
-        c = case.caches[0]
-        total += 3 * T * 2 * c.num_kv_heads * c.head_dim * eb   # read a, read cache, write cache
-    if case.freqs is not None and T:
-        pos = token_positions(case)
-        total += len(np.unique(pos)) * case.rope_dim * 4
-    total += (case.batch + 1) * 4                                 # offsets
-    for c in case.caches:
-        total += min(c.cache_batch, case.batch) * 4                # cache lengths
-        total += T * 4                                             # page-table entries (upper bound: one per token)
-    return int(total)
-
-
-def token_positions(case: sc.Case) -> np.ndarray:
-    off = case.offsets.astype(np.int64)
-    out = []
-    for b in range(case.batch):
-        n = int(off[b + 1] - off[b])
-        cl = int(case.caches[0].cache_lengths[b + case.batch_offset])
-        out.append(np.arange(cl, cl + n))
-    return np.concatenate(out) if out else np.zeros(0, np.int64)

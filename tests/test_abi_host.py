@@ -1,0 +1,226 @@
+"""Host-side checks of the C ABI, no GPU needed.
+
+* the library loads and exports every function include/qk_rope_paged.h
+  declares;
+* the package ends up with one HIP runtime in the process (torch's);
+* every invalid-argument path returns its status code before anything is
+  launched (the pointers below are never dereferenced: the calls fail on the
+  host first);
+* qrp_validate_host finds each kind of inconsistent metadata.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import qk_rope_paged_amd as qrp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qk_rope_paged.h")
+FAKE = 0x10000          # 16-byte aligned stand-in for a device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:int32_t|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"rope_split_store_paged", "qk_rmsnorm_rope_paged", "dual_band",
+                          "kv_cache_radd", "qrp_validate", "qrp_validate_host",
+                          "qrp_last_error", "qrp_abi_version"}
+    lib = ctypes.CDLL(qrp.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(qrp.EXPORTS)
+    assert qrp.abi_version() == 1
+
+
+def test_one_hip_runtime_in_process():
+    maps = open("/proc/self/maps").read()
+    libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(libs) <= 1, libs
+
+
+def _cache(**kw):
+    d = dict(blocks=FAKE, dtype=qrp.QRP_BF16, num_kv_heads=8, head_dim=128, page_size=128,
+             num_layers=2, kv_planes=2, num_pages=16, page_stride=2 * 2 * 128 * 8 * 128,
+             plane_stride=2 * 128 * 8 * 128, layer_stride=128 * 8 * 128, slot_stride=8 * 128,
+             head_stride=128, cache_lengths=FAKE, lookup_table=FAKE, cache_batch=4,
+             max_pages_per_seq=4)
+    d.update(kw)
+    return qrp.PagedCache(**d)
+
+
+def _rope(**kw):
+    d = dict(freqs_cis=FAKE, max_seq_len=512, rope_dim=128, interleaved=True)
+    d.update(kw)
+    return qrp.Rope(**d)
+
+
+def _store(cache=None, rope=None, **kw):
+    a = dict(qkv=FAKE, dtype=qrp.QRP_BF16, total_seq_len=8, qkv_row_stride=48 * 128, n_q_heads=32,
+             input_row_offsets=FAKE, batch_size=2, rope=rope or _rope(), cache=cache or _cache(),
+             layer_idx=1, q_output=FAKE, q_out_dtype=qrp.QRP_BF16, q_out_row_stride=32 * 128,
+             stream=0, raise_on_error=False)
+    a.update(kw)
+    return qrp.rope_split_store_paged(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), qrp.QRP_EUNSUPPORTED),
+    (dict(q_out_dtype=qrp.QRP_F32), qrp.QRP_EUNSUPPORTED),
+    (dict(batch_size=0), qrp.QRP_EINVAL),
+    (dict(input_row_offsets=None), qrp.QRP_EINVAL),
+    (dict(qkv=None), qrp.QRP_EINVAL),
+    (dict(q_output=None), qrp.QRP_EINVAL),
+    (dict(qkv=FAKE + 8), qrp.QRP_EALIGN),
+    (dict(q_output=FAKE + 4), qrp.QRP_EALIGN),
+    (dict(qkv_row_stride=48 * 128 + 4), qrp.QRP_EALIGN),
+    (dict(qkv_row_stride=47 * 128), qrp.QRP_EINVAL),
+    (dict(q_out_row_stride=31 * 128), qrp.QRP_EINVAL),
+    (dict(n_q_heads=0), qrp.QRP_EINVAL),
+    (dict(layer_idx=2), qrp.QRP_EINVAL),
+    (dict(batch_size=5), qrp.QRP_EINVAL),
+    (dict(cache=_cache(head_dim=96)), qrp.QRP_EUNSUPPORTED),
+    (dict(cache=_cache(dtype=qrp.QRP_F32)), qrp.QRP_EUNSUPPORTED),
+    (dict(cache=_cache(kv_planes=1)), qrp.QRP_EINVAL),
+    (dict(cache=_cache(page_size=0)), qrp.QRP_EINVAL),
+    (dict(cache=_cache(blocks=FAKE + 2)), qrp.QRP_EALIGN),
+    (dict(cache=_cache(head_stride=100)), qrp.QRP_EALIGN),
+    (dict(cache=_cache(lookup_table=None)), qrp.QRP_EINVAL),
+    (dict(rope=_rope(rope_dim=130)), qrp.QRP_EINVAL),
+    (dict(rope=_rope(rope_dim=7)), qrp.QRP_EINVAL),
+    (dict(rope=_rope(rope_dim=8)), qrp.QRP_EUNSUPPORTED),
+    (dict(rope=_rope(max_seq_len=0)), qrp.QRP_EINVAL),
+    (dict(rope=_rope(freqs_cis=None)), qrp.QRP_EINVAL),
+])
+def test_store_argument_errors(kw, code):
+    assert _store(**kw) == code
+    assert qrp.last_error() != ""
+
+
+def test_empty_batch_returns_ok_without_touching_anything():
+    assert _store(total_seq_len=0, qkv=None, q_output=None, input_row_offsets=None) == qrp.QRP_OK
+
+
+def _band(cache=None, **kw):
+    d = dict(q_col=0, n_q_heads=64, k_col=-1, v_col=-1, q_gamma=FAKE, k_gamma=FAKE, epsilon=1e-6,
+             cache=cache or _cache(), q_output=FAKE, q_out_row_stride=64 * 128)
+    d.update(kw)
+    return qrp.Band(**d)
+
+
+def _dual(main=None, index=None, **kw):
+    idx_cache = _cache(num_kv_heads=1, kv_planes=1, page_stride=128 * 128, plane_stride=128 * 128,
+                       layer_stride=128 * 128, slot_stride=128)
+    a = dict(buf=FAKE, dtype=qrp.QRP_BF16, total_seq_len=8, buf_row_stride=96 * 128,
+             main_band=main or _band(),
+             index_band=index or _band(cache=idx_cache, q_col=80 * 128, n_q_heads=16,
+                                       q_out_row_stride=16 * 128),
+             weight_offset=0.0, multiply_before_cast=True, input_row_offsets=FAKE, batch_size=2,
+             rope=_rope(rope_dim=64), layer_idx=0, stream=0, raise_on_error=False)
+    a.update(kw)
+    return qrp.dual_band(**a)
+
+
+def test_dual_band_geometry_and_argument_errors():
+    assert _dual(index=_band(cache=_cache(head_dim=64, num_kv_heads=1), n_q_heads=16)) == \
+        qrp.QRP_EGEOMETRY
+    assert _dual(index=_band(cache=_cache(dtype=qrp.QRP_F32), n_q_heads=16)) == qrp.QRP_EGEOMETRY
+    assert _dual(main=_band(k_col=64 * 128, v_col=72 * 128)) == qrp.QRP_EUNSUPPORTED
+    assert _dual(main=_band(q_col=40 * 128)) == qrp.QRP_EINVAL          # Q past the row end
+    assert _dual(main=_band(q_gamma=FAKE + 2)) == qrp.QRP_EALIGN
+    assert _dual(main=_band(q_output=None)) == qrp.QRP_EINVAL
+    assert _dual(buf_row_stride=96 * 128 + 3) == qrp.QRP_EALIGN
+
+
+def test_norm_band_errors():
+    def call(band, **kw):
+        a = dict(qkv=FAKE, dtype=qrp.QRP_BF16, total_seq_len=4, qkv_row_stride=48 * 128,
+                 band=band, weight_offset=0.0, multiply_before_cast=True, input_row_offsets=FAKE,
+                 batch_size=1, rope=_rope(), layer_idx=0, stream=0, raise_on_error=False)
+        a.update(kw)
+        return qrp.qk_rmsnorm_rope_paged(**a)
+    assert call(_band(n_q_heads=32, v_col=40 * 128)) == qrp.QRP_EINVAL      # V without K column
+    assert call(_band(n_q_heads=32, k_col=32 * 128, v_col=40 * 128,
+                      cache=_cache(kv_planes=1))) == qrp.QRP_EINVAL          # V without V plane
+    assert call(_band(n_q_heads=32, k_col=41 * 128)) == qrp.QRP_EINVAL      # K past the row end
+    assert call(_band(n_q_heads=32, q_col=4)) == qrp.QRP_EALIGN
+
+
+def test_radd_errors():
+    def call(**kw):
+        a = dict(a=FAKE, dtype=qrp.QRP_BF16, total_rows=4, a_row_stride=2 * 8 * 128,
+                 input_row_offsets=FAKE, batch_size=2, batch_offset=2, cache=_cache(),
+                 layer_idx=0, stream=0, raise_on_error=False)
+        a.update(kw)
+        return qrp.kv_cache_radd(**a)
+    assert call(batch_offset=3) == qrp.QRP_EINVAL                  # 3 + 2 > cache_batch 4
+    assert call(a_row_stride=2 * 8 * 128 - 8) == qrp.QRP_EINVAL
+    assert call(cache=_cache(kv_planes=1)) == qrp.QRP_EINVAL
+    assert call(a=FAKE + 6) == qrp.QRP_EALIGN
+    assert call(total_rows=0, a=None) == qrp.QRP_OK
+
+
+def test_raise_on_error_raises():
+    with pytest.raises(qrp.QrpError) as e:
+        _store(dtype=9, raise_on_error=True)
+    assert e.value.status == qrp.QRP_EUNSUPPORTED
+
+
+# --------------------------------------------------------------------------
+# qrp_validate_host
+# --------------------------------------------------------------------------
+
+def _meta():
+    off = np.array([0, 3, 3, 8], np.uint32)               # sequence 1 is empty
+    lens = np.array([0, 40, 4, 0], np.uint32)
+    tab = np.arange(16, dtype=np.uint32).reshape(4, 4)
+    return off, lens, tab
+
+
+def _validate(off, lens, tab, B=3, T=8, boff=0, P=16, num_pages=16, msl=64):
+    return qrp.qrp_validate_host(off, B, T, boff, lens, tab, tab.shape[0], tab.shape[1], P,
+                                 num_pages, msl)
+
+
+def test_validate_accepts_good_metadata():
+    off, lens, tab = _meta()
+    assert _validate(off, lens, tab) == qrp.QRP_OK
+    assert _validate(off, lens, tab, boff=1) == qrp.QRP_OK
+
+
+@pytest.mark.parametrize("mutate,fragment", [
+    (lambda o, l, t: o.__setitem__(0, 1), "offsets[0]"),
+    (lambda o, l, t: o.__setitem__(2, 2), "decrease"),
+    (lambda o, l, t: o.__setitem__(3, 9), "total_seq_len"),
+    (lambda o, l, t: l.__setitem__(2, 60), "max_seq_len"),
+    (lambda o, l, t: t.__setitem__((2, 0), 99), "num_pages"),
+    (lambda o, l, t: (t.__setitem__((2, 0), 0), l.__setitem__(2, 1)), "same cache row"),
+])
+def test_validate_finds_bad_metadata(mutate, fragment):
+    off, lens, tab = _meta()
+    mutate(off, lens, tab)
+    assert _validate(off, lens, tab) == qrp.QRP_EDATA
+    assert fragment in qrp.last_error()
+
+
+def test_validate_allows_shared_pages_with_distinct_rows():
+    off, lens, tab = _meta()
+    tab[2, 0] = 0            # sequence 2 writes rows 4..8 of the page sequence 0 writes rows 0..2 of
+    assert _validate(off, lens, tab) == qrp.QRP_OK
+
+
+def test_validate_page_index_and_batch_offset_bounds():
+    off, lens, tab = _meta()
+    lens[2] = 60                                              # positions 60..64 -> page index 4
+    assert _validate(off, lens, tab, msl=0) == qrp.QRP_EDATA
+    assert "max_pages_per_seq" in qrp.last_error()
+    off, lens, tab = _meta()
+    assert _validate(off, lens, tab, boff=2) == qrp.QRP_EDATA   # 2 + 3 > 4 sequences

@@ -131,7 +131,7 @@ def _check_sentinels(case, pool, written):
 
 @pytest.mark.parametrize("interleaved", [True, False])
 def test_tiny_store_matches_complex_brute_force(interleaved):
-    case = sc.c1() if interleaved else _store_case(interleaved=False)
+    case = sc.tiny_fp32() if interleaved else _store_case(interleaved=False)
     res = oracle.run_case(case)
     assert res.status == 0
     written = _check_store_against_brute(case, res, pair_tol=2.0 ** -23)

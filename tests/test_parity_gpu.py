@@ -48,20 +48,20 @@ def run_and_compare(case, ulps=1):
 # the five workloads
 # ---------------------------------------------------------------------------
 
-def test_c1_tiny_fp32():
-    run_and_compare(sc.c1())
+def test_tiny_fp32():
+    run_and_compare(sc.tiny_fp32())
 
 
-@pytest.mark.parametrize("cfg", ["c2", "c3", "c4", "c5"])
-@pytest.mark.parametrize("seed", [0, 101])
-def test_small_workloads(cfg, seed):
-    s = seed or int(cfg[1])
-    run_and_compare(sc.CONFIGS[cfg](seed=s, small=True))
+@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd"])
+@pytest.mark.parametrize("seed", [None, 101])
+def test_small_workloads(workload, seed):
+    kw = {} if seed is None else {"seed": seed}
+    run_and_compare(sc.WORKLOADS[workload](small=True, **kw))
 
 
-@pytest.mark.parametrize("cfg", ["c2", "c3", "c4", "c5"])
-def test_full_size_workloads(cfg):
-    run_and_compare(sc.CONFIGS[cfg]())
+@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd"])
+def test_full_size_workloads(workload):
+    run_and_compare(sc.WORKLOADS[workload]())
 
 
 # ---------------------------------------------------------------------------
