@@ -127,7 +127,7 @@ typedef struct qrp_rope {
  *                stored into the cache (V heads from v_col.. copied when
  *                v_col >= 0);
  *   k_col <  0 : K is already in the cache and is normalised and rotated in
- *                place ("the respective key caches are updated in place").
+ *                place (each band's key cache is modified in place).
  * A NULL gamma skips the norm for that role.  The norm of a head x is
  *   x_j / sqrt(mean(x^2) + epsilon) * (gamma_j + weight_offset)
  * and it is applied before the rotation.

@@ -7,7 +7,7 @@
  *   seq(t)   the sequence b whose ragged row range [off[b], off[b+1])
  *            holds token t (rope_split_store_paged_ragged page, Args:
  *            input_row_offsets; generic_kv_cache_radd_dispatch page, Args:
- *            input_row_offsets "start of each sequence");
+ *            input_row_offsets: one start row per sequence);
  *   pos(t)   cache_lengths[seq(t) + batch_offset] + t - off[seq(t)]
  *            (generic_kv_cache_radd_dispatch page, Description: batch
  *            offset and per-batch cache lengths locate the target rows);

@@ -16,8 +16,9 @@
  *
  * Readings of points the pages leave open (each also listed in the design doc):
  *   - freqs_cis rows hold (cos, sin) pairs for frequency i at columns
- *     (2i, 2i+1) whatever the Q/K layout ("interleaved rope frequencies",
- *     rope_split_store_paged_ragged page, Args: freqs_cis);
+ *     (2i, 2i+1) whatever the Q/K layout (the table is described as holding
+ *     interleaved frequencies: rope_split_store_paged_ragged page, Args:
+ *     freqs_cis);
  *   - the rotation multiplies by cos + i*sin;
  *   - half-split pairs element i with element i + rope_dim/2;
  *   - a partial rope rotates the FIRST rope_dim dimensions of a head
