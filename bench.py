@@ -9,6 +9,10 @@ prefill (32 Q / 8 KV heads, head_dim 128, bf16, half-split RoPE, theta 5e5,
 batch 8 with lengths U[128, 2048], page 128, 32 layers, layer 17).  Other
 workloads (decode, dual band, radd) are for measuring the other kernels.
 
+The default warm-up (300 launches) is long on purpose: the first few
+hundred launches over multi-GB pools run a few per cent slower (clocks and
+address-translation warm-up); the timed region measures steady state.
+
 Each step runs on its own set of buffers, cycling through enough sets that
 the data touched between two uses of a set exceeds the 256 MB Infinity
 Cache: every step reads its inputs from HBM, not from a warm cache.  Each
@@ -328,8 +332,8 @@ def check_parity(case, dc, shared_pool: bool) -> str:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "dual", "radd"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

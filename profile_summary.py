@@ -55,6 +55,12 @@ def trace(args) -> str:
         out.append(f"| `{name[:110]}` | {len(d)} | {statistics.mean(d):.2f} | "
                    f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
     band = [(k, v) for k, v in by.items() if BAND in k]
+    if args.warmup is not None and args.steps:
+        for name, v in band:
+            timed = [x[0] / 1e3 for x in v[args.warmup:args.warmup + args.steps]]
+            out += ["", f"Timed region of the bench (launches {args.warmup} to "
+                        f"{args.warmup + len(timed) - 1} of `{name[:60]}...`): "
+                        f"average {statistics.mean(timed):.2f} us over {len(timed)} launches."]
     for name, v in band:
         out += ["", f"`{name}`: LDS {v[0][5]} bytes, {v[0][2]} threads per block.", "",
                 "| grid threads (one batch) | launches | avg us | min us |", "|---|---|---|---|"]
@@ -145,6 +151,8 @@ def main() -> int:
     t.add_argument("dir")
     t.add_argument("--label", required=True)
     t.add_argument("--command", required=True)
+    t.add_argument("--warmup", type=int, default=None, help="warm-up launches before the timed region")
+    t.add_argument("--steps", type=int, default=0, help="launches in the timed region")
     p = sub.add_parser("traffic")
     p.add_argument("--fetch", required=True)
     p.add_argument("--write", required=True)

@@ -165,7 +165,13 @@ struct Builder {
     const uint64_t items = (uint64_t)total_tokens * a.groups_per_token;
     if (items >= (1ull << 31)) return fail(QRP_EINVAL, "batch too large for one launch");
     a.n_items = (uint32_t)items;
-    a.n_blocks = (uint32_t)((items + qrp::kWavesPerBlock - 1) / qrp::kWavesPerBlock);
+    // Large rope/store launches run one wave per block (measured faster);
+    // norm, radd and small launches group four waves per block.
+    uint32_t wpb = (!radd && !norm && items >= 8192) ? 1u : (uint32_t)qrp::kMaxWavesPerBlock;
+    const int forced_wpb = env_int("QRP_WAVES_PER_BLOCK", 0);
+    if (forced_wpb > 0) wpb = std::min<uint32_t>((uint32_t)forced_wpb, qrp::kMaxWavesPerBlock);
+    a.waves_per_block = wpb;
+    a.n_blocks = (uint32_t)((items + wpb - 1) / wpb);
     a.per_xcd = env_int("QRP_XCD_REMAP", 0) ? (a.n_blocks + qrp::kXcds - 1) / qrp::kXcds : 0;
     a.total_tokens = total_tokens;
     a.guess_mul = (((uint64_t)a.batch) << 32) / total_tokens;

@@ -32,19 +32,23 @@ enum SegKind : uint32_t {
 
 constexpr int kMaxSegs = 4;
 constexpr int kMaxCaches = 2;
-constexpr int kWavesPerBlock = 4;
-constexpr int kThreads = 64 * kWavesPerBlock;
+constexpr int kMaxWavesPerBlock = 4;
+constexpr int kThreads = 64 * kMaxWavesPerBlock;  // launch bound; blocks may be smaller
 constexpr int kXcds = 8;
 
-// Passes (rows of 64 lanes) one wave may hold in registers at once.
+// Passes (rows of 64 lanes) one wave may hold in registers at once.  Waves
+// that each move about 4 KB stream best on MI355X (measured with plain
+// copies and with this kernel): 2 passes of rope/store rows, 3 of norm rows,
+// 1 of radd rows (each radd pass reads two operands).  Smaller register
+// arrays also raise the number of resident waves.
 #ifndef QRP_MAX_PASSES_STORE
-#define QRP_MAX_PASSES_STORE 6
+#define QRP_MAX_PASSES_STORE 2
 #endif
 #ifndef QRP_MAX_PASSES_NORM
-#define QRP_MAX_PASSES_NORM 4
+#define QRP_MAX_PASSES_NORM 3
 #endif
 #ifndef QRP_MAX_PASSES_RADD
-#define QRP_MAX_PASSES_RADD 4
+#define QRP_MAX_PASSES_RADD 2
 #endif
 constexpr int kMaxPassesStore = QRP_MAX_PASSES_STORE;
 constexpr int kMaxPassesNorm = QRP_MAX_PASSES_NORM;
@@ -98,6 +102,7 @@ struct BandArgs {
   uint32_t groups_per_token;
   uint32_t n_items;         // total_tokens * groups_per_token waves of work
   uint32_t n_blocks;        // blocks holding work
+  uint32_t waves_per_block; // 1 .. kMaxWavesPerBlock
   uint32_t per_xcd;         // blocks per XCD after the XCD-contiguous remap (0: no remap)
   uint64_t guess_mul;       // floor(batch * 2^32 / total_tokens): token -> first sequence guess
 };

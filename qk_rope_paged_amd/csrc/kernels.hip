@@ -63,6 +63,7 @@ struct Fmt<uint16_t> {  // bf16 stored as raw 16-bit words
 #define QRP_NT_STORES 1
 #endif
 
+
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -154,11 +155,14 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-// Largest b < B with off[b] <= t.  The guess g = t * B / T (a host-computed
-// 32.32 fixed-point factor) is exact for one-token-per-sequence decode; its
-// two offsets are loaded together and checked, and a miss falls back to a
-// binary search over the side the guess left open.  Every index read is
-// <= B.  `hit` reports whether the guess held.
+// Largest b < B with off[b] <= t, for batches of kSmallBatch sequences or
+// more.  The guess g = t * B / T (a host-computed 32.32 fixed-point factor) is
+// exact for one-token-per-sequence decode: its two offsets are loaded
+// together and checked, and a miss falls back to a binary search over the
+// side the guess left open.  Every index read is <= B.  `hit` reports a
+// resolved guess.
+constexpr uint32_t kSmallBatch = 16;
+
 __device__ __forceinline__ uint32_t find_seq(const uint32_t* __restrict__ off, uint32_t B,
                                              uint32_t g, uint32_t t, uint32_t& start,
                                              uint32_t& end, bool& hit) {
@@ -261,7 +265,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   // well as loads, so a load issued after a store would wait for it).
   __shared__ uint4 lds_gamma[NORM ? kMaxSegs : 1][NORM ? CH : 1];
   if constexpr (NORM) {
-    for (uint32_t i = threadIdx.x; i < kMaxSegs * CH; i += kThreads) {
+    for (uint32_t i = threadIdx.x; i < kMaxSegs * CH; i += blockDim.x) {
       const uint32_t si = i / CH, c = i % CH;
       uint4 g = make_uint4(0, 0, 0, 0);
       if (si < a.nseg && a.seg[si].gamma != nullptr)
@@ -271,7 +275,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
     __syncthreads();
   }
 
-  const uint32_t item = blk * kWavesPerBlock + wave;
+  const uint32_t item = blk * a.waves_per_block + wave;
   if (item >= a.n_items) return;
 
   const uint32_t t = item / a.groups_per_token;
@@ -309,17 +313,58 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   }
 
   // ---- B: token -> sequence -> position -> page (wave-uniform) ----
-  // The guess's offsets and cache lengths are fetched together, so a decode
-  // wave pays one scalar-load latency before its page-table lookup.
-  uint32_t g = (uint32_t)(((uint64_t)t * a.guess_mul) >> 32);
-  g = g < a.batch ? g : a.batch - 1;
-  uint32_t clen_guess[kMaxCaches] = {0, 0};
+  uint32_t start, end, b;
+  uint32_t clen[kMaxCaches] = {0, 0};
+  if (a.batch < kSmallBatch) {
+    // Small batch: every offset and every sequence's cache length in one
+    // round of independent scalar loads (indices clamped in range), then a
+    // scan -- one load latency before the page-table lookup.
+    const uint32_t B = a.batch;
+    uint32_t o[kSmallBatch + 1];
+    uint32_t cl[kMaxCaches][kSmallBatch];
 #pragma unroll
-  for (int ci = 0; ci < kMaxCaches; ++ci)
-    if ((uint32_t)ci < a.ncache) clen_guess[ci] = a.cache[ci].cache_lengths[g + a.batch_offset];
-  uint32_t start, end;
-  bool hit;
-  const uint32_t b = find_seq(a.offsets, a.batch, g, t, start, end, hit);
+    for (uint32_t i = 0; i <= kSmallBatch; ++i) o[i] = a.offsets[i < B ? i : B];
+#pragma unroll
+    for (int ci = 0; ci < kMaxCaches; ++ci) {
+#pragma unroll
+      for (uint32_t i = 0; i < kSmallBatch; ++i)
+        cl[ci][i] = (uint32_t)ci < a.ncache
+                        ? a.cache[ci].cache_lengths[(i < B ? i : B - 1) + a.batch_offset]
+                        : 0u;
+    }
+    b = 0;
+#pragma unroll
+    for (uint32_t i = 1; i < kSmallBatch; ++i)
+      if (i < B && o[i] <= t) b = i;
+    start = o[0];
+    end = o[1];
+    clen[0] = cl[0][0];
+    clen[1] = cl[1][0];
+#pragma unroll
+    for (uint32_t i = 1; i < kSmallBatch; ++i) {
+      if (i == b) {
+        start = o[i];
+        end = o[i + 1];
+        clen[0] = cl[0][i];
+        clen[1] = cl[1][i];
+      }
+    }
+  } else {
+    // The guess's offsets and cache lengths are fetched together, so a
+    // decode wave pays one scalar-load latency before its page-table lookup.
+    uint32_t g = (uint32_t)(((uint64_t)t * a.guess_mul) >> 32);
+    g = g < a.batch ? g : a.batch - 1;
+    uint32_t clen_guess[kMaxCaches] = {0, 0};
+#pragma unroll
+    for (int ci = 0; ci < kMaxCaches; ++ci)
+      if ((uint32_t)ci < a.ncache) clen_guess[ci] = a.cache[ci].cache_lengths[g + a.batch_offset];
+    bool hit;
+    b = find_seq(a.offsets, a.batch, g, t, start, end, hit);
+#pragma unroll
+    for (int ci = 0; ci < kMaxCaches; ++ci)
+      if ((uint32_t)ci < a.ncache)
+        clen[ci] = hit ? clen_guess[ci] : a.cache[ci].cache_lengths[b + a.batch_offset];
+  }
   bool ok = start <= t && t < end;
   const uint32_t local = t - start;
   const uint32_t cseq = b + a.batch_offset;
@@ -329,8 +374,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   for (int ci = 0; ci < kMaxCaches; ++ci) {
     if ((uint32_t)ci < a.ncache) {
       const CacheDesc& cd = a.cache[ci];
-      const uint32_t clen = hit ? clen_guess[ci] : cd.cache_lengths[cseq];
-      const uint64_t p64 = (uint64_t)clen + local;
+      const uint64_t p64 = (uint64_t)clen[ci] + local;
       const uint64_t pidx = cd.page_shift != 0xFFFFFFFFu ? (p64 >> cd.page_shift)
                                                          : p64 / cd.page_size;
       const uint64_t slot = p64 - pidx * cd.page_size;
@@ -371,6 +415,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   float fl[RADD ? 1 : 2 * E];
   uint32_t fl_pos = pos[0];
   if constexpr (!RADD) load_freqs<T, IL>(a.freqs, a.rope_dim, fl_pos, c0, c1, j, rot0, rot1, fl);
+
 
   // ---- E: arithmetic and stores ----
 #pragma unroll
@@ -482,7 +527,8 @@ template <typename T, int D, bool IL, bool RADD, bool NORM>
 int launch_t(const BandArgs& a, void* stream) {
   constexpr int NPMAX = RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : kMaxPassesStore);
   const uint32_t grid = a.per_xcd ? a.per_xcd * kXcds : a.n_blocks;
-  hipLaunchKernelGGL((band_kernel<T, D, IL, NPMAX, RADD, NORM>), dim3(grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((band_kernel<T, D, IL, NPMAX, RADD, NORM>), dim3(grid),
+                     dim3(64 * a.waves_per_block), 0,
                      reinterpret_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }

@@ -5,8 +5,8 @@
   place of two);
 * the norm op with no gammas and K/V from the buffer equals the rope-only op;
 * half-split RoPE equals interleaved RoPE on each head's halves interleaved;
-* every launch configuration (passes per wave, XCD-contiguous remap) gives
-  the same bits;
+* every launch configuration (passes per wave, waves per block,
+  XCD-contiguous remap) gives the same bits;
 * the device validator accepts good metadata and rejects a shared row;
 * tokens whose metadata is out of range are skipped: nothing is written for
   them and every other token is exact;
@@ -115,17 +115,19 @@ def test_launch_configuration_does_not_change_bits(workload, monkeypatch):
     case = sc.WORKLOADS[workload](small=True)
     ref = None
     for remap in ("0", "1"):
-        for ppw in ("0", "1", "2", "3", "4", "6"):
-            monkeypatch.setenv("QRP_XCD_REMAP", remap)
-            monkeypatch.setenv("QRP_PASSES_PER_WAVE", ppw)
-            dc = gh.upload(case)
-            gh.run(dc)
-            torch.cuda.synchronize()
-            snap = _snapshot(dc)
-            if ref is None:
-                ref = snap
-            else:
-                _assert_same(ref, snap, f"{workload} remap={remap} ppw={ppw}")
+        for ppw in ("0", "1", "2", "3"):
+            for wpb in ("0", "1", "2", "4"):
+                monkeypatch.setenv("QRP_XCD_REMAP", remap)
+                monkeypatch.setenv("QRP_PASSES_PER_WAVE", ppw)
+                monkeypatch.setenv("QRP_WAVES_PER_BLOCK", wpb)
+                dc = gh.upload(case)
+                gh.run(dc)
+                torch.cuda.synchronize()
+                snap = _snapshot(dc)
+                if ref is None:
+                    ref = snap
+                else:
+                    _assert_same(ref, snap, f"{workload} remap={remap} ppw={ppw} wpb={wpb}")
 
 
 def test_validate_on_device():
