@@ -27,10 +27,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 SRC = os.path.join(HERE, "qrp_oracle.c")
 
-ORC_F32, ORC_BF16 = 0, 1
-_DT = {"f32": ORC_F32, "bf16": ORC_BF16}
-_SENT = {"f32": np.uint32(0x7FBADBAD), "bf16": np.uint16(0x7FBA)}
-_BITS = {"f32": np.uint32, "bf16": np.uint16}
+ORC_F32, ORC_BF16, ORC_F16 = 0, 1, 2
+_DT = {"f32": ORC_F32, "bf16": ORC_BF16, "f16": ORC_F16}
+_SENT = {"f32": np.uint32(0x7FBADBAD), "bf16": np.uint16(0x7FBA), "f16": np.uint16(0x7DBA)}
+_BITS = {"f32": np.uint32, "bf16": np.uint16, "f16": np.uint16}
 NO_PAGE = 0xFFFFFFFF
 
 
@@ -84,6 +84,10 @@ def load() -> ctypes.CDLL:
     lib.orc_round_bf16.restype = ctypes.c_uint16
     lib.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.orc_bf16_to_double.restype = ctypes.c_double
+    lib.orc_round_f16.argtypes = [ctypes.c_double]
+    lib.orc_round_f16.restype = ctypes.c_uint16
+    lib.orc_f16_to_double.argtypes = [ctypes.c_uint16]
+    lib.orc_f16_to_double.restype = ctypes.c_double
     lib.orc_rope_split_store_paged.argtypes = [P, I32, U32, U64, U32, P, U32, P, U32, U32, I32,
                                                ctypes.POINTER(OrcCache), U32, P, U64,
                                                ctypes.POINTER(OrcTrace)]
@@ -113,6 +117,14 @@ def round_bf16(x: float) -> int:
 
 def bf16_to_double(b: int) -> float:
     return float(load().orc_bf16_to_double(int(b)))
+
+
+def round_f16(x: float) -> int:
+    return int(load().orc_round_f16(float(x)))
+
+
+def f16_to_double(h: int) -> float:
+    return float(load().orc_f16_to_double(int(h)))
 
 
 @dataclass

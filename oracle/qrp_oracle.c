@@ -39,6 +39,8 @@
 
 static size_t elem_bytes(int32_t dt) { return dt == ORC_F32 ? 4u : 2u; }
 
+static int dtype_ok(int32_t dt) { return dt == ORC_F32 || dt == ORC_BF16 || dt == ORC_F16; }
+
 double orc_bf16_to_double(uint16_t b) {
   /* a bf16 value is the upper half of an IEEE binary32 word */
   uint32_t u = (uint32_t)b << 16;
@@ -72,20 +74,54 @@ uint16_t orc_round_bf16(double x) {
   return (uint16_t)(u >> 16);
 }
 
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double orc_f16_to_double(uint16_t h) {
+  const int sign = h >> 15, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+  return sign ? -v : v;
+}
+
+uint16_t orc_round_f16(double x) {
+  const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  if (isnan(x)) return (uint16_t)(sign | 0x7E00u); /* a quiet NaN */
+  if (isinf(x)) return (uint16_t)(sign | 0x7C00u);
+  if (x == 0.0) return sign;
+  /* 11 significant bits; below 2^-14 the spacing stays 2^-24 (subnormals) */
+  int e = ilogb(x);
+  if (e < -14) e = -14;
+  double quantum = ldexp(1.0, e - 10);
+  double r = fabs(nearbyint(x / quantum) * quantum); /* ties to even */
+  if (r >= 65536.0) return (uint16_t)(sign | 0x7C00u); /* past 65504 by half a spacing or more */
+  if (r < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+  int re = ilogb(r); /* the rounded value may have moved up one binade */
+  uint16_t mant = (uint16_t)((r / ldexp(1.0, re) - 1.0) * 1024.0);
+  return (uint16_t)(sign | (uint16_t)((re + 15) << 10) | mant);
+}
+
 static double get(const void* base, int32_t dt, int64_t i) {
   if (dt == ORC_F32) return (double)((const float*)base)[i];
+  if (dt == ORC_F16) return orc_f16_to_double(((const uint16_t*)base)[i]);
   return orc_bf16_to_double(((const uint16_t*)base)[i]);
 }
 
 /* value rounded to dtype, returned as double */
 static double round_to(int32_t dt, double v) {
   if (dt == ORC_F32) return (double)(float)v;
+  if (dt == ORC_F16) return orc_f16_to_double(orc_round_f16(v));
   return orc_bf16_to_double(orc_round_bf16(v));
 }
 
 static void put(void* base, int32_t dt, int64_t i, double v) {
   if (dt == ORC_F32)
     ((float*)base)[i] = (float)v;
+  else if (dt == ORC_F16)
+    ((uint16_t*)base)[i] = orc_round_f16(v);
   else
     ((uint16_t*)base)[i] = orc_round_bf16(v);
 }
@@ -240,7 +276,7 @@ static void do_head(const void* src, int64_t src_off, void* dst, int64_t dst_off
 static int32_t check_common(int32_t dtype, const orc_cache* c, uint32_t rope_dim,
                             uint32_t layer_idx, uint32_t max_seq_len) {
   if (!c || !c->pool || !c->cache_lengths || !c->lookup_table) return ORC_EINVAL;
-  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_EINVAL;
+  if (!dtype_ok(dtype)) return ORC_EINVAL;
   if (c->dtype != dtype) return ORC_EINVAL;
   if (c->head_dim == 0 || c->page_size == 0) return ORC_EINVAL;
   if (rope_dim == 0 || rope_dim % 2 || rope_dim > c->head_dim) return ORC_EINVAL;
@@ -393,7 +429,7 @@ int32_t orc_kv_cache_radd(const void* a, int32_t dtype, uint32_t T, uint64_t a_r
                           const uint32_t* off, uint32_t B, uint32_t batch_offset, orc_cache* c,
                           uint32_t layer_idx, int64_t* k_row_off, int64_t* v_row_off) {
   if (!c || !c->pool || !c->cache_lengths || !c->lookup_table) return ORC_EINVAL;
-  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_EINVAL;
+  if (!dtype_ok(dtype)) return ORC_EINVAL;
   if (c->dtype != dtype || c->kv_planes != 2 || layer_idx >= c->num_layers) return ORC_EINVAL;
   if ((uint64_t)batch_offset + B > c->cache_batch) return ORC_EINVAL;
   if (T == 0) return ORC_OK;

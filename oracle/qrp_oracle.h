@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2 };
 
 enum {
   ORC_OK = 0,
@@ -93,6 +93,10 @@ typedef struct orc_band {
 /* Exact double -> bf16 bits, round to nearest even. */
 uint16_t orc_round_bf16(double x);
 double orc_bf16_to_double(uint16_t b);
+
+/* Exact double -> IEEE binary16 bits, round to nearest even. */
+uint16_t orc_round_f16(double x);
+double orc_f16_to_double(uint16_t h);
 
 /* rope_split_store_paged_ragged page (signature, Summary, Args). */
 int32_t orc_rope_split_store_paged(

@@ -32,10 +32,11 @@ import numpy as np
 
 from . import prng
 
-F32, BF16 = "f32", "bf16"
-SENTINEL = {F32: np.uint32(0x7FBADBAD), BF16: np.uint16(0x7FBA)}  # signalling-NaN patterns
-BITS_DTYPE = {F32: np.uint32, BF16: np.uint16}
-ELEM_BYTES = {F32: 4, BF16: 2}
+F32, BF16, F16 = "f32", "bf16", "f16"
+# signalling-NaN patterns
+SENTINEL = {F32: np.uint32(0x7FBADBAD), BF16: np.uint16(0x7FBA), F16: np.uint16(0x7DBA)}
+BITS_DTYPE = {F32: np.uint32, BF16: np.uint16, F16: np.uint16}
+ELEM_BYTES = {F32: 4, BF16: 2, F16: 2}
 NO_PAGE = np.uint32(0xFFFFFFFF)
 
 # stream numbers (one per generated array)
@@ -43,7 +44,10 @@ S_LENS, S_CLEN, S_PERM, S_BUF, S_GAMMA, S_A, S_PREFILL, S_SPECIAL = 1, 2, 3, 4, 
 
 
 def to_bits(values: np.ndarray, dtype: str) -> np.ndarray:
-    """Doubles -> raw bits of ``dtype`` (binary32 RNE, then bf16 RNE)."""
+    """Doubles -> raw bits of ``dtype`` (binary16: numpy's RNE; bf16: binary32
+    RNE, then bf16 RNE)."""
+    if dtype == F16:
+        return np.asarray(values, dtype=np.float64).astype(np.float16).view(np.uint16)
     f = np.asarray(values, dtype=np.float64).astype(np.float32)
     u = f.view(np.uint32)
     if dtype == F32:
@@ -53,19 +57,24 @@ def to_bits(values: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == F16:
+        return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
     if dtype == F32:
         return bits.view(np.float32).astype(np.float64)
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def freqs_table(max_seq_len: int, rope_dim: int, base: float) -> np.ndarray:
-    """freqs_cis[p, 2i] = cos(p * base^(-2i/R)), [p, 2i+1] = sin(...), fp64 -> fp32."""
+def freqs_table(max_seq_len: int, rope_dim: int, base: float, freq_dtype: str = F32) -> np.ndarray:
+    """freqs_cis[p, 2i] = cos(p * base^(-2i/R)), [p, 2i+1] = sin(...), fp64 -> fp32
+    (-> bf16 for a bf16 table; the float32 array then holds bf16 values)."""
     i = np.arange(rope_dim // 2, dtype=np.float64)
     inv = base ** (-2.0 * i / rope_dim)
     ang = np.arange(max_seq_len, dtype=np.float64)[:, None] * inv[None, :]
     tab = np.empty((max_seq_len, rope_dim), dtype=np.float64)
     tab[:, 0::2] = np.cos(ang)
     tab[:, 1::2] = np.sin(ang)
+    if freq_dtype == BF16:
+        return bits_to_f64(to_bits(tab, BF16), BF16).astype(np.float32)
     return tab.astype(np.float32)
 
 
@@ -179,6 +188,7 @@ class Case:
     bands: List[Band] = field(default_factory=list)
     weight_offset: float = 0.0
     multiply_before_cast: bool = True
+    freq_dtype: str = F32               # table entries: f32, or bf16 values held in float32
 
     @property
     def T(self) -> int:
@@ -262,7 +272,8 @@ def make_store_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq
                     D: int, rope_dim: int, interleaved: bool, theta: float, max_seq_len: int,
                     P: int, L: int, layer: int, num_pages: Optional[int] = None,
                     max_pages: Optional[int] = None, slack: float = 0.25,
-                    q_out_pad: int = 0, row_pad: int = 0, specials: bool = False) -> Case:
+                    q_out_pad: int = 0, row_pad: int = 0, specials: bool = False,
+                    freq_dtype: str = F32) -> Case:
     """rope_split_store_paged workload: qkv [T, (Hq + 2Hk) D (+row_pad)] N(0, 1)."""
     lengths = np.asarray(lengths, dtype=np.int64)
     cache_lengths = np.asarray(cache_lengths, dtype=np.int64)
@@ -282,13 +293,16 @@ def make_store_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq
     if specials and T:
         _inject_specials(buf, seed, dtype, Hq, Hk, D, rope_dim)
     return Case(name=name, op="store", dtype=dtype, seed=seed, lengths=lengths, offsets=off,
-                buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta), rope_dim=rope_dim,
-                interleaved=interleaved, caches=[cache], layer_idx=layer, n_q_heads=Hq,
-                q_out_row_stride=Hq * D + q_out_pad)
+                buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta, freq_dtype),
+                rope_dim=rope_dim, interleaved=interleaved, caches=[cache], layer_idx=layer,
+                n_q_heads=Hq, q_out_row_stride=Hq * D + q_out_pad, freq_dtype=freq_dtype)
 
 
 def _special_values(dtype: str) -> np.ndarray:
     """+-0, +-inf, quiet/signalling NaNs with payloads, subnormals, extremes."""
+    if dtype == F16:
+        return np.array([0x0000, 0x8000, 0x7C00, 0xFC00, 0x7E01, 0x7C01, 0xFDBA, 0x0001, 0x83FF,
+                         0x7BFF, 0x0400], dtype=np.uint16)
     if dtype == F32:
         return np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00001, 0x7F800001,
                          0xFFBADBAD, 0x00000001, 0x807FFFFF, 0x7F7FFFFF, 0x00800000],
@@ -317,7 +331,7 @@ def make_norm_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq:
                    P: int, L: int, layer: int, k_in_cache: bool, q_norm: bool = True,
                    k_norm: bool = True, eps: float = 1e-6, weight_offset: float = 0.0,
                    multiply_before_cast: bool = True, slack: float = 0.25,
-                   gamma_std: float = 0.1) -> Case:
+                   gamma_std: float = 0.1, freq_dtype: str = F32) -> Case:
     """Single-band qk_rmsnorm_rope_paged workload.  Buffer [T, (Hq+2Hk) D] =
     Q | K | V; with ``k_in_cache`` K is prefilled in the cache and updated in
     place (the buffer's K and V columns are then unread)."""
@@ -340,9 +354,10 @@ def make_norm_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq:
                 q_gamma=g[0] if q_norm else None, k_gamma=g[1] if k_norm else None,
                 epsilon=eps, cache=0, q_out_row_stride=Hq * D)
     return Case(name=name, op="norm", dtype=dtype, seed=seed, lengths=lengths, offsets=off,
-                buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta), rope_dim=rope_dim,
-                interleaved=interleaved, caches=[cache], layer_idx=layer, bands=[band],
-                weight_offset=weight_offset, multiply_before_cast=multiply_before_cast)
+                buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta, freq_dtype),
+                rope_dim=rope_dim, interleaved=interleaved, caches=[cache], layer_idx=layer,
+                bands=[band], weight_offset=weight_offset,
+                multiply_before_cast=multiply_before_cast, freq_dtype=freq_dtype)
 
 
 def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_main: int,

@@ -43,6 +43,10 @@ MUTATIONS = {
     "bf16_truncate": ("double r = nearbyint(x / quantum) * quantum;",
                       "double r = trunc(x / quantum) * quantum;"),
     "bf16_no_subnormals": ("if (e < -126) e = -126;", ""),
+    "f16_truncate": ("double r = fabs(nearbyint(x / quantum) * quantum);",
+                     "double r = fabs(trunc(x / quantum) * quantum);"),
+    "f16_no_subnormals": ("if (e < -14) e = -14;", ""),
+    "f16_bias": ("ldexp(1.0 + (double)m / 1024.0, e - 15)", "ldexp(1.0 + (double)m / 1024.0, e - 16)"),
     "batch_offset_ignored": ("uint32_t cseq = (uint32_t)b + batch_offset;",
                              "uint32_t cseq = (uint32_t)b;"),
     "radd_adds_twice": ("float sum = cur + add; /* one IEEE binary32 add */",
@@ -54,6 +58,8 @@ MUTATIONS = {
 PIN_TESTS = [
     (pins.test_bf16_rounding_golden_cases, {}),
     (pins.test_bf16_rounding_matches_exhaustive_search, {}),
+    (pins.test_f16_rounding_golden_cases, {}),
+    (pins.test_f16_rounding_matches_numpy, {}),
     (pins.test_tiny_store_matches_complex_brute_force, {"interleaved": True}),
     (pins.test_tiny_store_matches_complex_brute_force, {"interleaved": False}),
     (pins.test_partial_rope_and_ragged_batch_brute_force, {"interleaved": True, "dtype": "bf16"}),

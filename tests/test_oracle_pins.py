@@ -4,7 +4,8 @@ Each test ties one part of the oracle to the documentation pages, to
 mathematics or to a brute-force computation written differently:
 
 * bf16 rounding: hand-derived IEEE-754 cases (tests/golden) and exhaustive
-  neighbour search;
+  neighbour search; binary16 rounding: hand-derived cases and numpy's own
+  float64 -> float16 conversion;
 * RoPE: Python complex multiplication on the tiny fp32 workload, both
   layouts, partial rope; position 0 is the identity; every pair keeps its
   length; unit vectors give (cos, sin) of p * theta_i computed here with
@@ -75,6 +76,36 @@ def test_bf16_special_values():
         assert oracle.round_bf16(oracle.bf16_to_double(b)) == b
 
 
+def test_f16_rounding_golden_cases():
+    n = 0
+    with open(os.path.join(GOLDEN, "f16_rne_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            val, bits = line.split()[:2]
+            assert oracle.round_f16(float.fromhex(val)) == int(bits, 16), line
+            n += 1
+    assert n >= 15
+
+
+def test_f16_rounding_matches_numpy():
+    # numpy's float64 -> float16 conversion is a separate, correctly rounded
+    # (ties-to-even) implementation of the same IEEE operation
+    rng = np.random.default_rng(7)
+    xs = np.concatenate([rng.standard_normal(4000), rng.standard_normal(1000) * 1e-5,
+                         rng.standard_normal(1000) * 3e4, rng.standard_normal(500) * 1e-7])
+    every = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    fin = np.sort(every[np.isfinite(every)].astype(np.float64))
+    mids = (fin[:-1] + fin[1:]) / 2
+    xs = np.concatenate([xs, rng.choice(mids, 2000)])
+    for x in xs:
+        want = int(np.float64(x).astype(np.float16).view(np.uint16))
+        assert oracle.round_f16(float(x)) == want, float(x).hex()
+    for h in (0x0000, 0x8000, 0x0001, 0x3C00, 0x4248, 0x7BFF, 0x0400):
+        assert oracle.round_f16(oracle.f16_to_double(h)) == h
+
+
 # --------------------------------------------------------------------------
 # RoPE and paged placement against brute force
 # --------------------------------------------------------------------------
@@ -140,7 +171,7 @@ def test_tiny_store_matches_complex_brute_force(interleaved):
 
 
 @pytest.mark.parametrize("interleaved", [True, False])
-@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16])
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
 def test_partial_rope_and_ragged_batch_brute_force(interleaved, dtype):
     # empty sequences between non-empty ones, partial rope, multi-page rows,
     # several layers, padded row strides
@@ -150,7 +181,7 @@ def test_partial_rope_and_ragged_batch_brute_force(interleaved, dtype):
                        seed=11)
     res = oracle.run_case(case)
     assert res.status == 0
-    tol = 2.0 ** -23 if dtype == sc.F32 else 2.0 ** -8
+    tol = {sc.F32: 2.0 ** -23, sc.BF16: 2.0 ** -8, sc.F16: 2.0 ** -11}[dtype]
     written = _check_store_against_brute(case, res, pair_tol=tol)
     _check_sentinels(case, res.pools[0], written)
     # q_out padding columns untouched
@@ -271,12 +302,12 @@ def test_identity_page_table_is_a_dense_cache():
 
 
 def test_copies_keep_every_bit_including_specials():
-    for dtype in (sc.F32, sc.BF16):
+    for dtype in (sc.F32, sc.BF16, sc.F16):
         case = _store_case(dtype=dtype, rope_dim=32, lengths=(6, 9), cache_lengths=(1, 3),
                            specials=True, seed=23)
         res = oracle.run_case(case)
-        written = _check_store_against_brute(case, res, pair_tol=2.0 ** -23 if dtype == sc.F32
-                                             else 2.0 ** -8)
+        tol = {sc.F32: 2.0 ** -23, sc.BF16: 2.0 ** -8, sc.F16: 2.0 ** -11}[dtype]
+        written = _check_store_against_brute(case, res, pair_tol=tol)
         _check_sentinels(case, res.pools[0], written)
 
 
@@ -394,7 +425,7 @@ def _radd_case(seed=51, dtype=sc.BF16, lengths=(3, 0, 7, 2), clen=(5, 1, 9, 0, 3
                              P=8, L=2, layer=1, a_values=a_values)
 
 
-@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16])
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
 def test_radd_is_one_binary32_add_per_element(dtype):
     case = _radd_case(dtype=dtype)
     # sprinkle subnormals, zeros of both signs and large values into a
