@@ -63,8 +63,9 @@ typedef enum qrp_status {
 } qrp_status;
 
 typedef enum qrp_dtype {
-  QRP_F32 = 0,
-  QRP_BF16 = 1
+  QRP_F32 = 0,   /* IEEE binary32 */
+  QRP_BF16 = 1,  /* bfloat16: the top 16 bits of a binary32 */
+  QRP_F16 = 2    /* IEEE binary16 */
 } qrp_dtype;
 
 /*
@@ -107,11 +108,14 @@ typedef struct qrp_paged_cache {
  * Description).  interleaved != 0 pairs dims (2i, 2i+1); interleaved == 0
  * (half-split) pairs dims (i, i + rope_dim/2).  A pair (x, y) becomes
  * (x cos - y sin, x sin + y cos).  rope_dim must be a multiple of
- * 16 bytes / sizeof(dtype) * 2 (16 for bf16, 8 for f32).
+ * 16 bytes / sizeof(dtype) * 2 (16 for bf16 and f16, 8 for f32).
+ * freq_dtype QRP_BF16 stores each entry as a bfloat16 (the table's dtype is
+ * a parameter of its own on the page, independent of the op's dtype); its
+ * values are widened exactly to binary32 before use.
  */
 typedef struct qrp_rope {
   const void* freqs_cis;
-  int32_t freq_dtype;          /* QRP_F32 */
+  int32_t freq_dtype;          /* QRP_F32 or QRP_BF16 (any op dtype) */
   uint32_t max_seq_len;
   uint32_t rope_dim;
   int32_t interleaved;

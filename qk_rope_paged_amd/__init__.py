@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libqk_rope_paged.so")
 
 QRP_OK, QRP_EINVAL, QRP_EALIGN, QRP_EUNSUPPORTED, QRP_EGEOMETRY, QRP_EHIP, QRP_EDATA = (
     0, -1, -2, -3, -4, -5, -6)
-QRP_F32, QRP_BF16 = 0, 1
+QRP_F32, QRP_BF16, QRP_F16 = 0, 1, 2
 STATUS_NAMES = {0: "QRP_OK", -1: "QRP_EINVAL", -2: "QRP_EALIGN", -3: "QRP_EUNSUPPORTED",
                 -4: "QRP_EGEOMETRY", -5: "QRP_EHIP", -6: "QRP_EDATA"}
 
@@ -182,13 +182,14 @@ class PagedCache:
 
 @dataclass
 class Rope:
-    freqs_cis: object        # float32 [max_seq_len, rope_dim]
+    freqs_cis: object        # [max_seq_len, rope_dim] of freq_dtype (float32 or bf16 words)
     max_seq_len: int
     rope_dim: int
     interleaved: bool
+    freq_dtype: int = QRP_F32
 
     def to_c(self) -> QrpRope:
-        return QrpRope(freqs_cis=_ptr(self.freqs_cis), freq_dtype=QRP_F32,
+        return QrpRope(freqs_cis=_ptr(self.freqs_cis), freq_dtype=self.freq_dtype,
                        max_seq_len=self.max_seq_len, rope_dim=self.rope_dim,
                        interleaved=int(bool(self.interleaved)))
 

@@ -31,11 +31,12 @@ int32_t fail(int32_t code, const std::string& msg) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 uint32_t elem_bytes(int32_t dt) { return dt == QRP_F32 ? 4u : 2u; }
 uint32_t chunk_elems(int32_t dt) { return 16u / elem_bytes(dt); }
-bool dtype_ok(int32_t dt) { return dt == QRP_F32 || dt == QRP_BF16; }
+bool dtype_ok(int32_t dt) { return dt == QRP_F32 || dt == QRP_BF16 || dt == QRP_F16; }
 
-// binary32 -> nearest-even bf16 -> binary32 (weight_offset is a Scalar[dtype])
+// binary32 -> nearest-even bf16 or binary16 -> binary32 (weight_offset is a Scalar[dtype])
 float to_dtype(int32_t dt, float v) {
   if (dt == QRP_F32) return v;
+  if (dt == QRP_F16) return (float)(_Float16)v;
   uint32_t u;
   std::memcpy(&u, &v, 4);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
@@ -82,7 +83,8 @@ int32_t check_cache(const qrp_paged_cache* c, int32_t dtype, uint32_t layer_idx,
 
 int32_t check_rope(const qrp_rope* r, int32_t dtype, uint32_t head_dim) {
   if (!r || !r->freqs_cis) return fail(QRP_EINVAL, "rope / freqs_cis is NULL");
-  if (r->freq_dtype != QRP_F32) return fail(QRP_EUNSUPPORTED, "freqs_cis must be float32");
+  if (r->freq_dtype != QRP_F32 && r->freq_dtype != QRP_BF16)
+    return fail(QRP_EUNSUPPORTED, "freqs_cis must be float32 or bfloat16");
   if (!aligned16(r->freqs_cis)) return fail(QRP_EALIGN, "freqs_cis not 16-byte aligned");
   if (r->max_seq_len == 0) return fail(QRP_EINVAL, "max_seq_len must be positive");
   if (r->rope_dim == 0 || r->rope_dim > head_dim || r->rope_dim % 2)
@@ -291,7 +293,8 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
   b.a.batch_offset = 0;
-  b.a.freqs = static_cast<const float*>(rope->freqs_cis);
+  b.a.freqs = rope->freqs_cis;
+  b.a.freq_bf16 = rope->freq_dtype == QRP_BF16;
   b.a.rope_dim = rope->rope_dim;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.multiply_before_cast = 1;
@@ -330,7 +333,8 @@ int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq
   b.a.ncache = 1;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
-  b.a.freqs = static_cast<const float*>(rope->freqs_cis);
+  b.a.freqs = rope->freqs_cis;
+  b.a.freq_bf16 = rope->freq_dtype == QRP_BF16;
   b.a.rope_dim = rope->rope_dim;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.weight_offset = to_dtype(dtype, weight_offset);
@@ -374,7 +378,8 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
   b.a.ncache = 2;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
-  b.a.freqs = static_cast<const float*>(rope->freqs_cis);
+  b.a.freqs = rope->freqs_cis;
+  b.a.freq_bf16 = rope->freq_dtype == QRP_BF16;
   b.a.rope_dim = rope->rope_dim;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.weight_offset = to_dtype(dtype, weight_offset);

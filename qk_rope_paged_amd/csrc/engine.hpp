@@ -87,7 +87,7 @@ struct BandArgs {
   SegDesc seg[kMaxSegs];
   CacheDesc cache[kMaxCaches];
   const uint32_t* offsets;  // [batch + 1]
-  const float* freqs;       // [max_seq_len][rope_dim]
+  const void* freqs;        // [max_seq_len][rope_dim], binary32 or bf16 entries
   uint32_t nseg;
   uint32_t ncache;
   uint32_t batch;
@@ -105,9 +105,10 @@ struct BandArgs {
   uint32_t waves_per_block; // 1 .. kMaxWavesPerBlock
   uint32_t per_xcd;         // blocks per XCD after the XCD-contiguous remap (0: no remap)
   uint64_t guess_mul;       // floor(batch * 2^32 / total_tokens): token -> first sequence guess
+  uint32_t freq_bf16;       // freqs entries are bf16 (else binary32)
 };
 
-enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
 // Largest passes-per-wave the kernel for this op holds in registers.
 inline uint32_t max_passes(bool radd, bool norm) {
@@ -120,7 +121,7 @@ int launch_band(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interl
 
 // Rows handled per 64-lane pass for a dtype / head_dim.
 inline uint32_t rows_per_pass(int32_t dtype, uint32_t head_dim) {
-  const uint32_t elems_per_chunk = dtype == DT_F32 ? 4u : 8u;
+  const uint32_t elems_per_chunk = dtype == DT_F32 ? 4u : 8u;  // 16 bytes of 4- or 2-byte elements
   const uint32_t lanes_per_row = head_dim / elems_per_chunk / 2u;
   return 64u / lanes_per_row;
 }

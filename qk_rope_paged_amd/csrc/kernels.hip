@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "engine.hpp"
 
 namespace qrp {
@@ -41,17 +43,20 @@ namespace {
 
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// Element types: float (binary32), Bf16 and F16 (16-bit words).
+struct Bf16 {
+  uint16_t bits;
+};
+struct F16 {
+  uint16_t bits;
+};
 
 // elements per 16-byte chunk
 template <typename T>
-struct Fmt;
-template <>
-struct Fmt<float> {
-  static constexpr int E = 4;
-};
-template <>
-struct Fmt<uint16_t> {  // bf16 stored as raw 16-bit words
-  static constexpr int E = 8;
+struct Fmt {
+  static constexpr int E = 16 / (int)sizeof(T);
 };
 
 // Streamed rows (read once / written once) may bypass cache retention with
@@ -90,17 +95,25 @@ __device__ __forceinline__ void st16s(void* p, const uint4 v) {
 
 template <typename T>
 __device__ __forceinline__ void unpack(const uint4 v, float* f) {
-  if constexpr (sizeof(T) == 4) {
+  if constexpr (std::is_same_v<T, float>) {
     f[0] = __uint_as_float(v.x);
     f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z);
     f[3] = __uint_as_float(v.w);
-  } else {
+  } else if constexpr (std::is_same_v<T, Bf16>) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(w[i] << 16);  // a bf16 is the top half of a binary32
       f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const h2v h = __builtin_bit_cast(h2v, w[i]);  // binary16 -> binary32 is exact
+      f[2 * i] = (float)h.x;
+      f[2 * i + 1] = (float)h.y;
     }
   }
 }
@@ -111,10 +124,21 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2v));
 }
 
+// two binary32 -> packed binary16, round to nearest even
+__device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
+  const f2v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
+}
+
 template <typename T>
 __device__ __forceinline__ uint4 pack(const float* f) {
   uint4 v;
-  if constexpr (sizeof(T) == 4) {
+  if constexpr (std::is_same_v<T, F16>) {
+    v.x = pack2_f16(f[0], f[1]);
+    v.y = pack2_f16(f[2], f[3]);
+    v.z = pack2_f16(f[4], f[5]);
+    v.w = pack2_f16(f[6], f[7]);
+  } else if constexpr (std::is_same_v<T, float>) {
     v.x = __float_as_uint(f[0]);
     v.y = __float_as_uint(f[1]);
     v.z = __float_as_uint(f[2]);
@@ -131,8 +155,10 @@ __device__ __forceinline__ uint4 pack(const float* f) {
 // value rounded to the storage dtype, back in binary32
 template <typename T>
 __device__ __forceinline__ float to_dtype(float x) {
-  if constexpr (sizeof(T) == 4) {
+  if constexpr (std::is_same_v<T, float>) {
     return x;
+  } else if constexpr (std::is_same_v<T, F16>) {
+    return (float)(_Float16)x;
   } else {
     return (float)(__bf16)x;
   }
@@ -199,54 +225,61 @@ __device__ __forceinline__ uint32_t seg_of(const BandArgs& a, uint32_t kp) {
   return s;
 }
 
-// This lane's (cos, sin) entries of freqs row `pos`: the 2E table floats of
-// the frequencies its chunks rotate (zero where a chunk is not rotated).
-template <typename T, bool IL>
-__device__ __forceinline__ void load_freqs(const float* __restrict__ freqs, uint32_t rope_dim,
-                                           uint32_t pos, uint32_t c0, uint32_t c1, uint32_t j,
-                                           bool rot0, bool rot1, float* fl) {
-  constexpr int E = Fmt<T>::E;
+// N consecutive freqs table entries (binary32 or bf16) as binary32.
+template <bool FB16, int N>
+__device__ __forceinline__ void table_entries(const void* base, int64_t idx, float* out) {
+  if constexpr (!FB16) {
+    const float* p = static_cast<const float*>(base) + idx;
 #pragma unroll
-  for (int e = 0; e < 2 * E; ++e) fl[e] = 0.f;
-  const float* fr = freqs + (int64_t)pos * rope_dim;
-  if constexpr (IL) {
-    // chunk c holds pairs c*E/2 .. c*E/2 + E/2 - 1: table columns c*E .. c*E + E - 1
-    if (rot0) {
-#pragma unroll
-      for (int q = 0; q < E / 4; ++q) {
-        const uint4 v = ld16(fr + c0 * E + 4 * q);
-        fl[4 * q] = __uint_as_float(v.x);
-        fl[4 * q + 1] = __uint_as_float(v.y);
-        fl[4 * q + 2] = __uint_as_float(v.z);
-        fl[4 * q + 3] = __uint_as_float(v.w);
-      }
+    for (int q = 0; q < N / 4; ++q) {
+      const uint4 v = ld16(p + 4 * q);
+      out[4 * q] = __uint_as_float(v.x);
+      out[4 * q + 1] = __uint_as_float(v.y);
+      out[4 * q + 2] = __uint_as_float(v.z);
+      out[4 * q + 3] = __uint_as_float(v.w);
     }
-    if (rot1) {
-#pragma unroll
-      for (int q = 0; q < E / 4; ++q) {
-        const uint4 v = ld16(fr + c1 * E + 4 * q);
-        fl[E + 4 * q] = __uint_as_float(v.x);
-        fl[E + 4 * q + 1] = __uint_as_float(v.y);
-        fl[E + 4 * q + 2] = __uint_as_float(v.z);
-        fl[E + 4 * q + 3] = __uint_as_float(v.w);
-      }
-    }
+  } else if constexpr (N == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    out[0] = __uint_as_float(v.x << 16);
+    out[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    out[2] = __uint_as_float(v.y << 16);
+    out[3] = __uint_as_float(v.y & 0xFFFF0000u);
   } else {
-    // a half-split lane j < rope_dim/(2E) rotates frequencies j*E .. j*E + E - 1
-    if (rot0) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + idx;
 #pragma unroll
-      for (int q = 0; q < E / 2; ++q) {
-        const uint4 v = ld16(fr + 2 * j * E + 4 * q);
-        fl[4 * q] = __uint_as_float(v.x);
-        fl[4 * q + 1] = __uint_as_float(v.y);
-        fl[4 * q + 2] = __uint_as_float(v.z);
-        fl[4 * q + 3] = __uint_as_float(v.w);
+    for (int q = 0; q < N / 8; ++q) {
+      const uint4 v = ld16(p + 8 * q);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[8 * q + 2 * i] = __uint_as_float(w[i] << 16);
+        out[8 * q + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
       }
     }
   }
 }
 
-template <typename T, int D, bool IL, int NPMAX, bool RADD, bool NORM>
+// This lane's (cos, sin) entries of freqs row `pos`: the 2E table values of
+// the frequencies its chunks rotate (zero where a chunk is not rotated).
+template <typename T, bool IL, bool FB16>
+__device__ __forceinline__ void load_freqs(const void* __restrict__ freqs, uint32_t rope_dim,
+                                           uint32_t pos, uint32_t c0, uint32_t c1, uint32_t j,
+                                           bool rot0, bool rot1, float* fl) {
+  constexpr int E = Fmt<T>::E;
+#pragma unroll
+  for (int e = 0; e < 2 * E; ++e) fl[e] = 0.f;
+  const int64_t row = (int64_t)pos * rope_dim;
+  if constexpr (IL) {
+    // chunk c holds pairs c*E/2 .. c*E/2 + E/2 - 1: table columns c*E .. c*E + E - 1
+    if (rot0) table_entries<FB16, E>(freqs, row + c0 * E, fl);
+    if (rot1) table_entries<FB16, E>(freqs, row + c1 * E, fl + E);
+  } else {
+    // a half-split lane j < rope_dim/(2E) rotates frequencies j*E .. j*E + E - 1
+    if (rot0) table_entries<FB16, 2 * E>(freqs, row + 2 * j * E, fl);
+  }
+}
+
+template <typename T, int D, bool IL, int NPMAX, bool RADD, bool NORM, bool FB16>
 __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   constexpr int E = Fmt<T>::E;
   constexpr int CH = D / E;      // 16-byte chunks per head row
@@ -414,7 +447,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   // ---- D: this lane's (cos, sin) entries of the token's freqs row ----
   float fl[RADD ? 1 : 2 * E];
   uint32_t fl_pos = pos[0];
-  if constexpr (!RADD) load_freqs<T, IL>(a.freqs, a.rope_dim, fl_pos, c0, c1, j, rot0, rot1, fl);
+  if constexpr (!RADD) load_freqs<T, IL, FB16>(a.freqs, a.rope_dim, fl_pos, c0, c1, j, rot0, rot1, fl);
 
 
   // ---- E: arithmetic and stores ----
@@ -488,7 +521,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
           // own position (uniform, taken at most once per wave).
           if (pos[sd.cache] != fl_pos) {
             fl_pos = pos[sd.cache];
-            load_freqs<T, IL>(a.freqs, a.rope_dim, fl_pos, c0, c1, j, rot0, rot1, fl);
+            load_freqs<T, IL, FB16>(a.freqs, a.rope_dim, fl_pos, c0, c1, j, rot0, rot1, fl);
           }
           if constexpr (IL) {
 #pragma unroll
@@ -523,35 +556,40 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   }
 }
 
-template <typename T, int D, bool IL, bool RADD, bool NORM>
+template <typename T, int D, bool IL, bool RADD, bool NORM, bool FB16>
 int launch_t(const BandArgs& a, void* stream) {
   constexpr int NPMAX = RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : kMaxPassesStore);
   const uint32_t grid = a.per_xcd ? a.per_xcd * kXcds : a.n_blocks;
-  hipLaunchKernelGGL((band_kernel<T, D, IL, NPMAX, RADD, NORM>), dim3(grid),
-                     dim3(64 * a.waves_per_block), 0,
-                     reinterpret_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL((band_kernel<T, D, IL, NPMAX, RADD, NORM, FB16>), dim3(grid),
+                     dim3(64 * a.waves_per_block), 0, reinterpret_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
-template <typename T, bool IL, bool RADD, bool NORM>
+template <typename T, bool IL, bool RADD, bool NORM, bool FB16>
 int launch_d(const BandArgs& a, uint32_t head_dim, void* stream) {
   switch (head_dim) {
-    case 64: return launch_t<T, 64, IL, RADD, NORM>(a, stream);
-    case 128: return launch_t<T, 128, IL, RADD, NORM>(a, stream);
-    case 256: return launch_t<T, 256, IL, RADD, NORM>(a, stream);
+    case 64: return launch_t<T, 64, IL, RADD, NORM, FB16>(a, stream);
+    case 128: return launch_t<T, 128, IL, RADD, NORM, FB16>(a, stream);
+    case 256: return launch_t<T, 256, IL, RADD, NORM, FB16>(a, stream);
     default: return (int)hipErrorInvalidValue;
   }
+}
+
+template <typename T, bool FB16>
+int launch_f(const BandArgs& a, uint32_t head_dim, bool interleaved, bool norm, void* stream) {
+  if (norm)
+    return interleaved ? launch_d<T, true, false, true, FB16>(a, head_dim, stream)
+                       : launch_d<T, false, false, true, FB16>(a, head_dim, stream);
+  return interleaved ? launch_d<T, true, false, false, FB16>(a, head_dim, stream)
+                     : launch_d<T, false, false, false, FB16>(a, head_dim, stream);
 }
 
 template <typename T>
 int launch_dt(const BandArgs& a, uint32_t head_dim, bool interleaved, bool radd, bool norm,
               void* stream) {
-  if (radd) return launch_d<T, true, true, false>(a, head_dim, stream);
-  if (norm)
-    return interleaved ? launch_d<T, true, false, true>(a, head_dim, stream)
-                       : launch_d<T, false, false, true>(a, head_dim, stream);
-  return interleaved ? launch_d<T, true, false, false>(a, head_dim, stream)
-                     : launch_d<T, false, false, false>(a, head_dim, stream);
+  if (radd) return launch_d<T, true, true, false, false>(a, head_dim, stream);
+  return a.freq_bf16 ? launch_f<T, true>(a, head_dim, interleaved, norm, stream)
+                     : launch_f<T, false>(a, head_dim, interleaved, norm, stream);
 }
 
 }  // namespace
@@ -561,7 +599,8 @@ int launch_band(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interl
   bool norm = false;
   for (uint32_t s = 0; s < a.nseg; ++s) norm = norm || a.seg[s].gamma != nullptr;
   if (dtype == DT_F32) return launch_dt<float>(a, head_dim, interleaved, radd, norm, stream);
-  return launch_dt<uint16_t>(a, head_dim, interleaved, radd, norm, stream);
+  if (dtype == DT_F16) return launch_dt<F16>(a, head_dim, interleaved, radd, norm, stream);
+  return launch_dt<Bf16>(a, head_dim, interleaved, radd, norm, stream);
 }
 
 }  // namespace qrp

@@ -365,7 +365,7 @@ def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_m
                    max_seq_len: int, P_main: int, P_index: int, eps_main: float = 1e-6,
                    eps_index: float = 1e-6, weight_offset: float = 0.0,
                    multiply_before_cast: bool = True, slack: float = 0.25,
-                   cache_lengths=None) -> Case:
+                   cache_lengths=None, freq_dtype: str = F32) -> Case:
     """Dual-band workload: buffer [T, (Hq_main + 2 Hk_main + Hq_index) D] =
     Q-main | K-main | V-main | Q-index; both bands' K caches updated in place."""
     lengths = np.asarray(lengths, dtype=np.int64)
@@ -392,10 +392,10 @@ def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_m
                       q_gamma=g[2], k_gamma=g[3], epsilon=eps_index, cache=1,
                       q_out_row_stride=Hq_index * D)
     return Case(name=name, op="dual", dtype=dtype, seed=seed, lengths=lengths, offsets=off,
-                buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta), rope_dim=rope_dim,
-                interleaved=interleaved, caches=[main, index], layer_idx=0,
+                buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta, freq_dtype),
+                rope_dim=rope_dim, interleaved=interleaved, caches=[main, index], layer_idx=0,
                 bands=[main_band, index_band], weight_offset=weight_offset,
-                multiply_before_cast=multiply_before_cast)
+                multiply_before_cast=multiply_before_cast, freq_dtype=freq_dtype)
 
 
 def make_radd_case(name: str, seed: int, dtype: str, lengths, cache_lengths, batch_offset: int,

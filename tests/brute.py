@@ -87,3 +87,10 @@ def ulp_bf16(x: np.ndarray) -> np.ndarray:
     ax = np.maximum(np.abs(x), 2.0 ** -126)
     e = np.floor(np.log2(ax))
     return np.power(2.0, e - 7)
+
+
+def ulp_f16(x: np.ndarray) -> np.ndarray:
+    """Spacing of IEEE binary16 values at |x| (2^-24 below the normal range)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -14)
+    e = np.floor(np.log2(ax))
+    return np.power(2.0, e - 10)

@@ -1,7 +1,7 @@
 """Device side of the tests and the benchmark: put a synthetic case on the GPU
 and run it through the C ABI (via the thin Python binding).
 
-Buffers hold raw bits (int16 for bf16, int32 for fp32).  Output buffers and
+Buffers hold raw bits (int16 for bf16 and f16, int32 for fp32).  Output buffers and
 cache pools start as the signalling-NaN sentinel so that any stray write,
 or any float round trip of a copied value, shows up in a bit comparison.
 ``q_output`` buffers carry GUARD sentinel rows before and after the rows
@@ -19,8 +19,8 @@ import qk_rope_paged_amd as qrp
 from synth import cases as sc
 
 GUARD = 2
-TORCH_BITS = {sc.F32: torch.int32, sc.BF16: torch.int16}
-QRP_DT = {sc.F32: qrp.QRP_F32, sc.BF16: qrp.QRP_BF16}
+TORCH_BITS = {sc.F32: torch.int32, sc.BF16: torch.int16, sc.F16: torch.int16}
+QRP_DT = {sc.F32: qrp.QRP_F32, sc.BF16: qrp.QRP_BF16, sc.F16: qrp.QRP_F16}
 
 
 def bits_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -31,13 +31,13 @@ def bits_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
 
 def sentinel_int(dtype: str) -> int:
     s = int(sc.SENTINEL[dtype])
-    bits = 16 if dtype == sc.BF16 else 32
+    bits = 32 if dtype == sc.F32 else 16
     return s - (1 << bits) if s >= 1 << (bits - 1) else s
 
 
 def to_numpy_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
     a = t.cpu().numpy()
-    return a.view(np.uint16 if dtype == sc.BF16 else np.uint32)
+    return a.view(np.uint32 if dtype == sc.F32 else np.uint16)
 
 
 @dataclass
@@ -95,8 +95,15 @@ def upload(case: sc.Case, device="cuda") -> DeviceCase:
     buf = bits_tensor(case.buf, device) if case.buf.size else torch.zeros(
         (0, case.row_stride), dtype=TORCH_BITS[case.dtype], device=device)
     off = torch.from_numpy(case.offsets.astype(np.uint32).view(np.int32)).to(device)
-    freqs = (torch.from_numpy(np.ascontiguousarray(case.freqs)).to(device)
-             if case.freqs is not None else torch.zeros(4, dtype=torch.float32, device=device))
+    if case.freqs is None:
+        freqs = torch.zeros(4, dtype=torch.float32, device=device)
+    elif case.freq_dtype == sc.BF16:
+        # the table holds bf16 values in float32: ship their top 16 bits
+        hi = (np.ascontiguousarray(case.freqs, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(hi.astype(np.uint32) << 16, case.freqs.view(np.uint32))
+        freqs = bits_tensor(hi, device)
+    else:
+        freqs = torch.from_numpy(np.ascontiguousarray(case.freqs)).to(device)
     dc = DeviceCase(case=case, buf=buf, offsets=off, freqs=freqs,
                     caches=[upload_cache(c, device) for c in case.caches])
     strides = ([case.q_out_row_stride] if case.op == "store"
@@ -113,7 +120,7 @@ def upload(case: sc.Case, device="cuda") -> DeviceCase:
 def rope_of(dc: DeviceCase) -> qrp.Rope:
     c = dc.case
     return qrp.Rope(freqs_cis=dc.freqs, max_seq_len=c.max_seq_len, rope_dim=c.rope_dim,
-                    interleaved=c.interleaved)
+                    interleaved=c.interleaved, freq_dtype=QRP_DT[c.freq_dtype])
 
 
 def band_of(dc: DeviceCase, i: int) -> qrp.Band:

@@ -7,12 +7,13 @@ The bar:
 * computed values (rotated and/or normalised):
     fp32:  |gpu - v| <= 1e-5 * max(|v|, m)
     bf16:  |gpu - v| <= ulps * ulp_bf16(max(|v|, 2^-8 * m))
+    f16:   |gpu - v| <= ulps * ulp_f16(max(|v|, 2^-11 * m))
   with v the oracle's unrounded value and m the length of v's RoPE pair
   (|v| for unrotated elements).  The pair-length floor is there because
   x*cos - y*sin can cancel: a bound relative to |v| alone would demand more
-  than binary32 arithmetic can give.  ulps = 1 ("one bf16 ulp on a value
-  computed in binary32"); 2 for multiply_before_cast = false, whose
-  intermediate roundings can flip.
+  than binary32 arithmetic can give.  ulps = 1 ("one ulp of the 16-bit
+  type on a value computed in binary32"); 2 for multiply_before_cast =
+  false, whose intermediate roundings can flip.
 """
 from __future__ import annotations
 
@@ -32,6 +33,8 @@ def tol_ok(gpu_bits: np.ndarray, exact: np.ndarray, mag: np.ndarray, dtype: str,
     g = sc.bits_to_f64(gpu_bits, dtype)
     if dtype == sc.F32:
         tol = 1e-5 * np.maximum(np.abs(exact), mag)
+    elif dtype == sc.F16:
+        tol = ulps * brute.ulp_f16(np.maximum(np.abs(exact), 2.0 ** -11 * mag))
     else:
         tol = ulps * brute.ulp_bf16(np.maximum(np.abs(exact), 2.0 ** -8 * mag))
     return np.abs(g - exact) <= tol

@@ -99,6 +99,16 @@ def _store(cache=None, rope=None, **kw):
     (dict(rope=_rope(rope_dim=8)), qrp.QRP_EUNSUPPORTED),
     (dict(rope=_rope(max_seq_len=0)), qrp.QRP_EINVAL),
     (dict(rope=_rope(freqs_cis=None)), qrp.QRP_EINVAL),
+    (dict(rope=_rope(freq_dtype=qrp.QRP_F16)), qrp.QRP_EUNSUPPORTED),
+    (dict(rope=_rope(freq_dtype=9)), qrp.QRP_EUNSUPPORTED),
+    (dict(rope=_rope(freqs_cis=FAKE + 8, freq_dtype=qrp.QRP_BF16)), qrp.QRP_EALIGN),
+    (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_F16), qrp.QRP_EUNSUPPORTED),   # cache is bf16
+    (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_BF16, cache=_cache(dtype=qrp.QRP_F16)),
+     qrp.QRP_EUNSUPPORTED),
+    (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_F16, cache=_cache(dtype=qrp.QRP_F16),
+          rope=_rope(rope_dim=8)), qrp.QRP_EUNSUPPORTED),
+    (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_F16, cache=_cache(dtype=qrp.QRP_F16),
+          qkv=FAKE + 8), qrp.QRP_EALIGN),
 ])
 def test_store_argument_errors(kw, code):
     assert _store(**kw) == code

@@ -76,7 +76,7 @@ def _store(name, seed, dtype, lengths, clen, D=128, R=None, il=True, Hq=8, Hk=2,
                               **kw)
 
 
-@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16])
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("il", [True, False])
 def test_store_head_dims_and_layouts(dtype, D, il):
@@ -85,10 +85,10 @@ def test_store_head_dims_and_layouts(dtype, D, il):
     run_and_compare(_store(f"store_{dtype}_{D}_{il}", 7, dtype, lens, clen, D=D, il=il))
 
 
-@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16])
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
 @pytest.mark.parametrize("il", [True, False])
 def test_store_partial_rope_padding_and_specials(dtype, il):
-    R = 32 if dtype == sc.BF16 else 16
+    R = 16 if dtype == sc.F32 else 32
     case = _store("store_partial", 8, dtype, [9, 4, 21], [2, 60, 7], D=128, R=R, il=il,
                   specials=True, q_out_pad=16, row_pad=24)
     run_and_compare(case)
@@ -122,12 +122,12 @@ def _norm(name, seed, dtype, lengths, clen, k_in_cache, D=128, R=64, il=True, **
                              k_in_cache=k_in_cache, **kw)
 
 
-@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16])
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
 @pytest.mark.parametrize("k_in_cache", [False, True])
 @pytest.mark.parametrize("il", [True, False])
 def test_norm_single_band(dtype, k_in_cache, il):
     case = _norm("norm", 14, dtype, [7, 0, 30, 3], [0, 5, 17, 200], k_in_cache, il=il,
-                 weight_offset=0.25 if dtype == sc.BF16 else 0.0, eps=1e-5)
+                 weight_offset=0.0 if dtype == sc.F32 else 0.25, eps=1e-5)
     run_and_compare(case)
 
 
@@ -137,8 +137,9 @@ def test_norm_on_one_role_only(q_norm, k_norm):
     run_and_compare(case)
 
 
-def test_norm_multiply_after_cast():
-    case = _norm("norm_mbc0", 16, sc.BF16, [25, 9], [0, 31], False, multiply_before_cast=False,
+@pytest.mark.parametrize("dtype", [sc.BF16, sc.F16])
+def test_norm_multiply_after_cast(dtype):
+    case = _norm("norm_mbc0", 16, dtype, [25, 9], [0, 31], False, multiply_before_cast=False,
                  weight_offset=0.5)
     run_and_compare(case, ulps=2)
 
@@ -166,4 +167,44 @@ def test_radd_fp32_and_subnormals():
     specials = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x0080, 0x7F7F, 0x3C00], np.uint16)
     flat = case.buf.reshape(-1)
     flat[::3] = specials[np.arange(len(flat[::3])) % len(specials)]
+    run_and_compare(case)
+
+
+def test_radd_f16_specials():
+    case = sc.make_radd_case("radd_f16", 22, sc.F16, [5, 11, 0, 3], [4, 1, 0, 9, 2], 1, Hk=2,
+                             D=128, P=16, L=2, layer=1)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x83FF, 0x0400, 0x7BFF, 0xFBFF, 0x3C00],
+                        np.uint16)
+    flat = case.buf.reshape(-1)
+    flat[::5] = specials[np.arange(len(flat[::5])) % len(specials)]
+    run_and_compare(case)
+
+
+# ---------------------------------------------------------------------------
+# bf16 freqs_cis tables (the table's dtype is its own parameter)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
+@pytest.mark.parametrize("il", [True, False])
+def test_store_bf16_freqs(dtype, il):
+    R = 64 if il else 128
+    case = _store(f"store_bf16freqs_{dtype}_{il}", 23, dtype, [9, 1, 26, 0, 4], [0, 70, 3, 8, 300],
+                  D=128, R=R, il=il, freq_dtype=sc.BF16)
+    run_and_compare(case)
+
+
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
+@pytest.mark.parametrize("il", [True, False])
+def test_norm_bf16_freqs(dtype, il):
+    case = _norm(f"norm_bf16freqs_{dtype}_{il}", 24, dtype, [13, 2, 0, 21], [1, 0, 44, 250],
+                 il ^ (dtype == sc.F16), il=il, freq_dtype=sc.BF16, weight_offset=0.0)
+    run_and_compare(case)
+
+
+def test_dual_band_bf16_freqs_f16():
+    case = sc.make_dual_case("dual_f16_bf16freqs", 25, sc.F16, [6, 0, 31, 2], Hq_main=16,
+                             Hk_main=4, Hq_index=4, D=128, rope_dim=64, interleaved=True,
+                             theta=1e4, max_seq_len=512, P_main=32, P_index=16, eps_main=1e-6,
+                             eps_index=1e-5, weight_offset=0.0, cache_lengths=[0, 3, 17, 400],
+                             freq_dtype=sc.BF16)
     run_and_compare(case)
