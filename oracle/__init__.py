@@ -103,6 +103,10 @@ def load() -> ctypes.CDLL:
     lib.orc_kv_cache_radd.argtypes = [P, I32, U32, U64, P, U32, U32, ctypes.POINTER(OrcCache),
                                       U32, P, P]
     lib.orc_kv_cache_radd.restype = I32
+    lib.orc_fused_qk_rope_bshd.argtypes = [P, I32, U32, U32, U32, P, P, U32, U32, I32,
+                                           ctypes.POINTER(OrcCache), U32, P,
+                                           ctypes.POINTER(OrcTrace)]
+    lib.orc_fused_qk_rope_bshd.restype = I32
     _lib = lib
     return lib
 
@@ -146,6 +150,11 @@ def touched_pages(case, ci: int) -> np.ndarray:
         return np.zeros(0, dtype=np.int64)
     seq = np.searchsorted(off, np.arange(T), side="right") - 1
     local = np.arange(T) - off[seq]
+    if case.op == "bshd":                    # only rows below the valid length touch the cache
+        real = local < np.asarray(case.lengths, dtype=np.int64)[seq]
+        seq, local = seq[real], local[real]
+        if len(seq) == 0:
+            return np.zeros(0, dtype=np.int64)
     cseq = seq + case.batch_offset
     pos = cache.cache_lengths.astype(np.int64)[cseq] + local
     pages = cache.lookup_table[cseq, pos // cache.page_size].astype(np.int64)
@@ -267,6 +276,20 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
                                    case.batch_offset, ctypes.byref(ocaches[0]), case.layer_idx,
                                    _ptr(krow), _ptr(vrow))
         res.traces.append(dict(k_row_off=krow, v_row_off=vrow))
+    elif case.op == "bshd":
+        cache = case.caches[0]
+        D, Hk, Hq = cache.head_dim, cache.num_kv_heads, case.n_q_heads
+        out = np.full((T, Hq * D), _SENT[case.dtype], dtype=_BITS[case.dtype])
+        valid = np.ascontiguousarray(case.lengths, dtype=np.uint32)
+        keep += [out, valid]
+        tr, otr = _trace(T, Hq, Hk, D, keep) if trace else (None, None)
+        t0 = time.perf_counter()
+        st = lib.orc_fused_qk_rope_bshd(
+            _ptr(buf), dt, case.batch, case.seq_len, Hq, _ptr(valid), _ptr(freqs),
+            case.max_seq_len, case.rope_dim, int(case.interleaved), ctypes.byref(ocaches[0]),
+            case.layer_idx, _ptr(out), ctypes.byref(otr) if otr is not None else None)
+        res.q_out.append(out)
+        res.traces.append(tr)
     else:
         raise ValueError(case.op)
     res.seconds = time.perf_counter() - t0

@@ -462,3 +462,74 @@ int32_t orc_kv_cache_radd(const void* a, int32_t dtype, uint32_t T, uint64_t a_r
   }
   return ORC_OK;
 }
+
+/* Padded continuous batching (generic_fused_qk_rope_bshd_continuous_batch
+ * page, signature and Args): q_proj and output are [B][S][n_q_heads][D].
+ * Row s of sequence b is a real token when s < valid_lengths[b]; it sits at
+ * position cache_lengths[b] + s, its Q heads are rotated into output and its
+ * K rows, already in the cache, are rotated in place.  Other rows get no
+ * rotation: their output row is the input row's bits and the cache is left
+ * alone.  Trace rows of Q are filled for every row (a copied row records its
+ * own values); k_row_off stays untouched (-1 from the caller) for rows
+ * without K work. */
+int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t B, uint32_t S,
+                               uint32_t n_q_heads, const uint32_t* valid_lengths,
+                               const float* freqs, uint32_t max_seq_len, uint32_t R,
+                               int32_t interleaved, orc_cache* c, uint32_t layer_idx,
+                               void* output, orc_trace* tr) {
+  int32_t st = check_common(dtype, c, R, layer_idx, max_seq_len);
+  if (st) return st;
+  if (B == 0 || S == 0) return ORC_OK;
+  if (!q_proj || !valid_lengths || !freqs || !output || n_q_heads == 0) return ORC_EINVAL;
+  if (B > c->cache_batch) return ORC_EINVAL;
+  const uint32_t D = c->head_dim, Hq = n_q_heads, Hk = c->num_kv_heads;
+  const int64_t row_len = (int64_t)Hq * D;
+
+  /* every real token's position and page must exist before anything is written */
+  for (uint32_t b = 0; b < B; ++b) {
+    for (uint32_t s = 0; s < S && s < valid_lengths[b]; ++s) {
+      uint64_t pos = (uint64_t)c->cache_lengths[b] + s;
+      if (pos >= max_seq_len) return ORC_EDATA;
+      uint64_t page;
+      uint32_t slot;
+      if ((st = locate(c, b, (uint32_t)pos, &page, &slot))) return st;
+    }
+  }
+
+  head_buf hb;
+  if (!head_buf_alloc(&hb, D)) return ORC_EINVAL;
+  for (uint32_t b = 0; b < B; ++b) {
+    for (uint32_t s = 0; s < S; ++s) {
+      const uint64_t t = (uint64_t)b * S + s;
+      const int64_t row = (int64_t)t * row_len;
+      if (s >= valid_lengths[b]) {
+        for (int64_t e = 0; e < row_len; ++e) copy_bits(output, row + e, q_proj, row + e, dtype);
+        if (tr && tr->q_exact)
+          for (int64_t e = 0; e < row_len; ++e) tr->q_exact[t * row_len + e] = get(q_proj, dtype, row + e);
+        if (tr && tr->q_mag)
+          for (int64_t e = 0; e < row_len; ++e) tr->q_mag[t * row_len + e] = fabs(get(q_proj, dtype, row + e));
+        continue;
+      }
+      const uint32_t pos = c->cache_lengths[b] + s;
+      uint64_t page = 0;
+      uint32_t slot = 0;
+      locate(c, b, pos, &page, &slot); /* checked above */
+      for (uint32_t h = 0; h < Hq; ++h) {
+        double* ex = tr && tr->q_exact ? tr->q_exact + (t * Hq + h) * D : NULL;
+        double* mg = tr && tr->q_mag ? tr->q_mag + (t * Hq + h) * D : NULL;
+        do_head(q_proj, row + (int64_t)h * D, output, row + (int64_t)h * D, dtype, D, NULL, 0.0,
+                0.0, 1, freqs, pos, R, interleaved, &hb, ex, mg);
+      }
+      for (uint32_t h = 0; h < Hk; ++h) {
+        int64_t dst = row_offset(c, page, 0, layer_idx, slot, h);
+        double* ex = tr && tr->k_exact ? tr->k_exact + (t * Hk + h) * D : NULL;
+        double* mg = tr && tr->k_mag ? tr->k_mag + (t * Hk + h) * D : NULL;
+        do_head(c->pool, dst, c->pool, dst, dtype, D, NULL, 0.0, 0.0, 1, freqs, pos, R,
+                interleaved, &hb, ex, mg);
+        if (tr && tr->k_row_off) tr->k_row_off[t * Hk + h] = dst;
+      }
+    }
+  }
+  free(hb.x);
+  return ORC_OK;
+}

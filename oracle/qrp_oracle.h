@@ -129,6 +129,19 @@ int32_t orc_kv_cache_radd(
     const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t batch_offset,
     orc_cache* cache, uint32_t layer_idx, int64_t* k_row_off, int64_t* v_row_off);
 
+/* generic_fused_qk_rope_bshd_continuous_batch page (signature, Args):
+ * q_proj and output [B][S][n_q_heads][head_dim], valid_lengths [B]; the
+ * cache's sequence b is batch row b (a continuous-batching cache is the
+ * one-page-per-sequence case).  Rows s >= valid_lengths[b] pass through
+ * (output = input bits, cache untouched: parity unpinned, the page only
+ * says RoPE is confined to the valid rows). */
+int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t batch_size,
+                               uint32_t seq_len, uint32_t n_q_heads,
+                               const uint32_t* valid_lengths, const float* freqs_cis,
+                               uint32_t max_seq_len, uint32_t rope_dim, int32_t interleaved,
+                               orc_cache* cache, uint32_t layer_idx, void* output,
+                               orc_trace* trace);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,15 +66,16 @@ def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 def freqs_table(max_seq_len: int, rope_dim: int, base: float, freq_dtype: str = F32) -> np.ndarray:
     """freqs_cis[p, 2i] = cos(p * base^(-2i/R)), [p, 2i+1] = sin(...), fp64 -> fp32
-    (-> bf16 for a bf16 table; the float32 array then holds bf16 values)."""
+    (a bf16 table: -> fp32 -> bf16; an f16 table: fp64 -> f16; the float32
+    array then holds those values)."""
     i = np.arange(rope_dim // 2, dtype=np.float64)
     inv = base ** (-2.0 * i / rope_dim)
     ang = np.arange(max_seq_len, dtype=np.float64)[:, None] * inv[None, :]
     tab = np.empty((max_seq_len, rope_dim), dtype=np.float64)
     tab[:, 0::2] = np.cos(ang)
     tab[:, 1::2] = np.sin(ang)
-    if freq_dtype == BF16:
-        return bits_to_f64(to_bits(tab, BF16), BF16).astype(np.float32)
+    if freq_dtype in (BF16, F16):
+        return bits_to_f64(to_bits(tab, freq_dtype), freq_dtype).astype(np.float32)
     return tab.astype(np.float32)
 
 
@@ -171,7 +172,7 @@ class Band:
 @dataclass
 class Case:
     name: str
-    op: str                             # 'store' | 'norm' | 'dual' | 'radd'
+    op: str                             # 'store' | 'norm' | 'dual' | 'radd' | 'bshd'
     dtype: str
     seed: int
     lengths: np.ndarray                 # int64 [B]
@@ -188,7 +189,8 @@ class Case:
     bands: List[Band] = field(default_factory=list)
     weight_offset: float = 0.0
     multiply_before_cast: bool = True
-    freq_dtype: str = F32               # table entries: f32, or bf16 values held in float32
+    freq_dtype: str = F32               # table entries: f32, or bf16 / f16 values held in float32
+    seq_len: int = 0                    # bshd: padded rows per sequence (lengths = valid lengths)
 
     @property
     def T(self) -> int:
@@ -429,8 +431,37 @@ def make_radd_case(name: str, seed: int, dtype: str, lengths, cache_lengths, bat
                 layer_idx=layer, batch_offset=batch_offset)
 
 
+def make_bshd_case(name: str, seed: int, dtype: str, valid_lengths, seq_len: int, cache_lengths,
+                   Hq: int, Hk: int, D: int, rope_dim: int, interleaved: bool, theta: float,
+                   max_seq_len: int, capacity: int, L: int, layer: int,
+                   num_blocks: Optional[int] = None, slack: float = 0.25,
+                   freq_dtype: Optional[str] = None) -> Case:
+    """Padded continuous-batching workload: q_proj [B, seq_len, Hq, D] N(0, 1)
+    held as [B * seq_len, Hq * D]; a continuous-batching cache of blocks of
+    ``capacity`` rows (one page per sequence, a seeded permutation of the
+    blocks), whose K and V rows [cache_len, cache_len + min(valid, seq_len))
+    hold N(0, 1) (the projection's K and V).  The table has the op's dtype
+    unless ``freq_dtype`` says otherwise."""
+    valid = np.asarray(valid_lengths, dtype=np.int64)
+    cl = np.asarray(cache_lengths, dtype=np.int64)
+    B = len(valid)
+    real = np.minimum(valid, seq_len)
+    cache = _paged_cache(seed, S_PERM, dtype, Hk, D, capacity, L, 2, cl, cl + real, 1, num_blocks,
+                         slack)
+    T = B * seq_len
+    width = Hq * D
+    buf = to_bits(prng.normal(seed, S_BUF, T * width), dtype).reshape(T, width)
+    _prefill_rows(cache, seed, S_PREFILL, layer, [0, 1], range(B), cl, real)
+    off = (np.arange(B + 1, dtype=np.int64) * seq_len).astype(np.uint32)
+    fdt = dtype if freq_dtype is None else freq_dtype
+    return Case(name=name, op="bshd", dtype=dtype, seed=seed, lengths=valid, offsets=off, buf=buf,
+                freqs=freqs_table(max_seq_len, rope_dim, theta, fdt), rope_dim=rope_dim,
+                interleaved=interleaved, caches=[cache], layer_idx=layer, n_q_heads=Hq,
+                q_out_row_stride=width, freq_dtype=fdt, seq_len=seq_len)
+
+
 # ---------------------------------------------------------------------------
-# the five workloads
+# the workloads
 # ---------------------------------------------------------------------------
 
 def tiny_fp32(seed: int = 1) -> Case:
@@ -484,5 +515,23 @@ def radd(seed: int = 5, small: bool = False) -> Case:
                           Hk=8, D=128, P=128, L=4, layer=3)
 
 
+def bshd(seed: int = 6, small: bool = False) -> Case:
+    """Padded continuous batching on the prefill shapes: every sequence padded
+    to the longest length the prefill batch draws (2048), valid lengths drawn
+    as the prefill lengths are, a bf16 table (the op's dtype)."""
+    if small:
+        B, S = 4, 300
+        valid = prng.integers(seed, S_LENS, B, 0, S)
+        clen = prng.integers(seed, S_CLEN, B, 0, 500)
+        return make_bshd_case("bshd_small", seed, BF16, valid, S, clen, Hq=32, Hk=8, D=128,
+                              rope_dim=128, interleaved=False, theta=5e5, max_seq_len=1024,
+                              capacity=1024, L=2, layer=1)
+    B, S = 8, 2048
+    valid = prng.integers(seed, S_LENS, B, 128, S)
+    return make_bshd_case("bshd", seed, BF16, valid, S, np.zeros(B, np.int64), Hq=32, Hk=8,
+                          D=128, rope_dim=128, interleaved=False, theta=5e5, max_seq_len=8192,
+                          capacity=8192, L=1, layer=0)
+
+
 WORKLOADS = {"tiny_fp32": tiny_fp32, "prefill": prefill, "decode": decode, "dual": dual,
-             "radd": radd}
+             "radd": radd, "bshd": bshd}

@@ -15,6 +15,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_bshd_pins as bshd_pins
 from tests import test_oracle_pins as pins
 
 MUTATIONS = {
@@ -53,6 +54,11 @@ MUTATIONS = {
                         "float sum = cur + add + add;"),
     "radd_halves_swapped": ("(int64_t)(plane * hidden)", "(int64_t)((1 - plane) * hidden)"),
     "unroped_dims_rounded": ("if (gamma || j < R)", "if (1)"),
+    "bshd_padded_rows_roped": ("if (s >= valid_lengths[b]) {", "if (s > valid_lengths[b]) {"),
+    "bshd_position_ignores_cache_len": ("const uint32_t pos = c->cache_lengths[b] + s;",
+                                        "const uint32_t pos = s;"),
+    "bshd_k_from_v_plane": ("int64_t dst = row_offset(c, page, 0, layer_idx, slot, h);",
+                            "int64_t dst = row_offset(c, page, 1, layer_idx, slot, h);"),
 }
 
 PIN_TESTS = [
@@ -73,6 +79,8 @@ PIN_TESTS = [
     (pins.test_rmsnorm_epsilon_sits_inside_the_root, {}),
     (pins.test_radd_is_one_binary32_add_per_element, {"dtype": "bf16"}),
     (pins.test_radd_is_one_binary32_add_per_element, {"dtype": "f32"}),
+    (bshd_pins.test_bshd_matches_complex_brute_force, {"dtype": "bf16", "interleaved": False}),
+    (bshd_pins.test_bshd_padded_rows_are_copied_bit_for_bit, {}),
 ]
 
 
