@@ -1,13 +1,14 @@
 #!/usr/bin/env python3
 """Throughput of the fused ragged RoPE + split + paged-KV store on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload prefill|decode|dual|radd]
+    python bench.py [--steps K] [--warmup W] [--workload prefill|decode|dual|radd|bshd]
 
 A step is one call of the pass over one batch of seeded synthetic input that
 is already resident in HBM.  The default workload is the Llama-3-8B-shaped
 prefill (32 Q / 8 KV heads, head_dim 128, bf16, half-split RoPE, theta 5e5,
 batch 8 with lengths U[128, 2048], page 128, 32 layers, layer 17).  Other
-workloads (decode, dual band, radd) are for measuring the other kernels.
+workloads (decode, dual band, radd, padded continuous batching) are for
+measuring the other operations.
 
 The default warm-up (300 launches) is long on purpose: the first few
 hundred launches over multi-GB pools run a few per cent slower (clocks and
@@ -93,8 +94,14 @@ def algorithmic_bytes(case) -> int:
 
     eb = sc.ELEM_BYTES[case.dtype]
     T = case.T
+    seq, pos = cache_rows(case)
     total = 0
-    if case.op == "store":
+    if case.op == "bshd":
+        c = case.caches[0]
+        D, Hk, Hq = c.head_dim, c.num_kv_heads, case.n_q_heads
+        total += 2 * T * Hq * D * eb                 # every q_proj row read and written
+        total += 2 * len(pos) * Hk * D * eb          # real rows: K read and written in place
+    elif case.op == "store":
         c = case.caches[0]
         D, Hk, Hq = c.head_dim, c.num_kv_heads, case.n_q_heads
         total += T * (Hq + 2 * Hk) * D * eb          # qkv read
@@ -111,34 +118,43 @@ def algorithmic_bytes(case) -> int:
     elif case.op == "radd":
         c = case.caches[0]
         total += 3 * T * 2 * c.num_kv_heads * c.head_dim * eb   # read a, read cache, write cache
-    if case.freqs is not None and T:
-        pos = token_positions(case)
-        total += len(np.unique(pos)) * case.rope_dim * 4
-    total += (case.batch + 1) * 4                                 # offsets
-    pos = token_positions(case)
-    seq = np.repeat(np.arange(case.batch), np.diff(case.offsets.astype(np.int64)))
+    if case.freqs is not None and len(pos):
+        total += len(np.unique(pos)) * case.rope_dim * sc.ELEM_BYTES[case.freq_dtype]
+    total += (case.batch + (0 if case.op == "bshd" else 1)) * 4   # offsets / valid lengths
     for c in case.caches:
         total += case.batch * 4                                    # cache lengths
-        if T:                                                      # distinct page-table entries
+        if len(pos):                                               # distinct page-table entries
             total += len(np.unique(seq * (c.max_pages_per_seq + 1) + pos // c.page_size)) * 4
     return int(total)
 
 
-def token_positions(case):
-    """Cache position of every token: its sequence's cache length plus its
+def cache_rows(case):
+    """(sequence, cache position) of every row that reaches the cache: every
+    token of a ragged op; the rows below their sequence's valid length on the
+    padded grid.  A position is the sequence's cache length plus the row's
     index within the sequence."""
     import numpy as np
 
     off = case.offsets.astype(np.int64)
-    out = []
+    seqs, out = [], []
     for b in range(case.batch):
         n = int(off[b + 1] - off[b])
+        if case.op == "bshd":
+            n = min(n, int(case.lengths[b]))
         cl = int(case.caches[0].cache_lengths[b + case.batch_offset])
         out.append(np.arange(cl, cl + n))
-    return np.concatenate(out) if out else np.zeros(0, np.int64)
+        seqs.append(np.full(n, b, np.int64))
+    if not out:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    return np.concatenate(seqs), np.concatenate(out)
 
 
-DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5}
+def case_tokens(case) -> int:
+    """Tokens a step processes (the padded grid counts its real rows only)."""
+    return len(cache_rows(case)[1]) if case.op == "bshd" else case.T
+
+
+DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5, "bshd": 6}
 
 
 def make_case(workload: str, seed: int = None):
@@ -150,14 +166,19 @@ def make_case(workload: str, seed: int = None):
 def workload_config(case, cases) -> dict:
     c = case.caches[0]
     cfg = {"workload": {"store": "rope_split_store_paged", "norm": "qk_rmsnorm_rope_paged",
-                        "dual": "dual_band", "radd": "kv_cache_radd"}[case.op] + ":" + case.name,
+                        "dual": "dual_band", "radd": "kv_cache_radd",
+                        "bshd": "fused_qk_rope_bshd_continuous_batch"}[case.op] + ":" + case.name,
            "batch": case.batch, "head_dim": c.head_dim, "kv_heads": c.num_kv_heads,
            "page_size": c.page_size, "num_layers": c.num_layers, "layer_idx": case.layer_idx,
            "seeds": [x.seed for x in cases], "tokens_per_batch": [x.T for x in cases],
            "tokens_mean": round(sum(x.T for x in cases) / len(cases), 1)}
-    if case.op == "store":
+    if case.op in ("store", "bshd"):
         cfg["q_heads"] = case.n_q_heads
-    if case.op in ("store", "norm", "dual"):
+    if case.op == "bshd":
+        cfg["seq_len"] = case.seq_len
+        cfg["real_tokens_per_batch"] = [case_tokens(x) for x in cases]
+        cfg["freq_dtype"] = case.freq_dtype
+    if case.op in ("store", "norm", "dual", "bshd"):
         cfg["rope"] = "interleaved" if case.interleaved else "half-split"
         cfg["rope_dim"] = case.rope_dim
     if case.op == "dual":
@@ -179,7 +200,7 @@ def build_sets(cases):
     def referenced(case):
         c = case.caches[0]
         seq = np.repeat(np.arange(case.batch), np.diff(case.offsets.astype(np.int64)))
-        pidx = token_positions(case) // c.page_size
+        pidx = cache_rows(case)[1] // c.page_size
         return np.unique(seq * c.max_pages_per_seq + pidx)
 
     first = cases[0]
@@ -307,7 +328,7 @@ def cpu_baseline(cases, seconds: float, max_passes: int) -> dict:
             raise RuntimeError(f"oracle failed with status {res.status}")
         total += res.seconds
         nbytes += algorithmic_bytes(case)
-        ntok += case.T
+        ntok += case_tokens(case)
         passes += 1
     return {"value": round(nbytes / total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} full passes over the first {min(passes, len(cases))} seeded "
@@ -334,7 +355,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "dual", "radd"])
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "decode", "dual", "radd", "bshd"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-max-passes", type=int, default=30)
@@ -394,7 +416,7 @@ def main() -> int:
     # own two events (an event pair adds about 2 us to what it measures)
     _, durs = time_launches(calls, K, 0)
     step_bytes = [set_bytes[k % n_sets] for k in range(K)]
-    step_tokens = [cases[k % n_sets].T for k in range(K)]
+    step_tokens = [case_tokens(cases[k % n_sets]) for k in range(K)]
     kern = sorted(durs)
     log(f"[bench] timed {K} steps: wall {wall * 1e3:.2f} ms, events {gpu_time * 1e3:.2f} ms "
         f"({gpu_time / K * 1e6:.2f} us per launch); single launches p10 {kern[K // 10] * 1e6:.2f} "

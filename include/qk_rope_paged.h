@@ -109,13 +109,13 @@ typedef struct qrp_paged_cache {
  * (half-split) pairs dims (i, i + rope_dim/2).  A pair (x, y) becomes
  * (x cos - y sin, x sin + y cos).  rope_dim must be a multiple of
  * 16 bytes / sizeof(dtype) * 2 (16 for bf16 and f16, 8 for f32).
- * freq_dtype QRP_BF16 stores each entry as a bfloat16 (the table's dtype is
- * a parameter of its own on the page, independent of the op's dtype); its
- * values are widened exactly to binary32 before use.
+ * freq_dtype QRP_BF16 / QRP_F16 store each entry as a bfloat16 / binary16
+ * (the table's dtype is a parameter of its own on the page, independent of
+ * the op's dtype); its values are widened exactly to binary32 before use.
  */
 typedef struct qrp_rope {
   const void* freqs_cis;
-  int32_t freq_dtype;          /* QRP_F32 or QRP_BF16 (any op dtype) */
+  int32_t freq_dtype;          /* QRP_F32, QRP_BF16 or QRP_F16 (any op dtype) */
   uint32_t max_seq_len;
   uint32_t rope_dim;
   int32_t interleaved;
@@ -215,6 +215,34 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
 int32_t kv_cache_radd(const void* a, int32_t dtype, uint32_t total_rows, uint64_t a_row_stride,
                       const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t batch_offset,
                       const qrp_paged_cache* cache, uint32_t layer_idx, void* stream);
+
+/*
+ * generic_fused_qk_rope_bshd_continuous_batch page (signature, Summary,
+ * Args).  Padded continuous batching: q_proj and output are device
+ * [batch_size][seq_len][n_q_heads][head_dim] of dtype, contiguous (output
+ * may not alias q_proj).  valid_lengths is device uint32 [batch_size].  For
+ * sequence b and row s < valid_lengths[b], at position
+ * p = cache_lengths[b] + s:
+ *   output[b][s][h] = RoPE(q_proj[b][s][h], p) for every Q head h;
+ *   the K row of every KV head at position p of sequence b (plane 0, layer
+ *   layer_idx) is read from the cache, rotated and written back in place
+ *   (the projection has already stored it there).
+ * Rows s >= valid_lengths[b] get no RoPE: their output row is q_proj's row,
+ * bit for bit, and their cache rows are not touched.  V is never touched.
+ * A continuous-batching cache (one contiguous block of rows per sequence)
+ * is the case page_size = rows per block, max_pages_per_seq = 1,
+ * lookup_table[b] = the block of sequence b; any paged cache also works.
+ * The table's entry type (freq_dtype) may be QRP_F32, QRP_BF16 or QRP_F16
+ * (the page gives the table the op's dtype).  Requires batch_size <=
+ * cache_batch and batch_size * seq_len < 2^31.  A valid row whose position
+ * or page is out of range writes nothing (run qrp_validate to find such
+ * metadata); batch_size == 0 or seq_len == 0 returns QRP_OK without a launch.
+ */
+int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, uint32_t batch_size,
+                                            uint32_t seq_len, uint32_t n_q_heads,
+                                            const uint32_t* valid_lengths, const qrp_rope* rope,
+                                            const qrp_paged_cache* cache, uint32_t layer_idx,
+                                            void* output, void* stream);
 
 /*
  * Debug check of the device metadata one of the calls above would use:

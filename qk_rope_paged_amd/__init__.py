@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "QRP_OK", -1: "QRP_EINVAL", -2: "QRP_EALIGN", -3: "QRP_EUNSUP
 
 # entry points declared in include/qk_rope_paged.h
 EXPORTS = ("rope_split_store_paged", "qk_rmsnorm_rope_paged", "dual_band", "kv_cache_radd",
-           "qrp_validate", "qrp_validate_host", "qrp_last_error", "qrp_abi_version")
+           "fused_qk_rope_bshd_continuous_batch", "qrp_validate", "qrp_validate_host", "qrp_last_error", "qrp_abi_version")
 
 
 class QrpError(RuntimeError):
@@ -72,7 +72,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         pass
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m qk_rope_paged_amd.build` "
+            f"{path} is missing: build it with `python qk_rope_paged_amd/build.py` "
             "(or __graft_entry__.build()); there is no non-HIP fallback")
     lib = ctypes.CDLL(path)
     P, U32, U64, I32, F = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32, ctypes.c_float
@@ -82,6 +82,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "qk_rmsnorm_rope_paged": [P, I32, U32, U64, PB, F, I32, P, U32, PR, U32, P],
         "dual_band": [P, I32, U32, U64, PB, PB, F, I32, P, U32, PR, U32, P],
         "kv_cache_radd": [P, I32, U32, U64, P, U32, U32, PC, U32, P],
+        "fused_qk_rope_bshd_continuous_batch": [P, I32, U32, U32, U32, P, PR, PC, U32, P, P],
         "qrp_validate": [P, U32, U32, U32, PC, U32, P],
         "qrp_validate_host": [P, U32, U32, U32, P, P, U32, U32, U32, U64, U32],
     }
@@ -259,6 +260,16 @@ def kv_cache_radd(a, dtype: int, total_rows: int, a_row_stride: int, input_row_o
     args = (_ptr(a), dtype, total_rows, a_row_stride, _ptr(input_row_offsets), batch_size,
             batch_offset, ctypes.byref(cc), layer_idx, _stream(stream))
     return _call(lib.kv_cache_radd, args, [cc], raise_on_error, prepare)
+
+
+def fused_qk_rope_bshd_continuous_batch(q_proj, dtype: int, batch_size: int, seq_len: int,
+                                        n_q_heads: int, valid_lengths, rope: Rope,
+                                        cache: PagedCache, layer_idx: int, output, stream=None,
+                                        raise_on_error: bool = True, prepare: bool = False):
+    cc, rc = cache.to_c(), rope.to_c()
+    args = (_ptr(q_proj), dtype, batch_size, seq_len, n_q_heads, _ptr(valid_lengths),
+            ctypes.byref(rc), ctypes.byref(cc), layer_idx, _ptr(output), _stream(stream))
+    return _call(lib.fused_qk_rope_bshd_continuous_batch, args, [cc, rc], raise_on_error, prepare)
 
 
 def qrp_validate(input_row_offsets, batch_size: int, total_seq_len: int, batch_offset: int,

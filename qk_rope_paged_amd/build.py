@@ -1,6 +1,6 @@
 """Build the HIP library in-tree: qk_rope_paged_amd/libqk_rope_paged.so (gfx950).
 
-    python -m qk_rope_paged_amd.build
+    python qk_rope_paged_amd/build.py
 
 hipcc compiles the kernels and the C-ABI for gfx950 only.  Packed binary32
 instructions are switched off for the device code (-packed-fp32-ops); hipcc's

@@ -83,8 +83,8 @@ int32_t check_cache(const qrp_paged_cache* c, int32_t dtype, uint32_t layer_idx,
 
 int32_t check_rope(const qrp_rope* r, int32_t dtype, uint32_t head_dim) {
   if (!r || !r->freqs_cis) return fail(QRP_EINVAL, "rope / freqs_cis is NULL");
-  if (r->freq_dtype != QRP_F32 && r->freq_dtype != QRP_BF16)
-    return fail(QRP_EUNSUPPORTED, "freqs_cis must be float32 or bfloat16");
+  if (!dtype_ok(r->freq_dtype))
+    return fail(QRP_EUNSUPPORTED, "freq_dtype must be QRP_F32, QRP_BF16 or QRP_F16");
   if (!aligned16(r->freqs_cis)) return fail(QRP_EALIGN, "freqs_cis not 16-byte aligned");
   if (r->max_seq_len == 0) return fail(QRP_EINVAL, "max_seq_len must be positive");
   if (r->rope_dim == 0 || r->rope_dim > head_dim || r->rope_dim % 2)
@@ -265,7 +265,7 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
                                uint32_t layer_idx, void* q_output, int32_t q_out_dtype,
                                uint64_t q_out_row_stride, void* stream) {
   g_err.clear();
-  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32 or QRP_BF16");
+  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
   if (q_out_dtype != dtype) return fail(QRP_EUNSUPPORTED, "q_out_dtype must equal dtype");
   if (total_seq_len == 0) return QRP_OK;
   int32_t st;
@@ -294,7 +294,7 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
   b.a.batch = batch_size;
   b.a.batch_offset = 0;
   b.a.freqs = rope->freqs_cis;
-  b.a.freq_bf16 = rope->freq_dtype == QRP_BF16;
+  b.a.freq_dtype = (uint32_t)rope->freq_dtype;
   b.a.rope_dim = rope->rope_dim;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.multiply_before_cast = 1;
@@ -314,7 +314,7 @@ int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq
                               uint32_t batch_size, const qrp_rope* rope, uint32_t layer_idx,
                               void* stream) {
   g_err.clear();
-  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32 or QRP_BF16");
+  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
   if (total_seq_len == 0) return QRP_OK;
   int32_t st;
   if ((st = check_batch(input_row_offsets, total_seq_len, batch_size))) return st;
@@ -334,7 +334,7 @@ int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
   b.a.freqs = rope->freqs_cis;
-  b.a.freq_bf16 = rope->freq_dtype == QRP_BF16;
+  b.a.freq_dtype = (uint32_t)rope->freq_dtype;
   b.a.rope_dim = rope->rope_dim;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.weight_offset = to_dtype(dtype, weight_offset);
@@ -349,7 +349,7 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
                   int32_t multiply_before_cast, const uint32_t* input_row_offsets,
                   uint32_t batch_size, const qrp_rope* rope, uint32_t layer_idx, void* stream) {
   g_err.clear();
-  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32 or QRP_BF16");
+  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
   if (!main_band || !index_band || !main_band->cache || !index_band->cache)
     return fail(QRP_EINVAL, "bands and their caches must be non-NULL");
   if (main_band->cache->dtype != index_band->cache->dtype ||
@@ -379,7 +379,7 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
   b.a.freqs = rope->freqs_cis;
-  b.a.freq_bf16 = rope->freq_dtype == QRP_BF16;
+  b.a.freq_dtype = (uint32_t)rope->freq_dtype;
   b.a.rope_dim = rope->rope_dim;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.weight_offset = to_dtype(dtype, weight_offset);
@@ -395,7 +395,7 @@ int32_t kv_cache_radd(const void* a, int32_t dtype, uint32_t total_rows, uint64_
                       const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t batch_offset,
                       const qrp_paged_cache* cache, uint32_t layer_idx, void* stream) {
   g_err.clear();
-  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32 or QRP_BF16");
+  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
   if (total_rows == 0) return QRP_OK;
   int32_t st;
   if ((st = check_batch(input_row_offsets, total_rows, batch_size))) return st;
@@ -424,6 +424,55 @@ int32_t kv_cache_radd(const void* a, int32_t dtype, uint32_t total_rows, uint64_
             0.f, (uint32_t)Hk, 0, 1);
   if ((st = b.finish(total_rows, true))) return st;
   return launch(b, true, true, stream);
+}
+
+int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, uint32_t batch_size,
+                                            uint32_t seq_len, uint32_t n_q_heads,
+                                            const uint32_t* valid_lengths, const qrp_rope* rope,
+                                            const qrp_paged_cache* cache, uint32_t layer_idx,
+                                            void* output, void* stream) {
+  g_err.clear();
+  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
+  if (batch_size == 0 || seq_len == 0) return QRP_OK;
+  int32_t st;
+  if ((st = check_cache(cache, dtype, layer_idx, "cache"))) return st;
+  if ((st = check_rope(rope, dtype, cache->head_dim))) return st;
+  if (!q_proj || !output || !valid_lengths)
+    return fail(QRP_EINVAL, "q_proj / output / valid_lengths is NULL");
+  if (n_q_heads == 0) return fail(QRP_EINVAL, "n_q_heads is 0");
+  if (!aligned16(q_proj) || !aligned16(output))
+    return fail(QRP_EALIGN, "q_proj / output not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(valid_lengths) & 3u)
+    return fail(QRP_EALIGN, "valid_lengths not 4-byte aligned");
+  if (batch_size > cache->cache_batch) return fail(QRP_EINVAL, "batch_size > cache_batch");
+  const uint64_t tokens = (uint64_t)batch_size * seq_len;
+  if (tokens >= (1ull << 31)) return fail(QRP_EINVAL, "batch_size * seq_len too large for one launch");
+  const uint64_t row = (uint64_t)n_q_heads * cache->head_dim;
+
+  Builder b;
+  b.dtype = dtype;
+  b.head_dim = cache->head_dim;
+  b.rpp = qrp::rows_per_pass(dtype, cache->head_dim);
+  b.a.cache[0] = make_cache(cache, layer_idx);
+  b.a.ncache = 1;
+  b.a.offsets = nullptr;
+  b.a.batch = batch_size;
+  b.a.batch_offset = 0;
+  b.a.valid_lengths = valid_lengths;
+  b.a.seq_len = seq_len;
+  b.a.freqs = rope->freqs_cis;
+  b.a.freq_dtype = (uint32_t)rope->freq_dtype;
+  b.a.rope_dim = rope->rope_dim;
+  b.a.max_seq_len = rope->max_seq_len;
+  b.a.multiply_before_cast = 1;
+  b.add_seg(qrp::SEG_Q, q_proj, (int64_t)row, output, (int64_t)row, nullptr, 0.f, n_q_heads, 0, 0);
+  b.add_seg(qrp::SEG_K_INPLACE, nullptr, 0, nullptr, 0, nullptr, 0.f, cache->num_kv_heads, 0, 0);
+  if ((st = b.finish((uint32_t)tokens, false))) return st;
+  const int e = qrp::launch_bshd(b.a, dtype, b.head_dim, rope->interleaved != 0, stream);
+  if (e != 0)
+    return fail(QRP_EHIP, std::string("kernel launch failed: ") +
+                               hipGetErrorString(static_cast<hipError_t>(e)));
+  return QRP_OK;
 }
 
 int32_t qrp_validate_host(const uint32_t* off, uint32_t B, uint32_t T, uint32_t batch_offset,

@@ -87,7 +87,7 @@ struct BandArgs {
   SegDesc seg[kMaxSegs];
   CacheDesc cache[kMaxCaches];
   const uint32_t* offsets;  // [batch + 1]
-  const void* freqs;        // [max_seq_len][rope_dim], binary32 or bf16 entries
+  const void* freqs;        // [max_seq_len][rope_dim] of freq_dtype
   uint32_t nseg;
   uint32_t ncache;
   uint32_t batch;
@@ -105,7 +105,12 @@ struct BandArgs {
   uint32_t waves_per_block; // 1 .. kMaxWavesPerBlock
   uint32_t per_xcd;         // blocks per XCD after the XCD-contiguous remap (0: no remap)
   uint64_t guess_mul;       // floor(batch * 2^32 / total_tokens): token -> first sequence guess
-  uint32_t freq_bf16;       // freqs entries are bf16 (else binary32)
+  uint32_t freq_dtype;      // DT_F32, DT_BF16 or DT_F16 table entries
+  // Padded [batch][seq_len] token grid (continuous batching): token t is
+  // row t % seq_len of sequence t / seq_len; rows at or past the sequence's
+  // valid length pass through.  Unused by the ragged ops.
+  const uint32_t* valid_lengths;
+  uint32_t seq_len;
 };
 
 enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
@@ -117,6 +122,10 @@ inline uint32_t max_passes(bool radd, bool norm) {
 
 // Launch the band engine; returns 0 or a hipError_t value.
 int launch_band(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interleaved, bool radd,
+                void* stream);
+
+// Launch the padded-grid (BSHD) variant: Q segments and in-place K only.
+int launch_bshd(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interleaved,
                 void* stream);
 
 // Rows handled per 64-lane pass for a dtype / head_dim.

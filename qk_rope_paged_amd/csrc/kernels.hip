@@ -225,10 +225,10 @@ __device__ __forceinline__ uint32_t seg_of(const BandArgs& a, uint32_t kp) {
   return s;
 }
 
-// N consecutive freqs table entries (binary32 or bf16) as binary32.
-template <bool FB16, int N>
+// N consecutive freqs table entries of type FDT, widened (exactly) to binary32.
+template <int FDT, int N>
 __device__ __forceinline__ void table_entries(const void* base, int64_t idx, float* out) {
-  if constexpr (!FB16) {
+  if constexpr (FDT == DT_F32) {
     const float* p = static_cast<const float*>(base) + idx;
 #pragma unroll
     for (int q = 0; q < N / 4; ++q) {
@@ -238,48 +238,72 @@ __device__ __forceinline__ void table_entries(const void* base, int64_t idx, flo
       out[4 * q + 2] = __uint_as_float(v.z);
       out[4 * q + 3] = __uint_as_float(v.w);
     }
-  } else if constexpr (N == 4) {
-    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
-    out[0] = __uint_as_float(v.x << 16);
-    out[1] = __uint_as_float(v.x & 0xFFFF0000u);
-    out[2] = __uint_as_float(v.y << 16);
-    out[3] = __uint_as_float(v.y & 0xFFFF0000u);
   } else {
     const uint16_t* p = static_cast<const uint16_t*>(base) + idx;
+    uint32_t w[N / 2];
+    if constexpr (N == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
 #pragma unroll
-    for (int q = 0; q < N / 8; ++q) {
-      const uint4 v = ld16(p + 8 * q);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int q = 0; q < N / 8; ++q) {
+        const uint4 v = ld16(p + 8 * q);
+        w[4 * q] = v.x;
+        w[4 * q + 1] = v.y;
+        w[4 * q + 2] = v.z;
+        w[4 * q + 3] = v.w;
+      }
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        out[8 * q + 2 * i] = __uint_as_float(w[i] << 16);
-        out[8 * q + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    for (int i = 0; i < N / 2; ++i) {
+      if constexpr (FDT == DT_BF16) {
+        out[2 * i] = __uint_as_float(w[i] << 16);
+        out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      } else {
+        const h2v h = __builtin_bit_cast(h2v, w[i]);
+        out[2 * i] = (float)h.x;
+        out[2 * i + 1] = (float)h.y;
       }
     }
   }
 }
 
-// This lane's (cos, sin) entries of freqs row `pos`: the 2E table values of
-// the frequencies its chunks rotate (zero where a chunk is not rotated).
-template <typename T, bool IL, bool FB16>
-__device__ __forceinline__ void load_freqs(const void* __restrict__ freqs, uint32_t rope_dim,
-                                           uint32_t pos, uint32_t c0, uint32_t c1, uint32_t j,
-                                           bool rot0, bool rot1, float* fl) {
+template <int FDT, typename T, bool IL>
+__device__ __forceinline__ void load_freqs_t(const void* __restrict__ freqs, int64_t row,
+                                             uint32_t c0, uint32_t c1, uint32_t j, bool rot0,
+                                             bool rot1, float* fl) {
   constexpr int E = Fmt<T>::E;
-#pragma unroll
-  for (int e = 0; e < 2 * E; ++e) fl[e] = 0.f;
-  const int64_t row = (int64_t)pos * rope_dim;
   if constexpr (IL) {
     // chunk c holds pairs c*E/2 .. c*E/2 + E/2 - 1: table columns c*E .. c*E + E - 1
-    if (rot0) table_entries<FB16, E>(freqs, row + c0 * E, fl);
-    if (rot1) table_entries<FB16, E>(freqs, row + c1 * E, fl + E);
+    if (rot0) table_entries<FDT, E>(freqs, row + c0 * E, fl);
+    if (rot1) table_entries<FDT, E>(freqs, row + c1 * E, fl + E);
   } else {
     // a half-split lane j < rope_dim/(2E) rotates frequencies j*E .. j*E + E - 1
-    if (rot0) table_entries<FB16, 2 * E>(freqs, row + 2 * j * E, fl);
+    if (rot0) table_entries<FDT, 2 * E>(freqs, row + 2 * j * E, fl);
   }
 }
 
-template <typename T, int D, bool IL, int NPMAX, bool RADD, bool NORM, bool FB16>
+// This lane's (cos, sin) entries of freqs row `pos`: the 2E table values of
+// the frequencies its chunks rotate (zero where a chunk is not rotated).
+// The table's entry type is uniform over the launch.
+template <typename T, bool IL>
+__device__ __forceinline__ void load_freqs(const BandArgs& a, uint32_t pos, uint32_t c0,
+                                           uint32_t c1, uint32_t j, bool rot0, bool rot1,
+                                           float* fl) {
+  constexpr int E = Fmt<T>::E;
+#pragma unroll
+  for (int e = 0; e < 2 * E; ++e) fl[e] = 0.f;
+  const int64_t row = (int64_t)pos * a.rope_dim;
+  if (a.freq_dtype == DT_F32)
+    load_freqs_t<DT_F32, T, IL>(a.freqs, row, c0, c1, j, rot0, rot1, fl);
+  else if (a.freq_dtype == DT_BF16)
+    load_freqs_t<DT_BF16, T, IL>(a.freqs, row, c0, c1, j, rot0, rot1, fl);
+  else
+    load_freqs_t<DT_F16, T, IL>(a.freqs, row, c0, c1, j, rot0, rot1, fl);
+}
+
+template <typename T, int D, bool IL, int NPMAX, bool RADD, bool NORM, bool BSHD>
 __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   constexpr int E = Fmt<T>::E;
   constexpr int CH = D / E;      // 16-byte chunks per head row
@@ -322,8 +346,8 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   const uint32_t c0 = j < hh ? j : hh + j;
   const uint32_t c1 = j < hh ? j + hh : j + LPR;
   const uint32_t rot_chunks = a.rope_dim / E;
-  const bool rot0 = !RADD && (IL ? c0 < rot_chunks : j < hh);
-  const bool rot1 = !RADD && (IL ? c1 < rot_chunks : j < hh);
+  bool rot0 = !RADD && (IL ? c0 < rot_chunks : j < hh);
+  bool rot1 = !RADD && (IL ? c1 < rot_chunks : j < hh);
 
   uint4 x[NPMAX][2];
   uint4 y[RADD ? NPMAX : 1][2];
@@ -348,7 +372,15 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   // ---- B: token -> sequence -> position -> page (wave-uniform) ----
   uint32_t start, end, b;
   uint32_t clen[kMaxCaches] = {0, 0};
-  if (a.batch < kSmallBatch) {
+  bool pass = false;  // padded grid: a row past its sequence's valid length
+  if constexpr (BSHD) {
+    b = t / a.seq_len;
+    start = b * a.seq_len;
+    end = start + a.seq_len;
+    const uint32_t vl = a.valid_lengths[b];
+    clen[0] = a.cache[0].cache_lengths[b];
+    pass = t - start >= vl;
+  } else if (a.batch < kSmallBatch) {
     // Small batch: every offset and every sequence's cache length in one
     // round of independent scalar loads (indices clamped in range), then a
     // scan -- one load latency before the page-table lookup.
@@ -411,15 +443,16 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       const uint64_t pidx = cd.page_shift != 0xFFFFFFFFu ? (p64 >> cd.page_shift)
                                                          : p64 / cd.page_size;
       const uint64_t slot = p64 - pidx * cd.page_size;
-      ok = ok && (a.max_seq_len == 0 || p64 < a.max_seq_len) && pidx < cd.max_pages;
+      ok = ok && (pass || ((a.max_seq_len == 0 || p64 < a.max_seq_len) && pidx < cd.max_pages));
       uint64_t page = 0;
-      if (ok) page = cd.table[(uint64_t)cseq * cd.max_pages + pidx];
-      ok = ok && page < cd.num_pages;
+      if (ok && !pass) page = cd.table[(uint64_t)cseq * cd.max_pages + pidx];
+      ok = ok && (pass || page < cd.num_pages);
       pos[ci] = (uint32_t)p64;
       base[ci] = (int64_t)page * cd.page_stride + cd.layer_off + (int64_t)slot * cd.slot_stride;
     }
   }
   if (!ok) return;  // out-of-range metadata: this token writes nothing
+  if (pass) rot0 = rot1 = false;  // a passed-through row is copied as it is
 
   // ---- C: loads from the cache (in-place K, radd accumulator) ----
 #pragma unroll
@@ -428,7 +461,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
     if ((uint32_t)p < np) {
       const uint32_t kp = p0 + p;
       const SegDesc& sd = a.seg[seg_of(a, kp)];
-      if (sd.kind == SEG_K_INPLACE || (RADD && sd.kind == SEG_RADD)) {
+      if ((sd.kind == SEG_K_INPLACE && !pass) || (RADD && sd.kind == SEG_RADD)) {
         const CacheDesc& cd = a.cache[sd.cache];
         const uint32_t h = min((kp - sd.pass_begin) * RPP + row, sd.n_heads - 1);
         const T* src = reinterpret_cast<const T*>(cd.blocks) + base[sd.cache] +
@@ -447,7 +480,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   // ---- D: this lane's (cos, sin) entries of the token's freqs row ----
   float fl[RADD ? 1 : 2 * E];
   uint32_t fl_pos = pos[0];
-  if constexpr (!RADD) load_freqs<T, IL, FB16>(a.freqs, a.rope_dim, fl_pos, c0, c1, j, rot0, rot1, fl);
+  if constexpr (!RADD) load_freqs<T, IL>(a, fl_pos, c0, c1, j, rot0, rot1, fl);
 
 
   // ---- E: arithmetic and stores ----
@@ -459,7 +492,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       const SegDesc& sd = a.seg[si];
       const uint32_t kind = sd.kind;
       const uint32_t h = (kp - sd.pass_begin) * RPP + row;
-      const bool active = h < sd.n_heads;
+      const bool active = h < sd.n_heads && !(BSHD && pass && kind != SEG_Q);
       T* dst;
       if (kind == SEG_Q) {
         dst = reinterpret_cast<T*>(sd.dst) + (int64_t)t * sd.dst_row_stride + (int64_t)h * D;
@@ -521,7 +554,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
           // own position (uniform, taken at most once per wave).
           if (pos[sd.cache] != fl_pos) {
             fl_pos = pos[sd.cache];
-            load_freqs<T, IL, FB16>(a.freqs, a.rope_dim, fl_pos, c0, c1, j, rot0, rot1, fl);
+            load_freqs<T, IL>(a, fl_pos, c0, c1, j, rot0, rot1, fl);
           }
           if constexpr (IL) {
 #pragma unroll
@@ -556,40 +589,40 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   }
 }
 
-template <typename T, int D, bool IL, bool RADD, bool NORM, bool FB16>
+template <typename T, int D, bool IL, bool RADD, bool NORM, bool BSHD>
 int launch_t(const BandArgs& a, void* stream) {
   constexpr int NPMAX = RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : kMaxPassesStore);
   const uint32_t grid = a.per_xcd ? a.per_xcd * kXcds : a.n_blocks;
-  hipLaunchKernelGGL((band_kernel<T, D, IL, NPMAX, RADD, NORM, FB16>), dim3(grid),
+  hipLaunchKernelGGL((band_kernel<T, D, IL, NPMAX, RADD, NORM, BSHD>), dim3(grid),
                      dim3(64 * a.waves_per_block), 0, reinterpret_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
-template <typename T, bool IL, bool RADD, bool NORM, bool FB16>
+template <typename T, bool IL, bool RADD, bool NORM, bool BSHD>
 int launch_d(const BandArgs& a, uint32_t head_dim, void* stream) {
   switch (head_dim) {
-    case 64: return launch_t<T, 64, IL, RADD, NORM, FB16>(a, stream);
-    case 128: return launch_t<T, 128, IL, RADD, NORM, FB16>(a, stream);
-    case 256: return launch_t<T, 256, IL, RADD, NORM, FB16>(a, stream);
+    case 64: return launch_t<T, 64, IL, RADD, NORM, BSHD>(a, stream);
+    case 128: return launch_t<T, 128, IL, RADD, NORM, BSHD>(a, stream);
+    case 256: return launch_t<T, 256, IL, RADD, NORM, BSHD>(a, stream);
     default: return (int)hipErrorInvalidValue;
   }
-}
-
-template <typename T, bool FB16>
-int launch_f(const BandArgs& a, uint32_t head_dim, bool interleaved, bool norm, void* stream) {
-  if (norm)
-    return interleaved ? launch_d<T, true, false, true, FB16>(a, head_dim, stream)
-                       : launch_d<T, false, false, true, FB16>(a, head_dim, stream);
-  return interleaved ? launch_d<T, true, false, false, FB16>(a, head_dim, stream)
-                     : launch_d<T, false, false, false, FB16>(a, head_dim, stream);
 }
 
 template <typename T>
 int launch_dt(const BandArgs& a, uint32_t head_dim, bool interleaved, bool radd, bool norm,
               void* stream) {
   if (radd) return launch_d<T, true, true, false, false>(a, head_dim, stream);
-  return a.freq_bf16 ? launch_f<T, true>(a, head_dim, interleaved, norm, stream)
-                     : launch_f<T, false>(a, head_dim, interleaved, norm, stream);
+  if (norm)
+    return interleaved ? launch_d<T, true, false, true, false>(a, head_dim, stream)
+                       : launch_d<T, false, false, true, false>(a, head_dim, stream);
+  return interleaved ? launch_d<T, true, false, false, false>(a, head_dim, stream)
+                     : launch_d<T, false, false, false, false>(a, head_dim, stream);
+}
+
+template <typename T>
+int launch_bshd_t(const BandArgs& a, uint32_t head_dim, bool interleaved, void* stream) {
+  return interleaved ? launch_d<T, true, false, false, true>(a, head_dim, stream)
+                     : launch_d<T, false, false, false, true>(a, head_dim, stream);
 }
 
 }  // namespace
@@ -601,6 +634,13 @@ int launch_band(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interl
   if (dtype == DT_F32) return launch_dt<float>(a, head_dim, interleaved, radd, norm, stream);
   if (dtype == DT_F16) return launch_dt<F16>(a, head_dim, interleaved, radd, norm, stream);
   return launch_dt<Bf16>(a, head_dim, interleaved, radd, norm, stream);
+}
+
+int launch_bshd(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interleaved,
+                void* stream) {
+  if (dtype == DT_F32) return launch_bshd_t<float>(a, head_dim, interleaved, stream);
+  if (dtype == DT_F16) return launch_bshd_t<F16>(a, head_dim, interleaved, stream);
+  return launch_bshd_t<Bf16>(a, head_dim, interleaved, stream);
 }
 
 }  // namespace qrp

@@ -86,6 +86,7 @@ class DeviceCase:
     caches: List[DeviceCache]
     q_out: List[torch.Tensor] = field(default_factory=list)      # with guard rows
     gammas: list = field(default_factory=list)
+    valid: torch.Tensor = None                                    # bshd: valid lengths
 
     def q_out_rows(self, i: int) -> torch.Tensor:
         return self.q_out[i][GUARD:GUARD + self.case.T]
@@ -102,12 +103,19 @@ def upload(case: sc.Case, device="cuda") -> DeviceCase:
         hi = (np.ascontiguousarray(case.freqs, np.float32).view(np.uint32) >> 16).astype(np.uint16)
         assert np.array_equal(hi.astype(np.uint32) << 16, case.freqs.view(np.uint32))
         freqs = bits_tensor(hi, device)
+    elif case.freq_dtype == sc.F16:
+        # binary16 values held in float32: the conversion back is exact
+        h = np.ascontiguousarray(case.freqs, np.float32).astype(np.float16)
+        assert np.array_equal(h.astype(np.float32), case.freqs)
+        freqs = bits_tensor(h.view(np.uint16), device)
     else:
         freqs = torch.from_numpy(np.ascontiguousarray(case.freqs)).to(device)
     dc = DeviceCase(case=case, buf=buf, offsets=off, freqs=freqs,
                     caches=[upload_cache(c, device) for c in case.caches])
-    strides = ([case.q_out_row_stride] if case.op == "store"
+    strides = ([case.q_out_row_stride] if case.op in ("store", "bshd")
                else [b.q_out_row_stride for b in case.bands])
+    if case.op == "bshd":
+        dc.valid = torch.from_numpy(np.asarray(case.lengths, np.uint32).view(np.int32)).to(device)
     for s in strides:
         dc.q_out.append(torch.full((case.T + 2 * GUARD, max(s, 1)), sentinel_int(case.dtype),
                                    dtype=TORCH_BITS[case.dtype], device=device))
@@ -154,4 +162,8 @@ def run(dc: DeviceCase, stream=None, raise_on_error=True, op=None, prepare=False
         return qrp.kv_cache_radd(
             dc.buf, dt, c.T, c.row_stride, dc.offsets, c.batch, c.batch_offset,
             dc.caches[0].desc, c.layer_idx, **kw)
+    if op == "bshd":
+        return qrp.fused_qk_rope_bshd_continuous_batch(
+            dc.buf, dt, c.batch, c.seq_len, c.n_q_heads, dc.valid, rope_of(dc),
+            dc.caches[0].desc, c.layer_idx, dc.q_out_rows(0), **kw)
     raise ValueError(op)

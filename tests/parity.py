@@ -69,6 +69,8 @@ def bands_of(case):
     """(q_out index, cache index, n_q_heads, q normed, k normed, has V) per band."""
     if case.op == "store":
         return [(0, 0, case.n_q_heads, False, False, True)]
+    if case.op == "bshd":
+        return [(0, 0, case.n_q_heads, False, False, False)]
     if case.op in ("norm", "dual"):
         return [(i, b.cache, b.n_q_heads, b.q_gamma is not None, b.k_gamma is not None,
                  b.v_col >= 0) for i, b in enumerate(case.bands)]
@@ -97,6 +99,12 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
         ora = res.q_out[qi]
         stride = ora.shape[1]
         assert np.array_equal(rows[:, Hq * D:stride], ora[:, Hq * D:]), "q_output padding written"
+        if case.op == "bshd" and T:
+            # rows at or past a sequence's valid length: the input row, bit for bit
+            S = case.seq_len
+            pad = (np.arange(T) % S) >= np.repeat(np.asarray(case.lengths, np.int64), S)
+            assert np.array_equal(rows[pad], case.buf[pad]), "a padded row is not the input row"
+            rep["q_passed_rows"] = int(pad.sum())
         if Hq and T:
             tr = res.traces[qi]
             check_rows(rows[:, :Hq * D].reshape(-1, D), ora[:, :Hq * D].reshape(-1, D),
@@ -118,10 +126,11 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
                 continue
             tr = res.traces[qi]
             koff = tr["k_row_off"].reshape(-1)
-            idx = koff[:, None] + np.arange(D)[None, :]
-            check_rows(g_flat[idx], o_flat[idx], tr["k_exact"].reshape(-1, D),
-                       tr["k_mag"].reshape(-1, D), _copy_cols(D, case.rope_dim, kn), dt, ulps,
-                       f"k{qi}", rep)
+            live = koff >= 0                       # rows the op wrote (bshd: real rows only)
+            idx = koff[live][:, None] + np.arange(D)[None, :]
+            check_rows(g_flat[idx], o_flat[idx], tr["k_exact"].reshape(-1, D)[live],
+                       tr["k_mag"].reshape(-1, D)[live], _copy_cols(D, case.rope_dim, kn), dt,
+                       ulps, f"k{qi}", rep)
             # written K rows are checked: blank them before the bitwise comparison
             g_flat[idx] = 0
             o_flat[idx] = 0

@@ -99,7 +99,7 @@ def _store(cache=None, rope=None, **kw):
     (dict(rope=_rope(rope_dim=8)), qrp.QRP_EUNSUPPORTED),
     (dict(rope=_rope(max_seq_len=0)), qrp.QRP_EINVAL),
     (dict(rope=_rope(freqs_cis=None)), qrp.QRP_EINVAL),
-    (dict(rope=_rope(freq_dtype=qrp.QRP_F16)), qrp.QRP_EUNSUPPORTED),
+    (dict(rope=_rope(freq_dtype=3)), qrp.QRP_EUNSUPPORTED),
     (dict(rope=_rope(freq_dtype=9)), qrp.QRP_EUNSUPPORTED),
     (dict(rope=_rope(freqs_cis=FAKE + 8, freq_dtype=qrp.QRP_BF16)), qrp.QRP_EALIGN),
     (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_F16), qrp.QRP_EUNSUPPORTED),   # cache is bf16
@@ -234,3 +234,40 @@ def test_validate_page_index_and_batch_offset_bounds():
     assert "max_pages_per_seq" in qrp.last_error()
     off, lens, tab = _meta()
     assert _validate(off, lens, tab, boff=2) == qrp.QRP_EDATA   # 2 + 3 > 4 sequences
+
+
+def _bshd(cache=None, rope=None, **kw):
+    a = dict(q_proj=FAKE, dtype=qrp.QRP_BF16, batch_size=2, seq_len=16, n_q_heads=32,
+             valid_lengths=FAKE, rope=rope or _rope(), cache=cache or _cache(), layer_idx=1,
+             output=FAKE + 4096, stream=0, raise_on_error=False)
+    a.update(kw)
+    return qrp.fused_qk_rope_bshd_continuous_batch(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), qrp.QRP_EUNSUPPORTED),
+    (dict(q_proj=None), qrp.QRP_EINVAL),
+    (dict(output=None), qrp.QRP_EINVAL),
+    (dict(valid_lengths=None), qrp.QRP_EINVAL),
+    (dict(n_q_heads=0), qrp.QRP_EINVAL),
+    (dict(q_proj=FAKE + 8), qrp.QRP_EALIGN),
+    (dict(output=FAKE + 2), qrp.QRP_EALIGN),
+    (dict(valid_lengths=FAKE + 2), qrp.QRP_EALIGN),
+    (dict(batch_size=5), qrp.QRP_EINVAL),
+    (dict(batch_size=4, seq_len=1 << 30), qrp.QRP_EINVAL),
+    (dict(layer_idx=2), qrp.QRP_EINVAL),
+    (dict(cache=_cache(dtype=qrp.QRP_F16)), qrp.QRP_EUNSUPPORTED),
+    (dict(cache=_cache(head_dim=80)), qrp.QRP_EUNSUPPORTED),
+    (dict(rope=_rope(rope_dim=130)), qrp.QRP_EINVAL),
+    (dict(rope=_rope(freq_dtype=4)), qrp.QRP_EUNSUPPORTED),
+    (dict(rope=_rope(max_seq_len=0)), qrp.QRP_EINVAL),
+])
+def test_bshd_argument_errors(kw, code):
+    assert _bshd(**kw) == code
+    assert qrp.last_error() != ""
+
+
+def test_bshd_empty_grid_returns_ok_without_touching_anything():
+    assert _bshd(batch_size=0, q_proj=None, output=None, valid_lengths=None) == qrp.QRP_OK
+    assert _bshd(seq_len=0, q_proj=None, output=None, valid_lengths=None) == qrp.QRP_OK
+
