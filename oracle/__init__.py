@@ -27,10 +27,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 SRC = os.path.join(HERE, "qrp_oracle.c")
 
-ORC_F32, ORC_BF16, ORC_F16 = 0, 1, 2
-_DT = {"f32": ORC_F32, "bf16": ORC_BF16, "f16": ORC_F16}
-_SENT = {"f32": np.uint32(0x7FBADBAD), "bf16": np.uint16(0x7FBA), "f16": np.uint16(0x7DBA)}
-_BITS = {"f32": np.uint32, "bf16": np.uint16, "f16": np.uint16}
+ORC_F32, ORC_BF16, ORC_F16, ORC_FP8 = 0, 1, 2, 3
+_DT = {"f32": ORC_F32, "bf16": ORC_BF16, "f16": ORC_F16, "fp8": ORC_FP8}
+_SENT = {"f32": np.uint32(0x7FBADBAD), "bf16": np.uint16(0x7FBA), "f16": np.uint16(0x7DBA),
+         "fp8": np.uint8(0x7F)}
+_BITS = {"f32": np.uint32, "bf16": np.uint16, "f16": np.uint16, "fp8": np.uint8}
 NO_PAGE = 0xFFFFFFFF
 
 
@@ -51,13 +52,18 @@ class OrcCache(ctypes.Structure):
                 ("layer_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
                 ("head_stride", ctypes.c_int64),
                 ("cache_lengths", ctypes.c_void_p), ("lookup_table", ctypes.c_void_p),
-                ("cache_batch", ctypes.c_uint32), ("max_pages_per_seq", ctypes.c_uint32)]
+                ("cache_batch", ctypes.c_uint32), ("max_pages_per_seq", ctypes.c_uint32),
+                ("scales", ctypes.c_void_p), ("scale_dtype", ctypes.c_int32),
+                ("s_page_stride", ctypes.c_int64), ("s_plane_stride", ctypes.c_int64),
+                ("s_layer_stride", ctypes.c_int64), ("s_slot_stride", ctypes.c_int64),
+                ("s_head_stride", ctypes.c_int64)]
 
 
 class OrcTrace(ctypes.Structure):
     _fields_ = [("q_exact", ctypes.c_void_p), ("q_mag", ctypes.c_void_p),
                 ("k_exact", ctypes.c_void_p), ("k_mag", ctypes.c_void_p),
-                ("k_row_off", ctypes.c_void_p), ("v_row_off", ctypes.c_void_p)]
+                ("k_row_off", ctypes.c_void_p), ("v_row_off", ctypes.c_void_p),
+                ("k_scale_off", ctypes.c_void_p), ("v_scale_off", ctypes.c_void_p)]
 
 
 class OrcBand(ctypes.Structure):
@@ -88,8 +94,12 @@ def load() -> ctypes.CDLL:
     lib.orc_round_f16.restype = ctypes.c_uint16
     lib.orc_f16_to_double.argtypes = [ctypes.c_uint16]
     lib.orc_f16_to_double.restype = ctypes.c_double
+    lib.orc_round_e4m3.argtypes = [ctypes.c_double]
+    lib.orc_round_e4m3.restype = ctypes.c_uint8
+    lib.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_to_double.restype = ctypes.c_double
     lib.orc_rope_split_store_paged.argtypes = [P, I32, U32, U64, U32, P, U32, P, U32, U32, I32,
-                                               ctypes.POINTER(OrcCache), U32, P, U64,
+                                               ctypes.POINTER(OrcCache), U32, P, I32, U64,
                                                ctypes.POINTER(OrcTrace)]
     lib.orc_rope_split_store_paged.restype = I32
     lib.orc_qk_rmsnorm_rope_paged.argtypes = [P, I32, U32, U64, ctypes.POINTER(OrcBand), F, I32,
@@ -101,7 +111,7 @@ def load() -> ctypes.CDLL:
                                   ctypes.POINTER(OrcTrace), ctypes.POINTER(OrcTrace)]
     lib.orc_dual_band.restype = I32
     lib.orc_kv_cache_radd.argtypes = [P, I32, U32, U64, P, U32, U32, ctypes.POINTER(OrcCache),
-                                      U32, P, P]
+                                      U32, ctypes.POINTER(OrcTrace)]
     lib.orc_kv_cache_radd.restype = I32
     lib.orc_fused_qk_rope_bshd.argtypes = [P, I32, U32, U32, U32, P, P, U32, U32, I32,
                                            ctypes.POINTER(OrcCache), U32, P,
@@ -131,12 +141,21 @@ def f16_to_double(h: int) -> float:
     return float(load().orc_f16_to_double(int(h)))
 
 
+def round_e4m3(x: float) -> int:
+    return int(load().orc_round_e4m3(float(x)))
+
+
+def e4m3_to_double(q: int) -> float:
+    return float(load().orc_e4m3_to_double(int(q)))
+
+
 @dataclass
 class OracleResult:
     status: int
     seconds: float = 0.0                                       # wall time of the C call
     q_out: List[np.ndarray] = field(default_factory=list)     # per band, raw bits
     pools: List[np.ndarray] = field(default_factory=list)     # per cache, after the op
+    scales: List[Optional[np.ndarray]] = field(default_factory=list)   # per FP8 cache, after
     page_maps: List[Optional[np.ndarray]] = field(default_factory=list)
     traces: List[dict] = field(default_factory=list)          # per band
 
@@ -161,12 +180,17 @@ def touched_pages(case, ci: int) -> np.ndarray:
     return np.unique(pages)
 
 
-def _orc_cache(cache, pool: np.ndarray, table: np.ndarray, num_pages: int, keep: list) -> OrcCache:
+def _orc_cache(cache, pool: np.ndarray, table: np.ndarray, num_pages: int, keep: list,
+               scales: Optional[np.ndarray] = None) -> OrcCache:
     st = cache.strides
     lens = np.ascontiguousarray(cache.cache_lengths, dtype=np.uint32)
     table = np.ascontiguousarray(table, dtype=np.uint32)
-    keep += [lens, table, pool]
-    return OrcCache(pool=_ptr(pool), dtype=_DT[cache.dtype], num_kv_heads=cache.num_kv_heads,
+    keep += [lens, table, pool, scales]
+    sst = cache.scale_strides if scales is not None else dict(
+        s_page_stride=0, s_plane_stride=0, s_layer_stride=0, s_slot_stride=0, s_head_stride=0)
+    return OrcCache(scales=_ptr(scales),
+                    scale_dtype=_DT[cache.scale_dtype] if scales is not None else 0, **sst,
+                    pool=_ptr(pool), dtype=_DT[cache.dtype], num_kv_heads=cache.num_kv_heads,
                     head_dim=cache.head_dim, page_size=cache.page_size,
                     kv_planes=cache.kv_planes, num_layers=cache.num_layers, num_pages=num_pages,
                     page_stride=st["page_stride"], plane_stride=st["plane_stride"],
@@ -180,7 +204,9 @@ def _trace(T: int, Hq: int, Hk: int, D: int, keep: list) -> tuple:
     tr = dict(q_exact=np.zeros((T, Hq, D)), q_mag=np.zeros((T, Hq, D)),
               k_exact=np.zeros((T, Hk, D)), k_mag=np.zeros((T, Hk, D)),
               k_row_off=np.full((T, Hk), -1, dtype=np.int64),
-              v_row_off=np.full((T, Hk), -1, dtype=np.int64))
+              v_row_off=np.full((T, Hk), -1, dtype=np.int64),
+              k_scale_off=np.full((T, Hk), -1, dtype=np.int64),
+              v_scale_off=np.full((T, Hk), -1, dtype=np.int64))
     keep.append(tr)
     return tr, OrcTrace(**{k: _ptr(v) for k, v in tr.items()})
 
@@ -207,26 +233,30 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
             ctab = np.full(tab.shape, NO_PAGE, dtype=np.uint64)
             ctab[valid] = remap[tab[valid]]
             pool = cache.materialize(pages)
+            scl = cache.materialize_scales(pages)
             res.page_maps.append(pages)
-            oc = _orc_cache(cache, pool, ctab.astype(np.uint32), len(pages), keep)
+            oc = _orc_cache(cache, pool, ctab.astype(np.uint32), len(pages), keep, scl)
         else:
             pool = cache.materialize()
+            scl = cache.materialize_scales()
             res.page_maps.append(None)
-            oc = _orc_cache(cache, pool, cache.lookup_table, cache.num_pages, keep)
+            oc = _orc_cache(cache, pool, cache.lookup_table, cache.num_pages, keep, scl)
         res.pools.append(pool)
+        res.scales.append(scl)
         ocaches.append(oc)
     keep.append(ocaches)
 
     if case.op == "store":
         cache = case.caches[0]
         D, Hk, Hq = cache.head_dim, cache.num_kv_heads, case.n_q_heads
-        q_out = np.full((T, case.q_out_row_stride), _SENT[case.dtype], dtype=_BITS[case.dtype])
+        qdt = case.q_dtype
+        q_out = np.full((T, case.q_out_row_stride), _SENT[qdt], dtype=_BITS[qdt])
         tr, otr = _trace(T, Hq, Hk, D, keep) if trace else (None, None)
         t0 = time.perf_counter()
         st = lib.orc_rope_split_store_paged(
             _ptr(buf), dt, T, case.row_stride, Hq, _ptr(off), case.batch, _ptr(freqs),
             case.max_seq_len, case.rope_dim, int(case.interleaved), ctypes.byref(ocaches[0]),
-            case.layer_idx, _ptr(q_out), case.q_out_row_stride,
+            case.layer_idx, _ptr(q_out), _DT[qdt], case.q_out_row_stride,
             ctypes.byref(otr) if otr is not None else None)
         res.q_out.append(q_out)
         res.traces.append(tr)
@@ -269,13 +299,15 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
     elif case.op == "radd":
         cache = case.caches[0]
         Hk = cache.num_kv_heads
-        krow = np.full((T, Hk), -1, dtype=np.int64)
-        vrow = np.full((T, Hk), -1, dtype=np.int64)
+        tr = {k: np.full((T, Hk), -1, dtype=np.int64)
+              for k in ("k_row_off", "v_row_off", "k_scale_off", "v_scale_off")}
+        keep.append(tr)
+        otr = OrcTrace(**{k: _ptr(v) for k, v in tr.items()})
         t0 = time.perf_counter()
         st = lib.orc_kv_cache_radd(_ptr(buf), dt, T, case.row_stride, _ptr(off), case.batch,
                                    case.batch_offset, ctypes.byref(ocaches[0]), case.layer_idx,
-                                   _ptr(krow), _ptr(vrow))
-        res.traces.append(dict(k_row_off=krow, v_row_off=vrow))
+                                   ctypes.byref(otr))
+        res.traces.append(tr)
     elif case.op == "bshd":
         cache = case.caches[0]
         D, Hk, Hq = cache.head_dim, cache.num_kv_heads, case.n_q_heads

@@ -37,9 +37,17 @@
 /* element access                                                      */
 /* ------------------------------------------------------------------ */
 
-static size_t elem_bytes(int32_t dt) { return dt == ORC_F32 ? 4u : 2u; }
+static size_t elem_bytes(int32_t dt) { return dt == ORC_F32 ? 4u : dt == ORC_FP8 ? 1u : 2u; }
 
+/* element types of the operations' inputs and outputs */
 static int dtype_ok(int32_t dt) { return dt == ORC_F32 || dt == ORC_BF16 || dt == ORC_F16; }
+
+/* a cache holds the op's dtype, or FP8 codes with a scale per row */
+static int cache_dtype_ok(const orc_cache* c, int32_t dtype) {
+  if (c->dtype == dtype) return 1;
+  return c->dtype == ORC_FP8 && c->scales &&
+         (c->scale_dtype == ORC_F32 || c->scale_dtype == ORC_BF16);
+}
 
 double orc_bf16_to_double(uint16_t b) {
   /* a bf16 value is the upper half of an IEEE binary32 word */
@@ -102,6 +110,38 @@ uint16_t orc_round_f16(double x) {
   int re = ilogb(r); /* the rounded value may have moved up one binade */
   uint16_t mant = (uint16_t)((r / ldexp(1.0, re) - 1.0) * 1024.0);
   return (uint16_t)(sign | (uint16_t)((re + 15) << 10) | mant);
+}
+
+/* OCP FP8 E4M3, the finite-only variant: 1 sign, 4 exponent (bias 7) and 3
+ * fraction bits; exponent field 0 holds subnormals m * 2^-9; the all-ones
+ * pattern S.1111.111 is NaN; the largest finite value is 1.75 * 2^8 = 448. */
+double orc_e4m3_to_double(uint8_t q) {
+  const int sign = q >> 7, e = (q >> 3) & 0xF, m = q & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+uint8_t orc_round_e4m3(double x) {
+  const uint8_t sign = signbit(x) ? 0x80u : 0u;
+  if (isnan(x)) return (uint8_t)(sign | 0x7Fu);
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  /* 4 significant bits; below 2^-6 the spacing stays 2^-9 (subnormals) */
+  int e = isinf(a) ? 8 : ilogb(a);
+  if (e < -6) e = -6;
+  double quantum = ldexp(1.0, e - 3);
+  double r = isinf(a) ? 448.0 : nearbyint(a / quantum) * quantum; /* ties to even */
+  if (r > 448.0) r = 448.0; /* no infinity in this format: saturate */
+  if (r < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -9)));
+  int re = ilogb(r); /* the rounded value may have moved up one binade */
+  uint8_t mant = (uint8_t)((r / ldexp(1.0, re) - 1.0) * 8.0);
+  return (uint8_t)(sign | (uint8_t)((re + 7) << 3) | mant);
 }
 
 static double get(const void* base, int32_t dt, int64_t i) {
@@ -250,39 +290,127 @@ static int head_buf_alloc(head_buf* hb, uint32_t D) {
   return 1;
 }
 
-/* Process one head: read x, optional norm, rope, write with the rule
- * "roped or normed elements are rounded; the rest move as raw bits". */
-static void do_head(const void* src, int64_t src_off, void* dst, int64_t dst_off, int32_t dt,
-                    uint32_t D, const void* gamma, double w, double eps, int32_t mbc,
-                    const float* freqs, uint32_t pos, uint32_t R, int32_t interleaved, head_buf* hb,
-                    double* exact, double* mag) {
-  for (uint32_t j = 0; j < D; ++j) hb->x[j] = get(src, dt, src_off + j);
+/* hb->x (already read) -> optional norm -> rope -> hb->y, pair lengths in hb->mag */
+static void head_math(head_buf* hb, uint32_t D, const void* gamma, int32_t dt, double w,
+                      double eps, int32_t mbc, const float* freqs, uint32_t pos, uint32_t R,
+                      int32_t interleaved) {
   const double* in = hb->x;
   if (gamma) {
     rmsnorm_head(hb->x, hb->xn, D, gamma, dt, w, eps, mbc);
     in = hb->xn;
   }
   rope_head(in, hb->y, hb->mag, D, freqs, pos, R, interleaved);
+}
+
+static void record(const head_buf* hb, uint32_t D, double* exact, double* mag) {
   for (uint32_t j = 0; j < D; ++j) {
-    if (gamma || j < R)
-      put(dst, dt, dst_off + j, hb->y[j]);
-    else
-      copy_bits(dst, dst_off + j, src, src_off + j, dt);
     if (exact) exact[j] = hb->y[j];
     if (mag) mag[j] = hb->mag[j];
   }
+}
+
+/* Store a head's result in a plain buffer of dtype dst_dt.  Elements below
+ * `first_moved` (the roped ones; all of them after a norm) are rounded to
+ * dst_dt; the others move as raw bits when the source has dst_dt, and are
+ * rounded (converted) when it does not. */
+static void store_plain(void* dst, int64_t dst_off, int32_t dst_dt, const double* y,
+                        const void* src, int64_t src_off, int32_t src_dt, uint32_t D,
+                        uint32_t first_moved) {
+  for (uint32_t j = 0; j < D; ++j) {
+    if (j < first_moved || src_dt != dst_dt)
+      put(dst, dst_dt, dst_off + j, y[j]);
+    else
+      copy_bits(dst, dst_off + j, src, src_off + j, dst_dt);
+  }
+}
+
+/* ---- FP8 cache rows: one scale per (page, plane, layer, slot, head) row ---- */
+
+static int64_t scale_offset(const orc_cache* c, uint64_t page, uint32_t plane, uint32_t layer,
+                            uint32_t slot, uint32_t h) {
+  return (int64_t)page * c->s_page_stride + (int64_t)plane * c->s_plane_stride +
+         (int64_t)layer * c->s_layer_stride + (int64_t)slot * c->s_slot_stride +
+         (int64_t)h * c->s_head_stride;
+}
+
+static float get_scale(const orc_cache* c, int64_t so) {
+  if (c->scale_dtype == ORC_F32) return ((const float*)c->scales)[so];
+  return (float)orc_bf16_to_double(((const uint16_t*)c->scales)[so]);
+}
+
+static void put_scale(orc_cache* c, int64_t so, float s) {
+  if (c->scale_dtype == ORC_F32)
+    ((float*)c->scales)[so] = s;
+  else
+    ((uint16_t*)c->scales)[so] = orc_round_bf16((double)s); /* exact: s is a bf16 value */
+}
+
+/* Quantize one head row (reading of the cache collection's scale dtype and
+ * granularity parameters, which the pages name without defining): every
+ * decision is taken in binary32.  v_j = binary32(y_j); amax = max |v_j|;
+ * s = amax / 448 (binary32 division), rounded to the scale dtype;
+ * r = 1 / s (binary32; 0 when s = 0); code_j = e4m3(clamp(v_j * r, +-448))
+ * with the product rounded to binary32 and the code by nearest-even. */
+static void quantize_row(orc_cache* c, int64_t off, int64_t so, const double* y, uint32_t D) {
+  float amax = 0.0f;
+  for (uint32_t j = 0; j < D; ++j) {
+    float v = (float)y[j];
+    if (fabsf(v) > amax) amax = fabsf(v);
+  }
+  float s = amax / 448.0f;
+  if (c->scale_dtype == ORC_BF16) s = (float)orc_bf16_to_double(orc_round_bf16((double)s));
+  float r = s > 0.0f ? 1.0f / s : 0.0f;
+  uint8_t* codes = (uint8_t*)c->pool + off;
+  for (uint32_t j = 0; j < D; ++j) {
+    float q = (float)y[j] * r;
+    if (q > 448.0f) q = 448.0f;
+    if (q < -448.0f) q = -448.0f;
+    codes[j] = orc_round_e4m3((double)q);
+  }
+  put_scale(c, so, s);
+}
+
+/* A cache row's values: plain dtypes widen exactly; FP8 codes are scaled by
+ * the row's scale with one binary32 multiply. */
+static void read_cache_row(const orc_cache* c, int64_t off, int64_t so, uint32_t D, double* x) {
+  if (c->dtype != ORC_FP8) {
+    for (uint32_t j = 0; j < D; ++j) x[j] = get(c->pool, c->dtype, off + j);
+    return;
+  }
+  const float s = get_scale(c, so);
+  const uint8_t* codes = (const uint8_t*)c->pool + off;
+  for (uint32_t j = 0; j < D; ++j) x[j] = (double)((float)orc_e4m3_to_double(codes[j]) * s);
+}
+
+/* Store a head's result in a cache row: a plain cache as store_plain does
+ * (its dtype is the op's), an FP8 cache by quantizing the whole row. */
+static void store_cache_row(orc_cache* c, int64_t off, int64_t so, const double* y,
+                            const void* src, int64_t src_off, int32_t src_dt, uint32_t D,
+                            uint32_t first_moved) {
+  if (c->dtype == ORC_FP8)
+    quantize_row(c, off, so, y, D);
+  else
+    store_plain(c->pool, off, c->dtype, y, src, src_off, src_dt, D, first_moved);
+}
+
+static void read_plain(const void* src, int32_t dt, int64_t off, uint32_t D, double* x) {
+  for (uint32_t j = 0; j < D; ++j) x[j] = get(src, dt, off + j);
 }
 
 static int32_t check_common(int32_t dtype, const orc_cache* c, uint32_t rope_dim,
                             uint32_t layer_idx, uint32_t max_seq_len) {
   if (!c || !c->pool || !c->cache_lengths || !c->lookup_table) return ORC_EINVAL;
   if (!dtype_ok(dtype)) return ORC_EINVAL;
-  if (c->dtype != dtype) return ORC_EINVAL;
+  if (!cache_dtype_ok(c, dtype)) return ORC_EINVAL;
   if (c->head_dim == 0 || c->page_size == 0) return ORC_EINVAL;
   if (rope_dim == 0 || rope_dim % 2 || rope_dim > c->head_dim) return ORC_EINVAL;
   if (layer_idx >= c->num_layers) return ORC_EINVAL;
   if (max_seq_len == 0) return ORC_EINVAL;
   return ORC_OK;
+}
+
+static void set_off(int64_t* rec, uint64_t i, int64_t v) {
+  if (rec) rec[i] = v;
 }
 
 /* ------------------------------------------------------------------ */
@@ -294,9 +422,11 @@ int32_t orc_rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t T,
                                    const uint32_t* off, uint32_t B, const float* freqs,
                                    uint32_t max_seq_len, uint32_t R, int32_t interleaved,
                                    orc_cache* c, uint32_t layer_idx, void* q_out,
-                                   uint64_t q_out_row_stride, orc_trace* tr) {
+                                   int32_t q_out_dtype, uint64_t q_out_row_stride,
+                                   orc_trace* tr) {
   int32_t st = check_common(dtype, c, R, layer_idx, max_seq_len);
   if (st) return st;
+  if (!dtype_ok(q_out_dtype)) return ORC_EINVAL;
   if (c->kv_planes != 2) return ORC_EINVAL;
   if (T == 0) return ORC_OK;
   if (!qkv || !off || !freqs || !q_out) return ORC_EINVAL;
@@ -314,28 +444,44 @@ int32_t orc_rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t T,
   for (uint32_t t = 0; t < T; ++t) {
     where_is(c, off, B, 0, t, max_seq_len, &w);
     const int64_t in_row = (int64_t)t * (int64_t)qkv_row_stride;
-    /* Q heads -> dense q_output */
+    /* Q heads -> dense q_output (of q_out_dtype) */
     for (uint32_t h = 0; h < Hq; ++h) {
-      double* ex = tr && tr->q_exact ? tr->q_exact + ((uint64_t)t * Hq + h) * D : NULL;
-      double* mg = tr && tr->q_mag ? tr->q_mag + ((uint64_t)t * Hq + h) * D : NULL;
-      do_head(qkv, in_row + (int64_t)h * D, q_out, (int64_t)t * (int64_t)q_out_row_stride + (int64_t)h * D,
-              dtype, D, NULL, 0.0, 0.0, 1, freqs, w.pos, R, interleaved, &hb, ex, mg);
+      const int64_t src = in_row + (int64_t)h * D;
+      read_plain(qkv, dtype, src, D, hb.x);
+      head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, w.pos, R, interleaved);
+      store_plain(q_out, (int64_t)t * (int64_t)q_out_row_stride + (int64_t)h * D, q_out_dtype,
+                  hb.y, qkv, src, dtype, D, R);
+      if (tr)
+        record(&hb, D, tr->q_exact ? tr->q_exact + ((uint64_t)t * Hq + h) * D : NULL,
+               tr->q_mag ? tr->q_mag + ((uint64_t)t * Hq + h) * D : NULL);
     }
     /* K heads -> plane 0 of the cache, roped */
     for (uint32_t h = 0; h < Hk; ++h) {
-      int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);
-      double* ex = tr && tr->k_exact ? tr->k_exact + ((uint64_t)t * Hk + h) * D : NULL;
-      double* mg = tr && tr->k_mag ? tr->k_mag + ((uint64_t)t * Hk + h) * D : NULL;
-      do_head(qkv, in_row + (int64_t)(Hq + h) * D, c->pool, dst, dtype, D, NULL, 0.0, 0.0, 1, freqs,
-              w.pos, R, interleaved, &hb, ex, mg);
-      if (tr && tr->k_row_off) tr->k_row_off[(uint64_t)t * Hk + h] = dst;
+      const int64_t src = in_row + (int64_t)(Hq + h) * D;
+      const int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);
+      const int64_t so = c->scales ? scale_offset(c, w.page, 0, layer_idx, w.slot, h) : -1;
+      read_plain(qkv, dtype, src, D, hb.x);
+      head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, w.pos, R, interleaved);
+      store_cache_row(c, dst, so, hb.y, qkv, src, dtype, D, R);
+      if (tr) {
+        record(&hb, D, tr->k_exact ? tr->k_exact + ((uint64_t)t * Hk + h) * D : NULL,
+               tr->k_mag ? tr->k_mag + ((uint64_t)t * Hk + h) * D : NULL);
+        set_off(tr->k_row_off, (uint64_t)t * Hk + h, dst);
+        set_off(tr->k_scale_off, (uint64_t)t * Hk + h, so);
+      }
     }
-    /* V heads -> plane 1 of the cache, bit copy */
+    /* V heads -> plane 1 of the cache: bits moved as they are (an FP8 cache
+     * quantizes the row instead) */
     for (uint32_t h = 0; h < Hk; ++h) {
-      int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);
-      int64_t src = in_row + (int64_t)(Hq + Hk + h) * D;
-      for (uint32_t j = 0; j < D; ++j) copy_bits(c->pool, dst + j, qkv, src + j, dtype);
-      if (tr && tr->v_row_off) tr->v_row_off[(uint64_t)t * Hk + h] = dst;
+      const int64_t src = in_row + (int64_t)(Hq + Hk + h) * D;
+      const int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);
+      const int64_t so = c->scales ? scale_offset(c, w.page, 1, layer_idx, w.slot, h) : -1;
+      read_plain(qkv, dtype, src, D, hb.x);
+      store_cache_row(c, dst, so, hb.x, qkv, src, dtype, D, 0);
+      if (tr) {
+        set_off(tr->v_row_off, (uint64_t)t * Hk + h, dst);
+        set_off(tr->v_scale_off, (uint64_t)t * Hk + h, so);
+      }
     }
   }
   free(hb.x);
@@ -372,31 +518,50 @@ int32_t orc_qk_rmsnorm_rope_paged(const void* buf, int32_t dtype, uint32_t T,
     where_is(c, off, B, 0, t, max_seq_len, &w);
     const int64_t in_row = (int64_t)t * (int64_t)buf_row_stride;
     for (uint32_t h = 0; h < Hq; ++h) {
-      double* ex = tr && tr->q_exact ? tr->q_exact + ((uint64_t)t * Hq + h) * D : NULL;
-      double* mg = tr && tr->q_mag ? tr->q_mag + ((uint64_t)t * Hq + h) * D : NULL;
-      do_head(buf, in_row + (int64_t)band->q_col + (int64_t)h * D, band->q_output,
-              (int64_t)t * (int64_t)band->q_out_row_stride + (int64_t)h * D, dtype, D,
-              band->q_gamma, wv, eps, multiply_before_cast, freqs, w.pos, R, interleaved, &hb, ex,
-              mg);
+      const int64_t src = in_row + (int64_t)band->q_col + (int64_t)h * D;
+      read_plain(buf, dtype, src, D, hb.x);
+      head_math(&hb, D, band->q_gamma, dtype, wv, eps, multiply_before_cast, freqs, w.pos, R,
+                interleaved);
+      store_plain(band->q_output, (int64_t)t * (int64_t)band->q_out_row_stride + (int64_t)h * D,
+                  dtype, hb.y, buf, src, dtype, D, band->q_gamma ? D : R);
+      if (tr)
+        record(&hb, D, tr->q_exact ? tr->q_exact + ((uint64_t)t * Hq + h) * D : NULL,
+               tr->q_mag ? tr->q_mag + ((uint64_t)t * Hq + h) * D : NULL);
     }
     for (uint32_t h = 0; h < Hk; ++h) {
-      int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);
-      double* ex = tr && tr->k_exact ? tr->k_exact + ((uint64_t)t * Hk + h) * D : NULL;
-      double* mg = tr && tr->k_mag ? tr->k_mag + ((uint64_t)t * Hk + h) * D : NULL;
-      if (band->k_col >= 0) /* K from the buffer */
-        do_head(buf, in_row + band->k_col + (int64_t)h * D, c->pool, dst, dtype, D, band->k_gamma,
-                wv, eps, multiply_before_cast, freqs, w.pos, R, interleaved, &hb, ex, mg);
-      else /* K already in the cache: updated in place (the row is read whole first) */
-        do_head(c->pool, dst, c->pool, dst, dtype, D, band->k_gamma, wv, eps,
-                multiply_before_cast, freqs, w.pos, R, interleaved, &hb, ex, mg);
-      if (tr && tr->k_row_off) tr->k_row_off[(uint64_t)t * Hk + h] = dst;
+      const int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);
+      const int64_t so = c->scales ? scale_offset(c, w.page, 0, layer_idx, w.slot, h) : -1;
+      const uint32_t moved = band->k_gamma ? D : R;
+      if (band->k_col >= 0) { /* K from the buffer */
+        const int64_t src = in_row + band->k_col + (int64_t)h * D;
+        read_plain(buf, dtype, src, D, hb.x);
+        head_math(&hb, D, band->k_gamma, dtype, wv, eps, multiply_before_cast, freqs, w.pos, R,
+                  interleaved);
+        store_cache_row(c, dst, so, hb.y, buf, src, dtype, D, moved);
+      } else { /* K already in the cache: updated in place (the row is read whole first) */
+        read_cache_row(c, dst, so, D, hb.x);
+        head_math(&hb, D, band->k_gamma, dtype, wv, eps, multiply_before_cast, freqs, w.pos, R,
+                  interleaved);
+        store_cache_row(c, dst, so, hb.y, c->pool, dst, c->dtype, D, moved);
+      }
+      if (tr) {
+        record(&hb, D, tr->k_exact ? tr->k_exact + ((uint64_t)t * Hk + h) * D : NULL,
+               tr->k_mag ? tr->k_mag + ((uint64_t)t * Hk + h) * D : NULL);
+        set_off(tr->k_row_off, (uint64_t)t * Hk + h, dst);
+        set_off(tr->k_scale_off, (uint64_t)t * Hk + h, so);
+      }
     }
     if (band->v_col >= 0) {
       for (uint32_t h = 0; h < Hk; ++h) {
-        int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);
-        int64_t src = in_row + band->v_col + (int64_t)h * D;
-        for (uint32_t j = 0; j < D; ++j) copy_bits(c->pool, dst + j, buf, src + j, dtype);
-        if (tr && tr->v_row_off) tr->v_row_off[(uint64_t)t * Hk + h] = dst;
+        const int64_t src = in_row + band->v_col + (int64_t)h * D;
+        const int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);
+        const int64_t so = c->scales ? scale_offset(c, w.page, 1, layer_idx, w.slot, h) : -1;
+        read_plain(buf, dtype, src, D, hb.x);
+        store_cache_row(c, dst, so, hb.x, buf, src, dtype, D, 0);
+        if (tr) {
+          set_off(tr->v_row_off, (uint64_t)t * Hk + h, dst);
+          set_off(tr->v_scale_off, (uint64_t)t * Hk + h, so);
+        }
       }
     }
   }
@@ -410,11 +575,11 @@ int32_t orc_dual_band(const void* buf, int32_t dtype, uint32_t T, uint64_t buf_r
                       const float* freqs, uint32_t max_seq_len, uint32_t R, int32_t interleaved,
                       uint32_t layer_idx, orc_trace* main_trace, orc_trace* index_trace) {
   if (!main_band || !index_band || !main_band->cache || !index_band->cache) return ORC_EINVAL;
-  /* the two bands must agree on dtype and head size (fused_dual_qk_rms_norm_rope_ragged_paged
-   * page, Description: identical RoPE geometry across both bands) */
-  if (main_band->cache->dtype != index_band->cache->dtype ||
-      main_band->cache->head_dim != index_band->cache->head_dim)
-    return ORC_EINVAL;
+  /* the two bands share the op's dtype and must agree on head size
+   * (fused_dual_qk_rms_norm_rope_ragged_paged page, Description: identical
+   * RoPE geometry across both bands); their caches' element types are
+   * independent parameters (signature: main_cache_dtype, index_cache_dtype) */
+  if (main_band->cache->head_dim != index_band->cache->head_dim) return ORC_EINVAL;
   /* one launch fusing two single-band launches: the same result as the two in turn */
   int32_t st = orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, main_band, weight_offset,
                                          multiply_before_cast, off, B, freqs, max_seq_len, R,
@@ -427,10 +592,10 @@ int32_t orc_dual_band(const void* buf, int32_t dtype, uint32_t T, uint64_t buf_r
 
 int32_t orc_kv_cache_radd(const void* a, int32_t dtype, uint32_t T, uint64_t a_row_stride,
                           const uint32_t* off, uint32_t B, uint32_t batch_offset, orc_cache* c,
-                          uint32_t layer_idx, int64_t* k_row_off, int64_t* v_row_off) {
+                          uint32_t layer_idx, orc_trace* tr) {
   if (!c || !c->pool || !c->cache_lengths || !c->lookup_table) return ORC_EINVAL;
-  if (!dtype_ok(dtype)) return ORC_EINVAL;
-  if (c->dtype != dtype || c->kv_planes != 2 || layer_idx >= c->num_layers) return ORC_EINVAL;
+  if (!dtype_ok(dtype) || !cache_dtype_ok(c, dtype)) return ORC_EINVAL;
+  if (c->kv_planes != 2 || layer_idx >= c->num_layers) return ORC_EINVAL;
   if ((uint64_t)batch_offset + B > c->cache_batch) return ORC_EINVAL;
   if (T == 0) return ORC_OK;
   if (!a || !off) return ORC_EINVAL;
@@ -443,23 +608,34 @@ int32_t orc_kv_cache_radd(const void* a, int32_t dtype, uint32_t T, uint64_t a_r
   for (uint32_t t = 0; t < T; ++t)
     if ((st = where_is(c, off, B, batch_offset, t, 0, &w))) return st;
 
+  double* row = (double*)malloc(sizeof(double) * D);
+  if (!row) return ORC_EINVAL;
   for (uint32_t t = 0; t < T; ++t) {
     where_is(c, off, B, batch_offset, t, 0, &w);
     for (uint32_t plane = 0; plane < 2; ++plane) { /* first half of a -> K, second -> V */
       for (uint32_t h = 0; h < Hk; ++h) {
-        int64_t dst = row_offset(c, w.page, plane, layer_idx, w.slot, h);
-        int64_t src = (int64_t)t * (int64_t)a_row_stride + (int64_t)(plane * hidden) + (int64_t)h * D;
+        const int64_t dst = row_offset(c, w.page, plane, layer_idx, w.slot, h);
+        const int64_t so = c->scales ? scale_offset(c, w.page, plane, layer_idx, w.slot, h) : -1;
+        const int64_t src = (int64_t)t * (int64_t)a_row_stride + (int64_t)(plane * hidden) + (int64_t)h * D;
+        read_cache_row(c, dst, so, D, row);
         for (uint32_t j = 0; j < D; ++j) {
-          float cur = (float)get(c->pool, dtype, dst + j);
+          float cur = (float)row[j];
           float add = (float)get(a, dtype, src + j);
           float sum = cur + add; /* one IEEE binary32 add */
-          put(c->pool, dtype, dst + j, (double)sum);
+          row[j] = (double)sum;
         }
-        int64_t* rec = plane == 0 ? k_row_off : v_row_off;
-        if (rec) rec[(uint64_t)t * Hk + h] = dst;
+        if (c->dtype == ORC_FP8)
+          quantize_row(c, dst, so, row, D);
+        else
+          for (uint32_t j = 0; j < D; ++j) put(c->pool, c->dtype, dst + j, row[j]);
+        if (tr) {
+          set_off(plane == 0 ? tr->k_row_off : tr->v_row_off, (uint64_t)t * Hk + h, dst);
+          set_off(plane == 0 ? tr->k_scale_off : tr->v_scale_off, (uint64_t)t * Hk + h, so);
+        }
       }
     }
   }
+  free(row);
   return ORC_OK;
 }
 
@@ -515,18 +691,26 @@ int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t B, ui
       uint32_t slot = 0;
       locate(c, b, pos, &page, &slot); /* checked above */
       for (uint32_t h = 0; h < Hq; ++h) {
-        double* ex = tr && tr->q_exact ? tr->q_exact + (t * Hq + h) * D : NULL;
-        double* mg = tr && tr->q_mag ? tr->q_mag + (t * Hq + h) * D : NULL;
-        do_head(q_proj, row + (int64_t)h * D, output, row + (int64_t)h * D, dtype, D, NULL, 0.0,
-                0.0, 1, freqs, pos, R, interleaved, &hb, ex, mg);
+        const int64_t src = row + (int64_t)h * D;
+        read_plain(q_proj, dtype, src, D, hb.x);
+        head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, pos, R, interleaved);
+        store_plain(output, src, dtype, hb.y, q_proj, src, dtype, D, R);
+        if (tr)
+          record(&hb, D, tr->q_exact ? tr->q_exact + (t * Hq + h) * D : NULL,
+                 tr->q_mag ? tr->q_mag + (t * Hq + h) * D : NULL);
       }
       for (uint32_t h = 0; h < Hk; ++h) {
-        int64_t dst = row_offset(c, page, 0, layer_idx, slot, h);
-        double* ex = tr && tr->k_exact ? tr->k_exact + (t * Hk + h) * D : NULL;
-        double* mg = tr && tr->k_mag ? tr->k_mag + (t * Hk + h) * D : NULL;
-        do_head(c->pool, dst, c->pool, dst, dtype, D, NULL, 0.0, 0.0, 1, freqs, pos, R,
-                interleaved, &hb, ex, mg);
-        if (tr && tr->k_row_off) tr->k_row_off[t * Hk + h] = dst;
+        const int64_t dst = row_offset(c, page, 0, layer_idx, slot, h);
+        const int64_t so = c->scales ? scale_offset(c, page, 0, layer_idx, slot, h) : -1;
+        read_cache_row(c, dst, so, D, hb.x);
+        head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, pos, R, interleaved);
+        store_cache_row(c, dst, so, hb.y, c->pool, dst, c->dtype, D, R);
+        if (tr) {
+          record(&hb, D, tr->k_exact ? tr->k_exact + (t * Hk + h) * D : NULL,
+                 tr->k_mag ? tr->k_mag + (t * Hk + h) * D : NULL);
+          set_off(tr->k_row_off, t * Hk + h, dst);
+          set_off(tr->k_scale_off, t * Hk + h, so);
+        }
       }
     }
   }

@@ -27,7 +27,15 @@
  *   - RMSNorm: mean of squares over the head, epsilon inside the square
  *     root, gamma + weight_offset as the scale, norm before rope;
  *   - multiply_before_cast=false: parity unpinned (named only on the
- *     fused_dual_qk_rms_norm_rope_ragged_paged page, signature).
+ *     fused_dual_qk_rms_norm_rope_ragged_paged page, signature);
+ *   - FP8 caches (the pages name a cache collection's scale dtype and
+ *     quantization granularity, nothing more): OCP E4M3 codes, one dynamic
+ *     absmax scale per written head row, every decision in binary32 (see
+ *     quantize_row); parity of the encoding is pinned, the granularity and
+ *     scale rule are a reading (unpinned);
+ *   - q_out_dtype (rope_split_store_paged_ragged page, Parameters): Q is
+ *     rounded once to it; un-roped elements move as bits when it equals the
+ *     input dtype and are converted (nearest-even) otherwise.
  */
 #ifndef QRP_ORACLE_H
 #define QRP_ORACLE_H
@@ -38,7 +46,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2, ORC_FP8 = 3 /* e4m3 codes: caches only */ };
 
 enum {
   ORC_OK = 0,
@@ -46,7 +54,10 @@ enum {
   ORC_EDATA = -6     /* metadata out of range (position, page, offsets) */
 };
 
-/* A paged K/V cache as the oracle sees it (host memory). */
+/* A paged K/V cache as the oracle sees it (host memory).  dtype is the op's
+ * dtype, or ORC_FP8: then every (page, plane, layer, slot, head) row of D
+ * codes has one scale, at the s_* strides in `scales` (ORC_F32 or ORC_BF16
+ * values); a row's value j is code_j * scale in binary32. */
 typedef struct orc_cache {
   void* pool;                 /* elements of `dtype` */
   int32_t dtype;
@@ -62,6 +73,9 @@ typedef struct orc_cache {
   const uint32_t* lookup_table;    /* [cache_batch][max_pages_per_seq] */
   uint32_t cache_batch;
   uint32_t max_pages_per_seq;
+  void* scales;               /* ORC_FP8 only, else NULL */
+  int32_t scale_dtype;
+  int64_t s_page_stride, s_plane_stride, s_layer_stride, s_slot_stride, s_head_stride;
 } orc_cache;
 
 /* Optional record of the unrounded results, for tolerance checks.
@@ -74,6 +88,8 @@ typedef struct orc_trace {
   double* k_mag;
   int64_t* k_row_off;  /* pool element offset of each K row written */
   int64_t* v_row_off;  /* pool element offset of each V row written */
+  int64_t* k_scale_off; /* FP8 caches: scale offset of each K row written */
+  int64_t* v_scale_off;
 } orc_trace;
 
 /* One band of the norm+rope op. */
@@ -98,13 +114,18 @@ double orc_bf16_to_double(uint16_t b);
 uint16_t orc_round_f16(double x);
 double orc_f16_to_double(uint16_t h);
 
+/* OCP FP8 E4M3 (finite-only variant): nearest-even, magnitudes past 448
+ * saturate to 448, NaN -> 0x7F with the sign kept. */
+uint8_t orc_round_e4m3(double x);
+double orc_e4m3_to_double(uint8_t q);
+
 /* rope_split_store_paged_ragged page (signature, Summary, Args). */
 int32_t orc_rope_split_store_paged(
     const void* qkv, int32_t dtype, uint32_t total_seq_len, uint64_t qkv_row_stride,
     uint32_t n_q_heads, const uint32_t* input_row_offsets, uint32_t batch_size,
     const float* freqs_cis, uint32_t max_seq_len, uint32_t rope_dim, int32_t interleaved,
-    orc_cache* cache, uint32_t layer_idx, void* q_output, uint64_t q_out_row_stride,
-    orc_trace* trace);
+    orc_cache* cache, uint32_t layer_idx, void* q_output, int32_t q_out_dtype,
+    uint64_t q_out_row_stride, orc_trace* trace);
 
 /* Single-band fused per-head RMSNorm + RoPE (fused_dual_qk_rms_norm_rope_ragged_paged
  * page, Summary and Description). */
@@ -127,7 +148,7 @@ int32_t orc_dual_band(
 int32_t orc_kv_cache_radd(
     const void* a, int32_t dtype, uint32_t total_rows, uint64_t a_row_stride,
     const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t batch_offset,
-    orc_cache* cache, uint32_t layer_idx, int64_t* k_row_off, int64_t* v_row_off);
+    orc_cache* cache, uint32_t layer_idx, orc_trace* trace);
 
 /* generic_fused_qk_rope_bshd_continuous_batch page (signature, Args):
  * q_proj and output [B][S][n_q_heads][head_dim], valid_lengths [B]; the

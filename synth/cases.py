@@ -33,10 +33,14 @@ import numpy as np
 from . import prng
 
 F32, BF16, F16 = "f32", "bf16", "f16"
+FP8 = "fp8"                             # OCP e4m3 codes with a scale per cache row (caches only)
 # signalling-NaN patterns
-SENTINEL = {F32: np.uint32(0x7FBADBAD), BF16: np.uint16(0x7FBA), F16: np.uint16(0x7DBA)}
-BITS_DTYPE = {F32: np.uint32, BF16: np.uint16, F16: np.uint16}
-ELEM_BYTES = {F32: 4, BF16: 2, F16: 2}
+SENTINEL = {F32: np.uint32(0x7FBADBAD), BF16: np.uint16(0x7FBA), F16: np.uint16(0x7DBA),
+            FP8: np.uint8(0x7F)}
+BITS_DTYPE = {F32: np.uint32, BF16: np.uint16, F16: np.uint16, FP8: np.uint8}
+ELEM_BYTES = {F32: 4, BF16: 2, F16: 2, FP8: 1}
+# the finite e4m3 codes (S.1111.111 is NaN)
+FP8_FINITE_CODES = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
 NO_PAGE = np.uint32(0xFFFFFFFF)
 
 # stream numbers (one per generated array)
@@ -96,6 +100,8 @@ class PagedCache:
     cache_lengths: np.ndarray          # uint32 [cache_batch]
     lookup_table: np.ndarray           # uint32 [cache_batch, max_pages_per_seq]
     prefill: list = field(default_factory=list)
+    scale_dtype: Optional[str] = None   # FP8 caches: F32 or BF16 scales, one per row
+    prefill_scales: list = field(default_factory=list)   # FP8: [n, Hk] scale bits per prefill entry
 
     @property
     def cache_batch(self) -> int:
@@ -126,8 +132,50 @@ class PagedCache:
         return int(np.prod(self.shape[1:]))
 
     @property
+    def scale_shape(self) -> tuple:
+        """FP8 caches: one scale per (page, plane, layer, slot, head) row."""
+        return self.shape[:5]
+
+    @property
+    def scale_strides(self) -> dict:
+        st = np.empty(5, dtype=np.int64)
+        acc = 1
+        for i in range(4, -1, -1):
+            st[i] = acc
+            acc *= self.scale_shape[i]
+        return dict(s_page_stride=int(st[0]), s_plane_stride=int(st[1]),
+                    s_layer_stride=int(st[2]), s_slot_stride=int(st[3]),
+                    s_head_stride=int(st[4]))
+
+    def materialize_scales(self, pages: Optional[np.ndarray] = None) -> Optional[np.ndarray]:
+        """FP8 caches: the scales array (sentinel except prefilled rows); with
+        ``pages`` only those pages, in that order.  None for other caches."""
+        if self.dtype != FP8:
+            return None
+        n = self.num_pages if pages is None else len(pages)
+        sc_ = np.full((n,) + self.scale_shape[1:], SENTINEL[self.scale_dtype],
+                      dtype=BITS_DTYPE[self.scale_dtype])
+        pg, pl, ly, sl, _ = self.prefill_arrays()
+        if len(pg):
+            vals = np.concatenate(self.prefill_scales)
+            if pages is not None:
+                remap = np.full(self.num_pages, -1, dtype=np.int64)
+                remap[np.asarray(pages, dtype=np.int64)] = np.arange(len(pages))
+                pg = remap[pg]
+                keep = pg >= 0
+                pg, pl, ly, sl, vals = pg[keep], pl[keep], ly[keep], sl[keep], vals[keep]
+            sc_[pg, pl, ly, sl] = vals
+        return sc_
+
+    @property
     def nbytes(self) -> int:
         return self.num_pages * self.page_elems * ELEM_BYTES[self.dtype]
+
+    @property
+    def scale_nbytes(self) -> int:
+        if self.dtype != FP8:
+            return 0
+        return int(np.prod(self.scale_shape)) * ELEM_BYTES[self.scale_dtype]
 
     def prefill_arrays(self):
         """(pages, planes, layers, slots) int64 arrays and values [n, Hk, D] bits."""
@@ -191,6 +239,11 @@ class Case:
     multiply_before_cast: bool = True
     freq_dtype: str = F32               # table entries: f32, or bf16 / f16 values held in float32
     seq_len: int = 0                    # bshd: padded rows per sequence (lengths = valid lengths)
+    q_out_dtype: Optional[str] = None   # store op: Q output dtype (None: dtype)
+
+    @property
+    def q_dtype(self) -> str:
+        return self.q_out_dtype or self.dtype
 
     @property
     def T(self) -> int:
@@ -221,7 +274,8 @@ def _offsets(lengths: np.ndarray) -> np.ndarray:
 
 def _paged_cache(seed: int, stream: int, dtype: str, Hk: int, D: int, P: int, L: int, planes: int,
                  cache_lengths: np.ndarray, rows_needed: np.ndarray, max_pages: int,
-                 num_pages: Optional[int], slack: float) -> PagedCache:
+                 num_pages: Optional[int], slack: float,
+                 scale_dtype: Optional[str] = None) -> PagedCache:
     """Pool + page table: sequence b takes the next ceil(rows_needed[b] / P) ids
     of a seeded permutation of the pool; left-over table entries take the
     remaining ids while any remain, then NO_PAGE."""
@@ -248,7 +302,8 @@ def _paged_cache(seed: int, stream: int, dtype: str, Hk: int, D: int, P: int, L:
             k += 1
     return PagedCache(dtype=dtype, num_kv_heads=Hk, head_dim=D, page_size=P, num_layers=L,
                       kv_planes=planes, num_pages=num_pages,
-                      cache_lengths=np.asarray(cache_lengths, dtype=np.uint32), lookup_table=table)
+                      cache_lengths=np.asarray(cache_lengths, dtype=np.uint32), lookup_table=table,
+                      scale_dtype=(scale_dtype or F32) if dtype == FP8 else None)
 
 
 def _prefill_rows(cache: PagedCache, seed: int, stream: int, layer: int, planes, seqs,
@@ -262,12 +317,22 @@ def _prefill_rows(cache: PagedCache, seed: int, stream: int, layer: int, planes,
     pos = np.concatenate(pos_list) if pos_list else np.zeros(0, np.int64)
     seq = np.concatenate(seq_list) if seq_list else np.zeros(0, np.int64)
     n_rows = len(pos) * len(planes)
-    vals = to_bits(prng.normal(seed, stream, n_rows * H * D, std=std), cache.dtype)
+    if cache.dtype == FP8:
+        # random finite codes and positive scales around 2^-7 (448 * scale ~ 2..5)
+        pick = prng.integers(seed, stream, n_rows * H * D, 0, len(FP8_FINITE_CODES) - 1)
+        vals = FP8_FINITE_CODES[pick]
+        u = prng.uniform01(seed, stream + 500, n_rows * H)
+        scales = to_bits((0.5 + u) * 2.0 ** -7, cache.scale_dtype)
+        scales = scales.reshape(len(planes), len(pos), H)
+    else:
+        vals = to_bits(prng.normal(seed, stream, n_rows * H * D, std=std), cache.dtype)
     vals = vals.reshape(len(planes), len(pos), H, D)
     pages = cache.lookup_table[seq, pos // P].astype(np.int64)
     for k, plane in enumerate(planes):
         cache.prefill.append((pages, np.full(len(pos), plane, np.int64),
                               np.full(len(pos), layer, np.int64), pos % P, vals[k]))
+        if cache.dtype == FP8:
+            cache.prefill_scales.append(scales[k])
 
 
 def make_store_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq: int, Hk: int,
@@ -275,15 +340,18 @@ def make_store_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq
                     P: int, L: int, layer: int, num_pages: Optional[int] = None,
                     max_pages: Optional[int] = None, slack: float = 0.25,
                     q_out_pad: int = 0, row_pad: int = 0, specials: bool = False,
-                    freq_dtype: str = F32) -> Case:
-    """rope_split_store_paged workload: qkv [T, (Hq + 2Hk) D (+row_pad)] N(0, 1)."""
+                    freq_dtype: str = F32, cache_dtype: Optional[str] = None,
+                    scale_dtype: str = F32, q_out_dtype: Optional[str] = None) -> Case:
+    """rope_split_store_paged workload: qkv [T, (Hq + 2Hk) D (+row_pad)] N(0, 1).
+    ``cache_dtype`` FP8 stores e4m3 rows with ``scale_dtype`` scales;
+    ``q_out_dtype`` sets Q's output dtype (default: dtype)."""
     lengths = np.asarray(lengths, dtype=np.int64)
     cache_lengths = np.asarray(cache_lengths, dtype=np.int64)
     rows = cache_lengths + lengths
     if max_pages is None:
         max_pages = max(1, (max_seq_len + P - 1) // P)
-    cache = _paged_cache(seed, S_PERM, dtype, Hk, D, P, L, 2, cache_lengths, rows, max_pages,
-                         num_pages, slack)
+    cache = _paged_cache(seed, S_PERM, cache_dtype or dtype, Hk, D, P, L, 2, cache_lengths, rows,
+                         max_pages, num_pages, slack, scale_dtype)
     off = _offsets(lengths)
     T = int(off[-1])
     width = (Hq + 2 * Hk) * D
@@ -297,7 +365,8 @@ def make_store_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq
     return Case(name=name, op="store", dtype=dtype, seed=seed, lengths=lengths, offsets=off,
                 buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta, freq_dtype),
                 rope_dim=rope_dim, interleaved=interleaved, caches=[cache], layer_idx=layer,
-                n_q_heads=Hq, q_out_row_stride=Hq * D + q_out_pad, freq_dtype=freq_dtype)
+                n_q_heads=Hq, q_out_row_stride=Hq * D + q_out_pad, freq_dtype=freq_dtype,
+                q_out_dtype=q_out_dtype)
 
 
 def _special_values(dtype: str) -> np.ndarray:
@@ -333,7 +402,8 @@ def make_norm_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq:
                    P: int, L: int, layer: int, k_in_cache: bool, q_norm: bool = True,
                    k_norm: bool = True, eps: float = 1e-6, weight_offset: float = 0.0,
                    multiply_before_cast: bool = True, slack: float = 0.25,
-                   gamma_std: float = 0.1, freq_dtype: str = F32) -> Case:
+                   gamma_std: float = 0.1, freq_dtype: str = F32,
+                   cache_dtype: Optional[str] = None, scale_dtype: str = F32) -> Case:
     """Single-band qk_rmsnorm_rope_paged workload.  Buffer [T, (Hq+2Hk) D] =
     Q | K | V; with ``k_in_cache`` K is prefilled in the cache and updated in
     place (the buffer's K and V columns are then unread)."""
@@ -341,8 +411,8 @@ def make_norm_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq:
     cache_lengths = np.asarray(cache_lengths, dtype=np.int64)
     rows = cache_lengths + lengths
     max_pages = max(1, (max_seq_len + P - 1) // P)
-    cache = _paged_cache(seed, S_PERM, dtype, Hk, D, P, L, 2, cache_lengths, rows, max_pages,
-                         None, slack)
+    cache = _paged_cache(seed, S_PERM, cache_dtype or dtype, Hk, D, P, L, 2, cache_lengths, rows,
+                         max_pages, None, slack, scale_dtype)
     off = _offsets(lengths)
     T = int(off[-1])
     width = (Hq + 2 * Hk) * D
@@ -367,7 +437,9 @@ def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_m
                    max_seq_len: int, P_main: int, P_index: int, eps_main: float = 1e-6,
                    eps_index: float = 1e-6, weight_offset: float = 0.0,
                    multiply_before_cast: bool = True, slack: float = 0.25,
-                   cache_lengths=None, freq_dtype: str = F32) -> Case:
+                   cache_lengths=None, freq_dtype: str = F32,
+                   main_cache_dtype: Optional[str] = None,
+                   index_cache_dtype: Optional[str] = None, scale_dtype: str = F32) -> Case:
     """Dual-band workload: buffer [T, (Hq_main + 2 Hk_main + Hq_index) D] =
     Q-main | K-main | V-main | Q-index; both bands' K caches updated in place."""
     lengths = np.asarray(lengths, dtype=np.int64)
@@ -377,10 +449,10 @@ def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_m
     rows = cl + lengths
     mp_main = max(1, (max_seq_len + P_main - 1) // P_main)
     mp_index = max(1, (max_seq_len + P_index - 1) // P_index)
-    main = _paged_cache(seed, S_PERM, dtype, Hk_main, D, P_main, 1, 2, cl, rows, mp_main, None,
-                        slack)
-    index = _paged_cache(seed, S_PERM + 1000, dtype, 1, D, P_index, 1, 1, cl, rows, mp_index, None,
-                         slack)
+    main = _paged_cache(seed, S_PERM, main_cache_dtype or dtype, Hk_main, D, P_main, 1, 2, cl, rows,
+                        mp_main, None, slack, scale_dtype)
+    index = _paged_cache(seed, S_PERM + 1000, index_cache_dtype or dtype, 1, D, P_index, 1, 1, cl,
+                         rows, mp_index, None, slack, scale_dtype)
     off = _offsets(lengths)
     T = int(off[-1])
     width = (Hq_main + 2 * Hk_main + Hq_index) * D
@@ -402,7 +474,8 @@ def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_m
 
 def make_radd_case(name: str, seed: int, dtype: str, lengths, cache_lengths, batch_offset: int,
                    Hk: int, D: int, P: int, L: int, layer: int, a_std: float = 0.02,
-                   slack: float = 0.25, a_values: Optional[np.ndarray] = None) -> Case:
+                   slack: float = 0.25, a_values: Optional[np.ndarray] = None,
+                   cache_dtype: Optional[str] = None, scale_dtype: str = F32) -> Case:
     """kv_cache_radd workload: a [T, 2 Hk D] N(0, a_std^2) added into rows
     [cache_len, cache_len + len) of cache sequences batch_offset + b, which
     hold N(0, 1) before the call."""
@@ -416,8 +489,8 @@ def make_radd_case(name: str, seed: int, dtype: str, lengths, cache_lengths, bat
     active = np.arange(batch_offset, batch_offset + B)
     rows[active] = cache_lengths[active] + lengths
     max_pages = max(1, int((rows.max() + P - 1) // P))
-    cache = _paged_cache(seed, S_PERM, dtype, Hk, D, P, L, 2, cache_lengths, rows, max_pages,
-                         None, slack)
+    cache = _paged_cache(seed, S_PERM, cache_dtype or dtype, Hk, D, P, L, 2, cache_lengths, rows,
+                         max_pages, None, slack, scale_dtype)
     off = _offsets(lengths)
     T = int(off[-1])
     width = 2 * Hk * D
@@ -435,7 +508,8 @@ def make_bshd_case(name: str, seed: int, dtype: str, valid_lengths, seq_len: int
                    Hq: int, Hk: int, D: int, rope_dim: int, interleaved: bool, theta: float,
                    max_seq_len: int, capacity: int, L: int, layer: int,
                    num_blocks: Optional[int] = None, slack: float = 0.25,
-                   freq_dtype: Optional[str] = None) -> Case:
+                   freq_dtype: Optional[str] = None, cache_dtype: Optional[str] = None,
+                   scale_dtype: str = F32) -> Case:
     """Padded continuous-batching workload: q_proj [B, seq_len, Hq, D] N(0, 1)
     held as [B * seq_len, Hq * D]; a continuous-batching cache of blocks of
     ``capacity`` rows (one page per sequence, a seeded permutation of the
@@ -446,8 +520,8 @@ def make_bshd_case(name: str, seed: int, dtype: str, valid_lengths, seq_len: int
     cl = np.asarray(cache_lengths, dtype=np.int64)
     B = len(valid)
     real = np.minimum(valid, seq_len)
-    cache = _paged_cache(seed, S_PERM, dtype, Hk, D, capacity, L, 2, cl, cl + real, 1, num_blocks,
-                         slack)
+    cache = _paged_cache(seed, S_PERM, cache_dtype or dtype, Hk, D, capacity, L, 2, cl, cl + real, 1,
+                         num_blocks, slack, scale_dtype)
     T = B * seq_len
     width = Hq * D
     buf = to_bits(prng.normal(seed, S_BUF, T * width), dtype).reshape(T, width)

@@ -94,3 +94,69 @@ def ulp_f16(x: np.ndarray) -> np.ndarray:
     ax = np.maximum(np.abs(x), 2.0 ** -14)
     e = np.floor(np.log2(ax))
     return np.power(2.0, e - 10)
+
+
+
+def e4m3_table():
+    """Every finite OCP E4M3 code (positive and negative) with its value,
+    decoded from the bit fields: sign, exponent field e (bias 7), fraction m;
+    e = 0 holds m * 2^-9."""
+    codes, vals = [], []
+    for c in range(256):
+        sign, e, m = c >> 7, (c >> 3) & 0xF, c & 7
+        if e == 15 and m == 7:
+            continue                                  # NaN
+        v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        codes.append(c)
+        vals.append(-v if sign else v)
+    return np.array(codes, dtype=np.uint8), np.array(vals)
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    table = np.full(256, np.nan)
+    c, v = e4m3_table()
+    table[c] = v
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def nearest_even_e4m3(x: float) -> int:
+    """Code of x by neighbour search among the non-negative finite values;
+    ties go to the even code; magnitudes past 448 saturate."""
+    c, v = e4m3_table()
+    pos = v >= 0
+    c, v = c[pos & ~((c == 0x80))], v[pos & ~((c == 0x80))]
+    order = np.argsort(v)
+    c, v = c[order], v[order]
+    a = abs(x)
+    if a >= 448.0:
+        best = 0x7E
+    else:
+        k = int(np.searchsorted(v, a))
+        cands = [i for i in (k - 1, k) if 0 <= i < len(v)]
+        best = int(c[min(cands, key=lambda i: (abs(float(v[i]) - a), int(c[i]) & 1))])
+    if math.copysign(1.0, x) < 0:
+        best |= 0x80
+    return best
+
+
+def quantize_row_f32(values: np.ndarray, scale_dtype: str):
+    """The row quantization in numpy binary32 arithmetic, codes by neighbour
+    search: returns (codes uint8 [D], scale bits)."""
+    v = np.asarray(values, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(v)) if v.size else np.float32(0)
+    s = np.float32(amax) / np.float32(448.0)
+    if scale_dtype == sc.BF16:
+        s = sc.bits_to_f64(sc.to_bits(np.array([s], np.float64), sc.BF16), sc.BF16).astype(
+            np.float32)[0]
+    r = np.float32(1.0) / s if s > 0 else np.float32(0.0)
+    q = np.clip(v * r, np.float32(-448.0), np.float32(448.0))
+    codes = np.array([nearest_even_e4m3(float(x)) for x in q], dtype=np.uint8)
+    bits = sc.to_bits(np.array([float(s)]), scale_dtype)[0]
+    return codes, bits
+
+
+def ulp_e4m3(x: np.ndarray) -> np.ndarray:
+    """Spacing of E4M3 values at |x| (2^-9 below the normal range)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -6)
+    e = np.floor(np.log2(ax))
+    return np.power(2.0, e - 3)

@@ -16,6 +16,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_bshd_pins as bshd_pins
+from tests import test_oracle_fp8_pins as fp8_pins
 from tests import test_oracle_pins as pins
 
 MUTATIONS = {
@@ -31,8 +32,8 @@ MUTATIONS = {
     "position_off_by_one": ("uint64_t pos = (uint64_t)c->cache_lengths[cseq] + (t - off[b]);",
                             "uint64_t pos = (uint64_t)c->cache_lengths[cseq] + (t - off[b]) + (t > 0);"),
     "slot_from_page_index": ("*slot = pos % c->page_size;", "*slot = (pos / c->page_size) % c->page_size;"),
-    "v_into_k_plane": ("int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);\n      int64_t src = in_row + (int64_t)(Hq + Hk + h) * D;",
-                       "int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h) + 1;\n      int64_t src = in_row + (int64_t)(Hq + Hk + h) * D;"),
+    "v_off_by_one_element": ("const int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);\n      const int64_t so = c->scales ? scale_offset(c, w.page, 1, layer_idx, w.slot, h) : -1;\n      read_plain(qkv,",
+                             "const int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h) + 1;\n      const int64_t so = c->scales ? scale_offset(c, w.page, 1, layer_idx, w.slot, h) : -1;\n      read_plain(qkv,"),
     "layer_ignored": ("(int64_t)layer * c->layer_stride +", ""),
     "eps_outside_root": ("double r = 1.0 / sqrt(ss / (double)D + eps);",
                          "double r = 1.0 / (sqrt(ss / (double)D) + eps);"),
@@ -53,7 +54,17 @@ MUTATIONS = {
     "radd_adds_twice": ("float sum = cur + add; /* one IEEE binary32 add */",
                         "float sum = cur + add + add;"),
     "radd_halves_swapped": ("(int64_t)(plane * hidden)", "(int64_t)((1 - plane) * hidden)"),
-    "unroped_dims_rounded": ("if (gamma || j < R)", "if (1)"),
+    "unroped_dims_rounded": ("if (j < first_moved || src_dt != dst_dt)", "if (1)"),
+    "e4m3_bias_8": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "e4m3_truncate": ("double r = isinf(a) ? 448.0 : nearbyint(a / quantum) * quantum;",
+                      "double r = isinf(a) ? 448.0 : trunc(a / quantum) * quantum;"),
+    "e4m3_no_subnormals": ("if (e < -6) e = -6;", ""),
+    "fp8_scale_for_max_240": ("float s = amax / 448.0f;", "float s = amax / 240.0f;"),
+    "fp8_dequant_ignores_scale": ("x[j] = (double)((float)orc_e4m3_to_double(codes[j]) * s);",
+                                  "x[j] = (double)((float)orc_e4m3_to_double(codes[j]));"),
+    "fp8_bf16_scale_not_rounded": ("if (c->scale_dtype == ORC_BF16) s = (float)orc_bf16_to_double(orc_round_bf16((double)s));", ""),
+    "fp8_v_scale_in_k_slot": ("const int64_t so = c->scales ? scale_offset(c, w.page, 1, layer_idx, w.slot, h) : -1;\n      read_plain(qkv,",
+                              "const int64_t so = c->scales ? scale_offset(c, w.page, 0, layer_idx, w.slot, h) : -1;\n      read_plain(qkv,"),
     "bshd_padded_rows_roped": ("if (s >= valid_lengths[b]) {", "if (s > valid_lengths[b]) {"),
     "bshd_position_ignores_cache_len": ("const uint32_t pos = c->cache_lengths[b] + s;",
                                         "const uint32_t pos = s;"),
@@ -81,6 +92,13 @@ PIN_TESTS = [
     (pins.test_radd_is_one_binary32_add_per_element, {"dtype": "f32"}),
     (bshd_pins.test_bshd_matches_complex_brute_force, {"dtype": "bf16", "interleaved": False}),
     (bshd_pins.test_bshd_padded_rows_are_copied_bit_for_bit, {}),
+    (fp8_pins.test_e4m3_rounding_golden_cases, {}),
+    (fp8_pins.test_e4m3_decode_matches_bit_fields, {}),
+    (fp8_pins.test_fp8_store_v_rows_match_binary32_quantization_exactly,
+     {"dtype": "bf16", "scale_dtype": "bf16"}),
+    (fp8_pins.test_fp8_store_k_rows_are_the_quantized_rotation,
+     {"interleaved": True, "scale_dtype": "f32"}),
+    (fp8_pins.test_fp8_radd_is_dequantize_add_requantize_bit_for_bit, {}),
 ]
 
 
