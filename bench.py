@@ -93,31 +93,40 @@ def algorithmic_bytes(case) -> int:
     from synth import cases as sc
 
     eb = sc.ELEM_BYTES[case.dtype]
+    qeb = sc.ELEM_BYTES[case.q_dtype]
     T = case.T
     seq, pos = cache_rows(case)
+
+    def row(c):   # bytes of one cache head row (an FP8 row carries its scale)
+        return c.head_dim * sc.ELEM_BYTES[c.dtype] + (
+            sc.ELEM_BYTES[c.scale_dtype] if c.dtype == sc.FP8 else 0)
+
     total = 0
     if case.op == "bshd":
         c = case.caches[0]
         D, Hk, Hq = c.head_dim, c.num_kv_heads, case.n_q_heads
         total += 2 * T * Hq * D * eb                 # every q_proj row read and written
-        total += 2 * len(pos) * Hk * D * eb          # real rows: K read and written in place
+        total += 2 * len(pos) * Hk * row(c)          # real rows: K read and written in place
     elif case.op == "store":
         c = case.caches[0]
         D, Hk, Hq = c.head_dim, c.num_kv_heads, case.n_q_heads
         total += T * (Hq + 2 * Hk) * D * eb          # qkv read
-        total += T * (Hq + 2 * Hk) * D * eb          # q_out + K + V written
+        total += T * Hq * D * qeb                    # q_out written
+        total += T * 2 * Hk * row(c)                 # K and V rows written
     elif case.op in ("norm", "dual"):
         for b in case.bands:
             c = case.caches[b.cache]
             D, Hk = c.head_dim, c.num_kv_heads
             total += 2 * T * b.n_q_heads * D * eb    # Q read + written
-            total += 2 * T * Hk * D * eb             # K read (buffer or cache) + written
+            total += T * Hk * (D * eb if b.k_col >= 0 else row(c))   # K read (buffer or cache)
+            total += T * Hk * row(c)                 # K written
             if b.v_col >= 0:
-                total += 2 * T * Hk * D * eb         # V read + written
+                total += T * Hk * (D * eb + row(c))  # V read + written
             total += (int(b.q_gamma is not None) + int(b.k_gamma is not None)) * D * eb
     elif case.op == "radd":
         c = case.caches[0]
-        total += 3 * T * 2 * c.num_kv_heads * c.head_dim * eb   # read a, read cache, write cache
+        rows = T * 2 * c.num_kv_heads
+        total += rows * (c.head_dim * eb + 2 * row(c))   # read a, read cache, write cache
     if case.freqs is not None and len(pos):
         total += len(np.unique(pos)) * case.rope_dim * sc.ELEM_BYTES[case.freq_dtype]
     total += (case.batch + (0 if case.op == "bshd" else 1)) * 4   # offsets / valid lengths
@@ -155,6 +164,7 @@ def case_tokens(case) -> int:
 
 
 DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5, "bshd": 6}
+DEFAULT_SEED.update({f"{k}_fp8": v for k, v in list(DEFAULT_SEED.items())})
 
 
 def make_case(workload: str, seed: int = None):
@@ -164,6 +174,7 @@ def make_case(workload: str, seed: int = None):
 
 
 def workload_config(case, cases) -> dict:
+    from synth import cases as sc
     c = case.caches[0]
     cfg = {"workload": {"store": "rope_split_store_paged", "norm": "qk_rmsnorm_rope_paged",
                         "dual": "dual_band", "radd": "kv_cache_radd",
@@ -174,6 +185,8 @@ def workload_config(case, cases) -> dict:
            "tokens_mean": round(sum(x.T for x in cases) / len(cases), 1)}
     if case.op in ("store", "bshd"):
         cfg["q_heads"] = case.n_q_heads
+    if any(x.dtype == sc.FP8 for x in case.caches):
+        cfg["kv_cache"] = "fp8 e4m3, " + case.caches[0].scale_dtype + " scale per row"
     if case.op == "bshd":
         cfg["seq_len"] = case.seq_len
         cfg["real_tokens_per_batch"] = [case_tokens(x) for x in cases]
@@ -356,7 +369,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "decode", "dual", "radd", "bshd"])
+                    choices=["prefill", "decode", "dual", "radd", "bshd", "prefill_fp8",
+                             "decode_fp8", "dual_fp8", "radd_fp8", "bshd_fp8"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-max-passes", type=int, default=30)

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define QRP_ABI_VERSION 1
+#define QRP_ABI_VERSION 2
 
 typedef enum qrp_status {
   QRP_OK = 0,
@@ -65,7 +65,8 @@ typedef enum qrp_status {
 typedef enum qrp_dtype {
   QRP_F32 = 0,   /* IEEE binary32 */
   QRP_BF16 = 1,  /* bfloat16: the top 16 bits of a binary32 */
-  QRP_F16 = 2    /* IEEE binary16 */
+  QRP_F16 = 2,   /* IEEE binary16 */
+  QRP_FP8 = 3    /* OCP FP8 E4M3 codes with a scale per row: caches only */
 } qrp_dtype;
 
 /*
@@ -81,10 +82,24 @@ typedef enum qrp_dtype {
  * page lookup_table[s * max_pages_per_seq + p / page_size].
  * blocks is device memory; cache_lengths [cache_batch] and lookup_table
  * [cache_batch * max_pages_per_seq] are device arrays of uint32.
+ *
+ * dtype QRP_FP8 (the collection's scale dtype and quantization granularity:
+ * rope_split_store_paged_ragged page, Args: kv_collection; named there, not
+ * defined -- this library's reading): every (page, plane, layer, slot,
+ * head) row holds head_dim OCP E4M3 codes and has one scale at
+ *   scales + page*scale_page_stride + plane*scale_plane_stride
+ *          + layer*scale_layer_stride + slot*scale_slot_stride
+ *          + head*scale_head_stride
+ * of scale_dtype (QRP_F32 or QRP_BF16); the row's values are code * scale.
+ * A row written by an op is quantized from its binary32 values v: amax =
+ * max |v|, scale = amax / 448 (rounded to scale_dtype), codes = nearest-even
+ * of clamp(v * (1 / scale), -448, 448) (all zero for an all-zero row); V
+ * rows are quantized too.  Values must be finite.  Other cache dtypes must
+ * equal the op's dtype and leave `scales` NULL.
  */
 typedef struct qrp_paged_cache {
   void* blocks;
-  int32_t dtype;               /* qrp_dtype; must equal the op's dtype */
+  int32_t dtype;               /* the op's dtype, or QRP_FP8 */
   uint32_t num_kv_heads;
   uint32_t head_dim;           /* 64, 128 or 256 */
   uint32_t page_size;          /* > 0 */
@@ -96,6 +111,10 @@ typedef struct qrp_paged_cache {
   const uint32_t* lookup_table;
   uint32_t cache_batch;
   uint32_t max_pages_per_seq;
+  void* scales;                /* QRP_FP8: device array of scale_dtype, else NULL */
+  int32_t scale_dtype;         /* QRP_F32 or QRP_BF16 */
+  int64_t scale_page_stride, scale_plane_stride, scale_layer_stride, scale_slot_stride,
+      scale_head_stride;       /* in scale elements */
 } qrp_paged_cache;
 
 /*
@@ -161,8 +180,11 @@ typedef struct qrp_band {
  * Token t of sequence b sits at position p = cache_lengths[b] + t - offsets[b].
  * Q head h of token t, rotated at p, goes to q_output[t][h*head_dim ..];
  * K heads, rotated, and V heads, copied bit for bit, go to row p of sequence
- * b's pages at layer layer_idx.  cache_lengths are not updated.
- * q_out_dtype must equal dtype (other output dtypes are not built).
+ * b's pages at layer layer_idx (an FP8 cache quantizes both rows).
+ * cache_lengths are not updated.  q_out_dtype (QRP_F32, QRP_BF16 or
+ * QRP_F16) may differ from dtype: Q is rounded once to it, and its
+ * un-rotated elements are converted (nearest-even) rather than copied;
+ * q_out_row_stride is in q_out_dtype elements.
  */
 int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_seq_len,
                                uint64_t qkv_row_stride, uint32_t n_q_heads,
@@ -193,8 +215,10 @@ int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq
  * [q_main | k_main | q_index | k_index] of each token.  Both bands read the
  * same buffer, offsets and freqs table; each row takes its own band's cache,
  * gamma, epsilon, output and Q columns.  The two caches must have the same
- * dtype and head_dim (QRP_EGEOMETRY otherwise: the page requires identical
- * RoPE geometry across the bands).  The result equals main_band's
+ * head_dim (QRP_EGEOMETRY otherwise: the page requires identical RoPE
+ * geometry across the bands); their dtypes are independent parameters on
+ * the page, but this library builds only both-plain or both-FP8 pairs
+ * (QRP_EUNSUPPORTED otherwise).  The result equals main_band's
  * qk_rmsnorm_rope_paged call followed by index_band's.
  */
 int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64_t buf_row_stride,

@@ -20,13 +20,14 @@ LIB_PATH = os.path.join(HERE, "libqk_rope_paged.so")
 
 QRP_OK, QRP_EINVAL, QRP_EALIGN, QRP_EUNSUPPORTED, QRP_EGEOMETRY, QRP_EHIP, QRP_EDATA = (
     0, -1, -2, -3, -4, -5, -6)
-QRP_F32, QRP_BF16, QRP_F16 = 0, 1, 2
+QRP_F32, QRP_BF16, QRP_F16, QRP_FP8 = 0, 1, 2, 3
 STATUS_NAMES = {0: "QRP_OK", -1: "QRP_EINVAL", -2: "QRP_EALIGN", -3: "QRP_EUNSUPPORTED",
                 -4: "QRP_EGEOMETRY", -5: "QRP_EHIP", -6: "QRP_EDATA"}
 
 # entry points declared in include/qk_rope_paged.h
 EXPORTS = ("rope_split_store_paged", "qk_rmsnorm_rope_paged", "dual_band", "kv_cache_radd",
-           "fused_qk_rope_bshd_continuous_batch", "qrp_validate", "qrp_validate_host", "qrp_last_error", "qrp_abi_version")
+           "fused_qk_rope_bshd_continuous_batch", "qrp_validate", "qrp_validate_host",
+           "qrp_last_error", "qrp_abi_version")
 
 
 class QrpError(RuntimeError):
@@ -44,7 +45,11 @@ class QrpPagedCache(ctypes.Structure):
                 ("layer_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
                 ("head_stride", ctypes.c_int64),
                 ("cache_lengths", ctypes.c_void_p), ("lookup_table", ctypes.c_void_p),
-                ("cache_batch", ctypes.c_uint32), ("max_pages_per_seq", ctypes.c_uint32)]
+                ("cache_batch", ctypes.c_uint32), ("max_pages_per_seq", ctypes.c_uint32),
+                ("scales", ctypes.c_void_p), ("scale_dtype", ctypes.c_int32),
+                ("scale_page_stride", ctypes.c_int64), ("scale_plane_stride", ctypes.c_int64),
+                ("scale_layer_stride", ctypes.c_int64), ("scale_slot_stride", ctypes.c_int64),
+                ("scale_head_stride", ctypes.c_int64)]
 
 
 class QrpRope(ctypes.Structure):
@@ -169,6 +174,13 @@ class PagedCache:
     lookup_table: object
     cache_batch: int
     max_pages_per_seq: int
+    scales: object = None            # QRP_FP8 caches: one scale per row
+    scale_dtype: int = QRP_F32
+    scale_page_stride: int = 0
+    scale_plane_stride: int = 0
+    scale_layer_stride: int = 0
+    scale_slot_stride: int = 0
+    scale_head_stride: int = 0
 
     def to_c(self) -> QrpPagedCache:
         return QrpPagedCache(
@@ -178,7 +190,11 @@ class PagedCache:
             plane_stride=self.plane_stride, layer_stride=self.layer_stride,
             slot_stride=self.slot_stride, head_stride=self.head_stride,
             cache_lengths=_ptr(self.cache_lengths), lookup_table=_ptr(self.lookup_table),
-            cache_batch=self.cache_batch, max_pages_per_seq=self.max_pages_per_seq)
+            cache_batch=self.cache_batch, max_pages_per_seq=self.max_pages_per_seq,
+            scales=_ptr(self.scales), scale_dtype=self.scale_dtype,
+            scale_page_stride=self.scale_page_stride, scale_plane_stride=self.scale_plane_stride,
+            scale_layer_stride=self.scale_layer_stride, scale_slot_stride=self.scale_slot_stride,
+            scale_head_stride=self.scale_head_stride)
 
 
 @dataclass

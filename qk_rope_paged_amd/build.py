@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libqk_rope_paged.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["kernels.hip", "abi.cpp"]
+SOURCES = ["kernels.hip", "kernels_fp8.hip", "kernels_qout.hip", "abi.cpp"]
 # measurement helper for the benchmark (not part of the C ABI)
 COPY_LIB_PATH = os.path.join(HERE, "libqrp_bench_copy.so")
 COPY_SOURCES = ["bench_copy.hip"]
@@ -30,22 +30,47 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-command-line-argument"]
+
+
 def command(out: str = LIB_PATH, extra=(), sources=SOURCES) -> list:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-command-line-argument",
-            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    """One hipcc line compiling and linking every source (kept for reference
+    and for one-off variant builds)."""
+    return [hipcc(), *FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             *[os.path.join(CSRC, s) for s in sources], *extra, "-o", out]
 
 
+def object_command(src: str, obj: str, extra=()) -> list:
+    return [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
+            os.path.join(CSRC, src), *extra, "-o", obj]
+
+
 def _compile(out: str, sources, verbose: bool) -> None:
+    """Compile every source to an object in parallel (the kernel translation
+    units are independent), then link them into `out`."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in sources]
+    procs = [subprocess.Popen(object_command(s, o), stdout=subprocess.PIPE,
+                              stderr=subprocess.PIPE, text=True) for s, o in zip(sources, objs)]
+    failed = []
+    for s, p in zip(sources, procs):
+        out_s, err_s = p.communicate()
+        if p.returncode != 0:
+            failed.append(s)
+            sys.stderr.write(out_s + err_s)
+        elif verbose:
+            sys.stderr.write(err_s)
+    if failed:
+        raise RuntimeError("hipcc failed on " + ", ".join(failed))
     tmp = out + ".tmp"
-    res = subprocess.run(command(tmp, sources=sources), capture_output=True, text=True)
+    res = subprocess.run([hipcc(), *FLAGS, "-shared", *objs, "-o", tmp], capture_output=True,
+                         text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building " + os.path.basename(out))
-    if verbose:
-        sys.stderr.write(res.stderr)
+        raise RuntimeError("hipcc failed linking " + os.path.basename(out))
     os.replace(tmp, out)
 
 

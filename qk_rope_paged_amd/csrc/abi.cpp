@@ -29,7 +29,7 @@ int32_t fail(int32_t code, const std::string& msg) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-uint32_t elem_bytes(int32_t dt) { return dt == QRP_F32 ? 4u : 2u; }
+uint32_t elem_bytes(int32_t dt) { return dt == QRP_F32 ? 4u : dt == QRP_FP8 ? 1u : 2u; }
 uint32_t chunk_elems(int32_t dt) { return 16u / elem_bytes(dt); }
 bool dtype_ok(int32_t dt) { return dt == QRP_F32 || dt == QRP_BF16 || dt == QRP_F16; }
 
@@ -59,7 +59,18 @@ int32_t check_cache(const qrp_paged_cache* c, int32_t dtype, uint32_t layer_idx,
   if (!c) return fail(QRP_EINVAL, w + ": cache is NULL");
   if (!c->blocks || !c->cache_lengths || !c->lookup_table)
     return fail(QRP_EINVAL, w + ": blocks, cache_lengths and lookup_table must be non-NULL");
-  if (c->dtype != dtype) return fail(QRP_EUNSUPPORTED, w + ": cache dtype differs from the op dtype");
+  if (c->dtype != dtype && c->dtype != QRP_FP8)
+    return fail(QRP_EUNSUPPORTED, w + ": cache dtype must be the op dtype or QRP_FP8");
+  if (c->dtype == QRP_FP8) {
+    if (!c->scales) return fail(QRP_EINVAL, w + ": an FP8 cache needs scales");
+    if (c->scale_dtype != QRP_F32 && c->scale_dtype != QRP_BF16)
+      return fail(QRP_EUNSUPPORTED, w + ": scale_dtype must be QRP_F32 or QRP_BF16");
+    if (reinterpret_cast<uintptr_t>(c->scales) & (elem_bytes(c->scale_dtype) - 1))
+      return fail(QRP_EALIGN, w + ": scales not aligned to their element size");
+    if (c->scale_page_stride < 0 || c->scale_plane_stride < 0 || c->scale_layer_stride < 0 ||
+        c->scale_slot_stride < 0 || c->scale_head_stride < 0)
+      return fail(QRP_EINVAL, w + ": negative scale stride");
+  }
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
     return fail(QRP_EUNSUPPORTED, w + ": head_dim must be 64, 128 or 256");
   if (c->num_kv_heads == 0 || c->page_size == 0 || c->num_pages == 0 || c->cache_batch == 0 ||
@@ -69,7 +80,7 @@ int32_t check_cache(const qrp_paged_cache* c, int32_t dtype, uint32_t layer_idx,
   if (c->kv_planes != 1 && c->kv_planes != 2) return fail(QRP_EINVAL, w + ": kv_planes must be 1 or 2");
   if (layer_idx >= c->num_layers) return fail(QRP_EINVAL, w + ": layer_idx >= num_layers");
   if (!aligned16(c->blocks)) return fail(QRP_EALIGN, w + ": blocks not 16-byte aligned");
-  const int64_t ce = chunk_elems(dtype);
+  const int64_t ce = chunk_elems(c->dtype);
   const int64_t st[5] = {c->page_stride, c->plane_stride, c->layer_stride, c->slot_stride,
                          c->head_stride};
   for (int64_t s : st) {
@@ -114,6 +125,15 @@ qrp::CacheDesc make_cache(const qrp_paged_cache* c, uint32_t layer_idx) {
     d.page_shift = s;
   }
   d.cache_batch = c->cache_batch;
+  if (c->dtype == QRP_FP8) {
+    d.scales = c->scales;
+    d.s_page_stride = c->scale_page_stride;
+    d.s_plane_stride = c->scale_plane_stride;
+    d.s_slot_stride = c->scale_slot_stride;
+    d.s_head_stride = c->scale_head_stride;
+    d.s_layer_off = (int64_t)layer_idx * c->scale_layer_stride;
+    d.scale_bf16 = c->scale_dtype == QRP_BF16;
+  }
   return d;
 }
 
@@ -181,8 +201,17 @@ struct Builder {
   }
 };
 
-int32_t launch(const Builder& b, bool interleaved, bool radd, void* stream) {
-  const int e = qrp::launch_band(b.a, b.dtype, b.head_dim, interleaved, radd, stream);
+int32_t launch(const Builder& b, bool interleaved, bool radd, void* stream, bool bshd = false,
+               int32_t q_dtype = -1) {
+  qrp::LaunchSpec s{};
+  s.dtype = b.dtype;
+  s.q_dtype = q_dtype < 0 ? b.dtype : q_dtype;
+  s.cache_fp8 = b.a.cache[0].scales != nullptr;
+  s.head_dim = b.head_dim;
+  s.interleaved = interleaved;
+  s.radd = radd;
+  s.bshd = bshd;
+  const int e = qrp::launch_band(b.a, s, stream);
   if (e != 0)
     return fail(QRP_EHIP, std::string("kernel launch failed: ") +
                                hipGetErrorString(static_cast<hipError_t>(e)));
@@ -266,7 +295,8 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
                                uint64_t q_out_row_stride, void* stream) {
   g_err.clear();
   if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
-  if (q_out_dtype != dtype) return fail(QRP_EUNSUPPORTED, "q_out_dtype must equal dtype");
+  if (!dtype_ok(q_out_dtype))
+    return fail(QRP_EUNSUPPORTED, "q_out_dtype must be QRP_F32, QRP_BF16 or QRP_F16");
   if (total_seq_len == 0) return QRP_OK;
   int32_t st;
   if ((st = check_batch(input_row_offsets, total_seq_len, batch_size))) return st;
@@ -276,8 +306,7 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
   if (!qkv || !q_output) return fail(QRP_EINVAL, "qkv / q_output is NULL");
   if (n_q_heads == 0) return fail(QRP_EINVAL, "n_q_heads is 0");
   if (!aligned16(qkv) || !aligned16(q_output)) return fail(QRP_EALIGN, "qkv / q_output not 16-byte aligned");
-  const uint32_t ce = chunk_elems(dtype);
-  if (qkv_row_stride % ce || q_out_row_stride % ce)
+  if (qkv_row_stride % chunk_elems(dtype) || q_out_row_stride % chunk_elems(q_out_dtype))
     return fail(QRP_EALIGN, "row strides must be multiples of 16 bytes");
   const uint64_t D = cache->head_dim, Hk = cache->num_kv_heads;
   if (qkv_row_stride < (n_q_heads + 2 * Hk) * D) return fail(QRP_EINVAL, "qkv_row_stride < q_dim + k_dim + v_dim");
@@ -305,7 +334,7 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
   b.add_seg(qrp::SEG_V_COPY, elem_ptr(qkv, (n_q_heads + Hk) * D, dtype), (int64_t)qkv_row_stride,
             nullptr, 0, nullptr, 0.f, (uint32_t)Hk, 0, 1);
   if ((st = b.finish(total_seq_len, false))) return st;
-  return launch(b, rope->interleaved != 0, false, stream);
+  return launch(b, rope->interleaved != 0, false, stream, false, q_out_dtype);
 }
 
 int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq_len,
@@ -352,9 +381,10 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
   if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
   if (!main_band || !index_band || !main_band->cache || !index_band->cache)
     return fail(QRP_EINVAL, "bands and their caches must be non-NULL");
-  if (main_band->cache->dtype != index_band->cache->dtype ||
-      main_band->cache->head_dim != index_band->cache->head_dim)
-    return fail(QRP_EGEOMETRY, "main and index bands differ in cache dtype or head_dim");
+  if (main_band->cache->head_dim != index_band->cache->head_dim)
+    return fail(QRP_EGEOMETRY, "main and index bands differ in head_dim");
+  if ((main_band->cache->dtype == QRP_FP8) != (index_band->cache->dtype == QRP_FP8))
+    return fail(QRP_EUNSUPPORTED, "dual_band: both caches FP8 or neither (mixed not built)");
   if (total_seq_len == 0) return QRP_OK;
   int32_t st;
   if ((st = check_batch(input_row_offsets, total_seq_len, batch_size))) return st;
@@ -468,11 +498,7 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
   b.add_seg(qrp::SEG_Q, q_proj, (int64_t)row, output, (int64_t)row, nullptr, 0.f, n_q_heads, 0, 0);
   b.add_seg(qrp::SEG_K_INPLACE, nullptr, 0, nullptr, 0, nullptr, 0.f, cache->num_kv_heads, 0, 0);
   if ((st = b.finish((uint32_t)tokens, false))) return st;
-  const int e = qrp::launch_bshd(b.a, dtype, b.head_dim, rope->interleaved != 0, stream);
-  if (e != 0)
-    return fail(QRP_EHIP, std::string("kernel launch failed: ") +
-                               hipGetErrorString(static_cast<hipError_t>(e)));
-  return QRP_OK;
+  return launch(b, rope->interleaved != 0, false, stream, true);
 }
 
 int32_t qrp_validate_host(const uint32_t* off, uint32_t B, uint32_t T, uint32_t batch_offset,

@@ -81,6 +81,12 @@ struct CacheDesc {
   uint32_t page_size;
   uint32_t page_shift;      // log2(page_size) when a power of two, else 0xFFFFFFFF
   uint32_t cache_batch;
+  // FP8 caches: one scale per (page, plane, layer, slot, head) row
+  void* scales;
+  int64_t s_page_stride, s_plane_stride, s_slot_stride, s_head_stride;
+  int64_t s_layer_off;      // layer_idx * scale layer stride
+  uint32_t scale_bf16;      // scales stored as bf16 (else binary32)
+  uint32_t pad_;
 };
 
 struct BandArgs {
@@ -113,7 +119,18 @@ struct BandArgs {
   uint32_t seq_len;
 };
 
-enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8 = 3 };
+
+// What to launch: the op's element types and shape of work.
+struct LaunchSpec {
+  int32_t dtype;            // input (and plain cache) dtype
+  int32_t q_dtype;          // Q output dtype
+  bool cache_fp8;           // caches hold FP8 codes with row scales
+  uint32_t head_dim;
+  bool interleaved;
+  bool radd;
+  bool bshd;                // padded [batch][seq_len] grid
+};
 
 // Largest passes-per-wave the kernel for this op holds in registers.
 inline uint32_t max_passes(bool radd, bool norm) {
@@ -121,12 +138,11 @@ inline uint32_t max_passes(bool radd, bool norm) {
 }
 
 // Launch the band engine; returns 0 or a hipError_t value.
-int launch_band(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interleaved, bool radd,
-                void* stream);
-
-// Launch the padded-grid (BSHD) variant: Q segments and in-place K only.
-int launch_bshd(const BandArgs& a, int32_t dtype, uint32_t head_dim, bool interleaved,
-                void* stream);
+int launch_band(const BandArgs& a, const LaunchSpec& s, void* stream);
+// The three translation units behind it.
+int launch_plain(const BandArgs& a, const LaunchSpec& s, void* stream);
+int launch_fp8(const BandArgs& a, const LaunchSpec& s, void* stream);
+int launch_qout(const BandArgs& a, const LaunchSpec& s, void* stream);
 
 // Rows handled per 64-lane pass for a dtype / head_dim.
 inline uint32_t rows_per_pass(int32_t dtype, uint32_t head_dim) {

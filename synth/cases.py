@@ -544,39 +544,46 @@ def tiny_fp32(seed: int = 1) -> Case:
                            layer=0, num_pages=8, max_pages=4)
 
 
-def prefill(seed: int = 2, small: bool = False) -> Case:
+def _kv(name: str, cache_dtype: Optional[str]) -> str:
+    return name if cache_dtype is None else f"{name}_{cache_dtype}"
+
+
+def prefill(seed: int = 2, small: bool = False, cache_dtype: Optional[str] = None) -> Case:
     if small:
         B = 4
         lens = prng.integers(seed, S_LENS, B, 1, 300)
-        return make_store_case("prefill_small", seed, BF16, lens, np.zeros(B, np.int64), Hq=32,
-                               Hk=8, D=128, rope_dim=128, interleaved=False, theta=5e5,
-                               max_seq_len=8192, P=128, L=4, layer=2)
+        return make_store_case(_kv("prefill_small", cache_dtype), seed, BF16, lens,
+                               np.zeros(B, np.int64), Hq=32, Hk=8, D=128, rope_dim=128,
+                               interleaved=False, theta=5e5, max_seq_len=8192, P=128, L=4,
+                               layer=2, cache_dtype=cache_dtype)
     B = 8
     lens = prng.integers(seed, S_LENS, B, 128, 2048)
-    return make_store_case("prefill", seed, BF16, lens, np.zeros(B, np.int64), Hq=32, Hk=8,
-                           D=128, rope_dim=128, interleaved=False, theta=5e5, max_seq_len=8192,
-                           P=128, L=32, layer=17)
+    return make_store_case(_kv("prefill", cache_dtype), seed, BF16, lens, np.zeros(B, np.int64),
+                           Hq=32, Hk=8, D=128, rope_dim=128, interleaved=False, theta=5e5,
+                           max_seq_len=8192, P=128, L=32, layer=17, cache_dtype=cache_dtype)
 
 
-def decode(seed: int = 3, small: bool = False) -> Case:
+def decode(seed: int = 3, small: bool = False, cache_dtype: Optional[str] = None) -> Case:
     B = 32 if small else 256
     lens = np.ones(B, dtype=np.int64)
     clen = prng.integers(seed, S_CLEN, B, 0, 8191)
-    return make_store_case("decode_small" if small else "decode", seed, BF16, lens, clen,
-                           Hq=32, Hk=8, D=128, rope_dim=128, interleaved=True, theta=5e5,
-                           max_seq_len=8192, P=128, L=1, layer=0,
-                           num_pages=1400 if small else 20000, max_pages=64)
+    return make_store_case(_kv("decode_small" if small else "decode", cache_dtype), seed, BF16,
+                           lens, clen, Hq=32, Hk=8, D=128, rope_dim=128, interleaved=True,
+                           theta=5e5, max_seq_len=8192, P=128, L=1, layer=0,
+                           num_pages=1400 if small else 20000, max_pages=64,
+                           cache_dtype=cache_dtype)
 
 
-def dual(seed: int = 4, small: bool = False) -> Case:
+def dual(seed: int = 4, small: bool = False, cache_dtype: Optional[str] = None) -> Case:
     B = 4 if small else 16
     lens = prng.integers(seed, S_LENS, B, 1, 150 if small else 1024)
-    return make_dual_case("dual_small" if small else "dual", seed, BF16, lens, Hq_main=64,
-                          Hk_main=8, Hq_index=16, D=128, rope_dim=64, interleaved=True,
-                          theta=1e4, max_seq_len=8192, P_main=64, P_index=64)
+    return make_dual_case(_kv("dual_small" if small else "dual", cache_dtype), seed, BF16, lens,
+                          Hq_main=64, Hk_main=8, Hq_index=16, D=128, rope_dim=64,
+                          interleaved=True, theta=1e4, max_seq_len=8192, P_main=64, P_index=64,
+                          main_cache_dtype=cache_dtype, index_cache_dtype=cache_dtype)
 
 
-def radd(seed: int = 5, small: bool = False) -> Case:
+def radd(seed: int = 5, small: bool = False, cache_dtype: Optional[str] = None) -> Case:
     if small:
         B, cb, boff = 6, 12, 4
         lens = prng.integers(seed, S_LENS, B, 1, 64)
@@ -585,11 +592,11 @@ def radd(seed: int = 5, small: bool = False) -> Case:
         B, cb, boff = 32, 64, 4
         lens = prng.integers(seed, S_LENS, B, 16, 512)
         clen = prng.integers(seed, S_CLEN, cb, 0, 4096)
-    return make_radd_case("radd_small" if small else "radd", seed, BF16, lens, clen, boff,
-                          Hk=8, D=128, P=128, L=4, layer=3)
+    return make_radd_case(_kv("radd_small" if small else "radd", cache_dtype), seed, BF16, lens,
+                          clen, boff, Hk=8, D=128, P=128, L=4, layer=3, cache_dtype=cache_dtype)
 
 
-def bshd(seed: int = 6, small: bool = False) -> Case:
+def bshd(seed: int = 6, small: bool = False, cache_dtype: Optional[str] = None) -> Case:
     """Padded continuous batching on the prefill shapes: every sequence padded
     to the longest length the prefill batch draws (2048), valid lengths drawn
     as the prefill lengths are, a bf16 table (the op's dtype)."""
@@ -597,15 +604,27 @@ def bshd(seed: int = 6, small: bool = False) -> Case:
         B, S = 4, 300
         valid = prng.integers(seed, S_LENS, B, 0, S)
         clen = prng.integers(seed, S_CLEN, B, 0, 500)
-        return make_bshd_case("bshd_small", seed, BF16, valid, S, clen, Hq=32, Hk=8, D=128,
-                              rope_dim=128, interleaved=False, theta=5e5, max_seq_len=1024,
-                              capacity=1024, L=2, layer=1)
+        return make_bshd_case(_kv("bshd_small", cache_dtype), seed, BF16, valid, S, clen, Hq=32,
+                              Hk=8, D=128, rope_dim=128, interleaved=False, theta=5e5,
+                              max_seq_len=1024, capacity=1024, L=2, layer=1,
+                              cache_dtype=cache_dtype)
     B, S = 8, 2048
     valid = prng.integers(seed, S_LENS, B, 128, S)
-    return make_bshd_case("bshd", seed, BF16, valid, S, np.zeros(B, np.int64), Hq=32, Hk=8,
-                          D=128, rope_dim=128, interleaved=False, theta=5e5, max_seq_len=8192,
-                          capacity=8192, L=1, layer=0)
+    return make_bshd_case(_kv("bshd", cache_dtype), seed, BF16, valid, S, np.zeros(B, np.int64),
+                          Hq=32, Hk=8, D=128, rope_dim=128, interleaved=False, theta=5e5,
+                          max_seq_len=8192, capacity=8192, L=1, layer=0, cache_dtype=cache_dtype)
+
+
+def _with_cache(fn, cache_dtype):
+    def make(seed: Optional[int] = None, small: bool = False) -> Case:
+        return fn(small=small, cache_dtype=cache_dtype) if seed is None else \
+            fn(seed, small=small, cache_dtype=cache_dtype)
+    make.__name__ = f"{fn.__name__}_{cache_dtype}"
+    return make
 
 
 WORKLOADS = {"tiny_fp32": tiny_fp32, "prefill": prefill, "decode": decode, "dual": dual,
              "radd": radd, "bshd": bshd}
+# the same workloads over FP8 caches (bf16 inputs; f32 scales, one per row)
+WORKLOADS.update({f"{k}_fp8": _with_cache(WORKLOADS[k], FP8)
+                  for k in ("prefill", "decode", "dual", "radd", "bshd")})

@@ -1,7 +1,8 @@
 """Device side of the tests and the benchmark: put a synthetic case on the GPU
 and run it through the C ABI (via the thin Python binding).
 
-Buffers hold raw bits (int16 for bf16 and f16, int32 for fp32).  Output buffers and
+Buffers hold raw bits (int16 for bf16 and f16, int32 for fp32, uint8 for
+FP8 cache codes; FP8 scales as int32 / int16 bits of f32 / bf16).  Output buffers and
 cache pools start as the signalling-NaN sentinel so that any stray write,
 or any float round trip of a copied value, shows up in a bit comparison.
 ``q_output`` buffers carry GUARD sentinel rows before and after the rows
@@ -19,25 +20,29 @@ import qk_rope_paged_amd as qrp
 from synth import cases as sc
 
 GUARD = 2
-TORCH_BITS = {sc.F32: torch.int32, sc.BF16: torch.int16, sc.F16: torch.int16}
-QRP_DT = {sc.F32: qrp.QRP_F32, sc.BF16: qrp.QRP_BF16, sc.F16: qrp.QRP_F16}
+TORCH_BITS = {sc.F32: torch.int32, sc.BF16: torch.int16, sc.F16: torch.int16, sc.FP8: torch.uint8}
+QRP_DT = {sc.F32: qrp.QRP_F32, sc.BF16: qrp.QRP_BF16, sc.F16: qrp.QRP_F16, sc.FP8: qrp.QRP_FP8}
 
 
 def bits_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
     a = np.ascontiguousarray(a)
+    if a.dtype == np.uint8:
+        return torch.from_numpy(a).to(device)
     signed = a.view(np.int16 if a.dtype == np.uint16 else np.int32)
     return torch.from_numpy(signed).to(device)
 
 
 def sentinel_int(dtype: str) -> int:
     s = int(sc.SENTINEL[dtype])
+    if dtype == sc.FP8:
+        return s                                   # a uint8 tensor
     bits = 32 if dtype == sc.F32 else 16
     return s - (1 << bits) if s >= 1 << (bits - 1) else s
 
 
 def to_numpy_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
     a = t.cpu().numpy()
-    return a.view(np.uint32 if dtype == sc.F32 else np.uint16)
+    return a.view(sc.BITS_DTYPE[dtype])
 
 
 @dataclass
@@ -47,6 +52,7 @@ class DeviceCache:
     cache_lengths: torch.Tensor
     lookup_table: torch.Tensor
     desc: qrp.PagedCache = None
+    scales: torch.Tensor = None        # FP8 caches: flat scale bits
 
     def pages(self, page_ids: np.ndarray) -> np.ndarray:
         """Copy the given pages back, shaped like the host pool."""
@@ -54,6 +60,15 @@ class DeviceCache:
         idx = torch.from_numpy(np.asarray(page_ids, dtype=np.int64)).to(self.pool.device)
         sel = view.index_select(0, idx)
         return to_numpy_bits(sel, self.host.dtype).reshape((len(page_ids),) + self.host.shape[1:])
+
+    def scale_pages(self, page_ids: np.ndarray) -> np.ndarray:
+        """FP8 caches: the scales of the given pages, shaped like the host's."""
+        h = self.host
+        per_page = int(np.prod(h.scale_shape[1:]))
+        view = self.scales.view(h.num_pages, per_page)
+        idx = torch.from_numpy(np.asarray(page_ids, dtype=np.int64)).to(self.scales.device)
+        sel = view.index_select(0, idx)
+        return to_numpy_bits(sel, h.scale_dtype).reshape((len(page_ids),) + h.scale_shape[1:])
 
 
 def upload_cache(c: sc.PagedCache, device="cuda") -> DeviceCache:
@@ -67,14 +82,23 @@ def upload_cache(c: sc.PagedCache, device="cuda") -> DeviceCache:
     lens = torch.from_numpy(c.cache_lengths.astype(np.uint32).view(np.int32)).to(device)
     tab = torch.from_numpy(np.ascontiguousarray(c.lookup_table, dtype=np.uint32).view(np.int32)).to(device)
     st = c.strides
-    desc = qrp.PagedCache(blocks=pool, dtype=QRP_DT[c.dtype], num_kv_heads=c.num_kv_heads,
+    scales, extra = None, {}
+    if c.dtype == sc.FP8:
+        scales = bits_tensor(c.materialize_scales().reshape(-1), device)
+        sst = c.scale_strides
+        extra = dict(scales=scales, scale_dtype=QRP_DT[c.scale_dtype],
+                     scale_page_stride=sst["s_page_stride"], scale_plane_stride=sst["s_plane_stride"],
+                     scale_layer_stride=sst["s_layer_stride"], scale_slot_stride=sst["s_slot_stride"],
+                     scale_head_stride=sst["s_head_stride"])
+    desc = qrp.PagedCache(**extra, blocks=pool, dtype=QRP_DT[c.dtype], num_kv_heads=c.num_kv_heads,
                           head_dim=c.head_dim, page_size=c.page_size, num_layers=c.num_layers,
                           kv_planes=c.kv_planes, num_pages=c.num_pages,
                           page_stride=st["page_stride"], plane_stride=st["plane_stride"],
                           layer_stride=st["layer_stride"], slot_stride=st["slot_stride"],
                           head_stride=st["head_stride"], cache_lengths=lens, lookup_table=tab,
                           cache_batch=c.cache_batch, max_pages_per_seq=c.max_pages_per_seq)
-    return DeviceCache(host=c, pool=pool, cache_lengths=lens, lookup_table=tab, desc=desc)
+    return DeviceCache(host=c, pool=pool, cache_lengths=lens, lookup_table=tab, desc=desc,
+                       scales=scales)
 
 
 @dataclass
@@ -116,9 +140,10 @@ def upload(case: sc.Case, device="cuda") -> DeviceCase:
                else [b.q_out_row_stride for b in case.bands])
     if case.op == "bshd":
         dc.valid = torch.from_numpy(np.asarray(case.lengths, np.uint32).view(np.int32)).to(device)
+    qdt = case.q_dtype
     for s in strides:
-        dc.q_out.append(torch.full((case.T + 2 * GUARD, max(s, 1)), sentinel_int(case.dtype),
-                                   dtype=TORCH_BITS[case.dtype], device=device))
+        dc.q_out.append(torch.full((case.T + 2 * GUARD, max(s, 1)), sentinel_int(qdt),
+                                   dtype=TORCH_BITS[qdt], device=device))
     for b in case.bands:
         dc.gammas.append((None if b.q_gamma is None else bits_tensor(b.q_gamma, device),
                           None if b.k_gamma is None else bits_tensor(b.k_gamma, device)))
@@ -149,7 +174,8 @@ def run(dc: DeviceCase, stream=None, raise_on_error=True, op=None, prepare=False
     if op == "store":
         return qrp.rope_split_store_paged(
             dc.buf, dt, c.T, c.row_stride, c.n_q_heads, dc.offsets, c.batch, rope_of(dc),
-            dc.caches[0].desc, c.layer_idx, dc.q_out_rows(0), dt, c.q_out_row_stride, **kw)
+            dc.caches[0].desc, c.layer_idx, dc.q_out_rows(0), QRP_DT[c.q_dtype],
+            c.q_out_row_stride, **kw)
     if op == "norm":
         return qrp.qk_rmsnorm_rope_paged(
             dc.buf, dt, c.T, c.row_stride, band_of(dc, 0), c.weight_offset,

@@ -8,6 +8,11 @@ The bar:
     fp32:  |gpu - v| <= 1e-5 * max(|v|, m)
     bf16:  |gpu - v| <= ulps * ulp_bf16(max(|v|, 2^-8 * m))
     f16:   |gpu - v| <= ulps * ulp_f16(max(|v|, 2^-11 * m))
+    FP8 cache rows (codes c, scale s): |c * s - v| <= s * ulp_e4m3(|v| / s)
+           (+ 2^-8 of the row's largest |v| with bf16 scales, whose rounding
+           can clamp the top code), and s within 2^-20 (f32) or one bf16 ulp
+           of the oracle's scale; V rows and radd rows bit for bit (the same
+           binary32 decisions on the same values)
   with v the oracle's unrounded value and m the length of v's RoPE pair
   (|v| for unrotated elements).  The pair-length floor is there because
   x*cos - y*sin can cancel: a bound relative to |v| alone would demand more
@@ -58,6 +63,34 @@ def check_rows(gpu: np.ndarray, ora: np.ndarray, exact: np.ndarray, mag: np.ndar
     rep[what + "_n"] = int(g.size)
 
 
+def check_fp8_rows(codes: np.ndarray, scales: np.ndarray, ora_codes: np.ndarray,
+                   ora_scales: np.ndarray, exact: np.ndarray, scale_dtype: str, what: str,
+                   rep: Report):
+    """FP8 rows [N, D] with their scale bits [N]: each dequantized value within
+    one E4M3 step (at the GPU's own scale) of the oracle's unrounded value,
+    each scale close to the oracle's."""
+    if codes.size == 0:
+        return
+    s = sc.bits_to_f64(scales, scale_dtype)[:, None]
+    so = sc.bits_to_f64(ora_scales, scale_dtype)[:, None]
+    deq = brute.e4m3_to_f64(codes) * s
+    safe = np.where(s > 0, s, 1.0)
+    tol = s * brute.ulp_e4m3(np.abs(exact) / safe)
+    if scale_dtype == sc.BF16:
+        tol = tol + 2.0 ** -8 * np.max(np.abs(exact), axis=1, keepdims=True)
+    ok = np.abs(deq - exact) <= tol
+    if not ok.all():
+        bad = np.argwhere(~ok)[:5]
+        det = [(int(r), int(c), float(deq[r, c]), float(exact[r, c]), float(s[r, 0]))
+               for r, c in bad]
+        raise AssertionError(f"{what}: {int((~ok).sum())} FP8 values out of tolerance, e.g. {det}")
+    srel = 2.0 ** -20 if scale_dtype == sc.F32 else 2.0 ** -7
+    sok = np.abs(s - so) <= srel * np.maximum(so, 1e-30)
+    assert sok.all(), f"{what}: scales differ from the oracle's: {s[~sok][:5]} vs {so[~sok][:5]}"
+    rep[what + "_code_exact_rate"] = float((codes == ora_codes).mean())
+    rep[what + "_n"] = int(codes.size)
+
+
 def _copy_cols(D: int, R: int, normed: bool) -> np.ndarray:
     cols = np.zeros(D, dtype=bool)
     if not normed:
@@ -84,17 +117,19 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
     assert res.status == 0, f"oracle status {res.status}"
     rep = Report()
     dt = case.dtype
+    qdt = case.q_dtype
     T = case.T
-    sent = sc.SENTINEL[dt]
     # the input buffer is unchanged
     if case.buf.size:
         assert np.array_equal(gh.to_numpy_bits(dc.buf, dt), case.buf), "input buffer modified"
     # ---- Q outputs ----
     for qi, ci, Hq, qn, kn, hv in bands_of(case):
         D = case.caches[ci].head_dim
-        full = gh.to_numpy_bits(dc.q_out[qi], dt)
+        full = gh.to_numpy_bits(dc.q_out[qi], qdt)
         g = gh.GUARD
-        assert np.all(full[:g] == sent) and np.all(full[g + T:] == sent), "q_output guard rows written"
+        qsent = sc.SENTINEL[qdt]
+        assert np.all(full[:g] == qsent) and np.all(full[g + T:] == qsent), \
+            "q_output guard rows written"
         rows = full[g:g + T]
         ora = res.q_out[qi]
         stride = ora.shape[1]
@@ -109,7 +144,7 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
             tr = res.traces[qi]
             check_rows(rows[:, :Hq * D].reshape(-1, D), ora[:, :Hq * D].reshape(-1, D),
                        tr["q_exact"].reshape(-1, D), tr["q_mag"].reshape(-1, D),
-                       _copy_cols(D, case.rope_dim, qn), dt, ulps, f"q{qi}", rep)
+                       _copy_cols(D, case.rope_dim, qn), qdt, ulps, f"q{qi}", rep)
     # ---- caches ----
     for ci, dcache in enumerate(dc.caches):
         host = dcache.host
@@ -119,8 +154,12 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
             pages = np.arange(host.num_pages)
         gpu_pool = dcache.pages(pages)
         D = host.head_dim
+        fp8 = host.dtype == sc.FP8
         g_flat = gpu_pool.reshape(-1).copy()
         o_flat = ora_pool.reshape(-1).copy()
+        if fp8:
+            gs_flat = dcache.scale_pages(pages).reshape(-1).copy()
+            os_flat = res.scales[ci].reshape(-1).copy()
         for qi, cj, Hq, qn, kn, hv in bands_of(case):
             if cj != ci or T == 0:
                 continue
@@ -128,12 +167,25 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
             koff = tr["k_row_off"].reshape(-1)
             live = koff >= 0                       # rows the op wrote (bshd: real rows only)
             idx = koff[live][:, None] + np.arange(D)[None, :]
-            check_rows(g_flat[idx], o_flat[idx], tr["k_exact"].reshape(-1, D)[live],
-                       tr["k_mag"].reshape(-1, D)[live], _copy_cols(D, case.rope_dim, kn), dt,
-                       ulps, f"k{qi}", rep)
+            if fp8:
+                soff = tr["k_scale_off"].reshape(-1)[live]
+                check_fp8_rows(g_flat[idx], gs_flat[soff], o_flat[idx], os_flat[soff],
+                               tr["k_exact"].reshape(-1, D)[live], host.scale_dtype, f"k{qi}",
+                               rep)
+                gs_flat[soff] = 0
+                os_flat[soff] = 0
+            else:
+                check_rows(g_flat[idx], o_flat[idx], tr["k_exact"].reshape(-1, D)[live],
+                           tr["k_mag"].reshape(-1, D)[live], _copy_cols(D, case.rope_dim, kn),
+                           dt, ulps, f"k{qi}", rep)
             # written K rows are checked: blank them before the bitwise comparison
             g_flat[idx] = 0
             o_flat[idx] = 0
+        if fp8 and not np.array_equal(gs_flat, os_flat):
+            bad = np.flatnonzero(gs_flat != os_flat)
+            raise AssertionError(f"cache {ci}: {len(bad)} scales differ outside the checked K "
+                                 f"rows, first at {bad[:5]} gpu={gs_flat[bad[:5]]} "
+                                 f"oracle={os_flat[bad[:5]]}")
         if not np.array_equal(g_flat, o_flat):
             bad = np.flatnonzero(g_flat != o_flat)
             raise AssertionError(f"cache {ci}: {len(bad)} elements differ outside the checked K "
@@ -141,7 +193,7 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
                                  f"gpu={g_flat[bad[:5]]} oracle={o_flat[bad[:5]]}")
         if res.page_maps[ci] is not None and untouched_pages:
             # pages the batch does not touch must hold nothing but the sentinel
-            n_dev = int((dcache.pool != gh.sentinel_int(dt)).sum().item())
-            n_touched = int((gpu_pool != sent).sum())
+            n_dev = int((dcache.pool != gh.sentinel_int(host.dtype)).sum().item())
+            n_touched = int((gpu_pool != sc.SENTINEL[host.dtype]).sum())
             assert n_dev == n_touched, "a page outside the batch was written"
     return rep

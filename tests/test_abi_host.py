@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(qrp.EXPORTS)
-    assert qrp.abi_version() == 1
+    assert qrp.abi_version() == 2
 
 
 def test_one_hip_runtime_in_process():
@@ -74,7 +74,7 @@ def _store(cache=None, rope=None, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), qrp.QRP_EUNSUPPORTED),
-    (dict(q_out_dtype=qrp.QRP_F32), qrp.QRP_EUNSUPPORTED),
+    (dict(q_out_dtype=7), qrp.QRP_EUNSUPPORTED),
     (dict(batch_size=0), qrp.QRP_EINVAL),
     (dict(input_row_offsets=None), qrp.QRP_EINVAL),
     (dict(qkv=None), qrp.QRP_EINVAL),
@@ -103,8 +103,8 @@ def _store(cache=None, rope=None, **kw):
     (dict(rope=_rope(freq_dtype=9)), qrp.QRP_EUNSUPPORTED),
     (dict(rope=_rope(freqs_cis=FAKE + 8, freq_dtype=qrp.QRP_BF16)), qrp.QRP_EALIGN),
     (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_F16), qrp.QRP_EUNSUPPORTED),   # cache is bf16
-    (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_BF16, cache=_cache(dtype=qrp.QRP_F16)),
-     qrp.QRP_EUNSUPPORTED),
+    (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_BF16, cache=_cache(dtype=qrp.QRP_F16),
+          q_out_row_stride=32 * 128 + 4), qrp.QRP_EALIGN),
     (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_F16, cache=_cache(dtype=qrp.QRP_F16),
           rope=_rope(rope_dim=8)), qrp.QRP_EUNSUPPORTED),
     (dict(dtype=qrp.QRP_F16, q_out_dtype=qrp.QRP_F16, cache=_cache(dtype=qrp.QRP_F16),
@@ -142,7 +142,8 @@ def _dual(main=None, index=None, **kw):
 def test_dual_band_geometry_and_argument_errors():
     assert _dual(index=_band(cache=_cache(head_dim=64, num_kv_heads=1), n_q_heads=16)) == \
         qrp.QRP_EGEOMETRY
-    assert _dual(index=_band(cache=_cache(dtype=qrp.QRP_F32), n_q_heads=16)) == qrp.QRP_EGEOMETRY
+    assert _dual(index=_band(cache=_cache(dtype=qrp.QRP_F32), n_q_heads=16)) == \
+        qrp.QRP_EUNSUPPORTED                                           # cache dtype != op dtype
     assert _dual(main=_band(k_col=64 * 128, v_col=72 * 128)) == qrp.QRP_EUNSUPPORTED
     assert _dual(main=_band(q_col=40 * 128)) == qrp.QRP_EINVAL          # Q past the row end
     assert _dual(main=_band(q_gamma=FAKE + 2)) == qrp.QRP_EALIGN
@@ -271,3 +272,35 @@ def test_bshd_empty_grid_returns_ok_without_touching_anything():
     assert _bshd(batch_size=0, q_proj=None, output=None, valid_lengths=None) == qrp.QRP_OK
     assert _bshd(seq_len=0, q_proj=None, output=None, valid_lengths=None) == qrp.QRP_OK
 
+
+
+def _fp8_cache(**kw):
+    d = dict(dtype=qrp.QRP_FP8, scales=FAKE + (1 << 20), scale_dtype=qrp.QRP_F32,
+             scale_page_stride=2 * 2 * 128 * 8, scale_plane_stride=2 * 128 * 8,
+             scale_layer_stride=128 * 8, scale_slot_stride=8, scale_head_stride=1)
+    d.update(kw)
+    return _cache(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cache=_fp8_cache(scales=None)), qrp.QRP_EINVAL),
+    (dict(cache=_fp8_cache(scale_dtype=qrp.QRP_F16)), qrp.QRP_EUNSUPPORTED),
+    (dict(cache=_fp8_cache(scale_dtype=qrp.QRP_FP8)), qrp.QRP_EUNSUPPORTED),
+    (dict(cache=_fp8_cache(scales=FAKE + 2)), qrp.QRP_EALIGN),
+    (dict(cache=_fp8_cache(scale_slot_stride=-8)), qrp.QRP_EINVAL),
+    (dict(cache=_fp8_cache(head_stride=100)), qrp.QRP_EALIGN),
+    (dict(cache=_fp8_cache(), qkv=FAKE + 4), qrp.QRP_EALIGN),
+    (dict(cache=_fp8_cache(), q_out_dtype=qrp.QRP_FP8), qrp.QRP_EUNSUPPORTED),
+    (dict(cache=_fp8_cache(), q_out_dtype=qrp.QRP_F32, q_out_row_stride=32 * 128 + 2),
+     qrp.QRP_EALIGN),
+])
+def test_fp8_cache_and_q_dtype_argument_errors(kw, code):
+    assert _store(**kw) == code
+    assert qrp.last_error() != ""
+
+
+def test_dual_band_mixed_fp8_and_plain_caches_is_unsupported():
+    idx_cache = _fp8_cache(num_kv_heads=1, kv_planes=1, page_stride=128 * 128,
+                           plane_stride=128 * 128, layer_stride=128 * 128, slot_stride=128)
+    assert _dual(index=_band(cache=idx_cache, q_col=80 * 128, n_q_heads=16,
+                             q_out_row_stride=16 * 128)) == qrp.QRP_EUNSUPPORTED
