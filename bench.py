@@ -44,8 +44,9 @@ METRIC = "effective HBM GB/s & tokens/s of fused RoPE+paged-store; % of HBM peak
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MALL_BYTES = 256 << 20         # Infinity Cache
 KERNEL_NAME = "band_kernel"
-KERNEL_SOURCES = ("qk_rope_paged_amd/csrc/kernels.hip", "qk_rope_paged_amd/csrc/engine.hpp",
-                  "qk_rope_paged_amd/csrc/abi.cpp")
+KERNEL_SOURCES = ("qk_rope_paged_amd/csrc/band_kernel.hpp", "qk_rope_paged_amd/csrc/kernels.hip",
+                  "qk_rope_paged_amd/csrc/kernels_fp8.hip", "qk_rope_paged_amd/csrc/kernels_qout.hip",
+                  "qk_rope_paged_amd/csrc/engine.hpp", "qk_rope_paged_amd/csrc/abi.cpp")
 
 
 def log(*a):

@@ -125,6 +125,11 @@ qrp::CacheDesc make_cache(const qrp_paged_cache* c, uint32_t layer_idx) {
     d.page_shift = s;
   }
   d.cache_batch = c->cache_batch;
+  return d;
+}
+
+qrp::ScaleDesc make_scales(const qrp_paged_cache* c, uint32_t layer_idx) {
+  qrp::ScaleDesc d{};
   if (c->dtype == QRP_FP8) {
     d.scales = c->scales;
     d.s_page_stride = c->scale_page_stride;
@@ -206,7 +211,7 @@ int32_t launch(const Builder& b, bool interleaved, bool radd, void* stream, bool
   qrp::LaunchSpec s{};
   s.dtype = b.dtype;
   s.q_dtype = q_dtype < 0 ? b.dtype : q_dtype;
-  s.cache_fp8 = b.a.cache[0].scales != nullptr;
+  s.cache_fp8 = b.a.scale[0].scales != nullptr;
   s.head_dim = b.head_dim;
   s.interleaved = interleaved;
   s.radd = radd;
@@ -318,6 +323,7 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
   b.head_dim = cache->head_dim;
   b.rpp = qrp::rows_per_pass(dtype, cache->head_dim);
   b.a.cache[0] = make_cache(cache, layer_idx);
+  b.a.scale[0] = make_scales(cache, layer_idx);
   b.a.ncache = 1;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
@@ -359,6 +365,7 @@ int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq
   b.head_dim = band->cache->head_dim;
   b.rpp = qrp::rows_per_pass(dtype, b.head_dim);
   b.a.cache[0] = make_cache(band->cache, layer_idx);
+  b.a.scale[0] = make_scales(band->cache, layer_idx);
   b.a.ncache = 1;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
@@ -404,7 +411,9 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
   b.head_dim = main_band->cache->head_dim;
   b.rpp = qrp::rows_per_pass(dtype, b.head_dim);
   b.a.cache[0] = make_cache(main_band->cache, layer_idx);
+  b.a.scale[0] = make_scales(main_band->cache, layer_idx);
   b.a.cache[1] = make_cache(index_band->cache, layer_idx);
+  b.a.scale[1] = make_scales(index_band->cache, layer_idx);
   b.a.ncache = 2;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
@@ -444,6 +453,7 @@ int32_t kv_cache_radd(const void* a, int32_t dtype, uint32_t total_rows, uint64_
   b.head_dim = cache->head_dim;
   b.rpp = qrp::rows_per_pass(dtype, b.head_dim);
   b.a.cache[0] = make_cache(cache, layer_idx);
+  b.a.scale[0] = make_scales(cache, layer_idx);
   b.a.ncache = 1;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
@@ -484,6 +494,7 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
   b.head_dim = cache->head_dim;
   b.rpp = qrp::rows_per_pass(dtype, cache->head_dim);
   b.a.cache[0] = make_cache(cache, layer_idx);
+  b.a.scale[0] = make_scales(cache, layer_idx);
   b.a.ncache = 1;
   b.a.offsets = nullptr;
   b.a.batch = batch_size;

@@ -268,7 +268,7 @@ __device__ __forceinline__ uint4 ld_fp8_chunk(const uint8_t* p) {
 }
 
 // The scale of one FP8 cache row (binary32 or bf16 storage).
-__device__ __forceinline__ float load_scale(const CacheDesc& cd, int64_t idx) {
+__device__ __forceinline__ float load_scale(const ScaleDesc& cd, int64_t idx) {
   if (cd.scale_bf16)
     return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t*>(cd.scales)[idx]) << 16);
   return reinterpret_cast<const float*>(cd.scales)[idx];
@@ -309,7 +309,7 @@ __device__ __forceinline__ float row_max(float v) {
 // lane's two chunks at row + c*E and, from the row's first lane, the scale.
 template <int LPR, int E>
 __device__ __forceinline__ void quantize_store(float* v0, float* v1, Fp8* row, uint32_t c0,
-                                               uint32_t c1, const CacheDesc& cd, int64_t sidx,
+                                               uint32_t c1, const ScaleDesc& cd, int64_t sidx,
                                                bool active, bool first) {
   float m = 0.f;
 #pragma unroll
@@ -617,8 +617,8 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       pos[ci] = (uint32_t)p64;
       base[ci] = (int64_t)page * cd.page_stride + cd.layer_off + (int64_t)slot * cd.slot_stride;
       if constexpr (QUANT)
-        sbase[ci] = (int64_t)page * cd.s_page_stride + cd.s_layer_off +
-                    (int64_t)slot * cd.s_slot_stride;
+        sbase[ci] = (int64_t)page * a.scale[ci].s_page_stride + a.scale[ci].s_layer_off +
+                    (int64_t)slot * a.scale[ci].s_slot_stride;
     }
   }
   if (!ok) return;  // out-of-range metadata: this token writes nothing
@@ -643,8 +643,9 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
           const uint8_t* src = reinterpret_cast<const uint8_t*>(cd.blocks) + roff;
           r0 = ld_fp8_chunk<E>(src + c0 * E);
           r1 = ld_fp8_chunk<E>(src + c1 * E);
-          rsc[p] = load_scale(cd, sbase[sd.cache] + (int64_t)sd.plane * cd.s_plane_stride +
-                                      (int64_t)h * cd.s_head_stride);
+          const ScaleDesc& sdsc = a.scale[sd.cache];
+          rsc[p] = load_scale(sdsc, sbase[sd.cache] + (int64_t)sd.plane * sdsc.s_plane_stride +
+                                        (int64_t)h * sdsc.s_head_stride);
         } else {
           const T* src = reinterpret_cast<const T*>(cd.blocks) + roff;
           r0 = ld16s(src + c0 * E);
@@ -704,9 +705,9 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
               vc0, vc1,
               reinterpret_cast<Fp8*>(cd.blocks) + base[sd.cache] +
                   (int64_t)sd.plane * cd.plane_stride + (int64_t)h * cd.head_stride,
-              c0, c1, cd,
-              sbase[sd.cache] + (int64_t)sd.plane * cd.s_plane_stride +
-                  (int64_t)h * cd.s_head_stride,
+              c0, c1, a.scale[sd.cache],
+              sbase[sd.cache] + (int64_t)sd.plane * a.scale[sd.cache].s_plane_stride +
+                  (int64_t)h * a.scale[sd.cache].s_head_stride,
               active, j == 0);
           continue;
         } else {
@@ -734,9 +735,9 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
                 v0, v1,
                 reinterpret_cast<Fp8*>(cd.blocks) + base[sd.cache] +
                     (int64_t)sd.plane * cd.plane_stride + (int64_t)h * cd.head_stride,
-                c0, c1, cd,
-                sbase[sd.cache] + (int64_t)sd.plane * cd.s_plane_stride +
-                    (int64_t)h * cd.s_head_stride,
+                c0, c1, a.scale[sd.cache],
+                sbase[sd.cache] + (int64_t)sd.plane * a.scale[sd.cache].s_plane_stride +
+                    (int64_t)h * a.scale[sd.cache].s_head_stride,
                 active, j == 0);
             continue;
           } else {
@@ -830,9 +831,9 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
                   v0, v1,
                   reinterpret_cast<Fp8*>(cd.blocks) + base[sd.cache] +
                       (int64_t)sd.plane * cd.plane_stride + (int64_t)h * cd.head_stride,
-                  c0, c1, cd,
-                  sbase[sd.cache] + (int64_t)sd.plane * cd.s_plane_stride +
-                      (int64_t)h * cd.s_head_stride,
+                  c0, c1, a.scale[sd.cache],
+                  sbase[sd.cache] + (int64_t)sd.plane * a.scale[sd.cache].s_plane_stride +
+                      (int64_t)h * a.scale[sd.cache].s_head_stride,
                   active, j == 0);
               continue;
             }

@@ -81,7 +81,12 @@ struct CacheDesc {
   uint32_t page_size;
   uint32_t page_shift;      // log2(page_size) when a power of two, else 0xFFFFFFFF
   uint32_t cache_batch;
-  // FP8 caches: one scale per (page, plane, layer, slot, head) row
+};
+
+// FP8 caches: one scale per (page, plane, layer, slot, head) row.  Kept
+// apart from CacheDesc (at the end of the kernel arguments) so that the
+// fields every launch reads keep compact, fixed offsets.
+struct ScaleDesc {
   void* scales;
   int64_t s_page_stride, s_plane_stride, s_slot_stride, s_head_stride;
   int64_t s_layer_off;      // layer_idx * scale layer stride
@@ -117,6 +122,7 @@ struct BandArgs {
   // valid length pass through.  Unused by the ragged ops.
   const uint32_t* valid_lengths;
   uint32_t seq_len;
+  ScaleDesc scale[kMaxCaches];
 };
 
 enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8 = 3 };
