@@ -168,8 +168,9 @@ struct Builder {
     ++a.nseg;
   }
 
-  // split tokens x passes into waves and blocks
-  int32_t finish(uint32_t total_tokens, bool radd) {
+  // split tokens x passes into waves and blocks (one pass per wave: radd, and
+  // the padded grid, whose waves resolve their row with one division)
+  int32_t finish(uint32_t total_tokens, bool radd, bool one_pass = false) {
     bool norm = false;
     for (uint32_t s = 0; s < a.nseg; ++s) norm = norm || a.seg[s].gamma != nullptr;
     const uint32_t npmax = qrp::max_passes(radd, norm);
@@ -178,9 +179,10 @@ struct Builder {
     const int forced = env_int("QRP_PASSES_PER_WAVE", 0);
     if (forced > 0) {
       ppg = std::min<uint32_t>((uint32_t)forced, std::min(npmax, ppt));
-    } else if (radd) {
+    } else if (radd || one_pass) {
       // a radd pass already carries two loads per chunk (a and the cache
-      // row): one pass per wave measured fastest
+      // row), and a padded-grid wave's metadata is one division: one pass
+      // per wave measured fastest for both
       ppg = 1;
     } else {
       // enough waves to cover every SIMD a few times over: shrink the group
@@ -508,7 +510,7 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
   b.a.multiply_before_cast = 1;
   b.add_seg(qrp::SEG_Q, q_proj, (int64_t)row, output, (int64_t)row, nullptr, 0.f, n_q_heads, 0, 0);
   b.add_seg(qrp::SEG_K_INPLACE, nullptr, 0, nullptr, 0, nullptr, 0.f, cache->num_kv_heads, 0, 0);
-  if ((st = b.finish((uint32_t)tokens, false))) return st;
+  if ((st = b.finish((uint32_t)tokens, false, true))) return st;
   return launch(b, rope->interleaved != 0, false, stream, true);
 }
 

@@ -850,13 +850,25 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   }
 }
 
-template <typename T, typename QT, typename CT, int D, bool IL, bool RADD, bool NORM, bool BSHD>
-int launch_t(const BandArgs& a, void* stream) {
-  constexpr int NPMAX = RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : kMaxPassesStore);
+template <typename T, typename QT, typename CT, int D, bool IL, int NPMAX, bool RADD, bool NORM,
+          bool BSHD>
+int launch_np(const BandArgs& a, void* stream) {
   const uint32_t grid = a.per_xcd ? a.per_xcd * kXcds : a.n_blocks;
   hipLaunchKernelGGL((band_kernel<T, QT, CT, D, IL, NPMAX, RADD, NORM, BSHD>), dim3(grid),
                      dim3(64 * a.waves_per_block), 0, reinterpret_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
+}
+
+// Store kernels built for one pass per wave hold fewer registers (more
+// waves resident); they run whenever the launch gives each wave one pass.
+template <typename T, typename QT, typename CT, int D, bool IL, bool RADD, bool NORM, bool BSHD>
+int launch_t(const BandArgs& a, void* stream) {
+  constexpr int NPMAX = RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : kMaxPassesStore);
+  if constexpr (!RADD && !NORM && NPMAX > 1) {
+    if (a.passes_per_group == 1)
+      return launch_np<T, QT, CT, D, IL, 1, RADD, NORM, BSHD>(a, stream);
+  }
+  return launch_np<T, QT, CT, D, IL, NPMAX, RADD, NORM, BSHD>(a, stream);
 }
 
 template <typename T, typename QT, typename CT, bool IL, bool RADD, bool NORM, bool BSHD>
