@@ -99,21 +99,21 @@ def load() -> ctypes.CDLL:
     lib.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.orc_e4m3_to_double.restype = ctypes.c_double
     lib.orc_rope_split_store_paged.argtypes = [P, I32, U32, U64, U32, P, U32, P, U32, U32, I32,
-                                               ctypes.POINTER(OrcCache), U32, P, I32, U64,
+                                               I32, ctypes.POINTER(OrcCache), U32, P, I32, U64,
                                                ctypes.POINTER(OrcTrace)]
     lib.orc_rope_split_store_paged.restype = I32
     lib.orc_qk_rmsnorm_rope_paged.argtypes = [P, I32, U32, U64, ctypes.POINTER(OrcBand), F, I32,
-                                              P, U32, P, U32, U32, I32, U32,
+                                              P, U32, P, U32, U32, I32, I32, U32,
                                               ctypes.POINTER(OrcTrace)]
     lib.orc_qk_rmsnorm_rope_paged.restype = I32
     lib.orc_dual_band.argtypes = [P, I32, U32, U64, ctypes.POINTER(OrcBand),
-                                  ctypes.POINTER(OrcBand), F, I32, P, U32, P, U32, U32, I32, U32,
-                                  ctypes.POINTER(OrcTrace), ctypes.POINTER(OrcTrace)]
+                                  ctypes.POINTER(OrcBand), F, I32, P, U32, P, U32, U32, I32, I32,
+                                  U32, ctypes.POINTER(OrcTrace), ctypes.POINTER(OrcTrace)]
     lib.orc_dual_band.restype = I32
     lib.orc_kv_cache_radd.argtypes = [P, I32, U32, U64, P, U32, U32, ctypes.POINTER(OrcCache),
                                       U32, ctypes.POINTER(OrcTrace)]
     lib.orc_kv_cache_radd.restype = I32
-    lib.orc_fused_qk_rope_bshd.argtypes = [P, I32, U32, U32, U32, P, P, U32, U32, I32,
+    lib.orc_fused_qk_rope_bshd.argtypes = [P, I32, U32, U32, U32, P, P, U32, U32, I32, I32,
                                            ctypes.POINTER(OrcCache), U32, P,
                                            ctypes.POINTER(OrcTrace)]
     lib.orc_fused_qk_rope_bshd.restype = I32
@@ -255,8 +255,8 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
         t0 = time.perf_counter()
         st = lib.orc_rope_split_store_paged(
             _ptr(buf), dt, T, case.row_stride, Hq, _ptr(off), case.batch, _ptr(freqs),
-            case.max_seq_len, case.rope_dim, int(case.interleaved), ctypes.byref(ocaches[0]),
-            case.layer_idx, _ptr(q_out), _DT[qdt], case.q_out_row_stride,
+            case.max_seq_len, case.rope_dim, int(case.interleaved), int(case.rope_tail),
+            ctypes.byref(ocaches[0]), case.layer_idx, _ptr(q_out), _DT[qdt], case.q_out_row_stride,
             ctypes.byref(otr) if otr is not None else None)
         res.q_out.append(q_out)
         res.traces.append(tr)
@@ -285,13 +285,14 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
                 _ptr(buf), dt, T, case.row_stride, ctypes.byref(obands[0]),
                 case.weight_offset, int(case.multiply_before_cast), _ptr(off), case.batch,
                 _ptr(freqs), case.max_seq_len, case.rope_dim, int(case.interleaved),
-                case.layer_idx, ctypes.byref(otrs[0]) if otrs[0] is not None else None)
+                int(case.rope_tail), case.layer_idx,
+                ctypes.byref(otrs[0]) if otrs[0] is not None else None)
         else:
             st = lib.orc_dual_band(
                 _ptr(buf), dt, T, case.row_stride, ctypes.byref(obands[0]),
                 ctypes.byref(obands[1]), case.weight_offset, int(case.multiply_before_cast),
                 _ptr(off), case.batch, _ptr(freqs), case.max_seq_len, case.rope_dim,
-                int(case.interleaved), case.layer_idx,
+                int(case.interleaved), int(case.rope_tail), case.layer_idx,
                 ctypes.byref(otrs[0]) if otrs[0] is not None else None,
                 ctypes.byref(otrs[1]) if otrs[1] is not None else None)
         res.q_out += q_outs
@@ -318,8 +319,9 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
         t0 = time.perf_counter()
         st = lib.orc_fused_qk_rope_bshd(
             _ptr(buf), dt, case.batch, case.seq_len, Hq, _ptr(valid), _ptr(freqs),
-            case.max_seq_len, case.rope_dim, int(case.interleaved), ctypes.byref(ocaches[0]),
-            case.layer_idx, _ptr(out), ctypes.byref(otr) if otr is not None else None)
+            case.max_seq_len, case.rope_dim, int(case.interleaved), int(case.rope_tail),
+            ctypes.byref(ocaches[0]), case.layer_idx, _ptr(out),
+            ctypes.byref(otr) if otr is not None else None)
         res.q_out.append(out)
         res.traces.append(tr)
     else:

@@ -234,10 +234,11 @@ static int32_t where_is(const orc_cache* c, const uint32_t* off, uint32_t B, uin
 /* per-head arithmetic                                                 */
 /* ------------------------------------------------------------------ */
 
-/* RoPE of one head x[D] at position pos; y gets the rotated values and
- * mag[j] the length of the pair j belongs to (|x_j| for dims >= R). */
+/* RoPE of one head x[D] at position pos over dims start .. start + R - 1;
+ * y gets the rotated values and mag[j] the length of the pair j belongs to
+ * (|x_j| for dims that do not rotate). */
 static void rope_head(const double* x, double* y, double* mag, uint32_t D, const float* freqs,
-                      uint32_t pos, uint32_t R, int32_t interleaved) {
+                      uint32_t pos, uint32_t R, int32_t interleaved, uint32_t start) {
   for (uint32_t j = 0; j < D; ++j) {
     y[j] = x[j];
     mag[j] = fabs(x[j]);
@@ -246,8 +247,8 @@ static void rope_head(const double* x, double* y, double* mag, uint32_t D, const
   for (uint32_t i = 0; i < R / 2; ++i) {
     double c = (double)row[2 * i];     /* cos(pos * theta_i) */
     double s = (double)row[2 * i + 1]; /* sin(pos * theta_i) */
-    uint32_t j0 = interleaved ? 2 * i : i;
-    uint32_t j1 = interleaved ? 2 * i + 1 : i + R / 2;
+    uint32_t j0 = start + (interleaved ? 2 * i : i);
+    uint32_t j1 = start + (interleaved ? 2 * i + 1 : i + R / 2);
     double re = x[j0], im = x[j1];
     /* (re + i im) * (c + i s) */
     y[j0] = re * c - im * s;
@@ -293,13 +294,13 @@ static int head_buf_alloc(head_buf* hb, uint32_t D) {
 /* hb->x (already read) -> optional norm -> rope -> hb->y, pair lengths in hb->mag */
 static void head_math(head_buf* hb, uint32_t D, const void* gamma, int32_t dt, double w,
                       double eps, int32_t mbc, const float* freqs, uint32_t pos, uint32_t R,
-                      int32_t interleaved) {
+                      int32_t interleaved, uint32_t start) {
   const double* in = hb->x;
   if (gamma) {
     rmsnorm_head(hb->x, hb->xn, D, gamma, dt, w, eps, mbc);
     in = hb->xn;
   }
-  rope_head(in, hb->y, hb->mag, D, freqs, pos, R, interleaved);
+  rope_head(in, hb->y, hb->mag, D, freqs, pos, R, interleaved, start);
 }
 
 static void record(const head_buf* hb, uint32_t D, double* exact, double* mag) {
@@ -309,15 +310,15 @@ static void record(const head_buf* hb, uint32_t D, double* exact, double* mag) {
   }
 }
 
-/* Store a head's result in a plain buffer of dtype dst_dt.  Elements below
- * `first_moved` (the roped ones; all of them after a norm) are rounded to
- * dst_dt; the others move as raw bits when the source has dst_dt, and are
- * rounded (converted) when it does not. */
+/* Store a head's result in a plain buffer of dtype dst_dt.  Elements lo ..
+ * hi - 1 (the roped ones; all of them after a norm) are rounded to dst_dt;
+ * the others move as raw bits when the source has dst_dt, and are rounded
+ * (converted) when it does not. */
 static void store_plain(void* dst, int64_t dst_off, int32_t dst_dt, const double* y,
                         const void* src, int64_t src_off, int32_t src_dt, uint32_t D,
-                        uint32_t first_moved) {
+                        uint32_t lo, uint32_t hi) {
   for (uint32_t j = 0; j < D; ++j) {
-    if (j < first_moved || src_dt != dst_dt)
+    if ((j >= lo && j < hi) || src_dt != dst_dt)
       put(dst, dst_dt, dst_off + j, y[j]);
     else
       copy_bits(dst, dst_off + j, src, src_off + j, dst_dt);
@@ -386,11 +387,11 @@ static void read_cache_row(const orc_cache* c, int64_t off, int64_t so, uint32_t
  * (its dtype is the op's), an FP8 cache by quantizing the whole row. */
 static void store_cache_row(orc_cache* c, int64_t off, int64_t so, const double* y,
                             const void* src, int64_t src_off, int32_t src_dt, uint32_t D,
-                            uint32_t first_moved) {
+                            uint32_t lo, uint32_t hi) {
   if (c->dtype == ORC_FP8)
     quantize_row(c, off, so, y, D);
   else
-    store_plain(c->pool, off, c->dtype, y, src, src_off, src_dt, D, first_moved);
+    store_plain(c->pool, off, c->dtype, y, src, src_off, src_dt, D, lo, hi);
 }
 
 static void read_plain(const void* src, int32_t dt, int64_t off, uint32_t D, double* x) {
@@ -421,7 +422,7 @@ int32_t orc_rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t T,
                                    uint64_t qkv_row_stride, uint32_t n_q_heads,
                                    const uint32_t* off, uint32_t B, const float* freqs,
                                    uint32_t max_seq_len, uint32_t R, int32_t interleaved,
-                                   orc_cache* c, uint32_t layer_idx, void* q_out,
+                                   int32_t rope_tail, orc_cache* c, uint32_t layer_idx, void* q_out,
                                    int32_t q_out_dtype, uint64_t q_out_row_stride,
                                    orc_trace* tr) {
   int32_t st = check_common(dtype, c, R, layer_idx, max_seq_len);
@@ -432,6 +433,8 @@ int32_t orc_rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t T,
   if (!qkv || !off || !freqs || !q_out) return ORC_EINVAL;
   if (B > c->cache_batch) return ORC_EINVAL;
   const uint32_t D = c->head_dim, Hq = n_q_heads, Hk = c->num_kv_heads;
+  /* the rotated dims: the first rope_dim, or with rope_tail the last */
+  const uint32_t r0 = rope_tail ? D - R : 0;
   if (qkv_row_stride < (uint64_t)(Hq + 2 * Hk) * D || q_out_row_stride < (uint64_t)Hq * D)
     return ORC_EINVAL;
   if ((st = check_offsets(off, B, T))) return st;
@@ -448,9 +451,9 @@ int32_t orc_rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t T,
     for (uint32_t h = 0; h < Hq; ++h) {
       const int64_t src = in_row + (int64_t)h * D;
       read_plain(qkv, dtype, src, D, hb.x);
-      head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, w.pos, R, interleaved);
+      head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, w.pos, R, interleaved, r0);
       store_plain(q_out, (int64_t)t * (int64_t)q_out_row_stride + (int64_t)h * D, q_out_dtype,
-                  hb.y, qkv, src, dtype, D, R);
+                  hb.y, qkv, src, dtype, D, r0, r0 + R);
       if (tr)
         record(&hb, D, tr->q_exact ? tr->q_exact + ((uint64_t)t * Hq + h) * D : NULL,
                tr->q_mag ? tr->q_mag + ((uint64_t)t * Hq + h) * D : NULL);
@@ -461,8 +464,8 @@ int32_t orc_rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t T,
       const int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);
       const int64_t so = c->scales ? scale_offset(c, w.page, 0, layer_idx, w.slot, h) : -1;
       read_plain(qkv, dtype, src, D, hb.x);
-      head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, w.pos, R, interleaved);
-      store_cache_row(c, dst, so, hb.y, qkv, src, dtype, D, R);
+      head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, w.pos, R, interleaved, r0);
+      store_cache_row(c, dst, so, hb.y, qkv, src, dtype, D, r0, r0 + R);
       if (tr) {
         record(&hb, D, tr->k_exact ? tr->k_exact + ((uint64_t)t * Hk + h) * D : NULL,
                tr->k_mag ? tr->k_mag + ((uint64_t)t * Hk + h) * D : NULL);
@@ -477,7 +480,7 @@ int32_t orc_rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t T,
       const int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);
       const int64_t so = c->scales ? scale_offset(c, w.page, 1, layer_idx, w.slot, h) : -1;
       read_plain(qkv, dtype, src, D, hb.x);
-      store_cache_row(c, dst, so, hb.x, qkv, src, dtype, D, 0);
+      store_cache_row(c, dst, so, hb.x, qkv, src, dtype, D, 0, 0);
       if (tr) {
         set_off(tr->v_row_off, (uint64_t)t * Hk + h, dst);
         set_off(tr->v_scale_off, (uint64_t)t * Hk + h, so);
@@ -493,7 +496,7 @@ int32_t orc_qk_rmsnorm_rope_paged(const void* buf, int32_t dtype, uint32_t T,
                                   float weight_offset, int32_t multiply_before_cast,
                                   const uint32_t* off, uint32_t B, const float* freqs,
                                   uint32_t max_seq_len, uint32_t R, int32_t interleaved,
-                                  uint32_t layer_idx, orc_trace* tr) {
+                                  int32_t rope_tail, uint32_t layer_idx, orc_trace* tr) {
   if (!band) return ORC_EINVAL;
   orc_cache* c = band->cache;
   int32_t st = check_common(dtype, c, R, layer_idx, max_seq_len);
@@ -503,6 +506,8 @@ int32_t orc_qk_rmsnorm_rope_paged(const void* buf, int32_t dtype, uint32_t T,
   if (!buf || !off || !freqs || (band->n_q_heads && !band->q_output)) return ORC_EINVAL;
   if (B > c->cache_batch) return ORC_EINVAL;
   const uint32_t D = c->head_dim, Hq = band->n_q_heads, Hk = c->num_kv_heads;
+  /* the rotated dims: the first rope_dim, or with rope_tail the last */
+  const uint32_t r0 = rope_tail ? D - R : 0;
   if ((st = check_offsets(off, B, T))) return st;
   where_t w;
   for (uint32_t t = 0; t < T; ++t)
@@ -521,9 +526,10 @@ int32_t orc_qk_rmsnorm_rope_paged(const void* buf, int32_t dtype, uint32_t T,
       const int64_t src = in_row + (int64_t)band->q_col + (int64_t)h * D;
       read_plain(buf, dtype, src, D, hb.x);
       head_math(&hb, D, band->q_gamma, dtype, wv, eps, multiply_before_cast, freqs, w.pos, R,
-                interleaved);
+                interleaved, r0);
       store_plain(band->q_output, (int64_t)t * (int64_t)band->q_out_row_stride + (int64_t)h * D,
-                  dtype, hb.y, buf, src, dtype, D, band->q_gamma ? D : R);
+                  dtype, hb.y, buf, src, dtype, D, band->q_gamma ? 0 : r0,
+                  band->q_gamma ? D : r0 + R);
       if (tr)
         record(&hb, D, tr->q_exact ? tr->q_exact + ((uint64_t)t * Hq + h) * D : NULL,
                tr->q_mag ? tr->q_mag + ((uint64_t)t * Hq + h) * D : NULL);
@@ -531,18 +537,18 @@ int32_t orc_qk_rmsnorm_rope_paged(const void* buf, int32_t dtype, uint32_t T,
     for (uint32_t h = 0; h < Hk; ++h) {
       const int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);
       const int64_t so = c->scales ? scale_offset(c, w.page, 0, layer_idx, w.slot, h) : -1;
-      const uint32_t moved = band->k_gamma ? D : R;
+      const uint32_t lo = band->k_gamma ? 0 : r0, hi = band->k_gamma ? D : r0 + R;
       if (band->k_col >= 0) { /* K from the buffer */
         const int64_t src = in_row + band->k_col + (int64_t)h * D;
         read_plain(buf, dtype, src, D, hb.x);
         head_math(&hb, D, band->k_gamma, dtype, wv, eps, multiply_before_cast, freqs, w.pos, R,
-                  interleaved);
-        store_cache_row(c, dst, so, hb.y, buf, src, dtype, D, moved);
+                  interleaved, r0);
+        store_cache_row(c, dst, so, hb.y, buf, src, dtype, D, lo, hi);
       } else { /* K already in the cache: updated in place (the row is read whole first) */
         read_cache_row(c, dst, so, D, hb.x);
         head_math(&hb, D, band->k_gamma, dtype, wv, eps, multiply_before_cast, freqs, w.pos, R,
-                  interleaved);
-        store_cache_row(c, dst, so, hb.y, c->pool, dst, c->dtype, D, moved);
+                  interleaved, r0);
+        store_cache_row(c, dst, so, hb.y, c->pool, dst, c->dtype, D, lo, hi);
       }
       if (tr) {
         record(&hb, D, tr->k_exact ? tr->k_exact + ((uint64_t)t * Hk + h) * D : NULL,
@@ -557,7 +563,7 @@ int32_t orc_qk_rmsnorm_rope_paged(const void* buf, int32_t dtype, uint32_t T,
         const int64_t dst = row_offset(c, w.page, 1, layer_idx, w.slot, h);
         const int64_t so = c->scales ? scale_offset(c, w.page, 1, layer_idx, w.slot, h) : -1;
         read_plain(buf, dtype, src, D, hb.x);
-        store_cache_row(c, dst, so, hb.x, buf, src, dtype, D, 0);
+        store_cache_row(c, dst, so, hb.x, buf, src, dtype, D, 0, 0);
         if (tr) {
           set_off(tr->v_row_off, (uint64_t)t * Hk + h, dst);
           set_off(tr->v_scale_off, (uint64_t)t * Hk + h, so);
@@ -573,7 +579,8 @@ int32_t orc_dual_band(const void* buf, int32_t dtype, uint32_t T, uint64_t buf_r
                       const orc_band* main_band, const orc_band* index_band, float weight_offset,
                       int32_t multiply_before_cast, const uint32_t* off, uint32_t B,
                       const float* freqs, uint32_t max_seq_len, uint32_t R, int32_t interleaved,
-                      uint32_t layer_idx, orc_trace* main_trace, orc_trace* index_trace) {
+                      int32_t rope_tail, uint32_t layer_idx, orc_trace* main_trace,
+                      orc_trace* index_trace) {
   if (!main_band || !index_band || !main_band->cache || !index_band->cache) return ORC_EINVAL;
   /* the two bands share the op's dtype and must agree on head size
    * (fused_dual_qk_rms_norm_rope_ragged_paged page, Description: identical
@@ -583,11 +590,11 @@ int32_t orc_dual_band(const void* buf, int32_t dtype, uint32_t T, uint64_t buf_r
   /* one launch fusing two single-band launches: the same result as the two in turn */
   int32_t st = orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, main_band, weight_offset,
                                          multiply_before_cast, off, B, freqs, max_seq_len, R,
-                                         interleaved, layer_idx, main_trace);
+                                         interleaved, rope_tail, layer_idx, main_trace);
   if (st) return st;
   return orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, index_band, weight_offset,
                                    multiply_before_cast, off, B, freqs, max_seq_len, R,
-                                   interleaved, layer_idx, index_trace);
+                                   interleaved, rope_tail, layer_idx, index_trace);
 }
 
 int32_t orc_kv_cache_radd(const void* a, int32_t dtype, uint32_t T, uint64_t a_row_stride,
@@ -651,7 +658,8 @@ int32_t orc_kv_cache_radd(const void* a, int32_t dtype, uint32_t T, uint64_t a_r
 int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t B, uint32_t S,
                                uint32_t n_q_heads, const uint32_t* valid_lengths,
                                const float* freqs, uint32_t max_seq_len, uint32_t R,
-                               int32_t interleaved, orc_cache* c, uint32_t layer_idx,
+                               int32_t interleaved, int32_t rope_tail, orc_cache* c,
+                               uint32_t layer_idx,
                                void* output, orc_trace* tr) {
   int32_t st = check_common(dtype, c, R, layer_idx, max_seq_len);
   if (st) return st;
@@ -659,6 +667,8 @@ int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t B, ui
   if (!q_proj || !valid_lengths || !freqs || !output || n_q_heads == 0) return ORC_EINVAL;
   if (B > c->cache_batch) return ORC_EINVAL;
   const uint32_t D = c->head_dim, Hq = n_q_heads, Hk = c->num_kv_heads;
+  /* the rotated dims: the first rope_dim, or with rope_tail the last */
+  const uint32_t r0 = rope_tail ? D - R : 0;
   const int64_t row_len = (int64_t)Hq * D;
 
   /* every real token's position and page must exist before anything is written */
@@ -693,8 +703,8 @@ int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t B, ui
       for (uint32_t h = 0; h < Hq; ++h) {
         const int64_t src = row + (int64_t)h * D;
         read_plain(q_proj, dtype, src, D, hb.x);
-        head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, pos, R, interleaved);
-        store_plain(output, src, dtype, hb.y, q_proj, src, dtype, D, R);
+        head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, pos, R, interleaved, r0);
+        store_plain(output, src, dtype, hb.y, q_proj, src, dtype, D, r0, r0 + R);
         if (tr)
           record(&hb, D, tr->q_exact ? tr->q_exact + (t * Hq + h) * D : NULL,
                  tr->q_mag ? tr->q_mag + (t * Hq + h) * D : NULL);
@@ -703,8 +713,8 @@ int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t B, ui
         const int64_t dst = row_offset(c, page, 0, layer_idx, slot, h);
         const int64_t so = c->scales ? scale_offset(c, page, 0, layer_idx, slot, h) : -1;
         read_cache_row(c, dst, so, D, hb.x);
-        head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, pos, R, interleaved);
-        store_cache_row(c, dst, so, hb.y, c->pool, dst, c->dtype, D, R);
+        head_math(&hb, D, NULL, dtype, 0.0, 0.0, 1, freqs, pos, R, interleaved, r0);
+        store_cache_row(c, dst, so, hb.y, c->pool, dst, c->dtype, D, r0, r0 + R);
         if (tr) {
           record(&hb, D, tr->k_exact ? tr->k_exact + (t * Hk + h) * D : NULL,
                  tr->k_mag ? tr->k_mag + (t * Hk + h) * D : NULL);

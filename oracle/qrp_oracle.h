@@ -21,8 +21,9 @@
  *     freqs_cis);
  *   - the rotation multiplies by cos + i*sin;
  *   - half-split pairs element i with element i + rope_dim/2;
- *   - a partial rope rotates the FIRST rope_dim dimensions of a head
- *     (parity unpinned: the pages fix no location);
+ *   - a partial rope rotates the FIRST rope_dim dimensions of a head, or
+ *     with rope_tail the LAST rope_dim (parity unpinned: the pages fix no
+ *     location; both conventions are offered);
  *   - position = cache_lengths[b + batch_offset] + local token index;
  *   - RMSNorm: mean of squares over the head, epsilon inside the square
  *     root, gamma + weight_offset as the scale, norm before rope;
@@ -124,7 +125,7 @@ int32_t orc_rope_split_store_paged(
     const void* qkv, int32_t dtype, uint32_t total_seq_len, uint64_t qkv_row_stride,
     uint32_t n_q_heads, const uint32_t* input_row_offsets, uint32_t batch_size,
     const float* freqs_cis, uint32_t max_seq_len, uint32_t rope_dim, int32_t interleaved,
-    orc_cache* cache, uint32_t layer_idx, void* q_output, int32_t q_out_dtype,
+    int32_t rope_tail, orc_cache* cache, uint32_t layer_idx, void* q_output, int32_t q_out_dtype,
     uint64_t q_out_row_stride, orc_trace* trace);
 
 /* Single-band fused per-head RMSNorm + RoPE (fused_dual_qk_rms_norm_rope_ragged_paged
@@ -134,7 +135,7 @@ int32_t orc_qk_rmsnorm_rope_paged(
     const orc_band* band, float weight_offset, int32_t multiply_before_cast,
     const uint32_t* input_row_offsets, uint32_t batch_size,
     const float* freqs_cis, uint32_t max_seq_len, uint32_t rope_dim, int32_t interleaved,
-    uint32_t layer_idx, orc_trace* trace);
+    int32_t rope_tail, uint32_t layer_idx, orc_trace* trace);
 
 /* Dual band: the main band then the index band, same offsets and freqs. */
 int32_t orc_dual_band(
@@ -142,7 +143,7 @@ int32_t orc_dual_band(
     const orc_band* main_band, const orc_band* index_band, float weight_offset,
     int32_t multiply_before_cast, const uint32_t* input_row_offsets, uint32_t batch_size,
     const float* freqs_cis, uint32_t max_seq_len, uint32_t rope_dim, int32_t interleaved,
-    uint32_t layer_idx, orc_trace* main_trace, orc_trace* index_trace);
+    int32_t rope_tail, uint32_t layer_idx, orc_trace* main_trace, orc_trace* index_trace);
 
 /* generic_kv_cache_radd_dispatch page (Summary, Description, Args). */
 int32_t orc_kv_cache_radd(
@@ -160,7 +161,8 @@ int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t batch
                                uint32_t seq_len, uint32_t n_q_heads,
                                const uint32_t* valid_lengths, const float* freqs_cis,
                                uint32_t max_seq_len, uint32_t rope_dim, int32_t interleaved,
-                               orc_cache* cache, uint32_t layer_idx, void* output,
+                               int32_t rope_tail, orc_cache* cache, uint32_t layer_idx,
+                               void* output,
                                orc_trace* trace);
 
 #ifdef __cplusplus

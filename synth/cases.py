@@ -240,6 +240,7 @@ class Case:
     freq_dtype: str = F32               # table entries: f32, or bf16 / f16 values held in float32
     seq_len: int = 0                    # bshd: padded rows per sequence (lengths = valid lengths)
     q_out_dtype: Optional[str] = None   # store op: Q output dtype (None: dtype)
+    rope_tail: bool = False             # a partial rope rotates the last rope_dim dims
 
     @property
     def q_dtype(self) -> str:
@@ -341,7 +342,8 @@ def make_store_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq
                     max_pages: Optional[int] = None, slack: float = 0.25,
                     q_out_pad: int = 0, row_pad: int = 0, specials: bool = False,
                     freq_dtype: str = F32, cache_dtype: Optional[str] = None,
-                    scale_dtype: str = F32, q_out_dtype: Optional[str] = None) -> Case:
+                    scale_dtype: str = F32, q_out_dtype: Optional[str] = None,
+                    rope_tail: bool = False) -> Case:
     """rope_split_store_paged workload: qkv [T, (Hq + 2Hk) D (+row_pad)] N(0, 1).
     ``cache_dtype`` FP8 stores e4m3 rows with ``scale_dtype`` scales;
     ``q_out_dtype`` sets Q's output dtype (default: dtype)."""
@@ -366,7 +368,7 @@ def make_store_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq
                 buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta, freq_dtype),
                 rope_dim=rope_dim, interleaved=interleaved, caches=[cache], layer_idx=layer,
                 n_q_heads=Hq, q_out_row_stride=Hq * D + q_out_pad, freq_dtype=freq_dtype,
-                q_out_dtype=q_out_dtype)
+                q_out_dtype=q_out_dtype, rope_tail=rope_tail)
 
 
 def _special_values(dtype: str) -> np.ndarray:
@@ -403,7 +405,8 @@ def make_norm_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq:
                    k_norm: bool = True, eps: float = 1e-6, weight_offset: float = 0.0,
                    multiply_before_cast: bool = True, slack: float = 0.25,
                    gamma_std: float = 0.1, freq_dtype: str = F32,
-                   cache_dtype: Optional[str] = None, scale_dtype: str = F32) -> Case:
+                   cache_dtype: Optional[str] = None, scale_dtype: str = F32,
+                   rope_tail: bool = False) -> Case:
     """Single-band qk_rmsnorm_rope_paged workload.  Buffer [T, (Hq+2Hk) D] =
     Q | K | V; with ``k_in_cache`` K is prefilled in the cache and updated in
     place (the buffer's K and V columns are then unread)."""
@@ -429,7 +432,8 @@ def make_norm_case(name: str, seed: int, dtype: str, lengths, cache_lengths, Hq:
                 buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta, freq_dtype),
                 rope_dim=rope_dim, interleaved=interleaved, caches=[cache], layer_idx=layer,
                 bands=[band], weight_offset=weight_offset,
-                multiply_before_cast=multiply_before_cast, freq_dtype=freq_dtype)
+                multiply_before_cast=multiply_before_cast, freq_dtype=freq_dtype,
+                rope_tail=rope_tail)
 
 
 def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_main: int,
@@ -439,7 +443,8 @@ def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_m
                    multiply_before_cast: bool = True, slack: float = 0.25,
                    cache_lengths=None, freq_dtype: str = F32,
                    main_cache_dtype: Optional[str] = None,
-                   index_cache_dtype: Optional[str] = None, scale_dtype: str = F32) -> Case:
+                   index_cache_dtype: Optional[str] = None, scale_dtype: str = F32,
+                   rope_tail: bool = False) -> Case:
     """Dual-band workload: buffer [T, (Hq_main + 2 Hk_main + Hq_index) D] =
     Q-main | K-main | V-main | Q-index; both bands' K caches updated in place."""
     lengths = np.asarray(lengths, dtype=np.int64)
@@ -469,7 +474,8 @@ def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_m
                 buf=buf, freqs=freqs_table(max_seq_len, rope_dim, theta, freq_dtype),
                 rope_dim=rope_dim, interleaved=interleaved, caches=[main, index], layer_idx=0,
                 bands=[main_band, index_band], weight_offset=weight_offset,
-                multiply_before_cast=multiply_before_cast, freq_dtype=freq_dtype)
+                multiply_before_cast=multiply_before_cast, freq_dtype=freq_dtype,
+                rope_tail=rope_tail)
 
 
 def make_radd_case(name: str, seed: int, dtype: str, lengths, cache_lengths, batch_offset: int,
@@ -509,7 +515,7 @@ def make_bshd_case(name: str, seed: int, dtype: str, valid_lengths, seq_len: int
                    max_seq_len: int, capacity: int, L: int, layer: int,
                    num_blocks: Optional[int] = None, slack: float = 0.25,
                    freq_dtype: Optional[str] = None, cache_dtype: Optional[str] = None,
-                   scale_dtype: str = F32) -> Case:
+                   scale_dtype: str = F32, rope_tail: bool = False) -> Case:
     """Padded continuous-batching workload: q_proj [B, seq_len, Hq, D] N(0, 1)
     held as [B * seq_len, Hq * D]; a continuous-batching cache of blocks of
     ``capacity`` rows (one page per sequence, a seeded permutation of the
@@ -531,7 +537,7 @@ def make_bshd_case(name: str, seed: int, dtype: str, valid_lengths, seq_len: int
     return Case(name=name, op="bshd", dtype=dtype, seed=seed, lengths=valid, offsets=off, buf=buf,
                 freqs=freqs_table(max_seq_len, rope_dim, theta, fdt), rope_dim=rope_dim,
                 interleaved=interleaved, caches=[cache], layer_idx=layer, n_q_heads=Hq,
-                q_out_row_stride=width, freq_dtype=fdt, seq_len=seq_len)
+                q_out_row_stride=width, freq_dtype=fdt, seq_len=seq_len, rope_tail=rope_tail)
 
 
 # ---------------------------------------------------------------------------

@@ -23,8 +23,8 @@ MUTATIONS = {
     "rotation_sign": ("y[j0] = re * c - im * s;", "y[j0] = re * c + im * s;"),
     "rotation_imag": ("y[j1] = re * s + im * c;", "y[j1] = im * c - re * s;"),
     "cos_sin_swapped": ("double c = (double)row[2 * i];", "double c = (double)row[2 * i + 1];"),
-    "half_split_partner": ("uint32_t j1 = interleaved ? 2 * i + 1 : i + R / 2;",
-                           "uint32_t j1 = interleaved ? 2 * i + 1 : i + D / 2;"),
+    "half_split_partner": ("uint32_t j1 = start + (interleaved ? 2 * i + 1 : i + R / 2);",
+                           "uint32_t j1 = start + (interleaved ? 2 * i + 1 : i + D / 2);"),
     "interleaved_freq_index": ("const float* row = freqs + (uint64_t)pos * R;",
                                "const float* row = freqs + (uint64_t)pos * D;"),
     "position_ignores_cache_len": ("uint64_t pos = (uint64_t)c->cache_lengths[cseq] + (t - off[b]);",
@@ -54,7 +54,9 @@ MUTATIONS = {
     "radd_adds_twice": ("float sum = cur + add; /* one IEEE binary32 add */",
                         "float sum = cur + add + add;"),
     "radd_halves_swapped": ("(int64_t)(plane * hidden)", "(int64_t)((1 - plane) * hidden)"),
-    "unroped_dims_rounded": ("if (j < first_moved || src_dt != dst_dt)", "if (1)"),
+    "unroped_dims_rounded": ("if ((j >= lo && j < hi) || src_dt != dst_dt)", "if (1)"),
+    "rope_tail_ignored": ("const uint32_t r0 = rope_tail ? D - R : 0;\n  if (qkv_row_stride",
+                          "const uint32_t r0 = 0;\n  if (qkv_row_stride"),
     "e4m3_bias_8": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     "e4m3_truncate": ("double r = isinf(a) ? 448.0 : nearbyint(a / quantum) * quantum;",
                       "double r = isinf(a) ? 448.0 : trunc(a / quantum) * quantum;"),
@@ -90,6 +92,7 @@ PIN_TESTS = [
     (pins.test_rmsnorm_epsilon_sits_inside_the_root, {}),
     (pins.test_radd_is_one_binary32_add_per_element, {"dtype": "bf16"}),
     (pins.test_radd_is_one_binary32_add_per_element, {"dtype": "f32"}),
+    (pins.test_trailing_partial_rope_brute_force, {"interleaved": False, "dtype": "bf16"}),
     (bshd_pins.test_bshd_matches_complex_brute_force, {"dtype": "bf16", "interleaved": False}),
     (bshd_pins.test_bshd_padded_rows_are_copied_bit_for_bit, {}),
     (fp8_pins.test_e4m3_rounding_golden_cases, {}),

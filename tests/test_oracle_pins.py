@@ -189,6 +189,53 @@ def test_partial_rope_and_ragged_batch_brute_force(interleaved, dtype):
     assert np.all(res.q_out[0][:, Hq * D:] == sc.SENTINEL[dtype])
 
 
+@pytest.mark.parametrize("interleaved", [True, False])
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16])
+def test_trailing_partial_rope_brute_force(interleaved, dtype):
+    """rope_tail: the LAST rope_dim dims of each head rotate, the first
+    D - rope_dim move as bits (the other convention for a partial rope)."""
+    R, D = 32, 64
+    case = sc.make_store_case("tail", 57, dtype, [5, 0, 9], [3, 2, 20], Hq=4, Hk=2, D=D,
+                              rope_dim=R, interleaved=interleaved, theta=1e4, max_seq_len=64,
+                              P=8, L=2, layer=1, rope_tail=True)
+    res = oracle.run_case(case)
+    assert res.status == 0
+    tol = {sc.F32: 2.0 ** -23, sc.BF16: 2.0 ** -8}[dtype]
+    cache = case.caches[0]
+    Hq, Hk = 4, 2
+    for t, b, cseq, pos in brute.walk_tokens(case):
+        page, slot = brute.page_slot(cache, cseq, pos)
+        for h in range(Hq + Hk):
+            x_bits = case.buf[t, h * D:(h + 1) * D]
+            y, mag = brute.rope_complex(brute.as_f64(x_bits[D - R:], dtype), case.freqs[pos], R,
+                                        interleaved)
+            got_bits = (res.q_out[0][t, h * D:(h + 1) * D] if h < Hq
+                        else res.pools[0][page, 0, 1, slot, h - Hq])
+            got = brute.as_f64(got_bits[D - R:], dtype)
+            assert np.all(np.abs(got - y) <= tol * mag), (t, h)
+            assert np.array_equal(got_bits[:D - R], x_bits[:D - R]), (t, h)
+
+
+def test_trailing_rope_is_leading_rope_of_rolled_heads():
+    """Rolling every head by D - R dims maps the trailing convention onto the
+    leading one: the two runs agree bit for bit after rolling back."""
+    R, D, Hq, Hk = 32, 64, 4, 2
+    mk = lambda tail: sc.make_store_case("roll", 58, sc.BF16, [6, 4], [0, 11], Hq=Hq, Hk=Hk, D=D,
+                                         rope_dim=R, interleaved=False, theta=1e4,
+                                         max_seq_len=64, P=8, L=1, layer=0, rope_tail=tail)
+    tail, lead = mk(True), mk(False)
+    H = Hq + 2 * Hk
+    lead.buf = np.ascontiguousarray(
+        np.roll(tail.buf.reshape(tail.T, H, D), -(D - R), axis=2).reshape(tail.T, H * D))
+    rt, rl = oracle.run_case(tail), oracle.run_case(lead)
+    qt = rt.q_out[0].reshape(tail.T, Hq, D)
+    ql = np.roll(rl.q_out[0].reshape(lead.T, Hq, D), D - R, axis=2)
+    assert np.array_equal(qt, ql)
+    kt = rt.pools[0][:, 0]
+    kl = np.roll(rl.pools[0][:, 0], D - R, axis=-1)
+    assert np.array_equal(kt, kl)
+
+
 def test_position_zero_is_identity():
     case = _store_case(lengths=(1, 1, 1), cache_lengths=(0, 0, 0), num_pages=12, seed=5)
     res = oracle.run_case(case)
