@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define QRP_ABI_VERSION 2
+#define QRP_ABI_VERSION 3
 
 typedef enum qrp_status {
   QRP_OK = 0,
@@ -124,7 +124,9 @@ typedef struct qrp_paged_cache {
  * frequency i at that position.  rope_dim <= head_dim; the first rope_dim
  * dimensions of a head are rotated and the rest pass through (the width of
  * the table fixes rope_dim: fused_dual_qk_rms_norm_rope_ragged_paged page,
- * Description).  interleaved != 0 pairs dims (2i, 2i+1); interleaved == 0
+ * Description); with rope_tail = 1 the LAST rope_dim dimensions rotate
+ * instead (the pages do not say which; both conventions are offered), and
+ * the pairs are formed within those dims in the same two layouts.  interleaved != 0 pairs dims (2i, 2i+1); interleaved == 0
  * (half-split) pairs dims (i, i + rope_dim/2).  A pair (x, y) becomes
  * (x cos - y sin, x sin + y cos).  rope_dim must be a multiple of
  * 16 bytes / sizeof(dtype) * 2 (16 for bf16 and f16, 8 for f32).
@@ -138,6 +140,7 @@ typedef struct qrp_rope {
   uint32_t max_seq_len;
   uint32_t rope_dim;
   int32_t interleaved;
+  int32_t rope_tail;           /* 0: the first rope_dim dims rotate; 1: the last rope_dim */
 } qrp_rope;
 
 /*

@@ -55,7 +55,7 @@ class QrpPagedCache(ctypes.Structure):
 class QrpRope(ctypes.Structure):
     _fields_ = [("freqs_cis", ctypes.c_void_p), ("freq_dtype", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_uint32), ("rope_dim", ctypes.c_uint32),
-                ("interleaved", ctypes.c_int32)]
+                ("interleaved", ctypes.c_int32), ("rope_tail", ctypes.c_int32)]
 
 
 class QrpBand(ctypes.Structure):
@@ -204,11 +204,13 @@ class Rope:
     rope_dim: int
     interleaved: bool
     freq_dtype: int = QRP_F32
+    rope_tail: bool = False          # rotate the last rope_dim dims of a head
 
     def to_c(self) -> QrpRope:
         return QrpRope(freqs_cis=_ptr(self.freqs_cis), freq_dtype=self.freq_dtype,
                        max_seq_len=self.max_seq_len, rope_dim=self.rope_dim,
-                       interleaved=int(bool(self.interleaved)))
+                       interleaved=int(bool(self.interleaved)),
+                       rope_tail=int(bool(self.rope_tail)))
 
 
 @dataclass

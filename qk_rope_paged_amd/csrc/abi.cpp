@@ -98,6 +98,7 @@ int32_t check_rope(const qrp_rope* r, int32_t dtype, uint32_t head_dim) {
     return fail(QRP_EUNSUPPORTED, "freq_dtype must be QRP_F32, QRP_BF16 or QRP_F16");
   if (!aligned16(r->freqs_cis)) return fail(QRP_EALIGN, "freqs_cis not 16-byte aligned");
   if (r->max_seq_len == 0) return fail(QRP_EINVAL, "max_seq_len must be positive");
+  if (r->rope_tail != 0 && r->rope_tail != 1) return fail(QRP_EINVAL, "rope_tail must be 0 or 1");
   if (r->rope_dim == 0 || r->rope_dim > head_dim || r->rope_dim % 2)
     return fail(QRP_EINVAL, "rope_dim must be even, positive and <= head_dim");
   if (r->rope_dim % (2 * chunk_elems(dtype)))
@@ -333,6 +334,7 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
   b.a.freqs = rope->freqs_cis;
   b.a.freq_dtype = (uint32_t)rope->freq_dtype;
   b.a.rope_dim = rope->rope_dim;
+  b.a.rope_off_chunks = rope->rope_tail ? (b.head_dim - rope->rope_dim) / chunk_elems(dtype) : 0;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.multiply_before_cast = 1;
   b.add_seg(qrp::SEG_Q, qkv, (int64_t)qkv_row_stride, q_output, (int64_t)q_out_row_stride, nullptr,
@@ -374,6 +376,7 @@ int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq
   b.a.freqs = rope->freqs_cis;
   b.a.freq_dtype = (uint32_t)rope->freq_dtype;
   b.a.rope_dim = rope->rope_dim;
+  b.a.rope_off_chunks = rope->rope_tail ? (b.head_dim - rope->rope_dim) / chunk_elems(dtype) : 0;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.weight_offset = to_dtype(dtype, weight_offset);
   b.a.multiply_before_cast = multiply_before_cast != 0;
@@ -422,6 +425,7 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
   b.a.freqs = rope->freqs_cis;
   b.a.freq_dtype = (uint32_t)rope->freq_dtype;
   b.a.rope_dim = rope->rope_dim;
+  b.a.rope_off_chunks = rope->rope_tail ? (b.head_dim - rope->rope_dim) / chunk_elems(dtype) : 0;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.weight_offset = to_dtype(dtype, weight_offset);
   b.a.multiply_before_cast = multiply_before_cast != 0;
@@ -506,6 +510,7 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
   b.a.freqs = rope->freqs_cis;
   b.a.freq_dtype = (uint32_t)rope->freq_dtype;
   b.a.rope_dim = rope->rope_dim;
+  b.a.rope_off_chunks = rope->rope_tail ? (b.head_dim - rope->rope_dim) / chunk_elems(dtype) : 0;
   b.a.max_seq_len = rope->max_seq_len;
   b.a.multiply_before_cast = 1;
   b.add_seg(qrp::SEG_Q, q_proj, (int64_t)row, output, (int64_t)row, nullptr, 0.f, n_q_heads, 0, 0);

@@ -447,6 +447,7 @@ __device__ __forceinline__ void load_freqs_t(const void* __restrict__ freqs, int
 
 // This lane's (cos, sin) entries of freqs row `pos`: the 2E table values of
 // the frequencies its chunks rotate (zero where a chunk is not rotated).
+// c0 / c1 are the chunks' places within the rotated dims.
 // The table's entry type is uniform over the launch.
 template <typename T, bool IL>
 __device__ __forceinline__ void load_freqs(const BandArgs& a, uint32_t pos, uint32_t c0,
@@ -508,12 +509,31 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   // this lane's row within a pass and its two chunks within the row
   const uint32_t row = lane / LPR;
   const uint32_t j = lane % LPR;
+  // The rotated dims are chunks oc .. oc + rope_dim/E - 1 (oc = 0, or the
+  // last rope_dim dims of the head).  Half-split, leading dims: lanes j < hh
+  // hold rotated chunk j and its partner j + hh, the other lanes two of the
+  // chunks 2hh .. that pass through.  The trailing layout is that list turned
+  // by oc chunks (mod D/E, a power of two): rotated chunks land on oc.., the
+  // pass-through ones on 0 .. oc - 1.  Branch-free, so the lanes stay
+  // converged while the first loads issue.
+  constexpr uint32_t NC = D / E;
+  static_assert((NC & (NC - 1)) == 0, "chunks per head must be a power of two");
+  const uint32_t oc = a.rope_off_chunks;
   const uint32_t hh = (IL || RADD) ? (uint32_t)LPR : a.rope_dim / (2 * E);
-  const uint32_t c0 = j < hh ? j : hh + j;
-  const uint32_t c1 = j < hh ? j + hh : j + LPR;
+  uint32_t c0, c1;
+  if constexpr (IL || RADD) {
+    c0 = j;
+    c1 = j + LPR;
+  } else {
+    const bool lead = j < hh;
+    c0 = (j + (lead ? 0u : hh) + oc) & (NC - 1);
+    c1 = (j + (lead ? hh : (uint32_t)LPR) + oc) & (NC - 1);
+  }
+  // interleaved: a chunk rotates when c - oc < rope_dim/E (unsigned, so the
+  // chunks before oc wrap past the bound)
   const uint32_t rot_chunks = a.rope_dim / E;
-  bool rot0 = !RADD && (IL ? c0 < rot_chunks : j < hh);
-  bool rot1 = !RADD && (IL ? c1 < rot_chunks : j < hh);
+  bool rot0 = !RADD && (IL ? c0 - oc < rot_chunks : j < hh);
+  bool rot1 = !RADD && (IL ? c1 - oc < rot_chunks : j < hh);
 
   uint4 x[NPMAX][2];
   uint4 y[RADD ? NPMAX : 1][2];
@@ -665,7 +685,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   // ---- D: this lane's (cos, sin) entries of the token's freqs row ----
   float fl[RADD ? 1 : 2 * E];
   uint32_t fl_pos = pos[0];
-  if constexpr (!RADD) load_freqs<T, IL>(a, fl_pos, c0, c1, j, rot0, rot1, fl);
+  if constexpr (!RADD) load_freqs<T, IL>(a, fl_pos, c0 - oc, c1 - oc, j, rot0, rot1, fl);
 
 
   // ---- E: arithmetic and stores ----
@@ -785,7 +805,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
           // own position (uniform, taken at most once per wave).
           if (pos[sd.cache] != fl_pos) {
             fl_pos = pos[sd.cache];
-            load_freqs<T, IL>(a, fl_pos, c0, c1, j, rot0, rot1, fl);
+            load_freqs<T, IL>(a, fl_pos, c0 - oc, c1 - oc, j, rot0, rot1, fl);
           }
           if constexpr (IL) {
 #pragma unroll

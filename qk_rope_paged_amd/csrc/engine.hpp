@@ -117,6 +117,7 @@ struct BandArgs {
   uint32_t per_xcd;         // blocks per XCD after the XCD-contiguous remap (0: no remap)
   uint64_t guess_mul;       // floor(batch * 2^32 / total_tokens): token -> first sequence guess
   uint32_t freq_dtype;      // DT_F32, DT_BF16 or DT_F16 table entries
+  uint32_t rope_off_chunks; // first rotated 16-byte chunk of a head (0: the leading dims)
   // Padded [batch][seq_len] token grid (continuous batching): token t is
   // row t % seq_len of sequence t / seq_len; rows at or past the sequence's
   // valid length pass through.  Unused by the ragged ops.

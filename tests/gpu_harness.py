@@ -153,7 +153,8 @@ def upload(case: sc.Case, device="cuda") -> DeviceCase:
 def rope_of(dc: DeviceCase) -> qrp.Rope:
     c = dc.case
     return qrp.Rope(freqs_cis=dc.freqs, max_seq_len=c.max_seq_len, rope_dim=c.rope_dim,
-                    interleaved=c.interleaved, freq_dtype=QRP_DT[c.freq_dtype])
+                    interleaved=c.interleaved, freq_dtype=QRP_DT[c.freq_dtype],
+                    rope_tail=c.rope_tail)
 
 
 def band_of(dc: DeviceCase, i: int) -> qrp.Band:

@@ -91,10 +91,15 @@ def check_fp8_rows(codes: np.ndarray, scales: np.ndarray, ora_codes: np.ndarray,
     rep[what + "_n"] = int(codes.size)
 
 
-def _copy_cols(D: int, R: int, normed: bool) -> np.ndarray:
+def _copy_cols(D: int, R: int, normed: bool, tail: bool = False) -> np.ndarray:
+    """Dims that move unchanged: those outside the rotated range (the first
+    R dims, or the last R with rope_tail), none after a norm."""
     cols = np.zeros(D, dtype=bool)
     if not normed:
-        cols[R:] = True
+        if tail:
+            cols[:D - R] = True
+        else:
+            cols[R:] = True
     return cols
 
 
@@ -144,7 +149,7 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
             tr = res.traces[qi]
             check_rows(rows[:, :Hq * D].reshape(-1, D), ora[:, :Hq * D].reshape(-1, D),
                        tr["q_exact"].reshape(-1, D), tr["q_mag"].reshape(-1, D),
-                       _copy_cols(D, case.rope_dim, qn), qdt, ulps, f"q{qi}", rep)
+                       _copy_cols(D, case.rope_dim, qn, case.rope_tail), qdt, ulps, f"q{qi}", rep)
     # ---- caches ----
     for ci, dcache in enumerate(dc.caches):
         host = dcache.host
@@ -176,7 +181,7 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
                 os_flat[soff] = 0
             else:
                 check_rows(g_flat[idx], o_flat[idx], tr["k_exact"].reshape(-1, D)[live],
-                           tr["k_mag"].reshape(-1, D)[live], _copy_cols(D, case.rope_dim, kn),
+                           tr["k_mag"].reshape(-1, D)[live], _copy_cols(D, case.rope_dim, kn, case.rope_tail),
                            dt, ulps, f"k{qi}", rep)
             # written K rows are checked: blank them before the bitwise comparison
             g_flat[idx] = 0

@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(qrp.EXPORTS)
-    assert qrp.abi_version() == 2
+    assert qrp.abi_version() == 3
 
 
 def test_one_hip_runtime_in_process():

@@ -213,3 +213,29 @@ def test_graph_replays_of_radd_match_eager():
         a = _bits(eager.caches[0].pool, case.dtype)
         b = _bits(graphed.caches[0].pool, case.dtype)
         assert np.array_equal(a, b), f"replay {i} differs from eager"
+
+
+@pytest.mark.parametrize("il", [True, False])
+def test_trailing_rope_equals_leading_rope_on_rolled_heads(il):
+    """Rolling every head by head_dim - rope_dim maps the trailing-dims
+    convention onto the leading one: two GPU runs agree bit for bit."""
+    _, gh, _ = _env()
+    D, R, Hq, Hk = 128, 64, 8, 2
+    mk = lambda tail: sc.make_store_case("roll", 33, sc.BF16, [40, 7, 0, 19], [0, 100, 3, 250],
+                                         Hq=Hq, Hk=Hk, D=D, rope_dim=R, interleaved=il, theta=5e5,
+                                         max_seq_len=512, P=32, L=1, layer=0, rope_tail=tail)
+    tail, lead = mk(True), mk(False)
+    H = Hq + 2 * Hk
+    lead.buf = np.ascontiguousarray(
+        np.roll(tail.buf.reshape(tail.T, H, D), -(D - R), axis=2).reshape(tail.T, H * D))
+    dt, dl = gh.upload(tail), gh.upload(lead)
+    gh.run(dt)
+    gh.run(dl)
+    torch.cuda.synchronize()
+    qt = _bits(dt.q_out_rows(0), sc.BF16).reshape(tail.T, Hq, D)
+    ql = np.roll(_bits(dl.q_out_rows(0), sc.BF16).reshape(lead.T, Hq, D), D - R, axis=2)
+    assert np.array_equal(qt, ql)
+    shape = tail.caches[0].shape
+    kt = _bits(dt.caches[0].pool, sc.BF16).reshape(shape)[:, 0]
+    kl = np.roll(_bits(dl.caches[0].pool, sc.BF16).reshape(shape)[:, 0], D - R, axis=-1)
+    assert np.array_equal(kt, kl)

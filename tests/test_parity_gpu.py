@@ -208,3 +208,41 @@ def test_dual_band_bf16_freqs_f16():
                              eps_index=1e-5, weight_offset=0.0, cache_lengths=[0, 3, 17, 400],
                              freq_dtype=sc.BF16)
     run_and_compare(case)
+
+
+# ---------------------------------------------------------------------------
+# trailing-dims partial rope (rope_tail)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
+@pytest.mark.parametrize("il", [True, False])
+@pytest.mark.parametrize("D,R", [(128, 64), (128, 32), (256, 64), (64, 32)])
+def test_store_trailing_partial_rope(dtype, il, D, R):
+    if dtype == sc.F32 and R == 32 and D == 64:
+        R = 16
+    run_and_compare(_store(f"tail_{dtype}_{il}_{D}_{R}", 70, dtype, [7, 0, 19, 3], [2, 9, 40, 0],
+                           D=D, R=R, il=il, rope_tail=True))
+
+
+@pytest.mark.parametrize("k_in_cache", [False, True])
+@pytest.mark.parametrize("il", [True, False])
+def test_norm_trailing_partial_rope(k_in_cache, il):
+    run_and_compare(_norm("norm_tail", 71, sc.BF16, [9, 4, 0, 17], [1, 0, 30, 5], k_in_cache,
+                          il=il, R=32, rope_tail=True, weight_offset=0.25))
+
+
+def test_dual_band_trailing_partial_rope():
+    case = sc.make_dual_case("dual_tail", 72, sc.BF16, [5, 0, 21, 8], Hq_main=16, Hk_main=4,
+                             Hq_index=4, D=128, rope_dim=64, interleaved=True, theta=1e4,
+                             max_seq_len=512, P_main=32, P_index=16, cache_lengths=[0, 3, 17, 400],
+                             rope_tail=True)
+    run_and_compare(case)
+
+
+def test_bshd_and_fp8_trailing_partial_rope():
+    run_and_compare(sc.make_bshd_case("bshd_tail", 73, sc.BF16, [5, 0, 17, 30], 24, [0, 9, 100, 3],
+                                      Hq=6, Hk=2, D=128, rope_dim=64, interleaved=False,
+                                      theta=1e4, max_seq_len=512, capacity=512, L=2, layer=1,
+                                      rope_tail=True))
+    run_and_compare(_store("fp8_tail", 74, sc.BF16, [6, 13, 2], [0, 5, 77], D=128, R=64, il=True,
+                           rope_tail=True, cache_dtype=sc.FP8))
