@@ -165,6 +165,7 @@ struct Builder {
     s.plane = plane;
     s.pass_begin = a.passes_per_token;
     s.n_passes = (n_heads + rpp - 1) / rpp;
+    if (kind == qrp::SEG_K_INPLACE) a.inplace_segs |= 1u << a.nseg;
     a.passes_per_token += s.n_passes;
     ++a.nseg;
   }
@@ -176,6 +177,7 @@ struct Builder {
     for (uint32_t s = 0; s < a.nseg; ++s) norm = norm || a.seg[s].gamma != nullptr;
     const uint32_t npmax = qrp::max_passes(radd, norm);
     const uint32_t ppt = a.passes_per_token;
+    if (ppt == 0) return fail(QRP_EINVAL, "no head rows to process");  // keeps n_items >= 1
     uint32_t ppg = std::min<uint32_t>(npmax, ppt);
     const int forced = env_int("QRP_PASSES_PER_WAVE", 0);
     if (forced > 0) {
@@ -190,6 +192,8 @@ struct Builder {
       const uint64_t want = 4096;
       while (ppg > 1 && (uint64_t)total_tokens * ((ppt + ppg - 1) / ppg) < want) --ppg;
     }
+    for (uint32_t i = 1; i < (uint32_t)qrp::kMaxSegs; ++i)
+      a.seg_begin[i - 1] = i < a.nseg ? a.seg[i].pass_begin : 0xFFFFFFFFu;
     a.passes_per_group = ppg;
     a.groups_per_token = (ppt + ppg - 1) / ppg;
     const uint64_t items = (uint64_t)total_tokens * a.groups_per_token;

@@ -382,7 +382,7 @@ __device__ __forceinline__ uint32_t seg_of(const BandArgs& a, uint32_t kp) {
   uint32_t s = 0;
 #pragma unroll
   for (int i = 1; i < kMaxSegs; ++i)
-    if ((uint32_t)i < a.nseg && kp >= a.seg[i].pass_begin) s = (uint32_t)i;
+    if (kp >= a.seg_begin[i - 1]) s = (uint32_t)i;
   return s;
 }
 
@@ -465,6 +465,32 @@ __device__ __forceinline__ void load_freqs(const BandArgs& a, uint32_t pos, uint
     load_freqs_t<DT_F16, T, IL>(a.freqs, row, c0, c1, j, rot0, rot1, fl);
 }
 
+// Bring every 64-byte line of the first BYTES bytes of the argument block
+// into the scalar cache at once: one dword load per line, all in flight
+// together, taken as operands by one empty asm statement (no instruction, no
+// memory access, so the loads complete before it and nothing else is
+// ordered by it).  The block is written just before the launch, so its lines
+// start cold: fetched this way they cost one miss latency per wave on the
+// launch's ramp, instead of one per line in the order the code first reads
+// them.  Returns the block's first dword, passed through the asm, so that
+// the caller's work depends on the fetch.
+template <uint32_t BYTES>
+__device__ __forceinline__ uint32_t touch_args() {
+  using kptr = const uint32_t __attribute__((address_space(4)))*;
+  const kptr k = (kptr)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr uint32_t N = (BYTES + 63) / 64;
+  static_assert(N >= 1 && N <= 12, "one asm operand per line");
+  uint32_t v[12];
+#pragma unroll
+  for (uint32_t i = 0; i < 12; ++i) {
+    const uint32_t l = i < N ? i : N - 1;
+    v[i] = k[l + 1 < N ? l * 16 : (BYTES - 4) / 4];  // the last line: the block's last dword
+  }
+  asm("" : "+s"(v[0]) : "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5]), "s"(v[6]),
+      "s"(v[7]), "s"(v[8]), "s"(v[9]), "s"(v[10]), "s"(v[11]));
+  return v[0];
+}
+
 // T: input (and norm / plain cache) element type; QT: Q output element type;
 // CT: cache element type (T, or Fp8 with a scale per row).
 template <typename T, typename QT, typename CT, int D, bool IL, int NPMAX, bool RADD, bool NORM,
@@ -478,11 +504,19 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   constexpr int RPP = 64 / LPR;  // head rows per pass
   static_assert(LPR >= 4 && LPR <= 32, "unsupported head_dim / dtype");
 
+  static_assert(offsetof(BandArgs, n_items) == 0, "the fetch returns n_items");
+  const uint32_t n_items =
+      touch_args<QUANT ? (uint32_t)sizeof(BandArgs) : (uint32_t)offsetof(BandArgs, scale)>();
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Waves past the work (a last block's spare waves, blocks the XCD remap
+  // adds) run on a clamped item and leave at the metadata check: no branch
+  // before the first loads, so the header's fields arrive in one round.
   uint32_t blk = blockIdx.x;
-  if (a.per_xcd) blk = (blk % kXcds) * a.per_xcd + blk / kXcds;
-  if (blk >= a.n_blocks) return;  // the whole block leaves together
+  blk = a.per_xcd ? (blk % kXcds) * a.per_xcd + blk / kXcds : blk;
+  const uint32_t item_raw = blk * a.waves_per_block + wave;
+  const bool dead = blk >= a.n_blocks || item_raw >= n_items;
+  const uint32_t item = dead ? n_items - 1 : item_raw;
 
   // Gammas of every segment, once per block, in LDS.  Reading them there
   // keeps the store loop free of vector-memory loads (vmcnt counts stores as
@@ -498,9 +532,6 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
     }
     __syncthreads();
   }
-
-  const uint32_t item = blk * a.waves_per_block + wave;
-  if (item >= a.n_items) return;
 
   const uint32_t t = item / a.groups_per_token;
   const uint32_t p0 = (item - t * a.groups_per_token) * a.passes_per_group;
@@ -545,10 +576,11 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
     if ((uint32_t)p < np) {
       const uint32_t kp = p0 + p;
       const SegDesc& sd = a.seg[seg_of(a, kp)];
-      if (sd.kind != SEG_K_INPLACE) {
-        const uint32_t h = min((kp - sd.pass_begin) * RPP + row, sd.n_heads - 1);
-        const T* src = reinterpret_cast<const T*>(sd.src) + (int64_t)t * sd.src_row_stride +
-                       (int64_t)h * D;
+      // the address before the branch: one scalar-load round for the fields
+      const uint32_t h = min((kp - sd.pass_begin) * RPP + row, sd.n_heads - 1);
+      const T* src = reinterpret_cast<const T*>(sd.src) + (int64_t)t * sd.src_row_stride +
+                     (int64_t)h * D;
+      if (!((a.inplace_segs >> seg_of(a, kp)) & 1u)) {
         x[p][0] = ld16s(src + c0 * E);
         x[p][1] = ld16s(src + c1 * E);
       }
@@ -616,7 +648,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       if ((uint32_t)ci < a.ncache)
         clen[ci] = hit ? clen_guess[ci] : a.cache[ci].cache_lengths[b + a.batch_offset];
   }
-  bool ok = start <= t && t < end;
+  bool ok = !dead && start <= t && t < end;
   const uint32_t local = t - start;
   const uint32_t cseq = b + a.batch_offset;
   uint32_t pos[kMaxCaches] = {0, 0};

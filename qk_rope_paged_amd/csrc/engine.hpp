@@ -18,6 +18,7 @@
 // [pass_begin, pass_begin + n_passes) of the token.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace qrp {
@@ -55,17 +56,19 @@ constexpr int kMaxPassesNorm = QRP_MAX_PASSES_NORM;
 constexpr int kMaxPassesRadd = QRP_MAX_PASSES_RADD;
 
 struct SegDesc {
+  // what a wave reads before its first buffer load: one 32-byte scalar load
   const void* src;          // buffer elements, already offset to the segment's first column
-  void* dst;                // dense output (SEG_Q)
-  const void* gamma;        // [D] of dtype, or nullptr: no norm
   int64_t src_row_stride;   // elements between tokens in src
-  int64_t dst_row_stride;   // elements between tokens in dst
-  float eps;
-  uint32_t n_heads;
   uint32_t kind;            // SegKind
-  uint32_t cache;           // cache slot (0 / 1) for the row address and position
-  uint32_t plane;           // cache plane written / read
   uint32_t pass_begin;
+  uint32_t n_heads;
+  uint32_t cache;           // cache slot (0 / 1) for the row address and position
+  // the rest, read after the metadata chain
+  void* dst;                // dense output (SEG_Q)
+  int64_t dst_row_stride;   // elements between tokens in dst
+  const void* gamma;        // [D] of dtype, or nullptr: no norm
+  float eps;
+  uint32_t plane;           // cache plane written / read
   uint32_t n_passes;
   uint32_t pad_;
 };
@@ -95,29 +98,33 @@ struct ScaleDesc {
 };
 
 struct BandArgs {
-  SegDesc seg[kMaxSegs];
-  CacheDesc cache[kMaxCaches];
-  const uint32_t* offsets;  // [batch + 1]
-  const void* freqs;        // [max_seq_len][rope_dim] of freq_dtype
-  uint32_t nseg;
-  uint32_t ncache;
-  uint32_t batch;
-  uint32_t total_tokens;
-  uint32_t batch_offset;
-  uint32_t rope_dim;
-  uint32_t max_seq_len;     // 0: positions unchecked (no rotation)
-  float weight_offset;      // already rounded to the dtype
-  uint32_t multiply_before_cast;
-  uint32_t passes_per_token;
-  uint32_t passes_per_group;
-  uint32_t groups_per_token;
+  // Everything a wave needs before its segment lookup, in the first 64
+  // bytes, so that the prologue is one round of scalar loads.
   uint32_t n_items;         // total_tokens * groups_per_token waves of work
   uint32_t n_blocks;        // blocks holding work
   uint32_t waves_per_block; // 1 .. kMaxWavesPerBlock
   uint32_t per_xcd;         // blocks per XCD after the XCD-contiguous remap (0: no remap)
+  uint32_t passes_per_token;
+  uint32_t passes_per_group;
+  uint32_t groups_per_token;
+  uint32_t inplace_segs;    // bit i: segment i reads its rows from the cache (SEG_K_INPLACE)
+  uint32_t seg_begin[kMaxSegs - 1];  // seg[i + 1].pass_begin, 0xFFFFFFFF past nseg
+  uint32_t rope_dim;
+  uint32_t rope_off_chunks; // first rotated 16-byte chunk of a head (0: the leading dims)
+  uint32_t batch;
+  uint32_t nseg;
+  uint32_t ncache;
+  SegDesc seg[kMaxSegs];
+  CacheDesc cache[kMaxCaches];
+  const uint32_t* offsets;  // [batch + 1]
+  const void* freqs;        // [max_seq_len][rope_dim] of freq_dtype
+  uint32_t total_tokens;
+  uint32_t batch_offset;
+  uint32_t max_seq_len;     // 0: positions unchecked (no rotation)
+  float weight_offset;      // already rounded to the dtype
+  uint32_t multiply_before_cast;
   uint64_t guess_mul;       // floor(batch * 2^32 / total_tokens): token -> first sequence guess
   uint32_t freq_dtype;      // DT_F32, DT_BF16 or DT_F16 table entries
-  uint32_t rope_off_chunks; // first rotated 16-byte chunk of a head (0: the leading dims)
   // Padded [batch][seq_len] token grid (continuous batching): token t is
   // row t % seq_len of sequence t / seq_len; rows at or past the sequence's
   // valid length pass through.  Unused by the ragged ops.
@@ -125,6 +132,7 @@ struct BandArgs {
   uint32_t seq_len;
   ScaleDesc scale[kMaxCaches];
 };
+static_assert(offsetof(BandArgs, seg) == 64, "the hot header fills one 64-byte line");
 
 enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8 = 3 };
 
