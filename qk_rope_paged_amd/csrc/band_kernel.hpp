@@ -633,20 +633,21 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       }
     }
   } else {
-    // The guess's offsets and cache lengths are fetched together, so a
-    // decode wave pays one scalar-load latency before its page-table lookup.
+    // The guess's offsets and both caches' lengths in one round (pointers
+    // first; with one cache the second pointer names the first cache's
+    // array, a valid load whose value goes unused), so a decode wave pays one
+    // load latency before its page-table lookup.
+    const uint32_t B = a.batch;
+    const uint32_t* const cl0 = a.cache[0].cache_lengths + a.batch_offset;
+    const uint32_t* const cl1 =
+        (a.ncache > 1 ? a.cache[1].cache_lengths : a.cache[0].cache_lengths) + a.batch_offset;
     uint32_t g = (uint32_t)(((uint64_t)t * a.guess_mul) >> 32);
-    g = g < a.batch ? g : a.batch - 1;
-    uint32_t clen_guess[kMaxCaches] = {0, 0};
-#pragma unroll
-    for (int ci = 0; ci < kMaxCaches; ++ci)
-      if ((uint32_t)ci < a.ncache) clen_guess[ci] = a.cache[ci].cache_lengths[g + a.batch_offset];
+    g = g < B ? g : B - 1;
+    const uint32_t cg0 = cl0[g], cg1 = cl1[g];
     bool hit;
-    b = find_seq(a.offsets, a.batch, g, t, start, end, hit);
-#pragma unroll
-    for (int ci = 0; ci < kMaxCaches; ++ci)
-      if ((uint32_t)ci < a.ncache)
-        clen[ci] = hit ? clen_guess[ci] : a.cache[ci].cache_lengths[b + a.batch_offset];
+    b = find_seq(a.offsets, B, g, t, start, end, hit);
+    clen[0] = hit ? cg0 : cl0[b];
+    clen[1] = hit ? cg1 : cl1[b];
   }
   bool ok = !dead && start <= t && t < end;
   const uint32_t local = t - start;
