@@ -518,19 +518,31 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   const bool dead = blk >= a.n_blocks || item_raw >= n_items;
   const uint32_t item = dead ? n_items - 1 : item_raw;
 
-  // Gammas of every segment, once per block, in LDS.  Reading them there
-  // keeps the store loop free of vector-memory loads (vmcnt counts stores as
-  // well as loads, so a load issued after a store would wait for it).
-  __shared__ uint4 lds_gamma[NORM ? kMaxSegs : 1][NORM ? CH : 1];
+  // Gammas of every segment, per wave, in LDS.  Reading them there keeps the
+  // store loop free of vector-memory loads (vmcnt counts stores as well as
+  // loads, so a load issued after a store would wait for it).  The gamma
+  // loads issue first, ahead of the buffer loads; each wave writes its own
+  // copy when phase E starts (it waits for its data there anyway), so no
+  // barrier holds the metadata chain.  LDS operations of one wave execute in
+  // order: the reads that follow see the write.
+  __shared__ uint4 lds_gamma[NORM ? kMaxWavesPerBlock : 1][NORM ? kMaxSegs : 1][NORM ? CH : 1];
+  constexpr uint32_t GPT = NORM ? (kMaxSegs * CH + 63) / 64 : 1;  // chunks per lane
+  uint4 gst[GPT];
   if constexpr (NORM) {
-    for (uint32_t i = threadIdx.x; i < kMaxSegs * CH; i += blockDim.x) {
+#pragma unroll
+    for (uint32_t k = 0; k < GPT; ++k) {
+      const uint32_t i = lane + 64 * k;
       const uint32_t si = i / CH, c = i % CH;
-      uint4 g = make_uint4(0, 0, 0, 0);
-      if (si < a.nseg && a.seg[si].gamma != nullptr)
-        g = ld16(reinterpret_cast<const T*>(a.seg[si].gamma) + c * E);
-      lds_gamma[si][c] = g;
+      // the segment differs across lanes: select among the uniform
+      // (scalar-loaded) pointers rather than index the argument array
+      const void* gp = nullptr;
+#pragma unroll
+      for (uint32_t q = 0; q < (uint32_t)kMaxSegs; ++q)
+        if (si == q && q < a.nseg) gp = a.seg[q].gamma;
+      gst[k] = make_uint4(0, 0, 0, 0);
+      if (i < kMaxSegs * CH && gp != nullptr)
+        gst[k] = ld16(reinterpret_cast<const T*>(gp) + c * E);
     }
-    __syncthreads();
   }
 
   const uint32_t t = item / a.groups_per_token;
@@ -722,6 +734,13 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
 
 
   // ---- E: arithmetic and stores ----
+  if constexpr (NORM) {
+#pragma unroll
+    for (uint32_t k = 0; k < GPT; ++k) {
+      const uint32_t i = lane + 64 * k;
+      if (i < kMaxSegs * CH) lds_gamma[wave][i / CH][i % CH] = gst[k];
+    }
+  }
 #pragma unroll
   for (int p = 0; p < NPMAX; ++p) {
     if ((uint32_t)p < np) {
@@ -815,8 +834,8 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
               ss = row_sum<LPR>(ss);
               const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + sd.eps);
               float g0[E], g1[E];
-              unpack<T>(lds_gamma[si][c0], g0);
-              unpack<T>(lds_gamma[si][c1], g1);
+              unpack<T>(lds_gamma[wave][si][c0], g0);
+              unpack<T>(lds_gamma[wave][si][c1], g1);
               const float w = a.weight_offset;
               if (a.multiply_before_cast) {
 #pragma unroll
