@@ -475,19 +475,37 @@ __device__ __forceinline__ void load_freqs(const BandArgs& a, uint32_t pos, uint
 // them.  Returns the block's first dword, passed through the asm, so that
 // the caller's work depends on the fetch.
 template <uint32_t BYTES>
-__device__ __forceinline__ uint32_t touch_args() {
+__device__ __forceinline__ void line_words(uint32_t (&v)[12]) {
   using kptr = const uint32_t __attribute__((address_space(4)))*;
   const kptr k = (kptr)__builtin_amdgcn_kernarg_segment_ptr();
   constexpr uint32_t N = (BYTES + 63) / 64;
   static_assert(N >= 1 && N <= 12, "one asm operand per line");
-  uint32_t v[12];
 #pragma unroll
   for (uint32_t i = 0; i < 12; ++i) {
     const uint32_t l = i < N ? i : N - 1;
     v[i] = k[l + 1 < N ? l * 16 : (BYTES - 4) / 4];  // the last line: the block's last dword
   }
+}
+
+template <uint32_t BYTES>
+__device__ __forceinline__ uint32_t touch_args() {
+  uint32_t v[12];
+  line_words<BYTES>(v);
   asm("" : "+s"(v[0]) : "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5]), "s"(v[6]),
       "s"(v[7]), "s"(v[8]), "s"(v[9]), "s"(v[10]), "s"(v[11]));
+  return v[0];
+}
+
+// The same, also passing four 64-bit values through the statement (the norm
+// kernels' gamma pointers, their first loads' addresses), so that they are
+// loaded in the same round.
+template <uint32_t BYTES>
+__device__ __forceinline__ uint32_t touch_args(uint64_t (&p)[4]) {
+  uint32_t v[12];
+  line_words<BYTES>(v);
+  asm("" : "+s"(v[0]), "+s"(p[0]), "+s"(p[1]), "+s"(p[2]), "+s"(p[3])
+      : "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5]), "s"(v[6]), "s"(v[7]), "s"(v[8]),
+        "s"(v[9]), "s"(v[10]), "s"(v[11]));
   return v[0];
 }
 
@@ -505,8 +523,19 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   static_assert(LPR >= 4 && LPR <= 32, "unsupported head_dim / dtype");
 
   static_assert(offsetof(BandArgs, n_items) == 0, "the fetch returns n_items");
-  const uint32_t n_items =
-      touch_args<QUANT ? (uint32_t)sizeof(BandArgs) : (uint32_t)offsetof(BandArgs, scale)>();
+  constexpr uint32_t ARG_BYTES =
+      QUANT ? (uint32_t)sizeof(BandArgs) : (uint32_t)offsetof(BandArgs, scale);
+  // norm kernels: every segment's gamma pointer (null for unused segments,
+  // whose descriptors are zero), fetched with the argument lines
+  uint64_t gpv[kMaxSegs] = {0, 0, 0, 0};
+  uint32_t n_items;
+  if constexpr (NORM) {
+#pragma unroll
+    for (int q = 0; q < kMaxSegs; ++q) gpv[q] = (uint64_t)a.seg[q].gamma;
+    n_items = touch_args<ARG_BYTES>(gpv);
+  } else {
+    n_items = touch_args<ARG_BYTES>();
+  }
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Waves past the work (a last block's spare waves, blocks the XCD remap
@@ -535,13 +564,19 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       const uint32_t si = i / CH, c = i % CH;
       // the segment differs across lanes: select among the uniform
       // (scalar-loaded) pointers rather than index the argument array
-      const void* gp = nullptr;
+      uint64_t gp = 0;
 #pragma unroll
       for (uint32_t q = 0; q < (uint32_t)kMaxSegs; ++q)
-        if (si == q && q < a.nseg) gp = a.seg[q].gamma;
+        if (si == q) gp = gpv[q];
       gst[k] = make_uint4(0, 0, 0, 0);
-      if (i < kMaxSegs * CH && gp != nullptr)
-        gst[k] = ld16(reinterpret_cast<const T*>(gp) + c * E);
+      // a global-memory pointer again (an integer cast would give a flat
+      // load, which also counts against the scalar loads' wait counter)
+      using v4u = unsigned int __attribute__((ext_vector_type(4)));
+      using gptr = const v4u __attribute__((address_space(1)))*;
+      if (i < kMaxSegs * CH && gp != 0) {
+        const v4u w = ((gptr)gp)[c];
+        gst[k] = make_uint4(w.x, w.y, w.z, w.w);
+      }
     }
   }
 
