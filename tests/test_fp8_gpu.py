@@ -10,7 +10,7 @@ match bit for bit.  Cases: every op (store, single-band norm with K from the
 buffer and in place, dual band, radd, padded grid), every input dtype, both
 layouts, f32 and bf16 scales, head_dim 64 / 128 / 256, the workloads at
 reduced and full size, every Q output dtype pair over plain and FP8 caches,
-and bit-identical results across launch configurations.
+and bit-identical results across launch configurations (XCD remap on and off).
 """
 from __future__ import annotations
 
@@ -129,18 +129,19 @@ def test_fp8_launch_configuration_does_not_change_bits(workload, monkeypatch):
     gh, _ = _gpu()
     case = sc.WORKLOADS[workload](small=True)
     ref = None
-    for ppw in ("0", "1", "3"):
-        for wpb in ("0", "1", "4"):
-            monkeypatch.setenv("QRP_PASSES_PER_WAVE", ppw)
-            monkeypatch.setenv("QRP_WAVES_PER_BLOCK", wpb)
-            dc = gh.upload(case)
-            gh.run(dc)
-            torch.cuda.synchronize()
-            snap = [gh.to_numpy_bits(q, case.q_dtype) for q in dc.q_out]
-            snap += [gh.to_numpy_bits(c.pool, c.host.dtype) for c in dc.caches]
-            snap += [gh.to_numpy_bits(c.scales, c.host.scale_dtype) for c in dc.caches]
-            if ref is None:
-                ref = snap
-            else:
-                for i, (x, y) in enumerate(zip(ref, snap)):
-                    assert np.array_equal(x, y), f"{workload} ppw={ppw} wpb={wpb}: buffer {i}"
+    for remap, ppw, wpb in [(r, p, w) for r in ("0", "1") for p in ("0", "1", "3")
+                            for w in ("0", "1", "4")]:
+        monkeypatch.setenv("QRP_XCD_REMAP", remap)
+        monkeypatch.setenv("QRP_PASSES_PER_WAVE", ppw)
+        monkeypatch.setenv("QRP_WAVES_PER_BLOCK", wpb)
+        dc = gh.upload(case)
+        gh.run(dc)
+        torch.cuda.synchronize()
+        snap = [gh.to_numpy_bits(q, case.q_dtype) for q in dc.q_out]
+        snap += [gh.to_numpy_bits(c.pool, c.host.dtype) for c in dc.caches]
+        snap += [gh.to_numpy_bits(c.scales, c.host.scale_dtype) for c in dc.caches]
+        if ref is None:
+            ref = snap
+        else:
+            for i, (x, y) in enumerate(zip(ref, snap)):
+                assert np.array_equal(x, y), f"{workload} remap={remap} ppw={ppw} wpb={wpb}: buffer {i}"
