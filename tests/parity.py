@@ -18,7 +18,11 @@ The bar:
   x*cos - y*sin can cancel: a bound relative to |v| alone would demand more
   than binary32 arithmetic can give.  ulps = 1 ("one ulp of the 16-bit
   type on a value computed in binary32"); 2 for multiply_before_cast =
-  false, whose intermediate roundings can flip.
+  false, whose intermediate roundings can flip.  With multiply_before_cast
+  false the normalised rows are also measured at the scale of m: both values
+  of a pair are rounded to the 16-bit type before the rotation, so a flipped
+  rounding moves a value by one ulp of its own size (at most m), and the
+  rotation carries that error to v however small cancellation makes |v|.
 """
 from __future__ import annotations
 
@@ -34,26 +38,32 @@ class Report(dict):
     pass
 
 
-def tol_ok(gpu_bits: np.ndarray, exact: np.ndarray, mag: np.ndarray, dtype: str, ulps: int):
+def tol_ok(gpu_bits: np.ndarray, exact: np.ndarray, mag: np.ndarray, dtype: str, ulps: int,
+           floor: float = None):
+    """``floor``: the fraction of the pair length m below which |v| is not
+    taken as the scale (default 2^-11 for f16, 2^-8 for bf16)."""
     g = sc.bits_to_f64(gpu_bits, dtype)
     if dtype == sc.F32:
         tol = 1e-5 * np.maximum(np.abs(exact), mag)
     elif dtype == sc.F16:
-        tol = ulps * brute.ulp_f16(np.maximum(np.abs(exact), 2.0 ** -11 * mag))
+        f = 2.0 ** -11 if floor is None else floor
+        tol = ulps * brute.ulp_f16(np.maximum(np.abs(exact), f * mag))
     else:
-        tol = ulps * brute.ulp_bf16(np.maximum(np.abs(exact), 2.0 ** -8 * mag))
+        f = 2.0 ** -8 if floor is None else floor
+        tol = ulps * brute.ulp_bf16(np.maximum(np.abs(exact), f * mag))
     return np.abs(g - exact) <= tol
 
 
 def check_rows(gpu: np.ndarray, ora: np.ndarray, exact: np.ndarray, mag: np.ndarray,
-               copy_cols: np.ndarray, dtype: str, ulps: int, what: str, rep: Report):
+               copy_cols: np.ndarray, dtype: str, ulps: int, what: str, rep: Report,
+               floor: float = None):
     """Rows [N, D]: copy columns bit-exact, the others within tolerance."""
     if gpu.size == 0:
         return
     assert np.array_equal(gpu[:, copy_cols], ora[:, copy_cols]), f"{what}: copied dims differ"
     comp = ~copy_cols
     g, o = gpu[:, comp], ora[:, comp]
-    ok = tol_ok(g, exact[:, comp], mag[:, comp], dtype, ulps)
+    ok = tol_ok(g, exact[:, comp], mag[:, comp], dtype, ulps, floor)
     if not ok.all():
         bad = np.argwhere(~ok)[:5]
         det = [(int(r), int(c), float(sc.bits_to_f64(g[r, c], dtype)), float(exact[:, comp][r, c]),
@@ -121,6 +131,8 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
     pools (for a pool other writers share)."""
     assert res.status == 0, f"oracle status {res.status}"
     rep = Report()
+    # normalised rows rounded before the rotation: measured at the pair's scale
+    pair_floor = 1.0 if (case.op in ("norm", "dual") and not case.multiply_before_cast) else None
     dt = case.dtype
     qdt = case.q_dtype
     T = case.T
@@ -149,7 +161,8 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
             tr = res.traces[qi]
             check_rows(rows[:, :Hq * D].reshape(-1, D), ora[:, :Hq * D].reshape(-1, D),
                        tr["q_exact"].reshape(-1, D), tr["q_mag"].reshape(-1, D),
-                       _copy_cols(D, case.rope_dim, qn, case.rope_tail), qdt, ulps, f"q{qi}", rep)
+                       _copy_cols(D, case.rope_dim, qn, case.rope_tail), qdt, ulps, f"q{qi}", rep,
+                       pair_floor if qn else None)
     # ---- caches ----
     for ci, dcache in enumerate(dc.caches):
         host = dcache.host
@@ -182,7 +195,7 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
             else:
                 check_rows(g_flat[idx], o_flat[idx], tr["k_exact"].reshape(-1, D)[live],
                            tr["k_mag"].reshape(-1, D)[live], _copy_cols(D, case.rope_dim, kn, case.rope_tail),
-                           dt, ulps, f"k{qi}", rep)
+                           dt, ulps, f"k{qi}", rep, pair_floor if kn else None)
             # written K rows are checked: blank them before the bitwise comparison
             g_flat[idx] = 0
             o_flat[idx] = 0
