@@ -26,7 +26,7 @@ import oracle  # noqa: E402
 from synth import cases as sc  # noqa: E402
 
 OPS = ("store", "norm", "dual", "radd", "bshd")
-N_PER_OP = 12
+N_PER_OP = 24
 MSL = 512
 
 
