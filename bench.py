@@ -46,7 +46,8 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 KERNEL_NAME = "band_kernel"
 KERNEL_SOURCES = ("qk_rope_paged_amd/csrc/band_kernel.hpp", "qk_rope_paged_amd/csrc/kernels.hip",
                   "qk_rope_paged_amd/csrc/kernels_fp8.hip", "qk_rope_paged_amd/csrc/kernels_qout.hip",
-                  "qk_rope_paged_amd/csrc/engine.hpp", "qk_rope_paged_amd/csrc/abi.cpp")
+                  "qk_rope_paged_amd/csrc/kernels_pack.hip", "qk_rope_paged_amd/csrc/engine.hpp",
+                  "qk_rope_paged_amd/csrc/abi.cpp")
 
 
 def log(*a):
@@ -164,7 +165,8 @@ def case_tokens(case) -> int:
     return len(cache_rows(case)[1]) if case.op == "bshd" else case.T
 
 
-DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5, "bshd": 6}
+DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5, "bshd": 6, "prefill_tp8": 2,
+                "dual_tp8": 4}
 DEFAULT_SEED.update({f"{k}_fp8": v for k, v in list(DEFAULT_SEED.items())})
 
 
@@ -371,7 +373,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "dual", "radd", "bshd", "prefill_fp8",
-                             "decode_fp8", "dual_fp8", "radd_fp8", "bshd_fp8"])
+                             "decode_fp8", "dual_fp8", "radd_fp8", "bshd_fp8", "prefill_tp8",
+                             "dual_tp8"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-max-passes", type=int, default=30)

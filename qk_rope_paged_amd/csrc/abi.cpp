@@ -148,6 +148,7 @@ struct Builder {
   int32_t dtype = QRP_BF16;
   uint32_t head_dim = 0;
   uint32_t rpp = 0;
+  bool pack = false;  // token-packed passes
 
   void add_seg(qrp::SegKind kind, const void* src, int64_t src_stride, void* dst, int64_t dst_stride,
                const void* gamma, float eps, uint32_t n_heads, uint32_t cache, uint32_t plane) {
@@ -171,11 +172,41 @@ struct Builder {
   }
 
   // split tokens x passes into waves and blocks (one pass per wave: radd, and
-  // the padded grid, whose waves resolve their row with one division)
-  int32_t finish(uint32_t total_tokens, bool radd, bool one_pass = false) {
+  // the padded grid, whose waves resolve their row with one division).
+  // allow_pack: the op has a token-packed build (the ragged ops, Q in the
+  // op's dtype).
+  int32_t finish(uint32_t total_tokens, bool radd, bool one_pass = false,
+                 bool allow_pack = false) {
     bool norm = false;
     for (uint32_t s = 0; s < a.nseg; ++s) norm = norm || a.seg[s].gamma != nullptr;
     const uint32_t npmax = qrp::max_passes(radd, norm);
+    // Per-token passes leave lanes idle when a segment's head count is not a
+    // multiple of the rows a pass holds (a GPU's share of the heads under
+    // head parallelism: 4 Q, 1 K, 1 V heads fill 6 of 24 rows).  Below 85 %
+    // of rows filled, the token-packed layout is used: one pass per head,
+    // over a block of rpp consecutive tokens (one row each).  QRP_PACK=0 / 1
+    // forces it off / on.
+    uint32_t units = total_tokens;  // waves' work units: tokens, or token blocks
+    if (allow_pack) {
+      uint64_t rows = 0, slots = 0;
+      for (uint32_t s = 0; s < a.nseg; ++s) {
+        rows += a.seg[s].n_heads;
+        slots += (uint64_t)a.seg[s].n_passes * rpp;
+      }
+      pack = rows * 100 < slots * 85;
+      const int forced_pack = env_int("QRP_PACK", -1);
+      if (forced_pack >= 0) pack = forced_pack != 0;
+    }
+    if (pack) {
+      uint32_t pb = 0;
+      for (uint32_t s = 0; s < a.nseg; ++s) {
+        a.seg[s].pass_begin = pb;
+        a.seg[s].n_passes = a.seg[s].n_heads;
+        pb += a.seg[s].n_heads;
+      }
+      a.passes_per_token = pb;
+      units = (total_tokens + rpp - 1) / rpp;
+    }
     const uint32_t ppt = a.passes_per_token;
     if (ppt == 0) return fail(QRP_EINVAL, "no head rows to process");  // keeps n_items >= 1
     uint32_t ppg = std::min<uint32_t>(npmax, ppt);
@@ -190,13 +221,13 @@ struct Builder {
     } else {
       // enough waves to cover every SIMD a few times over: shrink the group
       const uint64_t want = 4096;
-      while (ppg > 1 && (uint64_t)total_tokens * ((ppt + ppg - 1) / ppg) < want) --ppg;
+      while (ppg > 1 && (uint64_t)units * ((ppt + ppg - 1) / ppg) < want) --ppg;
     }
     for (uint32_t i = 1; i < (uint32_t)qrp::kMaxSegs; ++i)
       a.seg_begin[i - 1] = i < a.nseg ? a.seg[i].pass_begin : 0xFFFFFFFFu;
     a.passes_per_group = ppg;
     a.groups_per_token = (ppt + ppg - 1) / ppg;
-    const uint64_t items = (uint64_t)total_tokens * a.groups_per_token;
+    const uint64_t items = (uint64_t)units * a.groups_per_token;
     if (items >= (1ull << 31)) return fail(QRP_EINVAL, "batch too large for one launch");
     a.n_items = (uint32_t)items;
     // Large rope/store launches run one wave per block (measured faster);
@@ -223,6 +254,7 @@ int32_t launch(const Builder& b, bool interleaved, bool radd, void* stream, bool
   s.interleaved = interleaved;
   s.radd = radd;
   s.bshd = bshd;
+  s.pack = b.pack;
   const int e = qrp::launch_band(b.a, s, stream);
   if (e != 0)
     return fail(QRP_EHIP, std::string("kernel launch failed: ") +
@@ -347,7 +379,7 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
             0, nullptr, 0.f, (uint32_t)Hk, 0, 0);
   b.add_seg(qrp::SEG_V_COPY, elem_ptr(qkv, (n_q_heads + Hk) * D, dtype), (int64_t)qkv_row_stride,
             nullptr, 0, nullptr, 0.f, (uint32_t)Hk, 0, 1);
-  if ((st = b.finish(total_seq_len, false))) return st;
+  if ((st = b.finish(total_seq_len, false, false, q_out_dtype == dtype))) return st;
   return launch(b, rope->interleaved != 0, false, stream, false, q_out_dtype);
 }
 
@@ -385,7 +417,7 @@ int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq
   b.a.weight_offset = to_dtype(dtype, weight_offset);
   b.a.multiply_before_cast = multiply_before_cast != 0;
   add_band(b, band, qkv, qkv_row_stride, dtype, 0);
-  if ((st = b.finish(total_seq_len, false))) return st;
+  if ((st = b.finish(total_seq_len, false, false, true))) return st;
   return launch(b, rope->interleaved != 0, false, stream);
 }
 
@@ -436,7 +468,7 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
   // rows [q_main | k_main | q_index | k_index]
   add_band(b, main_band, buf, buf_row_stride, dtype, 0);
   add_band(b, index_band, buf, buf_row_stride, dtype, 1);
-  if ((st = b.finish(total_seq_len, false))) return st;
+  if ((st = b.finish(total_seq_len, false, false, true))) return st;
   return launch(b, rope->interleaved != 0, false, stream);
 }
 
@@ -472,7 +504,7 @@ int32_t kv_cache_radd(const void* a, int32_t dtype, uint32_t total_rows, uint64_
   b.add_seg(qrp::SEG_RADD, a, (int64_t)a_row_stride, nullptr, 0, nullptr, 0.f, (uint32_t)Hk, 0, 0);
   b.add_seg(qrp::SEG_RADD, elem_ptr(a, Hk * D, dtype), (int64_t)a_row_stride, nullptr, 0, nullptr,
             0.f, (uint32_t)Hk, 0, 1);
-  if ((st = b.finish(total_rows, true))) return st;
+  if ((st = b.finish(total_rows, true, false, true))) return st;
   return launch(b, true, true, stream);
 }
 

@@ -512,9 +512,10 @@ __device__ __forceinline__ uint32_t touch_args(uint64_t (&p)[4]) {
 // T: input (and norm / plain cache) element type; QT: Q output element type;
 // CT: cache element type (T, or Fp8 with a scale per row).
 template <typename T, typename QT, typename CT, int D, bool IL, int NPMAX, bool RADD, bool NORM,
-          bool BSHD>
+          bool BSHD, bool PACK = false>
 __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   constexpr bool QUANT = std::is_same_v<CT, Fp8>;
+  static_assert(!(PACK && BSHD), "the padded grid has no token-packed layout");
   static_assert(QUANT || std::is_same_v<CT, T>, "a cache holds the op dtype or FP8");
   constexpr int E = Fmt<T>::E;
   constexpr int CH = D / E;      // 16-byte chunks per head row
@@ -580,13 +581,26 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
     }
   }
 
-  const uint32_t t = item / a.groups_per_token;
-  const uint32_t p0 = (item - t * a.groups_per_token) * a.passes_per_group;
+  // A wave's unit: one token (its passes cover the token's head rows, RPP
+  // heads of one segment per pass), or with PACK a block of RPP consecutive
+  // tokens (a pass is one head of one segment, one row per token: nothing
+  // idles when segments have fewer heads than a pass has rows).
+  const uint32_t unit = item / a.groups_per_token;
+  const uint32_t p0 = (item - unit * a.groups_per_token) * a.passes_per_group;
   const uint32_t np = min(a.passes_per_group, a.passes_per_token - p0);
 
   // this lane's row within a pass and its two chunks within the row
   const uint32_t row = lane / LPR;
   const uint32_t j = lane % LPR;
+  // this row's token: wave-uniform, or per row with PACK (rows past the last
+  // token read the last one's rows and write nothing)
+  uint32_t t = unit;
+  bool tok_ok = true;
+  if constexpr (PACK) {
+    const uint32_t tr = unit * RPP + row;
+    tok_ok = tr < a.total_tokens;
+    t = tok_ok ? tr : a.total_tokens - 1;
+  }
   // The rotated dims are chunks oc .. oc + rope_dim/E - 1 (oc = 0, or the
   // last rope_dim dims of the head).  Half-split, leading dims: lanes j < hh
   // hold rotated chunk j and its partner j + hh, the other lanes two of the
@@ -624,7 +638,8 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       const uint32_t kp = p0 + p;
       const SegDesc& sd = a.seg[seg_of(a, kp)];
       // the address before the branch: one scalar-load round for the fields
-      const uint32_t h = min((kp - sd.pass_begin) * RPP + row, sd.n_heads - 1);
+      const uint32_t h = min(PACK ? kp - sd.pass_begin : (kp - sd.pass_begin) * RPP + row,
+                             sd.n_heads - 1);
       const T* src = reinterpret_cast<const T*>(sd.src) + (int64_t)t * sd.src_row_stride +
                      (int64_t)h * D;
       if (!((a.inplace_segs >> seg_of(a, kp)) & 1u)) {
@@ -696,7 +711,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
     clen[0] = hit ? cg0 : cl0[b];
     clen[1] = hit ? cg1 : cl1[b];
   }
-  bool ok = !dead && start <= t && t < end;
+  bool ok = !dead && tok_ok && start <= t && t < end;
   const uint32_t local = t - start;
   const uint32_t cseq = b + a.batch_offset;
   uint32_t pos[kMaxCaches] = {0, 0};
@@ -721,8 +736,15 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
                     (int64_t)slot * a.scale[ci].s_slot_stride;
     }
   }
-  if (!ok) return;  // out-of-range metadata: this token writes nothing
-  if (pass) rot0 = rot1 = false;  // a passed-through row is copied as it is
+  // out-of-range metadata: this token writes nothing.  With PACK the rows of
+  // one wave belong to different tokens: such rows stay (their wave's LDS
+  // gamma copy and row reductions need every lane) and are masked below.
+  if constexpr (!PACK) {
+    if (!ok) return;
+  }
+  // a passed-through row is copied as it is; a row that writes nothing
+  // (PACK) reads no freqs row either: its position is unchecked
+  if (pass || !ok) rot0 = rot1 = false;
 
   // ---- C: loads from the cache (in-place K, radd accumulator) ----
   float rsc[QUANT ? NPMAX : 1];  // FP8: scale of the row read
@@ -733,9 +755,10 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
     if ((uint32_t)p < np) {
       const uint32_t kp = p0 + p;
       const SegDesc& sd = a.seg[seg_of(a, kp)];
-      if ((sd.kind == SEG_K_INPLACE && !pass) || (RADD && sd.kind == SEG_RADD)) {
+      if (((sd.kind == SEG_K_INPLACE && !pass) || (RADD && sd.kind == SEG_RADD)) && ok) {
         const CacheDesc& cd = a.cache[sd.cache];
-        const uint32_t h = min((kp - sd.pass_begin) * RPP + row, sd.n_heads - 1);
+        const uint32_t h = min(PACK ? kp - sd.pass_begin : (kp - sd.pass_begin) * RPP + row,
+                               sd.n_heads - 1);
         const int64_t roff =
             base[sd.cache] + (int64_t)sd.plane * cd.plane_stride + (int64_t)h * cd.head_stride;
         uint4 r0, r1;
@@ -783,8 +806,8 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       const uint32_t si = seg_of(a, kp);
       const SegDesc& sd = a.seg[si];
       const uint32_t kind = sd.kind;
-      const uint32_t h = (kp - sd.pass_begin) * RPP + row;
-      const bool active = h < sd.n_heads && !(BSHD && pass && kind != SEG_Q);
+      const uint32_t h = PACK ? kp - sd.pass_begin : (kp - sd.pass_begin) * RPP + row;
+      const bool active = ok && h < sd.n_heads && !(BSHD && pass && kind != SEG_Q);
       T* dst;
       if (kind == SEG_Q) {
         dst = reinterpret_cast<T*>(sd.dst) + (int64_t)t * sd.dst_row_stride + (int64_t)h * D;
@@ -958,32 +981,34 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
 }
 
 template <typename T, typename QT, typename CT, int D, bool IL, int NPMAX, bool RADD, bool NORM,
-          bool BSHD>
+          bool BSHD, bool PACK>
 int launch_np(const BandArgs& a, void* stream) {
   const uint32_t grid = a.per_xcd ? a.per_xcd * kXcds : a.n_blocks;
-  hipLaunchKernelGGL((band_kernel<T, QT, CT, D, IL, NPMAX, RADD, NORM, BSHD>), dim3(grid),
+  hipLaunchKernelGGL((band_kernel<T, QT, CT, D, IL, NPMAX, RADD, NORM, BSHD, PACK>), dim3(grid),
                      dim3(64 * a.waves_per_block), 0, reinterpret_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
 // Store kernels built for one pass per wave hold fewer registers (more
 // waves resident); they run whenever the launch gives each wave one pass.
-template <typename T, typename QT, typename CT, int D, bool IL, bool RADD, bool NORM, bool BSHD>
+template <typename T, typename QT, typename CT, int D, bool IL, bool RADD, bool NORM, bool BSHD,
+          bool PACK>
 int launch_t(const BandArgs& a, void* stream) {
   constexpr int NPMAX = RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : kMaxPassesStore);
   if constexpr (!RADD && !NORM && NPMAX > 1) {
     if (a.passes_per_group == 1)
-      return launch_np<T, QT, CT, D, IL, 1, RADD, NORM, BSHD>(a, stream);
+      return launch_np<T, QT, CT, D, IL, 1, RADD, NORM, BSHD, PACK>(a, stream);
   }
-  return launch_np<T, QT, CT, D, IL, NPMAX, RADD, NORM, BSHD>(a, stream);
+  return launch_np<T, QT, CT, D, IL, NPMAX, RADD, NORM, BSHD, PACK>(a, stream);
 }
 
-template <typename T, typename QT, typename CT, bool IL, bool RADD, bool NORM, bool BSHD>
+template <typename T, typename QT, typename CT, bool IL, bool RADD, bool NORM, bool BSHD,
+          bool PACK = false>
 int launch_d(const BandArgs& a, uint32_t head_dim, void* stream) {
   switch (head_dim) {
-    case 64: return launch_t<T, QT, CT, 64, IL, RADD, NORM, BSHD>(a, stream);
-    case 128: return launch_t<T, QT, CT, 128, IL, RADD, NORM, BSHD>(a, stream);
-    case 256: return launch_t<T, QT, CT, 256, IL, RADD, NORM, BSHD>(a, stream);
+    case 64: return launch_t<T, QT, CT, 64, IL, RADD, NORM, BSHD, PACK>(a, stream);
+    case 128: return launch_t<T, QT, CT, 128, IL, RADD, NORM, BSHD, PACK>(a, stream);
+    case 256: return launch_t<T, QT, CT, 256, IL, RADD, NORM, BSHD, PACK>(a, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }
@@ -995,17 +1020,23 @@ inline bool has_norm(const BandArgs& a) {
 }
 
 // Every op for one (input, cache) element-type pair; Q in the input dtype.
-template <typename T, typename CT>
+// PACK: the token-packed layout (ragged ops only).
+template <typename T, typename CT, bool PACK = false>
 int launch_ops(const BandArgs& a, const LaunchSpec& s, void* stream) {
-  if (s.radd) return launch_d<T, T, CT, true, true, false, false>(a, s.head_dim, stream);
-  if (s.bshd)
-    return s.interleaved ? launch_d<T, T, CT, true, false, false, true>(a, s.head_dim, stream)
-                         : launch_d<T, T, CT, false, false, false, true>(a, s.head_dim, stream);
+  if (s.radd) return launch_d<T, T, CT, true, true, false, false, PACK>(a, s.head_dim, stream);
+  if (s.bshd) {
+    if constexpr (PACK)
+      return (int)hipErrorInvalidValue;
+    else
+      return s.interleaved ? launch_d<T, T, CT, true, false, false, true>(a, s.head_dim, stream)
+                           : launch_d<T, T, CT, false, false, false, true>(a, s.head_dim, stream);
+  }
   if (has_norm(a))
-    return s.interleaved ? launch_d<T, T, CT, true, false, true, false>(a, s.head_dim, stream)
-                         : launch_d<T, T, CT, false, false, true, false>(a, s.head_dim, stream);
-  return s.interleaved ? launch_d<T, T, CT, true, false, false, false>(a, s.head_dim, stream)
-                       : launch_d<T, T, CT, false, false, false, false>(a, s.head_dim, stream);
+    return s.interleaved
+               ? launch_d<T, T, CT, true, false, true, false, PACK>(a, s.head_dim, stream)
+               : launch_d<T, T, CT, false, false, true, false, PACK>(a, s.head_dim, stream);
+  return s.interleaved ? launch_d<T, T, CT, true, false, false, false, PACK>(a, s.head_dim, stream)
+                       : launch_d<T, T, CT, false, false, false, false, PACK>(a, s.head_dim, stream);
 }
 
 // The rope / split / store op with Q in its own dtype.

@@ -145,6 +145,7 @@ struct LaunchSpec {
   bool interleaved;
   bool radd;
   bool bshd;                // padded [batch][seq_len] grid
+  bool pack;                // token-packed passes (one head of a block of tokens)
 };
 
 // Largest passes-per-wave the kernel for this op holds in registers.
@@ -154,10 +155,11 @@ inline uint32_t max_passes(bool radd, bool norm) {
 
 // Launch the band engine; returns 0 or a hipError_t value.
 int launch_band(const BandArgs& a, const LaunchSpec& s, void* stream);
-// The three translation units behind it.
+// The translation units behind it.
 int launch_plain(const BandArgs& a, const LaunchSpec& s, void* stream);
 int launch_fp8(const BandArgs& a, const LaunchSpec& s, void* stream);
 int launch_qout(const BandArgs& a, const LaunchSpec& s, void* stream);
+int launch_pack(const BandArgs& a, const LaunchSpec& s, void* stream);
 
 // Rows handled per 64-lane pass for a dtype / head_dim.
 inline uint32_t rows_per_pass(int32_t dtype, uint32_t head_dim) {

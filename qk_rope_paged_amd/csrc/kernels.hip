@@ -1,5 +1,6 @@
 // kernels.hip -- the band engine's launches for caches of the op's own
-// dtype, and the dispatch to the FP8-cache and Q-dtype translation units.
+// dtype, and the dispatch to the FP8-cache, Q-dtype and token-packed
+// translation units.
 #include "band_kernel.hpp"
 
 namespace qrp {
@@ -11,6 +12,7 @@ int launch_plain(const BandArgs& a, const LaunchSpec& s, void* stream) {
 }
 
 int launch_band(const BandArgs& a, const LaunchSpec& s, void* stream) {
+  if (s.pack) return launch_pack(a, s, stream);
   if (s.q_dtype != s.dtype) return launch_qout(a, s, stream);
   if (s.cache_fp8) return launch_fp8(a, s, stream);
   return launch_plain(a, s, stream);

@@ -621,6 +621,32 @@ def bshd(seed: int = 6, small: bool = False, cache_dtype: Optional[str] = None) 
                           max_seq_len=8192, capacity=8192, L=1, layer=0, cache_dtype=cache_dtype)
 
 
+def prefill_tp8(seed: int = 2, small: bool = False, cache_dtype: Optional[str] = None) -> Case:
+    """The prefill at one GPU's share under 8-way head (tensor) parallelism:
+    a column-parallel QKV projection leaves each GPU Hq/8 = 4 Q heads and
+    Hk/8 = 1 KV head, against a cache holding that one head."""
+    B = 4 if small else 8
+    lens = prng.integers(seed, S_LENS, B, 1, 300) if small else \
+        prng.integers(seed, S_LENS, B, 128, 2048)
+    return make_store_case(_kv("prefill_tp8_small" if small else "prefill_tp8", cache_dtype),
+                           seed, BF16, lens, np.zeros(B, np.int64), Hq=4, Hk=1, D=128,
+                           rope_dim=128, interleaved=False, theta=5e5, max_seq_len=8192, P=128,
+                           L=4 if small else 32, layer=2 if small else 17,
+                           cache_dtype=cache_dtype)
+
+
+def dual_tp8(seed: int = 4, small: bool = False, cache_dtype: Optional[str] = None) -> Case:
+    """The dual band at one GPU's share under 8-way head parallelism: main
+    band 8 Q heads and 1 KV head; index band 2 Q heads and its single K head
+    (a one-head cache cannot split: every rank keeps it whole)."""
+    B = 4 if small else 16
+    lens = prng.integers(seed, S_LENS, B, 1, 150 if small else 1024)
+    return make_dual_case(_kv("dual_tp8_small" if small else "dual_tp8", cache_dtype), seed,
+                          BF16, lens, Hq_main=8, Hk_main=1, Hq_index=2, D=128, rope_dim=64,
+                          interleaved=True, theta=1e4, max_seq_len=8192, P_main=64, P_index=64,
+                          main_cache_dtype=cache_dtype, index_cache_dtype=cache_dtype)
+
+
 def _with_cache(fn, cache_dtype):
     def make(seed: Optional[int] = None, small: bool = False) -> Case:
         return fn(small=small, cache_dtype=cache_dtype) if seed is None else \
@@ -630,7 +656,7 @@ def _with_cache(fn, cache_dtype):
 
 
 WORKLOADS = {"tiny_fp32": tiny_fp32, "prefill": prefill, "decode": decode, "dual": dual,
-             "radd": radd, "bshd": bshd}
+             "radd": radd, "bshd": bshd, "prefill_tp8": prefill_tp8, "dual_tp8": dual_tp8}
 # the same workloads over FP8 caches (bf16 inputs; f32 scales, one per row)
 WORKLOADS.update({f"{k}_fp8": _with_cache(WORKLOADS[k], FP8)
                   for k in ("prefill", "decode", "dual", "radd", "bshd")})

@@ -239,3 +239,27 @@ def test_trailing_rope_equals_leading_rope_on_rolled_heads(il):
     kt = _bits(dt.caches[0].pool, sc.BF16).reshape(shape)[:, 0]
     kl = np.roll(_bits(dl.caches[0].pool, sc.BF16).reshape(shape)[:, 0], D - R, axis=-1)
     assert np.array_equal(kt, kl)
+
+
+@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "prefill_tp8",
+                                      "dual_tp8", "prefill_fp8", "decode_fp8", "dual_fp8",
+                                      "radd_fp8"])
+def test_token_packed_layout_gives_the_same_bits(workload, monkeypatch):
+    """The token-packed layout (a pass is one head of a block of consecutive
+    tokens) and the per-token layout compute every row alike: forced on and
+    off, every output row, cache element and scale is bit-identical, also for
+    head counts that would not pick packing by themselves."""
+    _, gh, _ = _env()
+    case = sc.WORKLOADS[workload](small=True)
+    snaps = []
+    for pack in ("0", "1"):
+        monkeypatch.setenv("QRP_PACK", pack)
+        dc = gh.upload(case)
+        gh.run(dc)
+        torch.cuda.synchronize()
+        snap = [gh.to_numpy_bits(q, case.q_dtype) for q in dc.q_out]
+        snap += [gh.to_numpy_bits(c.pool, c.host.dtype) for c in dc.caches]
+        snap += [gh.to_numpy_bits(c.scales, c.host.scale_dtype) for c in dc.caches
+                 if c.scales is not None]
+        snaps.append(snap)
+    _assert_same(snaps[0], snaps[1], f"{workload}: packed and per-token layouts")
