@@ -56,11 +56,14 @@ def trace(args) -> str:
                    f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
     band = [(k, v) for k, v in by.items() if BAND in k]
     if args.warmup is not None and args.steps:
-        for name, v in band:
-            timed = [x[0] / 1e3 for x in v[args.warmup:args.warmup + args.steps]]
-            out += ["", f"Timed region of the bench (launches {args.warmup} to "
-                        f"{args.warmup + len(timed) - 1} of `{name[:60]}...`): "
-                        f"average {statistics.mean(timed):.2f} us over {len(timed)} launches."]
+        # every band-kernel launch in launch order: batches whose waves hold
+        # one pass run the one-pass build, so one run can use two builds
+        seq = [dur for name, dur, *_ in rows if BAND in name]
+        timed = [d / 1e3 for d in seq[args.warmup:args.warmup + args.steps]]
+        names = ", ".join(f"`{k[:60]}...`" for k, _ in band)
+        out += ["", f"Timed region of the bench (band-kernel launches {args.warmup} to "
+                    f"{args.warmup + len(timed) - 1}, of {names}): "
+                    f"average {statistics.mean(timed):.2f} us over {len(timed)} launches."]
     for name, v in band:
         out += ["", f"`{name}`: LDS {v[0][5]} bytes, {v[0][2]} threads per block.", "",
                 "| grid threads (one batch) | launches | avg us | min us |", "|---|---|---|---|"]
