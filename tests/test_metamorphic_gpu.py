@@ -145,8 +145,12 @@ def test_validate_on_device():
     assert "same cache row" in qrp.last_error()
 
 
-def test_out_of_range_tokens_are_skipped():
+@pytest.mark.parametrize("pack", ["0", "1"])
+def test_out_of_range_tokens_are_skipped(pack, monkeypatch):
+    """Per-token layout: the token's wave leaves; token-packed layout: the
+    token's rows stay in their wave, masked (QRP_PACK forces either)."""
     _, gh, parity = _env()
+    monkeypatch.setenv("QRP_PACK", pack)
     lens, clen = [6, 9, 4], [10, 30, 5]
     good = sc.make_store_case("oob", 41, sc.BF16, lens, clen, Hq=8, Hk=2, D=128, rope_dim=128,
                               interleaved=True, theta=1e4, max_seq_len=512, P=16, L=1, layer=0)
