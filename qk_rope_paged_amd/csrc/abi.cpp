@@ -219,8 +219,11 @@ struct Builder {
       // per wave measured fastest for both
       ppg = 1;
     } else {
-      // enough waves to cover every SIMD a few times over: shrink the group
-      const uint64_t want = 4096;
+      // enough waves to cover every SIMD a few times over: shrink the group.
+      // A packed wave resolves the metadata of a block of tokens, so fewer,
+      // fuller waves pay off sooner (measured: 2 passes per wave for the
+      // store op and 3 for the norm op at 8-way head parallelism's shapes).
+      const uint64_t want = pack ? 2048 : 4096;
       while (ppg > 1 && (uint64_t)units * ((ppt + ppg - 1) / ppg) < want) --ppg;
     }
     for (uint32_t i = 1; i < (uint32_t)qrp::kMaxSegs; ++i)
