@@ -166,7 +166,7 @@ def case_tokens(case) -> int:
 
 
 DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5, "bshd": 6, "prefill_tp8": 2,
-                "dual_tp8": 4}
+                "decode_tp8": 3, "dual_tp8": 4}
 DEFAULT_SEED.update({f"{k}_fp8": v for k, v in list(DEFAULT_SEED.items())})
 
 
@@ -374,7 +374,7 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "dual", "radd", "bshd", "prefill_fp8",
                              "decode_fp8", "dual_fp8", "radd_fp8", "bshd_fp8", "prefill_tp8",
-                             "dual_tp8"])
+                             "decode_tp8", "dual_tp8"])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-max-passes", type=int, default=30)

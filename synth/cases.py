@@ -635,6 +635,19 @@ def prefill_tp8(seed: int = 2, small: bool = False, cache_dtype: Optional[str] =
                            cache_dtype=cache_dtype)
 
 
+def decode_tp8(seed: int = 3, small: bool = False, cache_dtype: Optional[str] = None) -> Case:
+    """The decode at one GPU's share under 8-way head parallelism: 4 Q heads
+    and 1 KV head per token."""
+    B = 32 if small else 256
+    lens = np.ones(B, dtype=np.int64)
+    clen = prng.integers(seed, S_CLEN, B, 0, 8191)
+    return make_store_case(_kv("decode_tp8_small" if small else "decode_tp8", cache_dtype), seed,
+                           BF16, lens, clen, Hq=4, Hk=1, D=128, rope_dim=128, interleaved=True,
+                           theta=5e5, max_seq_len=8192, P=128, L=1, layer=0,
+                           num_pages=1400 if small else 20000, max_pages=64,
+                           cache_dtype=cache_dtype)
+
+
 def dual_tp8(seed: int = 4, small: bool = False, cache_dtype: Optional[str] = None) -> Case:
     """The dual band at one GPU's share under 8-way head parallelism: main
     band 8 Q heads and 1 KV head; index band 2 Q heads and its single K head
@@ -656,7 +669,8 @@ def _with_cache(fn, cache_dtype):
 
 
 WORKLOADS = {"tiny_fp32": tiny_fp32, "prefill": prefill, "decode": decode, "dual": dual,
-             "radd": radd, "bshd": bshd, "prefill_tp8": prefill_tp8, "dual_tp8": dual_tp8}
+             "radd": radd, "bshd": bshd, "prefill_tp8": prefill_tp8, "decode_tp8": decode_tp8,
+             "dual_tp8": dual_tp8}
 # the same workloads over FP8 caches (bf16 inputs; f32 scales, one per row)
 WORKLOADS.update({f"{k}_fp8": _with_cache(WORKLOADS[k], FP8)
                   for k in ("prefill", "decode", "dual", "radd", "bshd")})

@@ -52,14 +52,14 @@ def test_tiny_fp32():
     run_and_compare(sc.tiny_fp32())
 
 
-@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "prefill_tp8", "dual_tp8"])
+@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "prefill_tp8", "decode_tp8", "dual_tp8"])
 @pytest.mark.parametrize("seed", [None, 101])
 def test_small_workloads(workload, seed):
     kw = {} if seed is None else {"seed": seed}
     run_and_compare(sc.WORKLOADS[workload](small=True, **kw))
 
 
-@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "prefill_tp8", "dual_tp8"])
+@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "prefill_tp8", "decode_tp8", "dual_tp8"])
 def test_full_size_workloads(workload):
     run_and_compare(sc.WORKLOADS[workload]())
 
