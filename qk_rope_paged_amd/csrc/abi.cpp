@@ -173,7 +173,7 @@ struct Builder {
 
   // split tokens x passes into waves and blocks (one pass per wave: radd, and
   // the padded grid, whose waves resolve their row with one division).
-  // allow_pack: the op has a token-packed build (the ragged ops, Q in the
+  // allow_pack: the op has a token-packed build (every op with Q in the
   // op's dtype).
   int32_t finish(uint32_t total_tokens, bool radd, bool one_pass = false,
                  bool allow_pack = false) {
@@ -554,7 +554,7 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
   b.a.multiply_before_cast = 1;
   b.add_seg(qrp::SEG_Q, q_proj, (int64_t)row, output, (int64_t)row, nullptr, 0.f, n_q_heads, 0, 0);
   b.add_seg(qrp::SEG_K_INPLACE, nullptr, 0, nullptr, 0, nullptr, 0.f, cache->num_kv_heads, 0, 0);
-  if ((st = b.finish((uint32_t)tokens, false, true))) return st;
+  if ((st = b.finish((uint32_t)tokens, false, true, true))) return st;
   return launch(b, rope->interleaved != 0, false, stream, true);
 }
 

@@ -515,7 +515,6 @@ template <typename T, typename QT, typename CT, int D, bool IL, int NPMAX, bool 
           bool BSHD, bool PACK = false>
 __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   constexpr bool QUANT = std::is_same_v<CT, Fp8>;
-  static_assert(!(PACK && BSHD), "the padded grid has no token-packed layout");
   static_assert(QUANT || std::is_same_v<CT, T>, "a cache holds the op dtype or FP8");
   constexpr int E = Fmt<T>::E;
   constexpr int CH = D / E;      // 16-byte chunks per head row
@@ -1020,17 +1019,14 @@ inline bool has_norm(const BandArgs& a) {
 }
 
 // Every op for one (input, cache) element-type pair; Q in the input dtype.
-// PACK: the token-packed layout (ragged ops only).
+// PACK: the token-packed layout.
 template <typename T, typename CT, bool PACK = false>
 int launch_ops(const BandArgs& a, const LaunchSpec& s, void* stream) {
   if (s.radd) return launch_d<T, T, CT, true, true, false, false, PACK>(a, s.head_dim, stream);
-  if (s.bshd) {
-    if constexpr (PACK)
-      return (int)hipErrorInvalidValue;
-    else
-      return s.interleaved ? launch_d<T, T, CT, true, false, false, true>(a, s.head_dim, stream)
-                           : launch_d<T, T, CT, false, false, false, true>(a, s.head_dim, stream);
-  }
+  if (s.bshd)
+    return s.interleaved
+               ? launch_d<T, T, CT, true, false, false, true, PACK>(a, s.head_dim, stream)
+               : launch_d<T, T, CT, false, false, false, true, PACK>(a, s.head_dim, stream);
   if (has_norm(a))
     return s.interleaved
                ? launch_d<T, T, CT, true, false, true, false, PACK>(a, s.head_dim, stream)

@@ -245,9 +245,9 @@ def test_trailing_rope_equals_leading_rope_on_rolled_heads(il):
     assert np.array_equal(kt, kl)
 
 
-@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "prefill_tp8",
-                                      "dual_tp8", "prefill_fp8", "decode_fp8", "dual_fp8",
-                                      "radd_fp8"])
+@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "bshd", "prefill_tp8",
+                                      "decode_tp8", "dual_tp8", "prefill_fp8", "decode_fp8",
+                                      "dual_fp8", "radd_fp8", "bshd_fp8"])
 def test_token_packed_layout_gives_the_same_bits(workload, monkeypatch):
     """The token-packed layout (a pass is one head of a block of consecutive
     tokens) and the per-token layout compute every row alike: forced on and
