@@ -173,8 +173,7 @@ struct Builder {
 
   // split tokens x passes into waves and blocks (one pass per wave: radd, and
   // the padded grid, whose waves resolve their row with one division).
-  // allow_pack: the op has a token-packed build (every op with Q in the
-  // op's dtype).
+  // allow_pack: the op has a token-packed build.
   int32_t finish(uint32_t total_tokens, bool radd, bool one_pass = false,
                  bool allow_pack = false) {
     bool norm = false;
@@ -382,7 +381,7 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
             0, nullptr, 0.f, (uint32_t)Hk, 0, 0);
   b.add_seg(qrp::SEG_V_COPY, elem_ptr(qkv, (n_q_heads + Hk) * D, dtype), (int64_t)qkv_row_stride,
             nullptr, 0, nullptr, 0.f, (uint32_t)Hk, 0, 1);
-  if ((st = b.finish(total_seq_len, false, false, q_out_dtype == dtype))) return st;
+  if ((st = b.finish(total_seq_len, false, false, true))) return st;
   return launch(b, rope->interleaved != 0, false, stream, false, q_out_dtype);
 }
 

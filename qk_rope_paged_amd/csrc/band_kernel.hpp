@@ -1035,11 +1035,12 @@ int launch_ops(const BandArgs& a, const LaunchSpec& s, void* stream) {
                        : launch_d<T, T, CT, false, false, false, false, PACK>(a, s.head_dim, stream);
 }
 
-// The rope / split / store op with Q in its own dtype.
-template <typename T, typename QT, typename CT>
+// The rope / split / store op with Q in its own dtype (PACK: token-packed).
+template <typename T, typename QT, typename CT, bool PACK = false>
 int launch_store(const BandArgs& a, const LaunchSpec& s, void* stream) {
-  return s.interleaved ? launch_d<T, QT, CT, true, false, false, false>(a, s.head_dim, stream)
-                       : launch_d<T, QT, CT, false, false, false, false>(a, s.head_dim, stream);
+  return s.interleaved
+             ? launch_d<T, QT, CT, true, false, false, false, PACK>(a, s.head_dim, stream)
+             : launch_d<T, QT, CT, false, false, false, false, PACK>(a, s.head_dim, stream);
 }
 
 }  // namespace

@@ -12,8 +12,8 @@ int launch_plain(const BandArgs& a, const LaunchSpec& s, void* stream) {
 }
 
 int launch_band(const BandArgs& a, const LaunchSpec& s, void* stream) {
-  if (s.pack) return launch_pack(a, s, stream);
   if (s.q_dtype != s.dtype) return launch_qout(a, s, stream);
+  if (s.pack) return launch_pack(a, s, stream);
   if (s.cache_fp8) return launch_fp8(a, s, stream);
   return launch_plain(a, s, stream);
 }

@@ -1,6 +1,6 @@
 // kernels_qout.hip -- the rope / split / store launches whose Q output has
 // a dtype of its own (rope_split_store_paged_ragged page, Parameters:
-// q_out_dtype), for plain and FP8 caches.
+// q_out_dtype), for plain and FP8 caches, in both layouts.
 #include "band_kernel.hpp"
 
 namespace qrp {
@@ -8,6 +8,9 @@ namespace {
 
 template <typename T, typename QT>
 int launch_q(const BandArgs& a, const LaunchSpec& s, void* stream) {
+  if (s.pack)
+    return s.cache_fp8 ? launch_store<T, QT, Fp8, true>(a, s, stream)
+                       : launch_store<T, QT, T, true>(a, s, stream);
   return s.cache_fp8 ? launch_store<T, QT, Fp8>(a, s, stream) : launch_store<T, QT, T>(a, s, stream);
 }
 
