@@ -109,7 +109,7 @@ def test_half_split_equals_permuted_interleaved(R):
     assert np.array_equal(k_h, k_i)
 
 
-@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "bshd"])
+@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "bshd", "prefill_tp8", "dual_tp8"])
 def test_launch_configuration_does_not_change_bits(workload, monkeypatch):
     _, gh, _ = _env()
     case = sc.WORKLOADS[workload](small=True)
