@@ -19,8 +19,9 @@
 //     quantization granularity): tables, Q outputs and caches of other
 //     element types, FP8 caches with one scale per written row.
 //
-// The kernel template is instantiated by three translation units (plain
-// caches; FP8 caches; Q outputs in another dtype) that build in parallel.
+// The kernel template is instantiated by four translation units (plain
+// caches; FP8 caches; Q outputs in another dtype; the token-packed layout)
+// that build in parallel.
 //
 // How it maps onto the chip.  The pass is HBM-bound (about one flop per byte
 // moved), so there is no MFMA and no LDS staging of bulk data:
@@ -30,6 +31,13 @@
 //     a RoPE pair never leaves its lane: half-split lanes hold chunk c and
 //     chunk c + rope_dim/16 (bf16), interleaved lanes hold two chunks whose
 //     pairs are inside the chunk;
+//   * when segments have fewer heads than a pass has rows, the token-packed
+//     layout instead gives a wave a block of RPP consecutive tokens: a pass is
+//     one head of one segment, one row per token, and the metadata below is
+//     resolved per row;
+//   * every wave fetches each 64-byte line of the argument block in one round
+//     at entry (the block is written just before the launch, so its lines
+//     start cold);
 //   * all buffer loads of a wave's passes are issued before the token's
 //     metadata chain (offsets -> cache length -> page table) resolves, so the
 //     chain overlaps the data fetch; the metadata is wave-uniform and read
@@ -37,9 +45,10 @@
 //   * the freqs row of the token's position lives in registers and serves
 //     every head of the token (each lane always needs the same columns);
 //   * the per-head sum of squares is reduced across the row's lanes with DPP
-//     (quad_perm, row_half_mirror, row_mirror);
-//   * blocks are remapped so that each XCD works on a contiguous token range
-//     (blocks are dealt to the 8 XCDs round-robin).
+//     (quad_perm, row_half_mirror, row_mirror); gammas are staged in LDS, one
+//     copy per wave, with no block barrier;
+//   * an XCD-contiguous block remap is available (QRP_XCD_REMAP=1) but off by
+//     default: blocks are dealt to the 8 XCDs round-robin.
 #ifndef QRP_BAND_KERNEL_HPP
 #define QRP_BAND_KERNEL_HPP
 
