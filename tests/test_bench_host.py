@@ -1,0 +1,41 @@
+"""Host logic of bench.py, on the CPU: the byte model against a hand count,
+and the source hash that decides whether a committed counter summary still
+describes the kernels."""
+from __future__ import annotations
+
+import bench
+from synth import cases as sc
+
+
+def test_algorithmic_bytes_of_the_tiny_case_by_hand():
+    # tiny_fp32: fp32, 2 sequences of 3 and 5 tokens at cache lengths 0 and 4,
+    # 4 Q and 2 KV heads of 64, page size 16, rope width 64
+    case = sc.tiny_fp32()
+    head = 64 * 4
+    per_token = 4 * head * 2 + 2 * head * 2 + 2 * head * 2   # Q, K, V read and written
+    freqs = 8 * 64 * 4              # positions 0-2 and 4-8: 8 distinct rows
+    metadata = 3 * 4 + 2 * 4 + 2 * 4  # offsets, cache lengths, one page entry per sequence
+    assert bench.algorithmic_bytes(case) == 8 * per_token + freqs + metadata
+
+
+def test_code_only_strips_comments_and_keeps_literals():
+    src = ('int a = 1;  // trailing\n'
+           '/* block\n   comment */\n'
+           '\n'
+           'const char* s = "not // a comment /* either */";\n'
+           "char c = '/';  /* x */ int b = 2;\n")
+    assert bench._code_only(src) == ('int a = 1;\n'
+                                     'const char* s = "not // a comment /* either */";\n'
+                                     "char c = '/';   int b = 2;")
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    f = tmp_path / "k.hpp"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", ("k.hpp",))
+    f.write_text("int f() { return 1; }\n")
+    h0 = bench.kernel_source_hash()
+    f.write_text("// a note\nint f() { return 1; }  /* same code */\n\n")
+    assert bench.kernel_source_hash() == h0
+    f.write_text("int f() { return 2; }\n")
+    assert bench.kernel_source_hash() != h0
