@@ -141,7 +141,7 @@ def test_norm_on_one_role_only(q_norm, k_norm):
 def test_norm_multiply_after_cast(dtype):
     case = _norm("norm_mbc0", 16, dtype, [25, 9], [0, 31], False, multiply_before_cast=False,
                  weight_offset=0.5)
-    run_and_compare(case, ulps=2)
+    run_and_compare(case)
 
 
 def test_norm_head_dim_64_and_256():
