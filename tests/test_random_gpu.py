@@ -17,6 +17,8 @@ keyed by the case index, so a failure names a reproducible case.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -28,7 +30,8 @@ import oracle  # noqa: E402
 from synth import cases as sc  # noqa: E402
 
 OPS = ("store", "norm", "dual", "radd", "bshd")
-N_PER_OP = 24
+# cases per op; QRP_RANDOM_CASES=1000 runs the 5,000-case soak
+N_PER_OP = int(os.environ.get("QRP_RANDOM_CASES", "24"))
 MSL = 512
 
 
