@@ -37,6 +37,9 @@
  * Errors       Every call returns a qrp_status; qrp_last_error() gives text
  *              for the last failure on the calling thread.
  * Degenerate   total_seq_len == 0 returns QRP_OK without a launch.
+ * Size         One launch holds fewer than 2^31 work items (tokens times
+ *              pass groups, or token blocks times pass groups); a larger
+ *              batch returns QRP_EINVAL and is split by the caller.
  * Aliasing     Outputs must not overlap inputs or each other, except the
  *              in-place cache updates the operation defines.  Two written
  *              rows must not share a cache slot.
