@@ -29,8 +29,8 @@ The bar:
   adds half an ulp: 4.75 ulps at the scale of m, however small cancellation
   makes |v|.  Their FP8 scales may differ from the oracle's by 10 ulps of
   the input type, relative (the row's largest value moves by up to 5 ulps
-  at sqrt 2 times its size); their codes are checked at the GPU's own scale
-  as above.
+  at sqrt 2 times its size), and their codes are checked at the GPU's own
+  scale as above, plus those 5 ulps at the scale of m (5 eps m).
 """
 from __future__ import annotations
 
@@ -83,7 +83,7 @@ def check_rows(gpu: np.ndarray, ora: np.ndarray, exact: np.ndarray, mag: np.ndar
 
 def check_fp8_rows(codes: np.ndarray, scales: np.ndarray, ora_codes: np.ndarray,
                    ora_scales: np.ndarray, exact: np.ndarray, scale_dtype: str, what: str,
-                   rep: Report, flip_eps: float = 0.0):
+                   rep: Report, flip_eps: float = 0.0, mag: np.ndarray = None):
     """FP8 rows [N, D] with their scale bits [N]: each dequantized value within
     one E4M3 step (at the GPU's own scale) of the oracle's unrounded value,
     each scale close to the oracle's."""
@@ -96,6 +96,10 @@ def check_fp8_rows(codes: np.ndarray, scales: np.ndarray, ora_codes: np.ndarray,
     tol = s * brute.ulp_e4m3(np.abs(exact) / safe)
     if scale_dtype == sc.BF16:
         tol = tol + 2.0 ** -8 * np.max(np.abs(exact), axis=1, keepdims=True)
+    if flip_eps:
+        # the value before quantization: 5 ulps of the input type at the
+        # pair's scale (5 eps m bounds them)
+        tol = tol + 5 * flip_eps * mag
     ok = np.abs(deq - exact) <= tol
     if not ok.all():
         bad = np.argwhere(~ok)[:5]
@@ -201,7 +205,7 @@ def compare(case, dc: gh.DeviceCase, res, ulps: int = 1, untouched_pages: bool =
                 soff = tr["k_scale_off"].reshape(-1)[live]
                 check_fp8_rows(g_flat[idx], gs_flat[soff], o_flat[idx], os_flat[soff],
                                tr["k_exact"].reshape(-1, D)[live], host.scale_dtype, f"k{qi}",
-                               rep, flip_eps if kn else 0.0)
+                               rep, flip_eps if kn else 0.0, tr["k_mag"].reshape(-1, D)[live])
                 gs_flat[soff] = 0
                 os_flat[soff] = 0
             else:

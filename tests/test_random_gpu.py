@@ -5,7 +5,8 @@ draws, per case, the op and every option it takes at once: input dtype,
 head_dim, rope width and placement (leading or trailing dims), layout,
 freqs-table dtype, cache dtype (plain or FP8 with f32 / bf16 scales), Q
 output dtype, page size (1, powers of two and others), head counts, batch
-size on both sides of the small-batch threshold, ragged and empty sequences,
+size on both sides of the small-batch threshold and up to 512 sequences,
+ragged and empty sequences,
 cache lengths up to the table's end, and the norm op's switches; odd cases
 force the per-token layout, even ones let the library pick (mostly the
 token-packed layout at these head counts).  Every case
@@ -49,10 +50,13 @@ def _geometry(rng):
 
 def _batch(rng, lo=1, hi=20, max_len=12):
     B = int(rng.integers(lo, hi + 1))            # both sides of the 16-sequence threshold
+    top = MSL - max_len
+    if rng.random() < 0.2:                       # up to 512 short sequences (deep searches),
+        B, max_len, top = int(rng.integers(hi + 1, 513)), 3, 64   # short caches: small pools
     lens = rng.integers(0, max_len + 1, B)
     if lens.sum() == 0:
         lens[int(rng.integers(B))] = 1
-    clen = rng.integers(0, MSL - max_len, B)
+    clen = rng.integers(0, top, B)
     clen[rng.random(B) < 0.2] = 0
     return lens, clen
 
