@@ -376,7 +376,20 @@ def cpu_baseline(cases, seconds: float, max_passes: int) -> dict:
     return {"value": round(nbytes / total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} full passes over the first {min(passes, len(cases))} seeded "
                       f"batches ({ntok} tokens), {total:.1f} s of oracle time (C call only)",
-            "tokens_per_s": round(ntok / total, 1)}
+            "tokens_per_s": round(ntok / total, 1),
+            "host": {"nproc": os.cpu_count(), "cpu_model": _cpu_model()}}
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo (empty where it is absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def check_parity(case, dc, shared_pool: bool) -> str:

@@ -39,3 +39,8 @@ def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h0
     f.write_text("int f() { return 2; }\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_cpu_model_reads_proc_cpuinfo():
+    # a string on any host (empty where /proc/cpuinfo has no model line)
+    assert isinstance(bench._cpu_model(), str)
