@@ -14,7 +14,7 @@
  * intermediate roundings that flag asks for).  radd is one IEEE fp32 add.
  * Copies (V, un-roped dimensions of the rope-only op) move raw bits.
  *
- * Readings of points the pages leave open (each also listed in the design doc):
+ * Readings of points the pages leave open:
  *   - freqs_cis rows hold (cos, sin) pairs for frequency i at columns
  *     (2i, 2i+1) whatever the Q/K layout (the table is described as holding
  *     interleaved frequencies: rope_split_store_paged_ragged page, Args:
