@@ -3,6 +3,7 @@
 Every case runs on seeded synthetic inputs shaped like the five workloads
 (tiny fp32; Llama-3-8B prefill and decode; dual-band RMSNorm + RoPE; radd),
 at reduced sizes that still span many waves and a ragged tail, at full size,
+in a long-context prefill that reaches the last freqs row,
 and on edge cases (empty batch and sequences, page size 1, head_dim 64/256,
 fp32 and bf16, partial rope in both layouts, padded strides, special values,
 multiply_before_cast = false, K from the buffer or in the cache).
@@ -62,6 +63,20 @@ def test_small_workloads(workload, seed):
 @pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "prefill_tp8", "decode_tp8", "dual_tp8"])
 def test_full_size_workloads(workload):
     run_and_compare(sc.WORKLOADS[workload]())
+
+
+@pytest.mark.parametrize("cache_dtype", [None, sc.FP8])
+def test_long_context_prefill_to_the_table_end(cache_dtype):
+    # Llama-3-8B heads over sequences that reach the last freqs row: one of
+    # 8192 new tokens (positions 0..8191), one continuing a 4096-row cache to
+    # 8191, and two long ragged ones -- about 27k tokens, several generations
+    # of waves per SIMD and three times the prefill workload's batch
+    lens = np.array([8192, 4096, 7999, 7001], np.int64)
+    clen = np.array([0, 4096, 192, 0], np.int64)
+    run_and_compare(sc.make_store_case("long_context", 41, sc.BF16, lens, clen, Hq=32, Hk=8,
+                                       D=128, rope_dim=128, interleaved=False, theta=5e5,
+                                       max_seq_len=8192, P=128, L=4, layer=2,
+                                       cache_dtype=cache_dtype))
 
 
 # ---------------------------------------------------------------------------
