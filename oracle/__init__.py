@@ -117,6 +117,9 @@ def load() -> ctypes.CDLL:
                                            ctypes.POINTER(OrcCache), U32, P,
                                            ctypes.POINTER(OrcTrace)]
     lib.orc_fused_qk_rope_bshd.restype = I32
+    lib.orc_matmul_fused_partial_rmsnorm.argtypes = [P, U64, P, U64, P, U64, U32, P, U64, U32,
+                                                     U32, P, U32, F, F, I32, P, P, P]
+    lib.orc_matmul_fused_partial_rmsnorm.restype = I32
     _lib = lib
     return lib
 
@@ -329,3 +332,37 @@ def run_case(case, trace: bool = True, compact_over: int = 1 << 31) -> OracleRes
     res.seconds = time.perf_counter() - t0
     res.status = int(st)
     return res
+
+
+@dataclass
+class GemvResult:
+    status: int
+    seconds: float = 0.0
+    normed: Optional[np.ndarray] = None     # raw bits [m, normed_row_stride]
+    unnormed: Optional[np.ndarray] = None   # raw bits [m, unnormed_row_stride]
+    y_exact: Optional[np.ndarray] = None    # [m, n] y before rounding
+    abs_dot: Optional[np.ndarray] = None    # [m, n] sum_k |x_k w_jk|
+    r: Optional[np.ndarray] = None          # [m] reciprocal root of each row's norm
+
+
+def run_gemv(case, trace: bool = True) -> GemvResult:
+    """The fused GEMV + partial RMSNorm on a case from synth.cases.make_gemv_case
+    (duck-typed).  Outputs start as sentinels, so padding columns stay visible."""
+    lib = load()
+    dt = _DT[case.dtype]
+    m, n = case.m, case.n
+    x = np.ascontiguousarray(case.x)
+    w = np.ascontiguousarray(case.w)
+    g = np.ascontiguousarray(case.gamma)
+    normed = np.full((m, case.normed_row_stride), _SENT[case.dtype], dtype=_BITS[case.dtype])
+    unnormed = np.full((m, case.unnormed_row_stride), _SENT[case.dtype], dtype=_BITS[case.dtype])
+    y = np.zeros((m, n)) if trace else None
+    a = np.zeros((m, n)) if trace else None
+    r = np.zeros(m) if trace else None
+    t0 = time.perf_counter()
+    st = lib.orc_matmul_fused_partial_rmsnorm(
+        _ptr(normed), case.normed_row_stride, _ptr(unnormed), case.unnormed_row_stride,
+        _ptr(x), x.shape[1], m, _ptr(w), w.shape[1], n, case.k, _ptr(g), case.n_normed,
+        case.epsilon, case.weight_offset, dt, _ptr(y), _ptr(a), _ptr(r))
+    return GemvResult(status=int(st), seconds=time.perf_counter() - t0, normed=normed,
+                      unnormed=unnormed, y_exact=y, abs_dot=a, r=r)

@@ -727,3 +727,56 @@ int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t B, ui
   free(hb.x);
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* fused GEMV + partial RMSNorm                                        */
+/* ------------------------------------------------------------------ */
+
+int32_t orc_matmul_fused_partial_rmsnorm(
+    void* normed_output, uint64_t normed_row_stride, void* unnormed_output,
+    uint64_t unnormed_row_stride, const void* input, uint64_t input_row_stride, uint32_t m,
+    const void* weight, uint64_t weight_row_stride, uint32_t n, uint32_t k, const void* gamma,
+    uint32_t n_normed, float epsilon, float weight_offset, int32_t dtype, double* y_exact,
+    double* abs_dot, double* r_out) {
+  (void)weight_offset; /* not consumed (MatmulFusedPartialRMSNorm page, Args) */
+  if (!dtype_ok(dtype) || n_normed > n) return ORC_EINVAL;
+  if (m == 0 || n == 0) return ORC_OK;
+  if (!input || !weight || (n_normed && (!gamma || !normed_output)) ||
+      (n_normed < n && !unnormed_output))
+    return ORC_EINVAL;
+  double* y = (double*)malloc(sizeof(double) * n);
+  if (!y) return ORC_EINVAL;
+  for (uint32_t i = 0; i < m; ++i) {
+    /* the GEMV: y_j = sum_k x_k W[j][k] (bf16, f16 and f32 products are
+     * exact in double) */
+    for (uint32_t j = 0; j < n; ++j) {
+      double s = 0.0, a = 0.0;
+      for (uint32_t kk = 0; kk < k; ++kk) {
+        const double p = get(input, dtype, (int64_t)i * (int64_t)input_row_stride + kk) *
+                         get(weight, dtype, (int64_t)j * (int64_t)weight_row_stride + kk);
+        s += p;
+        a += fabs(p);
+      }
+      y[j] = s;
+      if (y_exact) y_exact[(uint64_t)i * n + j] = s;
+      if (abs_dot) abs_dot[(uint64_t)i * n + j] = a;
+    }
+    /* RMSNorm over the leading n_normed columns as one vector */
+    double r = 0.0;
+    if (n_normed) {
+      double ss = 0.0;
+      for (uint32_t j = 0; j < n_normed; ++j) ss += y[j] * y[j];
+      r = 1.0 / sqrt(ss / (double)n_normed + (double)epsilon);
+      for (uint32_t j = 0; j < n_normed; ++j)
+        put(normed_output, dtype, (int64_t)i * (int64_t)normed_row_stride + j,
+            y[j] * r * get(gamma, dtype, j));
+    }
+    if (r_out) r_out[i] = r;
+    /* the trailing columns pass through */
+    for (uint32_t j = n_normed; j < n; ++j)
+      put(unnormed_output, dtype, (int64_t)i * (int64_t)unnormed_row_stride + (j - n_normed),
+          y[j]);
+  }
+  free(y);
+  return ORC_OK;
+}

@@ -36,7 +36,11 @@
  *     scale rule are a reading (unpinned);
  *   - q_out_dtype (rope_split_store_paged_ragged page, Parameters): Q is
  *     rounded once to it; un-roped elements move as bits when it equals the
- *     input dtype and are converted (nearest-even) otherwise.
+ *     input dtype and are converted (nearest-even) otherwise;
+ *   - the fused GEMV + partial RMSNorm (MatmulFusedPartialRMSNorm page):
+ *     n_normed is the length of gamma and of a normed row; the norm's mean
+ *     runs over those n_normed columns only; epsilon sits inside the root,
+ *     as in the other RMSNorm ops; several input rows are independent.
  */
 #ifndef QRP_ORACLE_H
 #define QRP_ORACLE_H
@@ -164,6 +168,24 @@ int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t batch
                                int32_t rope_tail, orc_cache* cache, uint32_t layer_idx,
                                void* output,
                                orc_trace* trace);
+
+/* MatmulFusedPartialRMSNorm page (Summary, execute, Args): per input row i,
+ * y = x_i W^T with W stored [n][k] (the page's default transpose_b), then the
+ * first n_normed columns of y are RMS-normalised as one vector,
+ *   normed[i][j] = y_j / sqrt(mean_{j < n_normed} y_j^2 + epsilon) * gamma_j,
+ * and the other n - n_normed columns pass through:
+ *   unnormed[i][j - n_normed] = y_j.
+ * y is exact up to double rounding; each output is rounded once to dtype.
+ * weight_offset is taken and not used (Args: weight_offset).  The page names
+ * a GEMV (one input row); several rows are handled one after another.
+ * Optional traces: y_exact and abs_dot [m][n] (y, and sum_k |x_k w_jk|),
+ * r_out [m] (the row's reciprocal root; 0 when n_normed is 0). */
+int32_t orc_matmul_fused_partial_rmsnorm(
+    void* normed_output, uint64_t normed_row_stride, void* unnormed_output,
+    uint64_t unnormed_row_stride, const void* input, uint64_t input_row_stride, uint32_t m,
+    const void* weight, uint64_t weight_row_stride, uint32_t n, uint32_t k, const void* gamma,
+    uint32_t n_normed, float epsilon, float weight_offset, int32_t dtype, double* y_exact,
+    double* abs_dot, double* r_out);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,7 @@ NO_PAGE = np.uint32(0xFFFFFFFF)
 
 # stream numbers (one per generated array)
 S_LENS, S_CLEN, S_PERM, S_BUF, S_GAMMA, S_A, S_PREFILL, S_SPECIAL = 1, 2, 3, 4, 5, 6, 7, 8
+S_X, S_W = 9, 10
 
 
 def to_bits(values: np.ndarray, dtype: str) -> np.ndarray:
@@ -674,3 +675,57 @@ WORKLOADS = {"tiny_fp32": tiny_fp32, "prefill": prefill, "decode": decode, "dual
 # the same workloads over FP8 caches (bf16 inputs; f32 scales, one per row)
 WORKLOADS.update({f"{k}_fp8": _with_cache(WORKLOADS[k], FP8)
                   for k in ("prefill", "decode", "dual", "radd", "bshd")})
+
+
+# ---------------------------------------------------------------------------
+# fused GEMV + partial RMSNorm
+# ---------------------------------------------------------------------------
+
+@dataclass
+class GemvCase:
+    """y = x W^T for m input rows; the first n_normed columns RMS-normalised
+    with gamma, the rest passed through.  Arrays hold raw bits of dtype, row
+    strides in elements are the arrays' second dimensions (padding columns of
+    x and W hold sentinels) and the output strides below."""
+    name: str
+    seed: int
+    dtype: str
+    m: int
+    k: int
+    n: int
+    n_normed: int
+    x: np.ndarray                 # [m, x_stride]
+    w: np.ndarray                 # [n, w_stride]
+    gamma: np.ndarray             # [n_normed] (one element when n_normed is 0)
+    epsilon: float
+    weight_offset: float
+    normed_row_stride: int
+    unnormed_row_stride: int
+    op: str = "gemv_norm"
+
+
+def make_gemv_case(name: str, seed: int, dtype: str, m: int, k: int, n: int, n_normed: int,
+                   epsilon: float = 1e-6, weight_offset: float = 0.0, x_pad: int = 0,
+                   w_pad: int = 0, out_pad: int = 0) -> GemvCase:
+    """x ~ N(0, 1), W ~ N(0, 1/k) (so y is about N(0, 1)), gamma ~ N(1, 0.1)."""
+    x = np.full((m, k + x_pad), SENTINEL[dtype], dtype=BITS_DTYPE[dtype])
+    x[:, :k] = to_bits(prng.normal(seed, S_X, m * k), dtype).reshape(m, k)
+    w = np.full((n, k + w_pad), SENTINEL[dtype], dtype=BITS_DTYPE[dtype])
+    w[:, :k] = to_bits(prng.normal(seed, S_W, n * k, std=1.0 / np.sqrt(k)), dtype).reshape(n, k)
+    gamma = to_bits(prng.normal(seed, S_GAMMA, max(n_normed, 1), mean=1.0, std=0.1), dtype)
+    return GemvCase(name=name, seed=seed, dtype=dtype, m=m, k=k, n=n, n_normed=n_normed, x=x,
+                    w=w, gamma=gamma, epsilon=epsilon, weight_offset=weight_offset,
+                    normed_row_stride=max(n_normed, 1) + out_pad,
+                    unnormed_row_stride=max(n - n_normed, 1) + out_pad)
+
+
+def gemv_norm(seed: int = 7, small: bool = False) -> GemvCase:
+    """One input row (a GEMV) of hidden size 7168 into 1536 normed and 576
+    passed-through columns (the shape of a low-rank query / key-value
+    projection); bf16.  The small form keeps the split at a tenth the size."""
+    if small:
+        return make_gemv_case("gemv_norm_small", seed, BF16, 1, 704, 216, 152)
+    return make_gemv_case("gemv_norm", seed, BF16, 1, 7168, 2112, 1536)
+
+
+GEMV_WORKLOADS = {"gemv_norm": gemv_norm}

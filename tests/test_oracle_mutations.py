@@ -17,6 +17,7 @@ import pytest
 import oracle
 from tests import test_oracle_bshd_pins as bshd_pins
 from tests import test_oracle_fp8_pins as fp8_pins
+from tests import test_oracle_gemv_pins as gemv_pins
 from tests import test_oracle_pins as pins
 
 MUTATIONS = {
@@ -72,6 +73,25 @@ MUTATIONS = {
                                         "const uint32_t pos = s;"),
     "bshd_k_from_v_plane": ("int64_t dst = row_offset(c, page, 0, layer_idx, slot, h);",
                             "int64_t dst = row_offset(c, page, 1, layer_idx, slot, h);"),
+    "gemv_drops_last_k": ("for (uint32_t kk = 0; kk < k; ++kk) {",
+                          "for (uint32_t kk = 0; kk + 1 < k; ++kk) {"),
+    "gemv_x_row_ignored": ("get(input, dtype, (int64_t)i * (int64_t)input_row_stride + kk)",
+                           "get(input, dtype, kk)"),
+    "gemv_weight_stride_is_k": ("get(weight, dtype, (int64_t)j * (int64_t)weight_row_stride + kk)",
+                                "get(weight, dtype, (int64_t)j * (int64_t)k + kk)"),
+    "partial_norm_eps_outside_root": (
+        "r = 1.0 / sqrt(ss / (double)n_normed + (double)epsilon);",
+        "r = 1.0 / (sqrt(ss / (double)n_normed) + (double)epsilon);"),
+    "partial_norm_mean_over_all_columns": (
+        "r = 1.0 / sqrt(ss / (double)n_normed + (double)epsilon);",
+        "r = 1.0 / sqrt(ss / (double)n + (double)epsilon);"),
+    "partial_norm_sums_all_columns": ("for (uint32_t j = 0; j < n_normed; ++j) ss += y[j] * y[j];",
+                                      "for (uint32_t j = 0; j < n; ++j) ss += y[j] * y[j];"),
+    "partial_norm_gamma_reversed": ("y[j] * r * get(gamma, dtype, j));",
+                                    "y[j] * r * get(gamma, dtype, n_normed - 1 - j));"),
+    "partial_norm_uses_weight_offset": ("y[j] * r * get(gamma, dtype, j));",
+                                        "y[j] * r * (get(gamma, dtype, j) + weight_offset));"),
+    "unnormed_from_wrong_column": ("          y[j]);\n  }\n  free(y);", "          y[j - n_normed]);\n  }\n  free(y);"),
 }
 
 PIN_TESTS = [
@@ -102,6 +122,11 @@ PIN_TESTS = [
     (fp8_pins.test_fp8_store_k_rows_are_the_quantized_rotation,
      {"interleaved": True, "scale_dtype": "f32"}),
     (fp8_pins.test_fp8_radd_is_dequantize_add_requantize_bit_for_bit, {}),
+    (gemv_pins.test_gemv_matches_exact_rational_sums, {}),
+    (gemv_pins.test_partial_norm_closed_form, {}),
+    (gemv_pins.test_partial_norm_unit_mean_square_and_scale_invariance, {}),
+    (gemv_pins.test_weight_offset_is_not_consumed, {}),
+    (gemv_pins.test_rows_are_independent, {}),
 ]
 
 
