@@ -1,14 +1,16 @@
 #!/usr/bin/env python3
 """Throughput of the fused ragged RoPE + split + paged-KV store on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload prefill|decode|dual|radd|bshd]
+    python bench.py [--steps K] [--warmup W] [--workload prefill|decode|dual|radd|bshd|...]
 
 A step is one call of the pass over one batch of seeded synthetic input that
 is already resident in HBM.  The default workload is the Llama-3-8B-shaped
 prefill (32 Q / 8 KV heads, head_dim 128, bf16, half-split RoPE, theta 5e5,
 batch 8 with lengths U[128, 2048], page 128, 32 layers, layer 17).  Other
 workloads (decode, dual band, radd, padded continuous batching) are for
-measuring the other operations.
+measuring the other operations; `gemv_norm` measures the fused GEMV +
+partial RMSNorm (one bf16 row of 7168 into 1536 normed and 576 passed-through
+columns), a kernel of its own.
 
 The default warm-up (300 launches) is long on purpose: the first few
 hundred launches over multi-GB pools run a few per cent slower (clocks and
@@ -48,6 +50,12 @@ KERNEL_SOURCES = ("qk_rope_paged_amd/csrc/band_kernel.hpp", "qk_rope_paged_amd/c
                   "qk_rope_paged_amd/csrc/kernels_fp8.hip", "qk_rope_paged_amd/csrc/kernels_qout.hip",
                   "qk_rope_paged_amd/csrc/kernels_pack.hip", "qk_rope_paged_amd/csrc/engine.hpp",
                   "qk_rope_paged_amd/csrc/abi.cpp")
+# the fused GEMV + partial RMSNorm (MatmulFusedPartialRMSNorm page): its own
+# kernel, sources and workloads
+GEMV_KERNEL_NAME = "gemv_norm_kernel"
+GEMV_SOURCES = ("qk_rope_paged_amd/csrc/gemv_norm.hip", "qk_rope_paged_amd/csrc/gemv_norm.hpp",
+                "qk_rope_paged_amd/csrc/abi.cpp")
+GEMV_WORKLOADS = ("gemv_norm",)
 
 
 def log(*a):
@@ -79,14 +87,22 @@ def _code_only(text: str) -> str:
     return "\n".join(ln for ln in lines if ln)
 
 
-def kernel_source_hash() -> str:
+def kernel_name(workload: str) -> str:
+    return GEMV_KERNEL_NAME if workload in GEMV_WORKLOADS else KERNEL_NAME
+
+
+def kernel_source_hash(sources=None) -> str:
     """Hash of the code of the kernel sources: a counter summary taken on the
     same code stays valid across edits of comments."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
+
+
+def source_hash_for(workload: str) -> str:
+    return kernel_source_hash(GEMV_SOURCES if workload in GEMV_WORKLOADS else None)
 
 
 def traffic_from_profiles(workload: str, seeds):
@@ -94,7 +110,7 @@ def traffic_from_profiles(workload: str, seeds):
     committed counter summary (per-batch read and write bytes, already scaled
     by the copy calibration), or None when the summary is missing, lacks a
     batch, or was taken from a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel_name(workload)}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -103,7 +119,7 @@ def traffic_from_profiles(workload: str, seeds):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != source_hash_for(workload):
         return None
     total = 0.0
     try:
@@ -122,6 +138,8 @@ def algorithmic_bytes(case) -> int:
     from synth import cases as sc
 
     eb = sc.ELEM_BYTES[case.dtype]
+    if case.op == "gemv_norm":   # x and W read, gamma read, every output written
+        return eb * (case.m * case.k + case.n * case.k + case.n_normed + case.m * case.n)
     qeb = sc.ELEM_BYTES[case.q_dtype]
     T = case.T
     seq, pos = cache_rows(case)
@@ -188,23 +206,32 @@ def cache_rows(case):
 
 
 def case_tokens(case) -> int:
-    """Tokens a step processes (the padded grid counts its real rows only)."""
+    """Tokens a step processes (the padded grid counts its real rows only;
+    the GEMV its input rows)."""
+    if case.op == "gemv_norm":
+        return case.m
     return len(cache_rows(case)[1]) if case.op == "bshd" else case.T
 
 
 DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5, "bshd": 6, "prefill_tp8": 2,
                 "decode_tp8": 3, "dual_tp8": 4}
 DEFAULT_SEED.update({f"{k}_fp8": v for k, v in list(DEFAULT_SEED.items())})
+DEFAULT_SEED["gemv_norm"] = 7
 
 
 def make_case(workload: str, seed: int = None):
     from synth import cases as sc
-    fn = sc.WORKLOADS[workload]
+    fn = sc.GEMV_WORKLOADS[workload] if workload in GEMV_WORKLOADS else sc.WORKLOADS[workload]
     return fn(seed=DEFAULT_SEED[workload] if seed is None else seed)
 
 
 def workload_config(case, cases) -> dict:
     from synth import cases as sc
+    if case.op == "gemv_norm":
+        return {"workload": "matmul_fused_partial_rmsnorm:" + case.name, "rows": case.m,
+                "k": case.k, "n": case.n, "n_normed": case.n_normed,
+                "weights": "W [n][k] N(0, 1/k), x N(0, 1), gamma N(1, 0.1)",
+                "seeds": [x.seed for x in cases]}
     c = case.caches[0]
     cfg = {"workload": {"store": "rope_split_store_paged", "norm": "qk_rmsnorm_rope_paged",
                         "dual": "dual_band", "radd": "kv_cache_radd",
@@ -366,7 +393,8 @@ def cpu_baseline(cases, seconds: float, max_passes: int) -> dict:
     total, passes, nbytes, ntok = 0.0, 0, 0, 0
     while passes < max_passes and (passes == 0 or total < seconds):
         case = cases[passes % len(cases)]
-        res = oracle.run_case(case, trace=False)
+        res = oracle.run_gemv(case, trace=False) if case.op == "gemv_norm" else \
+            oracle.run_case(case, trace=False)
         if res.status != 0:
             raise RuntimeError(f"oracle failed with status {res.status}")
         total += res.seconds
@@ -397,6 +425,14 @@ def check_parity(case, dc, shared_pool: bool) -> str:
     the same result; in-place ops accumulate, so they are not checked here).
     With a shared pool the other sets' pages are not expected to hold the
     sentinel."""
+    if case.op == "gemv_norm":
+        import oracle
+        from tests import gemv_parity
+        from tests import gpu_harness as gh
+        res = oracle.run_gemv(case)
+        gemv_parity.check(case, res, gh.to_numpy_bits(dc.normed, case.dtype),
+                          gh.to_numpy_bits(dc.unnormed, case.dtype))
+        return "ok"
     if case.op != "store":
         return "not checked (in-place op applied repeatedly)"
     import oracle
@@ -414,7 +450,7 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "dual", "radd", "bshd", "prefill_fp8",
                              "decode_fp8", "dual_fp8", "radd_fp8", "bshd_fp8", "prefill_tp8",
-                             "decode_tp8", "dual_tp8"])
+                             "decode_tp8", "dual_tp8", *GEMV_WORKLOADS])
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-max-passes", type=int, default=30)
@@ -452,8 +488,12 @@ def main() -> int:
     log(f"[bench] {first.name}: {n_sets} seeded batches, tokens {[c.T for c in cases]}, "
         f"mean bytes/step {sum(set_bytes) / n_sets:.0f} (generated in "
         f"{time.perf_counter() - t_gen:.1f}s)")
-    sets, shared_pool = build_sets(cases)
-    calls = [gh.run(dc, prepare=True) for dc in sets]
+    if first.op == "gemv_norm":
+        sets, shared_pool = [gh.upload_gemv(c) for c in cases], False
+        calls = [gh.run_gemv(dg, prepare=True) for dg in sets]
+    else:
+        sets, shared_pool = build_sets(cases)
+        calls = [gh.run(dc, prepare=True) for dc in sets]
     torch.cuda.synchronize()
 
     if args.copy_calibration_mib:
@@ -510,7 +550,7 @@ def main() -> int:
         "parity": parity_status,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": KERNEL_NAME},
+                     "traffic": traffic, "kernel": kernel_name(args.workload)},
     }
     if not args.no_copy_ceiling:
         del sets, calls

@@ -10,13 +10,20 @@
  *                            "fused_dual_qk_rms_norm_rope_ragged_paged" page
  *   dual_band                "fused_dual_qk_rms_norm_rope_ragged_paged" page
  *   kv_cache_radd            "generic_kv_cache_radd_dispatch" page
+ *   fused_qk_rope_bshd_continuous_batch
+ *                            "generic_fused_qk_rope_bshd_continuous_batch" page
+ *   matmul_fused_partial_rmsnorm
+ *                            "MatmulFusedPartialRMSNorm" page (the GEMV that
+ *                            feeds such a pass, with a partial RMSNorm)
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Ownership    The caller allocates and owns every buffer.  The library
  *              allocates no device memory, keeps no pointer after a call
  *              returns and holds no global state apart from a thread-local
- *              error string.
+ *              error string.  The one op that needs scratch memory
+ *              (matmul_fused_partial_rmsnorm) takes a caller-owned
+ *              workspace.
  * Asynchrony   Each call checks its host-visible arguments, enqueues ONE
  *              kernel on `stream` (a hipStream_t passed as void*; NULL is the
  *              null stream) and returns without synchronising.
@@ -53,7 +60,7 @@
 extern "C" {
 #endif
 
-#define QRP_ABI_VERSION 3
+#define QRP_ABI_VERSION 4
 
 typedef enum qrp_status {
   QRP_OK = 0,
@@ -273,6 +280,48 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
                                             const uint32_t* valid_lengths, const qrp_rope* rope,
                                             const qrp_paged_cache* cache, uint32_t layer_idx,
                                             void* output, void* stream);
+
+/*
+ * MatmulFusedPartialRMSNorm page (Summary, execute, Args): a GEMV fused with
+ * a partial RMSNorm.  For each of the m input rows x_i (m = 1 is the page's
+ * GEMV; up to 8 rows per call, each independent):
+ *   y = x_i W^T,  W stored [n][k] row-major (the page's default transpose_b;
+ *                 transpose_b = 0 returns QRP_EUNSUPPORTED),
+ *   normed_output[i][j]   = y_j / sqrt(mean_{j' < n_normed} y_j'^2 + epsilon)
+ *                           * gamma_j                   for j <  n_normed,
+ *   unnormed_output[i][j - n_normed] = y_j              for j >= n_normed.
+ * The mean runs over the n_normed leading columns only (n_normed is gamma's
+ * length); weight_offset is accepted and not used (the page's Args say the
+ * kernel does not consume it).  Products and sums are binary32 (one fused
+ * multiply-add per term, then a fixed 64-way tree), the norm is binary32, and
+ * each output is rounded once to dtype (QRP_F32, QRP_BF16 or QRP_F16; x, W,
+ * gamma and both outputs share it).
+ * Layout: input [m][input_row_stride], weight [n][weight_row_stride],
+ * normed_output [m][normed_row_stride], unnormed_output
+ * [m][unnormed_row_stride], gamma [n_normed]; all device memory, strides in
+ * elements.  input, weight and workspace are 16-byte aligned, k and the
+ * input/weight strides are multiples of 16 bytes (QRP_EALIGN otherwise);
+ * outputs and gamma are element-aligned.
+ * Workspace: device memory the caller owns, at least
+ * qrp_gemv_norm_workspace_bytes(m, n_normed) bytes (0 when n_normed = 0:
+ * NULL is then allowed).  It must be zero-filled before its first use; every
+ * call leaves its counter at zero again, so it is reused without clearing.
+ * Calls that overlap in time must not share a workspace.
+ * Errors: QRP_EINVAL for a NULL buffer that the call needs, n_normed > n, a
+ * stride below its row or a short workspace; QRP_EUNSUPPORTED for m > 8,
+ * transpose_b = 0 or another dtype.  m == 0 or n == 0 returns QRP_OK
+ * without a launch; k == 0 gives y = 0.
+ */
+uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed);
+
+int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_stride,
+                                     void* unnormed_output, uint64_t unnormed_row_stride,
+                                     const void* input, uint64_t input_row_stride, uint32_t m,
+                                     const void* weight, uint64_t weight_row_stride, uint32_t n,
+                                     uint32_t k, const void* gamma, uint32_t n_normed,
+                                     float epsilon, float weight_offset, int32_t dtype,
+                                     int32_t transpose_b, void* workspace,
+                                     uint64_t workspace_bytes, void* stream);
 
 /*
  * Debug check of the device metadata one of the calls above would use:

@@ -54,14 +54,15 @@ def trace(args) -> str:
         d = [x[0] / 1e3 for x in v]
         out.append(f"| `{name[:110]}` | {len(d)} | {statistics.mean(d):.2f} | "
                    f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
-    band = [(k, v) for k, v in by.items() if BAND in k]
+    kern = args.kernel
+    band = [(k, v) for k, v in by.items() if kern in k]
     if args.warmup is not None and args.steps:
         # every band-kernel launch in launch order: batches whose waves hold
         # one pass run the one-pass build, so one run can use two builds
-        seq = [dur for name, dur, *_ in rows if BAND in name]
+        seq = [dur for name, dur, *_ in rows if kern in name]
         timed = [d / 1e3 for d in seq[args.warmup:args.warmup + args.steps]]
         names = ", ".join(f"`{k[:60]}...`" for k, _ in band)
-        out += ["", f"Timed region of the bench (band-kernel launches {args.warmup} to "
+        out += ["", f"Timed region of the bench ({kern} launches {args.warmup} to "
                     f"{args.warmup + len(timed) - 1}, of {names}): "
                     f"average {statistics.mean(timed):.2f} us over {len(timed)} launches."]
     for name, v in band:
@@ -81,12 +82,12 @@ def _pmc(path: str):
                             "order by dispatch_id"))
 
 
-def _per_kernel(rows, counter):
+def _per_kernel(rows, counter, kern=BAND):
     band, calib = [], []
     for did, name, cn, cv in rows:
         if cn != counter:
             continue
-        if BAND in name:
+        if kern in name:
             band.append(cv)
         elif name == CALIB:
             calib.append(cv)
@@ -97,11 +98,12 @@ def traffic(args) -> str:
     import bench
 
     calib_kib = args.calib_mib * 1024
-    fb, fc = _per_kernel(_pmc(args.fetch), "FETCH_SIZE")
-    wb, wc = _per_kernel(_pmc(args.write), "WRITE_SIZE")
+    kern = bench.kernel_name(args.workload)
+    fb, fc = _per_kernel(_pmc(args.fetch), "FETCH_SIZE", kern)
+    wb, wc = _per_kernel(_pmc(args.write), "WRITE_SIZE", kern)
     tcc = _pmc(args.tcc)
-    hits, _ = _per_kernel(tcc, "TCC_HIT_sum")
-    miss, _ = _per_kernel(tcc, "TCC_MISS_sum")
+    hits, _ = _per_kernel(tcc, "TCC_HIT_sum", kern)
+    miss, _ = _per_kernel(tcc, "TCC_MISS_sum", kern)
     # the calibration copy is the largest copyBuffer dispatch(es)
     fcal = [v for v in fc if v > 0.25 * calib_kib]
     wcal = [v for v in wc if v > 0.5 * calib_kib]
@@ -115,14 +117,14 @@ def traffic(args) -> str:
     for i, (f, w) in enumerate(zip(fb, wb)):
         per.setdefault(seeds[i % args.sets], []).append((f * 1024 * fscale, w * 1024 * wscale))
     hit_rate = [h / (h + m) for h, m in zip(hits, miss) if h + m > 0]
-    lines = [f"# HBM traffic of {bench.KERNEL_NAME} on the {args.workload} workload "
+    lines = [f"# HBM traffic of {kern} on the {args.workload} workload "
              f"(rocprofv3 PMC, one line per seeded batch)",
              f"# command: {args.command}",
              f"# calibration: a {args.calib_mib} MiB device copy in the same run read "
              f"{statistics.median(fcal):.1f} KiB by FETCH_SIZE and wrote "
              f"{statistics.median(wcal):.1f} KiB by WRITE_SIZE; the kernel's counts are "
              f"multiplied by fetch_scale and write_scale",
-             f"kernel_source_sha256: {bench.kernel_source_hash()}",
+             f"kernel_source_sha256: {bench.source_hash_for(args.workload)}",
              f"fetch_scale: {fscale:.5f}",
              f"write_scale: {wscale:.5f}"]
     tot_r = tot_w = tot_a = 0.0
@@ -156,6 +158,7 @@ def main() -> int:
     t.add_argument("--command", required=True)
     t.add_argument("--warmup", type=int, default=None, help="warm-up launches before the timed region")
     t.add_argument("--steps", type=int, default=0, help="launches in the timed region")
+    t.add_argument("--kernel", default=BAND, help="name (or part) of the kernel timed")
     p = sub.add_parser("traffic")
     p.add_argument("--fetch", required=True)
     p.add_argument("--write", required=True)

@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "QRP_OK", -1: "QRP_EINVAL", -2: "QRP_EALIGN", -3: "QRP_EUNSUP
 
 # entry points declared in include/qk_rope_paged.h
 EXPORTS = ("rope_split_store_paged", "qk_rmsnorm_rope_paged", "dual_band", "kv_cache_radd",
-           "fused_qk_rope_bshd_continuous_batch", "qrp_validate", "qrp_validate_host",
+           "fused_qk_rope_bshd_continuous_batch", "matmul_fused_partial_rmsnorm",
+           "qrp_gemv_norm_workspace_bytes", "qrp_validate", "qrp_validate_host",
            "qrp_last_error", "qrp_abi_version")
 
 
@@ -88,6 +89,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dual_band": [P, I32, U32, U64, PB, PB, F, I32, P, U32, PR, U32, P],
         "kv_cache_radd": [P, I32, U32, U64, P, U32, U32, PC, U32, P],
         "fused_qk_rope_bshd_continuous_batch": [P, I32, U32, U32, U32, P, PR, PC, U32, P, P],
+        "matmul_fused_partial_rmsnorm": [P, U64, P, U64, P, U64, U32, P, U64, U32, U32, P, U32,
+                                         F, F, I32, I32, P, U64, P],
         "qrp_validate": [P, U32, U32, U32, PC, U32, P],
         "qrp_validate_host": [P, U32, U32, U32, P, P, U32, U32, U32, U64, U32],
     }
@@ -97,6 +100,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = I32
     lib.qrp_last_error.argtypes = []
     lib.qrp_last_error.restype = ctypes.c_char_p
+    lib.qrp_gemv_norm_workspace_bytes.argtypes = [U32, U32]
+    lib.qrp_gemv_norm_workspace_bytes.restype = U64
     lib.qrp_abi_version.argtypes = []
     lib.qrp_abi_version.restype = I32
     return lib
@@ -288,6 +293,25 @@ def fused_qk_rope_bshd_continuous_batch(q_proj, dtype: int, batch_size: int, seq
     args = (_ptr(q_proj), dtype, batch_size, seq_len, n_q_heads, _ptr(valid_lengths),
             ctypes.byref(rc), ctypes.byref(cc), layer_idx, _ptr(output), _stream(stream))
     return _call(lib.fused_qk_rope_bshd_continuous_batch, args, [cc, rc], raise_on_error, prepare)
+
+
+def gemv_norm_workspace_bytes(m: int, n_normed: int) -> int:
+    return int(lib.qrp_gemv_norm_workspace_bytes(m, n_normed))
+
+
+def matmul_fused_partial_rmsnorm(normed_output, normed_row_stride: int, unnormed_output,
+                                 unnormed_row_stride: int, input, input_row_stride: int, m: int,
+                                 weight, weight_row_stride: int, n: int, k: int, gamma,
+                                 n_normed: int, epsilon: float, weight_offset: float, dtype: int,
+                                 workspace, workspace_bytes: int, transpose_b: int = 1,
+                                 stream=None, raise_on_error: bool = True, prepare: bool = False):
+    """The fused GEMV + partial RMSNorm; `workspace` is a zero-filled device
+    buffer of at least gemv_norm_workspace_bytes(m, n_normed) bytes."""
+    args = (_ptr(normed_output), normed_row_stride, _ptr(unnormed_output), unnormed_row_stride,
+            _ptr(input), input_row_stride, m, _ptr(weight), weight_row_stride, n, k, _ptr(gamma),
+            n_normed, epsilon, weight_offset, dtype, transpose_b, _ptr(workspace),
+            workspace_bytes, _stream(stream))
+    return _call(lib.matmul_fused_partial_rmsnorm, args, [], raise_on_error, prepare)
 
 
 def qrp_validate(input_row_offsets, batch_size: int, total_seq_len: int, batch_offset: int,

@@ -1,0 +1,48 @@
+// gemv_norm.hpp -- launch descriptor of the fused GEMV + partial RMSNorm
+// kernel (MatmulFusedPartialRMSNorm page: Summary, execute, Args).
+//
+// y = x W^T for up to kGemvMaxRows input rows; the first n_normed columns of
+// each row are RMS-normalised as one vector and scaled by gamma, the other
+// columns are stored as they are.  One wave computes cols_per_wave columns
+// over the whole of k; the columns that need the norm go to a binary32
+// workspace, and the last block of those to arrive normalises every row.
+#pragma once
+
+#include <stdint.h>
+
+namespace qrp {
+
+constexpr uint32_t kGemvMaxRows = 8;
+constexpr uint64_t kGemvCounterBytes = 256;  // the arrival counter's own line(s)
+
+struct GemvArgs {
+  const void* x;          // [m][x_stride] elements
+  const void* w;          // [n][w_stride] elements (W stored row-major, y = x W^T)
+  const void* gamma;      // [n_normed]
+  void* normed;           // [m][normed_stride]
+  void* unnormed;         // [m][unnormed_stride]
+  float* ybuf;            // workspace: [m][n_normed] binary32 values of y
+  uint32_t* counter;      // workspace: arrival counter, zero between calls
+  int64_t x_stride, w_stride, normed_stride, unnormed_stride;
+  uint32_t m, n, kc;      // kc: 16-byte chunks per row of x and W
+  uint32_t n_normed;
+  uint32_t n_waves;        // ceil(n / cols_per_wave)
+  uint32_t n_norm_blocks;  // blocks holding a normed column: the arrivals
+  float eps;
+};
+
+// Columns one wave computes for m input rows (the x rows are re-read from
+// the L1 for every column group, so more rows take more columns per wave).
+inline uint32_t gemv_cols_per_wave(uint32_t m) { return m <= 2 ? 1u : 2u; }
+
+// Waves per block: a block arrives once, so larger blocks mean fewer
+// releases and fewer increments of the one counter (each is serialised).
+// The one-row build fits 16 waves (1024 threads) in 128 VGPRs, the two-row
+// build 8; the others need more registers.  Every build has at least the
+// four waves the norm uses.
+inline uint32_t gemv_waves_per_block(uint32_t m) { return m <= 1 ? 16u : m <= 2 ? 8u : 4u; }
+
+// Enqueue the kernel; returns a hipError_t value (0: launched).
+int launch_gemv_norm(const GemvArgs& a, int32_t dtype, void* stream);
+
+}  // namespace qrp

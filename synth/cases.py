@@ -703,6 +703,10 @@ class GemvCase:
     unnormed_row_stride: int
     op: str = "gemv_norm"
 
+    @property
+    def T(self) -> int:     # input rows: the tokens of a step
+        return self.m
+
 
 def make_gemv_case(name: str, seed: int, dtype: str, m: int, k: int, n: int, n_normed: int,
                    epsilon: float = 1e-6, weight_offset: float = 0.0, x_pad: int = 0,
@@ -711,7 +715,7 @@ def make_gemv_case(name: str, seed: int, dtype: str, m: int, k: int, n: int, n_n
     x = np.full((m, k + x_pad), SENTINEL[dtype], dtype=BITS_DTYPE[dtype])
     x[:, :k] = to_bits(prng.normal(seed, S_X, m * k), dtype).reshape(m, k)
     w = np.full((n, k + w_pad), SENTINEL[dtype], dtype=BITS_DTYPE[dtype])
-    w[:, :k] = to_bits(prng.normal(seed, S_W, n * k, std=1.0 / np.sqrt(k)), dtype).reshape(n, k)
+    w[:, :k] = to_bits(prng.normal(seed, S_W, n * k, std=1.0 / np.sqrt(max(k, 1))), dtype).reshape(n, k)
     gamma = to_bits(prng.normal(seed, S_GAMMA, max(n_normed, 1), mean=1.0, std=0.1), dtype)
     return GemvCase(name=name, seed=seed, dtype=dtype, m=m, k=k, n=n, n_normed=n_normed, x=x,
                     w=w, gamma=gamma, epsilon=epsilon, weight_offset=weight_offset,

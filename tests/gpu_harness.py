@@ -194,3 +194,46 @@ def run(dc: DeviceCase, stream=None, raise_on_error=True, op=None, prepare=False
             dc.buf, dt, c.batch, c.seq_len, c.n_q_heads, dc.valid, rope_of(dc),
             dc.caches[0].desc, c.layer_idx, dc.q_out_rows(0), **kw)
     raise ValueError(op)
+
+
+# ---------------------------------------------------------------------------
+# fused GEMV + partial RMSNorm
+# ---------------------------------------------------------------------------
+
+@dataclass
+class DeviceGemv:
+    case: sc.GemvCase
+    x: torch.Tensor
+    w: torch.Tensor
+    gamma: torch.Tensor
+    normed: torch.Tensor
+    unnormed: torch.Tensor
+    workspace: torch.Tensor            # uint8, zero-filled once
+
+
+def upload_gemv(case, device="cuda", workspace: torch.Tensor = None) -> DeviceGemv:
+    """Operands as raw bits; outputs start as sentinels; a zero-filled
+    workspace of the size the library asks for (or the one given)."""
+    bits = TORCH_BITS[case.dtype]
+    s = sentinel_int(case.dtype)
+    normed = torch.full((case.m, case.normed_row_stride), s, dtype=bits, device=device)
+    unnormed = torch.full((case.m, case.unnormed_row_stride), s, dtype=bits, device=device)
+    if workspace is None:
+        nbytes = max(qrp.gemv_norm_workspace_bytes(case.m, case.n_normed), 256)
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    return DeviceGemv(case=case, x=bits_tensor(case.x, device), w=bits_tensor(case.w, device),
+                      gamma=bits_tensor(case.gamma, device), normed=normed, unnormed=unnormed,
+                      workspace=workspace)
+
+
+def run_gemv(dg: DeviceGemv, stream=None, raise_on_error=True, prepare=False,
+             no_workspace=False):
+    c = dg.case
+    ws = None if no_workspace else dg.workspace
+    return qrp.matmul_fused_partial_rmsnorm(
+        dg.normed if c.n_normed else None, c.normed_row_stride,
+        dg.unnormed if c.n_normed < c.n else None, c.unnormed_row_stride,
+        dg.x, c.x.shape[1], c.m, dg.w, c.w.shape[1], c.n, c.k, dg.gamma, c.n_normed,
+        c.epsilon, c.weight_offset, QRP_DT[c.dtype], ws,
+        0 if ws is None else ws.numel(), stream=stream, raise_on_error=raise_on_error,
+        prepare=prepare)

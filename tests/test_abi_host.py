@@ -26,7 +26,7 @@ FAKE = 0x10000          # 16-byte aligned stand-in for a device address (never d
 
 def declared_functions():
     text = open(HEADER).read()
-    return re.findall(r"^\s*(?:int32_t|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:int32_t|uint64_t|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)
 
 
 def test_every_declared_function_is_exported():
@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(qrp.EXPORTS)
-    assert qrp.abi_version() == 3
+    assert qrp.abi_version() == 4
 
 
 def test_one_hip_runtime_in_process():
@@ -304,3 +304,53 @@ def test_dual_band_mixed_fp8_and_plain_caches_is_unsupported():
                            plane_stride=128 * 128, layer_stride=128 * 128, slot_stride=128)
     assert _dual(index=_band(cache=idx_cache, q_col=80 * 128, n_q_heads=16,
                              q_out_row_stride=16 * 128)) == qrp.QRP_EUNSUPPORTED
+
+
+def _gemv(**kw):
+    a = dict(normed_output=FAKE, normed_row_stride=1536, unnormed_output=FAKE,
+             unnormed_row_stride=576, input=FAKE, input_row_stride=7168, m=1, weight=FAKE,
+             weight_row_stride=7168, n=2112, k=7168, gamma=FAKE, n_normed=1536, epsilon=1e-6,
+             weight_offset=0.0, dtype=qrp.QRP_BF16, workspace=FAKE,
+             workspace_bytes=qrp.gemv_norm_workspace_bytes(1, 1536), stream=0,
+             raise_on_error=False)
+    a.update(kw)
+    return qrp.matmul_fused_partial_rmsnorm(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=qrp.QRP_FP8), qrp.QRP_EUNSUPPORTED),
+    (dict(transpose_b=0), qrp.QRP_EUNSUPPORTED),
+    (dict(m=9), qrp.QRP_EUNSUPPORTED),
+    (dict(n_normed=2113), qrp.QRP_EINVAL),
+    (dict(input=None), qrp.QRP_EINVAL),
+    (dict(weight=None), qrp.QRP_EINVAL),
+    (dict(gamma=None), qrp.QRP_EINVAL),
+    (dict(normed_output=None), qrp.QRP_EINVAL),
+    (dict(workspace=None), qrp.QRP_EINVAL),
+    (dict(unnormed_output=None), qrp.QRP_EINVAL),
+    (dict(workspace_bytes=qrp.gemv_norm_workspace_bytes(1, 1536) - 4), qrp.QRP_EINVAL),
+    (dict(m=2), qrp.QRP_EINVAL),                              # workspace sized for one row
+    (dict(input=FAKE + 8), qrp.QRP_EALIGN),
+    (dict(weight=FAKE + 8), qrp.QRP_EALIGN),
+    (dict(workspace=FAKE + 8), qrp.QRP_EALIGN),
+    (dict(normed_output=FAKE + 1), qrp.QRP_EALIGN),
+    (dict(gamma=FAKE + 1), qrp.QRP_EALIGN),
+    (dict(k=7164, input_row_stride=7164, weight_row_stride=7164), qrp.QRP_EALIGN),
+    (dict(weight_row_stride=7172), qrp.QRP_EALIGN),
+    (dict(input_row_stride=7160), qrp.QRP_EINVAL),
+    (dict(weight_row_stride=7160), qrp.QRP_EINVAL),
+    (dict(normed_row_stride=1535), qrp.QRP_EINVAL),
+    (dict(unnormed_row_stride=575), qrp.QRP_EINVAL),
+])
+def test_gemv_norm_argument_errors(kw, code):
+    assert _gemv(**kw) == code
+    assert qrp.last_error() != ""
+
+
+def test_gemv_norm_degenerate_sizes_and_workspace_size():
+    # nothing to compute: no launch, no pointer read
+    assert _gemv(m=0, input=None, weight=None, workspace=None) == qrp.QRP_OK
+    assert _gemv(n=0, n_normed=0, input=None, weight=None) == qrp.QRP_OK
+    # the workspace is the counter line plus m * n_normed binary32 values; none without a norm
+    assert qrp.gemv_norm_workspace_bytes(3, 100) == 256 + 4 * 3 * 100
+    assert qrp.gemv_norm_workspace_bytes(8, 0) == 0

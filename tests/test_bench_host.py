@@ -44,3 +44,13 @@ def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
 def test_cpu_model_reads_proc_cpuinfo():
     # a string on any host (empty where /proc/cpuinfo has no model line)
     assert isinstance(bench._cpu_model(), str)
+
+
+def test_gemv_bytes_by_hand_and_its_own_source_hash():
+    # one bf16 row of 7168 into 2112 columns, 1536 of them normed
+    case = bench.make_case("gemv_norm")
+    w, x, gamma, out = 2112 * 7168 * 2, 7168 * 2, 1536 * 2, 2112 * 2
+    assert bench.algorithmic_bytes(case) == w + x + gamma + out
+    assert bench.case_tokens(case) == 1
+    assert bench.kernel_name("gemv_norm") == bench.GEMV_KERNEL_NAME
+    assert bench.source_hash_for("gemv_norm") != bench.source_hash_for("prefill")

@@ -1,0 +1,130 @@
+"""GPU parity of the fused GEMV + partial RMSNorm (MatmulFusedPartialRMSNorm
+page) through the C ABI, against the CPU oracle, with the bar that
+tests/gemv_parity.py derives from the kernel's binary32 arithmetic.
+
+Cases: the bench shape (hidden 7168 -> 1536 normed + 576 passed through) at
+full and reduced size; every dtype with 1, 2, 3, 5 and 8 input rows, padded
+strides, a k that leaves a ragged last chunk round, and a norm boundary that
+splits a wave's columns; nothing normed (no workspace at all), everything
+normed (no passed-through output), k = 0, one column, many columns; rows
+of one call equal to the same rows called alone (the summation order does
+not depend on the row count); a reused workspace on two calls in a row,
+the second smaller, whose counter is back at zero after each; repeated
+calls give the same bits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from synth import cases as sc  # noqa: E402
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gemv_parity
+    from tests import gpu_harness as gh
+    return gh, gemv_parity
+
+
+def run_and_compare(case, workspace=None, no_workspace=False):
+    gh, gp = _gpu()
+    print(f"[gemv] {case.name} dtype={case.dtype} m={case.m} k={case.k} n={case.n} "
+          f"n_normed={case.n_normed}", flush=True)
+    res = oracle.run_gemv(case)
+    assert res.status == 0
+    dg = gh.upload_gemv(case, workspace=workspace)
+    gh.run_gemv(dg, no_workspace=no_workspace)
+    torch.cuda.synchronize()
+    rep = gp.check(case, res, gh.to_numpy_bits(dg.normed, case.dtype),
+                   gh.to_numpy_bits(dg.unnormed, case.dtype))
+    if case.n_normed:
+        counter = int(dg.workspace[:4].view(torch.int32).item())
+        assert counter == 0, f"arrival counter left at {counter}"
+    print(f"[gemv] {case.name} ok {rep}", flush=True)
+    return dg, rep
+
+
+@pytest.mark.parametrize("small", [True, False])
+def test_bench_shape(small):
+    run_and_compare(sc.gemv_norm(small=small))
+
+
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+def test_rows_dtypes_and_ragged_sizes(dtype, m):
+    E = 4 if dtype == sc.F32 else 8
+    k = E * (64 * 3 + 5)                 # three full chunk rounds and a ragged one
+    case = sc.make_gemv_case(f"rows_{dtype}_{m}", 20 + m, dtype, m=m, k=k, n=333, n_normed=201,
+                             epsilon=1e-5, x_pad=E, w_pad=2 * E, out_pad=3)
+    run_and_compare(case)
+
+
+def test_nothing_normed_needs_no_workspace():
+    run_and_compare(sc.make_gemv_case("no_norm", 31, sc.BF16, m=2, k=512, n=300, n_normed=0),
+                    no_workspace=True)
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_everything_normed(m):
+    run_and_compare(sc.make_gemv_case("all_norm", 32, sc.BF16, m=m, k=1024, n=777, n_normed=777))
+
+
+def test_k_zero_gives_zeros():
+    # padded strides keep the operand buffers non-empty (a real device address)
+    case = sc.make_gemv_case("k0", 33, sc.F32, m=2, k=0, n=10, n_normed=4, epsilon=1e-3,
+                             x_pad=4, w_pad=4)
+    dg, _ = run_and_compare(case)
+    gh, _ = _gpu()
+    assert np.all(gh.to_numpy_bits(dg.normed, sc.F32)[:, :4] == 0)
+    assert np.all(gh.to_numpy_bits(dg.unnormed, sc.F32)[:, :6] == 0)
+
+
+def test_one_column_and_many_columns():
+    run_and_compare(sc.make_gemv_case("n1", 34, sc.BF16, m=1, k=256, n=1, n_normed=1))
+    run_and_compare(sc.make_gemv_case("n1u", 35, sc.BF16, m=3, k=256, n=1, n_normed=0),
+                    no_workspace=True)
+    run_and_compare(sc.make_gemv_case("wide", 36, sc.BF16, m=1, k=128, n=40000,
+                                      n_normed=30001))
+
+
+def test_rows_match_single_row_calls():
+    gh, _ = _gpu()
+    case = sc.make_gemv_case("rows8", 37, sc.BF16, m=8, k=2048, n=500, n_normed=300)
+    dg = gh.upload_gemv(case)
+    gh.run_gemv(dg)
+    for i in (0, 3, 7):
+        one = sc.make_gemv_case("rows8", 37, sc.BF16, m=8, k=2048, n=500, n_normed=300)
+        one.m, one.x = 1, case.x[i:i + 1]
+        d1 = gh.upload_gemv(one)
+        gh.run_gemv(d1)
+        torch.cuda.synchronize()
+        assert torch.equal(d1.normed[0], dg.normed[i]), i
+        assert torch.equal(d1.unnormed[0], dg.unnormed[i]), i
+
+
+def test_workspace_reused_on_two_calls_the_second_smaller():
+    gh, _ = _gpu()
+    big = sc.make_gemv_case("ws_big", 38, sc.BF16, m=4, k=1024, n=900, n_normed=700)
+    small = sc.make_gemv_case("ws_small", 39, sc.BF16, m=2, k=512, n=200, n_normed=130)
+    dg, _ = run_and_compare(big)
+    run_and_compare(small, workspace=dg.workspace)
+
+
+def test_repeated_calls_give_the_same_bits():
+    gh, _ = _gpu()
+    case = sc.gemv_norm(small=True)
+    dg = gh.upload_gemv(case)
+    gh.run_gemv(dg)
+    torch.cuda.synchronize()
+    first = (dg.normed.clone(), dg.unnormed.clone())
+    for _ in range(5):
+        gh.run_gemv(dg)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], dg.normed) and torch.equal(first[1], dg.unnormed)
