@@ -54,7 +54,7 @@ KERNEL_SOURCES = ("qk_rope_paged_amd/csrc/band_kernel.hpp", "qk_rope_paged_amd/c
 # kernel, sources and workloads
 GEMV_KERNEL_NAME = "gemv_norm_kernel"
 GEMV_SOURCES = ("qk_rope_paged_amd/csrc/gemv_norm.hip", "qk_rope_paged_amd/csrc/gemv_norm.hpp",
-                "qk_rope_paged_amd/csrc/abi.cpp")
+                "qk_rope_paged_amd/csrc/abi_gemv.cpp")
 GEMV_WORKLOADS = ("gemv_norm",)
 
 

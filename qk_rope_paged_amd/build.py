@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libqk_rope_paged.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["kernels.hip", "kernels_fp8.hip", "kernels_qout.hip", "kernels_pack.hip", "gemv_norm.hip",
-           "abi.cpp"]
+           "abi.cpp", "abi_gemv.cpp"]
 # measurement helper for the benchmark (not part of the C ABI)
 COPY_LIB_PATH = os.path.join(HERE, "libqrp_bench_copy.so")
 COPY_SOURCES = ["bench_copy.hip"]

@@ -17,7 +17,7 @@
 #include <vector>
 
 #include "engine.hpp"
-#include "gemv_norm.hpp"
+#include "errors.hpp"
 #include "qk_rope_paged.h"
 
 namespace {
@@ -28,6 +28,15 @@ int32_t fail(int32_t code, const std::string& msg) {
   g_err = msg;
   return code;
 }
+
+}  // namespace
+
+namespace qrp {
+int32_t set_error(int32_t code, const std::string& msg) { return fail(code, msg); }
+void clear_error() { g_err.clear(); }
+}  // namespace qrp
+
+namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 uint32_t elem_bytes(int32_t dt) { return dt == QRP_F32 ? 4u : dt == QRP_FP8 ? 1u : 2u; }
@@ -556,81 +565,6 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
   b.add_seg(qrp::SEG_K_INPLACE, nullptr, 0, nullptr, 0, nullptr, 0.f, cache->num_kv_heads, 0, 0);
   if ((st = b.finish((uint32_t)tokens, false, true, true))) return st;
   return launch(b, rope->interleaved != 0, false, stream, true);
-}
-
-uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed) {
-  if (n_normed == 0) return 0;
-  return qrp::kGemvCounterBytes + 4ull * m * n_normed;
-}
-
-int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_stride,
-                                     void* unnormed_output, uint64_t unnormed_row_stride,
-                                     const void* input, uint64_t input_row_stride, uint32_t m,
-                                     const void* weight, uint64_t weight_row_stride, uint32_t n,
-                                     uint32_t k, const void* gamma, uint32_t n_normed,
-                                     float epsilon, float weight_offset, int32_t dtype,
-                                     int32_t transpose_b, void* workspace,
-                                     uint64_t workspace_bytes, void* stream) {
-  g_err.clear();
-  (void)weight_offset;  // not consumed by this op (its page's Args)
-  if (!dtype_ok(dtype)) return fail(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
-  if (transpose_b != 1)
-    return fail(QRP_EUNSUPPORTED, "only transpose_b = 1 (W stored [n][k]) is built");
-  if (n_normed > n) return fail(QRP_EINVAL, "n_normed > n");
-  if (m > qrp::kGemvMaxRows) return fail(QRP_EUNSUPPORTED, "m > 8 rows per call");
-  if (m == 0 || n == 0) return QRP_OK;
-  if (!input || !weight) return fail(QRP_EINVAL, "input / weight is NULL");
-  if (n_normed && (!gamma || !normed_output || !workspace))
-    return fail(QRP_EINVAL, "gamma, normed_output and workspace are needed when n_normed > 0");
-  if (n_normed < n && !unnormed_output)
-    return fail(QRP_EINVAL, "unnormed_output is NULL with columns past n_normed");
-  const uint32_t ce = chunk_elems(dtype);
-  const uintptr_t eb = elem_bytes(dtype) - 1;
-  if (!aligned16(input) || !aligned16(weight) || (workspace && !aligned16(workspace)))
-    return fail(QRP_EALIGN, "input, weight and workspace must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(normed_output) | reinterpret_cast<uintptr_t>(unnormed_output) |
-       reinterpret_cast<uintptr_t>(gamma)) & eb)
-    return fail(QRP_EALIGN, "outputs and gamma must be aligned to their element size");
-  if (k % ce || input_row_stride % ce || weight_row_stride % ce)
-    return fail(QRP_EALIGN, "k and the input / weight row strides must be multiples of 16 bytes");
-  if (input_row_stride < k || weight_row_stride < k)
-    return fail(QRP_EINVAL, "input / weight row stride < k");
-  if (n_normed && normed_row_stride < n_normed)
-    return fail(QRP_EINVAL, "normed_row_stride < n_normed");
-  if (n_normed < n && unnormed_row_stride < n - n_normed)
-    return fail(QRP_EINVAL, "unnormed_row_stride < n - n_normed");
-  if (workspace_bytes < qrp_gemv_norm_workspace_bytes(m, n_normed))
-    return fail(QRP_EINVAL, "workspace smaller than qrp_gemv_norm_workspace_bytes(m, n_normed)");
-
-  qrp::GemvArgs a{};
-  a.x = input;
-  a.w = weight;
-  a.gamma = gamma;
-  a.normed = normed_output;
-  a.unnormed = unnormed_output;
-  a.counter = static_cast<uint32_t*>(workspace);
-  a.ybuf = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                qrp::kGemvCounterBytes)
-                     : nullptr;
-  a.x_stride = (int64_t)input_row_stride;
-  a.w_stride = (int64_t)weight_row_stride;
-  a.normed_stride = (int64_t)normed_row_stride;
-  a.unnormed_stride = (int64_t)unnormed_row_stride;
-  a.m = m;
-  a.n = n;
-  a.kc = k / ce;
-  a.n_normed = n_normed;
-  const uint32_t cpw = qrp::gemv_cols_per_wave(m);
-  a.n_waves = (uint32_t)(((uint64_t)n + cpw - 1) / cpw);
-  const uint64_t norm_waves = ((uint64_t)n_normed + cpw - 1) / cpw;
-  const uint32_t wpb = qrp::gemv_waves_per_block(m);
-  a.n_norm_blocks = (uint32_t)((norm_waves + wpb - 1) / wpb);
-  a.eps = epsilon;
-  const int e = qrp::launch_gemv_norm(a, dtype, stream);
-  if (e != 0)
-    return fail(QRP_EHIP, std::string("kernel launch failed: ") +
-                              hipGetErrorString(static_cast<hipError_t>(e)));
-  return QRP_OK;
 }
 
 int32_t qrp_validate_host(const uint32_t* off, uint32_t B, uint32_t T, uint32_t batch_offset,
