@@ -42,6 +42,7 @@ int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_st
   if (n_normed > n) return qrp::set_error(QRP_EINVAL, "n_normed > n");
   if (m > qrp::kGemvMaxRows) return qrp::set_error(QRP_EUNSUPPORTED, "m > 8 rows per call");
   if (m == 0 || n == 0) return QRP_OK;
+  if (n >= (1u << 31)) return qrp::set_error(QRP_EINVAL, "n >= 2^31 columns in one launch");
   if (!input || !weight) return qrp::set_error(QRP_EINVAL, "input / weight is NULL");
   if (n_normed && (!gamma || !normed_output || !workspace))
     return qrp::set_error(QRP_EINVAL, "gamma, normed_output and workspace are needed when n_normed > 0");

@@ -341,6 +341,7 @@ def _gemv(**kw):
     (dict(weight_row_stride=7160), qrp.QRP_EINVAL),
     (dict(normed_row_stride=1535), qrp.QRP_EINVAL),
     (dict(unnormed_row_stride=575), qrp.QRP_EINVAL),
+    (dict(n=1 << 31, unnormed_row_stride=(1 << 31) - 1536), qrp.QRP_EINVAL),
 ])
 def test_gemv_norm_argument_errors(kw, code):
     assert _gemv(**kw) == code
