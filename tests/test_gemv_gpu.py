@@ -128,3 +128,48 @@ def test_repeated_calls_give_the_same_bits():
         gh.run_gemv(dg)
     torch.cuda.synchronize()
     assert torch.equal(first[0], dg.normed) and torch.equal(first[1], dg.unnormed)
+
+
+def _random_case(i: int):
+    rng = np.random.default_rng([4099, i])
+    dtype = (sc.F32, sc.BF16, sc.F16)[int(rng.integers(3))]
+    E = 4 if dtype == sc.F32 else 8
+    m = int(rng.integers(1, 9))
+    k = E * int(rng.integers(0, 400))
+    n = int(rng.integers(1, 3000))
+    nn = int(rng.choice([0, n, int(rng.integers(0, n + 1))]))
+    return sc.make_gemv_case(f"rand_gemv_{i}", 600 + i, dtype, m=m, k=k, n=n, n_normed=nn,
+                             epsilon=float(rng.choice([1e-6, 1e-3])),
+                             weight_offset=float(rng.choice([0.0, 0.5])),
+                             x_pad=E * int(rng.integers(0, 3)) + (E if k == 0 else 0),
+                             w_pad=E * int(rng.integers(0, 3)) + (E if k == 0 else 0),
+                             out_pad=int(rng.integers(0, 3)))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes(i):
+    case = _random_case(i)
+    run_and_compare(case, no_workspace=case.n_normed == 0)
+
+
+def test_graph_replays_match_eager():
+    # a captured launch reuses its workspace on every replay: the counter
+    # must be back at zero each time
+    gh, _ = _gpu()
+    case = sc.gemv_norm(small=True)
+    eager = gh.upload_gemv(case)
+    gh.run_gemv(eager)
+    torch.cuda.synchronize()
+    dg = gh.upload_gemv(case)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gh.run_gemv(dg, stream=s)
+    for _ in range(3):
+        dg.normed.fill_(0)
+        dg.unnormed.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dg.normed, eager.normed) and torch.equal(dg.unnormed, eager.unnormed)
+        assert int(dg.workspace[:4].view(torch.int32).item()) == 0
