@@ -14,6 +14,8 @@ calls give the same bits.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -146,7 +148,8 @@ def _random_case(i: int):
                              out_pad=int(rng.integers(0, 3)))
 
 
-@pytest.mark.parametrize("i", range(24))
+# QRP_RANDOM_CASES sets the count (1000: a soak of the arrival counter and the bar)
+@pytest.mark.parametrize("i", range(int(os.environ.get("QRP_RANDOM_CASES", "24"))))
 def test_random_shapes(i):
     case = _random_case(i)
     run_and_compare(case, no_workspace=case.n_normed == 0)
