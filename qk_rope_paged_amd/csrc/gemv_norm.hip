@@ -109,6 +109,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// y values were stored by other compute units (other L2s): agent-scope loads
 __device__ __forceinline__ float load_y(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
