@@ -388,7 +388,6 @@ def cpu_baseline(cases, seconds: float, max_passes: int) -> dict:
     """The CPU oracle as it stands, single-threaded, on the same batches
     (cycled), repeated until about `seconds` of oracle time."""
     import oracle
-    from tests import gpu_harness as gh
 
     total, passes, nbytes, ntok = 0.0, 0, 0, 0
     while passes < max_passes and (passes == 0 or total < seconds):
@@ -421,10 +420,10 @@ def _cpu_model() -> str:
 
 
 def check_parity(case, dc, shared_pool: bool) -> str:
-    """Compare the first device set against the oracle (store ops repeat to
-    the same result; in-place ops accumulate, so they are not checked here).
-    With a shared pool the other sets' pages are not expected to hold the
-    sentinel."""
+    """Part of the CPU-baseline leg: the oracle that leg times also checks the
+    first device set (store ops and the GEMV repeat to the same result;
+    in-place ops accumulate, so they are not checked here).  With a shared
+    pool the other sets' pages are not expected to hold the sentinel."""
     if case.op == "gemv_norm":
         import oracle
         from tests import gemv_parity
@@ -520,8 +519,16 @@ def main() -> int:
         f"({gpu_time / K * 1e6:.2f} us per launch); single launches p10 {kern[K // 10] * 1e6:.2f} "
         f"us, p90 {kern[(9 * K) // 10] * 1e6:.2f} us")
 
-    parity_status = "skipped" if args.no_parity else check_parity(first, sets[0], shared_pool)
-    log(f"[bench] parity: {parity_status}")
+    # the oracle runs only in the CPU-baseline leg: its first batch also
+    # checks the GPU's outputs (before the copy ceiling frees the buffers)
+    parity_status = "not checked (no CPU-baseline leg)"
+    cpu = None
+    if not args.no_cpu_baseline:
+        if not args.no_parity:
+            parity_status = check_parity(first, sets[0], shared_pool)
+            log(f"[bench] parity: {parity_status}")
+        log("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(cases, args.cpu_seconds, args.cpu_max_passes)
 
     mean_bytes = sum(step_bytes) / K
     value = sum(step_bytes) / wall / 1e9
@@ -559,9 +566,8 @@ def main() -> int:
         cc = copy_ceiling(int(mean_bytes), n_sets, max(20, K // 2))
         out["copy_ceiling"] = cc
         out["roofline"]["frac_of_copy_ceiling"] = round(achieved / cc["value"], 4)
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle ...")
-        out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds, args.cpu_max_passes)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
 
