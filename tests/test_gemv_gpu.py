@@ -10,7 +10,8 @@ normed (no passed-through output), k = 0, one column, many columns; rows
 of one call equal to the same rows called alone (the summation order does
 not depend on the row count); a reused workspace on two calls in a row,
 the second smaller, whose counter is back at zero after each; repeated
-calls give the same bits.
+calls give the same bits; seeded random shapes; HIP-graph replays; two
+calls overlapping on two streams with their own workspaces.
 """
 from __future__ import annotations
 
@@ -176,3 +177,27 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(dg.normed, eager.normed) and torch.equal(dg.unnormed, eager.unnormed)
         assert int(dg.workspace[:4].view(torch.int32).item()) == 0
+
+
+def test_overlapping_calls_on_two_streams_with_their_own_workspaces():
+    # no state is shared between calls but the workspace: two calls in
+    # flight together, each with its own, give the results of one at a time
+    gh, _ = _gpu()
+    cases = [sc.gemv_norm(small=True), sc.make_gemv_case("other", 40, sc.BF16, m=3, k=1536,
+                                                         n=1000, n_normed=640)]
+    ref = []
+    for c in cases:
+        d = gh.upload_gemv(c)
+        gh.run_gemv(d)
+        torch.cuda.synchronize()
+        ref.append(d)
+    devs = [gh.upload_gemv(c) for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(20):
+        for d, s in zip(devs, streams):
+            gh.run_gemv(d, stream=s)
+    torch.cuda.synchronize()
+    for d, r in zip(devs, ref):
+        assert torch.equal(d.normed, r.normed) and torch.equal(d.unnormed, r.unnormed)
+        assert int(d.workspace[:4].view(torch.int32).item()) == 0
