@@ -23,7 +23,7 @@
 // an arrival counter (an atomic increment that wraps to zero, so the counter
 // is zero again after every call).  Releases and increments of one counter
 // are serialised by the memory system (about 10 ns each, measured), so they
-// are taken per block of up to 16 waves, not per wave.  The block that draws
+// are taken per block of waves, not per wave.  The block that draws
 // the last ticket acquires, and its first four waves read the whole of y
 // back and normalise every row:
 //   ss = sum y_j^2 (per-thread fused multiply-adds in j order over every
@@ -292,7 +292,7 @@ int run(const GemvArgs& a, hipStream_t s) {
 // and gemv_waves_per_block()
 template <int DT>
 int run_rows(const GemvArgs& a, hipStream_t s) {
-  if (a.m <= 1) return run<DT, 1, 1, 8, 16>(a, s);
+  if (a.m <= 1) return run<DT, 1, 2, 8, 8>(a, s);
   if (a.m <= 2) return run<DT, 2, 1, 8, 8>(a, s);
   if (a.m <= 4) return run<DT, 4, 2, 4, 4>(a, s);
   return run<DT, 8, 2, 4, 4>(a, s);

@@ -31,16 +31,15 @@ struct GemvArgs {
   float eps;
 };
 
-// Columns one wave computes for m input rows (the x rows are re-read from
-// the L1 for every column group, so more rows take more columns per wave).
-inline uint32_t gemv_cols_per_wave(uint32_t m) { return m <= 2 ? 1u : 2u; }
-
-// Waves per block: a block arrives once, so larger blocks mean fewer
-// releases and fewer increments of the one counter (each is serialised).
-// The one-row build fits 16 waves (1024 threads) in 128 VGPRs, the two-row
-// build 8; the others need more registers.  Every build has at least the
-// four waves the norm uses.
-inline uint32_t gemv_waves_per_block(uint32_t m) { return m <= 1 ? 16u : m <= 2 ? 8u : 4u; }
+// Columns one wave computes for m input rows, and waves per block.  A block
+// arrives once, so larger blocks mean fewer releases and fewer increments
+// of the one counter (each is serialised), but fewer blocks leave compute
+// units idle.  Measured at one row of 7168 into 2112 columns (1536 normed):
+// 2 columns x 8 waves 12.8 us; 1 x 16: 14.4; 2 x 16: 18.7; 2 x 4: 14.3;
+// 4 x 4: 14.6; 3 x 8: 15.0.  Every build has at least the four waves the
+// norm uses.
+inline uint32_t gemv_cols_per_wave(uint32_t m) { return m == 2 ? 1u : 2u; }
+inline uint32_t gemv_waves_per_block(uint32_t m) { return m <= 2 ? 8u : 4u; }
 
 // Enqueue the kernel; returns a hipError_t value (0: launched).
 int launch_gemv_norm(const GemvArgs& a, int32_t dtype, void* stream);
