@@ -307,10 +307,12 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
  * NULL is then allowed).  It must be zero-filled before its first use; every
  * call leaves its counter at zero again, so it is reused without clearing.
  * Calls that overlap in time must not share a workspace.
+ * The summation order is fixed, so results are the same bits on every call
+ * and for every row count (a row gives the same outputs alone or among 8).
  * Errors: QRP_EINVAL for a NULL buffer that the call needs, n_normed > n,
- * n >= 2^31, a stride below its row or a short workspace; QRP_EUNSUPPORTED for m > 8,
- * transpose_b = 0 or another dtype.  m == 0 or n == 0 returns QRP_OK
- * without a launch; k == 0 gives y = 0.
+ * n >= 2^31, a stride below its row or a short workspace; QRP_EUNSUPPORTED
+ * for m > 8, transpose_b = 0 or another dtype.  m == 0 or n == 0 returns
+ * QRP_OK without a launch; k == 0 gives y = 0.
  */
 uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed);
 
