@@ -8,8 +8,8 @@
 // Work mapping.  One wave64 owns `CPW` consecutive output columns and sweeps
 // the whole of k: lane l takes the 16-byte chunks l, l + 64, l + 128, ... of
 // each W row (a wave reads 1 KB of a row per load instruction, fully
-// coalesced) and the same chunks of every x row (re-read from the L1; x is a
-// few KB).  U chunks per lane are loaded before any is used, so a wave keeps
+// coalesced) and the same chunks of every x row (from the L1 for one row;
+// several rows are copied to LDS once per block when they fit 64 KB).  U chunks per lane are loaded before any is used, so a wave keeps
 // U * CPW KB of W in flight.  Each lane sums its own terms in k order with
 // one fused multiply-add per term, then an xor butterfly over the 64 lanes
 // adds the partial sums; every lane ends with the same bits (each step adds
@@ -169,7 +169,7 @@ __device__ void norm_rows(const GemvArgs& a) {
   }
 }
 
-template <int DT, int MB, int CPW, int U, int WPB>
+template <int DT, int MB, int CPW, int U, int WPB, bool XL>
 __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
   const uint32_t lane = threadIdx.x & 63u;
   // the grid's last block may hold waves past the end: they skip the work
@@ -205,6 +205,17 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
 #pragma unroll
     for (int j = 0; j < CPW; ++j) acc[m][j] = 0.f;
 
+  // several x rows (XL): the block copies them to LDS once, row m at
+  // x_lds + m * kc; every wave would otherwise re-read them all from global
+  // memory, which overflows the L1
+  extern __shared__ gv4u x_lds[];
+  if constexpr (XL) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      for (uint32_t c = threadIdx.x; c < a.kc; c += 64u * WPB) x_lds[m * a.kc + c] = xrow[m][c];
+    __syncthreads();
+  }
+
   const gv4u zero = {0u, 0u, 0u, 0u};
   const uint32_t kc = live ? a.kc : 0u;
   for (uint32_t base = 0; base < kc; base += 64u * U) {
@@ -226,7 +237,12 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
       for (int j = 0; j < CPW; ++j) widen<DT>(wv[u][j], wf[j]);
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        const gv4u xv = in ? xrow[m][c] : zero;
+        gv4u xv = zero;
+        if constexpr (XL) {
+          if (in) xv = x_lds[m * a.kc + c];
+        } else {
+          if (in) xv = xrow[m][c];
+        }
         float xf[E];
         widen<DT>(xv, xf);
 #pragma unroll
@@ -279,11 +295,19 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
   norm_rows<DT>(a);
 }
 
+// Largest LDS copy of the x rows (more rows go through global memory).
+constexpr uint64_t kGemvMaxLdsBytes = 64 * 1024;
+
 template <int DT, int MB, int CPW, int U, int WPB>
 int run(const GemvArgs& a, hipStream_t s) {
   const uint32_t blocks = (a.n_waves + WPB - 1) / WPB;
-  hipLaunchKernelGGL((gemv_norm_kernel<DT, MB, CPW, U, WPB>), dim3(blocks), dim3(64 * WPB), 0, s,
-                     a);
+  const uint64_t lds = (uint64_t)MB * a.kc * 16;
+  if (MB > 1 && lds <= kGemvMaxLdsBytes)
+    hipLaunchKernelGGL((gemv_norm_kernel<DT, MB, CPW, U, WPB, (MB > 1)>), dim3(blocks),
+                       dim3(64 * WPB), (uint32_t)lds, s, a);
+  else
+    hipLaunchKernelGGL((gemv_norm_kernel<DT, MB, CPW, U, WPB, false>), dim3(blocks),
+                       dim3(64 * WPB), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -7,8 +7,9 @@ full and reduced size; every dtype with 1, 2, 3, 5 and 8 input rows, padded
 strides, a k that leaves a ragged last chunk round, and a norm boundary that
 splits a wave's columns; nothing normed (no workspace at all), everything
 normed (no passed-through output), k = 0, one column, many columns; rows
-of one call equal to the same rows called alone (the summation order does
-not depend on the row count); a reused workspace on two calls in a row,
+of one call equal to the same rows called alone, with the x rows staged in
+LDS and read from global memory (the summation order does not depend on the
+row count or on where x comes from); a reused workspace on two calls in a row,
 the second smaller, whose counter is back at zero after each; repeated
 calls give the same bits; seeded random shapes; HIP-graph replays; two
 calls overlapping on two streams with their own workspaces.
@@ -97,19 +98,28 @@ def test_one_column_and_many_columns():
                                       n_normed=30001))
 
 
-def test_rows_match_single_row_calls():
+@pytest.mark.parametrize("k", [2048, 7168])     # x rows through LDS (32 KB) / global memory
+def test_rows_match_single_row_calls(k):
     gh, _ = _gpu()
-    case = sc.make_gemv_case("rows8", 37, sc.BF16, m=8, k=2048, n=500, n_normed=300)
+    case = sc.make_gemv_case("rows8", 37, sc.BF16, m=8, k=k, n=500, n_normed=300)
     dg = gh.upload_gemv(case)
     gh.run_gemv(dg)
     for i in (0, 3, 7):
-        one = sc.make_gemv_case("rows8", 37, sc.BF16, m=8, k=2048, n=500, n_normed=300)
+        one = sc.make_gemv_case("rows8", 37, sc.BF16, m=8, k=k, n=500, n_normed=300)
         one.m, one.x = 1, case.x[i:i + 1]
         d1 = gh.upload_gemv(one)
         gh.run_gemv(d1)
         torch.cuda.synchronize()
         assert torch.equal(d1.normed[0], dg.normed[i]), i
         assert torch.equal(d1.unnormed[0], dg.unnormed[i]), i
+
+
+@pytest.mark.parametrize("m,k", [(4, 7168), (8, 7168), (3, 16384), (2, 64)])
+def test_x_rows_staged_in_lds_or_read_from_global_memory(m, k):
+    # the x rows go through LDS up to 64 KB (4 x 14 KB, 2 x 128 B) and
+    # through global memory past it (8 x 14 KB, 3 x 32 KB)
+    run_and_compare(sc.make_gemv_case(f"x_{m}_{k}", 41 + m, sc.BF16, m=m, k=k, n=300,
+                                      n_normed=200))
 
 
 def test_workspace_reused_on_two_calls_the_second_smaller():
