@@ -9,7 +9,7 @@
 // the whole of k: lane l takes the 16-byte chunks l, l + 64, l + 128, ... of
 // each W row (a wave reads 1 KB of a row per load instruction, fully
 // coalesced) and the same chunks of every x row (from the L1 for one row;
-// several rows are copied to LDS once per block when they fit 64 KB).  U chunks per lane are loaded before any is used, so a wave keeps
+// several rows are copied to LDS once per block when they fit 63 KB).  U chunks per lane are loaded before any is used, so a wave keeps
 // U * CPW KB of W in flight.  Each lane sums its own terms in k order with
 // one fused multiply-add per term, then an xor butterfly over the 64 lanes
 // adds the partial sums; every lane ends with the same bits (each step adds
@@ -295,8 +295,9 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
   norm_rows<DT>(a);
 }
 
-// Largest LDS copy of the x rows (more rows go through global memory).
-constexpr uint64_t kGemvMaxLdsBytes = 64 * 1024;
+// Largest LDS copy of the x rows (more rows go through global memory); 1 KB
+// of a 64 KB block allocation is left for the kernel's own LDS.
+constexpr uint64_t kGemvMaxLdsBytes = 63 * 1024;
 
 template <int DT, int MB, int CPW, int U, int WPB>
 int run(const GemvArgs& a, hipStream_t s) {

@@ -114,10 +114,10 @@ def test_rows_match_single_row_calls(k):
         assert torch.equal(d1.unnormed[0], dg.unnormed[i]), i
 
 
-@pytest.mark.parametrize("m,k", [(4, 7168), (8, 7168), (3, 16384), (2, 64)])
+@pytest.mark.parametrize("m,k", [(4, 7168), (8, 7168), (3, 16384), (2, 64), (4, 8192), (4, 8000)])
 def test_x_rows_staged_in_lds_or_read_from_global_memory(m, k):
-    # the x rows go through LDS up to 64 KB (4 x 14 KB, 2 x 128 B) and
-    # through global memory past it (8 x 14 KB, 3 x 32 KB)
+    # the x rows go through LDS up to 63 KB (4 x 14 KB, 2 x 128 B, 4 x 15.6 KB)
+    # and through global memory past it (8 x 14 KB, 3 x 32 KB, 4 x 16 KB)
     run_and_compare(sc.make_gemv_case(f"x_{m}_{k}", 41 + m, sc.BF16, m=m, k=k, n=300,
                                       n_normed=200))
 
