@@ -55,7 +55,7 @@ KERNEL_SOURCES = ("qk_rope_paged_amd/csrc/band_kernel.hpp", "qk_rope_paged_amd/c
 GEMV_KERNEL_NAME = "gemv_norm_kernel"
 GEMV_SOURCES = ("qk_rope_paged_amd/csrc/gemv_norm.hip", "qk_rope_paged_amd/csrc/gemv_norm.hpp",
                 "qk_rope_paged_amd/csrc/abi_gemv.cpp")
-GEMV_WORKLOADS = ("gemv_norm",)
+GEMV_WORKLOADS = ("gemv_norm", "gemv_norm_rows4")
 
 
 def log(*a):
@@ -216,7 +216,7 @@ def case_tokens(case) -> int:
 DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5, "bshd": 6, "prefill_tp8": 2,
                 "decode_tp8": 3, "dual_tp8": 4}
 DEFAULT_SEED.update({f"{k}_fp8": v for k, v in list(DEFAULT_SEED.items())})
-DEFAULT_SEED["gemv_norm"] = 7
+DEFAULT_SEED["gemv_norm"] = DEFAULT_SEED["gemv_norm_rows4"] = 7
 
 
 def make_case(workload: str, seed: int = None):

@@ -5,6 +5,9 @@ profiles/.
     # kernel durations (from `rocprofv3 --kernel-trace --stats -d DIR -- python bench.py ...`)
     python profile_summary.py trace DIR --label "..." --command "..."
 
+    # SQ counters per dispatch (one `rocprofv3 --pmc SQ_...` run)
+    python profile_summary.py counters DIR --workload gemv_norm --command "..."
+
     # HBM traffic per launch (from three `rocprofv3 --pmc ...` runs of
     # `bench.py --steps N --warmup 0 --sets N --copy-calibration-mib M ...`)
     python profile_summary.py traffic --fetch DIR --write DIR --tcc DIR \\
@@ -149,6 +152,25 @@ def traffic(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+def counters(args) -> str:
+    """Mean of each counter per dispatch of the workload's kernel (SQ
+    counters of one `rocprofv3 --pmc` pass)."""
+    import bench
+
+    kern = bench.kernel_name(args.workload)
+    per = {}
+    for did, name, cn, cv in _pmc(args.dir):
+        if kern in name:
+            per.setdefault(cn, {}).setdefault(did, 0.0)
+            per[cn][did] += cv
+    lines = [f"# SQ counters of {kern} on the {args.workload} workload (rocprofv3 PMC, mean per "
+             f"dispatch)", f"# command: {args.command}",
+             f"kernel_source_sha256: {bench.source_hash_for(args.workload)}"]
+    for cn in sorted(per):
+        lines.append(f"{cn}: {statistics.mean(per[cn].values()):.0f}   # over {len(per[cn])} dispatches")
+    return "\n".join(lines) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -168,8 +190,12 @@ def main() -> int:
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--calib-mib", type=int, required=True)
     p.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", required=True)
     args = ap.parse_args()
-    sys.stdout.write(trace(args) if args.mode == "trace" else traffic(args))
+    sys.stdout.write({"trace": trace, "traffic": traffic, "counters": counters}[args.mode](args))
     return 0
 
 

@@ -732,4 +732,11 @@ def gemv_norm(seed: int = 7, small: bool = False) -> GemvCase:
     return make_gemv_case("gemv_norm", seed, BF16, 1, 7168, 2112, 1536)
 
 
-GEMV_WORKLOADS = {"gemv_norm": gemv_norm}
+def gemv_norm_rows4(seed: int = 7, small: bool = False) -> GemvCase:
+    """The same projection over four rows at once (a few decode tokens)."""
+    if small:
+        return make_gemv_case("gemv_norm_rows4_small", seed, BF16, 4, 704, 216, 152)
+    return make_gemv_case("gemv_norm_rows4", seed, BF16, 4, 7168, 2112, 1536)
+
+
+GEMV_WORKLOADS = {"gemv_norm": gemv_norm, "gemv_norm_rows4": gemv_norm_rows4}

@@ -54,3 +54,6 @@ def test_gemv_bytes_by_hand_and_its_own_source_hash():
     assert bench.case_tokens(case) == 1
     assert bench.kernel_name("gemv_norm") == bench.GEMV_KERNEL_NAME
     assert bench.source_hash_for("gemv_norm") != bench.source_hash_for("prefill")
+    four = bench.make_case("gemv_norm_rows4")
+    assert bench.algorithmic_bytes(four) == w + 4 * x + gamma + 4 * out
+    assert bench.case_tokens(four) == 4
