@@ -102,6 +102,19 @@ __device__ __forceinline__ void store_elem(void* base, int64_t i, float v) {
   }
 }
 
+typedef __bf16 gbf2 __attribute__((ext_vector_type(2)));
+
+// acc + x.lo * w.lo + x.hi * w.hi for two packed 16-bit values per word
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t x, uint32_t w, float acc) {
+  if constexpr (DT == QRP_BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(gbf2, x),
+                                           __builtin_bit_cast(gbf2, w), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(gh2, x), __builtin_bit_cast(gh2, w), acc,
+                                  false);
+}
+
 // sum over the wave's 64 lanes; every lane gets the same bits
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -233,8 +246,10 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
       const uint32_t c = base + (uint32_t)u * 64u + lane;
       const bool in = c < kc;
       float wf[CPW][E];
+      if constexpr (DT == QRP_F32) {
 #pragma unroll
-      for (int j = 0; j < CPW; ++j) widen<DT>(wv[u][j], wf[j]);
+        for (int j = 0; j < CPW; ++j) widen<DT>(wv[u][j], wf[j]);
+      }
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         gv4u xv = zero;
@@ -243,12 +258,21 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
         } else {
           if (in) xv = xrow[m][c];
         }
-        float xf[E];
-        widen<DT>(xv, xf);
+        if constexpr (DT == QRP_F32) {
+          float xf[E];
+          widen<DT>(xv, xf);
 #pragma unroll
-        for (int j = 0; j < CPW; ++j)
+          for (int j = 0; j < CPW; ++j)
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[m][j] = __builtin_fmaf(xf[e], wf[j][e], acc[m][j]);
+            for (int e = 0; e < E; ++e) acc[m][j] = __builtin_fmaf(xf[e], wf[j][e], acc[m][j]);
+        } else {
+          // 16-bit types: one packed dot product per pair of elements, on
+          // the loaded words (the two products are exact in binary32)
+#pragma unroll
+          for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][j] = dot2<DT>(xv[i], wv[u][j][i], acc[m][j]);
+        }
       }
     }
   }

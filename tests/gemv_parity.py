@@ -3,8 +3,10 @@ binary32 arithmetic (u = 2^-24).
 
 The GEMV.  Each output y_j is the sum of k products.  The kernel gives each
 of a wave's 64 lanes the terms of every 64th 16-byte chunk, which the lane
-adds in k order with one fused multiply-add per term (n_l = ceil(kc / 64) *
-E terms, E elements per chunk), and then adds the 64 partial sums in a
+adds in k order (n_l = ceil(kc / 64) * E terms, E elements per chunk) --
+one fused multiply-add per term for fp32, one packed dot product per pair
+of terms for bf16 and f16 (their products are exact in binary32, so it
+rounds at most once per term) -- and then adds the 64 partial sums in a
 6-level tree.  Recursive summation of n terms errs by at most
 gamma_n = n u / (1 - n u) times the sum of the terms' magnitudes, so
     |y^ - y| <= D_j = gamma_{n_l + 6} * A_j,    A_j = sum_k |x_k w_jk|,

@@ -211,3 +211,19 @@ def test_overlapping_calls_on_two_streams_with_their_own_workspaces():
     for d, r in zip(devs, ref):
         assert torch.equal(d.normed, r.normed) and torch.equal(d.unnormed, r.unnormed)
         assert int(d.workspace[:4].view(torch.int32).item()) == 0
+
+
+@pytest.mark.parametrize("dtype,x_scale,w_std", [(sc.F16, 100.0, 1e-5), (sc.BF16, 1e30, 1e-39)])
+def test_subnormal_weights_are_not_flushed(dtype, x_scale, w_std):
+    # every weight is subnormal in the dtype; x is large, so the products are
+    # ordinary numbers: a flush of subnormal inputs would lose all of them
+    from synth import prng
+    case = sc.make_gemv_case(f"subnormal_{dtype}", 50, dtype, m=2, k=512, n=96, n_normed=40)
+    k, n = case.k, case.n
+    case.x = sc.to_bits(prng.normal(50, 9, 2 * k).reshape(2, k) * x_scale, dtype)
+    w = prng.normal(50, 10, n * k, std=w_std).reshape(n, k)
+    case.w = sc.to_bits(w, dtype)
+    vals = sc.bits_to_f64(case.w, dtype)
+    tiny = 2.0 ** -14 if dtype == sc.F16 else 2.0 ** -126
+    assert np.all(np.abs(vals) < tiny) and np.count_nonzero(vals) > 0.9 * vals.size
+    run_and_compare(case)
