@@ -342,7 +342,7 @@ int run(const GemvArgs& a, hipStream_t s) {
 template <int DT>
 int run_rows(const GemvArgs& a, hipStream_t s) {
   if (a.m <= 1) return run<DT, 1, 2, 8, 8>(a, s);
-  if (a.m <= 2) return run<DT, 2, 1, 8, 8>(a, s);
+  if (a.m <= 2) return run<DT, 2, 2, 8, 8>(a, s);
   if (a.m <= 4) return run<DT, 4, 2, 4, 4>(a, s);
   return run<DT, 8, 2, 4, 4>(a, s);
 }

@@ -36,9 +36,9 @@ struct GemvArgs {
 // of the one counter (each is serialised), but fewer blocks leave compute
 // units idle.  Measured at one row of 7168 into 2112 columns (1536 normed):
 // 2 columns x 8 waves 12.8 us; 1 x 16: 14.4; 2 x 16: 18.7; 2 x 4: 14.3;
-// 4 x 4: 14.6; 3 x 8: 15.0.  Every build has at least the four waves the
-// norm uses.
-inline uint32_t gemv_cols_per_wave(uint32_t m) { return m == 2 ? 1u : 2u; }
+// 4 x 4: 14.6; 3 x 8: 15.0; at two rows 2 x 8: 15.0, 1 x 8: 17.4.  Every
+// build has at least the four waves the norm uses.
+inline uint32_t gemv_cols_per_wave(uint32_t) { return 2u; }
 inline uint32_t gemv_waves_per_block(uint32_t m) { return m <= 2 ? 8u : 4u; }
 
 // Enqueue the kernel; returns a hipError_t value (0: launched).
