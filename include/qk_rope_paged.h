@@ -21,7 +21,8 @@
  * Ownership    The caller allocates and owns every buffer.  The library
  *              allocates no device memory, keeps no pointer after a call
  *              returns and holds no global state apart from a thread-local
- *              error string.  The one op that needs scratch memory
+ *              error string and the launch-shape overrides (set by
+ *              qrp_set_launch_override).  The one op that needs scratch memory
  *              (matmul_fused_partial_rmsnorm) takes a caller-owned
  *              workspace.
  * Asynchrony   Each call checks its host-visible arguments, enqueues ONE
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define QRP_ABI_VERSION 4
+#define QRP_ABI_VERSION 5
 
 typedef enum qrp_status {
   QRP_OK = 0,
@@ -353,6 +354,33 @@ const char* qrp_last_error(void);
 
 /* QRP_ABI_VERSION of the loaded library. */
 int32_t qrp_abi_version(void);
+
+/*
+ * Launch-shape overrides, for measurement and tests.  They change how a
+ * call's work is cut into waves and blocks, never what it computes (tests
+ * check every setting gives the same bits).  Each knob is one process-wide
+ * value; -1, the default, lets the library choose:
+ *   QRP_KNOB_PACK             0: per-token passes, 1: token-packed passes
+ *                             (ops that have both; the others ignore it)
+ *   QRP_KNOB_PASSES_PER_WAVE  1 .. 8, capped by the op's register budget
+ *   QRP_KNOB_WAVES_PER_BLOCK  1 .. 4
+ *   QRP_KNOB_XCD_REMAP        0: blocks dealt to the XCDs round-robin,
+ *                             1: consecutive blocks kept on one XCD
+ * The environment variables QRP_PACK, QRP_PASSES_PER_WAVE (0: the
+ * library's choice), QRP_WAVES_PER_BLOCK (0: the library's choice) and
+ * QRP_XCD_REMAP give the first values, read once when the library is
+ * loaded.  A launch reads the values current when it is enqueued; changing
+ * them while other threads launch is allowed but gives those launches
+ * either value.  `previous` (may be NULL) receives the old value.
+ * QRP_EINVAL for an unknown knob or a value out of range.
+ */
+enum {
+  QRP_KNOB_PACK = 0,
+  QRP_KNOB_PASSES_PER_WAVE = 1,
+  QRP_KNOB_WAVES_PER_BLOCK = 2,
+  QRP_KNOB_XCD_REMAP = 3
+};
+int32_t qrp_set_launch_override(int32_t knob, int32_t value, int32_t* previous);
 
 #ifdef __cplusplus
 }

@@ -63,7 +63,8 @@ class OrcTrace(ctypes.Structure):
     _fields_ = [("q_exact", ctypes.c_void_p), ("q_mag", ctypes.c_void_p),
                 ("k_exact", ctypes.c_void_p), ("k_mag", ctypes.c_void_p),
                 ("k_row_off", ctypes.c_void_p), ("v_row_off", ctypes.c_void_p),
-                ("k_scale_off", ctypes.c_void_p), ("v_scale_off", ctypes.c_void_p)]
+                ("k_scale_off", ctypes.c_void_p), ("v_scale_off", ctypes.c_void_p),
+                ("q_pre", ctypes.c_void_p), ("k_pre", ctypes.c_void_p)]
 
 
 class OrcBand(ctypes.Structure):
@@ -209,7 +210,8 @@ def _trace(T: int, Hq: int, Hk: int, D: int, keep: list) -> tuple:
               k_row_off=np.full((T, Hk), -1, dtype=np.int64),
               v_row_off=np.full((T, Hk), -1, dtype=np.int64),
               k_scale_off=np.full((T, Hk), -1, dtype=np.int64),
-              v_scale_off=np.full((T, Hk), -1, dtype=np.int64))
+              v_scale_off=np.full((T, Hk), -1, dtype=np.int64),
+              q_pre=np.full((T, Hq, D), np.nan), k_pre=np.full((T, Hk, D), np.nan))
     keep.append(tr)
     return tr, OrcTrace(**{k: _ptr(v) for k, v in tr.items()})
 

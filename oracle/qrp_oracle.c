@@ -259,14 +259,16 @@ static void rope_head(const double* x, double* y, double* mag, uint32_t D, const
   }
 }
 
-/* per-head RMSNorm: y_j = x_j / sqrt(mean(x^2) + eps) * (gamma_j + w) */
-static void rmsnorm_head(const double* x, double* y, uint32_t D, const void* gamma, int32_t dt,
-                         double w, double eps, int32_t multiply_before_cast) {
+/* per-head RMSNorm: y_j = x_j / sqrt(mean(x^2) + eps) * (gamma_j + w);
+ * pre_j gets x_j * r, the normalised value before any rounding */
+static void rmsnorm_head(const double* x, double* y, double* pre, uint32_t D, const void* gamma,
+                         int32_t dt, double w, double eps, int32_t multiply_before_cast) {
   double ss = 0.0;
   for (uint32_t j = 0; j < D; ++j) ss += x[j] * x[j];
   double r = 1.0 / sqrt(ss / (double)D + eps);
   for (uint32_t j = 0; j < D; ++j) {
     double g = get(gamma, dt, j);
+    pre[j] = x[j] * r;
     if (multiply_before_cast) {
       y[j] = x[j] * r * (g + w);
     } else {
@@ -279,15 +281,16 @@ static void rmsnorm_head(const double* x, double* y, uint32_t D, const void* gam
 
 /* Scratch for one head. */
 typedef struct {
-  double *x, *xn, *y, *mag;
+  double *x, *xn, *y, *mag, *pre;
 } head_buf;
 
 static int head_buf_alloc(head_buf* hb, uint32_t D) {
-  hb->x = (double*)malloc(sizeof(double) * D * 4);
+  hb->x = (double*)malloc(sizeof(double) * D * 5);
   if (!hb->x) return 0;
   hb->xn = hb->x + D;
   hb->y = hb->x + 2 * D;
   hb->mag = hb->x + 3 * D;
+  hb->pre = hb->x + 4 * D;
   return 1;
 }
 
@@ -297,7 +300,7 @@ static void head_math(head_buf* hb, uint32_t D, const void* gamma, int32_t dt, d
                       int32_t interleaved, uint32_t start) {
   const double* in = hb->x;
   if (gamma) {
-    rmsnorm_head(hb->x, hb->xn, D, gamma, dt, w, eps, mbc);
+    rmsnorm_head(hb->x, hb->xn, hb->pre, D, gamma, dt, w, eps, mbc);
     in = hb->xn;
   }
   rope_head(in, hb->y, hb->mag, D, freqs, pos, R, interleaved, start);
@@ -308,6 +311,12 @@ static void record(const head_buf* hb, uint32_t D, double* exact, double* mag) {
     if (exact) exact[j] = hb->y[j];
     if (mag) mag[j] = hb->mag[j];
   }
+}
+
+/* the normalised values before rounding, for a role that was normalised */
+static void record_pre(const head_buf* hb, uint32_t D, double* pre) {
+  if (pre)
+    for (uint32_t j = 0; j < D; ++j) pre[j] = hb->pre[j];
 }
 
 /* Store a head's result in a plain buffer of dtype dst_dt.  Elements lo ..
@@ -530,9 +539,12 @@ int32_t orc_qk_rmsnorm_rope_paged(const void* buf, int32_t dtype, uint32_t T,
       store_plain(band->q_output, (int64_t)t * (int64_t)band->q_out_row_stride + (int64_t)h * D,
                   dtype, hb.y, buf, src, dtype, D, band->q_gamma ? 0 : r0,
                   band->q_gamma ? D : r0 + R);
-      if (tr)
+      if (tr) {
         record(&hb, D, tr->q_exact ? tr->q_exact + ((uint64_t)t * Hq + h) * D : NULL,
                tr->q_mag ? tr->q_mag + ((uint64_t)t * Hq + h) * D : NULL);
+        if (band->q_gamma)
+          record_pre(&hb, D, tr->q_pre ? tr->q_pre + ((uint64_t)t * Hq + h) * D : NULL);
+      }
     }
     for (uint32_t h = 0; h < Hk; ++h) {
       const int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);
@@ -553,6 +565,8 @@ int32_t orc_qk_rmsnorm_rope_paged(const void* buf, int32_t dtype, uint32_t T,
       if (tr) {
         record(&hb, D, tr->k_exact ? tr->k_exact + ((uint64_t)t * Hk + h) * D : NULL,
                tr->k_mag ? tr->k_mag + ((uint64_t)t * Hk + h) * D : NULL);
+        if (band->k_gamma)
+          record_pre(&hb, D, tr->k_pre ? tr->k_pre + ((uint64_t)t * Hk + h) * D : NULL);
         set_off(tr->k_row_off, (uint64_t)t * Hk + h, dst);
         set_off(tr->k_scale_off, (uint64_t)t * Hk + h, so);
       }

@@ -95,6 +95,11 @@ typedef struct orc_trace {
   int64_t* v_row_off;  /* pool element offset of each V row written */
   int64_t* k_scale_off; /* FP8 caches: scale offset of each K row written */
   int64_t* v_scale_off;
+  /* Normalised roles only: x_j * r, the normalised value before any
+   * rounding (with multiply_before_cast=false it is the value the first
+   * rounding to dtype takes).  Shapes as q_exact / k_exact. */
+  double* q_pre;
+  double* k_pre;
 } orc_trace;
 
 /* One band of the norm+rope op. */

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "QRP_OK", -1: "QRP_EINVAL", -2: "QRP_EALIGN", -3: "QRP_EUNSUP
 EXPORTS = ("rope_split_store_paged", "qk_rmsnorm_rope_paged", "dual_band", "kv_cache_radd",
            "fused_qk_rope_bshd_continuous_batch", "matmul_fused_partial_rmsnorm",
            "qrp_gemv_norm_workspace_bytes", "qrp_validate", "qrp_validate_host",
-           "qrp_last_error", "qrp_abi_version")
+           "qrp_last_error", "qrp_abi_version", "qrp_set_launch_override")
 
 
 class QrpError(RuntimeError):
@@ -104,6 +104,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qrp_gemv_norm_workspace_bytes.restype = U64
     lib.qrp_abi_version.argtypes = []
     lib.qrp_abi_version.restype = I32
+    lib.qrp_set_launch_override.argtypes = [I32, I32, ctypes.POINTER(I32)]
+    lib.qrp_set_launch_override.restype = I32
     return lib
 
 
@@ -112,6 +114,42 @@ lib = _load()
 
 def last_error() -> str:
     return lib.qrp_last_error().decode()
+
+
+# launch-shape knobs (include/qk_rope_paged.h: qrp_set_launch_override)
+QRP_KNOB_PACK, QRP_KNOB_PASSES_PER_WAVE, QRP_KNOB_WAVES_PER_BLOCK, QRP_KNOB_XCD_REMAP = 0, 1, 2, 3
+_KNOBS = {"pack": QRP_KNOB_PACK, "passes_per_wave": QRP_KNOB_PASSES_PER_WAVE,
+          "waves_per_block": QRP_KNOB_WAVES_PER_BLOCK, "xcd_remap": QRP_KNOB_XCD_REMAP}
+
+
+def set_launch_override(knob: int, value: int) -> int:
+    """Set one launch-shape knob (-1: the library's choice); returns the old value."""
+    prev = ctypes.c_int32(0)
+    _check(lib.qrp_set_launch_override(knob, value, ctypes.byref(prev)), True)
+    return prev.value
+
+
+class launch_overrides:
+    """Context manager: ``with launch_overrides(pack=1, passes_per_wave=2): ...``
+    sets the named knobs (None or -1: the library's choice) and restores
+    their old values on exit."""
+
+    def __init__(self, **knobs):
+        unknown = set(knobs) - set(_KNOBS)
+        if unknown:
+            raise ValueError(f"unknown launch knobs {sorted(unknown)}")
+        self._set = {_KNOBS[k]: (-1 if v is None else int(v)) for k, v in knobs.items()}
+        self._old = {}
+
+    def __enter__(self):
+        for k, v in self._set.items():
+            self._old[k] = set_launch_override(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self._old.items():
+            set_launch_override(k, v)
+        return False
 
 
 def _check(status: int, raise_on_error: bool) -> int:

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -63,6 +64,38 @@ int env_int(const char* name, int dflt) {
   if (!s || !*s) return dflt;
   return std::atoi(s);
 }
+
+// Launch-shape overrides (qrp_set_launch_override), process-wide; -1 lets
+// the library choose.  The environment gives the first values, read once
+// when the library is loaded.
+constexpr int kKnobs = 4;
+std::atomic<int32_t> g_knob[kKnobs];
+
+bool knob_value_ok(int32_t knob, int32_t v) {
+  if (v == -1) return true;
+  switch (knob) {
+    case QRP_KNOB_PACK: return v == 0 || v == 1;
+    case QRP_KNOB_PASSES_PER_WAVE: return v >= 1 && v <= 8;
+    case QRP_KNOB_WAVES_PER_BLOCK: return v >= 1 && v <= qrp::kMaxWavesPerBlock;
+    case QRP_KNOB_XCD_REMAP: return v == 0 || v == 1;
+    default: return false;
+  }
+}
+
+struct KnobInit {
+  KnobInit() {
+    const char* names[kKnobs] = {"QRP_PACK", "QRP_PASSES_PER_WAVE", "QRP_WAVES_PER_BLOCK",
+                                 "QRP_XCD_REMAP"};
+    for (int k = 0; k < kKnobs; ++k) {
+      int v = env_int(names[k], -1);
+      // 0 meant "the library's choice" for the two counts
+      if ((k == QRP_KNOB_PASSES_PER_WAVE || k == QRP_KNOB_WAVES_PER_BLOCK) && v == 0) v = -1;
+      g_knob[k].store(knob_value_ok(k, v) ? v : -1);
+    }
+  }
+} g_knob_init;
+
+int32_t knob(int32_t k) { return g_knob[k].load(std::memory_order_relaxed); }
 
 int32_t check_cache(const qrp_paged_cache* c, int32_t dtype, uint32_t layer_idx, const char* what) {
   const std::string w(what);
@@ -193,8 +226,8 @@ struct Builder {
     // multiple of the rows a pass holds (a GPU's share of the heads under
     // head parallelism: 4 Q, 1 K, 1 V heads fill 6 of 24 rows).  Below 85 %
     // of rows filled, the token-packed layout is used: one pass per head,
-    // over a block of rpp consecutive tokens (one row each).  QRP_PACK=0 / 1
-    // forces it off / on.
+    // over a block of rpp consecutive tokens (one row each).  The
+    // QRP_KNOB_PACK override forces it off / on.
     uint32_t units = total_tokens;  // waves' work units: tokens, or token blocks
     if (allow_pack) {
       uint64_t rows = 0, slots = 0;
@@ -203,7 +236,7 @@ struct Builder {
         slots += (uint64_t)a.seg[s].n_passes * rpp;
       }
       pack = rows * 100 < slots * 85;
-      const int forced_pack = env_int("QRP_PACK", -1);
+      const int32_t forced_pack = knob(QRP_KNOB_PACK);
       if (forced_pack >= 0) pack = forced_pack != 0;
     }
     if (pack) {
@@ -219,7 +252,7 @@ struct Builder {
     const uint32_t ppt = a.passes_per_token;
     if (ppt == 0) return fail(QRP_EINVAL, "no head rows to process");  // keeps n_items >= 1
     uint32_t ppg = std::min<uint32_t>(npmax, ppt);
-    const int forced = env_int("QRP_PASSES_PER_WAVE", 0);
+    const int32_t forced = knob(QRP_KNOB_PASSES_PER_WAVE);
     if (forced > 0) {
       ppg = std::min<uint32_t>((uint32_t)forced, std::min(npmax, ppt));
     } else if (radd || one_pass) {
@@ -245,11 +278,11 @@ struct Builder {
     // Large rope/store launches run one wave per block (measured faster);
     // norm, radd and small launches group four waves per block.
     uint32_t wpb = (!radd && !norm && items >= 8192) ? 1u : (uint32_t)qrp::kMaxWavesPerBlock;
-    const int forced_wpb = env_int("QRP_WAVES_PER_BLOCK", 0);
+    const int32_t forced_wpb = knob(QRP_KNOB_WAVES_PER_BLOCK);
     if (forced_wpb > 0) wpb = std::min<uint32_t>((uint32_t)forced_wpb, qrp::kMaxWavesPerBlock);
     a.waves_per_block = wpb;
     a.n_blocks = (uint32_t)((items + wpb - 1) / wpb);
-    a.per_xcd = env_int("QRP_XCD_REMAP", 0) ? (a.n_blocks + qrp::kXcds - 1) / qrp::kXcds : 0;
+    a.per_xcd = knob(QRP_KNOB_XCD_REMAP) == 1 ? (a.n_blocks + qrp::kXcds - 1) / qrp::kXcds : 0;
     a.total_tokens = total_tokens;
     a.guess_mul = (((uint64_t)a.batch) << 32) / total_tokens;
     return QRP_OK;
@@ -342,6 +375,15 @@ extern "C" {
 const char* qrp_last_error(void) { return g_err.c_str(); }
 
 int32_t qrp_abi_version(void) { return QRP_ABI_VERSION; }
+
+int32_t qrp_set_launch_override(int32_t knob_id, int32_t value, int32_t* previous) {
+  g_err.clear();
+  if (knob_id < 0 || knob_id >= kKnobs) return fail(QRP_EINVAL, "unknown launch knob");
+  if (!knob_value_ok(knob_id, value)) return fail(QRP_EINVAL, "launch knob value out of range");
+  const int32_t old = g_knob[knob_id].exchange(value);
+  if (previous) *previous = old;
+  return QRP_OK;
+}
 
 int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_seq_len,
                                uint64_t qkv_row_stride, uint32_t n_q_heads,

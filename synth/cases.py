@@ -445,26 +445,28 @@ def make_dual_case(name: str, seed: int, dtype: str, lengths, Hq_main: int, Hk_m
                    cache_lengths=None, freq_dtype: str = F32,
                    main_cache_dtype: Optional[str] = None,
                    index_cache_dtype: Optional[str] = None, scale_dtype: str = F32,
-                   rope_tail: bool = False) -> Case:
+                   rope_tail: bool = False, index_cache_lengths=None) -> Case:
     """Dual-band workload: buffer [T, (Hq_main + 2 Hk_main + Hq_index) D] =
-    Q-main | K-main | V-main | Q-index; both bands' K caches updated in place."""
+    Q-main | K-main | V-main | Q-index; both bands' K caches updated in place.
+    The index cache has cache lengths of its own when ``index_cache_lengths``
+    is given (else the main cache's)."""
     lengths = np.asarray(lengths, dtype=np.int64)
     B = len(lengths)
     cl = np.zeros(B, dtype=np.int64) if cache_lengths is None else np.asarray(cache_lengths,
                                                                              dtype=np.int64)
-    rows = cl + lengths
+    cli = cl if index_cache_lengths is None else np.asarray(index_cache_lengths, dtype=np.int64)
     mp_main = max(1, (max_seq_len + P_main - 1) // P_main)
     mp_index = max(1, (max_seq_len + P_index - 1) // P_index)
-    main = _paged_cache(seed, S_PERM, main_cache_dtype or dtype, Hk_main, D, P_main, 1, 2, cl, rows,
-                        mp_main, None, slack, scale_dtype)
-    index = _paged_cache(seed, S_PERM + 1000, index_cache_dtype or dtype, 1, D, P_index, 1, 1, cl,
-                         rows, mp_index, None, slack, scale_dtype)
+    main = _paged_cache(seed, S_PERM, main_cache_dtype or dtype, Hk_main, D, P_main, 1, 2, cl,
+                        cl + lengths, mp_main, None, slack, scale_dtype)
+    index = _paged_cache(seed, S_PERM + 1000, index_cache_dtype or dtype, 1, D, P_index, 1, 1, cli,
+                         cli + lengths, mp_index, None, slack, scale_dtype)
     off = _offsets(lengths)
     T = int(off[-1])
     width = (Hq_main + 2 * Hk_main + Hq_index) * D
     buf = to_bits(prng.normal(seed, S_BUF, T * width), dtype).reshape(T, width)
     _prefill_rows(main, seed, S_PREFILL, 0, [0], range(B), cl, lengths)
-    _prefill_rows(index, seed, S_PREFILL + 1000, 0, [0], range(B), cl, lengths)
+    _prefill_rows(index, seed, S_PREFILL + 1000, 0, [0], range(B), cli, lengths)
     g = to_bits(prng.normal(seed, S_GAMMA, 4 * D, mean=1.0, std=0.1), dtype).reshape(4, D)
     main_band = Band(q_col=0, n_q_heads=Hq_main, k_col=-1, v_col=-1, q_gamma=g[0], k_gamma=g[1],
                      epsilon=eps_main, cache=0, q_out_row_stride=Hq_main * D)

@@ -7,6 +7,7 @@ arithmetic), and rotations use Python's complex multiplication.
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -160,3 +161,43 @@ def ulp_e4m3(x: np.ndarray) -> np.ndarray:
     ax = np.maximum(np.abs(x), 2.0 ** -6)
     e = np.floor(np.log2(ax))
     return np.power(2.0, e - 3)
+
+
+def f16_table():
+    """All finite IEEE binary16 values (as doubles) with their bits, sorted by value."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16).astype(np.float64)
+    fin = np.isfinite(vals)
+    bits, vals = bits[fin], vals[fin]
+    keep = ~((vals == 0) & (bits == 0x8000))
+    bits, vals = bits[keep], vals[keep]
+    order = np.argsort(vals, kind="stable")
+    return vals[order], bits[order]
+
+
+@functools.lru_cache(maxsize=None)
+def _table_16(dtype: str):
+    return bf16_table() if dtype == sc.BF16 else f16_table()
+
+
+def round_exact_16(q, dtype: str):
+    """Nearest-even bf16 / binary16 bits of an exact rational ``q``
+    (fractions.Fraction) by neighbour search over every finite value of the
+    type, with exact comparisons; also returns q's distance to the nearest
+    rounding midpoint, relative to |q|.  Finite results only."""
+    from fractions import Fraction
+    vals, bits = _table_16(dtype)
+    k = int(np.searchsorted(vals, float(q)))
+    cands = [i for i in range(k - 2, k + 2) if 0 <= i < len(vals)]
+    dist = {i: abs(Fraction(float(vals[i])) - q) for i in cands}
+    best = min(cands, key=lambda i: (dist[i], int(bits[i]) & 1))
+    lo = max((i for i in cands if Fraction(float(vals[i])) <= q), default=None)
+    hi = min((i for i in cands if Fraction(float(vals[i])) > q), default=None)
+    rel = Fraction(1)
+    if lo is not None and hi is not None and q != 0:
+        mid = (Fraction(float(vals[lo])) + Fraction(float(vals[hi]))) / 2
+        rel = abs(q - mid) / abs(q)
+    out = int(bits[best])
+    if out == 0 and q < 0:
+        out = 0x8000
+    return out, rel

@@ -165,9 +165,38 @@ def band_of(dc: DeviceCase, i: int) -> qrp.Band:
                     q_output=dc.q_out_rows(i), q_out_row_stride=b.q_out_row_stride)
 
 
+# launch-shape overrides held around every unprepared run() call (a test
+# sets them with monkeypatch.setattr), e.g. {"pack": 0}
+OVERRIDES: dict = {}
+
+
+def knobs(remap=None, ppw=None, wpb=None, pack=None):
+    """qrp.launch_overrides from the tests' settings: "0" or 0 for a count
+    (passes per wave, waves per block) is the library's choice."""
+    def count(v):
+        return None if v is None or int(v) == 0 else int(v)
+    kw = {}
+    if remap is not None:
+        kw["xcd_remap"] = int(remap)
+    if ppw is not None:
+        kw["passes_per_wave"] = count(ppw)
+    if wpb is not None:
+        kw["waves_per_block"] = count(wpb)
+    if pack is not None:
+        kw["pack"] = int(pack)
+    return qrp.launch_overrides(**kw)
+
+
 def run(dc: DeviceCase, stream=None, raise_on_error=True, op=None, prepare=False):
     """One call of the case's operation through the C ABI (or, with
     ``prepare``, the call bound to its marshalled arguments)."""
+    if OVERRIDES and not prepare:
+        with knobs(**OVERRIDES):
+            return _run(dc, stream, raise_on_error, op, prepare)
+    return _run(dc, stream, raise_on_error, op, prepare)
+
+
+def _run(dc: DeviceCase, stream, raise_on_error, op, prepare):
     c = dc.case
     op = op or c.op
     dt = QRP_DT[c.dtype]

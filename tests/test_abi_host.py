@@ -38,7 +38,41 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(qrp.EXPORTS)
-    assert qrp.abi_version() == 4
+    assert qrp.abi_version() == 5
+
+
+def test_launch_overrides_set_restore_and_reject():
+    old = qrp.set_launch_override(qrp.QRP_KNOB_PACK, 1)
+    assert qrp.set_launch_override(qrp.QRP_KNOB_PACK, old) == 1
+    with qrp.launch_overrides(pack=0, passes_per_wave=2, waves_per_block=4, xcd_remap=1):
+        assert qrp.set_launch_override(qrp.QRP_KNOB_PASSES_PER_WAVE, 2) == 2
+        assert qrp.set_launch_override(qrp.QRP_KNOB_XCD_REMAP, 1) == 1
+    assert qrp.set_launch_override(qrp.QRP_KNOB_PASSES_PER_WAVE, -1) == -1
+    for knob, value in ((4, 0), (-1, 0), (qrp.QRP_KNOB_PACK, 2),
+                        (qrp.QRP_KNOB_PASSES_PER_WAVE, 0), (qrp.QRP_KNOB_WAVES_PER_BLOCK, 5),
+                        (qrp.QRP_KNOB_XCD_REMAP, -2)):
+        with pytest.raises(qrp.QrpError):
+            qrp.set_launch_override(knob, value)
+    with pytest.raises(ValueError):
+        qrp.launch_overrides(bogus=1)
+
+
+def test_launch_override_environment_is_read_once_at_load():
+    # a fresh process: the variables set the first values; changing the
+    # environment afterwards changes nothing
+    import subprocess
+    import sys
+    code = ("import os, qk_rope_paged_amd as q\n"
+            "os.environ['QRP_PACK'] = '0'\n"
+            "print(q.set_launch_override(q.QRP_KNOB_PACK, -1),"
+            " q.set_launch_override(q.QRP_KNOB_PASSES_PER_WAVE, -1),"
+            " q.set_launch_override(q.QRP_KNOB_WAVES_PER_BLOCK, -1),"
+            " q.set_launch_override(q.QRP_KNOB_XCD_REMAP, -1))\n")
+    env = dict(os.environ, QRP_PACK="1", QRP_PASSES_PER_WAVE="0", QRP_WAVES_PER_BLOCK="2",
+               QRP_XCD_REMAP="1")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                         text=True, check=True).stdout.split()
+    assert out == ["1", "-1", "2", "1"]
 
 
 def test_one_hip_runtime_in_process():

@@ -131,11 +131,9 @@ def test_fp8_launch_configuration_does_not_change_bits(workload, monkeypatch):
     ref = None
     for remap, ppw, wpb in [(r, p, w) for r in ("0", "1") for p in ("0", "1", "3")
                             for w in ("0", "1", "4")]:
-        monkeypatch.setenv("QRP_XCD_REMAP", remap)
-        monkeypatch.setenv("QRP_PASSES_PER_WAVE", ppw)
-        monkeypatch.setenv("QRP_WAVES_PER_BLOCK", wpb)
         dc = gh.upload(case)
-        gh.run(dc)
+        with gh.knobs(remap, ppw, wpb):
+            gh.run(dc)
         torch.cuda.synchronize()
         snap = [gh.to_numpy_bits(q, case.q_dtype) for q in dc.q_out]
         snap += [gh.to_numpy_bits(c.pool, c.host.dtype) for c in dc.caches]

@@ -117,11 +117,9 @@ def test_launch_configuration_does_not_change_bits(workload, monkeypatch):
     for remap in ("0", "1"):
         for ppw in ("0", "1", "2", "3"):
             for wpb in ("0", "1", "2", "4"):
-                monkeypatch.setenv("QRP_XCD_REMAP", remap)
-                monkeypatch.setenv("QRP_PASSES_PER_WAVE", ppw)
-                monkeypatch.setenv("QRP_WAVES_PER_BLOCK", wpb)
                 dc = gh.upload(case)
-                gh.run(dc)
+                with gh.knobs(remap, ppw, wpb):
+                    gh.run(dc)
                 torch.cuda.synchronize()
                 snap = _snapshot(dc)
                 if ref is None:
@@ -150,7 +148,7 @@ def test_out_of_range_tokens_are_skipped(pack, monkeypatch):
     """Per-token layout: the token's wave leaves; token-packed layout: the
     token's rows stay in their wave, masked (QRP_PACK forces either)."""
     _, gh, parity = _env()
-    monkeypatch.setenv("QRP_PACK", pack)
+    monkeypatch.setattr(gh, "OVERRIDES", {"pack": int(pack)})
     lens, clen = [6, 9, 4], [10, 30, 5]
     good = sc.make_store_case("oob", 41, sc.BF16, lens, clen, Hq=8, Hk=2, D=128, rope_dim=128,
                               interleaved=True, theta=1e4, max_seq_len=512, P=16, L=1, layer=0)
@@ -257,9 +255,9 @@ def test_token_packed_layout_gives_the_same_bits(workload, monkeypatch):
     case = sc.WORKLOADS[workload](small=True)
     snaps = []
     for pack in ("0", "1"):
-        monkeypatch.setenv("QRP_PACK", pack)
         dc = gh.upload(case)
-        gh.run(dc)
+        with gh.knobs(pack=pack):
+            gh.run(dc)
         torch.cuda.synchronize()
         snap = [gh.to_numpy_bits(q, case.q_dtype) for q in dc.q_out]
         snap += [gh.to_numpy_bits(c.pool, c.host.dtype) for c in dc.caches]

@@ -18,6 +18,7 @@ import oracle
 from tests import test_oracle_bshd_pins as bshd_pins
 from tests import test_oracle_fp8_pins as fp8_pins
 from tests import test_oracle_gemv_pins as gemv_pins
+from tests import test_oracle_norm_pins as norm_pins
 from tests import test_oracle_pins as pins
 
 MUTATIONS = {
@@ -91,6 +92,31 @@ MUTATIONS = {
                                     "y[j] * r * get(gamma, dtype, n_normed - 1 - j));"),
     "partial_norm_uses_weight_offset": ("y[j] * r * get(gamma, dtype, j));",
                                         "y[j] * r * (get(gamma, dtype, j) + weight_offset));"),
+    "mbc_false_norm_unrounded": ("double n = round_to(dt, x[j] * r);", "double n = x[j] * r;"),
+    "mbc_false_gamma_sum_unrounded": ("double gw = round_to(dt, g + w);", "double gw = g + w;"),
+    "mbc_false_product_unrounded": ("y[j] = round_to(dt, n * gw);", "y[j] = n * gw;"),
+    "mbc_flag_ignored": ("if (multiply_before_cast) {", "if (1) {"),
+    "mbc_flag_inverted": ("if (multiply_before_cast) {", "if (!multiply_before_cast) {"),
+    "dual_index_uses_main_eps": (
+        "  return orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, index_band, weight_offset,",
+        "  orc_band ib_ = *index_band;\n  ib_.epsilon = main_band->epsilon;\n"
+        "  return orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, &ib_, weight_offset,"),
+    "dual_index_uses_main_cache_lengths": (
+        "  return orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, index_band, weight_offset,",
+        "  orc_cache ic_ = *index_band->cache;\n  ic_.cache_lengths = main_band->cache->cache_lengths;\n"
+        "  orc_band ib_ = *index_band;\n  ib_.cache = &ic_;\n"
+        "  return orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, &ib_, weight_offset,"),
+    "dual_index_uses_main_gammas": (
+        "  return orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, index_band, weight_offset,",
+        "  orc_band ib_ = *index_band;\n  ib_.q_gamma = main_band->q_gamma;\n  ib_.k_gamma = main_band->k_gamma;\n"
+        "  return orc_qk_rmsnorm_rope_paged(buf, dtype, T, buf_row_stride, &ib_, weight_offset,"),
+    "norm_k_rows_in_last_plane": (
+        "      const int64_t dst = row_offset(c, w.page, 0, layer_idx, w.slot, h);\n"
+        "      const int64_t so = c->scales ? scale_offset(c, w.page, 0, layer_idx, w.slot, h) : -1;\n"
+        "      const uint32_t lo",
+        "      const int64_t dst = row_offset(c, w.page, c->kv_planes - 1, layer_idx, w.slot, h);\n"
+        "      const int64_t so = c->scales ? scale_offset(c, w.page, 0, layer_idx, w.slot, h) : -1;\n"
+        "      const uint32_t lo"),
     "unnormed_from_wrong_column": ("          y[j]);\n  }\n  free(y);", "          y[j - n_normed]);\n  }\n  free(y);"),
 }
 
@@ -110,6 +136,11 @@ PIN_TESTS = [
     (pins.test_rmsnorm_constant_vector_closed_form, {}),
     (pins.test_rmsnorm_invariants, {}),
     (pins.test_rmsnorm_epsilon_sits_inside_the_root, {}),
+    (norm_pins.test_multiply_after_cast_closed_form, {"dtype": "bf16", "interleaved": True}),
+    (norm_pins.test_multiply_after_cast_closed_form, {"dtype": "f16", "interleaved": False}),
+    (norm_pins.test_multiply_before_cast_true_rounds_once, {"dtype": "bf16"}),
+    (norm_pins.test_dual_band_brute_force, {"dtype": "bf16", "interleaved": False}),
+    (norm_pins.test_dual_band_brute_force, {"dtype": "f32", "interleaved": True}),
     (pins.test_radd_is_one_binary32_add_per_element, {"dtype": "bf16"}),
     (pins.test_radd_is_one_binary32_add_per_element, {"dtype": "f32"}),
     (pins.test_trailing_partial_rope_brute_force, {"interleaved": False, "dtype": "bf16"}),

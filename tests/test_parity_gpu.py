@@ -172,6 +172,32 @@ def test_dual_band_small_with_distinct_eps_and_nonzero_cache_lengths():
     run_and_compare(case)
 
 
+@pytest.mark.parametrize("cache_dtype", [None, sc.FP8])
+@pytest.mark.parametrize("mbc", [True, False])
+@pytest.mark.parametrize("batch", [5, 40])
+def test_dual_band_index_cache_has_its_own_lengths(cache_dtype, mbc, batch):
+    # the index cache's lengths differ from the main cache's, so its rows sit
+    # at other positions (another freqs row) than the main band's; 5
+    # sequences take the small-batch lookup, 40 the guessed one
+    lens = prng.integers(27, 1, batch, 0, 12)
+    clm = prng.integers(27, 2, batch, 0, 900)
+    cli = prng.integers(27, 3, batch, 0, 900)
+    case = sc.make_dual_case(f"dual_own_lengths_{batch}", 27, sc.BF16, lens, Hq_main=16,
+                             Hk_main=4, Hq_index=4, D=128, rope_dim=64, interleaved=bool(batch % 2),
+                             theta=1e4, max_seq_len=1024, P_main=32, P_index=16, eps_main=1e-6,
+                             eps_index=1e-2, weight_offset=0.25, multiply_before_cast=mbc,
+                             cache_lengths=clm, index_cache_lengths=cli,
+                             main_cache_dtype=cache_dtype, index_cache_dtype=cache_dtype)
+    run_and_compare(case)
+
+
+@pytest.mark.parametrize("cache_dtype", [None, sc.FP8])
+def test_norm_multiply_after_cast_k_in_cache(cache_dtype):
+    case = _norm("norm_mbc0_inplace", 28, sc.BF16, [19, 3, 0, 40], [0, 7, 2, 100], True,
+                 multiply_before_cast=False, weight_offset=0.5, cache_dtype=cache_dtype)
+    run_and_compare(case)
+
+
 def test_radd_fp32_and_subnormals():
     case = sc.make_radd_case("radd_f32", 20, sc.F32, [4, 0, 13, 7], [3, 9, 1, 0, 30, 2, 5], 2,
                              Hk=3, D=64, P=8, L=2, layer=1)

@@ -12,8 +12,9 @@ force the per-token layout, even ones let the library pick (mostly the
 token-packed layout at these head counts).  Every case
 is valid by construction (positions stay below max_seq_len, rope widths are
 multiples of two 16-byte chunks); each is compared element by element with
-the parity bar of tests/parity.py (which widens it for normalised rows
-when multiply_before_cast is off, as that module derives).  The draws come from numpy generators
+the parity bar of tests/parity.py (which widens it for normalised values
+next to a midpoint of multiply_before_cast = false's first rounding, as that
+module derives).  The draws come from numpy generators
 keyed by the case index, so a failure names a reproducible case.
 """
 from __future__ import annotations
@@ -92,6 +93,10 @@ def random_case(op: str, k: int):
                                  cache_dtype=cdt, scale_dtype=sdt, rope_tail=tail)
     if op == "dual":
         lens, clen = _batch(rng)
+        kw = {}
+        if rng.random() < 0.5:                   # the index cache's own lengths
+            top = 64 if len(lens) > 20 else MSL - int(lens.max())   # many sequences: small pools
+            kw["index_cache_lengths"] = rng.integers(0, top, len(lens))
         return sc.make_dual_case(name, seed, dtype, lens, Hq_main=int(rng.integers(1, 9)),
                                  Hk_main=int(rng.integers(1, 4)), Hq_index=int(rng.integers(1, 5)),
                                  D=D, rope_dim=R, interleaved=il, theta=1e4, max_seq_len=MSL,
@@ -100,7 +105,7 @@ def random_case(op: str, k: int):
                                  weight_offset=_pick(rng, (0.0, 0.5)),
                                  multiply_before_cast=bool(rng.integers(2)), cache_lengths=clen,
                                  freq_dtype=fdt, main_cache_dtype=cdt, index_cache_dtype=cdt,
-                                 scale_dtype=sdt, rope_tail=tail)
+                                 scale_dtype=sdt, rope_tail=tail, **kw)
     if op == "radd":
         lens, clen_b = _batch(rng)
         off = int(rng.integers(0, 4))
@@ -126,9 +131,9 @@ def test_random_combination(op, k, monkeypatch):
         pytest.skip("no GPU")
     # odd cases force the per-token layout (small head counts would mostly
     # pick the token-packed one); even cases let the library choose
-    if k % 2:
-        monkeypatch.setenv("QRP_PACK", "0")
     from tests import gpu_harness as gh
+    if k % 2:
+        monkeypatch.setattr(gh, "OVERRIDES", {"pack": 0})
     from tests import parity
     case = random_case(op, k)
     print(f"[rand] {case.name} dtype={case.dtype} D={case.caches[0].head_dim} "
