@@ -24,7 +24,8 @@
  *              error string and the launch-shape overrides (set by
  *              qrp_set_launch_override).  The one op that needs scratch memory
  *              (matmul_fused_partial_rmsnorm) takes a caller-owned
- *              workspace.
+ *              workspace; its _noalloc form uses a fixed device array of
+ *              the library's own instead.
  * Asynchrony   Each call checks its host-visible arguments, enqueues ONE
  *              kernel on `stream` (a hipStream_t passed as void*; NULL is the
  *              null stream) and returns without synchronising.
@@ -61,7 +62,7 @@
 extern "C" {
 #endif
 
-#define QRP_ABI_VERSION 5
+#define QRP_ABI_VERSION 6
 
 typedef enum qrp_status {
   QRP_OK = 0,
@@ -325,6 +326,32 @@ int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_st
                                      float epsilon, float weight_offset, int32_t dtype,
                                      int32_t transpose_b, void* workspace,
                                      uint64_t workspace_bytes, void* stream);
+
+/*
+ * matmul_fused_partial_rmsnorm for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors
+ * (the same kernel, bit for bit) without the workspace: the scratch is the
+ * library's own, a device array of 256 + 4 * 131072 bytes that each GPU
+ * the library runs on holds until the process ends.  It serves
+ * m * n_normed <= 131072 (m rows of up to 131072 / m normed columns);
+ * larger calls return QRP_EINVAL and go through the workspace form.  The
+ * first call on a device (the device current on the calling thread, which
+ * must be the stream's) looks the array up and clears its counter with a
+ * kernel on `stream`; no call allocates or frees memory.  Every call on a
+ * GPU shares that GPU's array, and each call leaves its counter at zero:
+ * calls that overlap in time on one GPU (other streams, other threads)
+ * race and give wrong results; order them on one stream or use the
+ * workspace form.
+ */
+int32_t matmul_fused_partial_rmsnorm_noalloc(void* normed_output, uint64_t normed_row_stride,
+                                             void* unnormed_output, uint64_t unnormed_row_stride,
+                                             const void* input, uint64_t input_row_stride,
+                                             uint32_t m, const void* weight,
+                                             uint64_t weight_row_stride, uint32_t n, uint32_t k,
+                                             const void* gamma, uint32_t n_normed, float epsilon,
+                                             float weight_offset, int32_t dtype,
+                                             int32_t transpose_b, void* stream);
 
 /*
  * Debug check of the device metadata one of the calls above would use:

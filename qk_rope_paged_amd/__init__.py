@@ -27,6 +27,7 @@ STATUS_NAMES = {0: "QRP_OK", -1: "QRP_EINVAL", -2: "QRP_EALIGN", -3: "QRP_EUNSUP
 # entry points declared in include/qk_rope_paged.h
 EXPORTS = ("rope_split_store_paged", "qk_rmsnorm_rope_paged", "dual_band", "kv_cache_radd",
            "fused_qk_rope_bshd_continuous_batch", "matmul_fused_partial_rmsnorm",
+           "matmul_fused_partial_rmsnorm_noalloc",
            "qrp_gemv_norm_workspace_bytes", "qrp_validate", "qrp_validate_host",
            "qrp_last_error", "qrp_abi_version", "qrp_set_launch_override")
 
@@ -91,6 +92,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "fused_qk_rope_bshd_continuous_batch": [P, I32, U32, U32, U32, P, PR, PC, U32, P, P],
         "matmul_fused_partial_rmsnorm": [P, U64, P, U64, P, U64, U32, P, U64, U32, U32, P, U32,
                                          F, F, I32, I32, P, U64, P],
+        "matmul_fused_partial_rmsnorm_noalloc": [P, U64, P, U64, P, U64, U32, P, U64, U32, U32,
+                                                 P, U32, F, F, I32, I32, P],
         "qrp_validate": [P, U32, U32, U32, PC, U32, P],
         "qrp_validate_host": [P, U32, U32, U32, P, P, U32, U32, U32, U64, U32],
     }
@@ -350,6 +353,21 @@ def matmul_fused_partial_rmsnorm(normed_output, normed_row_stride: int, unnormed
             n_normed, epsilon, weight_offset, dtype, transpose_b, _ptr(workspace),
             workspace_bytes, _stream(stream))
     return _call(lib.matmul_fused_partial_rmsnorm, args, [], raise_on_error, prepare)
+
+
+def matmul_fused_partial_rmsnorm_noalloc(normed_output, normed_row_stride: int, unnormed_output,
+                                         unnormed_row_stride: int, input, input_row_stride: int,
+                                         m: int, weight, weight_row_stride: int, n: int, k: int,
+                                         gamma, n_normed: int, epsilon: float,
+                                         weight_offset: float, dtype: int, transpose_b: int = 1,
+                                         stream=None, raise_on_error: bool = True,
+                                         prepare: bool = False):
+    """The same op with the library's own scratch (m * n_normed <= 131072);
+    calls that overlap on one GPU race."""
+    args = (_ptr(normed_output), normed_row_stride, _ptr(unnormed_output), unnormed_row_stride,
+            _ptr(input), input_row_stride, m, _ptr(weight), weight_row_stride, n, k, _ptr(gamma),
+            n_normed, epsilon, weight_offset, dtype, transpose_b, _stream(stream))
+    return _call(lib.matmul_fused_partial_rmsnorm_noalloc, args, [], raise_on_error, prepare)
 
 
 def qrp_validate(input_row_offsets, batch_size: int, total_seq_len: int, batch_offset: int,

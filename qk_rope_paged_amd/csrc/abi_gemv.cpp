@@ -19,21 +19,21 @@ bool dtype_ok(int32_t dt) { return dt == QRP_F32 || dt == QRP_BF16 || dt == QRP_
 
 }  // namespace
 
-extern "C" {
-
-uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed) {
+extern "C" uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed) {
   if (n_normed == 0) return 0;
   return qrp::kGemvCounterBytes + 4ull * m * n_normed;
 }
 
-int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_stride,
-                                     void* unnormed_output, uint64_t unnormed_row_stride,
-                                     const void* input, uint64_t input_row_stride, uint32_t m,
-                                     const void* weight, uint64_t weight_row_stride, uint32_t n,
-                                     uint32_t k, const void* gamma, uint32_t n_normed,
-                                     float epsilon, float weight_offset, int32_t dtype,
-                                     int32_t transpose_b, void* workspace,
-                                     uint64_t workspace_bytes, void* stream) {
+namespace {
+
+// Both entry points.  no_alloc: the scratch is the library's own (the
+// workspace arguments are unused), sized for m * n_normed <= kGemvScratchFloats.
+int32_t gemv_call(void* normed_output, uint64_t normed_row_stride, void* unnormed_output,
+                  uint64_t unnormed_row_stride, const void* input, uint64_t input_row_stride,
+                  uint32_t m, const void* weight, uint64_t weight_row_stride, uint32_t n,
+                  uint32_t k, const void* gamma, uint32_t n_normed, float epsilon,
+                  float weight_offset, int32_t dtype, int32_t transpose_b, void* workspace,
+                  uint64_t workspace_bytes, void* stream, bool no_alloc) {
   qrp::clear_error();
   (void)weight_offset;  // not consumed by this op (its page's Args)
   if (!dtype_ok(dtype)) return qrp::set_error(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
@@ -44,7 +44,7 @@ int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_st
   if (m == 0 || n == 0) return QRP_OK;
   if (n >= (1u << 31)) return qrp::set_error(QRP_EINVAL, "n >= 2^31 columns in one launch");
   if (!input || !weight) return qrp::set_error(QRP_EINVAL, "input / weight is NULL");
-  if (n_normed && (!gamma || !normed_output || !workspace))
+  if (n_normed && (!gamma || !normed_output || (!workspace && !no_alloc)))
     return qrp::set_error(QRP_EINVAL, "gamma, normed_output and workspace are needed when n_normed > 0");
   if (n_normed < n && !unnormed_output)
     return qrp::set_error(QRP_EINVAL, "unnormed_output is NULL with columns past n_normed");
@@ -63,8 +63,21 @@ int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_st
     return qrp::set_error(QRP_EINVAL, "normed_row_stride < n_normed");
   if (n_normed < n && unnormed_row_stride < n - n_normed)
     return qrp::set_error(QRP_EINVAL, "unnormed_row_stride < n - n_normed");
-  if (workspace_bytes < qrp_gemv_norm_workspace_bytes(m, n_normed))
+  if (no_alloc) {
+    if ((uint64_t)m * n_normed > qrp::kGemvScratchFloats)
+      return qrp::set_error(QRP_EINVAL, "m * n_normed exceeds the library's scratch (" +
+                                            std::to_string(qrp::kGemvScratchFloats) +
+                                            " values); use matmul_fused_partial_rmsnorm");
+    workspace = nullptr;
+    if (n_normed) {
+      const int e = qrp::gemv_scratch(&workspace, stream);
+      if (e != 0)
+        return qrp::set_error(QRP_EHIP, std::string("scratch set-up failed: ") +
+                                            hipGetErrorString(static_cast<hipError_t>(e)));
+    }
+  } else if (workspace_bytes < qrp_gemv_norm_workspace_bytes(m, n_normed)) {
     return qrp::set_error(QRP_EINVAL, "workspace smaller than qrp_gemv_norm_workspace_bytes(m, n_normed)");
+  }
 
   qrp::GemvArgs a{};
   a.x = input;
@@ -95,6 +108,37 @@ int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_st
     return qrp::set_error(QRP_EHIP, std::string("kernel launch failed: ") +
                               hipGetErrorString(static_cast<hipError_t>(e)));
   return QRP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_stride,
+                                     void* unnormed_output, uint64_t unnormed_row_stride,
+                                     const void* input, uint64_t input_row_stride, uint32_t m,
+                                     const void* weight, uint64_t weight_row_stride, uint32_t n,
+                                     uint32_t k, const void* gamma, uint32_t n_normed,
+                                     float epsilon, float weight_offset, int32_t dtype,
+                                     int32_t transpose_b, void* workspace,
+                                     uint64_t workspace_bytes, void* stream) {
+  return gemv_call(normed_output, normed_row_stride, unnormed_output, unnormed_row_stride, input,
+                   input_row_stride, m, weight, weight_row_stride, n, k, gamma, n_normed,
+                   epsilon, weight_offset, dtype, transpose_b, workspace, workspace_bytes, stream,
+                   false);
+}
+
+int32_t matmul_fused_partial_rmsnorm_noalloc(void* normed_output, uint64_t normed_row_stride,
+                                             void* unnormed_output, uint64_t unnormed_row_stride,
+                                             const void* input, uint64_t input_row_stride,
+                                             uint32_t m, const void* weight,
+                                             uint64_t weight_row_stride, uint32_t n, uint32_t k,
+                                             const void* gamma, uint32_t n_normed, float epsilon,
+                                             float weight_offset, int32_t dtype,
+                                             int32_t transpose_b, void* stream) {
+  return gemv_call(normed_output, normed_row_stride, unnormed_output, unnormed_row_stride, input,
+                   input_row_stride, m, weight, weight_row_stride, n, k, gamma, n_normed,
+                   epsilon, weight_offset, dtype, transpose_b, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

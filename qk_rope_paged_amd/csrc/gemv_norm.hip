@@ -38,6 +38,9 @@
 
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include "gemv_norm.hpp"
 #include "qk_rope_paged.h"
 
@@ -347,7 +350,46 @@ int run_rows(const GemvArgs& a, hipStream_t s) {
   return run<DT, 8, 2, 4, 4>(a, s);
 }
 
+// Clears the arrival counter's line of a scratch buffer.
+__global__ void __launch_bounds__(64) clear_counter(uint32_t* c) {
+  if (threadIdx.x < kGemvCounterBytes / 4) c[threadIdx.x] = 0u;
+}
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device; null until that device is set up
+
 }  // namespace
+
+// Scratch of the entry point that allocates nothing: the arrival counter's
+// line, then the y values.  Each GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses this name as an address: it
+// stands for the host-side shadow of the variable; gemv_scratch() looks up
+// each device's copy.
+static __device__ __align__(256) unsigned char scratch[kGemvScratchBytes];
+
+int gemv_scratch(void** out, void* stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    // the counter must be zero before the first call (every call leaves it
+    // at zero); a kernel, not a memset, so that a captured first call
+    // records it as a kernel node
+    hipLaunchKernelGGL(clear_counter, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream),
+                       static_cast<uint32_t*>(p));
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
 
 int launch_gemv_norm(const GemvArgs& a, int32_t dtype, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -44,4 +44,15 @@ inline uint32_t gemv_waves_per_block(uint32_t m) { return m <= 2 ? 8u : 4u; }
 // Enqueue the kernel; returns a hipError_t value (0: launched).
 int launch_gemv_norm(const GemvArgs& a, int32_t dtype, void* stream);
 
+// The library's own scratch for callers that cannot allocate: per GPU, the
+// counter's line and then at most kGemvScratchFloats binary32 y values
+// (m * n_normed of them per call).
+constexpr uint64_t kGemvScratchFloats = 131072;
+constexpr uint64_t kGemvScratchBytes = kGemvCounterBytes + 4 * kGemvScratchFloats;
+
+// Device address of the current device's scratch (set up on the first call
+// for that device: its address looked up, its counter cleared on `stream`).
+// Returns a hipError_t value (0: *out is set).
+int gemv_scratch(void** out, void* stream);
+
 }  // namespace qrp

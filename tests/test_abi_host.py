@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(qrp.EXPORTS)
-    assert qrp.abi_version() == 5
+    assert qrp.abi_version() == 6
 
 
 def test_launch_overrides_set_restore_and_reject():
@@ -73,6 +73,19 @@ def test_launch_override_environment_is_read_once_at_load():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
                          text=True, check=True).stdout.split()
     assert out == ["1", "-1", "2", "1"]
+
+
+def test_noalloc_gemv_rejects_sizes_past_its_scratch_on_the_host():
+    # m * n_normed above the library's scratch: QRP_EINVAL before any device call
+    st = qrp.matmul_fused_partial_rmsnorm_noalloc(
+        FAKE, 65537, FAKE, 64, FAKE, 64, 2, FAKE, 64, 65600, 64, FAKE, 65537, 1e-6, 0.0,
+        qrp.QRP_BF16, stream=0, raise_on_error=False)
+    assert st == qrp.QRP_EINVAL and "scratch" in qrp.last_error()
+    # the workspace form is still checked as before
+    st = qrp.matmul_fused_partial_rmsnorm(FAKE, 64, FAKE, 16, FAKE, 64, 1, FAKE, 64, 80, 64, FAKE,
+                                          64, 1e-6, 0.0, qrp.QRP_BF16, FAKE, 16, stream=0,
+                                          raise_on_error=False)
+    assert st == qrp.QRP_EINVAL and "workspace" in qrp.last_error()
 
 
 def test_one_hip_runtime_in_process():
