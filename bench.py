@@ -27,8 +27,15 @@ Also measured in the same run: a plain streaming copy moving the same bytes
 
 Printed: one JSON line.  `value` is effective GB/s (algorithmic bytes per
 step / wall time per step), `roofline.achieved` the same bytes over the
-kernel's own average duration (HIP events around each launch on the launch
-stream), `cpu_baseline` the CPU oracle on the host, single-threaded.
+kernel's own average duration (HIP events around the timed launches on the
+launch stream), `kernel_us` that average and the p10/p50/p90 of single
+launches (each between its own events), `cpu_baseline` the CPU oracle on the
+host, single-threaded.  The default (prefill) line also carries `decode`:
+the Llama-3-8B-shaped decode workload (256 sequences of one new token),
+measured first with its own launch counts (--decode-steps, --decode-warmup)
+and its own same-size copy ceiling.  `roofline.traffic` and `tcc_hit_rate`
+come from the committed counter summary under profiles/ while its kernel
+source hash matches the sources built.
 """
 from __future__ import annotations
 
@@ -105,11 +112,9 @@ def source_hash_for(workload: str) -> str:
     return kernel_source_hash(GEMV_SOURCES if workload in GEMV_WORKLOADS else None)
 
 
-def traffic_from_profiles(workload: str, seeds):
-    """Measured HBM bytes per launch, averaged like the timed steps, from the
-    committed counter summary (per-batch read and write bytes, already scaled
-    by the copy calibration), or None when the summary is missing, lacks a
-    batch, or was taken from a different kernel source."""
+def _traffic_summary(workload: str):
+    """Key/value lines of the committed counter summary of this workload, or
+    None when it is missing or was taken from a different kernel source."""
     path = os.path.join(ROOT, "profiles", f"{kernel_name(workload)}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -118,8 +123,29 @@ def traffic_from_profiles(workload: str, seeds):
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
+                kv[k.strip()] = v.split("#")[0].strip()
     if kv.get("kernel_source_sha256") != source_hash_for(workload):
+        return None
+    return kv
+
+
+def tcc_hit_rate_from_profiles(workload: str):
+    """TCC hit rate (TCC_HIT / (TCC_HIT + TCC_MISS)) of the kernel on this
+    workload from the committed counter summary, or None (missing or stale)."""
+    kv = _traffic_summary(workload)
+    try:
+        return None if kv is None else float(kv["tcc_hit_rate"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_from_profiles(workload: str, seeds):
+    """Measured HBM bytes per launch, averaged like the timed steps, from the
+    committed counter summary (per-batch read and write bytes, already scaled
+    by the copy calibration), or None when the summary is missing, lacks a
+    batch, or was taken from a different kernel source."""
+    kv = _traffic_summary(workload)
+    if kv is None:
         return None
     total = 0.0
     try:
@@ -349,9 +375,51 @@ def time_region(calls, steps: int, warmup: int):
     return time.perf_counter() - t0, ev0.elapsed_time(ev1) / 1e3
 
 
-def copy_ceiling(nbytes: int, n_bufs: int, steps: int) -> dict:
+def time_graph(launchers, steps: int, max_nodes: int = 250, wall_out=None) -> float:
+    """Average GPU seconds per launch when the launches are replayed from a
+    HIP graph: min(steps, max_nodes) launches (cycling `launchers`, each a
+    function of the stream to launch on) are captured once and the graph is
+    replayed until `steps` launches have run, between one pair of events
+    (and two synchronisations: their wall time goes to `wall_out[0]`).
+    Launch-bound kernels are issued this way in a serving loop; the host's
+    per-launch cost then drops out of the measurement."""
+    import torch
+
+    n = min(steps, max_nodes)
+    reps = -(-steps // n)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(min(3, len(launchers))):
+            launchers[i](s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for k in range(n):
+            launchers[k % len(launchers)](s)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    if wall_out is not None:
+        wall_out[0] = time.perf_counter() - t0
+    del g
+    return ev0.elapsed_time(ev1) / 1e3 / (reps * n)
+
+
+def copy_ceiling(nbytes: int, n_bufs: int, steps: int, graph: bool = False) -> dict:
     """A plain streaming copy of nbytes/2 (read) into nbytes/2 (written),
-    cycling through n_bufs buffer pairs: the best of 1 and 4 chunks/thread."""
+    cycling through n_bufs buffer pairs: the best of 1 and 4 chunks/thread;
+    with `graph`, the launches are replayed from a HIP graph."""
     import ctypes
     import torch
     from qk_rope_paged_amd import build as hip_build
@@ -371,8 +439,18 @@ def copy_ceiling(nbytes: int, n_bufs: int, steps: int) -> dict:
                 if lib.qrp_bench_stream_copy(b.data_ptr(), a.data_ptr(), half, u, stream) != 0:
                     raise RuntimeError("copy launch failed")
             return f
-        _, gpu = time_region([mk(a, b) for a, b in bufs], steps, 10)
-        avg = gpu / steps
+        if graph:
+            def mkg(a, b, u=u):
+                def f(st):
+                    if lib.qrp_bench_stream_copy(b.data_ptr(), a.data_ptr(), half, u,
+                                                 st.cuda_stream) != 0:
+                        raise RuntimeError("copy launch failed")
+                return f
+            time_region([mk(a, b) for a, b in bufs], 10, 10)
+            avg = time_graph([mkg(a, b) for a, b in bufs], steps)
+        else:
+            _, gpu = time_region([mk(a, b) for a, b in bufs], steps, 10)
+            avg = gpu / steps
         if best is None or avg < best[1]:
             best = (u, avg)
     ok = all(torch.equal(a, b) for a, b in bufs[:2])
@@ -381,7 +459,8 @@ def copy_ceiling(nbytes: int, n_bufs: int, steps: int) -> dict:
     return {"value": round(2 * half / best[1] / 1e9, 2), "unit": "GB/s",
             "kernel_us": round(best[1] * 1e6, 3), "bytes": 2 * half,
             "chunks_per_thread": best[0], "verified": ok,
-            "kind": "nontemporal streaming copy, same bytes as one step (half read, half written)"}
+            "kind": "nontemporal streaming copy, same bytes as one step (half read, half written)"
+                    + (", launches replayed from a HIP graph" if graph else "")}
 
 
 def cpu_baseline(cases, seconds: float, max_passes: int) -> dict:
@@ -441,6 +520,125 @@ def check_parity(case, dc, shared_pool: bool) -> str:
     return "ok"
 
 
+def percentiles(values, qs=(10, 50, 90)):
+    """Nearest-rank percentiles of a list."""
+    v = sorted(values)
+    return {q: v[min(len(v) - 1, (q * len(v)) // 100)] for q in qs}
+
+
+def prepare(workload: str, base_seed: int, sets_arg: int):
+    """Seeded batches of the workload and their device buffer sets."""
+    import torch
+    from tests import gpu_harness as gh
+
+    t_gen = time.perf_counter()
+    first = make_case(workload, base_seed)
+    per_step = max(algorithmic_bytes(first), 1)
+    n_sets = sets_arg or min(16, max(2, -(-3 * MALL_BYTES // per_step) + 1))
+    cases = [first] + [make_case(workload, base_seed + 100 * k) for k in range(1, n_sets)]
+    set_bytes = [algorithmic_bytes(c) for c in cases]
+    log(f"[bench] {first.name}: {n_sets} seeded batches, tokens {[c.T for c in cases]}, "
+        f"mean bytes/step {sum(set_bytes) / n_sets:.0f} (generated in "
+        f"{time.perf_counter() - t_gen:.1f}s)")
+    if first.op == "gemv_norm":
+        sets, shared_pool = [gh.upload_gemv(c) for c in cases], False
+        calls = [gh.run_gemv(dg, prepare=True) for dg in sets]
+    else:
+        sets, shared_pool = build_sets(cases)
+        calls = [gh.run(dc, prepare=True) for dc in sets]
+    torch.cuda.synchronize()
+    return cases, set_bytes, sets, shared_pool, calls
+
+
+def measure(workload: str, calls, cases, set_bytes, steps: int, warmup: int,
+            launchers=None) -> dict:
+    """K launches back to back (cycling the sets) between one pair of HIP
+    events on the launch stream, then the same K launches each between its
+    own pair (the spread of single launches; an event pair adds about 2 us
+    to what it measures).  With `launchers`, the timed K launches are
+    replayed from a HIP graph instead (after W eager warm-up launches)."""
+    n_sets = len(cases)
+    if launchers is None:
+        wall, gpu_time = time_region(calls, steps, warmup)
+    else:
+        import torch
+        for i in range(warmup):
+            calls[i % n_sets]()
+        torch.cuda.synchronize()
+        w = [0.0]
+        gpu_time = time_graph(launchers, steps, max_nodes=steps, wall_out=w) * steps
+        wall = w[0]
+    _, durs = time_launches(calls, steps, 0)
+    step_bytes = [set_bytes[k % n_sets] for k in range(steps)]
+    step_tokens = [case_tokens(cases[k % n_sets]) for k in range(steps)]
+    us = percentiles([d * 1e6 for d in durs])
+    rate = percentiles([b / d / 1e9 for b, d in zip(step_bytes, durs)])
+    achieved = sum(step_bytes) / gpu_time / 1e9
+    log(f"[bench] {cases[0].name}: {steps} steps, wall {wall * 1e3:.2f} ms, events "
+        f"{gpu_time * 1e3:.2f} ms ({gpu_time / steps * 1e6:.2f} us per launch); single launches "
+        f"p10/p50/p90 {us[10]:.2f}/{us[50]:.2f}/{us[90]:.2f} us")
+    return {"wall": wall, "gpu_time": gpu_time, "step_bytes": step_bytes,
+            "step_tokens": step_tokens, "achieved": achieved,
+            "kernel_us": {"avg": round(gpu_time / steps * 1e6, 3),
+                          "single_launch_p10": round(us[10], 3),
+                          "single_launch_p50": round(us[50], 3),
+                          "single_launch_p90": round(us[90], 3)},
+            "single_launch_gbs": {"p10": round(rate[10], 1), "p50": round(rate[50], 1),
+                                  "p90": round(rate[90], 1)},
+            "traffic": traffic_from_profiles(workload, [cases[k % n_sets].seed
+                                                        for k in range(steps)]),
+            "tcc_hit_rate": tcc_hit_rate_from_profiles(workload)}
+
+
+def graph_launchers(sets, gemv: bool):
+    """One launcher per buffer set, taking the stream to launch on."""
+    from tests import gpu_harness as gh
+    if gemv:
+        return [lambda st, dg=dg: gh.run_gemv(dg, stream=st) for dg in sets]
+    return [lambda st, dc=dc: gh.run(dc, stream=st) for dc in sets]
+
+
+def decode_block(args) -> dict:
+    """The Llama-3-8B-shaped decode workload (256 sequences of one new token),
+    measured with its own launch counts and copy ceiling: the second
+    configuration the fused kernel is held to.  One decode launch takes less
+    GPU time than the host needs to issue it (a few microseconds through
+    the C ABI), so eagerly issued launches measure the host; the kernel's
+    rate comes from launches replayed from a HIP graph, the way a serving
+    loop issues them, and the copy ceiling is measured the same way.  The
+    eager figures are kept beside it."""
+    import torch
+
+    w = "decode"
+    cases, set_bytes, sets, _, calls = prepare(w, DEFAULT_SEED[w], 0)
+    m = measure(w, calls, cases, set_bytes, args.decode_steps, args.decode_warmup)
+    per_launch = time_graph(graph_launchers(sets, False), args.decode_steps)
+    del sets, calls
+    torch.cuda.empty_cache()
+    n = len(cases)
+    mean_bytes = sum(set_bytes) / n
+    achieved = mean_bytes / per_launch / 1e9
+    cc = copy_ceiling(int(mean_bytes), n, max(200, args.decode_steps), graph=True)
+    log(f"[bench] decode: graph replay {per_launch * 1e6:.3f} us per launch, copy "
+        f"{cc['kernel_us']:.3f} us")
+    return {"workload": workload_config(cases[0], cases)["workload"], "sequences": cases[0].batch,
+            "steps": args.decode_steps, "warmup": args.decode_warmup,
+            "kernel_us": {"graph_replay_avg": round(per_launch * 1e6, 3),
+                          "eager_avg": m["kernel_us"]["avg"],
+                          "eager_single_launch_p10": m["kernel_us"]["single_launch_p10"],
+                          "eager_single_launch_p50": m["kernel_us"]["single_launch_p50"],
+                          "eager_single_launch_p90": m["kernel_us"]["single_launch_p90"]},
+            "achieved": round(achieved, 2), "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "eager_achieved": round(m["achieved"], 2),
+            "tokens_per_s": round(case_tokens(cases[0]) / per_launch, 1),
+            "algorithmic_bytes_per_step": round(mean_bytes),
+            "copy_ceiling": {"value": cc["value"], "kernel_us": cc["kernel_us"],
+                             "kind": cc["kind"]},
+            "frac_of_copy_ceiling": round(achieved / cc["value"], 4),
+            "traffic": m["traffic"], "tcc_hit_rate": m["tcc_hit_rate"]}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,6 +654,13 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode block of the default (prefill) line")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the timed launches from a HIP graph (captured before "
+                         "the timed region)")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--decode-warmup", type=int, default=300)
     ap.add_argument("--seed", type=int, default=None, help="seed of the first batch")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
@@ -475,25 +680,17 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
-    from tests import gpu_harness as gh
 
-    t_gen = time.perf_counter()
+    # The default line also carries the decode configuration, measured
+    # first, on its own buffers.
+    decode = None
+    if args.workload == "prefill" and not args.no_decode:
+        decode = decode_block(args)
+
     base_seed = args.seed if args.seed is not None else DEFAULT_SEED[args.workload]
-    first = make_case(args.workload, base_seed)
-    per_step = max(algorithmic_bytes(first), 1)
-    n_sets = args.sets or min(16, max(2, -(-3 * MALL_BYTES // per_step) + 1))
-    cases = [first] + [make_case(args.workload, base_seed + 100 * k) for k in range(1, n_sets)]
-    set_bytes = [algorithmic_bytes(c) for c in cases]
-    log(f"[bench] {first.name}: {n_sets} seeded batches, tokens {[c.T for c in cases]}, "
-        f"mean bytes/step {sum(set_bytes) / n_sets:.0f} (generated in "
-        f"{time.perf_counter() - t_gen:.1f}s)")
-    if first.op == "gemv_norm":
-        sets, shared_pool = [gh.upload_gemv(c) for c in cases], False
-        calls = [gh.run_gemv(dg, prepare=True) for dg in sets]
-    else:
-        sets, shared_pool = build_sets(cases)
-        calls = [gh.run(dc, prepare=True) for dc in sets]
-    torch.cuda.synchronize()
+    cases, set_bytes, sets, shared_pool, calls = prepare(args.workload, base_seed, args.sets)
+    first = cases[0]
+    n_sets = len(cases)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -508,16 +705,9 @@ def main() -> int:
     K = args.steps
     # Timed region: K steps back to back on the launch stream, bracketed by
     # one pair of HIP events (GPU time) and two synchronisations (wall time).
-    wall, gpu_time = time_region(calls, K, args.warmup)
-    # spread of single launches: the same K launches again, each between its
-    # own two events (an event pair adds about 2 us to what it measures)
-    _, durs = time_launches(calls, K, 0)
-    step_bytes = [set_bytes[k % n_sets] for k in range(K)]
-    step_tokens = [case_tokens(cases[k % n_sets]) for k in range(K)]
-    kern = sorted(durs)
-    log(f"[bench] timed {K} steps: wall {wall * 1e3:.2f} ms, events {gpu_time * 1e3:.2f} ms "
-        f"({gpu_time / K * 1e6:.2f} us per launch); single launches p10 {kern[K // 10] * 1e6:.2f} "
-        f"us, p90 {kern[(9 * K) // 10] * 1e6:.2f} us")
+    launchers = graph_launchers(sets, first.op == "gemv_norm") if args.graph else None
+    m = measure(args.workload, calls, cases, set_bytes, K, args.warmup, launchers)
+    wall, gpu_time = m["wall"], m["gpu_time"]
 
     # the oracle runs only in the CPU-baseline leg: its first batch also
     # checks the GPU's outputs (before the copy ceiling frees the buffers)
@@ -530,10 +720,9 @@ def main() -> int:
         log("[bench] timing the CPU oracle ...")
         cpu = cpu_baseline(cases, args.cpu_seconds, args.cpu_max_passes)
 
-    mean_bytes = sum(step_bytes) / K
-    value = sum(step_bytes) / wall / 1e9
-    achieved = sum(step_bytes) / gpu_time / 1e9
-    traffic = traffic_from_profiles(args.workload, [cases[k % n_sets].seed for k in range(K)])
+    mean_bytes = sum(m["step_bytes"]) / K
+    value = sum(m["step_bytes"]) / wall / 1e9
+    achieved = m["achieved"]
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -548,16 +737,17 @@ def main() -> int:
         "dtype": first.dtype,
         "data": "synthetic (seeded batches with the workload's shapes and length distribution)",
         "config": workload_config(first, cases),
-        "tokens_per_s": round(sum(step_tokens) / wall, 1),
+        "tokens_per_s": round(sum(m["step_tokens"]) / wall, 1),
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": round(mean_bytes),
-        "kernel_us": {"avg": round(gpu_time / K * 1e6, 3),
-                      "single_launch_p10": round(kern[K // 10] * 1e6, 3),
-                      "single_launch_p90": round(kern[(9 * K) // 10] * 1e6, 3)},
+        "kernel_us": m["kernel_us"],
+        "timed_launches": "replayed from a HIP graph" if args.graph else "issued eagerly",
+        "single_launch_gbs": m["single_launch_gbs"],
         "parity": parity_status,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": kernel_name(args.workload)},
+                     "traffic": m["traffic"], "tcc_hit_rate": m["tcc_hit_rate"],
+                     "kernel": kernel_name(args.workload)},
     }
     if not args.no_copy_ceiling:
         del sets, calls
@@ -566,6 +756,8 @@ def main() -> int:
         cc = copy_ceiling(int(mean_bytes), n_sets, max(20, K // 2))
         out["copy_ceiling"] = cc
         out["roofline"]["frac_of_copy_ceiling"] = round(achieved / cc["value"], 4)
+    if decode is not None:
+        out["decode"] = decode
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -387,6 +387,29 @@ __device__ __forceinline__ uint32_t find_seq(const uint32_t* __restrict__ off, u
   return lo;
 }
 
+// The small-batch metadata (17 offsets, 16 cache lengths of each cache)
+// through one empty asm statement: no instruction, but the compiler must have
+// every value in an SGPR at that point, which keeps all 49 loads ahead of it
+// (issued together, waited for once).  The values are uniform.
+__device__ __forceinline__ void pin49(uint32_t* o, uint32_t* c, uint32_t* d) {
+#pragma unroll
+  for (int i = 0; i < 17; ++i) o[i] = __builtin_amdgcn_readfirstlane(o[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    c[i] = __builtin_amdgcn_readfirstlane(c[i]);
+    d[i] = __builtin_amdgcn_readfirstlane(d[i]);
+  }
+  asm(""
+      : "+s"(o[0]), "+s"(o[1]), "+s"(o[2]), "+s"(o[3]), "+s"(o[4]), "+s"(o[5]), "+s"(o[6]),
+        "+s"(o[7]), "+s"(o[8]), "+s"(o[9]), "+s"(o[10]), "+s"(o[11]), "+s"(o[12]), "+s"(o[13]),
+        "+s"(o[14]), "+s"(o[15]), "+s"(o[16]), "+s"(c[0]), "+s"(c[1]), "+s"(c[2]), "+s"(c[3]),
+        "+s"(c[4]), "+s"(c[5]), "+s"(c[6]), "+s"(c[7]), "+s"(c[8]), "+s"(c[9]), "+s"(c[10]),
+        "+s"(c[11]), "+s"(c[12]), "+s"(c[13]), "+s"(c[14]), "+s"(c[15]), "+s"(d[0]), "+s"(d[1]),
+        "+s"(d[2]), "+s"(d[3]), "+s"(d[4]), "+s"(d[5]), "+s"(d[6]), "+s"(d[7]), "+s"(d[8]),
+        "+s"(d[9]), "+s"(d[10]), "+s"(d[11]), "+s"(d[12]), "+s"(d[13]), "+s"(d[14]),
+        "+s"(d[15]));
+}
+
 __device__ __forceinline__ uint32_t seg_of(const BandArgs& a, uint32_t kp) {
   uint32_t s = 0;
 #pragma unroll
@@ -439,6 +462,11 @@ __device__ __forceinline__ void table_entries(const void* base, int64_t idx, flo
   }
 }
 
+// The loads are unconditional: a chunk that does not rotate reads the
+// table's first entries instead (every table has at least rope_dim >= 2E
+// columns and one row), and its values go unused.  A load under a lane
+// condition would be compiled into a branch that waits for every load in
+// flight before the next one issues.
 template <int FDT, typename T, bool IL>
 __device__ __forceinline__ void load_freqs_t(const void* __restrict__ freqs, int64_t row,
                                              uint32_t c0, uint32_t c1, uint32_t j, bool rot0,
@@ -446,25 +474,23 @@ __device__ __forceinline__ void load_freqs_t(const void* __restrict__ freqs, int
   constexpr int E = Fmt<T>::E;
   if constexpr (IL) {
     // chunk c holds pairs c*E/2 .. c*E/2 + E/2 - 1: table columns c*E .. c*E + E - 1
-    if (rot0) table_entries<FDT, E>(freqs, row + c0 * E, fl);
-    if (rot1) table_entries<FDT, E>(freqs, row + c1 * E, fl + E);
+    table_entries<FDT, E>(freqs, rot0 ? row + c0 * E : 0, fl);
+    table_entries<FDT, E>(freqs, rot1 ? row + c1 * E : 0, fl + E);
   } else {
     // a half-split lane j < rope_dim/(2E) rotates frequencies j*E .. j*E + E - 1
-    if (rot0) table_entries<FDT, 2 * E>(freqs, row + 2 * j * E, fl);
+    table_entries<FDT, 2 * E>(freqs, rot0 ? row + 2 * j * E : 0, fl);
   }
 }
 
 // This lane's (cos, sin) entries of freqs row `pos`: the 2E table values of
-// the frequencies its chunks rotate (zero where a chunk is not rotated).
+// the frequencies its chunks rotate (table values of no meaning where a
+// chunk is not rotated: the rotation selects the unrotated value there).
 // c0 / c1 are the chunks' places within the rotated dims.
 // The table's entry type is uniform over the launch.
 template <typename T, bool IL>
 __device__ __forceinline__ void load_freqs(const BandArgs& a, uint32_t pos, uint32_t c0,
                                            uint32_t c1, uint32_t j, bool rot0, bool rot1,
                                            float* fl) {
-  constexpr int E = Fmt<T>::E;
-#pragma unroll
-  for (int e = 0; e < 2 * E; ++e) fl[e] = 0.f;
   const int64_t row = (int64_t)pos * a.rope_dim;
   if (a.freq_dtype == DT_F32)
     load_freqs_t<DT_F32, T, IL>(a.freqs, row, c0, c1, j, rot0, rot1, fl);
@@ -671,20 +697,30 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   } else if (a.batch < kSmallBatch) {
     // Small batch: every offset and every sequence's cache length in one
     // round of independent scalar loads (indices clamped in range), then a
-    // scan -- one load latency before the page-table lookup.
-    const uint32_t B = a.batch;
+    // scan -- one load latency before the page-table lookup.  Every load is
+    // unconditional: a load guarded by the cache count would be compiled
+    // into a branch of its own that waits for the loads before it (16
+    // dependent rounds).  With one cache the second pointer names the first
+    // cache's array (valid loads, values unused).  The batch size and
+    // offset, and then the loaded values, pass through empty asm statements:
+    // the compiler must hold them in SGPRs there, so those fields are read
+    // (scalar-cache hits) before the first metadata load, and every metadata
+    // load is issued before the first wait on one.
+    uint32_t B = a.batch, boff = a.batch_offset;
+    const uint32_t* offp = a.offsets;
+    const uint32_t* clp0 = a.cache[0].cache_lengths;
+    const uint32_t* clp1 = a.ncache > 1 ? a.cache[1].cache_lengths : clp0;
+    asm("" : "+s"(B), "+s"(boff));
     uint32_t o[kSmallBatch + 1];
     uint32_t cl[kMaxCaches][kSmallBatch];
 #pragma unroll
-    for (uint32_t i = 0; i <= kSmallBatch; ++i) o[i] = a.offsets[i < B ? i : B];
+    for (uint32_t i = 0; i <= kSmallBatch; ++i) o[i] = offp[i < B ? i : B];
 #pragma unroll
-    for (int ci = 0; ci < kMaxCaches; ++ci) {
-#pragma unroll
-      for (uint32_t i = 0; i < kSmallBatch; ++i)
-        cl[ci][i] = (uint32_t)ci < a.ncache
-                        ? a.cache[ci].cache_lengths[(i < B ? i : B - 1) + a.batch_offset]
-                        : 0u;
+    for (uint32_t i = 0; i < kSmallBatch; ++i) {
+      cl[0][i] = clp0[(i < B ? i : B - 1) + boff];
+      cl[1][i] = clp1[(i < B ? i : B - 1) + boff];
     }
+    pin49(o, cl[0], cl[1]);
     b = 0;
 #pragma unroll
     for (uint32_t i = 1; i < kSmallBatch; ++i)
@@ -725,6 +761,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   uint32_t pos[kMaxCaches] = {0, 0};
   int64_t base[kMaxCaches] = {0, 0};
   int64_t sbase[kMaxCaches] = {0, 0};  // FP8: the row's scale index before plane and head
+  uint64_t pidx_c[kMaxCaches] = {0, 0}, slot_c[kMaxCaches] = {0, 0};
 #pragma unroll
   for (int ci = 0; ci < kMaxCaches; ++ci) {
     if ((uint32_t)ci < a.ncache) {
@@ -732,12 +769,33 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       const uint64_t p64 = (uint64_t)clen[ci] + local;
       const uint64_t pidx = cd.page_shift != 0xFFFFFFFFu ? (p64 >> cd.page_shift)
                                                          : p64 / cd.page_size;
-      const uint64_t slot = p64 - pidx * cd.page_size;
+      slot_c[ci] = p64 - pidx * cd.page_size;
+      pidx_c[ci] = pidx;
       ok = ok && (pass || ((a.max_seq_len == 0 || p64 < a.max_seq_len) && pidx < cd.max_pages));
+      pos[ci] = (uint32_t)p64;
+    }
+  }
+  // One-pass waves (decode-sized launches, the padded grid) load the freqs
+  // row as soon as the position is known: its address needs no page-table
+  // entry, so the two lookups overlap (measured on decode: 3.17 -> 3.09 us
+  // per launch; with more passes per wave the loads' registers cost more
+  // than the overlap gains).
+  constexpr bool EARLY_FREQS = NPMAX == 1 && !RADD;
+  float fl[RADD ? 1 : 2 * E];
+  uint32_t fl_pos = pos[0];
+  if constexpr (EARLY_FREQS) {
+    const bool fok = ok && !pass;
+    load_freqs<T, IL>(a, fl_pos, c0 - oc, c1 - oc, j, rot0 && fok, rot1 && fok, fl);
+  }
+#pragma unroll
+  for (int ci = 0; ci < kMaxCaches; ++ci) {
+    if ((uint32_t)ci < a.ncache) {
+      const CacheDesc& cd = a.cache[ci];
+      const uint64_t pidx = pidx_c[ci];
+      const uint64_t slot = slot_c[ci];
       uint64_t page = 0;
       if (ok && !pass) page = cd.table[(uint64_t)cseq * cd.max_pages + pidx];
       ok = ok && (pass || page < cd.num_pages);
-      pos[ci] = (uint32_t)p64;
       base[ci] = (int64_t)page * cd.page_stride + cd.layer_off + (int64_t)slot * cd.slot_stride;
       if constexpr (QUANT)
         sbase[ci] = (int64_t)page * a.scale[ci].s_page_stride + a.scale[ci].s_layer_off +
@@ -794,9 +852,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   }
 
   // ---- D: this lane's (cos, sin) entries of the token's freqs row ----
-  float fl[RADD ? 1 : 2 * E];
-  uint32_t fl_pos = pos[0];
-  if constexpr (!RADD) load_freqs<T, IL>(a, fl_pos, c0 - oc, c1 - oc, j, rot0, rot1, fl);
+  if constexpr (!RADD && !EARLY_FREQS) load_freqs<T, IL>(a, fl_pos, c0 - oc, c1 - oc, j, rot0, rot1, fl);
 
 
   // ---- E: arithmetic and stores ----

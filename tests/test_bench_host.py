@@ -57,3 +57,31 @@ def test_gemv_bytes_by_hand_and_its_own_source_hash():
     four = bench.make_case("gemv_norm_rows4")
     assert bench.algorithmic_bytes(four) == w + 4 * x + gamma + 4 * out
     assert bench.case_tokens(four) == 4
+
+
+def test_percentiles_nearest_rank():
+    p = bench.percentiles(list(range(1, 101)))
+    assert p == {10: 11, 50: 51, 90: 91}
+    assert bench.percentiles([5.0]) == {10: 5.0, 50: 5.0, 90: 5.0}
+
+
+def test_counter_summary_gives_traffic_and_tcc_hit_rate(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    src = tmp_path / "qk_rope_paged_amd" / "csrc"
+    src.mkdir(parents=True)
+    for rel in bench.KERNEL_SOURCES:
+        (tmp_path / rel).write_text("int k;\n")
+    h = bench.kernel_source_hash()
+    (tmp_path / "profiles" / "band_kernel_decode_traffic.txt").write_text(
+        "# header\n"
+        f"kernel_source_sha256: {h}\n"
+        "seed_3_bytes: 100 50   # read, written\n"
+        "seed_103_bytes: 300 150   # read, written\n"
+        "tcc_hit_rate: 0.4500   # TCC_HIT / (TCC_HIT + TCC_MISS)\n")
+    assert bench.traffic_from_profiles("decode", [3, 103, 3, 103]) == 300
+    assert bench.tcc_hit_rate_from_profiles("decode") == 0.45
+    # a summary of other kernel code is not used
+    (tmp_path / bench.KERNEL_SOURCES[0]).write_text("int k2;\n")
+    assert bench.traffic_from_profiles("decode", [3]) is None
+    assert bench.tcc_hit_rate_from_profiles("decode") is None
