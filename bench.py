@@ -55,7 +55,8 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 KERNEL_NAME = "band_kernel"
 KERNEL_SOURCES = ("qk_rope_paged_amd/csrc/band_kernel.hpp", "qk_rope_paged_amd/csrc/kernels.hip",
                   "qk_rope_paged_amd/csrc/kernels_fp8.hip", "qk_rope_paged_amd/csrc/kernels_qout.hip",
-                  "qk_rope_paged_amd/csrc/kernels_pack.hip", "qk_rope_paged_amd/csrc/engine.hpp",
+                  "qk_rope_paged_amd/csrc/kernels_pack.hip", "qk_rope_paged_amd/csrc/kernels_mixed.hip",
+                  "qk_rope_paged_amd/csrc/engine.hpp",
                   "qk_rope_paged_amd/csrc/abi.cpp")
 # the fused GEMV + partial RMSNorm (MatmulFusedPartialRMSNorm page): its own
 # kernel, sources and workloads

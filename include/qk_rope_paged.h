@@ -231,10 +231,11 @@ int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq
  * same buffer, offsets and freqs table; each row takes its own band's cache,
  * gamma, epsilon, output and Q columns.  The two caches must have the same
  * head_dim (QRP_EGEOMETRY otherwise: the page requires identical RoPE
- * geometry across the bands); their dtypes are independent parameters on
- * the page, but this library builds only both-plain or both-FP8 pairs
- * (QRP_EUNSUPPORTED otherwise).  The result equals main_band's
- * qk_rmsnorm_rope_paged call followed by index_band's.
+ * geometry across the bands).  Their element types are independent
+ * parameters on the page (Signature: main_cache_dtype, index_cache_dtype):
+ * each cache may hold the op's dtype or FP8 codes, in any pairing.  The
+ * result equals main_band's qk_rmsnorm_rope_paged call followed by
+ * index_band's.
  */
 int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64_t buf_row_stride,
                   const qrp_band* main_band, const qrp_band* index_band, float weight_offset,

@@ -172,6 +172,9 @@ qrp::CacheDesc make_cache(const qrp_paged_cache* c, uint32_t layer_idx) {
   return d;
 }
 
+// Bit i of the launch's fp8_caches: cache i holds FP8 codes.
+uint32_t fp8_bit(const qrp_paged_cache* c, uint32_t i) { return c->dtype == QRP_FP8 ? 1u << i : 0u; }
+
 qrp::ScaleDesc make_scales(const qrp_paged_cache* c, uint32_t layer_idx) {
   qrp::ScaleDesc d{};
   if (c->dtype == QRP_FP8) {
@@ -218,8 +221,9 @@ struct Builder {
   // the padded grid, whose waves resolve their row with one division).
   // allow_pack: the op has a token-packed build.
   int32_t finish(uint32_t total_tokens, bool radd, bool one_pass = false,
-                 bool allow_pack = false) {
-    bool norm = false;
+                 bool allow_pack = false, bool norm_build = false) {
+    // norm_build: the launch runs the norm kernels whatever its gammas
+    bool norm = norm_build;
     for (uint32_t s = 0; s < a.nseg; ++s) norm = norm || a.seg[s].gamma != nullptr;
     const uint32_t npmax = qrp::max_passes(radd, norm);
     // Per-token passes leave lanes idle when a segment's head count is not a
@@ -275,9 +279,13 @@ struct Builder {
     const uint64_t items = (uint64_t)units * a.groups_per_token;
     if (items >= (1ull << 31)) return fail(QRP_EINVAL, "batch too large for one launch");
     a.n_items = (uint32_t)items;
-    // Large rope/store launches run one wave per block (measured faster);
-    // norm, radd and small launches group four waves per block.
-    uint32_t wpb = (!radd && !norm && items >= 8192) ? 1u : (uint32_t)qrp::kMaxWavesPerBlock;
+    // Rope/store launches of one pass per wave (decode-sized batches, the
+    // padded grid) run two waves per block, large multi-pass ones one wave
+    // per block, norm, radd and the other small launches four (measured:
+    // decode 3.09 -> 3.01 us per launch with two instead of four, the padded
+    // grid 49.11 -> 48.98 with two instead of one).
+    uint32_t wpb = (uint32_t)qrp::kMaxWavesPerBlock;
+    if (!radd && !norm) wpb = ppg == 1 ? 2u : (items >= 8192 ? 1u : wpb);
     const int32_t forced_wpb = knob(QRP_KNOB_WAVES_PER_BLOCK);
     if (forced_wpb > 0) wpb = std::min<uint32_t>((uint32_t)forced_wpb, qrp::kMaxWavesPerBlock);
     a.waves_per_block = wpb;
@@ -294,7 +302,9 @@ int32_t launch(const Builder& b, bool interleaved, bool radd, void* stream, bool
   qrp::LaunchSpec s{};
   s.dtype = b.dtype;
   s.q_dtype = q_dtype < 0 ? b.dtype : q_dtype;
-  s.cache_fp8 = b.a.scale[0].scales != nullptr;
+  // one plain and one FP8 cache: the mixed build; otherwise every cache alike
+  s.cache_mixed = b.a.ncache == 2 && (b.a.fp8_caches == 1u || b.a.fp8_caches == 2u);
+  s.cache_fp8 = b.a.fp8_caches != 0 && !s.cache_mixed;
   s.head_dim = b.head_dim;
   s.interleaved = interleaved;
   s.radd = radd;
@@ -417,6 +427,7 @@ int32_t rope_split_store_paged(const void* qkv, int32_t dtype, uint32_t total_se
   b.rpp = qrp::rows_per_pass(dtype, cache->head_dim);
   b.a.cache[0] = make_cache(cache, layer_idx);
   b.a.scale[0] = make_scales(cache, layer_idx);
+  b.a.fp8_caches = fp8_bit(cache, 0);
   b.a.ncache = 1;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
@@ -460,6 +471,7 @@ int32_t qk_rmsnorm_rope_paged(const void* qkv, int32_t dtype, uint32_t total_seq
   b.rpp = qrp::rows_per_pass(dtype, b.head_dim);
   b.a.cache[0] = make_cache(band->cache, layer_idx);
   b.a.scale[0] = make_scales(band->cache, layer_idx);
+  b.a.fp8_caches = fp8_bit(band->cache, 0);
   b.a.ncache = 1;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
@@ -485,8 +497,6 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
     return fail(QRP_EINVAL, "bands and their caches must be non-NULL");
   if (main_band->cache->head_dim != index_band->cache->head_dim)
     return fail(QRP_EGEOMETRY, "main and index bands differ in head_dim");
-  if ((main_band->cache->dtype == QRP_FP8) != (index_band->cache->dtype == QRP_FP8))
-    return fail(QRP_EUNSUPPORTED, "dual_band: both caches FP8 or neither (mixed not built)");
   if (total_seq_len == 0) return QRP_OK;
   int32_t st;
   if ((st = check_batch(input_row_offsets, total_seq_len, batch_size))) return st;
@@ -509,6 +519,7 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
   b.a.scale[0] = make_scales(main_band->cache, layer_idx);
   b.a.cache[1] = make_cache(index_band->cache, layer_idx);
   b.a.scale[1] = make_scales(index_band->cache, layer_idx);
+  b.a.fp8_caches = fp8_bit(main_band->cache, 0) | fp8_bit(index_band->cache, 1);
   b.a.ncache = 2;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
@@ -522,7 +533,9 @@ int32_t dual_band(const void* buf, int32_t dtype, uint32_t total_seq_len, uint64
   // rows [q_main | k_main | q_index | k_index]
   add_band(b, main_band, buf, buf_row_stride, dtype, 0);
   add_band(b, index_band, buf, buf_row_stride, dtype, 1);
-  if ((st = b.finish(total_seq_len, false, false, true))) return st;
+  // a plain cache beside an FP8 one: the mixed build, per-token layout only
+  const bool mixed = (main_band->cache->dtype == QRP_FP8) != (index_band->cache->dtype == QRP_FP8);
+  if ((st = b.finish(total_seq_len, false, false, !mixed, mixed))) return st;
   return launch(b, rope->interleaved != 0, false, stream);
 }
 
@@ -550,6 +563,7 @@ int32_t kv_cache_radd(const void* a, int32_t dtype, uint32_t total_rows, uint64_
   b.rpp = qrp::rows_per_pass(dtype, b.head_dim);
   b.a.cache[0] = make_cache(cache, layer_idx);
   b.a.scale[0] = make_scales(cache, layer_idx);
+  b.a.fp8_caches = fp8_bit(cache, 0);
   b.a.ncache = 1;
   b.a.offsets = input_row_offsets;
   b.a.batch = batch_size;
@@ -591,6 +605,7 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
   b.rpp = qrp::rows_per_pass(dtype, cache->head_dim);
   b.a.cache[0] = make_cache(cache, layer_idx);
   b.a.scale[0] = make_scales(cache, layer_idx);
+  b.a.fp8_caches = fp8_bit(cache, 0);
   b.a.ncache = 1;
   b.a.offsets = nullptr;
   b.a.batch = batch_size;

@@ -77,6 +77,9 @@ struct F16 {
 struct Fp8 {
   uint8_t bits;
 };
+// Cache type of a launch whose two caches differ: one holds the op's dtype,
+// the other FP8 codes (BandArgs::fp8_caches says which).
+struct MixFp8 {};
 
 // elements per 16-byte chunk
 template <typename T>
@@ -549,8 +552,18 @@ __device__ __forceinline__ uint32_t touch_args(uint64_t (&p)[4]) {
 template <typename T, typename QT, typename CT, int D, bool IL, int NPMAX, bool RADD, bool NORM,
           bool BSHD, bool PACK = false>
 __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
+  // QUANT: every cache holds FP8 codes; MIX: the caches differ (a per-cache
+  // run-time bit); QANY: FP8 rows may occur.
   constexpr bool QUANT = std::is_same_v<CT, Fp8>;
-  static_assert(QUANT || std::is_same_v<CT, T>, "a cache holds the op dtype or FP8");
+  constexpr bool MIX = std::is_same_v<CT, MixFp8>;
+  constexpr bool QANY = QUANT || MIX;
+  static_assert(QANY || std::is_same_v<CT, T>, "a cache holds the op dtype or FP8");
+  static_assert(!MIX || (NORM && !RADD && !BSHD && !PACK), "mixed caches: the norm ops' build");
+  // does cache ci hold FP8 codes
+  auto fp8_cache = [&](uint32_t ci) -> bool {
+    if constexpr (MIX) return (a.fp8_caches >> ci) & 1u;
+    return QUANT;
+  };
   constexpr int E = Fmt<T>::E;
   constexpr int CH = D / E;      // 16-byte chunks per head row
   constexpr int LPR = CH / 2;    // lanes per head row
@@ -559,7 +572,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
 
   static_assert(offsetof(BandArgs, n_items) == 0, "the fetch returns n_items");
   constexpr uint32_t ARG_BYTES =
-      QUANT ? (uint32_t)sizeof(BandArgs) : (uint32_t)offsetof(BandArgs, scale);
+      QANY ? (uint32_t)sizeof(BandArgs) : (uint32_t)offsetof(BandArgs, scale);
   // norm kernels: every segment's gamma pointer (null for unused segments,
   // whose descriptors are zero), fetched with the argument lines
   uint64_t gpv[kMaxSegs] = {0, 0, 0, 0};
@@ -797,7 +810,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       if (ok && !pass) page = cd.table[(uint64_t)cseq * cd.max_pages + pidx];
       ok = ok && (pass || page < cd.num_pages);
       base[ci] = (int64_t)page * cd.page_stride + cd.layer_off + (int64_t)slot * cd.slot_stride;
-      if constexpr (QUANT)
+      if constexpr (QANY)
         sbase[ci] = (int64_t)page * a.scale[ci].s_page_stride + a.scale[ci].s_layer_off +
                     (int64_t)slot * a.scale[ci].s_slot_stride;
     }
@@ -813,11 +826,11 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   if (pass || !ok) rot0 = rot1 = false;
 
   // ---- C: loads from the cache (in-place K, radd accumulator) ----
-  float rsc[QUANT ? NPMAX : 1];  // FP8: scale of the row read
+  float rsc[QANY ? NPMAX : 1];  // FP8: scale of the row read
 #pragma unroll
   for (int p = 0; p < NPMAX; ++p) {
     if constexpr (RADD) y[p][0] = y[p][1] = make_uint4(0, 0, 0, 0);
-    if constexpr (QUANT) rsc[p] = 0.f;
+    if constexpr (QANY) rsc[p] = 0.f;
     if ((uint32_t)p < np) {
       const uint32_t kp = p0 + p;
       const SegDesc& sd = a.seg[seg_of(a, kp)];
@@ -828,13 +841,14 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
         const int64_t roff =
             base[sd.cache] + (int64_t)sd.plane * cd.plane_stride + (int64_t)h * cd.head_stride;
         uint4 r0, r1;
-        if constexpr (QUANT) {
+        if (QANY && fp8_cache(sd.cache)) {
           const uint8_t* src = reinterpret_cast<const uint8_t*>(cd.blocks) + roff;
           r0 = ld_fp8_chunk<E>(src + c0 * E);
           r1 = ld_fp8_chunk<E>(src + c1 * E);
           const ScaleDesc& sdsc = a.scale[sd.cache];
-          rsc[p] = load_scale(sdsc, sbase[sd.cache] + (int64_t)sd.plane * sdsc.s_plane_stride +
-                                        (int64_t)h * sdsc.s_head_stride);
+          if constexpr (QANY)
+            rsc[p] = load_scale(sdsc, sbase[sd.cache] + (int64_t)sd.plane * sdsc.s_plane_stride +
+                                          (int64_t)h * sdsc.s_head_stride);
         } else {
           const T* src = reinterpret_cast<const T*>(cd.blocks) + roff;
           r0 = ld16s(src + c0 * E);
@@ -919,7 +933,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
         }
       } else {
         if (kind == SEG_V_COPY) {
-          if constexpr (QUANT) {
+          if (QANY && fp8_cache(sd.cache)) {
             // V bits cannot move into an FP8 row as they are: quantize them
             const CacheDesc& cd = a.cache[sd.cache];
             float v0[E], v1[E];
@@ -940,9 +954,10 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
           }
         } else {
           float v0[E], v1[E];
-          if (QUANT && kind == SEG_K_INPLACE) {
-            fp8_values<E>(x[p][0], rsc[QUANT ? p : 0], v0);
-            fp8_values<E>(x[p][1], rsc[QUANT ? p : 0], v1);
+          const bool fp8_row = QANY && kind != SEG_Q && fp8_cache(sd.cache);
+          if (fp8_row && kind == SEG_K_INPLACE) {
+            fp8_values<E>(x[p][0], rsc[QANY ? p : 0], v0);
+            fp8_values<E>(x[p][1], rsc[QANY ? p : 0], v1);
           } else {
             unpack<T>(x[p][0], v0);
             unpack<T>(x[p][1], v1);
@@ -1018,8 +1033,8 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
               continue;
             }
           }
-          if constexpr (QUANT) {
-            if (kind != SEG_Q) {
+          if constexpr (QANY) {
+            if (fp8_row) {
               const CacheDesc& cd = a.cache[sd.cache];
               quantize_store<LPR, E>(
                   v0, v1,

@@ -125,6 +125,7 @@ struct BandArgs {
   uint32_t multiply_before_cast;
   uint64_t guess_mul;       // floor(batch * 2^32 / total_tokens): token -> first sequence guess
   uint32_t freq_dtype;      // DT_F32, DT_BF16 or DT_F16 table entries
+  uint32_t fp8_caches;      // bit i: cache i holds FP8 codes (the mixed-cache build reads it)
   // Padded [batch][seq_len] token grid (continuous batching): token t is
   // row t % seq_len of sequence t / seq_len; rows at or past the sequence's
   // valid length pass through.  Unused by the ragged ops.
@@ -141,6 +142,7 @@ struct LaunchSpec {
   int32_t dtype;            // input (and plain cache) dtype
   int32_t q_dtype;          // Q output dtype
   bool cache_fp8;           // caches hold FP8 codes with row scales
+  bool cache_mixed;         // two caches, one plain and one FP8 (BandArgs::fp8_caches)
   uint32_t head_dim;
   bool interleaved;
   bool radd;
@@ -160,6 +162,7 @@ int launch_plain(const BandArgs& a, const LaunchSpec& s, void* stream);
 int launch_fp8(const BandArgs& a, const LaunchSpec& s, void* stream);
 int launch_qout(const BandArgs& a, const LaunchSpec& s, void* stream);
 int launch_pack(const BandArgs& a, const LaunchSpec& s, void* stream);
+int launch_mixed(const BandArgs& a, const LaunchSpec& s, void* stream);
 
 // Rows handled per 64-lane pass for a dtype / head_dim.
 inline uint32_t rows_per_pass(int32_t dtype, uint32_t head_dim) {

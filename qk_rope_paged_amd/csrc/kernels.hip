@@ -1,6 +1,6 @@
 // kernels.hip -- the band engine's launches for caches of the op's own
-// dtype, and the dispatch to the FP8-cache, Q-dtype and token-packed
-// translation units.
+// dtype, and the dispatch to the FP8-cache, Q-dtype, token-packed and
+// mixed-cache translation units.
 #include "band_kernel.hpp"
 
 namespace qrp {
@@ -12,6 +12,7 @@ int launch_plain(const BandArgs& a, const LaunchSpec& s, void* stream) {
 }
 
 int launch_band(const BandArgs& a, const LaunchSpec& s, void* stream) {
+  if (s.cache_mixed) return launch_mixed(a, s, stream);
   if (s.q_dtype != s.dtype) return launch_qout(a, s, stream);
   if (s.pack) return launch_pack(a, s, stream);
   if (s.cache_fp8) return launch_fp8(a, s, stream);

@@ -346,11 +346,19 @@ def test_fp8_cache_and_q_dtype_argument_errors(kw, code):
     assert qrp.last_error() != ""
 
 
-def test_dual_band_mixed_fp8_and_plain_caches_is_unsupported():
+def test_dual_band_mixed_fp8_and_plain_caches_pass_the_host_checks():
+    # one plain and one FP8 cache is a supported pairing: every host check
+    # passes and the call gets as far as the launch (QRP_EHIP without a GPU)
     idx_cache = _fp8_cache(num_kv_heads=1, kv_planes=1, page_stride=128 * 128,
                            plane_stride=128 * 128, layer_stride=128 * 128, slot_stride=128)
-    assert _dual(index=_band(cache=idx_cache, q_col=80 * 128, n_q_heads=16,
-                             q_out_row_stride=16 * 128)) == qrp.QRP_EUNSUPPORTED
+    st = _dual(index=_band(cache=idx_cache, q_col=80 * 128, n_q_heads=16,
+                           q_out_row_stride=16 * 128))
+    assert st in (qrp.QRP_OK, qrp.QRP_EHIP), qrp.last_error()
+    # the FP8 side is still checked like any FP8 cache
+    bad = _fp8_cache(num_kv_heads=1, kv_planes=1, page_stride=128 * 128, plane_stride=128 * 128,
+                     layer_stride=128 * 128, slot_stride=128, scales=None)
+    assert _dual(index=_band(cache=bad, q_col=80 * 128, n_q_heads=16,
+                             q_out_row_stride=16 * 128)) == qrp.QRP_EINVAL
 
 
 def _gemv(**kw):

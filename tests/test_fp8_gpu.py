@@ -10,7 +10,8 @@ match bit for bit.  Cases: every op (store, single-band norm with K from the
 buffer and in place, dual band, radd, padded grid), every input dtype, both
 layouts, f32 and bf16 scales, head_dim 64 / 128 / 256, the workloads at
 reduced and full size, every Q output dtype pair over plain and FP8 caches,
-and bit-identical results across launch configurations (XCD remap on and off).
+the dual band with one plain and one FP8 cache (either way round), and
+bit-identical results across launch configurations (XCD remap on and off).
 """
 from __future__ import annotations
 
@@ -122,6 +123,60 @@ def test_q_output_dtype(dtype, q_out, cache):
         R = 32 if il else 64
         run_and_compare(_store(f"qout_{dtype}_{q_out}_{cache}_{il}", 66, dtype, R=R, il=il,
                                cache=cache, q_out=q_out))
+
+
+def _mixed_dual(main, index, small=True, seed=4):
+    """The dual-band workload's shapes (64 Q-main, 8 KV, 16 Q-index heads,
+    head_dim 128, partial rope 64) with the two caches of different types."""
+    B = 4 if small else 16
+    from synth import prng
+    lens = prng.integers(seed, sc.S_LENS, B, 1, 150 if small else 1024)
+    return sc.make_dual_case(f"dual_mixed_{main}_{index}_{'small' if small else 'full'}", seed,
+                             sc.BF16, lens, Hq_main=64, Hk_main=8, Hq_index=16, D=128,
+                             rope_dim=64, interleaved=True, theta=1e4, max_seq_len=8192,
+                             P_main=64, P_index=64, main_cache_dtype=main,
+                             index_cache_dtype=index)
+
+
+@pytest.mark.parametrize("small", [True, False])
+@pytest.mark.parametrize("main,index", [(sc.BF16, sc.FP8), (sc.FP8, sc.BF16)])
+def test_fp8_dual_band_mixed_cache_dtypes(main, index, small):
+    # fused_dual_qk_rms_norm_rope_ragged_paged page, Signature: the two
+    # caches' element types are separate parameters
+    run_and_compare(_mixed_dual(main, index, small))
+
+
+@pytest.mark.parametrize("main,index", [(sc.F16, sc.FP8), (sc.FP8, sc.F16)])
+def test_fp8_dual_band_mixed_half_split_bf16_scales_own_lengths(main, index):
+    case = sc.make_dual_case("fp8_dual_mixed_hs", 64, sc.F16, [5, 0, 40, 9, 17], Hq_main=16,
+                             Hk_main=4, Hq_index=4, D=128, rope_dim=64, interleaved=False,
+                             theta=1e4, max_seq_len=1024, P_main=32, P_index=16, eps_main=1e-6,
+                             eps_index=1e-3, weight_offset=0.25, multiply_before_cast=False,
+                             cache_lengths=[3, 0, 100, 7, 500],
+                             index_cache_lengths=[0, 9, 33, 200, 1], main_cache_dtype=main,
+                             index_cache_dtype=index, scale_dtype=sc.BF16)
+    run_and_compare(case)
+
+
+def test_fp8_dual_band_mixed_launch_configuration_does_not_change_bits():
+    gh, _ = _gpu()
+    case = _mixed_dual(sc.BF16, sc.FP8)
+    ref = None
+    for remap, ppw, wpb in [(r, p, w) for r in ("0", "1") for p in ("0", "1", "2", "3")
+                            for w in ("0", "1", "4")]:
+        dc = gh.upload(case)
+        with gh.knobs(remap, ppw, wpb, pack=1):      # packing is not used for mixed pairs
+            gh.run(dc)
+        torch.cuda.synchronize()
+        snap = [gh.to_numpy_bits(q, case.q_dtype) for q in dc.q_out]
+        snap += [gh.to_numpy_bits(c.pool, c.host.dtype) for c in dc.caches]
+        snap += [gh.to_numpy_bits(c.scales, c.host.scale_dtype) for c in dc.caches
+                 if c.scales is not None]
+        if ref is None:
+            ref = snap
+        else:
+            for i, (x, y) in enumerate(zip(ref, snap)):
+                assert np.array_equal(x, y), f"mixed dual remap={remap} ppw={ppw} wpb={wpb}: buffer {i}"
 
 
 @pytest.mark.parametrize("workload", ["prefill_fp8", "radd_fp8", "dual_fp8"])

@@ -3,7 +3,8 @@
 The other GPU tests vary one or two options around a workload; this one
 draws, per case, the op and every option it takes at once: input dtype,
 head_dim, rope width and placement (leading or trailing dims), layout,
-freqs-table dtype, cache dtype (plain or FP8 with f32 / bf16 scales), Q
+freqs-table dtype, cache dtype (plain or FP8 with f32 / bf16 scales, the
+dual band's two caches sometimes one of each), Q
 output dtype, page size (1, powers of two and others), head counts, batch
 size on both sides of the small-batch threshold and up to 512 sequences,
 ragged and empty sequences,
@@ -97,6 +98,9 @@ def random_case(op: str, k: int):
         if rng.random() < 0.5:                   # the index cache's own lengths
             top = 64 if len(lens) > 20 else MSL - int(lens.max())   # many sequences: small pools
             kw["index_cache_lengths"] = rng.integers(0, top, len(lens))
+        idt = cdt
+        if rng.random() < 0.3:                   # one plain and one FP8 cache
+            idt = None if fp8 else sc.FP8
         return sc.make_dual_case(name, seed, dtype, lens, Hq_main=int(rng.integers(1, 9)),
                                  Hk_main=int(rng.integers(1, 4)), Hq_index=int(rng.integers(1, 5)),
                                  D=D, rope_dim=R, interleaved=il, theta=1e4, max_seq_len=MSL,
@@ -104,7 +108,7 @@ def random_case(op: str, k: int):
                                  eps_main=1e-6, eps_index=_pick(rng, (1e-6, 1e-3)),
                                  weight_offset=_pick(rng, (0.0, 0.5)),
                                  multiply_before_cast=bool(rng.integers(2)), cache_lengths=clen,
-                                 freq_dtype=fdt, main_cache_dtype=cdt, index_cache_dtype=cdt,
+                                 freq_dtype=fdt, main_cache_dtype=cdt, index_cache_dtype=idt,
                                  scale_dtype=sdt, rope_tail=tail, **kw)
     if op == "radd":
         lens, clen_b = _batch(rng)
