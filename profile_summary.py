@@ -61,13 +61,19 @@ def trace(args) -> str:
     band = [(k, v) for k, v in by.items() if kern in k]
     if args.warmup is not None and args.steps:
         # every band-kernel launch in launch order: batches whose waves hold
-        # one pass run the one-pass build, so one run can use two builds
+        # one pass run the one-pass build, so one run can use two builds.
+        # With --graph the bench replays its K timed launches from a HIP
+        # graph: after the W warm-up launches come 3 eager launches, two
+        # untimed replays (2K launches), then the K timed ones.
         seq = [dur for name, dur, *_ in rows if kern in name]
-        timed = [d / 1e3 for d in seq[args.warmup:args.warmup + args.steps]]
+        first = args.warmup + (3 + 2 * args.steps if args.graph else 0)
+        timed = [d / 1e3 for d in seq[first:first + args.steps]]
         names = ", ".join(f"`{k[:60]}...`" for k, _ in band)
-        out += ["", f"Timed region of the bench ({kern} launches {args.warmup} to "
-                    f"{args.warmup + len(timed) - 1}, of {names}): "
-                    f"average {statistics.mean(timed):.2f} us over {len(timed)} launches."]
+        out += ["", f"Timed region of the bench ({kern} launches {first} to "
+                    f"{first + len(timed) - 1}, of {names}"
+                    f"{', replayed from a HIP graph' if args.graph else ''}): "
+                    f"average {statistics.mean(timed):.2f} us, median "
+                    f"{statistics.median(timed):.2f} us over {len(timed)} launches."]
     for name, v in band:
         out += ["", f"`{name}`: LDS {v[0][5]} bytes, {v[0][2]} threads per block.", "",
                 "| grid threads (one batch) | launches | avg us | min us |", "|---|---|---|---|"]
@@ -181,6 +187,7 @@ def main() -> int:
     t.add_argument("--warmup", type=int, default=None, help="warm-up launches before the timed region")
     t.add_argument("--steps", type=int, default=0, help="launches in the timed region")
     t.add_argument("--kernel", default=BAND, help="name (or part) of the kernel timed")
+    t.add_argument("--graph", action="store_true", help="the bench ran with --graph")
     p = sub.add_parser("traffic")
     p.add_argument("--fetch", required=True)
     p.add_argument("--write", required=True)

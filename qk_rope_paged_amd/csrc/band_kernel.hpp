@@ -354,6 +354,36 @@ __device__ __forceinline__ void quantize_store(float* v0, float* v1, Fp8* row, u
   }
 }
 
+// Rotate a lane's two chunks by its (cos, sin) entries fl: interleaved
+// chunks hold their pairs inside each chunk; half-split lanes hold element e
+// of the real half in v0 and its partner in v1.  rot0 / rot1 say whether the
+// chunk rotates at all.
+template <bool IL, int E>
+__device__ __forceinline__ void rope_chunks(float* v0, float* v1, const float* fl, bool rot0,
+                                            bool rot1) {
+  if constexpr (IL) {
+#pragma unroll
+    for (int m = 0; m < E / 2; ++m) {
+      const float a0 = v0[2 * m], b0 = v0[2 * m + 1];
+      const float cs = fl[2 * m], sn = fl[2 * m + 1];
+      v0[2 * m] = rot0 ? a0 * cs - b0 * sn : a0;
+      v0[2 * m + 1] = rot0 ? a0 * sn + b0 * cs : b0;
+      const float a1 = v1[2 * m], b1 = v1[2 * m + 1];
+      const float cs1 = fl[E + 2 * m], sn1 = fl[E + 2 * m + 1];
+      v1[2 * m] = rot1 ? a1 * cs1 - b1 * sn1 : a1;
+      v1[2 * m + 1] = rot1 ? a1 * sn1 + b1 * cs1 : b1;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float re = v0[e], im = v1[e];
+      const float cs = fl[2 * e], sn = fl[2 * e + 1];
+      v0[e] = rot0 ? re * cs - im * sn : re;
+      v1[e] = rot0 ? re * sn + im * cs : im;
+    }
+  }
+}
+
 // Largest b < B with off[b] <= t, for batches of kSmallBatch sequences or
 // more.  The guess g = t * B / T (a host-computed 32.32 fixed-point factor) is
 // exact for one-token-per-sequence decode: its two offsets are loaded
@@ -953,8 +983,8 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
             o1 = x[p][1];
           }
         } else {
-          float v0[E], v1[E];
           const bool fp8_row = QANY && kind != SEG_Q && fp8_cache(sd.cache);
+          float v0[E], v1[E];
           if (fp8_row && kind == SEG_K_INPLACE) {
             fp8_values<E>(x[p][0], rsc[QANY ? p : 0], v0);
             fp8_values<E>(x[p][1], rsc[QANY ? p : 0], v1);
@@ -996,27 +1026,7 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
             fl_pos = pos[sd.cache];
             load_freqs<T, IL>(a, fl_pos, c0 - oc, c1 - oc, j, rot0, rot1, fl);
           }
-          if constexpr (IL) {
-#pragma unroll
-            for (int m = 0; m < E / 2; ++m) {
-              const float a0 = v0[2 * m], b0 = v0[2 * m + 1];
-              const float cs = fl[2 * m], sn = fl[2 * m + 1];
-              v0[2 * m] = rot0 ? a0 * cs - b0 * sn : a0;
-              v0[2 * m + 1] = rot0 ? a0 * sn + b0 * cs : b0;
-              const float a1 = v1[2 * m], b1 = v1[2 * m + 1];
-              const float cs1 = fl[E + 2 * m], sn1 = fl[E + 2 * m + 1];
-              v1[2 * m] = rot1 ? a1 * cs1 - b1 * sn1 : a1;
-              v1[2 * m + 1] = rot1 ? a1 * sn1 + b1 * cs1 : b1;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-              const float re = v0[e], im = v1[e];
-              const float cs = fl[2 * e], sn = fl[2 * e + 1];
-              v0[e] = rot0 ? re * cs - im * sn : re;
-              v1[e] = rot0 ? re * sn + im * cs : im;
-            }
-          }
+          rope_chunks<IL, E>(v0, v1, fl, rot0, rot1);
           if constexpr (!std::is_same_v<QT, T>) {
             if (kind == SEG_Q) {
               // Q in its own dtype: one rounding (un-roped elements converted)
