@@ -393,7 +393,9 @@ int32_t qrp_abi_version(void);
  *   QRP_KNOB_PASSES_PER_WAVE  1 .. 8, capped by the op's register budget
  *   QRP_KNOB_WAVES_PER_BLOCK  1 .. 4
  *   QRP_KNOB_XCD_REMAP        0: blocks dealt to the XCDs round-robin,
- *                             1: consecutive blocks kept on one XCD
+ *                             1: consecutive blocks kept on one XCD,
+ *                             2: each token's (or token block's) waves
+ *                             kept on one XCD, tokens dealt round-robin
  * The environment variables QRP_PACK, QRP_PASSES_PER_WAVE (0: the
  * library's choice), QRP_WAVES_PER_BLOCK (0: the library's choice) and
  * QRP_XCD_REMAP give the first values, read once when the library is

@@ -77,7 +77,7 @@ bool knob_value_ok(int32_t knob, int32_t v) {
     case QRP_KNOB_PACK: return v == 0 || v == 1;
     case QRP_KNOB_PASSES_PER_WAVE: return v >= 1 && v <= 8;
     case QRP_KNOB_WAVES_PER_BLOCK: return v >= 1 && v <= qrp::kMaxWavesPerBlock;
-    case QRP_KNOB_XCD_REMAP: return v == 0 || v == 1;
+    case QRP_KNOB_XCD_REMAP: return v >= 0 && v <= 2;
     default: return false;
   }
 }
@@ -290,7 +290,24 @@ struct Builder {
     if (forced_wpb > 0) wpb = std::min<uint32_t>((uint32_t)forced_wpb, qrp::kMaxWavesPerBlock);
     a.waves_per_block = wpb;
     a.n_blocks = (uint32_t)((items + wpb - 1) / wpb);
-    a.per_xcd = knob(QRP_KNOB_XCD_REMAP) == 1 ? (a.n_blocks + qrp::kXcds - 1) / qrp::kXcds : 0;
+    // Token-packed launches of one pass per wave (a decode batch's share
+    // of the heads) keep each token block's waves on one XCD, so they share
+    // its L2 for their metadata and freqs rows (decode at 8-way head
+    // parallelism: 3.08 -> 2.86 us per launch).  Everything else is dealt
+    // round-robin: keeping units on one XCD measured 1-6 % slower there.
+    int32_t remap = knob(QRP_KNOB_XCD_REMAP);
+    if (remap < 0) remap = (pack && ppg == 1) ? 2 : 0;
+    a.per_xcd = remap == 1 ? (a.n_blocks + qrp::kXcds - 1) / qrp::kXcds : 0;
+    if (remap == 2) {
+      // every unit's waves on one XCD: bpu blocks per unit, units dealt to
+      // the XCDs in turn
+      const uint64_t bpu = (a.groups_per_token + wpb - 1) / wpb;
+      const uint64_t per = (units + qrp::kXcds - 1) / qrp::kXcds;
+      const uint64_t blocks = (uint64_t)qrp::kXcds * bpu * per;
+      if (blocks >= (1ull << 31)) return fail(QRP_EINVAL, "batch too large for one launch");
+      a.per_xcd = qrp::kUnitsOnXcd | (uint32_t)bpu;
+      a.n_blocks = (uint32_t)blocks;
+    }
     a.total_tokens = total_tokens;
     a.guess_mul = (((uint64_t)a.batch) << 32) / total_tokens;
     return QRP_OK;

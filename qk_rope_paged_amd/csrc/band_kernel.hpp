@@ -620,9 +620,25 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   // adds) run on a clamped item and leave at the metadata check: no branch
   // before the first loads, so the header's fields arrive in one round.
   uint32_t blk = blockIdx.x;
-  blk = a.per_xcd ? (blk % kXcds) * a.per_xcd + blk / kXcds : blk;
-  const uint32_t item_raw = blk * a.waves_per_block + wave;
-  const bool dead = blk >= a.n_blocks || item_raw >= n_items;
+  uint32_t item_raw;
+  bool dead;
+  if (a.per_xcd & kUnitsOnXcd) {
+    // Blocks are dealt to the XCDs round-robin (block b runs on XCD b % 8).
+    // Give each unit (token, or token block) bpu consecutive blocks of one
+    // XCD -- blocks x, x + 8, x + 16, ... -- so that its waves share that
+    // XCD's L2 (one fetch of its freqs row and metadata), while the units
+    // at work at any moment stay neighbours, spread over all XCDs.
+    const uint32_t bpu = a.per_xcd & ~kUnitsOnXcd;
+    const uint32_t x = blk % kXcds, sl = blk / kXcds;
+    const uint32_t jq = sl / bpu;
+    const uint32_t g = (sl - jq * bpu) * a.waves_per_block + wave;  // group within the unit
+    item_raw = (jq * kXcds + x) * a.groups_per_token + g;
+    dead = g >= a.groups_per_token || item_raw >= n_items;
+  } else {
+    blk = a.per_xcd ? (blk % kXcds) * a.per_xcd + blk / kXcds : blk;
+    item_raw = blk * a.waves_per_block + wave;
+    dead = blk >= a.n_blocks || item_raw >= n_items;
+  }
   const uint32_t item = dead ? n_items - 1 : item_raw;
 
   // Gammas of every segment, per wave, in LDS.  Reading them there keeps the
@@ -818,12 +834,13 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
       pos[ci] = (uint32_t)p64;
     }
   }
-  // One-pass waves (decode-sized launches, the padded grid) load the freqs
-  // row as soon as the position is known: its address needs no page-table
-  // entry, so the two lookups overlap (measured on decode: 3.17 -> 3.09 us
-  // per launch; with more passes per wave the loads' registers cost more
-  // than the overlap gains).
-  constexpr bool EARLY_FREQS = NPMAX == 1 && !RADD;
+  // One-pass waves (decode-sized launches, the padded grid) and the store
+  // op over FP8 caches load the freqs row as soon as the position is known:
+  // its address needs no page-table entry, so the two lookups overlap
+  // (measured: decode 3.17 -> 3.09 us per launch, prefill over an FP8
+  // cache 35.12 -> 34.50; the plain prefill and the dual band ran 0.6 and
+  // 1.2 % slower with it, so they keep the freqs load after the lookup).
+  constexpr bool EARLY_FREQS = (NPMAX == 1 || (QUANT && !NORM)) && !RADD;
   float fl[RADD ? 1 : 2 * E];
   uint32_t fl_pos = pos[0];
   if constexpr (EARLY_FREQS) {
@@ -1072,7 +1089,8 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
 template <typename T, typename QT, typename CT, int D, bool IL, int NPMAX, bool RADD, bool NORM,
           bool BSHD, bool PACK>
 int launch_np(const BandArgs& a, void* stream) {
-  const uint32_t grid = a.per_xcd ? a.per_xcd * kXcds : a.n_blocks;
+  const uint32_t grid =
+      (a.per_xcd && !(a.per_xcd & kUnitsOnXcd)) ? a.per_xcd * kXcds : a.n_blocks;
   hipLaunchKernelGGL((band_kernel<T, QT, CT, D, IL, NPMAX, RADD, NORM, BSHD, PACK>), dim3(grid),
                      dim3(64 * a.waves_per_block), 0, reinterpret_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();

@@ -36,6 +36,7 @@ constexpr int kMaxCaches = 2;
 constexpr int kMaxWavesPerBlock = 4;
 constexpr int kThreads = 64 * kMaxWavesPerBlock;  // launch bound; blocks may be smaller
 constexpr int kXcds = 8;
+constexpr uint32_t kUnitsOnXcd = 0x80000000u;  // BandArgs::per_xcd flag
 
 // Passes (rows of 64 lanes) one wave may hold in registers at once.  Waves
 // that each move about 4 KB stream best on MI355X (measured with plain
@@ -103,7 +104,8 @@ struct BandArgs {
   uint32_t n_items;         // total_tokens * groups_per_token waves of work
   uint32_t n_blocks;        // blocks holding work
   uint32_t waves_per_block; // 1 .. kMaxWavesPerBlock
-  uint32_t per_xcd;         // blocks per XCD after the XCD-contiguous remap (0: no remap)
+  uint32_t per_xcd;         // blocks per XCD after the XCD-contiguous remap (0: no remap);
+                            // kUnitsOnXcd | b: each unit's waves in b blocks of one XCD
   uint32_t passes_per_token;
   uint32_t passes_per_group;
   uint32_t groups_per_token;

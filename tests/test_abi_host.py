@@ -50,7 +50,7 @@ def test_launch_overrides_set_restore_and_reject():
     assert qrp.set_launch_override(qrp.QRP_KNOB_PASSES_PER_WAVE, -1) == -1
     for knob, value in ((4, 0), (-1, 0), (qrp.QRP_KNOB_PACK, 2),
                         (qrp.QRP_KNOB_PASSES_PER_WAVE, 0), (qrp.QRP_KNOB_WAVES_PER_BLOCK, 5),
-                        (qrp.QRP_KNOB_XCD_REMAP, -2)):
+                        (qrp.QRP_KNOB_XCD_REMAP, -2), (qrp.QRP_KNOB_XCD_REMAP, 3)):
         with pytest.raises(qrp.QrpError):
             qrp.set_launch_override(knob, value)
     with pytest.raises(ValueError):

@@ -162,7 +162,7 @@ def test_fp8_dual_band_mixed_launch_configuration_does_not_change_bits():
     gh, _ = _gpu()
     case = _mixed_dual(sc.BF16, sc.FP8)
     ref = None
-    for remap, ppw, wpb in [(r, p, w) for r in ("0", "1") for p in ("0", "1", "2", "3")
+    for remap, ppw, wpb in [(r, p, w) for r in ("0", "1", "2") for p in ("0", "1", "2", "3")
                             for w in ("0", "1", "4")]:
         dc = gh.upload(case)
         with gh.knobs(remap, ppw, wpb, pack=1):      # packing is not used for mixed pairs
@@ -184,7 +184,7 @@ def test_fp8_launch_configuration_does_not_change_bits(workload, monkeypatch):
     gh, _ = _gpu()
     case = sc.WORKLOADS[workload](small=True)
     ref = None
-    for remap, ppw, wpb in [(r, p, w) for r in ("0", "1") for p in ("0", "1", "3")
+    for remap, ppw, wpb in [(r, p, w) for r in ("0", "1", "2") for p in ("0", "1", "3")
                             for w in ("0", "1", "4")]:
         dc = gh.upload(case)
         with gh.knobs(remap, ppw, wpb):

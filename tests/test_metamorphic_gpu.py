@@ -114,7 +114,7 @@ def test_launch_configuration_does_not_change_bits(workload, monkeypatch):
     _, gh, _ = _env()
     case = sc.WORKLOADS[workload](small=True)
     ref = None
-    for remap in ("0", "1"):
+    for remap in ("0", "1", "2"):
         for ppw in ("0", "1", "2", "3"):
             for wpb in ("0", "1", "2", "4"):
                 dc = gh.upload(case)
