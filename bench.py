@@ -285,11 +285,14 @@ def workload_config(case, cases) -> dict:
     return cfg
 
 
-def build_sets(cases):
+def build_sets(cases, share_freqs: bool = True):
     """One device copy per case.  Store-op pools larger than 2 GiB are shared:
     every set after the first gets a page table whose referenced entries
     point at fresh pages, disjoint from the pages any other set touches, so
-    no set overwrites another's rows."""
+    no set overwrites another's rows.  With `share_freqs`, sets whose freqs
+    table equals the first set's use that one device table: a model's
+    freqs_cis is one buffer read by every layer at every step, while the
+    batches' own inputs, caches and metadata stay separate (and cold)."""
     import numpy as np
     import torch
     from tests import gpu_harness as gh
@@ -331,6 +334,10 @@ def build_sets(cases):
         dc.caches = [gh.DeviceCache(host=host, pool=base.pool, cache_lengths=lens,
                                     lookup_table=ttab, desc=desc)]
         sets.append(dc)
+    if share_freqs and first.freqs is not None:
+        for dc, case in zip(sets[1:], cases[1:]):
+            if case.freq_dtype == first.freq_dtype and np.array_equal(case.freqs, first.freqs):
+                dc.freqs = sets[0].freqs
     return sets, shared
 
 
@@ -527,7 +534,7 @@ def percentiles(values, qs=(10, 50, 90)):
     return {q: v[min(len(v) - 1, (q * len(v)) // 100)] for q in qs}
 
 
-def prepare(workload: str, base_seed: int, sets_arg: int):
+def prepare(workload: str, base_seed: int, sets_arg: int, share_freqs: bool = True):
     """Seeded batches of the workload and their device buffer sets."""
     import torch
     from tests import gpu_harness as gh
@@ -545,7 +552,7 @@ def prepare(workload: str, base_seed: int, sets_arg: int):
         sets, shared_pool = [gh.upload_gemv(c) for c in cases], False
         calls = [gh.run_gemv(dg, prepare=True) for dg in sets]
     else:
-        sets, shared_pool = build_sets(cases)
+        sets, shared_pool = build_sets(cases, share_freqs)
         calls = [gh.run(dc, prepare=True) for dc in sets]
     torch.cuda.synchronize()
     return cases, set_bytes, sets, shared_pool, calls
@@ -611,7 +618,7 @@ def decode_block(args) -> dict:
     import torch
 
     w = "decode"
-    cases, set_bytes, sets, _, calls = prepare(w, DEFAULT_SEED[w], 0)
+    cases, set_bytes, sets, _, calls = prepare(w, DEFAULT_SEED[w], 0, not args.per_set_freqs)
     m = measure(w, calls, cases, set_bytes, args.decode_steps, args.decode_warmup)
     per_launch = time_graph(graph_launchers(sets, False), args.decode_steps)
     del sets, calls
@@ -657,6 +664,9 @@ def main() -> int:
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode block of the default (prefill) line")
+    ap.add_argument("--per-set-freqs", action="store_true",
+                    help="give every buffer set its own copy of the freqs table (default: the "
+                         "sets share one, as a model's layers do)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed launches from a HIP graph (captured before "
                          "the timed region)")
@@ -689,7 +699,8 @@ def main() -> int:
         decode = decode_block(args)
 
     base_seed = args.seed if args.seed is not None else DEFAULT_SEED[args.workload]
-    cases, set_bytes, sets, shared_pool, calls = prepare(args.workload, base_seed, args.sets)
+    cases, set_bytes, sets, shared_pool, calls = prepare(args.workload, base_seed, args.sets,
+                                                         not args.per_set_freqs)
     first = cases[0]
     n_sets = len(cases)
 
@@ -737,7 +748,10 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": first.dtype,
         "data": "synthetic (seeded batches with the workload's shapes and length distribution)",
-        "config": workload_config(first, cases),
+        "config": {**workload_config(first, cases),
+                   **({} if first.op == "gemv_norm" else
+                      {"freqs_table": "one copy per batch" if args.per_set_freqs else
+                       "one table shared by every batch"})},
         "tokens_per_s": round(sum(m["step_tokens"]) / wall, 1),
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": round(mean_bytes),
