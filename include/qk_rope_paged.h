@@ -295,10 +295,14 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
  *   unnormed_output[i][j - n_normed] = y_j              for j >= n_normed.
  * The mean runs over the n_normed leading columns only (n_normed is gamma's
  * length); weight_offset is accepted and not used (the page's Args say the
- * kernel does not consume it).  Products and sums are binary32 (one fused
- * multiply-add per term, then a fixed 64-way tree), the norm is binary32, and
- * each output is rounded once to dtype (QRP_F32, QRP_BF16 or QRP_F16; x, W,
- * gamma and both outputs share it).
+ * kernel does not consume it).  Products and sums are binary32: one wave
+ * computes a column, each lane adding its terms in k order -- one fused
+ * multiply-add per term for QRP_F32, one packed dot product per pair of
+ * terms for QRP_BF16 and QRP_F16 (both products exact, so at most one
+ * rounding per term) -- then a fixed 64-way tree adds the lanes.  The norm
+ * is binary32 (a row's sum of squares over 256 threads in a fixed order),
+ * and each output is rounded once to dtype (QRP_F32, QRP_BF16 or QRP_F16;
+ * x, W, gamma and both outputs share it).
  * Layout: input [m][input_row_stride], weight [n][weight_row_stride],
  * normed_output [m][normed_row_stride], unnormed_output
  * [m][unnormed_row_stride], gamma [n_normed]; all device memory, strides in
@@ -307,8 +311,10 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
  * outputs and gamma are element-aligned.
  * Workspace: device memory the caller owns, at least
  * qrp_gemv_norm_workspace_bytes(m, n_normed) bytes (0 when n_normed = 0:
- * NULL is then allowed).  It must be zero-filled before its first use; every
- * call leaves its counter at zero again, so it is reused without clearing.
+ * NULL is then allowed): a 256-byte arrival counter line, then
+ * 4 * m * n_normed bytes of binary32 y values.  It must be zero-filled before
+ * its first use; every call leaves its counter at zero again, so it is
+ * reused without clearing.
  * Calls that overlap in time must not share a workspace.
  * The summation order is fixed, so results are the same bits on every call
  * and for every row count (a row gives the same outputs alone or among 8).

@@ -97,11 +97,6 @@ int32_t gemv_call(void* normed_output, uint64_t normed_row_stride, void* unnorme
   a.n = n;
   a.kc = k / ce;
   a.n_normed = n_normed;
-  const uint32_t cpw = qrp::gemv_cols_per_wave(m);
-  a.n_waves = (uint32_t)(((uint64_t)n + cpw - 1) / cpw);
-  const uint64_t norm_waves = ((uint64_t)n_normed + cpw - 1) / cpw;
-  const uint32_t wpb = qrp::gemv_waves_per_block(m);
-  a.n_norm_blocks = (uint32_t)((norm_waves + wpb - 1) / wpb);
   a.eps = epsilon;
   const int e = qrp::launch_gemv_norm(a, dtype, stream);
   if (e != 0)

@@ -5,39 +5,48 @@
 // bandwidth, not by the matrix cores: it streams W with 16-byte
 // non-temporal loads and does the products on the vector ALUs.
 //
-// Work mapping.  One wave64 owns `CPW` consecutive output columns and sweeps
-// the whole of k: lane l takes the 16-byte chunks l, l + 64, l + 128, ... of
-// each W row (a wave reads 1 KB of a row per load instruction, fully
-// coalesced) and the same chunks of every x row (from the L1 for one row;
-// several rows are copied to LDS once per block when they fit 63 KB).  U chunks per lane are loaded before any is used, so a wave keeps
-// U * CPW KB of W in flight.  Each lane sums its own terms in k order with
-// one fused multiply-add per term, then an xor butterfly over the 64 lanes
-// adds the partial sums; every lane ends with the same bits (each step adds
-// the same two values, and binary32 addition commutes), so the order of
-// additions is fixed and the result does not depend on the launch.
+// Work mapping.  One wave64 owns a group of CPW consecutive output columns
+// and sweeps the whole of k: lane l takes the 16-byte chunks l, l + 64,
+// l + 128, ... of each W row (a wave reads 1 KB of a row per load
+// instruction, fully coalesced) and the same chunks of every x row (from
+// the L1 for one row; several rows are copied to LDS once per block when
+// they fit 63 KB).  U chunks per lane are loaded before any is used, so a
+// wave keeps U * CPW KB of W in flight.  Each lane sums its own terms in k
+// order -- for fp32 one fused multiply-add per term, for bf16 and f16 one
+// packed dot product per pair of terms (v_dot2, whose two products are
+// exact in binary32) -- then an xor butterfly over the 64 lanes adds the
+// partial sums; every lane ends with the same bits (each step adds the same
+// two values, and binary32 addition commutes).  The order of additions is
+// therefore fixed: the result does not depend on the launch shape, and a
+// row gives the same bits alone or among others.
+//
+// Launch shape.  At most one block of 8 waves per compute unit.  Blocks
+// [0, nbn) take the groups that hold normed columns, the others the
+// passed-through groups; within each set the groups go round-robin over
+// the blocks (see run()).
 //
 // The partial norm.  A row's norm needs all n_normed columns, which many
-// waves produce.  Those waves store their binary32 y values in a workspace;
-// then each block that holds a normed column meets at a barrier, and one
-// thread releases the block's values at agent scope and takes a ticket from
-// an arrival counter (an atomic increment that wraps to zero, so the counter
-// is zero again after every call).  Releases and increments of one counter
-// are serialised by the memory system (about 10 ns each, measured), so they
-// are taken per block of waves, not per wave.  The block that draws
-// the last ticket acquires, and its first four waves read the whole of y
-// back and normalise every row:
+// blocks produce.  Their waves store binary32 y values in a workspace; then
+// each normed block meets at a barrier, and one thread releases the block's
+// values at agent scope and takes a ticket from an arrival counter (an
+// atomic increment that wraps to zero, so the counter is zero again after
+// every call).  Arrivals are serialised -- each release writes back its
+// XCD's L2 (about 130 ns apart on one XCD, measured) and the increments of
+// the one counter follow each other -- so they are taken per block, not
+// per wave.  The block that draws the last ticket acquires, and its first
+// four waves read the whole of y back and normalise every row:
 //   ss = sum y_j^2 (per-thread fused multiply-adds in j order over every
 //        256th column, the butterfly, then the four wave sums in order),
 //   r = 1 / sqrt(ss / n_normed + eps),
 //   out_j = (y_j * r) * gamma_j, rounded to the storage dtype.
 // No wave waits for another, so nothing can hang on a missing arrival.
 // The columns past n_normed are rounded and stored by the wave that made
-// them.  Waves of the normed columns come first in the grid, so their
-// arrival overlaps the streaming of the rest.
+// them.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -81,18 +90,6 @@ __device__ __forceinline__ void widen(const gv4u v, float* f) {
   }
 }
 
-// element i of a dtype array, widened
-template <int DT>
-__device__ __forceinline__ float load_elem(const void* base, int64_t i) {
-  if constexpr (DT == QRP_F32) {
-    return reinterpret_cast<const float*>(base)[i];
-  } else if constexpr (DT == QRP_BF16) {
-    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[i] << 16);
-  } else {
-    return (float)reinterpret_cast<const _Float16*>(base)[i];
-  }
-}
-
 // v rounded to the dtype (nearest even) and stored as element i
 template <int DT>
 __device__ __forceinline__ void store_elem(void* base, int64_t i, float v) {
@@ -130,8 +127,26 @@ __device__ __forceinline__ float load_y(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// element i of a dtype array as raw bits, and those bits widened (exact)
+template <int DT>
+__device__ __forceinline__ uint32_t load_bits(const void* base, int64_t i) {
+  if constexpr (DT == QRP_F32)
+    return reinterpret_cast<const uint32_t*>(base)[i];
+  else
+    return reinterpret_cast<const uint16_t*>(base)[i];
+}
+template <int DT>
+__device__ __forceinline__ float bits_value(uint32_t b) {
+  if constexpr (DT == QRP_F32)
+    return __uint_as_float(b);
+  else if constexpr (DT == QRP_BF16)
+    return __uint_as_float(b << 16);
+  else
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
 // The norm is done by the first 256 threads (four waves, present in every
-// build) of the last block; each holds up to kNormHeld of a row's y values
+// launch) of the last block; each holds up to kNormHeld of a row's y values
 // and gammas, so a row of up to 2048 normed columns is read in one round.
 constexpr uint32_t kNormThreads = 256;
 constexpr int kNormHeld = 8;
@@ -140,63 +155,124 @@ constexpr int kNormHeld = 8;
 // (every thread of it calls this: the barriers need them all).  Thread t
 // sums columns t, t + 256, ... in order (padding terms add exact zeros),
 // each wave adds its 64 sums in the butterfly, and the four wave sums are
-// added in wave order, so the order does not depend on the block size or on
-// how many rounds a row takes.
-template <int DT>
+// added in wave order, so the order does not depend on the launch shape, on
+// how many rounds a row takes or on how many rows are normalised together.
+//
+// The loads are what this tail waits on, so they are issued together and
+// unconditionally: indexes past the end are clamped to the last column (a
+// value read and then replaced by zero), the raw gamma bits are widened
+// after every load has been issued, and with up to 2048 normed columns all
+// the rows' y values and the gammas (shared by the rows) are read in one
+// round before any is used.
+template <int DT, int MB>
 __device__ void norm_rows(const GemvArgs& a) {
-  __shared__ float wave_part[kNormThreads / 64];
+  __shared__ float wave_part[MB][kNormThreads / 64];
   const uint32_t t = threadIdx.x;
-  const bool worker = t < kNormThreads;
+  const bool worker = t < kNormThreads;  // wave-uniform
   const uint32_t nn = a.n_normed;
-  const bool one_round = nn <= kNormThreads * (uint32_t)kNormHeld;
-  for (uint32_t m = 0; m < a.m; ++m) {
-    const float* yr = a.ybuf + (uint64_t)m * nn;
-    void* out = reinterpret_cast<char*>(a.normed) +
-                (int64_t)m * a.normed_stride * (int64_t)(16 / chunk_elems<DT>());
-    float v[kNormHeld], g[kNormHeld];
-    float ss = 0.f;
-    for (uint32_t base = 0; base < nn; base += kNormThreads * (uint32_t)kNormHeld) {
+  const int64_t out_row = a.normed_stride;
+  if (nn <= kNormThreads * (uint32_t)kNormHeld) {
+    float v[MB][kNormHeld], g[kNormHeld];
+    if (worker) {
+      uint32_t gb[kNormHeld];
 #pragma unroll
       for (int i = 0; i < kNormHeld; ++i) {
-        const uint32_t j = base + t + kNormThreads * (uint32_t)i;
-        const bool in = worker && j < nn;
-        v[i] = in ? load_y(yr + j) : 0.f;
-        g[i] = in ? load_elem<DT>(a.gamma, j) : 0.f;
+        const uint32_t jc = min(t + kNormThreads * (uint32_t)i, nn - 1);
+        gb[i] = load_bits<DT>(a.gamma, jc);
+#pragma unroll
+        for (int r = 0; r < MB; ++r) {
+          const uint32_t rc = min((uint32_t)r, a.m - 1);
+          v[r][i] = load_y(a.ybuf + (uint64_t)rc * nn + jc);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < kNormHeld; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+      for (int i = 0; i < kNormHeld; ++i) {
+        const bool in = t + kNormThreads * (uint32_t)i < nn;
+        g[i] = in ? bits_value<DT>(gb[i]) : 0.f;
+#pragma unroll
+        for (int r = 0; r < MB; ++r) v[r][i] = in ? v[r][i] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < MB; ++r) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < kNormHeld; ++i) ss = __builtin_fmaf(v[r][i], v[r][i], ss);
+        ss = wave_sum(ss);
+        if ((t & 63u) == 0) wave_part[r][t >> 6] = ss;
+      }
     }
-    ss = wave_sum(ss);
-    if (worker && (t & 63u) == 0) wave_part[t >> 6] = ss;
     __syncthreads();
-    const float total = ((wave_part[0] + wave_part[1]) + wave_part[2]) + wave_part[3];
-    const float r = 1.0f / __builtin_sqrtf(total / (float)nn + a.eps);
-    if (one_round) {
+    if (worker) {
 #pragma unroll
-      for (int i = 0; i < kNormHeld; ++i) {
-        const uint32_t j = t + kNormThreads * (uint32_t)i;
-        if (worker && j < nn) store_elem<DT>(out, j, (v[i] * r) * g[i]);
+      for (int r = 0; r < MB; ++r) {
+        if ((uint32_t)r >= a.m) break;
+        const float total =
+            ((wave_part[r][0] + wave_part[r][1]) + wave_part[r][2]) + wave_part[r][3];
+        const float rs = 1.0f / __builtin_sqrtf(total / (float)nn + a.eps);
+#pragma unroll
+        for (int i = 0; i < kNormHeld; ++i) {
+          const uint32_t j = t + kNormThreads * (uint32_t)i;
+          if (j < nn) store_elem<DT>(a.normed, (int64_t)r * out_row + j, (v[r][i] * rs) * g[i]);
+        }
       }
-    } else if (worker) {
-      for (uint32_t j = t; j < nn; j += kNormThreads)
-        store_elem<DT>(out, j, (load_y(yr + j) * r) * load_elem<DT>(a.gamma, j));
+    }
+    return;
+  }
+  // longer rows: one row at a time, kNormHeld columns per thread per round
+  for (uint32_t r = 0; r < a.m; ++r) {
+    const float* yr = a.ybuf + (uint64_t)r * nn;
+    float ss = 0.f;
+    if (worker) {
+      for (uint32_t base = 0; base < nn; base += kNormThreads * (uint32_t)kNormHeld) {
+        float v[kNormHeld];
+#pragma unroll
+        for (int i = 0; i < kNormHeld; ++i)
+          v[i] = load_y(yr + min(base + t + kNormThreads * (uint32_t)i, nn - 1));
+#pragma unroll
+        for (int i = 0; i < kNormHeld; ++i) {
+          const float x = base + t + kNormThreads * (uint32_t)i < nn ? v[i] : 0.f;
+          ss = __builtin_fmaf(x, x, ss);
+        }
+      }
+      ss = wave_sum(ss);
+      if ((t & 63u) == 0) wave_part[0][t >> 6] = ss;
+    }
+    __syncthreads();
+    if (worker) {
+      const float total =
+          ((wave_part[0][0] + wave_part[0][1]) + wave_part[0][2]) + wave_part[0][3];
+      const float rs = 1.0f / __builtin_sqrtf(total / (float)nn + a.eps);
+      for (uint32_t base = 0; base < nn; base += kNormThreads * (uint32_t)kNormHeld) {
+        float v[kNormHeld];
+        uint32_t gb[kNormHeld];
+#pragma unroll
+        for (int i = 0; i < kNormHeld; ++i) {
+          const uint32_t jc = min(base + t + kNormThreads * (uint32_t)i, nn - 1);
+          v[i] = load_y(yr + jc);
+          gb[i] = load_bits<DT>(a.gamma, jc);
+        }
+#pragma unroll
+        for (int i = 0; i < kNormHeld; ++i) {
+          const uint32_t j = base + t + kNormThreads * (uint32_t)i;
+          if (j < nn)
+            store_elem<DT>(a.normed, (int64_t)r * out_row + j,
+                           (v[i] * rs) * bits_value<DT>(gb[i]));
+        }
+      }
     }
     __syncthreads();  // wave_part is reused by the next row
   }
 }
 
-template <int DT, int MB, int CPW, int U, int WPB, bool XL>
-__global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
-  const uint32_t lane = threadIdx.x & 63u;
-  // the grid's last block may hold waves past the end: they skip the work
-  // but still meet the block at its barrier
-  const uint32_t wave_raw = blockIdx.x * WPB + (threadIdx.x >> 6);
-  const bool live = wave_raw < a.n_waves;
-  const uint32_t wave = live ? wave_raw : a.n_waves - 1;
-  const uint32_t n0 = wave * CPW;
-
-  // operand rows; columns and rows past the ends are clamped so every load
-  // stays in bounds, and their results are never stored
+// Columns [g * CPW, g * CPW + CPW) of every row, by one wave: the wave's
+// dot products, then lane m * CPW + j stores (row m, column g * CPW + j) --
+// into the workspace for a normed column, rounded to the output otherwise.
+// Columns and rows past the ends are clamped so every load stays in bounds,
+// and their results are never stored.
+template <int DT, int MB, int CPW, int U, bool XL>
+__device__ __forceinline__ void column_group(const GemvArgs& a, uint32_t g, uint32_t lane,
+                                             const gv4u* x_lds) {
+  const uint32_t n0 = g * CPW;
   const gv4u* wrow[CPW];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
@@ -221,19 +297,8 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
 #pragma unroll
     for (int j = 0; j < CPW; ++j) acc[m][j] = 0.f;
 
-  // several x rows (XL): the block copies them to LDS once, row m at
-  // x_lds + m * kc; every wave would otherwise re-read them all from global
-  // memory, which overflows the L1
-  extern __shared__ gv4u x_lds[];
-  if constexpr (XL) {
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-      for (uint32_t c = threadIdx.x; c < a.kc; c += 64u * WPB) x_lds[m * a.kc + c] = xrow[m][c];
-    __syncthreads();
-  }
-
   const gv4u zero = {0u, 0u, 0u, 0u};
-  const uint32_t kc = live ? a.kc : 0u;
+  const uint32_t kc = a.kc;
   for (uint32_t base = 0; base < kc; base += 64u * U) {
     gv4u wv[U][CPW];
 #pragma unroll
@@ -257,7 +322,7 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
       for (int m = 0; m < MB; ++m) {
         gv4u xv = zero;
         if constexpr (XL) {
-          if (in) xv = x_lds[m * a.kc + c];
+          if (in) xv = x_lds[m * kc + c];
         } else {
           if (in) xv = xrow[m][c];
         }
@@ -280,7 +345,6 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
     }
   }
 
-  // totals, then lane m * CPW + j stores (row m, column n0 + j)
   float mine = 0.f;
   uint32_t my_row = 0, my_col = 0;
   bool store = false;
@@ -296,8 +360,7 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
         store = true;
       }
     }
-  store = store && live && my_row < a.m && my_col < a.n;
-  if (store) {
+  if (store && my_row < a.m && my_col < a.n) {
     if (my_col < a.n_normed)
       __hip_atomic_store(a.ybuf + (uint64_t)my_row * a.n_normed + my_col, mine,
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -305,49 +368,157 @@ __global__ void __launch_bounds__(64 * WPB) gemv_norm_kernel(const GemvArgs a) {
       store_elem<DT>(a.unnormed, (int64_t)my_row * a.unnormed_stride + (my_col - a.n_normed),
                      mine);
   }
-  // block-uniform: blocks past the normed columns are done
-  if (blockIdx.x * (uint32_t)(WPB * CPW) >= a.n_normed) return;
+}
 
-  // arrive once per block; the block holding the last ticket normalises
-  __shared__ uint32_t block_ticket;
+// chunk c of x row m (rows past the last are clamped to it)
+template <int DT>
+__device__ __forceinline__ gv4u xrow_chunk(const GemvArgs& a, int m, uint32_t c) {
+  const uint32_t row = min((uint32_t)m, a.m - 1);
+  return reinterpret_cast<const gv4u*>(reinterpret_cast<const char*>(a.x) +
+                                       (int64_t)row * a.x_stride *
+                                           (int64_t)(16 / chunk_elems<DT>()))[c];
+}
+
+// Waves per block.
+constexpr uint32_t kGemvMaxWaves = 8;
+// Bytes of W each block of normed groups streams (the launch shape).
+constexpr uint64_t kGemvNormBlockBytes = 200 * 1024;
+
+template <int DT, int MB, int CPW, int U, bool XL>
+__global__ void __launch_bounds__(64 * kGemvMaxWaves) gemv_norm_kernel(const GemvArgs a) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t w = threadIdx.x >> 6;
+  const uint32_t nw = blockDim.x >> 6;
+  const uint32_t nb = gridDim.x;
+  const uint32_t b = blockIdx.x;
+
+  // several x rows (XL): the block copies them to LDS once, row m at
+  // x_lds + m * kc; every wave would otherwise re-read them all from global
+  // memory, which overflows the L1
+  extern __shared__ gv4u x_lds[];
+  if constexpr (XL) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      for (uint32_t c = threadIdx.x; c < a.kc; c += blockDim.x) x_lds[m * a.kc + c] = xrow_chunk<DT>(a, m, c);
+    __syncthreads();
+  }
+
+  // Blocks [0, nbn) compute the normed groups, the others the passed-through
+  // ones; within each set wave w of block b takes groups w * nbs + b, then
+  // every (nw * nbs)-th after it (nbs blocks in the set), so consecutive
+  // groups go to different compute units.
+  const uint32_t nbn = a.n_norm_blocks;
+  const uint32_t ng = a.n_norm_groups;
+  if (b >= nbn) {
+    const uint32_t nbu = nb - nbn;
+    for (uint32_t g = ng + w * nbu + (b - nbn); g < a.n_groups; g += nw * nbu)
+      column_group<DT, MB, CPW, U, XL>(a, g, lane, x_lds);
+    return;
+  }
+  for (uint32_t g = w * nbn + b; g < ng; g += nw * nbn)
+    column_group<DT, MB, CPW, U, XL>(a, g, lane, x_lds);
+
+  // arrive once per block; the block that draws the last ticket normalises
+  __shared__ uint32_t block_last;
   __syncthreads();  // every wave's y values are stored
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    block_ticket = __builtin_amdgcn_atomic_inc32(a.counter, a.n_norm_blocks - 1,
-                                                 __ATOMIC_RELAXED, "agent");
+    block_last = __builtin_amdgcn_atomic_inc32(a.counter, nbn - 1, __ATOMIC_RELAXED, "agent") ==
+                 nbn - 1;
   }
-  __syncthreads();
-  if (block_ticket != a.n_norm_blocks - 1) return;  // block-uniform
+  // with no block of their own, the passed-through groups come after
+  if (nb == nbn)
+    for (uint32_t g = ng + w * nb + b; g < a.n_groups; g += nw * nb)
+      column_group<DT, MB, CPW, U, XL>(a, g, lane, x_lds);
+  __syncthreads();  // block_last is set
+  if (!block_last) return;  // block-uniform
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  norm_rows<DT>(a);
+  norm_rows<DT, MB>(a);
 }
 
 // Largest LDS copy of the x rows (more rows go through global memory); 1 KB
 // of a 64 KB block allocation is left for the kernel's own LDS.
 constexpr uint64_t kGemvMaxLdsBytes = 63 * 1024;
 
-template <int DT, int MB, int CPW, int U, int WPB>
-int run(const GemvArgs& a, hipStream_t s) {
-  const uint32_t blocks = (a.n_waves + WPB - 1) / WPB;
+// compute units of the current device (looked up once per device)
+std::mutex g_cu_mu;
+std::vector<uint32_t> g_cu_count;
+
+int device_cus(uint32_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  std::lock_guard<std::mutex> lock(g_cu_mu);
+  if ((size_t)dev >= g_cu_count.size()) g_cu_count.resize((size_t)dev + 1, 0u);
+  if (!g_cu_count[dev]) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return (int)e;
+    g_cu_count[dev] = cus > 0 ? (uint32_t)cus : 1u;
+  }
+  *out = g_cu_count[dev];
+  return 0;
+}
+
+template <int DT, int MB, int CPW, int U>
+int launch(const GemvArgs& a, uint32_t blocks, uint32_t waves, hipStream_t s) {
   const uint64_t lds = (uint64_t)MB * a.kc * 16;
   if (MB > 1 && lds <= kGemvMaxLdsBytes)
-    hipLaunchKernelGGL((gemv_norm_kernel<DT, MB, CPW, U, WPB, (MB > 1)>), dim3(blocks),
-                       dim3(64 * WPB), (uint32_t)lds, s, a);
+    hipLaunchKernelGGL((gemv_norm_kernel<DT, MB, CPW, U, (MB > 1)>), dim3(blocks),
+                       dim3(64 * waves), (uint32_t)lds, s, a);
   else
-    hipLaunchKernelGGL((gemv_norm_kernel<DT, MB, CPW, U, WPB, false>), dim3(blocks),
-                       dim3(64 * WPB), 0, s, a);
+    hipLaunchKernelGGL((gemv_norm_kernel<DT, MB, CPW, U, false>), dim3(blocks), dim3(64 * waves),
+                       0, s, a);
   return (int)hipGetLastError();
 }
 
-// rows per launch -> (rows held, columns per wave, chunks in flight per lane,
-// waves per block); the columns and waves must match gemv_cols_per_wave()
-// and gemv_waves_per_block()
+// The launch shape.  At most one block per compute unit: every compute
+// unit draws about the same share of HBM bandwidth, so one given two blocks
+// finishes last, at twice the time.  The normed groups get blocks of their
+// own, each streaming about kGemvNormBlockBytes of W (and at most two
+// rounds of its waves): every such block arrives once, and the arrivals
+// are serialised (a release writes back the XCD's L2, about 130 ns apart on
+// one XCD, and the increments of the one counter follow each other), so
+// more normed blocks stream the normed columns faster but arrive more
+// slowly; at one row of 7168 into 1536 normed columns the time is flat
+// between 96 and 128 such blocks.  The passed-through groups take few of
+// the remaining compute units (one round of their waves where they fit),
+// which leaves the normed blocks a larger share of the bandwidth.
+template <int DT, int MB, int CPW, int U>
+int run(GemvArgs& a, hipStream_t s) {
+  uint32_t cus = 0;
+  const int e = device_cus(&cus);
+  if (e != 0) return e;
+  const uint64_t groups = ((uint64_t)a.n + CPW - 1) / CPW;
+  const uint64_t norm_groups = ((uint64_t)a.n_normed + CPW - 1) / CPW;
+  a.n_groups = (uint32_t)groups;
+  a.n_norm_groups = (uint32_t)norm_groups;
+  const uint64_t nw = kGemvMaxWaves;
+  uint64_t nbn = 0, nbu;
+  if (norm_groups) {
+    const uint64_t bytes = norm_groups * CPW * (uint64_t)a.kc * 16;
+    nbn = std::max((bytes + kGemvNormBlockBytes - 1) / kGemvNormBlockBytes,
+                   (norm_groups + 2 * nw - 1) / (2 * nw));
+    nbn = std::max<uint64_t>(1, std::min<uint64_t>(nbn, std::min<uint64_t>(norm_groups,
+                                                                            cus * 3 / 4)));
+    nbu = std::min<uint64_t>(cus - std::min<uint64_t>(cus, nbn),
+                             (groups - norm_groups + nw - 1) / nw);
+  } else {
+    // nothing to arrive for: every compute unit streams (about 5 % faster
+    // than one round of 8 waves per block at one row of 7168 into 2112)
+    nbu = std::max<uint64_t>(1, std::min<uint64_t>(cus, groups));
+  }
+  a.n_norm_blocks = (uint32_t)nbn;
+  return launch<DT, MB, CPW, U>(a, (uint32_t)(nbn + nbu), (uint32_t)nw, s);
+}
+
+// rows per launch -> (rows held, columns per group, chunks in flight per lane)
 template <int DT>
-int run_rows(const GemvArgs& a, hipStream_t s) {
-  if (a.m <= 1) return run<DT, 1, 2, 8, 8>(a, s);
-  if (a.m <= 2) return run<DT, 2, 2, 8, 8>(a, s);
-  if (a.m <= 4) return run<DT, 4, 2, 4, 4>(a, s);
-  return run<DT, 8, 2, 4, 4>(a, s);
+int run_rows(GemvArgs& a, hipStream_t s) {
+  if (a.m <= 1) return run<DT, 1, 2, 16>(a, s);
+  if (a.m <= 2) return run<DT, 2, 2, 8>(a, s);
+  if (a.m <= 4) return run<DT, 4, 2, 4>(a, s);
+  return run<DT, 8, 2, 4>(a, s);
 }
 
 // Clears the arrival counter's line of a scratch buffer.
@@ -391,7 +562,7 @@ int gemv_scratch(void** out, void* stream) {
   return 0;
 }
 
-int launch_gemv_norm(const GemvArgs& a, int32_t dtype, void* stream) {
+int launch_gemv_norm(GemvArgs& a, int32_t dtype, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == QRP_F32) return run_rows<QRP_F32>(a, s);
   if (dtype == QRP_F16) return run_rows<QRP_F16>(a, s);

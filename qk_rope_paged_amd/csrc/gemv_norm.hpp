@@ -3,7 +3,7 @@
 //
 // y = x W^T for up to kGemvMaxRows input rows; the first n_normed columns of
 // each row are RMS-normalised as one vector and scaled by gamma, the other
-// columns are stored as they are.  One wave computes cols_per_wave columns
+// columns are stored as they are.  One wave computes a group of columns
 // over the whole of k; the columns that need the norm go to a binary32
 // workspace, and the last block of those to arrive normalises every row.
 #pragma once
@@ -26,23 +26,16 @@ struct GemvArgs {
   int64_t x_stride, w_stride, normed_stride, unnormed_stride;
   uint32_t m, n, kc;      // kc: 16-byte chunks per row of x and W
   uint32_t n_normed;
-  uint32_t n_waves;        // ceil(n / cols_per_wave)
-  uint32_t n_norm_blocks;  // blocks holding a normed column: the arrivals
   float eps;
+  // launch shape (set by launch_gemv_norm)
+  uint32_t n_groups;       // column groups: ceil(n / columns per group)
+  uint32_t n_norm_groups;  // groups holding a normed column (the leading ones)
+  uint32_t n_norm_blocks;  // blocks holding a normed group: the arrivals
 };
 
-// Columns one wave computes for m input rows, and waves per block.  A block
-// arrives once, so larger blocks mean fewer releases and fewer increments
-// of the one counter (each is serialised), but fewer blocks leave compute
-// units idle.  Measured at one row of 7168 into 2112 columns (1536 normed):
-// 2 columns x 8 waves 12.8 us; 1 x 16: 14.4; 2 x 16: 18.7; 2 x 4: 14.3;
-// 4 x 4: 14.6; 3 x 8: 15.0; at two rows 2 x 8: 15.0, 1 x 8: 17.4.  Every
-// build has at least the four waves the norm uses.
-inline uint32_t gemv_cols_per_wave(uint32_t) { return 2u; }
-inline uint32_t gemv_waves_per_block(uint32_t m) { return m <= 2 ? 8u : 4u; }
-
-// Enqueue the kernel; returns a hipError_t value (0: launched).
-int launch_gemv_norm(const GemvArgs& a, int32_t dtype, void* stream);
+// Enqueue the kernel (its launch shape is chosen from the sizes and the
+// device's compute-unit count); returns a hipError_t value (0: launched).
+int launch_gemv_norm(GemvArgs& a, int32_t dtype, void* stream);
 
 // The library's own scratch for callers that cannot allocate: per GPU, the
 // counter's line and then at most kGemvScratchFloats binary32 y values

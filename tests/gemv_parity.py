@@ -1,8 +1,8 @@
 """Parity bar of the fused GEMV + partial RMSNorm, derived from the kernel's
 binary32 arithmetic (u = 2^-24).
 
-The GEMV.  Each output y_j is the sum of k products.  The kernel gives each
-of a wave's 64 lanes the terms of every 64th 16-byte chunk, which the lane
+The GEMV.  Each output y_j is the sum of k products.  One wave computes
+it: each of its 64 lanes takes every 64th 16-byte chunk, which the lane
 adds in k order (n_l = ceil(kc / 64) * E terms, E elements per chunk) --
 one fused multiply-add per term for fp32, one packed dot product per pair
 of terms for bf16 and f16 (their products are exact in binary32, so it
