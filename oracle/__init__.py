@@ -119,7 +119,7 @@ def load() -> ctypes.CDLL:
                                            ctypes.POINTER(OrcTrace)]
     lib.orc_fused_qk_rope_bshd.restype = I32
     lib.orc_matmul_fused_partial_rmsnorm.argtypes = [P, U64, P, U64, P, U64, U32, P, U64, U32,
-                                                     U32, P, U32, F, F, I32, P, P, P]
+                                                     U32, P, U32, F, F, I32, I32, P, P, P]
     lib.orc_matmul_fused_partial_rmsnorm.restype = I32
     _lib = lib
     return lib
@@ -365,6 +365,7 @@ def run_gemv(case, trace: bool = True) -> GemvResult:
     st = lib.orc_matmul_fused_partial_rmsnorm(
         _ptr(normed), case.normed_row_stride, _ptr(unnormed), case.unnormed_row_stride,
         _ptr(x), x.shape[1], m, _ptr(w), w.shape[1], n, case.k, _ptr(g), case.n_normed,
-        case.epsilon, case.weight_offset, dt, _ptr(y), _ptr(a), _ptr(r))
+        case.epsilon, case.weight_offset, dt, int(getattr(case, "transpose_b", 1)), _ptr(y),
+        _ptr(a), _ptr(r))
     return GemvResult(status=int(st), seconds=time.perf_counter() - t0, normed=normed,
                       unnormed=unnormed, y_exact=y, abs_dot=a, r=r)

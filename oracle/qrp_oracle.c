@@ -750,8 +750,8 @@ int32_t orc_matmul_fused_partial_rmsnorm(
     void* normed_output, uint64_t normed_row_stride, void* unnormed_output,
     uint64_t unnormed_row_stride, const void* input, uint64_t input_row_stride, uint32_t m,
     const void* weight, uint64_t weight_row_stride, uint32_t n, uint32_t k, const void* gamma,
-    uint32_t n_normed, float epsilon, float weight_offset, int32_t dtype, double* y_exact,
-    double* abs_dot, double* r_out) {
+    uint32_t n_normed, float epsilon, float weight_offset, int32_t dtype, int32_t transpose_b,
+    double* y_exact, double* abs_dot, double* r_out) {
   (void)weight_offset; /* not consumed (MatmulFusedPartialRMSNorm page, Args) */
   if (!dtype_ok(dtype) || n_normed > n) return ORC_EINVAL;
   if (m == 0 || n == 0) return ORC_OK;
@@ -761,13 +761,17 @@ int32_t orc_matmul_fused_partial_rmsnorm(
   double* y = (double*)malloc(sizeof(double) * n);
   if (!y) return ORC_EINVAL;
   for (uint32_t i = 0; i < m; ++i) {
-    /* the GEMV: y_j = sum_k x_k W[j][k] (bf16, f16 and f32 products are
-     * exact in double) */
+    /* the GEMV: y_j = sum_k x_k B[k][j] with B = W^T (W stored [n][k],
+     * transpose_b) or B = W (W stored [k][n]); bf16, f16 and f32 products
+     * are exact in double */
     for (uint32_t j = 0; j < n; ++j) {
       double s = 0.0, a = 0.0;
       for (uint32_t kk = 0; kk < k; ++kk) {
+        const int64_t widx = transpose_b
+                                 ? (int64_t)j * (int64_t)weight_row_stride + kk
+                                 : (int64_t)kk * (int64_t)weight_row_stride + j;
         const double p = get(input, dtype, (int64_t)i * (int64_t)input_row_stride + kk) *
-                         get(weight, dtype, (int64_t)j * (int64_t)weight_row_stride + kk);
+                         get(weight, dtype, widx);
         s += p;
         a += fabs(p);
       }

@@ -175,7 +175,9 @@ int32_t orc_fused_qk_rope_bshd(const void* q_proj, int32_t dtype, uint32_t batch
                                orc_trace* trace);
 
 /* MatmulFusedPartialRMSNorm page (Summary, execute, Args): per input row i,
- * y = x_i W^T with W stored [n][k] (the page's default transpose_b), then the
+ * y = x_i W^T with W stored [n][k] (transpose_b != 0, the page's default),
+ * or y = x_i W with W stored [k][n] (transpose_b == 0; weight_row_stride is
+ * then the stride of W's k rows), then the
  * first n_normed columns of y are RMS-normalised as one vector,
  *   normed[i][j] = y_j / sqrt(mean_{j < n_normed} y_j^2 + epsilon) * gamma_j,
  * and the other n - n_normed columns pass through:
@@ -189,8 +191,8 @@ int32_t orc_matmul_fused_partial_rmsnorm(
     void* normed_output, uint64_t normed_row_stride, void* unnormed_output,
     uint64_t unnormed_row_stride, const void* input, uint64_t input_row_stride, uint32_t m,
     const void* weight, uint64_t weight_row_stride, uint32_t n, uint32_t k, const void* gamma,
-    uint32_t n_normed, float epsilon, float weight_offset, int32_t dtype, double* y_exact,
-    double* abs_dot, double* r_out);
+    uint32_t n_normed, float epsilon, float weight_offset, int32_t dtype, int32_t transpose_b,
+    double* y_exact, double* abs_dot, double* r_out);
 
 #ifdef __cplusplus
 }

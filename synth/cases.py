@@ -704,6 +704,7 @@ class GemvCase:
     normed_row_stride: int
     unnormed_row_stride: int
     op: str = "gemv_norm"
+    transpose_b: int = 1          # 1: w is W [n, w_stride]; 0: w is W^T stored [k, w_stride]
 
     @property
     def T(self) -> int:     # input rows: the tokens of a step
@@ -712,17 +713,25 @@ class GemvCase:
 
 def make_gemv_case(name: str, seed: int, dtype: str, m: int, k: int, n: int, n_normed: int,
                    epsilon: float = 1e-6, weight_offset: float = 0.0, x_pad: int = 0,
-                   w_pad: int = 0, out_pad: int = 0) -> GemvCase:
-    """x ~ N(0, 1), W ~ N(0, 1/k) (so y is about N(0, 1)), gamma ~ N(1, 0.1)."""
+                   w_pad: int = 0, out_pad: int = 0, transpose_b: bool = True) -> GemvCase:
+    """x ~ N(0, 1), W ~ N(0, 1/k) (so y is about N(0, 1)), gamma ~ N(1, 0.1).
+    W's values do not depend on transpose_b: with transpose_b False the same
+    [n, k] matrix is stored transposed, as [k, n + w_pad]."""
     x = np.full((m, k + x_pad), SENTINEL[dtype], dtype=BITS_DTYPE[dtype])
     x[:, :k] = to_bits(prng.normal(seed, S_X, m * k), dtype).reshape(m, k)
-    w = np.full((n, k + w_pad), SENTINEL[dtype], dtype=BITS_DTYPE[dtype])
-    w[:, :k] = to_bits(prng.normal(seed, S_W, n * k, std=1.0 / np.sqrt(max(k, 1))), dtype).reshape(n, k)
+    wv = to_bits(prng.normal(seed, S_W, n * k, std=1.0 / np.sqrt(max(k, 1))), dtype).reshape(n, k)
+    if transpose_b:
+        w = np.full((n, k + w_pad), SENTINEL[dtype], dtype=BITS_DTYPE[dtype])
+        w[:, :k] = wv
+    else:
+        w = np.full((k, n + w_pad), SENTINEL[dtype], dtype=BITS_DTYPE[dtype])
+        w[:, :n] = wv.T
     gamma = to_bits(prng.normal(seed, S_GAMMA, max(n_normed, 1), mean=1.0, std=0.1), dtype)
     return GemvCase(name=name, seed=seed, dtype=dtype, m=m, k=k, n=n, n_normed=n_normed, x=x,
                     w=w, gamma=gamma, epsilon=epsilon, weight_offset=weight_offset,
                     normed_row_stride=max(n_normed, 1) + out_pad,
-                    unnormed_row_stride=max(n - n_normed, 1) + out_pad)
+                    unnormed_row_stride=max(n - n_normed, 1) + out_pad,
+                    transpose_b=1 if transpose_b else 0)
 
 
 def gemv_norm(seed: int = 7, small: bool = False) -> GemvCase:

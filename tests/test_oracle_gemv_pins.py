@@ -12,6 +12,10 @@ page: Summary, execute, Args) against facts that do not come from the oracle.
   epsilon = 0; the normed part is invariant under scaling x by a power of
   two while the rest scales exactly; weight_offset is not consumed.
 * Output padding keeps its sentinels.
+* W stored [k][n] (transpose_b False, the page's Parameters): exact rational
+  sums indexed W[k][j] on a case whose k, n and padded stride all differ,
+  a square case whose transpose differs (W != W^T), and bit equality with
+  the [n][k] form on the same matrix.
 """
 from __future__ import annotations
 
@@ -26,11 +30,17 @@ from tests import brute
 
 
 def _exact(case):
-    """y[i][j] as exact fractions, by direct summation over k."""
+    """y[i][j] as exact fractions, by direct summation over k (W read as
+    w[j][k] when stored [n][k], as w[k][j] when stored [k][n])."""
     F = fractions.Fraction
     x = brute.as_f64(case.x[:, :case.k], case.dtype)
-    w = brute.as_f64(case.w[:, :case.k], case.dtype)
-    return [[sum(F(float(x[i, kk])) * F(float(w[j, kk])) for kk in range(case.k))
+    if case.transpose_b:
+        w = brute.as_f64(case.w[:, :case.k], case.dtype)
+        wjk = lambda j, kk: w[j, kk]
+    else:
+        w = brute.as_f64(case.w[:, :case.n], case.dtype)
+        wjk = lambda j, kk: w[kk, j]
+    return [[sum(F(float(x[i, kk])) * F(float(wjk(j, kk))) for kk in range(case.k))
              for j in range(case.n)] for i in range(case.m)]
 
 
@@ -136,3 +146,44 @@ def test_rows_are_independent():
         r = oracle.run_gemv(one)
         assert np.array_equal(r.normed[0], full.normed[i])
         assert np.array_equal(r.unnormed[0], full.unnormed[i])
+
+
+def test_w_stored_k_by_n_matches_exact_rational_sums():
+    for dtype in (sc.BF16, sc.F32, sc.F16):
+        case = sc.make_gemv_case("pin_t", 15, dtype, m=2, k=24, n=9, n_normed=0, x_pad=3,
+                                 w_pad=7, out_pad=2, transpose_b=False)
+        assert case.w.shape == (24, 16)
+        res = oracle.run_gemv(case)
+        assert res.status == 0
+        ex = _exact(case)
+        for i in range(case.m):
+            for j in range(case.n):
+                y = float(ex[i][j])
+                assert abs(res.y_exact[i, j] - y) <= 2.0 ** -50 * res.abs_dot[i, j] + 1e-300
+                if dtype == sc.F16:
+                    assert int(res.unnormed[i, j]) == int(np.float16(y).view(np.uint16))
+                else:
+                    assert int(res.unnormed[i, j]) == _rounded_bits(y, dtype), (dtype, i, j)
+
+
+def test_w_stored_k_by_n_is_not_read_as_n_by_k():
+    # a square W whose transpose differs: reading W[j][k] in place of W[k][j]
+    # gives other sums; x = e_1 picks row 1 of the stored [k][n] array
+    case = sc.make_gemv_case("pin_t", 16, sc.F32, m=1, k=8, n=8, n_normed=0, transpose_b=False)
+    stored = np.arange(64, dtype=np.float64).reshape(8, 8)   # stored[k][j]
+    case.w = sc.to_bits(stored, sc.F32)
+    x = np.zeros((1, 8))
+    x[0, 1] = 1.0
+    case.x = sc.to_bits(x, sc.F32)
+    res = oracle.run_gemv(case)
+    assert res.y_exact[0].tolist() == stored[1].tolist()     # y_j = W[k=1][j]
+
+
+def test_w_stored_k_by_n_equals_w_stored_n_by_k():
+    for dtype in (sc.BF16, sc.F32):
+        a = sc.make_gemv_case("pin_t", 17, dtype, m=3, k=40, n=21, n_normed=13, w_pad=4)
+        b = sc.make_gemv_case("pin_t", 17, dtype, m=3, k=40, n=21, n_normed=13, w_pad=4,
+                              transpose_b=False)
+        assert np.array_equal(a.w[:, :40].T, b.w[:, :21])
+        ra, rb = oracle.run_gemv(a), oracle.run_gemv(b)
+        assert np.array_equal(ra.normed, rb.normed) and np.array_equal(ra.unnormed, rb.unnormed)

@@ -78,8 +78,13 @@ MUTATIONS = {
                           "for (uint32_t kk = 0; kk + 1 < k; ++kk) {"),
     "gemv_x_row_ignored": ("get(input, dtype, (int64_t)i * (int64_t)input_row_stride + kk)",
                            "get(input, dtype, kk)"),
-    "gemv_weight_stride_is_k": ("get(weight, dtype, (int64_t)j * (int64_t)weight_row_stride + kk)",
-                                "get(weight, dtype, (int64_t)j * (int64_t)k + kk)"),
+    "gemv_weight_stride_is_k": ("? (int64_t)j * (int64_t)weight_row_stride + kk",
+                                "? (int64_t)j * (int64_t)k + kk"),
+    "gemv_transpose_flag_ignored": ("const int64_t widx = transpose_b", "const int64_t widx = 1"),
+    "gemv_k_by_n_stride_is_n": (": (int64_t)kk * (int64_t)weight_row_stride + j;",
+                                ": (int64_t)kk * (int64_t)n + j;"),
+    "gemv_k_by_n_read_as_n_by_k": (": (int64_t)kk * (int64_t)weight_row_stride + j;",
+                                   ": (int64_t)j * (int64_t)weight_row_stride + kk;"),
     "partial_norm_eps_outside_root": (
         "r = 1.0 / sqrt(ss / (double)n_normed + (double)epsilon);",
         "r = 1.0 / (sqrt(ss / (double)n_normed) + (double)epsilon);"),
@@ -158,6 +163,8 @@ PIN_TESTS = [
     (gemv_pins.test_partial_norm_unit_mean_square_and_scale_invariance, {}),
     (gemv_pins.test_weight_offset_is_not_consumed, {}),
     (gemv_pins.test_rows_are_independent, {}),
+    (gemv_pins.test_w_stored_k_by_n_matches_exact_rational_sums, {}),
+    (gemv_pins.test_w_stored_k_by_n_is_not_read_as_n_by_k, {}),
 ]
 
 
