@@ -63,7 +63,7 @@ KERNEL_SOURCES = ("qk_rope_paged_amd/csrc/band_kernel.hpp", "qk_rope_paged_amd/c
 GEMV_KERNEL_NAME = "gemv_norm_kernel"
 GEMV_SOURCES = ("qk_rope_paged_amd/csrc/gemv_norm.hip", "qk_rope_paged_amd/csrc/gemv_norm.hpp",
                 "qk_rope_paged_amd/csrc/abi_gemv.cpp")
-GEMV_WORKLOADS = ("gemv_norm", "gemv_norm_rows4")
+GEMV_WORKLOADS = ("gemv_norm", "gemv_norm_rows4", "gemv_norm_t")
 
 
 def log(*a):
@@ -96,6 +96,8 @@ def _code_only(text: str) -> str:
 
 
 def kernel_name(workload: str) -> str:
+    if workload == "gemv_norm_t":
+        return "gemv_norm_t_kernel"     # W stored [k][n]
     return GEMV_KERNEL_NAME if workload in GEMV_WORKLOADS else KERNEL_NAME
 
 
@@ -243,7 +245,7 @@ def case_tokens(case) -> int:
 DEFAULT_SEED = {"prefill": 2, "decode": 3, "dual": 4, "radd": 5, "bshd": 6, "prefill_tp8": 2,
                 "decode_tp8": 3, "dual_tp8": 4}
 DEFAULT_SEED.update({f"{k}_fp8": v for k, v in list(DEFAULT_SEED.items())})
-DEFAULT_SEED["gemv_norm"] = DEFAULT_SEED["gemv_norm_rows4"] = 7
+DEFAULT_SEED["gemv_norm"] = DEFAULT_SEED["gemv_norm_rows4"] = DEFAULT_SEED["gemv_norm_t"] = 7
 
 
 def make_case(workload: str, seed: int = None):

@@ -288,22 +288,30 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
  * MatmulFusedPartialRMSNorm page (Summary, execute, Args): a GEMV fused with
  * a partial RMSNorm.  For each of the m input rows x_i (m = 1 is the page's
  * GEMV; up to 8 rows per call, each independent):
- *   y = x_i W^T,  W stored [n][k] row-major (the page's default transpose_b;
- *                 transpose_b = 0 returns QRP_EUNSUPPORTED),
+ *   y = x_i W^T,  W stored [n][k] row-major (transpose_b = 1, the page's
+ *                 default), or
+ *   y = x_i W,    W stored [k][n] row-major (transpose_b = 0; the page's
+ *                 Parameters: transpose_b),
  *   normed_output[i][j]   = y_j / sqrt(mean_{j' < n_normed} y_j'^2 + epsilon)
  *                           * gamma_j                   for j <  n_normed,
  *   unnormed_output[i][j - n_normed] = y_j              for j >= n_normed.
  * The mean runs over the n_normed leading columns only (n_normed is gamma's
  * length); weight_offset is accepted and not used (the page's Args say the
- * kernel does not consume it).  Products and sums are binary32: one wave
- * computes a column, each lane adding its terms in k order -- one fused
- * multiply-add per term for QRP_F32, one packed dot product per pair of
- * terms for QRP_BF16 and QRP_F16 (both products exact, so at most one
- * rounding per term) -- then a fixed 64-way tree adds the lanes.  The norm
+ * kernel does not consume it).  Products and sums are binary32.  With W
+ * stored [n][k] one wave computes a column, each lane adding its terms in k
+ * order -- one fused multiply-add per term for QRP_F32, one packed dot
+ * product per pair of terms for QRP_BF16 and QRP_F16 (both products exact,
+ * so at most one rounding per term) -- then a fixed 64-way tree adds the
+ * lanes.  With W stored [k][n] a block of 256 threads computes a group of
+ * columns, each thread adding every 256th 16-byte k-chunk's terms in k order
+ * (one fused multiply-add per term), then the 64-way tree in each wave and
+ * the four wave sums in order.  With W stored [k][n], n times the element
+ * size need not be a multiple of 16 bytes, but the row stride must.  The norm
  * is binary32 (a row's sum of squares over 256 threads in a fixed order),
  * and each output is rounded once to dtype (QRP_F32, QRP_BF16 or QRP_F16;
  * x, W, gamma and both outputs share it).
- * Layout: input [m][input_row_stride], weight [n][weight_row_stride],
+ * Layout: input [m][input_row_stride], weight [n][weight_row_stride]
+ * (transpose_b = 1) or [k][weight_row_stride] (transpose_b = 0),
  * normed_output [m][normed_row_stride], unnormed_output
  * [m][unnormed_row_stride], gamma [n_normed]; all device memory, strides in
  * elements.  input, weight and workspace are 16-byte aligned, k and the
@@ -320,7 +328,9 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
  * and for every row count (a row gives the same outputs alone or among 8).
  * Errors: QRP_EINVAL for a NULL buffer that the call needs, n_normed > n,
  * n >= 2^31, a stride below its row or a short workspace; QRP_EUNSUPPORTED
- * for m > 8, transpose_b = 0 or another dtype.  m == 0 or n == 0 returns
+ * for m > 8 or another dtype; QRP_EINVAL for transpose_b other than 0 or
+ * 1, or a weight row stride below k (transpose_b = 1) or n (transpose_b =
+ * 0).  m == 0 or n == 0 returns
  * QRP_OK without a launch; k == 0 gives y = 0.
  */
 uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed);

@@ -37,8 +37,8 @@ int32_t gemv_call(void* normed_output, uint64_t normed_row_stride, void* unnorme
   qrp::clear_error();
   (void)weight_offset;  // not consumed by this op (its page's Args)
   if (!dtype_ok(dtype)) return qrp::set_error(QRP_EUNSUPPORTED, "dtype must be QRP_F32, QRP_BF16 or QRP_F16");
-  if (transpose_b != 1)
-    return qrp::set_error(QRP_EUNSUPPORTED, "only transpose_b = 1 (W stored [n][k]) is built");
+  if (transpose_b != 0 && transpose_b != 1)
+    return qrp::set_error(QRP_EINVAL, "transpose_b must be 0 (W stored [k][n]) or 1 (W stored [n][k])");
   if (n_normed > n) return qrp::set_error(QRP_EINVAL, "n_normed > n");
   if (m > qrp::kGemvMaxRows) return qrp::set_error(QRP_EUNSUPPORTED, "m > 8 rows per call");
   if (m == 0 || n == 0) return QRP_OK;
@@ -57,8 +57,10 @@ int32_t gemv_call(void* normed_output, uint64_t normed_row_stride, void* unnorme
     return qrp::set_error(QRP_EALIGN, "outputs and gamma must be aligned to their element size");
   if (k % ce || input_row_stride % ce || weight_row_stride % ce)
     return qrp::set_error(QRP_EALIGN, "k and the input / weight row strides must be multiples of 16 bytes");
-  if (input_row_stride < k || weight_row_stride < k)
-    return qrp::set_error(QRP_EINVAL, "input / weight row stride < k");
+  if (input_row_stride < k) return qrp::set_error(QRP_EINVAL, "input row stride < k");
+  if (weight_row_stride < (transpose_b ? k : n))
+    return qrp::set_error(QRP_EINVAL, transpose_b ? "weight row stride < k (W stored [n][k])"
+                                                  : "weight row stride < n (W stored [k][n])");
   if (n_normed && normed_row_stride < n_normed)
     return qrp::set_error(QRP_EINVAL, "normed_row_stride < n_normed");
   if (n_normed < n && unnormed_row_stride < n - n_normed)
@@ -98,6 +100,7 @@ int32_t gemv_call(void* normed_output, uint64_t normed_row_stride, void* unnorme
   a.kc = k / ce;
   a.n_normed = n_normed;
   a.eps = epsilon;
+  a.transpose_b = (uint32_t)transpose_b;
   const int e = qrp::launch_gemv_norm(a, dtype, stream);
   if (e != 0)
     return qrp::set_error(QRP_EHIP, std::string("kernel launch failed: ") +

@@ -436,6 +436,160 @@ __global__ void __launch_bounds__(64 * kGemvMaxWaves) gemv_norm_kernel(const Gem
   norm_rows<DT, MB>(a);
 }
 
+// W stored [k][n] (transpose_b = 0): y_j = sum_k x_k W[k][j].  A row of W
+// now holds many columns, so a wave cannot stream one column's k values
+// contiguously.  Instead a block of 256 threads owns a unit of TP 16-byte
+// column chunks (TP * E columns) over the whole of k: thread t takes the
+// k-chunks q = t, t + 256, ... (E rows each) and loads, for each of its
+// rows, the unit's 16 bytes of that row, plus the E x values of the
+// k-chunk for every input row.  Each access is 16 bytes of a different
+// line; the line's other chunks belong to neighbouring units, which the
+// grid places on the same XCD at the same time (unit u on XCD u / per), so
+// the L2 serves them and HBM sees each line once -- the loads are ordinary
+// ones, so that the lines stay in the L2.
+//
+// Summation order per column: thread t adds its k-chunks in k order, each
+// chunk's E terms in k order (one fused multiply-add per term: every
+// product of two binary32-or-narrower values is exact in binary32, so each
+// term rounds once), then the butterfly over its wave's 64 lanes, then the
+// four wave sums in wave order -- fixed, and the same for every row count.
+// The partial norm is the one of the [n][k] kernel: one arrival per block
+// holding a normed column, and the last block normalises.
+template <int DT, int MB, int TP, int UT>
+__global__ void __launch_bounds__(256) gemv_norm_t_kernel(const GemvArgs a) {
+  constexpr int E = chunk_elems<DT>();
+  constexpr int NC = TP * E;  // columns per unit
+  const uint32_t t = threadIdx.x;
+  const uint32_t lane = t & 63u;
+  const uint32_t w = t >> 6;
+  // blocks are dealt to the XCDs in turn (block b on XCD b % 8): XCD x takes
+  // units [x * per, (x + 1) * per), so neighbouring units share its L2
+  const uint32_t unit = (blockIdx.x % 8u) * a.units_per_xcd + blockIdx.x / 8u;
+  if (unit >= a.n_groups) return;  // block-uniform, before any barrier
+  const uint32_t n0 = unit * NC;
+  const int64_t es = 16 / E;  // element bytes
+  const char* wcol = reinterpret_cast<const char*>(a.w) + (int64_t)n0 * es;
+  const int64_t wrow = a.w_stride * es;
+  const char* xb = reinterpret_cast<const char*>(a.x);
+  const int64_t xrow = a.x_stride * es;
+
+  float acc[MB][NC];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[m][c] = 0.f;
+
+  const gv4u zero = {0u, 0u, 0u, 0u};
+  const uint32_t kc = a.kc;
+  for (uint32_t base = 0; base < kc; base += 256u * UT) {
+    gv4u wv[UT][E][TP], xv[UT][MB];
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      const uint32_t q = base + (uint32_t)u * 256u + t;
+      const bool in = q < kc;
+      const uint32_t qc = in ? q : 0u;
+#pragma unroll
+      for (int r = 0; r < E; ++r)
+#pragma unroll
+        for (int p = 0; p < TP; ++p) {
+          // a chunk past the row's stride (the last unit of a ragged n) is
+          // never read: its columns are never stored
+          const bool inp = in && n0 + (uint32_t)(p * E) < (uint64_t)a.w_stride;
+          wv[u][r][p] = inp ? *reinterpret_cast<const gv4u*>(wcol + (int64_t)(qc * E + r) * wrow +
+                                                             p * 16)
+                            : zero;
+        }
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const uint32_t row = min((uint32_t)m, a.m - 1);
+        xv[u][m] = in ? *reinterpret_cast<const gv4u*>(xb + (int64_t)row * xrow + (int64_t)qc * 16)
+                      : zero;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        float wf[TP][E];
+#pragma unroll
+        for (int p = 0; p < TP; ++p) widen<DT>(wv[u][r][p], wf[p]);
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          float xf[E];
+          widen<DT>(xv[u][m], xf);
+#pragma unroll
+          for (int p = 0; p < TP; ++p)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              acc[m][p * E + e] = __builtin_fmaf(xf[r], wf[p][e], acc[m][p * E + e]);
+        }
+      }
+    }
+  }
+
+  // each column's 256 thread sums: the butterfly in each wave, then the four
+  // wave sums in order; thread m * NC + c stores (row m, column n0 + c)
+  __shared__ float part[4][MB * NC];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float v = wave_sum(acc[m][c]);
+      if (lane == 0) part[w][m * NC + c] = v;
+    }
+  __syncthreads();
+  if (t < (uint32_t)(MB * NC)) {
+    const uint32_t my_row = t / NC, my_col = n0 + t % NC;
+    const float y = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+    if (my_row < a.m && my_col < a.n) {
+      if (my_col < a.n_normed)
+        __hip_atomic_store(a.ybuf + (uint64_t)my_row * a.n_normed + my_col, y, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else
+        store_elem<DT>(a.unnormed,
+                       (int64_t)my_row * a.unnormed_stride + (my_col - a.n_normed), y);
+    }
+  }
+  if (unit >= a.n_norm_blocks) return;  // block-uniform: no normed column here
+
+  // arrive once per block; the block that draws the last ticket normalises
+  __shared__ uint32_t block_last;
+  __syncthreads();  // every thread's y values are stored
+  if (t == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    block_last = __builtin_amdgcn_atomic_inc32(a.counter, a.n_norm_blocks - 1, __ATOMIC_RELAXED,
+                                               "agent") == a.n_norm_blocks - 1;
+  }
+  __syncthreads();
+  if (!block_last) return;  // block-uniform
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  norm_rows<DT, MB>(a);
+}
+
+// The [k][n] launch: one block per unit of TP column chunks, the units of
+// each XCD contiguous.
+template <int DT, int MB, int TP, int UT>
+int run_t(GemvArgs& a, hipStream_t s) {
+  constexpr uint64_t NC = (uint64_t)TP * chunk_elems<DT>();
+  const uint64_t units = ((uint64_t)a.n + NC - 1) / NC;
+  const uint64_t per = (units + 7) / 8;
+  a.n_groups = (uint32_t)units;
+  a.n_norm_groups = (uint32_t)(((uint64_t)a.n_normed + NC - 1) / NC);
+  a.n_norm_blocks = a.n_norm_groups;  // units [0, n_norm_groups) arrive
+  a.units_per_xcd = (uint32_t)per;
+  hipLaunchKernelGGL((gemv_norm_t_kernel<DT, MB, TP, UT>), dim3((uint32_t)(8 * per)), dim3(256), 0,
+                     s, a);
+  return (int)hipGetLastError();
+}
+
+template <int DT>
+int run_t_rows(GemvArgs& a, hipStream_t s) {
+  if (a.m <= 1) return run_t<DT, 1, 2, 2>(a, s);
+  if (a.m <= 2) return run_t<DT, 2, 2, 1>(a, s);
+  if (a.m <= 4) return run_t<DT, 4, 1, 1>(a, s);
+  return run_t<DT, 8, 1, 1>(a, s);
+}
+
 // Largest LDS copy of the x rows (more rows go through global memory); 1 KB
 // of a 64 KB block allocation is left for the kernel's own LDS.
 constexpr uint64_t kGemvMaxLdsBytes = 63 * 1024;
@@ -564,6 +718,11 @@ int gemv_scratch(void** out, void* stream) {
 
 int launch_gemv_norm(GemvArgs& a, int32_t dtype, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!a.transpose_b) {
+    if (dtype == QRP_F32) return run_t_rows<QRP_F32>(a, s);
+    if (dtype == QRP_F16) return run_t_rows<QRP_F16>(a, s);
+    return run_t_rows<QRP_BF16>(a, s);
+  }
   if (dtype == QRP_F32) return run_rows<QRP_F32>(a, s);
   if (dtype == QRP_F16) return run_rows<QRP_F16>(a, s);
   return run_rows<QRP_BF16>(a, s);

@@ -27,10 +27,12 @@ struct GemvArgs {
   uint32_t m, n, kc;      // kc: 16-byte chunks per row of x and W
   uint32_t n_normed;
   float eps;
+  uint32_t transpose_b;    // 1: W stored [n][w_stride]; 0: W stored [k][w_stride]
   // launch shape (set by launch_gemv_norm)
   uint32_t n_groups;       // column groups: ceil(n / columns per group)
   uint32_t n_norm_groups;  // groups holding a normed column (the leading ones)
   uint32_t n_norm_blocks;  // blocks holding a normed group: the arrivals
+  uint32_t units_per_xcd;  // W stored [k][n]: column units each XCD takes, in turn
 };
 
 // Enqueue the kernel (its launch shape is chosen from the sizes and the

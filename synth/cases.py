@@ -734,13 +734,22 @@ def make_gemv_case(name: str, seed: int, dtype: str, m: int, k: int, n: int, n_n
                     transpose_b=1 if transpose_b else 0)
 
 
-def gemv_norm(seed: int = 7, small: bool = False) -> GemvCase:
+def gemv_norm(seed: int = 7, small: bool = False, transpose_b: bool = True) -> GemvCase:
     """One input row (a GEMV) of hidden size 7168 into 1536 normed and 576
     passed-through columns (the shape of a low-rank query / key-value
-    projection); bf16.  The small form keeps the split at a tenth the size."""
+    projection); bf16.  The small form keeps the split at a tenth the size.
+    transpose_b False stores the same W as [k][n]."""
+    sfx = "" if transpose_b else "_t"
     if small:
-        return make_gemv_case("gemv_norm_small", seed, BF16, 1, 704, 216, 152)
-    return make_gemv_case("gemv_norm", seed, BF16, 1, 7168, 2112, 1536)
+        return make_gemv_case("gemv_norm_small" + sfx, seed, BF16, 1, 704, 216, 152,
+                              transpose_b=transpose_b)
+    return make_gemv_case("gemv_norm" + sfx, seed, BF16, 1, 7168, 2112, 1536,
+                          transpose_b=transpose_b)
+
+
+def gemv_norm_t(seed: int = 7, small: bool = False) -> GemvCase:
+    """The gemv_norm projection with W stored [k][n] (transpose_b False)."""
+    return gemv_norm(seed, small, transpose_b=False)
 
 
 def gemv_norm_rows4(seed: int = 7, small: bool = False) -> GemvCase:
@@ -750,4 +759,5 @@ def gemv_norm_rows4(seed: int = 7, small: bool = False) -> GemvCase:
     return make_gemv_case("gemv_norm_rows4", seed, BF16, 4, 7168, 2112, 1536)
 
 
-GEMV_WORKLOADS = {"gemv_norm": gemv_norm, "gemv_norm_rows4": gemv_norm_rows4}
+GEMV_WORKLOADS = {"gemv_norm": gemv_norm, "gemv_norm_rows4": gemv_norm_rows4,
+                  "gemv_norm_t": gemv_norm_t}

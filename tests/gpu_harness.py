@@ -264,5 +264,5 @@ def run_gemv(dg: DeviceGemv, stream=None, raise_on_error=True, prepare=False,
         dg.unnormed if c.n_normed < c.n else None, c.unnormed_row_stride,
         dg.x, c.x.shape[1], c.m, dg.w, c.w.shape[1], c.n, c.k, dg.gamma, c.n_normed,
         c.epsilon, c.weight_offset, QRP_DT[c.dtype], ws,
-        0 if ws is None else ws.numel(), stream=stream, raise_on_error=raise_on_error,
-        prepare=prepare)
+        0 if ws is None else ws.numel(), transpose_b=int(getattr(c, "transpose_b", 1)),
+        stream=stream, raise_on_error=raise_on_error, prepare=prepare)

@@ -374,7 +374,9 @@ def _gemv(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=qrp.QRP_FP8), qrp.QRP_EUNSUPPORTED),
-    (dict(transpose_b=0), qrp.QRP_EUNSUPPORTED),
+    (dict(transpose_b=2), qrp.QRP_EINVAL),
+    (dict(transpose_b=0, weight_row_stride=2104), qrp.QRP_EINVAL),   # W [k][n]: stride < n
+    (dict(transpose_b=0, weight_row_stride=2116), qrp.QRP_EALIGN),   # not 16-byte rows
     (dict(m=9), qrp.QRP_EUNSUPPORTED),
     (dict(n_normed=2113), qrp.QRP_EINVAL),
     (dict(input=None), qrp.QRP_EINVAL),

@@ -254,3 +254,80 @@ def test_subnormal_weights_are_not_flushed(dtype, x_scale, w_std):
     tiny = 2.0 ** -14 if dtype == sc.F16 else 2.0 ** -126
     assert np.all(np.abs(vals) < tiny) and np.count_nonzero(vals) > 0.9 * vals.size
     run_and_compare(case)
+
+
+# ---- W stored [k][n] (transpose_b = 0; MatmulFusedPartialRMSNorm page, Parameters) ----
+
+@pytest.mark.parametrize("small", [True, False])
+def test_w_stored_k_by_n_bench_shape(small):
+    run_and_compare(sc.gemv_norm(small=small, transpose_b=False))
+
+
+@pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+def test_w_stored_k_by_n_rows_dtypes_and_ragged_sizes(dtype, m):
+    # k-chunks over two rounds of the 256 threads and a ragged third; n not a
+    # multiple of the 16-column unit, W rows padded
+    E = 4 if dtype == sc.F32 else 8
+    k = E * (256 * 2 + 5)
+    case = sc.make_gemv_case(f"t_rows_{dtype}_{m}", 70 + m, dtype, m=m, k=k, n=333, n_normed=201,
+                             epsilon=1e-5, x_pad=E, w_pad=3 * E - 333 % E, out_pad=3,
+                             transpose_b=False)
+    run_and_compare(case)
+
+
+@pytest.mark.parametrize("n,w_pad", [(150, 2), (16, 0), (1, 7), (8, 0), (17, 7)])
+def test_w_stored_k_by_n_last_unit_at_the_row_end(n, w_pad):
+    # the last unit's second column chunk starts at or past the row stride
+    # (n = 150, stride 152; n = 1, stride 8): it is not read
+    case = sc.make_gemv_case(f"t_end_{n}", 80 + n, sc.BF16, m=1, k=512, n=n,
+                             n_normed=min(n, 5), w_pad=w_pad, transpose_b=False)
+    assert case.w.shape[1] % 8 == 0
+    run_and_compare(case)
+
+
+@pytest.mark.parametrize("m", [2, 8])
+def test_w_stored_k_by_n_rows_match_single_row_calls(m):
+    gh, _ = _gpu()
+    mk = lambda: sc.make_gemv_case("t_rows", 90, sc.BF16, m=m, k=2048, n=500, n_normed=300,
+                                   w_pad=4, transpose_b=False)
+    case = mk()
+    dg = gh.upload_gemv(case)
+    gh.run_gemv(dg)
+    for i in range(m):
+        one = mk()
+        one.m, one.x = 1, case.x[i:i + 1]
+        d1 = gh.upload_gemv(one)
+        gh.run_gemv(d1)
+        torch.cuda.synchronize()
+        assert torch.equal(d1.normed[0], dg.normed[i]), i
+        assert torch.equal(d1.unnormed[0], dg.unnormed[i]), i
+
+
+def test_w_stored_k_by_n_nothing_normed_and_k_zero():
+    run_and_compare(sc.make_gemv_case("t_nonorm", 91, sc.BF16, m=2, k=512, n=300, n_normed=0,
+                                      w_pad=4, transpose_b=False), no_workspace=True)
+    case = sc.make_gemv_case("t_k0", 92, sc.F32, m=2, k=0, n=10, n_normed=4, epsilon=1e-3,
+                             x_pad=4, w_pad=2, transpose_b=False)
+    # k = 0: W has no rows; keep the buffer non-empty (a real device address)
+    case.w = np.full((1, 12), sc.SENTINEL[sc.F32], dtype=case.w.dtype)
+    dg, _ = run_and_compare(case)
+    gh, _ = _gpu()
+    assert np.all(gh.to_numpy_bits(dg.normed, sc.F32)[:, :4] == 0)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_w_stored_k_by_n_random_shapes(i):
+    rng = np.random.default_rng([4111, i])
+    dtype = (sc.F32, sc.BF16, sc.F16)[int(rng.integers(3))]
+    E = 4 if dtype == sc.F32 else 8
+    m = int(rng.integers(1, 9))
+    k = E * int(rng.integers(1, 700))
+    n = int(rng.integers(1, 3000))
+    nn = int(rng.choice([0, n, int(rng.integers(0, n + 1))]))
+    case = sc.make_gemv_case(f"t_rand_{i}", 700 + i, dtype, m=m, k=k, n=n, n_normed=nn,
+                             epsilon=float(rng.choice([1e-6, 1e-3])),
+                             x_pad=E * int(rng.integers(0, 3)),
+                             w_pad=(-n) % E + E * int(rng.integers(0, 3)),
+                             out_pad=int(rng.integers(0, 3)), transpose_b=False)
+    run_and_compare(case, no_workspace=nn == 0)
