@@ -303,9 +303,9 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
  * product per pair of terms for QRP_BF16 and QRP_F16 (both products exact,
  * so at most one rounding per term) -- then a fixed 64-way tree adds the
  * lanes.  With W stored [k][n] a block of 256 threads computes a group of
- * columns, each thread adding every 256th 16-byte k-chunk's terms in k order
- * (one fused multiply-add per term), then the 64-way tree in each wave and
- * the four wave sums in order.  With W stored [k][n], n times the element
+ * columns, thread t adding the terms of rows t, t + 256, ... in k order (one
+ * fused multiply-add per term), then the 64-way tree in each wave and the
+ * four wave sums in order.  With W stored [k][n], n times the element
  * size need not be a multiple of 16 bytes, but the row stride must.  The norm
  * is binary32 (a row's sum of squares over 256 threads in a fixed order),
  * and each output is rounded once to dtype (QRP_F32, QRP_BF16 or QRP_F16;

@@ -145,6 +145,12 @@ __device__ __forceinline__ float bits_value(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
+// element i of a dtype array, widened (exact)
+template <int DT>
+__device__ __forceinline__ float load_elem_bits(const void* base, uint32_t i) {
+  return bits_value<DT>(load_bits<DT>(base, (int64_t)i));
+}
+
 // The norm is done by the first 256 threads (four waves, present in every
 // launch) of the last block; each holds up to kNormHeld of a row's y values
 // and gammas, so a row of up to 2048 normed columns is read in one round.
@@ -440,19 +446,18 @@ __global__ void __launch_bounds__(64 * kGemvMaxWaves) gemv_norm_kernel(const Gem
 // now holds many columns, so a wave cannot stream one column's k values
 // contiguously.  Instead a block of 256 threads owns a unit of TP 16-byte
 // column chunks (TP * E columns) over the whole of k: thread t takes the
-// k-chunks q = t, t + 256, ... (E rows each) and loads, for each of its
-// rows, the unit's 16 bytes of that row, plus the E x values of the
-// k-chunk for every input row.  Each access is 16 bytes of a different
-// line; the line's other chunks belong to neighbouring units, which the
+// rows t, t + 256, t + 512, ... and loads, for each, the unit's 16 bytes
+// of that row and the row's x value of every input row (a wave's load
+// instruction covers 64 consecutive rows).  Each W access is 16 bytes of a
+// different line; the line's other chunks belong to neighbouring units, which the
 // grid places on the same XCD at the same time (unit u on XCD u / per), so
 // the L2 serves them and HBM sees each line once -- the loads are ordinary
 // ones, so that the lines stay in the L2.
 //
-// Summation order per column: thread t adds its k-chunks in k order, each
-// chunk's E terms in k order (one fused multiply-add per term: every
-// product of two binary32-or-narrower values is exact in binary32, so each
-// term rounds once), then the butterfly over its wave's 64 lanes, then the
-// four wave sums in wave order -- fixed, and the same for every row count.
+// Summation order per column: thread t adds its rows' terms in k order
+// (one fused multiply-add per term, so each term rounds once), then the
+// butterfly over its wave's 64 lanes, then the four wave sums in wave
+// order -- fixed, and the same for every row count.
 // The partial norm is the one of the [n][k] kernel: one arrival per block
 // holding a normed column, and the last block normalises.
 template <int DT, int MB, int TP, int UT>
@@ -479,51 +484,44 @@ __global__ void __launch_bounds__(256) gemv_norm_t_kernel(const GemvArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[m][c] = 0.f;
 
+  // thread t takes rows t, t + 256, t + 512, ...: a wave's load instruction
+  // reads 64 consecutive rows, so its addresses stay close together
   const gv4u zero = {0u, 0u, 0u, 0u};
-  const uint32_t kc = a.kc;
-  for (uint32_t base = 0; base < kc; base += 256u * UT) {
-    gv4u wv[UT][E][TP], xv[UT][MB];
+  const uint32_t k = a.kc * (uint32_t)E;
+  constexpr int RT = UT * E;  // rows per thread per round
+  for (uint32_t base = 0; base < k; base += 256u * RT) {
+    gv4u wv[RT][TP];
+    float xs[RT][MB];
 #pragma unroll
-    for (int u = 0; u < UT; ++u) {
-      const uint32_t q = base + (uint32_t)u * 256u + t;
-      const bool in = q < kc;
-      const uint32_t qc = in ? q : 0u;
+    for (int i = 0; i < RT; ++i) {
+      const uint32_t row = base + (uint32_t)i * 256u + t;
+      const bool in = row < k;
+      const uint32_t rc = in ? row : 0u;
 #pragma unroll
-      for (int r = 0; r < E; ++r)
-#pragma unroll
-        for (int p = 0; p < TP; ++p) {
-          // a chunk past the row's stride (the last unit of a ragged n) is
-          // never read: its columns are never stored
-          const bool inp = in && n0 + (uint32_t)(p * E) < (uint64_t)a.w_stride;
-          wv[u][r][p] = inp ? *reinterpret_cast<const gv4u*>(wcol + (int64_t)(qc * E + r) * wrow +
-                                                             p * 16)
-                            : zero;
-        }
+      for (int p = 0; p < TP; ++p) {
+        // a chunk past the row's stride (the last unit of a ragged n) is
+        // never read: its columns are never stored
+        const bool inp = in && n0 + (uint32_t)(p * E) < (uint64_t)a.w_stride;
+        wv[i][p] = inp ? *reinterpret_cast<const gv4u*>(wcol + (int64_t)rc * wrow + p * 16) : zero;
+      }
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        const uint32_t row = min((uint32_t)m, a.m - 1);
-        xv[u][m] = in ? *reinterpret_cast<const gv4u*>(xb + (int64_t)row * xrow + (int64_t)qc * 16)
-                      : zero;
+        const uint32_t xr = min((uint32_t)m, a.m - 1);
+        xs[i][m] = in ? load_elem_bits<DT>(xb + (int64_t)xr * xrow, rc) : 0.f;
       }
     }
 #pragma unroll
-    for (int u = 0; u < UT; ++u) {
+    for (int i = 0; i < RT; ++i) {
+      float wf[TP][E];
 #pragma unroll
-      for (int r = 0; r < E; ++r) {
-        float wf[TP][E];
+      for (int p = 0; p < TP; ++p) widen<DT>(wv[i][p], wf[p]);
 #pragma unroll
-        for (int p = 0; p < TP; ++p) widen<DT>(wv[u][r][p], wf[p]);
+      for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          float xf[E];
-          widen<DT>(xv[u][m], xf);
+        for (int p = 0; p < TP; ++p)
 #pragma unroll
-          for (int p = 0; p < TP; ++p)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-              acc[m][p * E + e] = __builtin_fmaf(xf[r], wf[p][e], acc[m][p * E + e]);
-        }
-      }
+          for (int e = 0; e < E; ++e)
+            acc[m][p * E + e] = __builtin_fmaf(xs[i][m], wf[p][e], acc[m][p * E + e]);
     }
   }
 

@@ -11,10 +11,10 @@ rounds at most once per term) -- and then adds the 64 partial sums in a
 gamma_n = n u / (1 - n u) times the sum of the terms' magnitudes, so
     |y^ - y| <= D_j = gamma_{n_l + 6} * A_j,    A_j = sum_k |x_k w_jk|,
 with y the oracle's exact sum.  With W stored [k][n] (transpose_b = 0) a
-block of 256 threads computes a column: each thread adds the E terms of
-every 256th 16-byte k-chunk in k order, one fused multiply-add per term
-(n_l = ceil(kc / 256) * E), then the 6-level butterfly and the four wave
-sums (3 more adds): D_j = gamma_{n_l + 9} * A_j.  A passed-through output
+block of 256 threads computes a column: thread t adds the terms of rows
+t, t + 256, ... in k order, one fused multiply-add per term
+(n_l = ceil(k / 256)), then the 6-level butterfly and the four wave sums
+(3 more adds): D_j = gamma_{n_l + 9} * A_j.  A passed-through output
 is y^ rounded to the dtype, the oracle's is y rounded: they differ by at
 most D_j plus one ulp of the larger.
 
@@ -63,7 +63,7 @@ def bounds(case, res):
     if getattr(case, "transpose_b", 1):
         D = _gamma(-(-kc // 64) * E + 6) * res.abs_dot       # [m, n]
     else:
-        D = _gamma(-(-kc // 256) * E + 9) * res.abs_dot
+        D = _gamma(-(-case.k // 256) + 9) * res.abs_dot
     nn = case.n_normed
     un_tol = 1.01 * D[:, nn:]
     if nn == 0:
