@@ -316,7 +316,8 @@ def test_w_stored_k_by_n_nothing_normed_and_k_zero():
     assert np.all(gh.to_numpy_bits(dg.normed, sc.F32)[:, :4] == 0)
 
 
-@pytest.mark.parametrize("i", range(12))
+# QRP_RANDOM_CASES sets twice the count here
+@pytest.mark.parametrize("i", range(int(os.environ.get("QRP_RANDOM_CASES", "24")) // 2))
 def test_w_stored_k_by_n_random_shapes(i):
     rng = np.random.default_rng([4111, i])
     dtype = (sc.F32, sc.BF16, sc.F16)[int(rng.integers(3))]
