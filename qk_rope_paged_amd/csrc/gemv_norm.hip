@@ -405,7 +405,8 @@ __global__ void __launch_bounds__(64 * kGemvMaxWaves) gemv_norm_kernel(const Gem
   if constexpr (XL) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
-      for (uint32_t c = threadIdx.x; c < a.kc; c += blockDim.x) x_lds[m * a.kc + c] = xrow_chunk<DT>(a, m, c);
+      for (uint32_t c = threadIdx.x; c < a.kc; c += blockDim.x)
+        x_lds[m * a.kc + c] = xrow_chunk<DT>(a, m, c);
     __syncthreads();
   }
 
