@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define QRP_ABI_VERSION 6
+#define QRP_ABI_VERSION 7
 
 typedef enum qrp_status {
   QRP_OK = 0,
@@ -302,11 +302,14 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
  * order -- one fused multiply-add per term for QRP_F32, one packed dot
  * product per pair of terms for QRP_BF16 and QRP_F16 (both products exact,
  * so at most one rounding per term) -- then a fixed 64-way tree adds the
- * lanes.  With W stored [k][n] a block of 256 threads computes a group of
- * columns, thread t adding the terms of rows t, t + 256, ... in k order (one
- * fused multiply-add per term), then the 64-way tree in each wave and the
- * four wave sums in order.  With W stored [k][n], n times the element
- * size need not be a multiple of 16 bytes, but the row stride must.  The norm
+ * lanes.  With W stored [k][n] the columns are cut into tiles of 128 bytes
+ * of a row and k into slices (their count depends on n, k, the dtype and
+ * the device's compute-unit count, never on m); for each tile and slice,
+ * 512 threads each add the terms of 8 consecutive rows of every 512 in k
+ * order (one fused multiply-add per term), then a fixed 8-way tree, the 8
+ * wave sums in order, and the slices' sums in slice order.  With W stored
+ * [k][n], n times the element size need not be a multiple of 16 bytes, but
+ * the row stride must.  The norm
  * is binary32 (a row's sum of squares over 256 threads in a fixed order),
  * and each output is rounded once to dtype (QRP_F32, QRP_BF16 or QRP_F16;
  * x, W, gamma and both outputs share it).
@@ -318,11 +321,13 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
  * input/weight strides are multiples of 16 bytes (QRP_EALIGN otherwise);
  * outputs and gamma are element-aligned.
  * Workspace: device memory the caller owns, at least
- * qrp_gemv_norm_workspace_bytes(m, n_normed) bytes (0 when n_normed = 0:
- * NULL is then allowed): a 256-byte arrival counter line, then
- * 4 * m * n_normed bytes of binary32 y values.  It must be zero-filled before
- * its first use; every call leaves its counter at zero again, so it is
- * reused without clearing.
+ * qrp_gemv_norm_workspace_bytes(m, n_normed, transpose_b) bytes: 1280 bytes
+ * of arrival counters, then 4 * m * n_normed bytes of binary32 y values, and
+ * with W stored [k][n] (transpose_b = 0), from the next 256-byte boundary,
+ * 65536 * m bytes of binary32 partial sums of the k slices.  With W stored
+ * [n][k] and n_normed = 0 the size is 0 and NULL is allowed.  It must be
+ * zero-filled before its first use; every call leaves its counters at zero
+ * again, so it is reused without clearing.
  * Calls that overlap in time must not share a workspace.
  * The summation order is fixed, so results are the same bits on every call
  * and for every row count (a row gives the same outputs alone or among 8).
@@ -333,7 +338,7 @@ int32_t fused_qk_rope_bshd_continuous_batch(const void* q_proj, int32_t dtype, u
  * 0).  m == 0 or n == 0 returns
  * QRP_OK without a launch; k == 0 gives y = 0.
  */
-uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed);
+uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed, int32_t transpose_b);
 
 int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_stride,
                                      void* unnormed_output, uint64_t unnormed_row_stride,
@@ -349,14 +354,15 @@ int32_t matmul_fused_partial_rmsnorm(void* normed_output, uint64_t normed_row_st
  * memory: code being captured into a HIP graph, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments, results and errors
  * (the same kernel, bit for bit) without the workspace: the scratch is the
- * library's own, a device array of 256 + 4 * 131072 bytes that each GPU
- * the library runs on holds until the process ends.  It serves
- * m * n_normed <= 131072 (m rows of up to 131072 / m normed columns);
+ * library's own, a device array of 1280 + 4 * 131072 + 8 * 65536 bytes
+ * (1 MiB and 1280 bytes) that each GPU the library runs on holds until the
+ * process ends.  It serves m * n_normed <= 131072 (m rows of up to
+ * 131072 / m normed columns);
  * larger calls return QRP_EINVAL and go through the workspace form.  The
  * first call on a device (the device current on the calling thread, which
  * must be the stream's) looks the array up and clears its counter with a
  * kernel on `stream`; no call allocates or frees memory.  Every call on a
- * GPU shares that GPU's array, and each call leaves its counter at zero:
+ * GPU shares that GPU's array, and each call leaves its counters at zero:
  * calls that overlap in time on one GPU (other streams, other threads)
  * race and give wrong results; order them on one stream or use the
  * workspace form.

@@ -103,7 +103,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = I32
     lib.qrp_last_error.argtypes = []
     lib.qrp_last_error.restype = ctypes.c_char_p
-    lib.qrp_gemv_norm_workspace_bytes.argtypes = [U32, U32]
+    lib.qrp_gemv_norm_workspace_bytes.argtypes = [U32, U32, I32]
     lib.qrp_gemv_norm_workspace_bytes.restype = U64
     lib.qrp_abi_version.argtypes = []
     lib.qrp_abi_version.restype = I32
@@ -336,8 +336,8 @@ def fused_qk_rope_bshd_continuous_batch(q_proj, dtype: int, batch_size: int, seq
     return _call(lib.fused_qk_rope_bshd_continuous_batch, args, [cc, rc], raise_on_error, prepare)
 
 
-def gemv_norm_workspace_bytes(m: int, n_normed: int) -> int:
-    return int(lib.qrp_gemv_norm_workspace_bytes(m, n_normed))
+def gemv_norm_workspace_bytes(m: int, n_normed: int, transpose_b: int = 1) -> int:
+    return int(lib.qrp_gemv_norm_workspace_bytes(m, n_normed, transpose_b))
 
 
 def matmul_fused_partial_rmsnorm(normed_output, normed_row_stride: int, unnormed_output,
@@ -347,7 +347,8 @@ def matmul_fused_partial_rmsnorm(normed_output, normed_row_stride: int, unnormed
                                  workspace, workspace_bytes: int, transpose_b: int = 1,
                                  stream=None, raise_on_error: bool = True, prepare: bool = False):
     """The fused GEMV + partial RMSNorm; `workspace` is a zero-filled device
-    buffer of at least gemv_norm_workspace_bytes(m, n_normed) bytes."""
+    buffer of at least gemv_norm_workspace_bytes(m, n_normed, transpose_b)
+    bytes."""
     args = (_ptr(normed_output), normed_row_stride, _ptr(unnormed_output), unnormed_row_stride,
             _ptr(input), input_row_stride, m, _ptr(weight), weight_row_stride, n, k, _ptr(gamma),
             n_normed, epsilon, weight_offset, dtype, transpose_b, _ptr(workspace),

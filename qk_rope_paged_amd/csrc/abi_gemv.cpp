@@ -19,9 +19,9 @@ bool dtype_ok(int32_t dt) { return dt == QRP_F32 || dt == QRP_BF16 || dt == QRP_
 
 }  // namespace
 
-extern "C" uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed) {
-  if (n_normed == 0) return 0;
-  return qrp::kGemvCounterBytes + 4ull * m * n_normed;
+extern "C" uint64_t qrp_gemv_norm_workspace_bytes(uint32_t m, uint32_t n_normed,
+                                                  int32_t transpose_b) {
+  return qrp::gemv_workspace_bytes(m, n_normed, transpose_b != 0);
 }
 
 namespace {
@@ -44,8 +44,12 @@ int32_t gemv_call(void* normed_output, uint64_t normed_row_stride, void* unnorme
   if (m == 0 || n == 0) return QRP_OK;
   if (n >= (1u << 31)) return qrp::set_error(QRP_EINVAL, "n >= 2^31 columns in one launch");
   if (!input || !weight) return qrp::set_error(QRP_EINVAL, "input / weight is NULL");
-  if (n_normed && (!gamma || !normed_output || (!workspace && !no_alloc)))
-    return qrp::set_error(QRP_EINVAL, "gamma, normed_output and workspace are needed when n_normed > 0");
+  if (n_normed && (!gamma || !normed_output))
+    return qrp::set_error(QRP_EINVAL, "gamma and normed_output are needed when n_normed > 0");
+  const uint64_t ws_need = qrp::gemv_workspace_bytes(m, n_normed, transpose_b != 0);
+  if (ws_need && !workspace && !no_alloc)
+    return qrp::set_error(QRP_EINVAL, transpose_b ? "workspace is needed when n_normed > 0"
+                                                  : "workspace is needed with W stored [k][n]");
   if (n_normed < n && !unnormed_output)
     return qrp::set_error(QRP_EINVAL, "unnormed_output is NULL with columns past n_normed");
   const uint32_t ce = chunk_elems(dtype);
@@ -71,14 +75,15 @@ int32_t gemv_call(void* normed_output, uint64_t normed_row_stride, void* unnorme
                                             std::to_string(qrp::kGemvScratchFloats) +
                                             " values); use matmul_fused_partial_rmsnorm");
     workspace = nullptr;
-    if (n_normed) {
+    if (ws_need) {
       const int e = qrp::gemv_scratch(&workspace, stream);
       if (e != 0)
         return qrp::set_error(QRP_EHIP, std::string("scratch set-up failed: ") +
                                             hipGetErrorString(static_cast<hipError_t>(e)));
     }
-  } else if (workspace_bytes < qrp_gemv_norm_workspace_bytes(m, n_normed)) {
-    return qrp::set_error(QRP_EINVAL, "workspace smaller than qrp_gemv_norm_workspace_bytes(m, n_normed)");
+  } else if (workspace_bytes < ws_need) {
+    return qrp::set_error(QRP_EINVAL,
+                          "workspace smaller than qrp_gemv_norm_workspace_bytes(m, n_normed, transpose_b)");
   }
 
   qrp::GemvArgs a{};
@@ -87,10 +92,13 @@ int32_t gemv_call(void* normed_output, uint64_t normed_row_stride, void* unnorme
   a.gamma = gamma;
   a.normed = normed_output;
   a.unnormed = unnormed_output;
-  a.counter = static_cast<uint32_t*>(workspace);
-  a.ybuf = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                qrp::kGemvCounterBytes)
-                     : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.counter = reinterpret_cast<uint32_t*>(ws);
+  a.tile_counter = ws ? reinterpret_cast<uint32_t*>(ws + qrp::kGemvTileCounterOffset) : nullptr;
+  a.ybuf = ws ? reinterpret_cast<float*>(ws + qrp::kGemvCounterBytes) : nullptr;
+  a.partials = ws && !transpose_b
+                   ? reinterpret_cast<float*>(ws + qrp::gemv_partials_offset(m, n_normed))
+                   : nullptr;
   a.x_stride = (int64_t)input_row_stride;
   a.w_stride = (int64_t)weight_row_stride;
   a.normed_stride = (int64_t)normed_row_stride;

@@ -151,6 +151,22 @@ __device__ __forceinline__ float load_elem_bits(const void* base, uint32_t i) {
   return bits_value<DT>(load_bits<DT>(base, (int64_t)i));
 }
 
+// y values of row r, column j (< n_normed): from the workspace, stored by
+// other compute units ...
+struct YFromWorkspace {
+  const float* y;
+  uint32_t nn;
+  __device__ float operator()(uint32_t r, uint32_t j) const {
+    return load_y(y + (uint64_t)r * nn + j);
+  }
+};
+// ... or from this block's LDS
+struct YFromLds {
+  const float* y;
+  uint32_t nn;
+  __device__ float operator()(uint32_t r, uint32_t j) const { return y[r * nn + j]; }
+};
+
 // The norm is done by the first 256 threads (four waves, present in every
 // launch) of the last block; each holds up to kNormHeld of a row's y values
 // and gammas, so a row of up to 2048 normed columns is read in one round.
@@ -170,8 +186,8 @@ constexpr int kNormHeld = 8;
 // after every load has been issued, and with up to 2048 normed columns all
 // the rows' y values and the gammas (shared by the rows) are read in one
 // round before any is used.
-template <int DT, int MB>
-__device__ void norm_rows(const GemvArgs& a) {
+template <int DT, int MB, class Y>
+__device__ void norm_rows(const GemvArgs& a, const Y& y_at) {
   __shared__ float wave_part[MB][kNormThreads / 64];
   const uint32_t t = threadIdx.x;
   const bool worker = t < kNormThreads;  // wave-uniform
@@ -188,7 +204,7 @@ __device__ void norm_rows(const GemvArgs& a) {
 #pragma unroll
         for (int r = 0; r < MB; ++r) {
           const uint32_t rc = min((uint32_t)r, a.m - 1);
-          v[r][i] = load_y(a.ybuf + (uint64_t)rc * nn + jc);
+          v[r][i] = y_at(rc, jc);
         }
       }
 #pragma unroll
@@ -226,14 +242,13 @@ __device__ void norm_rows(const GemvArgs& a) {
   }
   // longer rows: one row at a time, kNormHeld columns per thread per round
   for (uint32_t r = 0; r < a.m; ++r) {
-    const float* yr = a.ybuf + (uint64_t)r * nn;
     float ss = 0.f;
     if (worker) {
       for (uint32_t base = 0; base < nn; base += kNormThreads * (uint32_t)kNormHeld) {
         float v[kNormHeld];
 #pragma unroll
         for (int i = 0; i < kNormHeld; ++i)
-          v[i] = load_y(yr + min(base + t + kNormThreads * (uint32_t)i, nn - 1));
+          v[i] = y_at(r, min(base + t + kNormThreads * (uint32_t)i, nn - 1));
 #pragma unroll
         for (int i = 0; i < kNormHeld; ++i) {
           const float x = base + t + kNormThreads * (uint32_t)i < nn ? v[i] : 0.f;
@@ -254,7 +269,7 @@ __device__ void norm_rows(const GemvArgs& a) {
 #pragma unroll
         for (int i = 0; i < kNormHeld; ++i) {
           const uint32_t jc = min(base + t + kNormThreads * (uint32_t)i, nn - 1);
-          v[i] = load_y(yr + jc);
+          v[i] = y_at(r, jc);
           gb[i] = load_bits<DT>(a.gamma, jc);
         }
 #pragma unroll
@@ -440,156 +455,271 @@ __global__ void __launch_bounds__(64 * kGemvMaxWaves) gemv_norm_kernel(const Gem
   __syncthreads();  // block_last is set
   if (!block_last) return;  // block-uniform
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  norm_rows<DT, MB>(a);
+  norm_rows<DT, MB>(a, YFromWorkspace{a.ybuf, a.n_normed});
 }
 
 // W stored [k][n] (transpose_b = 0): y_j = sum_k x_k W[k][j].  A row of W
-// now holds many columns, so a wave cannot stream one column's k values
-// contiguously.  Instead a block of 256 threads owns a unit of TP 16-byte
-// column chunks (TP * E columns) over the whole of k: thread t takes the
-// rows t, t + 256, t + 512, ... and loads, for each, the unit's 16 bytes
-// of that row and the row's x value of every input row (a wave's load
-// instruction covers 64 consecutive rows).  Each W access is 16 bytes of a
-// different line; the line's other chunks belong to neighbouring units, which the
-// grid places on the same XCD at the same time (unit u on XCD u / per), so
-// the L2 serves them and HBM sees each line once -- the loads are ordinary
-// ones, so that the lines stay in the L2.
+// holds many columns, so a column's k values lie a row apart.  A compute
+// unit issues only about one line request every 8 cycles (measured), so
+// every request should bring a whole 128-byte line: the columns are cut
+// into tiles of 128 bytes of a row (64 bf16 or f16 columns, 32 fp32), and 8
+// lanes read one row's tile, 16 bytes each.  A tile is narrow, so k is cut
+// too: block b takes tile b % tiles and slice b / tiles of split_rows rows
+// of k, and the chip streams W with whole lines from every compute unit.
 //
-// Summation order per column: thread t adds its rows' terms in k order
-// (one fused multiply-add per term, so each term rounds once), then the
-// butterfly over its wave's 64 lanes, then the four wave sums in wave
-// order -- fixed, and the same for every row count.
-// The partial norm is the one of the [n][k] kernel: one arrival per block
-// holding a normed column, and the last block normalises.
-template <int DT, int MB, int TP, int UT>
-__global__ void __launch_bounds__(256) gemv_norm_t_kernel(const GemvArgs a) {
-  constexpr int E = chunk_elems<DT>();
-  constexpr int NC = TP * E;  // columns per unit
-  const uint32_t t = threadIdx.x;
-  const uint32_t lane = t & 63u;
-  const uint32_t w = t >> 6;
-  // blocks are dealt to the XCDs in turn (block b on XCD b % 8): XCD x takes
-  // units [x * per, (x + 1) * per), so neighbouring units share its L2
-  const uint32_t unit = (blockIdx.x % 8u) * a.units_per_xcd + blockIdx.x / 8u;
-  if (unit >= a.n_groups) return;  // block-uniform, before any barrier
-  const uint32_t n0 = unit * NC;
-  const int64_t es = 16 / E;  // element bytes
-  const char* wcol = reinterpret_cast<const char*>(a.w) + (int64_t)n0 * es;
-  const int64_t wrow = a.w_stride * es;
-  const char* xb = reinterpret_cast<const char*>(a.x);
-  const int64_t xrow = a.x_stride * es;
+// In a block of 512 threads, thread t reads chunk t % 8 of the tile and
+// belongs to row group t / 8 (64 groups); each round a group takes RG
+// consecutive rows (the block RG * 64), loading RG chunks of W and, for each
+// x row, the x values of those rows as whole 16-byte chunks.  Per column the
+// sum runs: each thread's terms in k order (one fused multiply-add per
+// term), the xor butterfly over its wave's 8 groups, the 8 wave sums in wave
+// order, then the slices' sums in slice order.  The order is fixed by the
+// sizes and the slice count, which depends on n, k, the dtype and the
+// device's compute-unit count, not on the row count: a row gives the same
+// bits alone or among others.
+//
+// With k cut, each block stores its sums in the workspace and releases
+// them.  Normally it then takes a ticket from its tile's counter (an
+// increment that wraps to zero); the tile's last block acquires and adds
+// the slices' sums, and, as in the [n][k] kernel, each tile holding normed
+// columns stores its y values, releases them and arrives once at the norm's
+// counter; the last one normalises every row.  When the normed columns'
+// slice sums are few, the blocks of normed tiles take their ticket from the
+// norm's counter at once (single arrival), and the last of them adds every
+// normed column's slices itself (in the same order) before normalising;
+// only tiles with passed-through columns still meet at their own counter.
+// Without k cut, a block's sums are y itself.
+constexpr uint32_t kTileLanes = 8;  // lanes reading one row's tile (128 bytes)
+constexpr uint32_t kTWaves = 8;     // waves per block
+constexpr uint32_t kTGroups = kTWaves * 64 / kTileLanes;  // row groups per block
 
-  float acc[MB][NC];
+// 16-byte chunk v, element i, widened (exact)
+template <int DT>
+__device__ __forceinline__ float chunk_elem(const gv4u v, int i) {
+  if constexpr (DT == QRP_F32) {
+    return __uint_as_float(v[i]);
+  } else if constexpr (DT == QRP_BF16) {
+    return __uint_as_float((i & 1) ? (v[i >> 1] & 0xFFFF0000u) : (v[i >> 1] << 16));
+  } else {
+    const gh2 h = __builtin_bit_cast(gh2, (uint32_t)v[i >> 1]);
+    return (float)((i & 1) ? h.y : h.x);
+  }
+}
+
+// With the single arrival (few slice sums in all), the last block to arrive
+// adds the slices of every normed column in slice order -- the same sums
+// as a tile's last block makes -- into LDS, and normalises from there.  Each
+// thread takes every 512th (row, column) pair; the loads of four pairs and
+// four slices are issued together.
+constexpr uint32_t kGemvSingleMaxY = 8192;         // m * n_normed held in LDS
+constexpr uint32_t kGemvSingleMaxSlices = 16384;  // k_splits * m * n_normed read
+
+template <int DT, int MB>
+__device__ void norm_from_slices(const GemvArgs& a) {
+  constexpr uint32_t CT = kTileLanes * chunk_elems<DT>();
+  constexpr uint32_t NT = 64 * kTWaves;
+  __shared__ float y_lds[kGemvSingleMaxY];
+  const uint32_t t = threadIdx.x;
+  const uint32_t nn = a.n_normed, total = a.m * nn, S = a.k_splits;
+  const uint64_t slice_stride = (uint64_t)a.m * CT;
+  for (uint32_t base = t; base < total; base += 4 * NT) {
+    const float* src[4];
+#pragma unroll
+    for (uint32_t h = 0; h < 4; ++h) {
+      const uint32_t idx = min(base + h * NT, total - 1);
+      const uint32_t r = idx / nn, j = idx % nn;
+      src[h] = a.partials + ((uint64_t)(j / CT) * S * a.m + r) * CT + j % CT;
+    }
+    float y[4];
+    for (uint32_t s0 = 0; s0 < S; s0 += 4) {
+      float v[4][4];
+#pragma unroll
+      for (uint32_t h = 0; h < 4; ++h)
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i) v[h][i] = load_y(src[h] + min(s0 + i, S - 1) * slice_stride);
+#pragma unroll
+      for (uint32_t h = 0; h < 4; ++h)
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i)
+          if (s0 + i < S) y[h] = (s0 + i == 0) ? v[h][i] : y[h] + v[h][i];
+    }
+#pragma unroll
+    for (uint32_t h = 0; h < 4; ++h)
+      if (base + h * NT < total) y_lds[base + h * NT] = y[h];
+  }
+  __syncthreads();
+  norm_rows<DT, MB>(a, YFromLds{y_lds, nn});
+}
+
+template <int DT, int MB, int RG>
+__global__ void __launch_bounds__(64 * kTWaves) gemv_norm_t_kernel(const GemvArgs a) {
+  constexpr int E = chunk_elems<DT>();
+  constexpr uint32_t CT = kTileLanes * E;  // columns per tile
+  constexpr int XC = RG / E;               // x chunks per row group and x row
+  static_assert(RG % 8 == 0 && MB * CT <= 64 * kTWaves, "tile shape");
+  const uint32_t t = threadIdx.x;
+  const uint32_t w = t >> 6;
+  const uint32_t p = t & (kTileLanes - 1u);
+  const uint32_t grp = t / kTileLanes;
+  const uint32_t tile = blockIdx.x % a.n_groups;
+  const uint32_t split = blockIdx.x / a.n_groups;
+  const uint32_t n0 = tile * CT;
+  const int64_t es = 16 / E;  // element bytes
+  const uint32_t k = a.kc * (uint32_t)E;
+  const uint32_t kb = split * a.split_rows;
+  const uint32_t ke = min(k, kb + a.split_rows);
+  // a chunk past the row's stride (the last tile of a ragged n) is never
+  // read; one inside it but past n is read and its columns never stored
+  const bool col_in = n0 + p * (uint32_t)E < (uint64_t)a.w_stride;
+  const char* wp = reinterpret_cast<const char*>(a.w) + (int64_t)(n0 + p * E) * es;
+  const int64_t wrow = a.w_stride * es;
+  const char* xp[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+    xp[m] = reinterpret_cast<const char*>(a.x) +
+            (int64_t)min((uint32_t)m, a.m - 1) * a.x_stride * es;
+
+  float acc[MB][E];
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[m][c] = 0.f;
+    for (int e = 0; e < E; ++e) acc[m][e] = 0.f;
 
-  // thread t takes rows t, t + 256, t + 512, ...: a wave's load instruction
-  // reads 64 consecutive rows, so its addresses stay close together
   const gv4u zero = {0u, 0u, 0u, 0u};
-  const uint32_t k = a.kc * (uint32_t)E;
-  constexpr int RT = UT * E;  // rows per thread per round
-  for (uint32_t base = 0; base < k; base += 256u * RT) {
-    gv4u wv[RT][TP];
-    float xs[RT][MB];
+  for (uint32_t base = kb + grp * RG; base < ke; base += kTGroups * RG) {
+    // rows base .. base + RG - 1; k and ke are multiples of E, so each x
+    // chunk (E rows) is wholly inside or wholly past the slice
+    gv4u wv[RG];
+    gv4u xv[MB][XC];
 #pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const uint32_t row = base + (uint32_t)i * 256u + t;
-      const bool in = row < k;
-      const uint32_t rc = in ? row : 0u;
+    for (int i = 0; i < RG; ++i) {
+      const uint32_t r = base + (uint32_t)i;
+      wv[i] = (r < ke && col_in)
+                  ? __builtin_nontemporal_load(reinterpret_cast<const gv4u*>(wp + (int64_t)r * wrow))
+                  : zero;
+    }
 #pragma unroll
-      for (int p = 0; p < TP; ++p) {
-        // a chunk past the row's stride (the last unit of a ragged n) is
-        // never read: its columns are never stored
-        const bool inp = in && n0 + (uint32_t)(p * E) < (uint64_t)a.w_stride;
-        wv[i][p] = inp ? *reinterpret_cast<const gv4u*>(wcol + (int64_t)rc * wrow + p * 16) : zero;
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int c = 0; c < XC; ++c) {
+        const uint32_t r = base + (uint32_t)(c * E);
+        xv[m][c] = r < ke ? *reinterpret_cast<const gv4u*>(xp[m] + (int64_t)r * es) : zero;
       }
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      float wf[E];
+      widen<DT>(wv[i], wf);
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        const uint32_t xr = min((uint32_t)m, a.m - 1);
-        xs[i][m] = in ? load_elem_bits<DT>(xb + (int64_t)xr * xrow, rc) : 0.f;
+        const float xm = chunk_elem<DT>(xv[m][i / E], i % E);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[m][e] = __builtin_fmaf(xm, wf[e], acc[m][e]);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      float wf[TP][E];
-#pragma unroll
-      for (int p = 0; p < TP; ++p) widen<DT>(wv[i][p], wf[p]);
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int p = 0; p < TP; ++p)
-#pragma unroll
-          for (int e = 0; e < E; ++e)
-            acc[m][p * E + e] = __builtin_fmaf(xs[i][m], wf[p][e], acc[m][p * E + e]);
     }
   }
 
-  // each column's 256 thread sums: the butterfly in each wave, then the four
-  // wave sums in order; thread m * NC + c stores (row m, column n0 + c)
-  __shared__ float part[4][MB * NC];
+  // the butterfly over the wave's 8 groups (lanes p, p + 8, ..., p + 56),
+  // then the 8 wave sums in order; thread t < MB * CT holds (row t / CT,
+  // column n0 + t % CT)
+  __shared__ float part[kTWaves][MB * CT];
+  __shared__ uint32_t tile_flag, norm_flag;
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float v = wave_sum(acc[m][c]);
-      if (lane == 0) part[w][m * NC + c] = v;
+    for (int e = 0; e < E; ++e) {
+      float v = acc[m][e];
+      v += __shfl_xor(v, 8, 64);
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if ((t & 63u) < kTileLanes) part[w][m * CT + p * E + e] = v;
     }
   __syncthreads();
-  if (t < (uint32_t)(MB * NC)) {
-    const uint32_t my_row = t / NC, my_col = n0 + t % NC;
-    const float y = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
-    if (my_row < a.m && my_col < a.n) {
-      if (my_col < a.n_normed)
-        __hip_atomic_store(a.ybuf + (uint64_t)my_row * a.n_normed + my_col, y, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      else
-        store_elem<DT>(a.unnormed,
-                       (int64_t)my_row * a.unnormed_stride + (my_col - a.n_normed), y);
-    }
+  const bool holder = t < MB * CT;
+  const uint32_t my_row = t / CT, tc = t % CT, my_col = n0 + tc;
+  float y = 0.f;
+  if (holder) {
+    y = part[0][t];
+#pragma unroll
+    for (uint32_t v = 1; v < kTWaves; ++v) y += part[v][t];
   }
-  if (unit >= a.n_norm_blocks) return;  // block-uniform: no normed column here
 
-  // arrive once per block; the block that draws the last ticket normalises
-  __shared__ uint32_t block_last;
-  __syncthreads();  // every thread's y values are stored
+  const bool normed_tile = tile < a.n_norm_groups;
+  bool norm_last = false;  // this block normalises
+  if (a.k_splits > 1) {
+    // This slice's sums go to the workspace.  Blocks of a tile with
+    // passed-through columns (every tile, without the single arrival) take
+    // a ticket from the tile's counter: the last adds the slices for them.
+    // With the single arrival, blocks of normed tiles also take one from the
+    // norm's counter: the last of all adds the normed columns' slices.
+    const uint64_t slice_stride = (uint64_t)a.m * CT;
+    float* tile_part = a.partials + (uint64_t)tile * a.k_splits * slice_stride;
+    if (holder && my_row < a.m)
+      __hip_atomic_store(tile_part + split * slice_stride + (uint64_t)my_row * CT + tc, y,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool tile_arrives =
+        !a.single_arrival || max(n0, a.n_normed) < min(n0 + CT, a.n);  // passed-through columns
+    const bool norm_arrives = a.single_arrival && normed_tile;
+    __syncthreads();  // every thread's sums are stored
+    if (t == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      tile_flag = tile_arrives && __builtin_amdgcn_atomic_inc32(a.tile_counter + tile,
+                                                                a.k_splits - 1, __ATOMIC_RELAXED,
+                                                                "agent") == a.k_splits - 1;
+      const uint32_t last = a.n_norm_groups * a.k_splits - 1;
+      norm_flag = norm_arrives && __builtin_amdgcn_atomic_inc32(a.counter, last, __ATOMIC_RELAXED,
+                                                                "agent") == last;
+    }
+    __syncthreads();
+    const bool tile_last = tile_flag;  // block-uniform
+    norm_last = norm_flag;
+    if (!tile_last && !norm_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (tile_last && holder && my_row < a.m) {
+      const float* src = tile_part + (uint64_t)my_row * CT + tc;
+      // the slices in order, their loads issued eight at a time
+      y = 0.f;
+      for (uint32_t s0 = 0; s0 < a.k_splits; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i)
+          v[i] = load_y(src + min(s0 + i, a.k_splits - 1) * slice_stride);
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i)
+          if (s0 + i < a.k_splits) y = (s0 + i == 0) ? v[i] : y + v[i];
+      }
+    }
+    if (!tile_last) y = 0.f;  // nothing of this tile is stored below
+  }
+
+  // the tile's outputs: y values of normed columns to the workspace (not
+  // with the single arrival: the normalising block reads the slices),
+  // passed-through columns rounded to the output
+  const bool store_y = a.k_splits == 1 || tile_flag;
+  if (store_y && holder && my_row < a.m && my_col < a.n) {
+    if (my_col >= a.n_normed)
+      store_elem<DT>(a.unnormed, (int64_t)my_row * a.unnormed_stride + (my_col - a.n_normed), y);
+    else if (!a.single_arrival)
+      __hip_atomic_store(a.ybuf + (uint64_t)my_row * a.n_normed + my_col, y, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if (a.single_arrival) {
+    if (norm_last) norm_from_slices<DT, MB>(a);
+    return;
+  }
+  if (!normed_tile) return;  // block-uniform: no normed column here
+
+  // arrive once per tile; the tile that draws the last ticket normalises
+  __syncthreads();  // every thread's y values are stored (and the flags read)
   if (t == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    block_last = __builtin_amdgcn_atomic_inc32(a.counter, a.n_norm_blocks - 1, __ATOMIC_RELAXED,
-                                               "agent") == a.n_norm_blocks - 1;
+    norm_flag = __builtin_amdgcn_atomic_inc32(a.counter, a.n_norm_groups - 1, __ATOMIC_RELAXED,
+                                              "agent") == a.n_norm_groups - 1;
   }
   __syncthreads();
-  if (!block_last) return;  // block-uniform
+  if (!norm_flag) return;  // block-uniform
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  norm_rows<DT, MB>(a);
-}
-
-// The [k][n] launch: one block per unit of TP column chunks, the units of
-// each XCD contiguous.  One chunk per unit (one block per 8 bf16 columns)
-// measured fastest at one row of 7168 into 2112: 26.9 us, against 29.2 with
-// two chunks (half the blocks) and 40-131 us with a unit's chunks spread
-// over 2-8 neighbouring lanes (a quarter to an eighth of the blocks).
-template <int DT, int MB, int TP, int UT>
-int run_t(GemvArgs& a, hipStream_t s) {
-  constexpr uint64_t NC = (uint64_t)TP * chunk_elems<DT>();
-  const uint64_t units = ((uint64_t)a.n + NC - 1) / NC;
-  const uint64_t per = (units + 7) / 8;
-  a.n_groups = (uint32_t)units;
-  a.n_norm_groups = (uint32_t)(((uint64_t)a.n_normed + NC - 1) / NC);
-  a.n_norm_blocks = a.n_norm_groups;  // units [0, n_norm_groups) arrive
-  a.units_per_xcd = (uint32_t)per;
-  hipLaunchKernelGGL((gemv_norm_t_kernel<DT, MB, TP, UT>), dim3((uint32_t)(8 * per)), dim3(256), 0,
-                     s, a);
-  return (int)hipGetLastError();
-}
-
-template <int DT>
-int run_t_rows(GemvArgs& a, hipStream_t s) {
-  if (a.m <= 1) return run_t<DT, 1, 1, 2>(a, s);
-  if (a.m <= 2) return run_t<DT, 2, 1, 2>(a, s);
-  if (a.m <= 4) return run_t<DT, 4, 1, 1>(a, s);
-  return run_t<DT, 8, 1, 1>(a, s);
+  norm_rows<DT, MB>(a, YFromWorkspace{a.ybuf, a.n_normed});
 }
 
 // Largest LDS copy of the x rows (more rows go through global memory); 1 KB
@@ -614,6 +744,63 @@ int device_cus(uint32_t* out) {
   }
   *out = g_cu_count[dev];
   return 0;
+}
+
+// Bytes of W each block of a [k][n] launch streams (the slice count).
+constexpr uint64_t kGemvTSliceBytes = 256 * 1024;
+
+// The [k][n] launch: tiles x slices blocks.  With fewer tiles than compute
+// units, k is cut into slices of about kGemvTSliceBytes of W each, with at
+// most one block per compute unit and at least one round of a block's row
+// groups per slice; the slice length is a multiple of 8 rows.  Every block
+// arrives once (a release and an increment, about 1.2 us measured), so
+// fewer, longer slices can finish sooner: at one row of 7168 into 2112 (33
+// tiles), 4 slices of 1792 rows took 13.2 us, against 13.6 with 5, 14.6
+// with 7 and 14.5 with 3.  When the normed columns' slice sums are few
+// (kGemvSingleMaxY, kGemvSingleMaxSlices) the blocks of normed tiles arrive
+// at the norm's counter directly; otherwise each tile's last block adds its
+// slices first and arrives in its turn, one more release and increment in
+// the chain (17.6 us instead of 13.2 at the shape above).
+template <int DT, int MB, int RG>
+int run_t(GemvArgs& a, hipStream_t s) {
+  uint32_t cus = 0;
+  const int e = device_cus(&cus);
+  if (e != 0) return e;
+  constexpr uint64_t E = chunk_elems<DT>();
+  constexpr uint64_t CT = kTileLanes * E;
+  const uint64_t tiles = ((uint64_t)a.n + CT - 1) / CT;
+  const uint64_t k = (uint64_t)a.kc * E;
+  const uint64_t limit = std::min<uint64_t>(cus, kGemvMaxSplitBlocks);
+  uint64_t splits = 1;
+  if (tiles < limit && k) {
+    const uint64_t tile_row = kTileLanes * 16;  // bytes of a tile in one row of W
+    const uint64_t by_bytes = (k * tile_row + kGemvTSliceBytes - 1) / kGemvTSliceBytes;
+    const uint64_t by_rounds = (k + kTGroups * RG - 1) / (kTGroups * RG);
+    splits = std::max<uint64_t>(1, std::min(limit / tiles, std::min(by_bytes, by_rounds)));
+  }
+  uint64_t rows = (k + splits - 1) / splits;
+  rows = (rows + 7) / 8 * 8;
+  splits = rows ? (k + rows - 1) / rows : 1;
+  a.n_groups = (uint32_t)tiles;
+  a.n_norm_groups = (uint32_t)(((uint64_t)a.n_normed + CT - 1) / CT);
+  a.n_norm_blocks = a.n_norm_groups;
+  a.k_splits = (uint32_t)splits;
+  a.split_rows = (uint32_t)rows;
+  const uint64_t ys = (uint64_t)a.m * a.n_normed;
+  a.single_arrival = splits > 1 && ys && ys <= kGemvSingleMaxY &&
+                     splits * ys <= kGemvSingleMaxSlices;
+  hipLaunchKernelGGL((gemv_norm_t_kernel<DT, MB, RG>), dim3((uint32_t)(tiles * splits)),
+                     dim3(64 * kTWaves), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+// rows per launch -> rows held (8 rows of k per row group and round)
+template <int DT>
+int run_t_rows(GemvArgs& a, hipStream_t s) {
+  if (a.m <= 1) return run_t<DT, 1, 8>(a, s);
+  if (a.m <= 2) return run_t<DT, 2, 8>(a, s);
+  if (a.m <= 4) return run_t<DT, 4, 8>(a, s);
+  return run_t<DT, 8, 8>(a, s);
 }
 
 template <int DT, int MB, int CPW, int U>
@@ -679,7 +866,7 @@ int run_rows(GemvArgs& a, hipStream_t s) {
 
 // Clears the arrival counter's line of a scratch buffer.
 __global__ void __launch_bounds__(64) clear_counter(uint32_t* c) {
-  if (threadIdx.x < kGemvCounterBytes / 4) c[threadIdx.x] = 0u;
+  for (uint32_t i = threadIdx.x; i < kGemvCounterBytes / 4; i += 64) c[i] = 0u;
 }
 
 std::mutex g_scratch_mu;

@@ -10,11 +10,12 @@ rounds at most once per term) -- and then adds the 64 partial sums in a
 6-level tree.  Recursive summation of n terms errs by at most
 gamma_n = n u / (1 - n u) times the sum of the terms' magnitudes, so
     |y^ - y| <= D_j = gamma_{n_l + 6} * A_j,    A_j = sum_k |x_k w_jk|,
-with y the oracle's exact sum.  With W stored [k][n] (transpose_b = 0) a
-block of 256 threads computes a column: thread t adds the terms of rows
-t, t + 256, ... in k order, one fused multiply-add per term
-(n_l = ceil(k / 256)), then the 6-level butterfly and the four wave sums
-(3 more adds): D_j = gamma_{n_l + 9} * A_j.  A passed-through output
+with y the oracle's exact sum.  With W stored [k][n] (transpose_b = 0) k
+is cut into S <= ceil(k / 512) slices; in each, a thread adds the terms of
+8 consecutive rows of every 512 in k order, one fused multiply-add per term
+(n_l <= 8 ceil(k / 512)), then come the 3-level butterfly over the wave's
+row groups, the eight wave sums (7 adds) and the S slice sums (S - 1 adds):
+D_j = gamma_{n_l + S + 9} * A_j.  A passed-through output
 is y^ rounded to the dtype, the oracle's is y rounded: they differ by at
 most D_j plus one ulp of the larger.
 
@@ -63,7 +64,8 @@ def bounds(case, res):
     if getattr(case, "transpose_b", 1):
         D = _gamma(-(-kc // 64) * E + 6) * res.abs_dot       # [m, n]
     else:
-        D = _gamma(-(-case.k // 256) + 9) * res.abs_dot
+        rounds = -(-case.k // 512)
+        D = _gamma(8 * rounds + rounds + 9) * res.abs_dot
     nn = case.n_normed
     un_tol = 1.01 * D[:, nn:]
     if nn == 0:

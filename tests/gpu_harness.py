@@ -248,7 +248,8 @@ def upload_gemv(case, device="cuda", workspace: torch.Tensor = None) -> DeviceGe
     normed = torch.full((case.m, case.normed_row_stride), s, dtype=bits, device=device)
     unnormed = torch.full((case.m, case.unnormed_row_stride), s, dtype=bits, device=device)
     if workspace is None:
-        nbytes = max(qrp.gemv_norm_workspace_bytes(case.m, case.n_normed), 256)
+        nbytes = max(qrp.gemv_norm_workspace_bytes(case.m, case.n_normed,
+                                                   int(getattr(case, "transpose_b", 1))), 256)
         workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return DeviceGemv(case=case, x=bits_tensor(case.x, device), w=bits_tensor(case.w, device),
                       gamma=bits_tensor(case.gamma, device), normed=normed, unnormed=unnormed,

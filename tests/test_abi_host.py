@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(qrp.EXPORTS)
-    assert qrp.abi_version() == 6
+    assert qrp.abi_version() == 7
 
 
 def test_launch_overrides_set_restore_and_reject():
@@ -377,6 +377,9 @@ def _gemv(**kw):
     (dict(transpose_b=2), qrp.QRP_EINVAL),
     (dict(transpose_b=0, weight_row_stride=2104), qrp.QRP_EINVAL),   # W [k][n]: stride < n
     (dict(transpose_b=0, weight_row_stride=2116), qrp.QRP_EALIGN),   # not 16-byte rows
+    (dict(transpose_b=0, weight_row_stride=2112), qrp.QRP_EINVAL),   # [n][k]-sized workspace
+    (dict(transpose_b=0, weight_row_stride=2112, n_normed=0, normed_output=None, gamma=None,
+          workspace=None, workspace_bytes=0), qrp.QRP_EINVAL),       # [k][n] always needs one
     (dict(m=9), qrp.QRP_EUNSUPPORTED),
     (dict(n_normed=2113), qrp.QRP_EINVAL),
     (dict(input=None), qrp.QRP_EINVAL),
@@ -409,6 +412,11 @@ def test_gemv_norm_degenerate_sizes_and_workspace_size():
     # nothing to compute: no launch, no pointer read
     assert _gemv(m=0, input=None, weight=None, workspace=None) == qrp.QRP_OK
     assert _gemv(n=0, n_normed=0, input=None, weight=None) == qrp.QRP_OK
-    # the workspace is the counter line plus m * n_normed binary32 values; none without a norm
-    assert qrp.gemv_norm_workspace_bytes(3, 100) == 256 + 4 * 3 * 100
+    # the workspace is the counters plus m * n_normed binary32 values; with W
+    # stored [n][k] none without a norm; with W stored [k][n] the slices'
+    # partial sums follow, from a 256-byte boundary
+    assert qrp.gemv_norm_workspace_bytes(3, 100) == 1280 + 4 * 3 * 100
     assert qrp.gemv_norm_workspace_bytes(8, 0) == 0
+    assert qrp.gemv_norm_workspace_bytes(3, 100, 0) == 1280 + 1280 + 65536 * 3
+    assert qrp.gemv_norm_workspace_bytes(8, 0, 0) == 1280 + 65536 * 8
+    assert qrp.gemv_norm_workspace_bytes(1, 1536, 0) == 1280 + 6144 + 65536

@@ -38,8 +38,9 @@ def _gpu():
 
 
 def counters_left(workspace) -> int:
-    """Non-zero words in a workspace's arrival-counter header (its size is
-    what the workspace needs for one normed value, less that value)."""
+    """Non-zero bytes in a workspace's arrival-counter header (its size is
+    what a [n][k] workspace needs for one normed value, less that value);
+    every call must leave the norm's and the tiles' counters at zero."""
     import qk_rope_paged_amd as qrp
     hdr = qrp.gemv_norm_workspace_bytes(1, 1) - 4
     return int(torch.count_nonzero(workspace[:hdr]).item())
@@ -56,9 +57,8 @@ def run_and_compare(case, workspace=None, no_workspace=False):
     torch.cuda.synchronize()
     rep = gp.check(case, res, gh.to_numpy_bits(dg.normed, case.dtype),
                    gh.to_numpy_bits(dg.unnormed, case.dtype))
-    if case.n_normed:
-        left = counters_left(dg.workspace)
-        assert left == 0, f"{left} arrival counter words left non-zero"
+    left = counters_left(dg.workspace)
+    assert left == 0, f"{left} arrival counter bytes left non-zero"
     print(f"[gemv] {case.name} ok {rep}", flush=True)
     return dg, rep
 
@@ -266,8 +266,8 @@ def test_w_stored_k_by_n_bench_shape(small):
 @pytest.mark.parametrize("dtype", [sc.F32, sc.BF16, sc.F16])
 @pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
 def test_w_stored_k_by_n_rows_dtypes_and_ragged_sizes(dtype, m):
-    # k-chunks over two rounds of the 256 threads and a ragged third; n not a
-    # multiple of the 16-column unit, W rows padded
+    # k over several slices, each a whole round of the block's 512 rows and
+    # a ragged one; n not a multiple of the tile, W rows padded
     E = 4 if dtype == sc.F32 else 8
     k = E * (256 * 2 + 5)
     case = sc.make_gemv_case(f"t_rows_{dtype}_{m}", 70 + m, dtype, m=m, k=k, n=333, n_normed=201,
@@ -278,19 +278,23 @@ def test_w_stored_k_by_n_rows_dtypes_and_ragged_sizes(dtype, m):
 
 @pytest.mark.parametrize("n,w_pad", [(150, 2), (16, 0), (1, 7), (8, 0), (17, 7)])
 def test_w_stored_k_by_n_last_unit_at_the_row_end(n, w_pad):
-    # the last unit's second column chunk starts at or past the row stride
-    # (n = 150, stride 152; n = 1, stride 8): it is not read
+    # the last tile's chunks from the row stride on are not read (n = 150,
+    # stride 152: the tile's fourth chunk onward; n = 1, stride 8: all but
+    # the first)
     case = sc.make_gemv_case(f"t_end_{n}", 80 + n, sc.BF16, m=1, k=512, n=n,
                              n_normed=min(n, 5), w_pad=w_pad, transpose_b=False)
     assert case.w.shape[1] % 8 == 0
     run_and_compare(case)
 
 
-@pytest.mark.parametrize("m", [2, 8])
-def test_w_stored_k_by_n_rows_match_single_row_calls(m):
+@pytest.mark.parametrize("m,nn", [(2, 300), (8, 300), (8, 1100)])
+def test_w_stored_k_by_n_rows_match_single_row_calls(m, nn):
+    # k in two slices; with 8 rows of 1100 normed columns the slices' sums
+    # meet per tile first, with one row they meet at the norm's counter
+    # directly: the sums are added in the same order either way
     gh, _ = _gpu()
-    mk = lambda: sc.make_gemv_case("t_rows", 90, sc.BF16, m=m, k=2048, n=500, n_normed=300,
-                                   w_pad=4, transpose_b=False)
+    mk = lambda: sc.make_gemv_case("t_rows", 90, sc.BF16, m=m, k=2048, n=1200, n_normed=nn,
+                                   w_pad=0, transpose_b=False)
     case = mk()
     dg = gh.upload_gemv(case)
     gh.run_gemv(dg)
@@ -305,8 +309,9 @@ def test_w_stored_k_by_n_rows_match_single_row_calls(m):
 
 
 def test_w_stored_k_by_n_nothing_normed_and_k_zero():
-    run_and_compare(sc.make_gemv_case("t_nonorm", 91, sc.BF16, m=2, k=512, n=300, n_normed=0,
-                                      w_pad=4, transpose_b=False), no_workspace=True)
+    # nothing normed: the slices' sums still meet in the workspace
+    run_and_compare(sc.make_gemv_case("t_nonorm", 91, sc.BF16, m=2, k=4096, n=300, n_normed=0,
+                                      w_pad=4, transpose_b=False))
     case = sc.make_gemv_case("t_k0", 92, sc.F32, m=2, k=0, n=10, n_normed=4, epsilon=1e-3,
                              x_pad=4, w_pad=2, transpose_b=False)
     # k = 0: W has no rows; keep the buffer non-empty (a real device address)
@@ -331,4 +336,23 @@ def test_w_stored_k_by_n_random_shapes(i):
                              x_pad=E * int(rng.integers(0, 3)),
                              w_pad=(-n) % E + E * int(rng.integers(0, 3)),
                              out_pad=int(rng.integers(0, 3)), transpose_b=False)
-    run_and_compare(case, no_workspace=nn == 0)
+    run_and_compare(case)
+
+
+@pytest.mark.parametrize("dtype,m,k,n,nn", [
+    (sc.BF16, 1, 16384, 64, 64),     # one tile: 16 slices
+    (sc.F16, 3, 24576, 130, 100),    # three tiles, the last of 2 columns: many slices
+    (sc.F32, 2, 8192, 40, 33),       # fp32 tiles of 32 columns
+    (sc.BF16, 2, 512 * 7 + 8, 2112, 1536),   # the last slice 8 rows longer than a round
+    (sc.BF16, 8, 4096, 2112, 1536),  # 8 rows of y past the LDS copy: tiles meet first
+    (sc.F16, 4, 8192, 1000, 700),    # many slice sums: tiles meet first
+    (sc.BF16, 1, 8, 700, 500),       # one row group's rows: one slice
+    (sc.BF16, 2, 1024, 64 * 260, 64 * 200),  # more tiles than compute units: one slice
+    (sc.F32, 1, 4, 33, 33),          # k of one chunk
+])
+def test_w_stored_k_by_n_slices(dtype, m, k, n, nn):
+    # how k is cut into slices follows from n, k and the dtype; each case
+    # holds a different count, down to one, and the counters end at zero
+    E = 4 if dtype == sc.F32 else 8
+    run_and_compare(sc.make_gemv_case(f"t_slices_{dtype}_{k}_{n}", 95, dtype, m=m, k=k, n=n,
+                                      n_normed=nn, w_pad=(-n) % E, transpose_b=False))

@@ -40,7 +40,8 @@ def _noalloc(qrp, gh, dg, raise_on_error=True):
         dg.normed if c.n_normed else None, c.normed_row_stride,
         dg.unnormed if c.n_normed < c.n else None, c.unnormed_row_stride,
         dg.x, c.x.shape[1], c.m, dg.w, c.w.shape[1], c.n, c.k, dg.gamma, c.n_normed,
-        c.epsilon, c.weight_offset, gh.QRP_DT[c.dtype], raise_on_error=raise_on_error)
+        c.epsilon, c.weight_offset, gh.QRP_DT[c.dtype],
+        transpose_b=int(getattr(c, "transpose_b", 1)), raise_on_error=raise_on_error)
 
 
 def _pair(case, check_oracle):
@@ -72,6 +73,20 @@ def test_noalloc_matches_the_workspace_call_on_calls_in_a_row():
                             SCRATCH_VALUES // 8), False)
     _pair(sc.make_gemv_case("noalloc_unnormed", 84, sc.F32, 2, 256, 500, 0), True)
     _pair(sc.gemv_norm(small=True), True)
+
+
+def test_noalloc_w_stored_k_by_n_on_calls_in_a_row():
+    # W stored [k][n]: the slices' sums and the tiles' counters live in the
+    # scratch too -- a split call, a smaller one, nothing normed, eight rows
+    _pair(sc.make_gemv_case("noalloc_t_big", 87, sc.BF16, 4, 8192, 1000, 700,
+                            transpose_b=False), True)
+    _pair(sc.make_gemv_case("noalloc_t_small", 88, sc.F32, 1, 512, 100, 60,
+                            transpose_b=False), True)
+    _pair(sc.make_gemv_case("noalloc_t_unnormed", 89, sc.F16, 2, 4096, 64, 0,
+                            transpose_b=False), True)
+    _pair(sc.make_gemv_case("noalloc_t_rows8", 90, sc.BF16, 8, 2048, 200, 130,
+                            transpose_b=False), True)
+    _pair(sc.gemv_norm(small=True, transpose_b=False), True)
 
 
 def test_noalloc_rejects_sizes_past_its_scratch():
