@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define QRP_ABI_VERSION 7
+#define QRP_ABI_VERSION 8
 
 typedef enum qrp_status {
   QRP_OK = 0,
@@ -418,9 +418,14 @@ int32_t qrp_abi_version(void);
  *                             1: consecutive blocks kept on one XCD,
  *                             2: each token's (or token block's) waves
  *                             kept on one XCD, tokens dealt round-robin
+ *   QRP_KNOB_TAIL_UNITS       >= 0: the last this-many tokens (token blocks
+ *                             when packed) of a launch of several passes
+ *                             per wave run one pass per wave (the
+ *                             library's choice: about 1536 such waves, at
+ *                             most a quarter of the launch's tokens)
  * The environment variables QRP_PACK, QRP_PASSES_PER_WAVE (0: the
- * library's choice), QRP_WAVES_PER_BLOCK (0: the library's choice) and
- * QRP_XCD_REMAP give the first values, read once when the library is
+ * library's choice), QRP_WAVES_PER_BLOCK (0: the library's choice),
+ * QRP_XCD_REMAP and QRP_TAIL_UNITS give the first values, read once when the library is
  * loaded.  A launch reads the values current when it is enqueued; changing
  * them while other threads launch is allowed but gives those launches
  * either value.  `previous` (may be NULL) receives the old value.
@@ -430,7 +435,8 @@ enum {
   QRP_KNOB_PACK = 0,
   QRP_KNOB_PASSES_PER_WAVE = 1,
   QRP_KNOB_WAVES_PER_BLOCK = 2,
-  QRP_KNOB_XCD_REMAP = 3
+  QRP_KNOB_XCD_REMAP = 3,
+  QRP_KNOB_TAIL_UNITS = 4
 };
 int32_t qrp_set_launch_override(int32_t knob, int32_t value, int32_t* previous);
 

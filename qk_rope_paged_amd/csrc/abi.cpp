@@ -68,7 +68,7 @@ int env_int(const char* name, int dflt) {
 // Launch-shape overrides (qrp_set_launch_override), process-wide; -1 lets
 // the library choose.  The environment gives the first values, read once
 // when the library is loaded.
-constexpr int kKnobs = 4;
+constexpr int kKnobs = 5;
 std::atomic<int32_t> g_knob[kKnobs];
 
 bool knob_value_ok(int32_t knob, int32_t v) {
@@ -78,6 +78,7 @@ bool knob_value_ok(int32_t knob, int32_t v) {
     case QRP_KNOB_PASSES_PER_WAVE: return v >= 1 && v <= 8;
     case QRP_KNOB_WAVES_PER_BLOCK: return v >= 1 && v <= qrp::kMaxWavesPerBlock;
     case QRP_KNOB_XCD_REMAP: return v >= 0 && v <= 2;
+    case QRP_KNOB_TAIL_UNITS: return v >= 0;
     default: return false;
   }
 }
@@ -85,7 +86,7 @@ bool knob_value_ok(int32_t knob, int32_t v) {
 struct KnobInit {
   KnobInit() {
     const char* names[kKnobs] = {"QRP_PACK", "QRP_PASSES_PER_WAVE", "QRP_WAVES_PER_BLOCK",
-                                 "QRP_XCD_REMAP"};
+                                 "QRP_XCD_REMAP", "QRP_TAIL_UNITS"};
     for (int k = 0; k < kKnobs; ++k) {
       int v = env_int(names[k], -1);
       // 0 meant "the library's choice" for the two counts
@@ -189,6 +190,9 @@ qrp::ScaleDesc make_scales(const qrp_paged_cache* c, uint32_t layer_idx) {
   return d;
 }
 
+// One-pass waves at the end of a multi-pass launch (see Builder::finish).
+constexpr uint32_t kTailWaves = 1536;
+
 struct Builder {
   qrp::BandArgs a{};
   int32_t dtype = QRP_BF16;
@@ -276,9 +280,27 @@ struct Builder {
       a.seg_begin[i - 1] = i < a.nseg ? a.seg[i].pass_begin : 0xFFFFFFFFu;
     a.passes_per_group = ppg;
     a.groups_per_token = (ppt + ppg - 1) / ppg;
-    const uint64_t items = (uint64_t)units * a.groups_per_token;
+    int32_t remap = knob(QRP_KNOB_XCD_REMAP);
+    if (remap < 0) remap = (pack && ppg == 1) ? 2 : 0;
+    // Multi-pass launches end on one-pass waves: the last `tail` units'
+    // passes each get a wave of their own, so the grid drains on short
+    // waves.  About 1536 such waves, at most a quarter of the units
+    // (measured: prefill 33.55 -> 33.31 us, dual 54.30 -> 53.6, dual over
+    // FP8 caches 55.6 -> 54.8; tails of 4000 waves and more were slower).
+    // Not with every unit's waves on one XCD: that mapping counts groups of
+    // passes_per_group.
+    uint32_t tail = 0;
+    if (ppg > 1 && remap != 2) {
+      const int32_t forced_tail = knob(QRP_KNOB_TAIL_UNITS);
+      tail = forced_tail >= 0 ? std::min<uint32_t>((uint32_t)forced_tail, units)
+                              : std::min<uint32_t>((kTailWaves + ppt - 1) / ppt, units / 4);
+    }
+    const uint64_t head_units = units - tail;
+    const uint64_t items = head_units * a.groups_per_token + (uint64_t)tail * ppt;
     if (items >= (1ull << 31)) return fail(QRP_EINVAL, "batch too large for one launch");
     a.n_items = (uint32_t)items;
+    a.tail_item = (uint32_t)(head_units * a.groups_per_token);
+    a.tail_unit = (uint32_t)head_units;
     // Rope/store launches of one pass per wave (decode-sized batches, the
     // padded grid) run two waves per block, large multi-pass ones one wave
     // per block, norm, radd and the other small launches four (measured:
@@ -295,8 +317,6 @@ struct Builder {
     // its L2 for their metadata and freqs rows (decode at 8-way head
     // parallelism: 3.08 -> 2.86 us per launch).  Everything else is dealt
     // round-robin: keeping units on one XCD measured 1-6 % slower there.
-    int32_t remap = knob(QRP_KNOB_XCD_REMAP);
-    if (remap < 0) remap = (pack && ppg == 1) ? 2 : 0;
     a.per_xcd = remap == 1 ? (a.n_blocks + qrp::kXcds - 1) / qrp::kXcds : 0;
     if (remap == 2) {
       // every unit's waves on one XCD: bpu blocks per unit, units dealt to

@@ -678,9 +678,19 @@ __global__ void __launch_bounds__(kThreads) band_kernel(const BandArgs a) {
   // heads of one segment per pass), or with PACK a block of RPP consecutive
   // tokens (a pass is one head of one segment, one row per token: nothing
   // idles when segments have fewer heads than a pass has rows).
-  const uint32_t unit = item / a.groups_per_token;
-  const uint32_t p0 = (item - unit * a.groups_per_token) * a.passes_per_group;
-  const uint32_t np = min(a.passes_per_group, a.passes_per_token - p0);
+  uint32_t unit, p0, np;
+  if (item < a.tail_item) {
+    unit = item / a.groups_per_token;
+    p0 = (item - unit * a.groups_per_token) * a.passes_per_group;
+    np = min(a.passes_per_group, a.passes_per_token - p0);
+  } else {
+    // the launch's last units: one pass per wave
+    const uint32_t r = item - a.tail_item;
+    const uint32_t q = r / a.passes_per_token;
+    unit = a.tail_unit + q;
+    p0 = r - q * a.passes_per_token;
+    np = 1;
+  }
 
   // this lane's row within a pass and its two chunks within the row
   const uint32_t row = lane / LPR;

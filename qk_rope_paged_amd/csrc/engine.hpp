@@ -133,6 +133,12 @@ struct BandArgs {
   // valid length pass through.  Unused by the ragged ops.
   const uint32_t* valid_lengths;
   uint32_t seq_len;
+  // The launch's last units run one pass per wave: items [tail_item,
+  // n_items) are unit tail_unit + r / passes_per_token, pass
+  // r % passes_per_token (r = item - tail_item).  Shorter waves at the end
+  // of the grid let it drain sooner.  tail_item == n_items: no tail.
+  uint32_t tail_item;
+  uint32_t tail_unit;
   ScaleDesc scale[kMaxCaches];
 };
 static_assert(offsetof(BandArgs, seg) == 64, "the hot header fills one 64-byte line");

@@ -170,7 +170,7 @@ def band_of(dc: DeviceCase, i: int) -> qrp.Band:
 OVERRIDES: dict = {}
 
 
-def knobs(remap=None, ppw=None, wpb=None, pack=None):
+def knobs(remap=None, ppw=None, wpb=None, pack=None, tail=None):
     """qrp.launch_overrides from the tests' settings: "0" or 0 for a count
     (passes per wave, waves per block) is the library's choice."""
     def count(v):
@@ -184,6 +184,8 @@ def knobs(remap=None, ppw=None, wpb=None, pack=None):
         kw["waves_per_block"] = count(wpb)
     if pack is not None:
         kw["pack"] = int(pack)
+    if tail is not None:
+        kw["tail_units"] = int(tail)
     return qrp.launch_overrides(**kw)
 
 

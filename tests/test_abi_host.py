@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(qrp.EXPORTS)
-    assert qrp.abi_version() == 7
+    assert qrp.abi_version() == 8
 
 
 def test_launch_overrides_set_restore_and_reject():
@@ -48,7 +48,9 @@ def test_launch_overrides_set_restore_and_reject():
         assert qrp.set_launch_override(qrp.QRP_KNOB_PASSES_PER_WAVE, 2) == 2
         assert qrp.set_launch_override(qrp.QRP_KNOB_XCD_REMAP, 1) == 1
     assert qrp.set_launch_override(qrp.QRP_KNOB_PASSES_PER_WAVE, -1) == -1
-    for knob, value in ((4, 0), (-1, 0), (qrp.QRP_KNOB_PACK, 2),
+    with qrp.launch_overrides(tail_units=7):
+        assert qrp.set_launch_override(qrp.QRP_KNOB_TAIL_UNITS, 0) == 7
+    for knob, value in ((5, 0), (-1, 0), (qrp.QRP_KNOB_PACK, 2), (qrp.QRP_KNOB_TAIL_UNITS, -2),
                         (qrp.QRP_KNOB_PASSES_PER_WAVE, 0), (qrp.QRP_KNOB_WAVES_PER_BLOCK, 5),
                         (qrp.QRP_KNOB_XCD_REMAP, -2), (qrp.QRP_KNOB_XCD_REMAP, 3)):
         with pytest.raises(qrp.QrpError):

@@ -128,6 +128,29 @@ def test_launch_configuration_does_not_change_bits(workload, monkeypatch):
                     _assert_same(ref, snap, f"{workload} remap={remap} ppw={ppw} wpb={wpb}")
 
 
+@pytest.mark.parametrize("workload", ["prefill", "dual", "bshd", "prefill_tp8", "dual_tp8",
+                                      "prefill_fp8"])
+def test_one_pass_tail_does_not_change_bits(workload):
+    """The last units of a multi-pass launch may run one pass per wave
+    (QRP_KNOB_TAIL_UNITS): every tail size, from none to the whole launch,
+    with every pass count and XCD mapping, gives the same bits."""
+    _, gh, _ = _env()
+    case = sc.WORKLOADS[workload](small=True)
+    ref = None
+    for remap in ("0", "1"):
+        for ppw in ("0", "2", "3"):
+            for tail in (0, 1, 2, 5, 33, 10 ** 6):
+                dc = gh.upload(case)
+                with gh.knobs(remap, ppw, tail=tail):
+                    gh.run(dc)
+                torch.cuda.synchronize()
+                snap = _snapshot(dc)
+                if ref is None:
+                    ref = snap
+                else:
+                    _assert_same(ref, snap, f"{workload} remap={remap} ppw={ppw} tail={tail}")
+
+
 def test_validate_on_device():
     qrp, gh, _ = _env()
     case = sc.prefill(small=True)
