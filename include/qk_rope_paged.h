@@ -423,9 +423,14 @@ int32_t qrp_abi_version(void);
  *                             per wave run one pass per wave (the
  *                             library's choice: about 1536 such waves, at
  *                             most a quarter of the launch's tokens)
+ *   QRP_KNOB_LDS_BYTES        0 .. 65536: LDS bytes reserved per block,
+ *                             unused by the kernel (it caps the blocks
+ *                             resident on a compute unit; the library's
+ *                             choice: 32768 for radd over a plain cache,
+ *                             else 0)
  * The environment variables QRP_PACK, QRP_PASSES_PER_WAVE (0: the
  * library's choice), QRP_WAVES_PER_BLOCK (0: the library's choice),
- * QRP_XCD_REMAP and QRP_TAIL_UNITS give the first values, read once when the library is
+ * QRP_XCD_REMAP, QRP_TAIL_UNITS and QRP_LDS_BYTES give the first values, read once when the library is
  * loaded.  A launch reads the values current when it is enqueued; changing
  * them while other threads launch is allowed but gives those launches
  * either value.  `previous` (may be NULL) receives the old value.
@@ -436,7 +441,8 @@ enum {
   QRP_KNOB_PASSES_PER_WAVE = 1,
   QRP_KNOB_WAVES_PER_BLOCK = 2,
   QRP_KNOB_XCD_REMAP = 3,
-  QRP_KNOB_TAIL_UNITS = 4
+  QRP_KNOB_TAIL_UNITS = 4,
+  QRP_KNOB_LDS_BYTES = 5
 };
 int32_t qrp_set_launch_override(int32_t knob, int32_t value, int32_t* previous);
 

@@ -121,10 +121,10 @@ def last_error() -> str:
 
 # launch-shape knobs (include/qk_rope_paged.h: qrp_set_launch_override)
 QRP_KNOB_PACK, QRP_KNOB_PASSES_PER_WAVE, QRP_KNOB_WAVES_PER_BLOCK, QRP_KNOB_XCD_REMAP = 0, 1, 2, 3
-QRP_KNOB_TAIL_UNITS = 4
+QRP_KNOB_TAIL_UNITS, QRP_KNOB_LDS_BYTES = 4, 5
 _KNOBS = {"pack": QRP_KNOB_PACK, "passes_per_wave": QRP_KNOB_PASSES_PER_WAVE,
           "waves_per_block": QRP_KNOB_WAVES_PER_BLOCK, "xcd_remap": QRP_KNOB_XCD_REMAP,
-          "tail_units": QRP_KNOB_TAIL_UNITS}
+          "tail_units": QRP_KNOB_TAIL_UNITS, "lds_bytes": QRP_KNOB_LDS_BYTES}
 
 
 def set_launch_override(knob: int, value: int) -> int:

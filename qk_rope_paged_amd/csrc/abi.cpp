@@ -68,7 +68,7 @@ int env_int(const char* name, int dflt) {
 // Launch-shape overrides (qrp_set_launch_override), process-wide; -1 lets
 // the library choose.  The environment gives the first values, read once
 // when the library is loaded.
-constexpr int kKnobs = 5;
+constexpr int kKnobs = 6;
 std::atomic<int32_t> g_knob[kKnobs];
 
 bool knob_value_ok(int32_t knob, int32_t v) {
@@ -79,6 +79,7 @@ bool knob_value_ok(int32_t knob, int32_t v) {
     case QRP_KNOB_WAVES_PER_BLOCK: return v >= 1 && v <= qrp::kMaxWavesPerBlock;
     case QRP_KNOB_XCD_REMAP: return v >= 0 && v <= 2;
     case QRP_KNOB_TAIL_UNITS: return v >= 0;
+    case QRP_KNOB_LDS_BYTES: return v >= 0 && v <= 65536;
     default: return false;
   }
 }
@@ -86,7 +87,7 @@ bool knob_value_ok(int32_t knob, int32_t v) {
 struct KnobInit {
   KnobInit() {
     const char* names[kKnobs] = {"QRP_PACK", "QRP_PASSES_PER_WAVE", "QRP_WAVES_PER_BLOCK",
-                                 "QRP_XCD_REMAP", "QRP_TAIL_UNITS"};
+                                 "QRP_XCD_REMAP", "QRP_TAIL_UNITS", "QRP_LDS_BYTES"};
     for (int k = 0; k < kKnobs; ++k) {
       int v = env_int(names[k], -1);
       // 0 meant "the library's choice" for the two counts
@@ -192,6 +193,9 @@ qrp::ScaleDesc make_scales(const qrp_paged_cache* c, uint32_t layer_idx) {
 
 // One-pass waves at the end of a multi-pass launch (see Builder::finish).
 constexpr uint32_t kTailWaves = 1536;
+// LDS reserved per block of a radd launch over a plain cache (an occupancy
+// cap; see Builder::finish).
+constexpr uint32_t kRaddLdsBytes = 32768;
 
 struct Builder {
   qrp::BandArgs a{};
@@ -229,7 +233,6 @@ struct Builder {
     // norm_build: the launch runs the norm kernels whatever its gammas
     bool norm = norm_build;
     for (uint32_t s = 0; s < a.nseg; ++s) norm = norm || a.seg[s].gamma != nullptr;
-    const uint32_t npmax = qrp::max_passes(radd, norm);
     // Per-token passes leave lanes idle when a segment's head count is not a
     // multiple of the rows a pass holds (a GPU's share of the heads under
     // head parallelism: 4 Q, 1 K, 1 V heads fill 6 of 24 rows).  Below 85 %
@@ -259,7 +262,8 @@ struct Builder {
     }
     const uint32_t ppt = a.passes_per_token;
     if (ppt == 0) return fail(QRP_EINVAL, "no head rows to process");  // keeps n_items >= 1
-    uint32_t ppg = std::min<uint32_t>(npmax, ppt);
+    const uint32_t npmax = qrp::max_passes(radd, norm, pack);
+    uint32_t ppg = std::min<uint32_t>(qrp::default_passes(radd, norm, pack), ppt);
     const int32_t forced = knob(QRP_KNOB_PASSES_PER_WAVE);
     if (forced > 0) {
       ppg = std::min<uint32_t>((uint32_t)forced, std::min(npmax, ppt));
@@ -311,6 +315,14 @@ struct Builder {
     const int32_t forced_wpb = knob(QRP_KNOB_WAVES_PER_BLOCK);
     if (forced_wpb > 0) wpb = std::min<uint32_t>((uint32_t)forced_wpb, qrp::kMaxWavesPerBlock);
     a.waves_per_block = wpb;
+    // radd over a plain cache streams best with at most 5 blocks (20 waves)
+    // resident per compute unit: reserving 32 KB of the 160 KB LDS per block
+    // caps it (measured: 19.59 -> 18.99 us on the radd workload; 4 blocks
+    // gave the same, 3 were 21 % slower, and the cap slowed radd over FP8
+    // caches, the prefill and the padded grid).
+    const int32_t forced_lds = knob(QRP_KNOB_LDS_BYTES);
+    a.lds_bytes = forced_lds >= 0 ? (uint32_t)forced_lds
+                  : (radd && a.fp8_caches == 0 && !pack && wpb == 4) ? kRaddLdsBytes : 0u;
     a.n_blocks = (uint32_t)((items + wpb - 1) / wpb);
     // Token-packed launches of one pass per wave (a decode batch's share
     // of the heads) keep each token block's waves on one XCD, so they share

@@ -1102,7 +1102,8 @@ int launch_np(const BandArgs& a, void* stream) {
   const uint32_t grid =
       (a.per_xcd && !(a.per_xcd & kUnitsOnXcd)) ? a.per_xcd * kXcds : a.n_blocks;
   hipLaunchKernelGGL((band_kernel<T, QT, CT, D, IL, NPMAX, RADD, NORM, BSHD, PACK>), dim3(grid),
-                     dim3(64 * a.waves_per_block), 0, reinterpret_cast<hipStream_t>(stream), a);
+                     dim3(64 * a.waves_per_block), a.lds_bytes,
+                     reinterpret_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
@@ -1111,7 +1112,8 @@ int launch_np(const BandArgs& a, void* stream) {
 template <typename T, typename QT, typename CT, int D, bool IL, bool RADD, bool NORM, bool BSHD,
           bool PACK>
 int launch_t(const BandArgs& a, void* stream) {
-  constexpr int NPMAX = RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : kMaxPassesStore);
+  constexpr int NPMAX =
+      RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : (PACK ? kMaxPassesStorePack : kMaxPassesStore));
   if constexpr (!RADD && !NORM && NPMAX > 1) {
     if (a.passes_per_group == 1)
       return launch_np<T, QT, CT, D, IL, 1, RADD, NORM, BSHD, PACK>(a, stream);

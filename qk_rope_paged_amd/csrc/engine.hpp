@@ -38,13 +38,20 @@ constexpr int kThreads = 64 * kMaxWavesPerBlock;  // launch bound; blocks may be
 constexpr int kXcds = 8;
 constexpr uint32_t kUnitsOnXcd = 0x80000000u;  // BandArgs::per_xcd flag
 
-// Passes (rows of 64 lanes) one wave may hold in registers at once.  Waves
-// that each move about 4 KB stream best on MI355X (measured with plain
-// copies and with this kernel): 2 passes of rope/store rows, 3 of norm rows,
-// 1 of radd rows (each radd pass reads two operands).  Smaller register
-// arrays also raise the number of resident waves.
+// Passes (rows of 64 lanes) one wave may hold in registers at once, and
+// how many it runs by default.  Waves that each move about 4 KB stream best
+// on MI355X (measured with plain copies and with this kernel): 2 passes of
+// rope/store rows, 3 of norm rows, 1 of radd rows (each radd pass reads two
+// operands).  The per-token store kernels are built for up to 3 passes and
+// run 2: that build ran the prefill 1 % faster at 2 passes than a build for
+// 2 (same-box A/B, twice), while 3 passes per wave were 7 % slower; the
+// token-packed store kernels are built for 2 (the 3-pass build ran them 1 %
+// slower).
 #ifndef QRP_MAX_PASSES_STORE
-#define QRP_MAX_PASSES_STORE 2
+#define QRP_MAX_PASSES_STORE 3
+#endif
+#ifndef QRP_MAX_PASSES_STORE_PACK
+#define QRP_MAX_PASSES_STORE_PACK 2
 #endif
 #ifndef QRP_MAX_PASSES_NORM
 #define QRP_MAX_PASSES_NORM 3
@@ -53,6 +60,8 @@ constexpr uint32_t kUnitsOnXcd = 0x80000000u;  // BandArgs::per_xcd flag
 #define QRP_MAX_PASSES_RADD 2
 #endif
 constexpr int kMaxPassesStore = QRP_MAX_PASSES_STORE;
+constexpr int kMaxPassesStorePack = QRP_MAX_PASSES_STORE_PACK;
+constexpr int kDefaultPassesStore = 2;
 constexpr int kMaxPassesNorm = QRP_MAX_PASSES_NORM;
 constexpr int kMaxPassesRadd = QRP_MAX_PASSES_RADD;
 
@@ -139,6 +148,9 @@ struct BandArgs {
   // of the grid let it drain sooner.  tail_item == n_items: no tail.
   uint32_t tail_item;
   uint32_t tail_unit;
+  // Host side only: dynamic LDS reserved per block at launch (unused by the
+  // kernel), which caps the blocks resident on a compute unit.
+  uint32_t lds_bytes;
   ScaleDesc scale[kMaxCaches];
 };
 static_assert(offsetof(BandArgs, seg) == 64, "the hot header fills one 64-byte line");
@@ -159,8 +171,15 @@ struct LaunchSpec {
 };
 
 // Largest passes-per-wave the kernel for this op holds in registers.
-inline uint32_t max_passes(bool radd, bool norm) {
-  return radd ? kMaxPassesRadd : (norm ? kMaxPassesNorm : kMaxPassesStore);
+inline uint32_t max_passes(bool radd, bool norm, bool pack) {
+  return radd ? kMaxPassesRadd
+              : (norm ? kMaxPassesNorm : (pack ? kMaxPassesStorePack : kMaxPassesStore));
+}
+
+// Passes per wave a launch runs unless overridden (before it is shrunk to
+// give small launches enough waves).
+inline uint32_t default_passes(bool radd, bool norm, bool pack) {
+  return (radd || norm) ? max_passes(radd, norm, pack) : (uint32_t)kDefaultPassesStore;
 }
 
 // Launch the band engine; returns 0 or a hipError_t value.

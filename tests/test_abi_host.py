@@ -50,7 +50,7 @@ def test_launch_overrides_set_restore_and_reject():
     assert qrp.set_launch_override(qrp.QRP_KNOB_PASSES_PER_WAVE, -1) == -1
     with qrp.launch_overrides(tail_units=7):
         assert qrp.set_launch_override(qrp.QRP_KNOB_TAIL_UNITS, 0) == 7
-    for knob, value in ((5, 0), (-1, 0), (qrp.QRP_KNOB_PACK, 2), (qrp.QRP_KNOB_TAIL_UNITS, -2),
+    for knob, value in ((6, 0), (-1, 0), (qrp.QRP_KNOB_LDS_BYTES, 65537), (qrp.QRP_KNOB_PACK, 2), (qrp.QRP_KNOB_TAIL_UNITS, -2),
                         (qrp.QRP_KNOB_PASSES_PER_WAVE, 0), (qrp.QRP_KNOB_WAVES_PER_BLOCK, 5),
                         (qrp.QRP_KNOB_XCD_REMAP, -2), (qrp.QRP_KNOB_XCD_REMAP, 3)):
         with pytest.raises(qrp.QrpError):
