@@ -69,12 +69,15 @@ def test_launch_override_environment_is_read_once_at_load():
             "print(q.set_launch_override(q.QRP_KNOB_PACK, -1),"
             " q.set_launch_override(q.QRP_KNOB_PASSES_PER_WAVE, -1),"
             " q.set_launch_override(q.QRP_KNOB_WAVES_PER_BLOCK, -1),"
-            " q.set_launch_override(q.QRP_KNOB_XCD_REMAP, -1))\n")
+            " q.set_launch_override(q.QRP_KNOB_XCD_REMAP, -1),"
+            " q.set_launch_override(q.QRP_KNOB_TAIL_UNITS, -1),"
+            " q.set_launch_override(q.QRP_KNOB_LDS_BYTES, -1))\n")
     env = dict(os.environ, QRP_PACK="1", QRP_PASSES_PER_WAVE="0", QRP_WAVES_PER_BLOCK="2",
-               QRP_XCD_REMAP="1")
+               QRP_XCD_REMAP="1", QRP_TAIL_UNITS="0", QRP_LDS_BYTES="70000")
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
                          text=True, check=True).stdout.split()
-    assert out == ["1", "-1", "2", "1"]
+    # QRP_LDS_BYTES past 65536 is out of range: the library's choice stays
+    assert out == ["1", "-1", "2", "1", "0", "-1"]
 
 
 def test_noalloc_gemv_rejects_sizes_past_its_scratch_on_the_host():
