@@ -262,8 +262,9 @@ struct Builder {
     }
     const uint32_t ppt = a.passes_per_token;
     if (ppt == 0) return fail(QRP_EINVAL, "no head rows to process");  // keeps n_items >= 1
-    const uint32_t npmax = qrp::max_passes(radd, norm, pack);
-    uint32_t ppg = std::min<uint32_t>(qrp::default_passes(radd, norm, pack), ppt);
+    const bool fp8 = a.fp8_caches != 0;
+    const uint32_t npmax = qrp::max_passes(radd, norm, pack, fp8);
+    uint32_t ppg = std::min<uint32_t>(qrp::default_passes(radd, norm, pack, fp8), ppt);
     const int32_t forced = knob(QRP_KNOB_PASSES_PER_WAVE);
     if (forced > 0) {
       ppg = std::min<uint32_t>((uint32_t)forced, std::min(npmax, ppt));

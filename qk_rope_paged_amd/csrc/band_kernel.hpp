@@ -1112,8 +1112,11 @@ int launch_np(const BandArgs& a, void* stream) {
 template <typename T, typename QT, typename CT, int D, bool IL, bool RADD, bool NORM, bool BSHD,
           bool PACK>
 int launch_t(const BandArgs& a, void* stream) {
+  constexpr bool FP8 = std::is_same_v<CT, Fp8> || std::is_same_v<CT, MixFp8>;
   constexpr int NPMAX =
-      RADD ? kMaxPassesRadd : (NORM ? kMaxPassesNorm : (PACK ? kMaxPassesStorePack : kMaxPassesStore));
+      RADD ? kMaxPassesRadd
+           : (NORM ? ((PACK || FP8) ? kMaxPassesNorm : kMaxPassesNormPlain)
+                   : (PACK ? kMaxPassesStorePack : kMaxPassesStore));
   if constexpr (!RADD && !NORM && NPMAX > 1) {
     if (a.passes_per_group == 1)
       return launch_np<T, QT, CT, D, IL, 1, RADD, NORM, BSHD, PACK>(a, stream);

@@ -53,8 +53,15 @@ constexpr uint32_t kUnitsOnXcd = 0x80000000u;  // BandArgs::per_xcd flag
 #ifndef QRP_MAX_PASSES_STORE_PACK
 #define QRP_MAX_PASSES_STORE_PACK 2
 #endif
+// The norm kernels hold 3 passes, except per-token launches over plain
+// caches, built for 2: that build needs 95 VGPRs against 103, which leaves
+// room for a fifth wave per SIMD (dual 53.54 -> 52.39 us); over FP8 caches
+// and in the token-packed layout the 2-pass build was 11 % and 6 % slower.
 #ifndef QRP_MAX_PASSES_NORM
 #define QRP_MAX_PASSES_NORM 3
+#endif
+#ifndef QRP_MAX_PASSES_NORM_PLAIN
+#define QRP_MAX_PASSES_NORM_PLAIN 2
 #endif
 #ifndef QRP_MAX_PASSES_RADD
 #define QRP_MAX_PASSES_RADD 2
@@ -63,6 +70,7 @@ constexpr int kMaxPassesStore = QRP_MAX_PASSES_STORE;
 constexpr int kMaxPassesStorePack = QRP_MAX_PASSES_STORE_PACK;
 constexpr int kDefaultPassesStore = 2;
 constexpr int kMaxPassesNorm = QRP_MAX_PASSES_NORM;
+constexpr int kMaxPassesNormPlain = QRP_MAX_PASSES_NORM_PLAIN;
 constexpr int kMaxPassesRadd = QRP_MAX_PASSES_RADD;
 
 struct SegDesc {
@@ -171,15 +179,17 @@ struct LaunchSpec {
 };
 
 // Largest passes-per-wave the kernel for this op holds in registers.
-inline uint32_t max_passes(bool radd, bool norm, bool pack) {
-  return radd ? kMaxPassesRadd
-              : (norm ? kMaxPassesNorm : (pack ? kMaxPassesStorePack : kMaxPassesStore));
+// fp8: some cache of the launch holds FP8 codes.
+inline uint32_t max_passes(bool radd, bool norm, bool pack, bool fp8) {
+  if (radd) return kMaxPassesRadd;
+  if (norm) return (pack || fp8) ? kMaxPassesNorm : kMaxPassesNormPlain;
+  return pack ? kMaxPassesStorePack : kMaxPassesStore;
 }
 
 // Passes per wave a launch runs unless overridden (before it is shrunk to
 // give small launches enough waves).
-inline uint32_t default_passes(bool radd, bool norm, bool pack) {
-  return (radd || norm) ? max_passes(radd, norm, pack) : (uint32_t)kDefaultPassesStore;
+inline uint32_t default_passes(bool radd, bool norm, bool pack, bool fp8) {
+  return (radd || norm) ? max_passes(radd, norm, pack, fp8) : (uint32_t)kDefaultPassesStore;
 }
 
 // Launch the band engine; returns 0 or a hipError_t value.
