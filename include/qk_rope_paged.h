@@ -421,8 +421,9 @@ int32_t qrp_abi_version(void);
  *   QRP_KNOB_TAIL_UNITS       >= 0: the last this-many tokens (token blocks
  *                             when packed) of a launch of several passes
  *                             per wave run one pass per wave (the
- *                             library's choice: about 1536 such waves, at
- *                             most a quarter of the launch's tokens)
+ *                             library's choice: about 1536 such waves, 768
+ *                             for the store op over FP8 caches, at most a
+ *                             quarter of the launch's tokens)
  *   QRP_KNOB_LDS_BYTES        0 .. 65536: LDS bytes reserved per block,
  *                             unused by the kernel (it caps the blocks
  *                             resident on a compute unit; the library's

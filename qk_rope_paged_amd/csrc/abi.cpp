@@ -297,8 +297,11 @@ struct Builder {
     uint32_t tail = 0;
     if (ppg > 1 && remap != 2) {
       const int32_t forced_tail = knob(QRP_KNOB_TAIL_UNITS);
+      // the store op over FP8 caches drains best on about half as many
+      // (prefill over FP8: 34.04 -> 33.73 us with 768 instead of 1536)
+      const uint32_t waves = (fp8 && !norm) ? kTailWaves / 2 : kTailWaves;
       tail = forced_tail >= 0 ? std::min<uint32_t>((uint32_t)forced_tail, units)
-                              : std::min<uint32_t>((kTailWaves + ppt - 1) / ppt, units / 4);
+                              : std::min<uint32_t>((waves + ppt - 1) / ppt, units / 4);
     }
     const uint64_t head_units = units - tail;
     const uint64_t items = head_units * a.groups_per_token + (uint64_t)tail * ppt;
