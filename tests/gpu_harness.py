@@ -170,7 +170,7 @@ def band_of(dc: DeviceCase, i: int) -> qrp.Band:
 OVERRIDES: dict = {}
 
 
-def knobs(remap=None, ppw=None, wpb=None, pack=None, tail=None):
+def knobs(remap=None, ppw=None, wpb=None, pack=None, tail=None, lds=None):
     """qrp.launch_overrides from the tests' settings: "0" or 0 for a count
     (passes per wave, waves per block) is the library's choice."""
     def count(v):
@@ -186,6 +186,8 @@ def knobs(remap=None, ppw=None, wpb=None, pack=None, tail=None):
         kw["pack"] = int(pack)
     if tail is not None:
         kw["tail_units"] = int(tail)
+    if lds is not None:
+        kw["lds_bytes"] = int(lds)
     return qrp.launch_overrides(**kw)
 
 

@@ -151,6 +151,28 @@ def test_one_pass_tail_does_not_change_bits(workload):
                     _assert_same(ref, snap, f"{workload} remap={remap} ppw={ppw} tail={tail}")
 
 
+@pytest.mark.parametrize("workload", ["prefill", "decode", "dual", "radd", "bshd", "radd_fp8",
+                                      "dual_tp8"])
+def test_reserved_lds_does_not_change_bits(workload):
+    """LDS reserved per block (QRP_KNOB_LDS_BYTES; radd over a plain cache
+    reserves 32 KB by default) caps the resident blocks and changes nothing
+    else: every size gives the same bits."""
+    _, gh, _ = _env()
+    case = sc.WORKLOADS[workload](small=True)
+    ref = None
+    for lds in (-1, 0, 1, 16384, 32768, 49152):
+        for wpb in ("0", "1"):
+            dc = gh.upload(case)
+            with gh.knobs(wpb=wpb, lds=lds):
+                gh.run(dc)
+            torch.cuda.synchronize()
+            snap = _snapshot(dc)
+            if ref is None:
+                ref = snap
+            else:
+                _assert_same(ref, snap, f"{workload} lds={lds} wpb={wpb}")
+
+
 def test_validate_on_device():
     qrp, gh, _ = _env()
     case = sc.prefill(small=True)
