@@ -428,11 +428,14 @@ int32_t qrp_abi_version(void);
  *                             unused by the kernel (it caps the blocks
  *                             resident on a compute unit; the library's
  *                             choice: 32768 for radd over a plain cache,
- *                             else 0)
+ *                             else 0).  The norm kernels' own 4 KB per
+ *                             block comes on top; a launch whose total
+ *                             passes the device's per-block LDS limit fails
+ *                             (QRP_EHIP).
  * The environment variables QRP_PACK, QRP_PASSES_PER_WAVE (0: the
  * library's choice), QRP_WAVES_PER_BLOCK (0: the library's choice),
- * QRP_XCD_REMAP, QRP_TAIL_UNITS and QRP_LDS_BYTES give the first values, read once when the library is
- * loaded.  A launch reads the values current when it is enqueued; changing
+ * QRP_XCD_REMAP, QRP_TAIL_UNITS and QRP_LDS_BYTES give the first values,
+ * read once when the library is loaded.  A launch reads the values current when it is enqueued; changing
  * them while other threads launch is allowed but gives those launches
  * either value.  `previous` (may be NULL) receives the old value.
  * QRP_EINVAL for an unknown knob or a value out of range.

@@ -41,8 +41,8 @@ constexpr uint32_t kUnitsOnXcd = 0x80000000u;  // BandArgs::per_xcd flag
 // Passes (rows of 64 lanes) one wave may hold in registers at once, and
 // how many it runs by default.  Waves that each move about 4 KB stream best
 // on MI355X (measured with plain copies and with this kernel): 2 passes of
-// rope/store rows, 3 of norm rows, 1 of radd rows (each radd pass reads two
-// operands).  The per-token store kernels are built for up to 3 passes and
+// rope/store rows, 2 or 3 of norm rows (below), 1 of radd rows (each radd
+// pass reads two operands).  The per-token store kernels are built for up to 3 passes and
 // run 2: that build ran the prefill 1 % faster at 2 passes than a build for
 // 2 (same-box A/B, twice), while 3 passes per wave were 7 % slower; the
 // token-packed store kernels are built for 2 (the 3-pass build ran them 1 %
