@@ -10,7 +10,10 @@ size on both sides of the small-batch threshold and up to 512 sequences,
 ragged and empty sequences,
 cache lengths up to the table's end, and the norm op's switches; odd cases
 force the per-token layout, even ones let the library pick (mostly the
-token-packed layout at these head counts).  Every case
+token-packed layout at these head counts), and every third case also draws
+the launch shape (passes per wave, the one-pass tail's size, waves per
+block, the XCD mapping, LDS reserved per block), which never changes the
+bits.  Every case
 is valid by construction (positions stay below max_seq_len, rope widths are
 multiples of two 16-byte chunks); each is compared element by element with
 the parity bar of tests/parity.py (which widens it for normalised values
@@ -128,22 +131,36 @@ def random_case(op: str, k: int):
                              freq_dtype=fdt, cache_dtype=cdt, scale_dtype=sdt, rope_tail=tail)
 
 
+def launch_knobs(op: str, k: int) -> dict:
+    """The case's launch-shape overrides (gpu_harness.knobs arguments):
+    odd cases force the per-token layout (small head counts would mostly
+    pick the token-packed one); every third case draws the rest of the
+    shape, with several passes per wave more often than the library would
+    pick at these sizes, so that the one-pass tail is exercised."""
+    kw = {"pack": 0} if k % 2 else {}
+    if k % 3 == 1:
+        rng = np.random.default_rng([104729, OPS.index(op), k])
+        kw.update(ppw=_pick(rng, ("0", "2", "3")), tail=_pick(rng, (None, 0, 1, 3, 1000)),
+                  wpb=_pick(rng, ("0", "1", "2", "4")), remap=_pick(rng, ("0", "1")),
+                  lds=_pick(rng, (None, 0, 16384)))
+    return kw
+
+
 @pytest.mark.parametrize("k", range(N_PER_OP))
 @pytest.mark.parametrize("op", OPS)
 def test_random_combination(op, k, monkeypatch):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    # odd cases force the per-token layout (small head counts would mostly
-    # pick the token-packed one); even cases let the library choose
     from tests import gpu_harness as gh
-    if k % 2:
-        monkeypatch.setattr(gh, "OVERRIDES", {"pack": 0})
+    kn = launch_knobs(op, k)
+    if kn:
+        monkeypatch.setattr(gh, "OVERRIDES", kn)
     from tests import parity
     case = random_case(op, k)
     print(f"[rand] {case.name} dtype={case.dtype} D={case.caches[0].head_dim} "
           f"R={case.rope_dim} il={case.interleaved} tail={case.rope_tail} "
           f"fdt={case.freq_dtype} cache={[c.dtype for c in case.caches]} q={case.q_dtype} "
-          f"T={case.T} B={case.batch}", flush=True)
+          f"T={case.T} B={case.batch} knobs={kn}", flush=True)
     res = oracle.run_case(case)
     dc = gh.upload(case)
     gh.run(dc)
