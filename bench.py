@@ -429,7 +429,8 @@ def time_graph(launchers, steps: int, max_nodes: int = 250, wall_out=None) -> fl
 
 def copy_ceiling(nbytes: int, n_bufs: int, steps: int, graph: bool = False) -> dict:
     """A plain streaming copy of nbytes/2 (read) into nbytes/2 (written),
-    cycling through n_bufs buffer pairs: the best of 1 and 4 chunks/thread;
+    cycling through n_bufs buffer pairs: the best of 1, 2, 4 and 8
+    chunks/thread;
     with `graph`, the launches are replayed from a HIP graph."""
     import ctypes
     import torch
@@ -444,7 +445,7 @@ def copy_ceiling(nbytes: int, n_bufs: int, steps: int, graph: bool = False) -> d
              torch.empty(half // 8, dtype=torch.int64, device="cuda")) for _ in range(n_bufs)]
     stream = torch.cuda.current_stream().cuda_stream
     best = None
-    for u in (1, 4):
+    for u in (1, 2, 4, 8):
         def mk(a, b, u=u):
             def f():
                 if lib.qrp_bench_stream_copy(b.data_ptr(), a.data_ptr(), half, u, stream) != 0:
@@ -718,8 +719,9 @@ def main() -> int:
         del src, dst
 
     K = args.steps
-    # The copy ceiling (a plain copy of one step's mean bytes) is measured
-    # just before the timed region: the GPU has idled while the batches were
+    # The copy ceiling (a plain copy of one step's mean bytes, replayed from
+    # a HIP graph when the timed launches are) is measured just before the
+    # timed region: the GPU has idled while the batches were
     # generated on the host, and this brings it back to its steady clock
     # before the W warm-up steps, as a serving loop that runs continuously
     # would find it.
@@ -727,7 +729,7 @@ def main() -> int:
     if not args.no_copy_ceiling:
         log("[bench] timing the copy ceiling ...")
         cc_bytes = sum(set_bytes[k % n_sets] for k in range(K)) / K
-        cc = copy_ceiling(int(cc_bytes), n_sets, max(20, K // 2))
+        cc = copy_ceiling(int(cc_bytes), n_sets, max(20, K // 2), graph=args.graph)
 
     # Timed region: K steps back to back on the launch stream, bracketed by
     # one pair of HIP events (GPU time) and two synchronisations (wall time).

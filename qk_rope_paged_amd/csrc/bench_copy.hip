@@ -30,10 +30,17 @@ __global__ void __launch_bounds__(256) stream_copy(v4u* __restrict__ dst, const 
   }
 }
 
+template <int U>
+void launch_copy(v4u* dst, const v4u* src, uint64_t n16, hipStream_t s) {
+  const uint64_t grid = (n16 + 256 * U - 1) / (256 * U);
+  hipLaunchKernelGGL(stream_copy<U>, dim3((uint32_t)grid), dim3(256), 0, s, dst, src, n16);
+}
+
 }  // namespace
 
 // Copy nbytes (a multiple of 16; both pointers 16-byte aligned) from src to
-// dst on `stream` with U = chunks per thread (1 or 4).  Returns a hipError_t.
+// dst on `stream` with U = chunks per thread (1, 2, 4 or 8).  Returns a
+// hipError_t.
 extern "C" int32_t qrp_bench_stream_copy(void* dst, const void* src, uint64_t nbytes,
                                          int32_t chunks_per_thread, void* stream) {
   if (nbytes % 16 || (reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15u)
@@ -41,14 +48,14 @@ extern "C" int32_t qrp_bench_stream_copy(void* dst, const void* src, uint64_t nb
   const uint64_t n16 = nbytes / 16;
   if (n16 == 0) return 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (chunks_per_thread == 4) {
-    const uint64_t grid = (n16 + 1023) / 1024;
-    hipLaunchKernelGGL(stream_copy<4>, dim3((uint32_t)grid), dim3(256), 0, s,
-                       static_cast<v4u*>(dst), static_cast<const v4u*>(src), n16);
-  } else {
-    const uint64_t grid = (n16 + 255) / 256;
-    hipLaunchKernelGGL(stream_copy<1>, dim3((uint32_t)grid), dim3(256), 0, s,
-                       static_cast<v4u*>(dst), static_cast<const v4u*>(src), n16);
+  v4u* d = static_cast<v4u*>(dst);
+  const v4u* r = static_cast<const v4u*>(src);
+  switch (chunks_per_thread) {
+    case 1: launch_copy<1>(d, r, n16, s); break;
+    case 2: launch_copy<2>(d, r, n16, s); break;
+    case 4: launch_copy<4>(d, r, n16, s); break;
+    case 8: launch_copy<8>(d, r, n16, s); break;
+    default: return (int32_t)hipErrorInvalidValue;
   }
   return (int32_t)hipGetLastError();
 }
